@@ -1,0 +1,222 @@
+/*
+ * whisper_mi355x.h — C ABI of the Whisper large-v3 inference hot path on
+ * MI355X (gfx950): log-mel front end, encoder, cross-attention K/V, and the
+ * batched decoder step over a caller-owned fp8 (OCP E4M3) self-attention KV
+ * cache.
+ *
+ * Sources. The calls follow the problem as the pages state it:
+ *  - whisper_blaze showcase page ("Hopper-Native CUDA Kernels for Whisper"),
+ *    "The Solution": the five kernels (GEMM, flash attention for encoder self /
+ *    decoder causal self / decoder cross attention, GPU mel spectrogram,
+ *    fused residual+LayerNorm, fp8 quantise with per-tensor scales), and the
+ *    "Using it" direct kernel calls (quantise_e4m3, layernorm_fused,
+ *    decoder_self_attn, mel_spectrogram);
+ *  - whisper-blaze project page, "Direct Kernel API": quantise_e4m3 returns
+ *    codes and a per-tensor scale, dequantise_e4m3 takes codes, scale, shape;
+ *    layernorm_fused_residual returns (normed, total);
+ *  - "Blazingly fast whisper transcriptions with Inference Endpoints",
+ *    "Inference Stack": compute in bfloat16, KV cache stored as float8 (one
+ *    byte per element), quantised on the way in.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument is device memory owned by the caller unless
+ *    stated otherwise; the library never allocates, frees or retains caller
+ *    memory and keeps no state between calls apart from thread-local error
+ *    text.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream). Work
+ *    is enqueued asynchronously; no call synchronises.
+ *  - Argument, shape, dtype, alignment (16 bytes for tensors and workspaces;
+ *    4 bytes for the int32 token / length / argmax / key-count arrays, the
+ *    fp32 scale arrays and the device error word) and workspace-size checks
+ *    run before any launch; a failing check returns a
+ *    status and launches nothing. Launch failures return WHISPER_ERR_HIP.
+ *    Nothing throws or aborts across the ABI. whisper_last_error() returns
+ *    text for the last failure on the calling thread.
+ *  - Activations that feed a GEMM or attention are stored in `dims->act`
+ *    (bf16 or fp32); the residual stream between blocks, accumulation,
+ *    softmax and LayerNorm statistics are fp32; logits are fp32.
+ *  - Concurrent calls that share a workspace or output buffer race; calls on
+ *    distinct buffers may run on distinct streams.
+ */
+#ifndef WHISPER_MI355X_H
+#define WHISPER_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WHISPER_OK = 0,
+  WHISPER_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, bad enum */
+  WHISPER_ERR_SHAPE = 2,       /* dims inconsistent or unsupported */
+  WHISPER_ERR_DTYPE = 3,       /* dtype not supported by this call */
+  WHISPER_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  WHISPER_ERR_WORKSPACE = 5,   /* workspace smaller than the size query returns */
+  WHISPER_ERR_CAPACITY = 6,    /* KV cache slot out of range (also written to the device error word) */
+  WHISPER_ERR_HIP = 7          /* a HIP launch failed */
+} whisper_status;
+
+typedef enum { WHISPER_F32 = 0, WHISPER_BF16 = 1 } whisper_dtype;
+
+/* Model shape. head_dim must be 64 and n_heads*64 == d_model; n_audio_ctx is
+ * the number of encoder frames per 30 s chunk (1500); n_text_ctx the number of
+ * learned decoder positions. */
+typedef struct {
+  int n_mels, n_audio_ctx, d_model, n_heads, head_dim, d_ffn;
+  int n_enc_layers, n_dec_layers, n_vocab, n_text_ctx;
+  whisper_dtype act;
+} whisper_dims;
+
+enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3 };
+
+/* ------------------------------------------------------------------ weights
+ * Logical weights are fp32 device tensors in PyTorch layout, passed as an
+ * array of whisper_weight_count() pointers in this order:
+ *   encoder (only if n_enc_layers > 0):
+ *     conv1.weight [d, n_mels, 3], conv1.bias [d], conv2.weight [d, d, 3], conv2.bias [d],
+ *     per layer: attn_ln.{weight,bias} [d], attn.query.{weight [d,d], bias [d]},
+ *                attn.key.weight [d,d] (no bias), attn.value.{weight,bias},
+ *                attn.out.{weight,bias}, mlp_ln.{weight,bias},
+ *                mlp.0.{weight [f,d], bias [f]}, mlp.2.{weight [d,f], bias [d]}   (15 tensors)
+ *     ln_post.{weight,bias}
+ *   decoder (only if n_dec_layers > 0):
+ *     token_embedding [n_vocab, d] (also the tied output projection),
+ *     positional_embedding [n_text_ctx, d],
+ *     per layer: attn_ln.{w,b}, attn.query.{w,b}, attn.key.w, attn.value.{w,b}, attn.out.{w,b},
+ *                cross_attn_ln.{w,b}, cross_attn.query.{w,b}, cross_attn.key.w,
+ *                cross_attn.value.{w,b}, cross_attn.out.{w,b},
+ *                mlp_ln.{w,b}, mlp.0.{w,b}, mlp.2.{w,b}                          (24 tensors)
+ *     ln.{weight,bias}
+ * whisper_pack_weights converts them once into the library's packed buffer
+ * (activation dtype for matrices, fp32 for biases and LayerNorm parameters;
+ * fused QKV, tap-major conv filters, all decoder layers' cross K/V stacked,
+ * encoder sinusoidal positions precomputed). The packed buffer is caller
+ * memory of whisper_packed_weights_size() bytes; the logical tensors may be
+ * freed once the pack has completed on `stream`. */
+int whisper_weight_count(const whisper_dims* dims);
+size_t whisper_packed_weights_size(const whisper_dims* dims);
+whisper_status whisper_pack_weights(const whisper_dims* dims, const float* const* logical, void* packed,
+                                    void* stream);
+
+/* Workspace bytes for a call (`which` is one of WHISPER_WS_*) at `batch`
+ * chunks (LOGMEL, ENCODE, CROSS_KV) or rows (DECODE). 0 on invalid input. */
+size_t whisper_workspace_size(const whisper_dims* dims, int batch, int which);
+
+/* ------------------------------------------------------------------ front end
+ * Log-mel features of `batch` chunks (showcase page, mel_spectrogram.cu card;
+ * direct kernel call mel_spectrogram(audio) -> [1, 128, T]).
+ * audio:   [batch, n_samples] fp32, 16 kHz, n_samples <= 480000 (zero-padded to
+ *          30 s; framing reflects at the 480000-sample edges).
+ * mel_out: [batch, n_mels, 3000] fp32 (row stride 3000).
+ * Reading: 400-point periodic-Hann frames, hop 160, centre reflect padding,
+ * 201-bin power spectrum, Slaney mel 0-8 kHz, log10 floor 1e-10, clamp to
+ * chunk max - 8, (x + 4) / 4. */
+whisper_status whisper_logmel(const whisper_dims* dims, const float* audio, int batch, int n_samples,
+                              float* mel_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ encoder
+ * mel [batch, n_mels, 3000] fp32 -> enc_out [batch, n_audio_ctx, d] (act dtype):
+ * conv k3 s1 + GELU, conv k3 s2 + GELU, + sinusoidal positions, n_enc_layers
+ * pre-LN blocks (fused residual+LayerNorm, bidirectional attention, GELU MLP),
+ * final LayerNorm. */
+whisper_status whisper_encode(const whisper_dims* dims, const void* packed, const float* mel, int batch,
+                              void* enc_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Encoder blocks [layer_begin, layer_end) on hidden states h_in [batch,
+ * n_audio_ctx, d] (act dtype, read only) -> h_out (same shape); with
+ * apply_ln_post != 0 the final LayerNorm is applied. Uses the ENCODE workspace. */
+whisper_status whisper_encode_layers(const whisper_dims* dims, const void* packed, const void* h_in, int batch,
+                                     int layer_begin, int layer_end, int apply_ln_post, void* h_out, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* Cross-attention keys/values of every decoder layer, once per chunk batch:
+ * K = enc W_k^T, V = enc W_v^T + b_v, written head-major as
+ * cross_kv [n_dec_layers][2][batch][n_heads][n_audio_ctx][64] (act dtype). */
+whisper_status whisper_cross_kv(const whisper_dims* dims, const void* packed, const void* enc_out, int batch,
+                                void* cross_kv, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ decoder step
+ * One batched decoder step with given tokens (teacher forcing or greedy).
+ * tokens:    [batch] int32 token ids.
+ * lengths:   [batch] int32, in/out. lengths[b] is the cache slot the new token's
+ *            K/V go to and its position; +1 on return.
+ * kv_cache:  [n_dec_layers][2][batch][n_heads][kv_cap][64] uint8 OCP-E4M3 codes
+ *            (K then V), caller-owned. Per layer the new token's K and V are
+ *            quantised from the fp32 projection output as
+ *            code = e4m3_rne_saturate(fl32(x * fl32(1/scale))) into slot
+ *            lengths[b], then attention reads slots 0..lengths[b] dequantised.
+ * kv_scales: [n_dec_layers][2] fp32 (K, V), constant while codes are live.
+ * cross_kv:  from whisper_cross_kv for the same batch.
+ * logits:    [batch, n_vocab] fp32 or NULL (then kept in the workspace).
+ * argmax:    [batch] int32 greedy token (lowest index on ties).
+ * dev_error: device int32 or NULL; set to WHISPER_ERR_CAPACITY when a slot is
+ *            >= kv_cap or >= n_text_ctx (that row's write is skipped), or
+ *            WHISPER_ERR_INVALID_ARG for a token id out of range. */
+whisper_status whisper_decode_step(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
+                                   const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                   const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
+                                   int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ kernel-level calls
+ * fp8 E4M3 codec with a per-tensor scale (project page quantise_e4m3 /
+ * dequantise_e4m3). x: n values of dtype `dt`. With scale_in == NULL the scale
+ * is computed on the device as fl32(amax)/448 (1.0 if amax is 0) and written
+ * to scale_out; this needs a workspace of whisper_fp8_workspace_size() bytes.
+ * codes[i] = e4m3_rne_saturate(fl32(x[i] * fl32(1/scale))). */
+size_t whisper_fp8_workspace_size(void);
+whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, const float* scale_in,
+                                    uint8_t* codes, float* scale_out, void* ws, size_t ws_bytes, void* stream);
+/* y[i] = fl32(value(codes[i]) * scale[0]), stored in dtype dt. */
+whisper_status whisper_fp8_dequantize(const uint8_t* codes, size_t n, const float* scale, void* y,
+                                      whisper_dtype dt, void* stream);
+
+/* Fused residual + LayerNorm (showcase page, layernorm_fused.cu card; project
+ * page layernorm_fused_residual): total = fl32(h + residual) (h alone if
+ * residual is NULL), normed = (total - mean) / sqrt(var + eps) * gamma + beta,
+ * biased variance over d_model, fp32 statistics. h and normed: [M, d_model] in
+ * dims->act; residual and total: [M, d_model] fp32 (the residual stream is
+ * kept in fp32 between blocks); gamma, beta: [d_model] fp32. normed or total
+ * may be NULL (not written). total may alias residual. */
+whisper_status whisper_layernorm_fused(const whisper_dims* dims, const void* h, const float* residual,
+                                       const float* gamma, const float* beta, float eps, int M, void* normed,
+                                       float* total, void* stream);
+
+/* Projection GEMM (showcase page, gemm_hopper.cu card): y = act(x . w^T + bias)
+ * with x [M, K] (row stride lda elements), w [N, K], bias [N] fp32 or NULL,
+ * y [M, N]; act 0 = none, 1 = exact GELU. dt = WHISPER_BF16 needs K % 64 == 0
+ * and lda % 8 == 0. path: 0 auto, 1 tiled MFMA, 2 skinny (M <= 128, K % 128 == 0). */
+whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const void* w, const float* bias, int M,
+                              int N, int K, int act, void* y, int path, void* stream);
+
+/* Encoder bidirectional self-attention (flash_attn_hopper.cu card): qkv
+ * [batch, T, 3*n_heads*64] (Q | K | V, heads contiguous) -> out [batch, T,
+ * n_heads*64], per head softmax(q k^T / 8) v; no score matrix is stored. */
+whisper_status whisper_attention_encoder(whisper_dtype dt, const void* qkv, int batch, int T, int n_heads,
+                                         void* out, void* stream);
+
+/* Decoder self-attention over an e4m3 cache (direct kernel call
+ * decoder_self_attn): q [batch, n_heads*64]; k_codes, v_codes [batch][n_heads]
+ * [cap][64]; scales [2] fp32 (K, V); n_keys [batch] int32 keys 0..n_keys-1
+ * are attended (clamped to cap). out [batch, n_heads*64]. */
+whisper_status whisper_attention_decode_self(whisper_dtype dt, const void* q, int batch, int n_heads, int cap,
+                                             const uint8_t* k_codes, const uint8_t* v_codes, const float* scales,
+                                             const int32_t* n_keys, void* out, void* stream);
+
+/* Decoder cross-attention: q [batch, n_heads*64], k and v head-major
+ * [batch][n_heads][T][64] -> out [batch, n_heads*64]. Workspace:
+ * whisper_attention_decode_cross_workspace_size(). */
+size_t whisper_attention_decode_cross_workspace_size(int batch, int n_heads, int T);
+whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, const void* k, const void* v,
+                                              int batch, int n_heads, int T, void* out, void* ws, size_t ws_bytes,
+                                              void* stream);
+
+const char* whisper_status_string(whisper_status status);
+const char* whisper_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WHISPER_MI355X_H */

@@ -317,7 +317,7 @@ def cross_kv(enc, W, n_heads, n_layers):
 
 # =========================================================================== decoder step
 
-def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None):
+def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, forced_codes=None):
     """One batched decoder step with teacher-forced tokens.
 
     tokens, lengths: [B] ints; lengths[b] is both the cache slot the new
@@ -331,11 +331,18 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None):
     cross: list over layers of (K_c, V_c), each indexable as K_c[b] -> [H, T, dh].
     rows: optional list of batch rows to compute (others are skipped);
         rows are independent, so a subset gives exactly those rows' results.
+    forced_codes: optional forced_codes[layer][kv][b] -> [H, dh] uint8 codes
+        stored in the new slot instead of the oracle's own quantisation. A
+        value close to a rounding boundary has two valid codes; once another
+        implementation's choice has been checked against the oracle's own code
+        and pre-quantisation value (both returned in the trace), the oracle can
+        continue from the same cache contents.
 
     The new token's K and V are written first and then read back from the
     cache with the rest (quantise-on-write, dequantise-on-read).
     Returns (logits [B, V] float64, trace dict with the fp32 pre-quantisation
-    K/V values [L, 2, B, H, dh] and the last residual stream).
+    K/V values [L, 2, B, H, dh], the oracle's own codes [L, 2, B, H, dh] and
+    the last residual stream).
     """
     n_layers = len(cross)
     bsz = len(tokens)
@@ -346,6 +353,7 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None):
     for b in rows:
         x[b] = W["decoder.token_embedding"][tokens[b]] + W["decoder.positional_embedding"][lengths[b]]
     pre = np.zeros((n_layers, 2, bsz, n_heads, dh), dtype=np.float32)
+    own = np.zeros((n_layers, 2, bsz, n_heads, dh), dtype=np.uint8)
     for layer in range(n_layers):
         p = f"decoder.blocks.{layer}."
         a = layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
@@ -362,7 +370,9 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None):
                     slot[:, pos, :] = vb
                 else:
                     pre[layer, kv, b] = e4m3_pre_quant(vb, scales[layer][kv])
-                    slot[:, pos, :] = e4m3_quantize(vb, scales[layer][kv])
+                    own[layer, kv, b] = e4m3_quantize(vb, scales[layer][kv])
+                    forced = None if forced_codes is None else forced_codes[layer][kv][b]
+                    slot[:, pos, :] = own[layer, kv, b] if forced is None else forced
             for h in range(n_heads):
                 kc_ = cache[layer][0][b][h, :pos + 1, :]
                 vc_ = cache[layer][1][b][h, :pos + 1, :]
@@ -388,7 +398,7 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None):
                        W[p + "mlp.2.weight"], W[p + "mlp.2.bias"])
     y = layer_norm(x, W["decoder.ln.weight"], W["decoder.ln.bias"])
     logits = y @ W["decoder.token_embedding"].T
-    return logits, {"pre_quant": pre, "x": x}
+    return logits, {"pre_quant": pre, "codes": own, "x": x}
 
 
 def greedy_token(logits):

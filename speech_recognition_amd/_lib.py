@@ -1,0 +1,218 @@
+"""ctypes binding of libwhisper_mi355x.so: same names and arguments as the C
+ABI in include/whisper_mi355x.h; only marshalling happens here.
+
+Pointers may be passed as torch tensors (their data_ptr() is used), plain
+ints or None (NULL). `stream` defaults to torch's current stream on the
+current device. A non-OK status raises WhisperError with the library's own
+message. Loading fails loudly if the library has not been built: there is no
+fallback path.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwhisper_mi355x.so")
+
+WHISPER_F32, WHISPER_BF16 = 0, 1
+WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE = 0, 1, 2, 3
+
+EXPORTS = [
+    "whisper_weight_count", "whisper_packed_weights_size", "whisper_pack_weights", "whisper_workspace_size",
+    "whisper_logmel", "whisper_encode", "whisper_encode_layers", "whisper_cross_kv", "whisper_decode_step",
+    "whisper_fp8_workspace_size", "whisper_fp8_quantize", "whisper_fp8_dequantize", "whisper_layernorm_fused",
+    "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
+    "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
+    "whisper_status_string", "whisper_last_error",
+]
+
+
+class WhisperError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"whisper status {status}: {msg}")
+        self.status = status
+
+
+class WhisperDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "n_mels", "n_audio_ctx", "d_model", "n_heads", "head_dim", "d_ffn",
+        "n_enc_layers", "n_dec_layers", "n_vocab", "n_text_ctx", "act")]
+
+
+def make_dims(d):
+    """WhisperDims from a workload Dims-like object (or pass a WhisperDims)."""
+    if isinstance(d, WhisperDims):
+        return d
+    return WhisperDims(d.n_mels, d.n_audio_ctx, d.d_model, d.n_heads, d.head_dim, d.d_ffn,
+                       d.n_enc_layers, d.n_dec_layers, d.n_vocab, d.n_text_ctx,
+                       WHISPER_BF16 if d.act == "bf16" else WHISPER_F32)
+
+
+_lib = None
+P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+_SIG = {
+    "whisper_weight_count": (I, [P]),
+    "whisper_packed_weights_size": (Z, [P]),
+    "whisper_pack_weights": (I, [P, P, P, P]),
+    "whisper_workspace_size": (Z, [P, I, I]),
+    "whisper_logmel": (I, [P, P, I, I, P, P, Z, P]),
+    "whisper_encode": (I, [P, P, P, I, P, P, Z, P]),
+    "whisper_encode_layers": (I, [P, P, P, I, I, I, I, P, P, Z, P]),
+    "whisper_cross_kv": (I, [P, P, P, I, P, P, Z, P]),
+    "whisper_decode_step": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_fp8_workspace_size": (Z, []),
+    "whisper_fp8_quantize": (I, [P, I, Z, P, P, P, P, Z, P]),
+    "whisper_fp8_dequantize": (I, [P, Z, P, P, I, P]),
+    "whisper_layernorm_fused": (I, [P, P, P, P, P, F, I, P, P, P]),
+    "whisper_linear": (I, [I, P, I, P, P, I, I, I, I, P, I, P]),
+    "whisper_attention_encoder": (I, [I, P, I, I, I, P, P]),
+    "whisper_attention_decode_self": (I, [I, P, I, I, I, P, P, P, P, P, P]),
+    "whisper_attention_decode_cross_workspace_size": (Z, [I, I, I]),
+    "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
+    "whisper_status_string": (ctypes.c_char_p, [I]),
+    "whisper_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load the library (once). Raises if it is missing: build it first."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run speech_recognition_amd/build.py "
+                              "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is not None:
+        return s if isinstance(s, int) else s.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status):
+    if status != 0:
+        raise WhisperError(status, lib().whisper_last_error().decode())
+
+
+def _dims_ptr(d):
+    dd = make_dims(d)
+    return dd, ctypes.byref(dd)
+
+
+# ------------------------------------------------------------------ size queries
+def whisper_weight_count(dims):
+    dd, dp = _dims_ptr(dims)
+    return lib().whisper_weight_count(dp)
+
+
+def whisper_packed_weights_size(dims):
+    dd, dp = _dims_ptr(dims)
+    return lib().whisper_packed_weights_size(dp)
+
+
+def whisper_workspace_size(dims, batch, which):
+    dd, dp = _dims_ptr(dims)
+    return lib().whisper_workspace_size(dp, batch, which)
+
+
+def whisper_fp8_workspace_size():
+    return lib().whisper_fp8_workspace_size()
+
+
+def whisper_attention_decode_cross_workspace_size(batch, n_heads, T):
+    return lib().whisper_attention_decode_cross_workspace_size(batch, n_heads, T)
+
+
+# ------------------------------------------------------------------ calls
+def whisper_pack_weights(dims, logical, packed, stream=None):
+    """logical: sequence of fp32 device tensors (or pointers) in the ABI's order."""
+    dd, dp = _dims_ptr(dims)
+    arr = (ctypes.c_void_p * len(logical))(*[_p(t) for t in logical])
+    _check(lib().whisper_pack_weights(dp, arr, _p(packed), _stream(stream)))
+
+
+def whisper_logmel(dims, audio, batch, n_samples, mel_out, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_logmel(dp, _p(audio), batch, n_samples, _p(mel_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_encode(dims, packed, mel, batch, enc_out, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_encode(dp, _p(packed), _p(mel), batch, _p(enc_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_encode_layers(dims, packed, h_in, batch, layer_begin, layer_end, apply_ln_post, h_out, ws, ws_bytes,
+                          stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_encode_layers(dp, _p(packed), _p(h_in), batch, layer_begin, layer_end, int(apply_ln_post),
+                                       _p(h_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_cross_kv(dims, packed, enc_out, batch, cross_kv, ws=None, ws_bytes=0, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_cross_kv(dp, _p(packed), _p(enc_out), batch, _p(cross_kv), _p(ws), ws_bytes,
+                                  _stream(stream)))
+
+
+def whisper_decode_step(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits, argmax,
+                        dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_step(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
+                                     _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax), _p(dev_error), _p(ws),
+                                     ws_bytes, _stream(stream)))
+
+
+def whisper_fp8_quantize(x, dt, n, scale_in, codes, scale_out, ws=None, ws_bytes=0, stream=None):
+    _check(lib().whisper_fp8_quantize(_p(x), dt, n, _p(scale_in), _p(codes), _p(scale_out), _p(ws), ws_bytes,
+                                      _stream(stream)))
+
+
+def whisper_fp8_dequantize(codes, n, scale, y, dt, stream=None):
+    _check(lib().whisper_fp8_dequantize(_p(codes), n, _p(scale), _p(y), dt, _stream(stream)))
+
+
+def whisper_layernorm_fused(dims, h, residual, gamma, beta, eps, M, normed, total, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_layernorm_fused(dp, _p(h), _p(residual), _p(gamma), _p(beta), eps, M, _p(normed),
+                                         _p(total), _stream(stream)))
+
+
+def whisper_linear(dt, x, lda, w, bias, M, N, K, act, y, path=0, stream=None):
+    _check(lib().whisper_linear(dt, _p(x), lda, _p(w), _p(bias), M, N, K, act, _p(y), path, _stream(stream)))
+
+
+def whisper_attention_encoder(dt, qkv, batch, T, n_heads, out, stream=None):
+    _check(lib().whisper_attention_encoder(dt, _p(qkv), batch, T, n_heads, _p(out), _stream(stream)))
+
+
+def whisper_attention_decode_self(dt, q, batch, n_heads, cap, k_codes, v_codes, scales, n_keys, out, stream=None):
+    _check(lib().whisper_attention_decode_self(dt, _p(q), batch, n_heads, cap, _p(k_codes), _p(v_codes),
+                                               _p(scales), _p(n_keys), _p(out), _stream(stream)))
+
+
+def whisper_attention_decode_cross(dt, q, k, v, batch, n_heads, T, out, ws, ws_bytes, stream=None):
+    _check(lib().whisper_attention_decode_cross(dt, _p(q), _p(k), _p(v), batch, n_heads, T, _p(out), _p(ws),
+                                                ws_bytes, _stream(stream)))
+
+
+def whisper_status_string(status):
+    return lib().whisper_status_string(status).decode()
+
+
+def whisper_last_error():
+    return lib().whisper_last_error().decode()

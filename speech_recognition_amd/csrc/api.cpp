@@ -1,0 +1,597 @@
+// C-ABI host layer: argument validation, packed-weight and workspace layout,
+// and the launch sequences of log-mel, encoder, cross K/V and decoder step.
+// All checks run before the first launch; nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "whisper_mi355x.h"
+
+using namespace wh;
+
+namespace {
+
+thread_local std::string g_err;
+
+whisper_status fail(whisper_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define WH_TRY(expr)                                                                                \
+  do {                                                                                              \
+    hipError_t e_ = (expr);                                                                         \
+    if (e_ != hipSuccess) return fail(WHISPER_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define WH_CHECK(st)                   \
+  do {                                 \
+    whisper_status s_ = (st);          \
+    if (s_ != WHISPER_OK) return s_;   \
+  } while (0)
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+ActType act_of(whisper_dtype t) { return t == WHISPER_BF16 ? ACT_BF16 : ACT_F32; }
+size_t esz(whisper_dtype t) { return t == WHISPER_BF16 ? 2 : 4; }
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+constexpr int N_FRAMES = 3000;  // STFT frames per 30 s chunk; the conv stem halves them
+
+whisper_status check_dims(const whisper_dims* d) {
+  if (!d) return fail(WHISPER_ERR_INVALID_ARG, "dims is NULL");
+  if (d->act != WHISPER_F32 && d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "dims->act must be F32 or BF16");
+  if (d->head_dim != 64) return fail(WHISPER_ERR_SHAPE, "head_dim must be 64");
+  if (d->n_heads <= 0 || d->n_heads * 64 != d->d_model) return fail(WHISPER_ERR_SHAPE, "n_heads * 64 must equal d_model");
+  if (d->d_model > 2048) return fail(WHISPER_ERR_SHAPE, "d_model must be <= 2048");
+  if (d->d_ffn <= 0 || d->d_ffn % 128) return fail(WHISPER_ERR_SHAPE, "d_ffn must be a positive multiple of 128");
+  if (d->n_enc_layers < 0 || d->n_dec_layers < 0) return fail(WHISPER_ERR_SHAPE, "layer counts must be >= 0");
+  if (d->n_audio_ctx <= 0 || d->n_audio_ctx * 2 != N_FRAMES) return fail(WHISPER_ERR_SHAPE, "n_audio_ctx must be 1500");
+  if (d->n_mels <= 0 || d->n_mels > 512) return fail(WHISPER_ERR_SHAPE, "n_mels must be in 1..512");
+  if (d->act == WHISPER_BF16 && (3 * d->n_mels) % 64) return fail(WHISPER_ERR_SHAPE, "bf16 needs 3*n_mels % 64 == 0");
+  if (d->n_dec_layers > 0 && (d->n_vocab <= 0 || d->n_text_ctx <= 0)) return fail(WHISPER_ERR_SHAPE, "decoder needs n_vocab, n_text_ctx > 0");
+  return WHISPER_OK;
+}
+
+// ------------------------------------------------------------------ packed layout
+struct EncL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, w1, b1, w2, b2; };
+struct DecL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, wqc, bqc, woc, boc, ln3g, ln3b, w1, b1, w2, b2; };
+struct Packed {
+  size_t conv1w = 0, conv1b = 0, conv2w = 0, conv2b = 0, pe = 0, lnpg = 0, lnpb = 0;
+  std::vector<EncL> enc;
+  size_t tok = 0, pos = 0, ckvw = 0, ckvb = 0, lnfg = 0, lnfb = 0;
+  std::vector<DecL> dec;
+  size_t total = 0;
+};
+
+Packed layout(const whisper_dims* d) {
+  Packed P;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  const size_t e = esz(d->act), D = d->d_model, F = d->d_ffn, f4 = 4;
+  if (d->n_enc_layers > 0) {
+    P.conv1w = take(D * 3 * d->n_mels * e); P.conv1b = take(D * f4);
+    P.conv2w = take(D * 3 * D * e); P.conv2b = take(D * f4);
+    P.pe = take((size_t)d->n_audio_ctx * D * f4);
+    for (int l = 0; l < d->n_enc_layers; ++l) {
+      EncL L;
+      L.ln1g = take(D * f4); L.ln1b = take(D * f4);
+      L.wqkv = take(3 * D * D * e); L.bqkv = take(3 * D * f4);
+      L.wo = take(D * D * e); L.bo = take(D * f4);
+      L.ln2g = take(D * f4); L.ln2b = take(D * f4);
+      L.w1 = take(F * D * e); L.b1 = take(F * f4);
+      L.w2 = take(D * F * e); L.b2 = take(D * f4);
+      P.enc.push_back(L);
+    }
+    P.lnpg = take(D * f4); P.lnpb = take(D * f4);
+  }
+  if (d->n_dec_layers > 0) {
+    P.tok = take((size_t)d->n_vocab * D * e);
+    P.pos = take((size_t)d->n_text_ctx * D * e);
+    for (int l = 0; l < d->n_dec_layers; ++l) {
+      DecL L;
+      L.ln1g = take(D * f4); L.ln1b = take(D * f4);
+      L.wqkv = take(3 * D * D * e); L.bqkv = take(3 * D * f4);
+      L.wo = take(D * D * e); L.bo = take(D * f4);
+      L.ln2g = take(D * f4); L.ln2b = take(D * f4);
+      L.wqc = take(D * D * e); L.bqc = take(D * f4);
+      L.woc = take(D * D * e); L.boc = take(D * f4);
+      L.ln3g = take(D * f4); L.ln3b = take(D * f4);
+      L.w1 = take(F * D * e); L.b1 = take(F * f4);
+      L.w2 = take(D * F * e); L.b2 = take(D * f4);
+      P.dec.push_back(L);
+    }
+    P.ckvw = take((size_t)d->n_dec_layers * 2 * D * D * e);
+    P.ckvb = take((size_t)d->n_dec_layers * 2 * D * f4);
+    P.lnfg = take(D * f4); P.lnfb = take(D * f4);
+  }
+  P.total = off;
+  return P;
+}
+
+int weight_count(const whisper_dims* d) {
+  return (d->n_enc_layers > 0 ? 4 + 15 * d->n_enc_layers + 2 : 0) + (d->n_dec_layers > 0 ? 2 + 24 * d->n_dec_layers + 2 : 0);
+}
+
+// ------------------------------------------------------------------ workspace layout
+struct EncWS { size_t x0, g1, x, a, dlt, qkv, att, hf, total; };
+EncWS enc_ws(const whisper_dims* d, int B) {
+  EncWS W;
+  const size_t e = esz(d->act), D = d->d_model, T = d->n_audio_ctx, rows = (size_t)B * T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  W.x = take(rows * D * 4);  // fp32 residual stream
+  W.a = take(rows * D * e);
+  W.dlt = take(rows * D * e);
+  W.att = take(rows * D * e);
+  const size_t qkv_b = std::max(rows * 3 * D * e, (size_t)B * (N_FRAMES + 2) * d->n_mels * e);
+  W.qkv = take(qkv_b);
+  W.x0 = W.qkv;  // conv1 input lives in the QKV buffer before the first block
+  const size_t hf_b = std::max(rows * d->d_ffn * e, (size_t)B * (N_FRAMES + 2) * D * e);
+  W.hf = take(hf_b);
+  W.g1 = W.hf;   // conv1 output lives in the MLP buffer before the first block
+  W.total = off;
+  return W;
+}
+
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, cross, total; };
+DecWS dec_ws(const whisper_dims* d, int B) {
+  DecWS W;
+  const size_t e = esz(d->act), D = d->d_model;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  W.x = take(B * D * 4); W.a = take(B * D * e); W.dlt = take(B * D * e); W.q = take(B * D * e);
+  W.att = take(B * D * e); W.qc = take(B * D * e);
+  W.hf = take((size_t)B * d->d_ffn * e);
+  W.logits = take((size_t)B * d->n_vocab * 4);
+  W.cross = take(attn_decode_cross_ws(B, d->n_heads, d->n_audio_ctx));
+  W.total = off;
+  return W;
+}
+
+template <typename T> T* at(const void* base, size_t off) { return (T*)((char*)base + off); }
+
+// ------------------------------------------------------------------ GEMM helpers
+GemmParams gp(const void* A, long lda, const void* B, long ldb, int M, int N, int K, const float* bias, void* C,
+              long ldc) {
+  GemmParams p{};
+  p.A = A; p.lda = lda; p.B = B; p.ldb = ldb; p.M = M; p.N = N; p.K = K; p.batch = 1;
+  p.bias = bias; p.C = C; p.ldc = ldc;
+  return p;
+}
+
+// ------------------------------------------------------------------ encoder blocks
+// The residual stream X is fp32 in the workspace. `h_in` is either that
+// buffer already holding the stem output (in_is_x) or caller hidden states in
+// the activation type, which the first LayerNorm copies into X.
+whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const Packed& P, const EncWS& W,
+                              const void* h_in, bool in_is_x, int B, int l0, int l1, bool ln_post, void* out,
+                              void* ws, hipStream_t s) {
+  const ActType t = act_of(d->act);
+  const int D = d->d_model, T = d->n_audio_ctx, M = B * T, F = d->d_ffn;
+  float* X = at<float>(ws, W.x);
+  void* A = at<void>(ws, W.a);
+  void* Dl = at<void>(ws, W.dlt);
+  void* QKV = at<void>(ws, W.qkv);
+  void* ATT = at<void>(ws, W.att);
+  void* HF = at<void>(ws, W.hf);
+  bool x_ready = in_is_x;  // X holds the residual stream
+  bool have_delta = false; // Dl holds a block output not yet added to X
+  for (int l = l0; l < l1; ++l) {
+    const EncL& L = P.enc[l];
+    const float* g1 = at<float>(packed, L.ln1g);
+    const float* b1 = at<float>(packed, L.ln1b);
+    if (have_delta)
+      WH_TRY(launch_layernorm(t, false, Dl, X, g1, b1, 1e-5f, M, D, A, X, s));
+    else if (x_ready)
+      WH_TRY(launch_layernorm(t, true, X, nullptr, g1, b1, 1e-5f, M, D, A, nullptr, s));
+    else
+      WH_TRY(launch_layernorm(t, false, h_in, nullptr, g1, b1, 1e-5f, M, D, A, X, s));
+    x_ready = true;
+    WH_TRY(launch_gemm(t, EPI_STORE, gp(A, D, at<void>(packed, L.wqkv), D, M, 3 * D, D, at<float>(packed, L.bqkv), QKV, 3 * D), s));
+    WH_TRY(launch_attn_encoder(t, QKV, B, T, d->n_heads, ATT, s));
+    WH_TRY(launch_gemm(t, EPI_STORE, gp(ATT, D, at<void>(packed, L.wo), D, M, D, D, at<float>(packed, L.bo), Dl, D), s));
+    WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s));
+    WH_TRY(launch_gemm(t, EPI_GELU, gp(A, D, at<void>(packed, L.w1), D, M, F, D, at<float>(packed, L.b1), HF, F), s));
+    WH_TRY(launch_gemm(t, EPI_STORE, gp(HF, F, at<void>(packed, L.w2), F, M, D, F, at<float>(packed, L.b2), Dl, D), s));
+    have_delta = true;
+  }
+  const float* gp_ = at<float>(packed, P.lnpg);
+  const float* bp_ = at<float>(packed, P.lnpb);
+  if (ln_post) {
+    if (have_delta) WH_TRY(launch_layernorm(t, false, Dl, X, gp_, bp_, 1e-5f, M, D, out, nullptr, s));
+    else if (x_ready) WH_TRY(launch_layernorm(t, true, X, nullptr, gp_, bp_, 1e-5f, M, D, out, nullptr, s));
+    else WH_TRY(launch_layernorm(t, false, h_in, nullptr, gp_, bp_, 1e-5f, M, D, out, nullptr, s));
+  } else {
+    if (have_delta) WH_TRY(launch_layernorm(t, false, Dl, X, gp_, bp_, 1e-5f, M, D, nullptr, X, s));
+    else if (!x_ready) WH_TRY(launch_layernorm(t, false, h_in, nullptr, gp_, bp_, 1e-5f, M, D, nullptr, X, s));
+    WH_TRY(launch_convert(t, X, out, (size_t)M * D, s));
+  }
+  return WHISPER_OK;
+}
+
+whisper_status check_ptrs(std::initializer_list<const void*> ps, const char* what) {
+  for (const void* p : ps) {
+    if (!p) return fail(WHISPER_ERR_INVALID_ARG, std::string(what) + ": NULL pointer");
+    if (!aligned16(p)) return fail(WHISPER_ERR_ALIGN, std::string(what) + ": pointer not 16-byte aligned");
+  }
+  return WHISPER_OK;
+}
+
+// Small index / scale arrays only need their element alignment.
+whisper_status check_ptrs4(std::initializer_list<const void*> ps, const char* what) {
+  for (const void* p : ps) {
+    if (!p) return fail(WHISPER_ERR_INVALID_ARG, std::string(what) + ": NULL pointer");
+    if ((uintptr_t)p & 3u) return fail(WHISPER_ERR_ALIGN, std::string(what) + ": pointer not 4-byte aligned");
+  }
+  return WHISPER_OK;
+}
+
+whisper_status check_ws(void* ws, size_t have, size_t need, const char* what) {
+  if (need > have) return fail(WHISPER_ERR_WORKSPACE, std::string(what) + ": workspace of " + std::to_string(have) +
+                                                          " bytes, need " + std::to_string(need));
+  if (need && !ws) return fail(WHISPER_ERR_INVALID_ARG, std::string(what) + ": workspace is NULL");
+  if (ws && !aligned16(ws)) return fail(WHISPER_ERR_ALIGN, std::string(what) + ": workspace not 16-byte aligned");
+  return WHISPER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* whisper_status_string(whisper_status st) {
+  switch (st) {
+    case WHISPER_OK: return "ok";
+    case WHISPER_ERR_INVALID_ARG: return "invalid argument";
+    case WHISPER_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case WHISPER_ERR_DTYPE: return "unsupported dtype";
+    case WHISPER_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case WHISPER_ERR_WORKSPACE: return "workspace too small";
+    case WHISPER_ERR_CAPACITY: return "KV cache capacity exceeded";
+    case WHISPER_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* whisper_last_error(void) { return g_err.c_str(); }
+
+int whisper_weight_count(const whisper_dims* d) {
+  if (check_dims(d) != WHISPER_OK) return 0;
+  return weight_count(d);
+}
+
+size_t whisper_packed_weights_size(const whisper_dims* d) {
+  if (check_dims(d) != WHISPER_OK) return 0;
+  return layout(d).total;
+}
+
+whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w, void* packed, void* stream) {
+  WH_CHECK(check_dims(d));
+  if (!w) return fail(WHISPER_ERR_INVALID_ARG, "pack: weight table is NULL");
+  WH_CHECK(check_ptrs({packed}, "pack"));
+  const int n = weight_count(d);
+  for (int i = 0; i < n; ++i) {
+    if (!w[i]) return fail(WHISPER_ERR_INVALID_ARG, "pack: weight " + std::to_string(i) + " is NULL");
+    if (((uintptr_t)w[i] & 3u) != 0) return fail(WHISPER_ERR_ALIGN, "pack: weight " + std::to_string(i) + " not 4-byte aligned");
+  }
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  const ActType t = act_of(d->act);
+  const hipStream_t s = S(stream);
+  const size_t D = d->d_model, F = d->d_ffn, e = esz(d->act);
+  int i = 0;
+  auto cvt = [&](const float* src, size_t off, size_t cnt) { return launch_convert(t, src, at<void>(packed, off), cnt, s); };
+  auto cpy = [&](const float* src, size_t off, size_t cnt) { return launch_copy_f32(src, at<float>(packed, off), cnt, s); };
+  if (d->n_enc_layers > 0) {
+    WH_TRY(launch_pack_conv(t, w[i++], D, d->n_mels, 3, at<void>(packed, P.conv1w), s));
+    WH_TRY(cpy(w[i++], P.conv1b, D));
+    WH_TRY(launch_pack_conv(t, w[i++], D, D, 3, at<void>(packed, P.conv2w), s));
+    WH_TRY(cpy(w[i++], P.conv2b, D));
+    WH_TRY(launch_sinusoids(at<float>(packed, P.pe), d->n_audio_ctx, D, s));
+    for (int l = 0; l < d->n_enc_layers; ++l) {
+      const EncL& L = P.enc[l];
+      WH_TRY(cpy(w[i + 0], L.ln1g, D)); WH_TRY(cpy(w[i + 1], L.ln1b, D));
+      WH_TRY(cvt(w[i + 2], L.wqkv, D * D)); WH_TRY(cpy(w[i + 3], L.bqkv, D));
+      WH_TRY(cvt(w[i + 4], L.wqkv + D * D * e, D * D));
+      WH_TRY(launch_fill_f32(at<float>(packed, L.bqkv + D * 4), 0.f, D, s));
+      WH_TRY(cvt(w[i + 5], L.wqkv + 2 * D * D * e, D * D)); WH_TRY(cpy(w[i + 6], L.bqkv + 2 * D * 4, D));
+      WH_TRY(cvt(w[i + 7], L.wo, D * D)); WH_TRY(cpy(w[i + 8], L.bo, D));
+      WH_TRY(cpy(w[i + 9], L.ln2g, D)); WH_TRY(cpy(w[i + 10], L.ln2b, D));
+      WH_TRY(cvt(w[i + 11], L.w1, F * D)); WH_TRY(cpy(w[i + 12], L.b1, F));
+      WH_TRY(cvt(w[i + 13], L.w2, D * F)); WH_TRY(cpy(w[i + 14], L.b2, D));
+      i += 15;
+    }
+    WH_TRY(cpy(w[i++], P.lnpg, D));
+    WH_TRY(cpy(w[i++], P.lnpb, D));
+  }
+  if (d->n_dec_layers > 0) {
+    WH_TRY(cvt(w[i++], P.tok, (size_t)d->n_vocab * D));
+    WH_TRY(cvt(w[i++], P.pos, (size_t)d->n_text_ctx * D));
+    for (int l = 0; l < d->n_dec_layers; ++l) {
+      const DecL& L = P.dec[l];
+      const size_t ck = P.ckvw + (size_t)l * 2 * D * D * e, cb = P.ckvb + (size_t)l * 2 * D * 4;
+      WH_TRY(cpy(w[i + 0], L.ln1g, D)); WH_TRY(cpy(w[i + 1], L.ln1b, D));
+      WH_TRY(cvt(w[i + 2], L.wqkv, D * D)); WH_TRY(cpy(w[i + 3], L.bqkv, D));
+      WH_TRY(cvt(w[i + 4], L.wqkv + D * D * e, D * D));
+      WH_TRY(launch_fill_f32(at<float>(packed, L.bqkv + D * 4), 0.f, D, s));
+      WH_TRY(cvt(w[i + 5], L.wqkv + 2 * D * D * e, D * D)); WH_TRY(cpy(w[i + 6], L.bqkv + 2 * D * 4, D));
+      WH_TRY(cvt(w[i + 7], L.wo, D * D)); WH_TRY(cpy(w[i + 8], L.bo, D));
+      WH_TRY(cpy(w[i + 9], L.ln2g, D)); WH_TRY(cpy(w[i + 10], L.ln2b, D));
+      WH_TRY(cvt(w[i + 11], L.wqc, D * D)); WH_TRY(cpy(w[i + 12], L.bqc, D));
+      WH_TRY(cvt(w[i + 13], ck, D * D));
+      WH_TRY(launch_fill_f32(at<float>(packed, cb), 0.f, D, s));
+      WH_TRY(cvt(w[i + 14], ck + D * D * e, D * D)); WH_TRY(cpy(w[i + 15], cb + D * 4, D));
+      WH_TRY(cvt(w[i + 16], L.woc, D * D)); WH_TRY(cpy(w[i + 17], L.boc, D));
+      WH_TRY(cpy(w[i + 18], L.ln3g, D)); WH_TRY(cpy(w[i + 19], L.ln3b, D));
+      WH_TRY(cvt(w[i + 20], L.w1, F * D)); WH_TRY(cpy(w[i + 21], L.b1, F));
+      WH_TRY(cvt(w[i + 22], L.w2, D * F)); WH_TRY(cpy(w[i + 23], L.b2, D));
+      i += 24;
+    }
+    WH_TRY(cpy(w[i++], P.lnfg, D));
+    WH_TRY(cpy(w[i++], P.lnfb, D));
+  }
+  return WHISPER_OK;
+}
+
+size_t whisper_workspace_size(const whisper_dims* d, int batch, int which) {
+  if (check_dims(d) != WHISPER_OK || batch <= 0) return 0;
+  switch (which) {
+    case WHISPER_WS_LOGMEL: return al256(logmel_ws(batch, d->n_mels));
+    case WHISPER_WS_ENCODE: return enc_ws(d, batch).total;
+    case WHISPER_WS_CROSS_KV: return 0;
+    case WHISPER_WS_DECODE: return dec_ws(d, batch).total;
+  }
+  return 0;
+}
+
+whisper_status whisper_logmel(const whisper_dims* d, const float* audio, int B, int n_samples, float* mel_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "logmel: batch must be > 0");
+  if (n_samples <= 0 || n_samples > 480000) return fail(WHISPER_ERR_SHAPE, "logmel: n_samples must be in 1..480000");
+  WH_CHECK(check_ptrs({audio, mel_out}, "logmel"));
+  WH_CHECK(check_ws(ws, ws_bytes, whisper_workspace_size(d, B, WHISPER_WS_LOGMEL), "logmel"));
+  (void)hipGetLastError();
+  WH_TRY(launch_logmel(audio, B, n_samples, d->n_mels, mel_out, ws, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_encode_layers(const whisper_dims* d, const void* packed, const void* h_in, int B, int l0,
+                                     int l1, int apply_ln_post, void* h_out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  WH_CHECK(check_dims(d));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "encode_layers: batch must be > 0");
+  if (d->n_enc_layers <= 0 || l0 < 0 || l1 < l0 || l1 > d->n_enc_layers)
+    return fail(WHISPER_ERR_SHAPE, "encode_layers: layer range outside the encoder");
+  WH_CHECK(check_ptrs({packed, h_in, h_out}, "encode_layers"));
+  const EncWS W = enc_ws(d, B);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "encode_layers"));
+  (void)hipGetLastError();
+  return run_enc_layers(d, packed, layout(d), W, h_in, false, B, l0, l1, apply_ln_post != 0, h_out, ws, S(stream));
+}
+
+whisper_status whisper_encode(const whisper_dims* d, const void* packed, const float* mel, int B, void* enc_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "encode: batch must be > 0");
+  if (d->n_enc_layers <= 0) return fail(WHISPER_ERR_SHAPE, "encode: no encoder layers");
+  WH_CHECK(check_ptrs({packed, mel, enc_out}, "encode"));
+  const EncWS W = enc_ws(d, B);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "encode"));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  const ActType t = act_of(d->act);
+  const hipStream_t s = S(stream);
+  const int D = d->d_model, T = d->n_audio_ctx, nm = d->n_mels;
+  const long R = N_FRAMES + 2;  // padded time rows of the conv inputs
+  void* X0 = at<void>(ws, W.x0);
+  void* G1 = at<void>(ws, W.g1);
+  float* X = at<float>(ws, W.x);
+  WH_TRY(launch_mel_to_conv_input(t, mel, B, nm, N_FRAMES, X0, s));
+  WH_TRY(launch_zero_rows(t, G1, D, R, B, 0, (int)R - 1, s));
+  const size_t e = esz(d->act);
+  // conv1 (k3, s1, p1): output row t reads padded input rows t..t+2 = one contiguous 3*n_mels slice
+  GemmParams c1 = gp(X0, nm, at<void>(packed, P.conv1w), 3 * nm, N_FRAMES, D, 3 * nm, at<float>(packed, P.conv1b),
+                     (char*)G1 + D * e, D);
+  c1.batch = B; c1.strideA = R * nm; c1.strideC = R * D;
+  WH_TRY(launch_gemm(t, EPI_GELU, c1, s));
+  // conv2 (k3, s2, p1): output row t reads padded rows 2t..2t+2, so the row stride is 2*d
+  GemmParams c2 = gp(G1, 2 * D, at<void>(packed, P.conv2w), 3 * D, T, D, 3 * D, at<float>(packed, P.conv2b), X, D);
+  c2.batch = B; c2.strideA = R * D; c2.strideC = (long)T * D; c2.pe = at<float>(packed, P.pe);
+  WH_TRY(launch_gemm(t, EPI_GELU_PE, c2, s));
+  return run_enc_layers(d, packed, P, W, X, true, B, 0, d->n_enc_layers, true, enc_out, ws, s);
+}
+
+whisper_status whisper_cross_kv(const whisper_dims* d, const void* packed, const void* enc_out, int B, void* cross_kv,
+                                void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  WH_CHECK(check_dims(d));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "cross_kv: batch must be > 0");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "cross_kv: no decoder layers");
+  WH_CHECK(check_ptrs({packed, enc_out, cross_kv}, "cross_kv"));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  const int D = d->d_model, T = d->n_audio_ctx;
+  GemmParams p = gp(enc_out, D, at<void>(packed, P.ckvw), D, B * T, d->n_dec_layers * 2 * D, D,
+                    at<float>(packed, P.ckvb), cross_kv, 0);
+  p.ckv_T = T; p.ckv_B = B; p.ckv_H = d->n_heads; p.ckv_d = D;
+  WH_TRY(launch_gemm(act_of(d->act), EPI_CROSSKV, p, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, int B, int cap, const int32_t* tokens,
+                                   int32_t* lengths, uint8_t* kv_cache, const float* kv_scales, const void* cross_kv,
+                                   float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  WH_CHECK(check_dims(d));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_step: batch must be > 0");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_step: no decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_step: kv_cap must be in 1..4096");
+  WH_CHECK(check_ptrs({packed, kv_cache, cross_kv}, "decode_step"));
+  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, "decode_step"));
+  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, "decode_step: logits not 16-byte aligned");
+  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_step: dev_error not 4-byte aligned");
+  const DecWS W = dec_ws(d, B);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_step"));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  const ActType t = act_of(d->act);
+  const hipStream_t s = S(stream);
+  const int D = d->d_model, H = d->n_heads, T = d->n_audio_ctx, F = d->d_ffn, L = d->n_dec_layers;
+  const size_t e = esz(d->act);
+  float* X = at<float>(ws, W.x);
+  void* A = at<void>(ws, W.a);
+  void* Dl = at<void>(ws, W.dlt);
+  void* Q = at<void>(ws, W.q);
+  void* ATT = at<void>(ws, W.att);
+  void* QC = at<void>(ws, W.qc);
+  void* HF = at<void>(ws, W.hf);
+  float* LG = logits ? logits : at<float>(ws, W.logits);
+  float* CR = at<float>(ws, W.cross);
+  WH_TRY(launch_embed(t, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
+                      d->n_text_ctx, cap, X, dev_error, s));
+  const size_t kv_layer = (size_t)2 * B * H * cap * 64;
+  const size_t ckv_layer = (size_t)2 * B * H * T * 64 * e;
+  for (int l = 0; l < L; ++l) {
+    const DecL& Lw = P.dec[l];
+    if (l == 0)
+      WH_TRY(launch_layernorm(t, true, X, nullptr, at<float>(packed, Lw.ln1g), at<float>(packed, Lw.ln1b), 1e-5f, B, D, A, nullptr, s));
+    else
+      WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln1g), at<float>(packed, Lw.ln1b), 1e-5f, B, D, A, X, s));
+    GemmParams pq = gp(A, D, at<void>(packed, Lw.wqkv), D, B, 3 * D, D, at<float>(packed, Lw.bqkv), Q, D);
+    pq.kv_cache = kv_cache; pq.kv_scales = kv_scales; pq.lengths = lengths; pq.dev_error = dev_error;
+    pq.kv_cap = cap; pq.kv_B = B; pq.kv_H = H; pq.kv_layer = l; pq.d_model = D;
+    WH_TRY(launch_gemm_skinny(t, EPI_DEC_QKV, pq, s));
+    const uint8_t* kc = kv_cache + l * kv_layer;
+    WH_TRY(launch_attn_decode_self(t, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap, ATT, s));
+    WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(ATT, D, at<void>(packed, Lw.wo), D, B, D, D, at<float>(packed, Lw.bo), Dl, D), s));
+    WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln2g), at<float>(packed, Lw.ln2b), 1e-5f, B, D, A, X, s));
+    WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(A, D, at<void>(packed, Lw.wqc), D, B, D, D, at<float>(packed, Lw.bqc), QC, D), s));
+    const char* ck = (const char*)cross_kv + l * ckv_layer;
+    WH_TRY(launch_attn_decode_cross(t, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, CR, s));
+    WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(ATT, D, at<void>(packed, Lw.woc), D, B, D, D, at<float>(packed, Lw.boc), Dl, D), s));
+    WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln3g), at<float>(packed, Lw.ln3b), 1e-5f, B, D, A, X, s));
+    WH_TRY(launch_gemm_skinny(t, EPI_GELU, gp(A, D, at<void>(packed, Lw.w1), D, B, F, D, at<float>(packed, Lw.b1), HF, F), s));
+    WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(HF, F, at<void>(packed, Lw.w2), F, B, D, F, at<float>(packed, Lw.b2), Dl, D), s));
+  }
+  WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, P.lnfg), at<float>(packed, P.lnfb), 1e-5f, B, D, A, nullptr, s));
+  WH_TRY(launch_gemm_skinny(t, EPI_F32, gp(A, D, at<void>(packed, P.tok), D, B, d->n_vocab, D, nullptr, LG, d->n_vocab), s));
+  WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
+  return WHISPER_OK;
+}
+
+size_t whisper_fp8_workspace_size(void) { return 1024 * sizeof(float); }
+
+whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, const float* scale_in, uint8_t* codes,
+                                    float* scale_out, void* ws, size_t ws_bytes, void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "fp8_quantize: dtype must be F32 or BF16");
+  if (n == 0) return fail(WHISPER_ERR_INVALID_ARG, "fp8_quantize: n must be > 0");
+  WH_CHECK(check_ptrs({x, codes}, "fp8_quantize"));
+  if (!scale_in && !scale_out) return fail(WHISPER_ERR_INVALID_ARG, "fp8_quantize: need scale_in or scale_out");
+  if (scale_in && ((uintptr_t)scale_in & 3u)) return fail(WHISPER_ERR_ALIGN, "fp8_quantize: scale_in not 4-byte aligned");
+  if (scale_out && ((uintptr_t)scale_out & 3u)) return fail(WHISPER_ERR_ALIGN, "fp8_quantize: scale_out not 4-byte aligned");
+  if (!scale_in) WH_CHECK(check_ws(ws, ws_bytes, whisper_fp8_workspace_size(), "fp8_quantize"));
+  (void)hipGetLastError();
+  const hipStream_t s = S(stream);
+  const float* sc = scale_in;
+  if (!scale_in) {
+    size_t blocks = (n + 255) / 256;
+    const int np = (int)(blocks > 1024 ? 1024 : blocks);
+    WH_TRY(launch_amax(act_of(dt), x, n, (float*)ws, np, scale_out, s));
+    sc = scale_out;
+  } else if (scale_out) {
+    WH_TRY(launch_copy_f32(scale_in, scale_out, 1, s));
+  }
+  WH_TRY(launch_fp8_quantize(act_of(dt), x, n, sc, codes, s));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_fp8_dequantize(const uint8_t* codes, size_t n, const float* scale, void* y, whisper_dtype dt,
+                                      void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "fp8_dequantize: dtype must be F32 or BF16");
+  if (n == 0) return fail(WHISPER_ERR_INVALID_ARG, "fp8_dequantize: n must be > 0");
+  WH_CHECK(check_ptrs({codes, y}, "fp8_dequantize"));
+  WH_CHECK(check_ptrs4({scale}, "fp8_dequantize"));
+  (void)hipGetLastError();
+  WH_TRY(launch_fp8_dequantize(act_of(dt), codes, n, scale, y, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_layernorm_fused(const whisper_dims* d, const void* h, const float* res, const float* gamma,
+                                       const float* beta, float eps, int M, void* normed, float* total, void* stream) {
+  if (!d) return fail(WHISPER_ERR_INVALID_ARG, "layernorm: dims is NULL");
+  if (d->act != WHISPER_F32 && d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "layernorm: bad dtype");
+  if (d->d_model <= 0 || d->d_model % 4 || d->d_model > 2048) return fail(WHISPER_ERR_SHAPE, "layernorm: d_model must be a multiple of 4 in 4..2048");
+  if (M <= 0) return fail(WHISPER_ERR_INVALID_ARG, "layernorm: M must be > 0");
+  if (!(eps > 0.f)) return fail(WHISPER_ERR_INVALID_ARG, "layernorm: eps must be > 0");
+  WH_CHECK(check_ptrs({h, gamma, beta}, "layernorm"));
+  if (!normed && !total) return fail(WHISPER_ERR_INVALID_ARG, "layernorm: normed and total are both NULL");
+  for (const void* p : {(const void*)res, (const void*)normed, (const void*)total})
+    if (p && !aligned16(p)) return fail(WHISPER_ERR_ALIGN, "layernorm: pointer not 16-byte aligned");
+  (void)hipGetLastError();
+  WH_TRY(launch_layernorm(act_of(d->act), false, h, res, gamma, beta, eps, M, d->d_model, normed, total, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const void* w, const float* bias, int M, int N,
+                              int K, int act, void* y, int path, void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "linear: bad dtype");
+  if (M <= 0 || N <= 0 || K <= 0 || lda <= 0) return fail(WHISPER_ERR_INVALID_ARG, "linear: sizes must be > 0");
+  if (act != 0 && act != 1) return fail(WHISPER_ERR_INVALID_ARG, "linear: act must be 0 or 1");
+  if (path < 0 || path > 2) return fail(WHISPER_ERR_INVALID_ARG, "linear: path must be 0, 1 or 2");
+  WH_CHECK(check_ptrs({x, w, y}, "linear"));
+  if (bias && !aligned16(bias)) return fail(WHISPER_ERR_ALIGN, "linear: bias not 16-byte aligned");
+  if (dt == WHISPER_BF16 && (K % 64 || lda % 8)) return fail(WHISPER_ERR_SHAPE, "linear: bf16 needs K % 64 == 0 and lda % 8 == 0");
+  if (path == 2 && (dt != WHISPER_BF16 || M > 128 || K % 128)) return fail(WHISPER_ERR_SHAPE, "linear: skinny path needs bf16, M <= 128, K % 128 == 0");
+  (void)hipGetLastError();
+  GemmParams p = gp(x, lda, w, K, M, N, K, bias, y, N);
+  const Epi epi = act ? EPI_GELU : EPI_STORE;
+  const bool skinny = path == 2 || (path == 0 && dt == WHISPER_BF16 && M <= 128 && K % 128 == 0);
+  WH_TRY(skinny ? launch_gemm_skinny(act_of(dt), epi, p, S(stream)) : launch_gemm(act_of(dt), epi, p, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_attention_encoder(whisper_dtype dt, const void* qkv, int B, int T, int H, void* out,
+                                         void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "attention_encoder: bad dtype");
+  if (B <= 0 || T <= 0 || H <= 0) return fail(WHISPER_ERR_INVALID_ARG, "attention_encoder: sizes must be > 0");
+  WH_CHECK(check_ptrs({qkv, out}, "attention_encoder"));
+  (void)hipGetLastError();
+  WH_TRY(launch_attn_encoder(act_of(dt), qkv, B, T, H, out, S(stream)));
+  return WHISPER_OK;
+}
+
+whisper_status whisper_attention_decode_self(whisper_dtype dt, const void* q, int B, int H, int cap,
+                                             const uint8_t* k_codes, const uint8_t* v_codes, const float* scales,
+                                             const int32_t* n_keys, void* out, void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "attention_decode_self: bad dtype");
+  if (B <= 0 || H <= 0) return fail(WHISPER_ERR_INVALID_ARG, "attention_decode_self: sizes must be > 0");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "attention_decode_self: cap must be in 1..4096");
+  WH_CHECK(check_ptrs({q, k_codes, v_codes, out}, "attention_decode_self"));
+  WH_CHECK(check_ptrs4({scales, n_keys}, "attention_decode_self"));
+  (void)hipGetLastError();
+  WH_TRY(launch_attn_decode_self(act_of(dt), q, (long)H * 64, k_codes, v_codes, scales, n_keys, 0, B, H, cap, out,
+                                 S(stream)));
+  return WHISPER_OK;
+}
+
+size_t whisper_attention_decode_cross_workspace_size(int B, int H, int T) {
+  if (B <= 0 || H <= 0 || T <= 0) return 0;
+  return attn_decode_cross_ws(B, H, T);
+}
+
+whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, const void* k, const void* v, int B,
+                                              int H, int T, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "attention_decode_cross: bad dtype");
+  if (B <= 0 || H <= 0 || T <= 0) return fail(WHISPER_ERR_INVALID_ARG, "attention_decode_cross: sizes must be > 0");
+  if (T > 4096) return fail(WHISPER_ERR_SHAPE, "attention_decode_cross: T must be <= 4096");
+  WH_CHECK(check_ptrs({q, k, v, out}, "attention_decode_cross"));
+  WH_CHECK(check_ws(ws, ws_bytes, attn_decode_cross_ws(B, H, T), "attention_decode_cross"));
+  (void)hipGetLastError();
+  WH_TRY(launch_attn_decode_cross(act_of(dt), q, k, v, B, H, T, out, (float*)ws, S(stream)));
+  return WHISPER_OK;
+}
+
+}  // extern "C"

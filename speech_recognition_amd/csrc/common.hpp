@@ -1,0 +1,88 @@
+// Device helpers shared by the gfx950 kernels of the Whisper hot path:
+// bf16 / OCP-e4m3 conversions done on bits, MFMA operand vector types and
+// wave64 reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wh {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16;
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------------ bf16 storage
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ u16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+// Storage type traits: activations are bf16 (u16 bits) or fp32.
+template <typename T> struct Act;
+template <> struct Act<u16> {
+  static __device__ __forceinline__ float ld(const u16* p) { return bf2f(*p); }
+  static __device__ __forceinline__ float cvt(u16 v) { return bf2f(v); }
+  static __device__ __forceinline__ u16 st(float v) { return f2bf(v); }
+  static __device__ __forceinline__ float round(float v) { return bf2f(f2bf(v)); }
+};
+template <> struct Act<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ float cvt(float v) { return v; }
+  static __device__ __forceinline__ float st(float v) { return v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+
+// ------------------------------------------------------------------ OCP E4M3FN
+// 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; no infinities; S.1111.111
+// is NaN; largest finite magnitude 448. Encoding rounds to nearest even and
+// saturates magnitudes >= 448 to +-448; the sign bit is always kept.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;         // |y| >= 448: saturate
+  if (a < 0x3c800000u) {                             // |y| < 2^-6: subnormal, step 2^-9
+    const float s = __uint_as_float(a) * 512.0f;     // exact scaling by a power of two
+    return sign | (uint32_t)__builtin_rintf(s);      // 0..8 (8 is the smallest normal)
+  }
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // round 23 -> 3 mantissa bits, ties to even
+  uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  if ((c & 0x7fu) == 0x7fu) v = __uint_as_float(0x7fc00000u);
+  return (c & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) { return __builtin_bit_cast(To, f); }
+
+}  // namespace wh

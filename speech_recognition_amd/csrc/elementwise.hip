@@ -1,0 +1,356 @@
+// Memory-bound kernels of the hot path: fused residual + LayerNorm (the
+// whisper_blaze showcase page's layernorm_fused.cu card: residual add and
+// LayerNorm in one pass; the project page's "Direct Kernel API" returns both
+// the normalised value and the pre-norm sum), the e4m3 codec with a
+// per-tensor scale (fp8_quantize.cu card; project page quantise_e4m3 /
+// dequantise_e4m3), weight packing, decoder embeddings and the greedy argmax.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace wh {
+
+// ------------------------------------------------------------------ vector IO
+template <typename T> struct Vec4;
+template <> struct Vec4<u16> {
+  static __device__ __forceinline__ void ld(const u16* p, float v[4]) {
+    const uint2 u = *(const uint2*)p;
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void st(u16* p, const float v[4]) {
+    uint2 u;
+    u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *(uint2*)p = u;
+  }
+};
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void ld(const float* p, float v[4]) {
+    const float4 u = *(const float4*)p; v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  static __device__ __forceinline__ void st(float* p, const float v[4]) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// ------------------------------------------------------------------ residual + LayerNorm
+// One wave64 per row; each lane holds up to 8 groups of 4 elements (d <= 2048)
+// in registers, so the row is read once and written once. The residual
+// stream is fp32: total = fl32(h + residual) (h alone if there is no
+// residual); statistics in fp32 over total (two passes over registers: mean,
+// then mean squared deviation); normed is stored in the activation type.
+template <typename TH, typename T>
+__global__ __launch_bounds__(256) void layernorm_kernel(const TH* h, const float* res, const float* g,
+                                                        const float* b, float eps, int M, int d, T* normed,
+                                                        float* total) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const int nc = d >> 2;
+  const long off = (long)row * d;
+  float v[8][4];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = lane + i * 64;
+    if (c < nc) {
+      Vec4<TH>::ld(h + off + c * 4, v[i]);
+      if (res) {
+        const float4 r = *(const float4*)(res + off + c * 4);
+        v[i][0] += r.x; v[i][1] += r.y; v[i][2] += r.z; v[i][3] += r.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sum += v[i][k];
+    }
+  }
+  const float mean = wave_sum(sum) / (float)d;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (lane + i * 64 < nc)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { const float t = v[i][k] - mean; sq += t * t; }
+  const float var = wave_sum(sq) / (float)d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = lane + i * 64;
+    if (c < nc) {
+      if (total) *(float4*)(total + off + c * 4) = make_float4(v[i][0], v[i][1], v[i][2], v[i][3]);
+      if (normed) {
+        const float4 gg = *(const float4*)(g + c * 4), bb = *(const float4*)(b + c * 4);
+        float o[4] = {(v[i][0] - mean) * rstd * gg.x + bb.x, (v[i][1] - mean) * rstd * gg.y + bb.y,
+                      (v[i][2] - mean) * rstd * gg.z + bb.z, (v[i][3] - mean) * rstd * gg.w + bb.w};
+        Vec4<T>::st(normed + off + c * 4, o);
+      }
+    }
+  }
+}
+
+hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* res, const float* g, const float* b,
+                            float eps, int M, int d, void* normed, float* total, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  dim3 grid((M + 3) / 4);
+  if (t == ACT_BF16 && !h_f32)
+    hipLaunchKernelGGL((layernorm_kernel<u16, u16>), grid, dim3(256), 0, s, (const u16*)h, res, g, b, eps, M, d,
+                       (u16*)normed, total);
+  else if (t == ACT_BF16)
+    hipLaunchKernelGGL((layernorm_kernel<float, u16>), grid, dim3(256), 0, s, (const float*)h, res, g, b, eps, M, d,
+                       (u16*)normed, total);
+  else
+    hipLaunchKernelGGL((layernorm_kernel<float, float>), grid, dim3(256), 0, s, (const float*)h, res, g, b, eps, M,
+                       d, (float*)normed, total);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ e4m3 codec
+template <typename T>
+__global__ __launch_bounds__(256) void amax_partial(const T* x, size_t n, float* partial) {
+  float m = 0.f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(Act<T>::cvt(x[i])));
+  m = wave_max(m);
+  __shared__ float sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+__global__ __launch_bounds__(64) void amax_final(const float* partial, int n, float* scale_out) {
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 64) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  if (threadIdx.x == 0) scale_out[0] = (m > 0.f) ? m / 448.0f : 1.0f;
+}
+
+hipError_t launch_amax(ActType t, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
+                       hipStream_t s) {
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(amax_partial<u16>, dim3(n_partial), dim3(256), 0, s, (const u16*)x, n, partial);
+  else
+    hipLaunchKernelGGL(amax_partial<float>, dim3(n_partial), dim3(256), 0, s, (const float*)x, n, partial);
+  hipLaunchKernelGGL(amax_final, dim3(1), dim3(64), 0, s, partial, n_partial, scale_out);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* x, size_t n, const float* scale, uint8_t* codes) {
+  const float inv = 1.0f / scale[0];
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    codes[i] = (uint8_t)e4m3_encode(Act<T>::cvt(x[i]) * inv);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_dequantize_kernel(const uint8_t* codes, size_t n, const float* scale, T* y) {
+  const float s = scale[0];
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    y[i] = Act<T>::st(e4m3_decode(codes[i]) * s);
+}
+
+static int grid_for(size_t n) {
+  size_t g = (n + 255) / 256;
+  return (int)(g > 8192 ? 8192 : (g < 1 ? 1 : g));
+}
+
+hipError_t launch_fp8_quantize(ActType t, const void* x, size_t n, const float* scale, uint8_t* codes,
+                               hipStream_t s) {
+  if (!n) return hipSuccess;
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(fp8_quantize_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, (const u16*)x, n, scale, codes);
+  else
+    hipLaunchKernelGGL(fp8_quantize_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, (const float*)x, n, scale,
+                       codes);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dequantize(ActType t, const uint8_t* codes, size_t n, const float* scale, void* y,
+                                 hipStream_t s) {
+  if (!n) return hipSuccess;
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(fp8_dequantize_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale, (u16*)y);
+  else
+    hipLaunchKernelGGL(fp8_dequantize_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale, (float*)y);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ packing / layout
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const float* src, T* dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    dst[i] = Act<T>::st(src[i]);
+}
+
+hipError_t launch_convert(ActType t, const float* src, void* dst, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  if (t == ACT_BF16) hipLaunchKernelGGL(convert_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, src, (u16*)dst, n);
+  else hipLaunchKernelGGL(convert_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, src, (float*)dst, n);
+  return hipGetLastError();
+}
+
+// conv weight [c_out][c_in][k] -> implicit-GEMM layout [c_out][k * c_in] (tap-major)
+template <typename T>
+__global__ __launch_bounds__(256) void pack_conv_kernel(const float* w, int c_out, int c_in, int k, T* dst) {
+  const size_t n = (size_t)c_out * c_in * k;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int o = (int)(i / ((size_t)c_in * k));
+    const int r = (int)(i - (size_t)o * c_in * k);
+    const int j = r / c_in, ci = r - j * c_in;
+    dst[i] = Act<T>::st(w[((size_t)o * c_in + ci) * k + j]);
+  }
+}
+
+hipError_t launch_pack_conv(ActType t, const float* w, int c_out, int c_in, int k, void* dst, hipStream_t s) {
+  const size_t n = (size_t)c_out * c_in * k;
+  if (t == ACT_BF16) hipLaunchKernelGGL(pack_conv_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, w, c_out, c_in, k, (u16*)dst);
+  else hipLaunchKernelGGL(pack_conv_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, w, c_out, c_in, k, (float*)dst);
+  return hipGetLastError();
+}
+
+// Fixed encoder positions: channel c < C/2 holds sin(t * 10000^(-c/(C/2-1))),
+// channel C/2 + c the matching cosine; evaluated in double.
+__global__ __launch_bounds__(256) void sinusoids_kernel(float* pe, int T, int C) {
+  const int half = C / 2;
+  const double inc = log(10000.0) / (double)(half - 1);
+  const size_t n = (size_t)T * C;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int t = (int)(i / C), c = (int)(i - (size_t)t * C);
+    const int cc = c < half ? c : c - half;
+    const double a = (double)t * exp(-inc * (double)cc);
+    pe[i] = (float)(c < half ? sin(a) : cos(a));
+  }
+}
+
+hipError_t launch_sinusoids(float* pe, int T, int C, hipStream_t s) {
+  hipLaunchKernelGGL(sinusoids_kernel, dim3(grid_for((size_t)T * C)), dim3(256), 0, s, pe, T, C);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* dst, float v, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = v;
+}
+hipError_t launch_fill_f32(float* dst, float v, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, dst, v, n);
+  return hipGetLastError();
+}
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* src, float* dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = src[i];
+}
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s) {
+  if (!n) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(grid_for(n)), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+// mel [B][n_mels][F] fp32 -> conv1 input [B][F+2][n_mels] (time-major, rows 1..F),
+// through a 32x32 LDS tile so both sides stay coalesced.
+template <typename T>
+__global__ __launch_bounds__(256) void mel_to_conv_kernel(const float* mel, int n_mels, int F, T* x0) {
+  __shared__ float tile[32][33];
+  const int b = blockIdx.z, t0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const float* src = mel + (size_t)b * n_mels * F;
+  for (int r = ty; r < 32; r += 8) {
+    const int m = m0 + r, t = t0 + tx;
+    tile[r][tx] = (m < n_mels && t < F) ? src[(size_t)m * F + t] : 0.f;
+  }
+  __syncthreads();
+  T* dst = x0 + (size_t)b * (F + 2) * n_mels;
+  for (int r = ty; r < 32; r += 8) {
+    const int t = t0 + r, m = m0 + tx;
+    if (t < F && m < n_mels) dst[(size_t)(t + 1) * n_mels + m] = Act<T>::st(tile[tx][r]);
+  }
+}
+
+hipError_t launch_mel_to_conv_input(ActType t, const float* mel, int B, int n_mels, int n_frames, void* x0,
+                                    hipStream_t s) {
+  dim3 grid((n_frames + 31) / 32, (n_mels + 31) / 32, B);
+  if (t == ACT_BF16) hipLaunchKernelGGL(mel_to_conv_kernel<u16>, grid, dim3(256), 0, s, mel, n_mels, n_frames, (u16*)x0);
+  else hipLaunchKernelGGL(mel_to_conv_kernel<float>, grid, dim3(256), 0, s, mel, n_mels, n_frames, (float*)x0);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return launch_zero_rows(t, x0, n_mels, n_frames + 2, B, 0, n_frames + 1, s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void zero_rows_kernel(T* base, long row_elems, long rows_per_batch, int row_a,
+                                                        int row_b) {
+  const int b = blockIdx.y;
+  T* p0 = base + ((long)b * rows_per_batch + row_a) * row_elems;
+  T* p1 = base + ((long)b * rows_per_batch + row_b) * row_elems;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < row_elems; i += (long)gridDim.x * 256) {
+    p0[i] = T(0);
+    p1[i] = T(0);
+  }
+}
+
+hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per_batch, int B, int row_a, int row_b,
+                            hipStream_t s) {
+  dim3 grid((unsigned)((row_elems + 255) / 256), B);
+  if (t == ACT_BF16) hipLaunchKernelGGL(zero_rows_kernel<u16>, grid, dim3(256), 0, s, (u16*)base, row_elems, rows_per_batch, row_a, row_b);
+  else hipLaunchKernelGGL(zero_rows_kernel<float>, grid, dim3(256), 0, s, (float*)base, row_elems, rows_per_batch, row_a, row_b);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decoder embedding / argmax
+// x[b] = tok_emb[tokens[b]] + pos_emb[lengths[b]] into the fp32 residual stream.
+// Out-of-range token ids or positions write zeros and raise the device error.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* pos_emb, const int32_t* tokens,
+                                                    const int32_t* lengths, int d, int n_vocab, int n_ctx, int cap,
+                                                    float* x, int32_t* dev_error) {
+  const int b = blockIdx.x;
+  const int tok = tokens[b], pos = lengths[b];
+  const bool ok = tok >= 0 && tok < n_vocab && pos >= 0 && pos < n_ctx && pos < cap;
+  if (!ok && dev_error && threadIdx.x == 0) *dev_error = (pos >= cap) ? 6 : 1;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = 0.f;
+    if (ok) v = Act<T>::cvt(tok_emb[(size_t)tok * d + c]) + Act<T>::cvt(pos_emb[(size_t)pos * d + c]);
+    x[(size_t)b * d + c] = v;
+  }
+}
+
+hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
+                        int32_t* dev_error, hipStream_t s) {
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(embed_kernel<u16>, dim3(B), dim3(256), 0, s, (const u16*)tok_emb, (const u16*)pos_emb, tokens,
+                       lengths, d, n_vocab, n_ctx, cap, x, dev_error);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(B), dim3(256), 0, s, (const float*)tok_emb, (const float*)pos_emb,
+                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error);
+  return hipGetLastError();
+}
+
+// Greedy token per row: largest logit, lowest index on ties; then lengths[b] += 1.
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V, int32_t* out, int32_t* lengths) {
+  const int b = blockIdx.x;
+  const float* row = logits + (size_t)b * V;
+  float best = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float v = row[i];
+    if (v > best) { best = v; idx = i; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = idx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (sv[w] > best || (sv[w] == best && si[w] < idx)) { best = sv[w]; idx = si[w]; }
+    out[b] = idx == 0x7fffffff ? 0 : idx;
+    if (lengths) lengths[b] += 1;
+  }
+}
+
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(256), 0, s, logits, V, argmax, lengths);
+  return hipGetLastError();
+}
+
+}  // namespace wh

@@ -1,0 +1,89 @@
+// Launch-level interface between the C-ABI host layer (api.cpp) and the
+// kernel translation units. Everything here enqueues on a stream and returns
+// the launch status; argument checks happen in api.cpp before any launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wh {
+
+enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+
+// ------------------------------------------------------------------ GEMM
+// C = epilogue(A[M,K] . B[N,K]^T + bias); A rows may overlap (lda < K) for
+// the implicit-GEMM convolutions. Batched over blockIdx.z with element strides.
+enum Epi {
+  EPI_STORE = 0,    // C = acc + bias (act type)
+  EPI_GELU = 1,     // C = gelu(acc + bias)
+  EPI_GELU_PE = 2,  // C (fp32 residual stream) = gelu(acc + bias) + pe[row, col]
+  EPI_F32 = 3,      // C (fp32) = acc + bias
+  EPI_CROSSKV = 4,  // scatter acc + bias head-major into [L][2][B][H][T][64]
+  EPI_DEC_QKV = 5,  // q -> q_out; k, v -> e4m3 codes at cache slot lengths[row]
+};
+
+struct GemmParams {
+  const void* A; long lda; long strideA;
+  const void* B; long ldb;
+  int M, N, K, batch;
+  const float* bias;
+  void* C; long ldc; long strideC;
+  const float* pe;
+  // EPI_CROSSKV
+  int ckv_T, ckv_B, ckv_H, ckv_d;
+  // EPI_DEC_QKV
+  uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
+  int kv_cap, kv_B, kv_H, kv_layer, d_model;
+};
+
+hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
+// Skinny path for decode (M <= 128): weights streamed once, K split over waves.
+hipError_t launch_gemm_skinny(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ LayerNorm
+// h is in the activation type (or fp32 when h_f32); residual and total are the
+// fp32 residual stream; normed is in the activation type.
+hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* res, const float* g, const float* b,
+                            float eps, int M, int d, void* normed, float* total, hipStream_t s);
+
+// ------------------------------------------------------------------ fp8 codec
+hipError_t launch_amax(ActType t, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
+                       hipStream_t s);
+hipError_t launch_fp8_quantize(ActType t, const void* x, size_t n, const float* scale, uint8_t* codes,
+                               hipStream_t s);
+hipError_t launch_fp8_dequantize(ActType t, const uint8_t* codes, size_t n, const float* scale, void* y,
+                                 hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+// Encoder self-attention over the packed QKV [B*T, 3*H*64] -> out [B*T, H*64].
+hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, void* out, hipStream_t s);
+// Decode causal self-attention over e4m3 codes [B][H][cap][64]; n_keys[b] = lengths[b] + add.
+hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
+                                   const uint8_t* v_codes, const float* scales, const int32_t* lengths,
+                                   int len_add, int B, int H, int cap, void* out, hipStream_t s);
+// Decode cross-attention over head-major K/V [B][H][T][64]; split over T.
+size_t attn_decode_cross_ws(int B, int H, int T);
+hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
+                                    void* out, float* ws, hipStream_t s);
+
+// ------------------------------------------------------------------ log-mel
+size_t logmel_ws(int B, int n_mels);
+hipError_t launch_logmel(const float* audio, int B, int n_samples, int n_mels, float* mel_out, void* ws,
+                         hipStream_t s);
+
+// ------------------------------------------------------------------ misc
+hipError_t launch_mel_to_conv_input(ActType t, const float* mel, int B, int n_mels, int n_frames, void* x0,
+                                    hipStream_t s);
+hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per_batch, int B, int row_a,
+                            int row_b, hipStream_t s);
+hipError_t launch_convert(ActType t, const float* src, void* dst, size_t n, hipStream_t s);
+hipError_t launch_pack_conv(ActType t, const float* w, int c_out, int c_in, int k, void* dst, hipStream_t s);
+hipError_t launch_sinusoids(float* pe, int T, int C, hipStream_t s);
+hipError_t launch_fill_f32(float* dst, float v, size_t n, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
+hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
+                        int32_t* dev_error, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s);
+
+}  // namespace wh

@@ -1,0 +1,99 @@
+"""Device-buffer plumbing around the C ABI.
+
+torch provides device memory and the stream; every step of the hot path runs
+in the library's HIP kernels through the ctypes binding. The helpers here
+only size and allocate buffers and pass pointers.
+"""
+import torch
+
+from . import _lib as L
+
+__all__ = ["Whisper", "DecodeState", "act_dtype"]
+
+
+def act_dtype(dims):
+    return torch.bfloat16 if dims.act == "bf16" else torch.float32
+
+
+def _empty_bytes(n, device):
+    return torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+
+
+class Whisper:
+    """Packed weights plus per-call workspaces for one model shape."""
+
+    def __init__(self, dims, logical_weights, device="cuda"):
+        """logical_weights: fp32 device tensors in the ABI's canonical order."""
+        self.dims = dims
+        self.device = torch.device(device)
+        n = L.whisper_weight_count(dims)
+        if n != len(logical_weights):
+            raise ValueError(f"expected {n} weight tensors, got {len(logical_weights)}")
+        for t in logical_weights:
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device.type != "cuda":
+                raise ValueError("logical weights must be contiguous fp32 device tensors")
+        self.packed = _empty_bytes(L.whisper_packed_weights_size(dims), self.device)
+        L.whisper_pack_weights(dims, logical_weights, self.packed)
+        self._ws = {}
+
+    def workspace(self, batch, which):
+        nbytes = L.whisper_workspace_size(self.dims, batch, which)
+        key = which
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = _empty_bytes(nbytes, self.device)
+            self._ws[key] = ws
+        return ws, nbytes
+
+    # ---------------------------------------------------------------- stages
+    def logmel(self, audio, out=None):
+        B, n = audio.shape
+        mel = out if out is not None else torch.empty(B, self.dims.n_mels, 3000, dtype=torch.float32,
+                                                      device=self.device)
+        ws, nb = self.workspace(B, L.WS_LOGMEL)
+        L.whisper_logmel(self.dims, audio, B, n, mel, ws, nb)
+        return mel
+
+    def encode(self, mel, out=None):
+        B = mel.shape[0]
+        enc = out if out is not None else torch.empty(B, self.dims.n_audio_ctx, self.dims.d_model,
+                                                      dtype=act_dtype(self.dims), device=self.device)
+        ws, nb = self.workspace(B, L.WS_ENCODE)
+        L.whisper_encode(self.dims, self.packed, mel, B, enc, ws, nb)
+        return enc
+
+    def encode_layers(self, h, layer_begin, layer_end, ln_post=False, out=None):
+        B = h.shape[0]
+        o = out if out is not None else torch.empty_like(h)
+        ws, nb = self.workspace(B, L.WS_ENCODE)
+        L.whisper_encode_layers(self.dims, self.packed, h, B, layer_begin, layer_end, ln_post, o, ws, nb)
+        return o
+
+    def cross_kv(self, enc, out=None):
+        B = enc.shape[0]
+        d = self.dims
+        ckv = out if out is not None else torch.empty(d.n_dec_layers, 2, B, d.n_heads, d.n_audio_ctx, 64,
+                                                      dtype=act_dtype(d), device=self.device)
+        L.whisper_cross_kv(d, self.packed, enc, B, ckv)
+        return ckv
+
+    def decode_step(self, state, tokens, logits=None):
+        B = state.batch
+        ws, nb = self.workspace(B, L.WS_DECODE)
+        L.whisper_decode_step(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
+                              state.kv_scales, state.cross_kv, logits, state.argmax, state.dev_error, ws, nb)
+        return state.argmax
+
+
+class DecodeState:
+    """Caller-owned decode state: fp8 self-KV cache, scales, lengths, cross K/V."""
+
+    def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda"):
+        self.batch, self.cap = batch, cap
+        self.kv_cache = torch.zeros(dims.n_dec_layers, 2, batch, dims.n_heads, cap, 64, dtype=torch.uint8,
+                                    device=device)
+        self.kv_scales = kv_scales.to(device=device, dtype=torch.float32).contiguous()
+        self.lengths = lengths.to(device=device, dtype=torch.int32).contiguous().clone()
+        self.cross_kv = cross_kv
+        self.argmax = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.dev_error = torch.zeros(4, dtype=torch.int32, device=device)

@@ -1,0 +1,214 @@
+"""GPU parity of the individual kernels against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import whisper_oracle as O
+from speech_recognition_amd import _lib as L
+from tests.gpu_util import TOL, bf16_bits, host, need_gpu, rel_err, say
+from workload import CONFIGS, gen_normal
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+# ------------------------------------------------------------------ fp8 codec
+def test_fp8_quantize_all_bf16_patterns_bit_exact():
+    say("fp8 quantize: all 65536 bf16 bit patterns, scale 1")
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    x = bits.view(torch.bfloat16).to(DEV)
+    scale = torch.ones(4, dtype=torch.float32, device=DEV)
+    codes = torch.empty(65536, dtype=torch.uint8, device=DEV)
+    L.whisper_fp8_quantize(x, L.WHISPER_BF16, 65536, scale, codes, None)
+    torch.cuda.synchronize()
+    ref = O.e4m3_quantize(x.float().cpu().numpy(), 1.0)
+    assert np.array_equal(codes.cpu().numpy(), ref)
+
+
+def test_fp8_quantize_fp32_scaled_bit_exact_and_amax_scale():
+    say("fp8 quantize: 1M fp32 values, device amax scale")
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(1 << 20, generator=g) * 3.7).to(DEV)
+    codes = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    scale = torch.zeros(4, dtype=torch.float32, device=DEV)
+    ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=DEV)
+    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), None, codes, scale, ws, ws.numel())
+    torch.cuda.synchronize()
+    xs = x.cpu().numpy()
+    s_ref = O.e4m3_scale_from_amax(xs)
+    assert scale[0].item() == float(s_ref)
+    assert np.array_equal(codes.cpu().numpy(), O.e4m3_quantize(xs, s_ref))
+    # a scale that is not a power of two and saturates part of the range
+    s2 = torch.full((4,), 0.0123, dtype=torch.float32, device=DEV)
+    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), s2, codes, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), O.e4m3_quantize(xs, np.float32(0.0123)))
+
+
+def test_fp8_dequantize_all_codes():
+    say("fp8 dequantize: all 256 codes")
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(DEV)
+    for s in (1.0, 0.0123):
+        scale = torch.full((4,), s, dtype=torch.float32, device=DEV)
+        y = torch.empty(256, dtype=torch.float32, device=DEV)
+        L.whisper_fp8_dequantize(codes, 256, scale, y, L.WHISPER_F32)
+        torch.cuda.synchronize()
+        ref = O.e4m3_dequantize(np.arange(256), np.float32(s)).astype(np.float32)
+        got = y.cpu().numpy()
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok].view(np.uint32), ref[ok].view(np.uint32))
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("act,d,M", [("bf16", 1280, 1500), ("bf16", 1280, 37), ("f32", 384, 300)])
+def test_layernorm_fused(act, d, M):
+    say(f"layernorm act={act} d={d} M={M}")
+    dims = CONFIGS["v3_layer"].with_(act=act, d_model=d, n_heads=d // 64)
+    bf = act == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    h = gen_normal(DEV, (M, d), 9, 6, 1, bf16=bf).to(dt)
+    r = gen_normal(DEV, (M, d), 9, 6, 2, std=2.0)          # fp32 residual stream
+    gam = gen_normal(DEV, (d,), 9, 6, 3, std=0.5) + 1
+    bet = gen_normal(DEV, (d,), 9, 6, 4, std=0.5)
+    normed = torch.empty_like(h)
+    total = torch.empty(M, d, dtype=torch.float32, device=DEV)
+    L.whisper_layernorm_fused(dims, h, r, gam, bet, 1e-5, M, normed, total)
+    normed0 = torch.empty_like(h)
+    total0 = torch.empty(M, d, dtype=torch.float32, device=DEV)
+    L.whisper_layernorm_fused(dims, h, None, gam, bet, 1e-5, M, normed0, total0)
+    # in place on the residual stream, as the encoder and decoder use it
+    r2 = r.clone()
+    normed2 = torch.empty_like(h)
+    L.whisper_layernorm_fused(dims, h, r2, gam, bet, 1e-5, M, normed2, r2)
+    torch.cuda.synchronize()
+    # total is the single fp32 rounding of h + r, bit for bit
+    ref_total = (h.float().cpu() + r.cpu()).numpy()
+    assert np.array_equal(total.cpu().numpy(), ref_total)
+    assert np.array_equal(r2.cpu().numpy(), ref_total) and torch.equal(normed2, normed)
+    assert np.array_equal(total0.cpu().numpy(), h.float().cpu().numpy())
+    n_ref, _ = O.residual_layer_norm(host(h), host(r), host(gam), host(bet))
+    for i in range(0, M, max(1, M // 7)):
+        assert rel_err(host(normed)[i], n_ref[i]) < TOL
+    assert rel_err(host(normed), n_ref) < TOL
+    n0_ref = O.layer_norm(host(h), host(gam), host(bet))
+    assert rel_err(host(normed0), n0_ref) < TOL
+
+
+# ------------------------------------------------------------------ GEMM
+@pytest.mark.parametrize("act,M,N,K,gelu,path", [
+    ("bf16", 300, 200, 256, 0, 1), ("bf16", 300, 384, 1280, 1, 1), ("bf16", 129, 128, 64, 0, 1),
+    ("bf16", 64, 1280, 1280, 0, 2), ("bf16", 90, 200, 5120, 1, 2), ("bf16", 1, 51, 128, 0, 2),
+    ("f32", 77, 130, 240, 1, 1)])
+def test_linear(act, M, N, K, gelu, path):
+    say(f"linear act={act} M={M} N={N} K={K} gelu={gelu} path={path}")
+    bf = act == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    x = gen_normal(DEV, (M, K), 9, 6, 10, bf16=bf).to(dt)
+    w = gen_normal(DEV, (N, K), 9, 6, 11, std=0.05, bf16=bf).to(dt)
+    b = gen_normal(DEV, (N,), 9, 6, 12, std=0.5)
+    y = torch.empty(M, N, dtype=dt, device=DEV)
+    L.whisper_linear(L.WHISPER_BF16 if bf else L.WHISPER_F32, x, K, w, b, M, N, K, gelu, y, path)
+    torch.cuda.synchronize()
+    ref = O.linear(host(x), host(w), host(b))
+    if gelu:
+        ref = O.gelu(ref)
+    assert rel_err(host(y), ref) < TOL
+    # per-row bound too (rows are the unit that later steps see)
+    for i in (0, M // 2, M - 1):
+        assert rel_err(host(y)[i], ref[i]) < TOL
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("act,B,T,H", [("bf16", 2, 300, 3), ("bf16", 1, 1500, 2), ("f32", 1, 200, 2)])
+def test_attention_encoder(act, B, T, H):
+    say(f"attention_encoder act={act} B={B} T={T} H={H}")
+    bf = act == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    d = 64 * H
+    qkv = gen_normal(DEV, (B, T, 3 * d), 9, 6, 20, std=1.5, bf16=bf).to(dt)
+    out = torch.empty(B, T, d, dtype=dt, device=DEV)
+    L.whisper_attention_encoder(L.WHISPER_BF16 if bf else L.WHISPER_F32, qkv, B, T, H, out)
+    torch.cuda.synchronize()
+    q = host(qkv)
+    for b in range(B):
+        ref = O.attention(q[b, :, :d], q[b, :, d:2 * d], q[b, :, 2 * d:], H)
+        assert rel_err(host(out)[b], ref) < TOL
+
+
+def test_attention_decode_self_fp8():
+    B, H, cap = 5, 3, 100
+    say(f"attention_decode_self B={B} H={H} cap={cap}")
+    g = torch.Generator().manual_seed(5)
+    kc = torch.randint(0, 256, (B, H, cap, 64), generator=g, dtype=torch.int32)
+    vc = torch.randint(0, 256, (B, H, cap, 64), generator=g, dtype=torch.int32)
+    kc[(kc & 0x7F) == 0x7F] = 0x40   # no NaN codes among the keys
+    vc[(vc & 0x7F) == 0x7F] = 0x41
+    n_keys = torch.tensor([1, 17, 64, 99, 100], dtype=torch.int32)
+    # poison every slot past n_keys with NaN codes: causality means they are never read
+    for b in range(B):
+        kc[b, :, n_keys[b]:] = 0x7F
+        vc[b, :, n_keys[b]:] = 0xFF
+    kc, vc = kc.to(torch.uint8), vc.to(torch.uint8)
+    q = gen_normal(DEV, (B, H * 64), 9, 6, 30, bf16=True).to(torch.bfloat16)
+    scales = torch.tensor([0.004, 0.01, 0, 0], dtype=torch.float32, device=DEV)
+    out = torch.empty(B, H * 64, dtype=torch.bfloat16, device=DEV)
+    L.whisper_attention_decode_self(L.WHISPER_BF16, q, B, H, cap, kc.to(DEV), vc.to(DEV), scales,
+                                    n_keys.to(DEV), out)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all()
+    qh = host(q)
+    for b in range(B):
+        n = int(n_keys[b])
+        for h in range(H):
+            kh = O.e4m3_dequantize(kc[b, h, :n].numpy(), np.float32(0.004))
+            vh = O.e4m3_dequantize(vc[b, h, :n].numpy(), np.float32(0.01))
+            ref = O.softmax(kh @ qh[b, h * 64:(h + 1) * 64] / 8.0) @ vh
+            assert rel_err(got[b, h * 64:(h + 1) * 64], ref) < TOL, (b, h)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_attention_decode_cross(act):
+    B, H, T = 3, 2, 1500
+    say(f"attention_decode_cross act={act} B={B} H={H} T={T}")
+    bf = act == "bf16"
+    dt = torch.bfloat16 if bf else torch.float32
+    q = gen_normal(DEV, (B, H * 64), 9, 6, 40, std=0.5, bf16=bf).to(dt)
+    k = gen_normal(DEV, (B, H, T, 64), 9, 6, 41, bf16=bf).to(dt)
+    v = gen_normal(DEV, (B, H, T, 64), 9, 6, 42, bf16=bf).to(dt)
+    out = torch.empty(B, H * 64, dtype=dt, device=DEV)
+    nws = L.whisper_attention_decode_cross_workspace_size(B, H, T)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    L.whisper_attention_decode_cross(L.WHISPER_BF16 if bf else L.WHISPER_F32, q, k, v, B, H, T, out, ws, nws)
+    torch.cuda.synchronize()
+    qh, kh, vh, got = host(q), host(k), host(v), host(out)
+    for b in range(B):
+        for h in range(H):
+            ref = O.softmax(kh[b, h] @ qh[b, h * 64:(h + 1) * 64] / 8.0) @ vh[b, h]
+            assert rel_err(got[b, h * 64:(h + 1) * 64], ref) < TOL
+
+
+# ------------------------------------------------------------------ log-mel
+@pytest.mark.parametrize("n_mels,n_samples", [(128, 480000), (80, 160000)])
+def test_logmel(n_mels, n_samples):
+    from workload import gen_audio_tones
+    say(f"logmel n_mels={n_mels} n_samples={n_samples}")
+    dims = CONFIGS["v3_encoder"] if n_mels == 128 else CONFIGS["tiny_f32"]
+    B = 2
+    audio = gen_audio_tones(DEV, 9, B, seconds=n_samples / 16000, total=n_samples)
+    mel = torch.empty(B, n_mels, 3000, dtype=torch.float32, device=DEV)
+    nws = L.whisper_workspace_size(dims, B, L.WS_LOGMEL)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    L.whisper_logmel(dims, audio, B, n_samples, mel, ws, nws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.log_mel(audio[b].cpu().numpy(), n_mels)
+        e = rel_err(host(mel)[b], ref)
+        say(f"  chunk {b}: rel err {e:.2e}")
+        assert e < 1e-3

@@ -1,0 +1,307 @@
+"""GPU parity of the composed hot path against the oracle (teacher forcing),
+through the C ABI: encoder layer, full encoder from audio, the tiny fp32
+model end to end, and the batched large-v3 decoder step over an fp8 KV cache.
+
+Batch rows and chunks are independent, so at the large shapes the oracle runs
+on a few rows/chunks only and those rows must match."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import whisper_oracle as O
+from speech_recognition_amd import _lib as L
+from speech_recognition_amd.runtime import DecodeState, Whisper, act_dtype
+from tests.gpu_util import TOL, host, need_gpu, rel_err, say
+from workload import (CONFIGS, gen_audio_tones, gen_normal, gen_prefill_kv, gen_prefill_lengths, gen_tokens,
+                      gen_weights)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def model_for(dims, ln_random=False):
+    W = gen_weights(DEV, dims, ln_random=ln_random)
+    m = Whisper(dims, list(W.values()))
+    torch.cuda.synchronize()
+    return m, W
+
+
+def host_weights(W, prefix=None):
+    return {k: v.double().cpu().numpy() for k, v in W.items() if prefix is None or k.startswith(prefix)}
+
+
+# ------------------------------------------------------------------ encoder
+@pytest.mark.parametrize("ln_post", [False, True])
+def test_encoder_layer_large_v3(ln_post):
+    dims = CONFIGS["v3_layer"]
+    say(f"encoder layer large-v3 B=1 ln_post={ln_post}")
+    m, W = model_for(dims, ln_random=True)
+    h = gen_normal(DEV, (1, 1500, 1280), dims.cfg_id, 6, bf16=True).to(torch.bfloat16)
+    out = m.encode_layers(h, 0, 1, ln_post=ln_post)
+    out2 = m.encode_layers(h, 0, 1, ln_post=ln_post)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "encoder layer is not deterministic"
+    Wh = host_weights(W)
+    ref = O.encoder_layers(host(h)[0], Wh, dims.n_heads, [0], ln_post=ln_post)
+    e = rel_err(host(out)[0], ref)
+    say(f"  rel err {e:.3e}")
+    assert e < TOL
+
+
+def _encoder_from_audio(dims, B, chunks):
+    m, W = model_for(dims)
+    audio = gen_audio_tones(DEV, dims.cfg_id, B)
+    mel = m.logmel(audio)
+    enc = m.encode(mel)
+    torch.cuda.synchronize()
+    Wh = host_weights(W, "encoder.")
+    for b in chunks:
+        mref = O.log_mel(audio[b].cpu().numpy(), dims.n_mels)
+        em = rel_err(host(mel)[b], mref)
+        ref = O.encoder(mref, Wh, dims.n_heads, dims.n_enc_layers)
+        e = rel_err(host(enc)[b], ref)
+        say(f"  chunk {b}: mel rel err {em:.2e}, encoder rel err {e:.3e}")
+        assert em < 1e-3 and e < TOL
+
+
+def test_encoder_from_audio_two_layers():
+    dims = CONFIGS["v3_encoder"].with_(n_enc_layers=2)
+    say("encoder large-v3 shape, 2 layers, B=3 from audio")
+    _encoder_from_audio(dims, 3, [0, 2])
+
+
+def test_encoder_full_large_v3_from_audio():
+    dims = CONFIGS["v3_encoder"]
+    say("full 32-layer large-v3 encoder, B=8 from audio; oracle on chunks 0 and 7")
+    _encoder_from_audio(dims, 8, [0, 7])
+
+
+# ------------------------------------------------------------------ decoder helpers
+def code_mismatch_ok(g, o, pre):
+    """End-to-end fp8 codes (teacher forced): a GPU code equal to the oracle's
+    passes; a differing one must be the e4m3 rounding of some value within
+    delta = TOL * max|y| of the oracle's pre-quantisation value y, i.e. within
+    the same tolerance the activations are held to (max over the layer's K or
+    V row). pre: [H, 64] oracle pre-quantisation values.
+    Returns (ok, n_differing)."""
+    g = np.asarray(g, np.int64)
+    o = np.asarray(o, np.int64)
+    diff = g != o
+    if not diff.any():
+        return True, 0
+    y = pre.astype(np.float64)
+    delta = TOL * np.abs(y).max()
+    vlo = O.e4m3_value(O.e4m3_encode((y - delta).astype(np.float32)))
+    vhi = O.e4m3_value(O.e4m3_encode((y + delta).astype(np.float32)))
+    vg = O.e4m3_value(g)
+    ok = (~diff) | ((vg >= vlo) & (vg <= vhi))
+    return bool(ok.all()), int(diff.sum())
+
+
+def codec_on_oracle_values_bit_exact(pre, codes_ref):
+    """The GPU codec fed the oracle's own pre-quantisation values (scale 1)
+    must reproduce the oracle's codes bit for bit."""
+    y = torch.from_numpy(np.ascontiguousarray(pre, dtype=np.float32)).to(DEV)
+    one = torch.ones(4, dtype=torch.float32, device=DEV)
+    c = torch.empty(y.numel(), dtype=torch.uint8, device=DEV)
+    L.whisper_fp8_quantize(y, L.WHISPER_F32, y.numel(), one, c, None)
+    torch.cuda.synchronize()
+    return np.array_equal(c.cpu().numpy(), np.asarray(codes_ref).reshape(-1))
+
+
+def check_logits_argmax(lg_gpu, am_gpu, lg_ref, rows, tag):
+    n_tied = 0
+    for b in rows:
+        e = rel_err(lg_gpu[b], lg_ref[b])
+        assert e < TOL, f"{tag} row {b}: logits rel err {e:.3e}"
+        top2 = np.sort(lg_ref[b])[-2:]
+        bound = 2 * np.abs(lg_gpu[b] - lg_ref[b]).max()
+        if top2[1] - top2[0] <= bound:
+            n_tied += 1
+            continue
+        assert am_gpu[b] == int(np.argmax(lg_ref[b])), f"{tag} row {b}: argmax differs"
+    return n_tied
+
+
+def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag):
+    """Teacher-forced decode on the GPU from a prefilled fp8 cache vs the oracle on `rows`."""
+    H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
+    m, W = model_for(dims, ln_random=True)
+    dt = act_dtype(dims)
+    enc = gen_normal(DEV, (B, T, d), dims.cfg_id, 5, bf16=dims.act == "bf16").to(dt)
+    ckv = m.cross_kv(enc)
+    lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max) if prefill_max else torch.zeros(
+        B, dtype=torch.int32, device=DEV)
+    scales = torch.ones(Lyr, 2, dtype=torch.float32)
+    prefill = {}
+    if prefill_max:
+        for l in range(Lyr):
+            for kv in range(2):
+                x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, H, prefill_max)
+                scales[l, kv] = float(O.e4m3_scale_from_amax(np.array([x.abs().max().item()], np.float32)))
+                prefill[(l, kv)] = x
+    state = DecodeState(dims, B, cap, ckv, scales, lengths0)
+    for (l, kv), x in prefill.items():
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+        L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), state.kv_scales[l, kv:kv + 1].contiguous().clone(),
+                               codes, None)
+        state.kv_cache[l, kv, :, :, :prefill_max, :] = codes
+    tokens = gen_tokens(DEV, dims.cfg_id, steps, B, dims.n_vocab)
+    logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
+    gpu_steps = []
+    for t in range(steps):
+        pos = state.lengths.clone()
+        m.decode_step(state, tokens[t], logits)
+        torch.cuda.synchronize()
+        gpu_steps.append((host(logits), state.argmax.cpu().numpy().copy(), pos.cpu().numpy()))
+    assert int(state.dev_error[0].item()) == 0
+    assert np.array_equal(state.lengths.cpu().numpy(), lengths0.cpu().numpy() + steps)
+    cache_gpu = state.kv_cache.cpu().numpy()
+
+    # ---- oracle on the chosen rows
+    Wh = host_weights(W, "decoder.")
+    sc = scales.numpy()
+    enc_h = {b: host(enc[b]) for b in rows}
+    cross_rows = {b: O.cross_kv(enc_h[b], Wh, H, Lyr) for b in rows}
+    cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
+    cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
+    lengths = lengths0.cpu().numpy().copy()
+    for (l, kv), x in prefill.items():
+        xh = x.cpu().numpy()
+        for b in rows:
+            cache[l][kv][b][:, :prefill_max, :] = O.e4m3_quantize(xh[b], sc[l, kv])
+            n0 = int(lengths[b])  # later slots were overwritten by the decode steps
+            assert np.array_equal(cache[l][kv][b][:, :n0], cache_gpu[l, kv, b, :, :n0]), \
+                "prefill codes differ between the GPU codec and the oracle codec"
+    tok = tokens.cpu().numpy()
+    n_flips = n_codes = n_tied = 0
+    for t in range(steps):
+        # the oracle continues from the GPU's codes for the new slot; they are
+        # checked against the oracle's own codes right after
+        forced = [[{b: cache_gpu[l, kv, b, :, int(lengths[b]), :] for b in rows} for kv in range(2)]
+                  for l in range(Lyr)]
+        lg_ref, tr = O.decode_step(Wh, H, tok[t], lengths, cache, sc, cross, rows=rows, forced_codes=forced)
+        lg_g, am_g, pos = gpu_steps[t]
+        n_tied += check_logits_argmax(lg_g, am_g, lg_ref, rows, f"{tag} step {t}")
+        for b in rows:
+            for l in range(Lyr):
+                for kv in range(2):
+                    own = tr["codes"][l, kv, b]
+                    ok, nf = code_mismatch_ok(forced[l][kv][b], own, tr["pre_quant"][l, kv, b])
+                    assert ok, f"{tag} step {t} row {b} layer {l} kv {kv}: {nf} fp8 codes differ beyond the band"
+                    assert codec_on_oracle_values_bit_exact(tr["pre_quant"][l, kv, b], own)
+                    n_flips += nf
+                    n_codes += H * 64
+        lengths = lengths + 1
+    say(f"  {tag}: code flips {n_flips}/{n_codes} ({100.0 * n_flips / max(n_codes, 1):.3f}%), "
+        f"tied argmax rows excluded {n_tied}/{steps * len(rows)}")
+    assert n_flips <= 0.25 * n_codes
+
+
+def test_decode_large_v3_shape_4_layers():
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode large-v3 shape, 4 layers, B=64, cap 672, prefill U[1,448], 3 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4")
+
+
+def test_decode_large_v3_full():
+    dims = CONFIGS["v3_decode"]
+    say("decode large-v3, 32 layers, B=64, cap 672, prefill U[1,448], 2 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0))})
+    run_decode_case(dims, 64, 672, 448, 2, rows, "v3x32")
+
+
+def test_decode_turbo_shape_batch90_empty_cache():
+    dims = CONFIGS["turbo_longform"]
+    say("decode turbo shape, 4 layers, B=90, empty cache s=1, 3 steps")
+    run_decode_case(dims, 90, 228, 0, 3, [0, 89], "turbo")
+
+
+# ------------------------------------------------------------------ tiny fp32 end to end
+def test_tiny_fp32_end_to_end():
+    dims = CONFIGS["tiny_f32"]
+    say("tiny fp32: 10 s clip -> log-mel -> 4-layer encoder -> cross K/V -> 16 decode steps")
+    m, W = model_for(dims)
+    audio = gen_audio_tones(DEV, dims.cfg_id, 1, seconds=10.0)
+    mel = m.logmel(audio)
+    enc = m.encode(mel)
+    ckv = m.cross_kv(enc)
+    steps = 16
+    state = DecodeState(dims, 1, 448, ckv, torch.ones(dims.n_dec_layers, 2), torch.zeros(1, dtype=torch.int32))
+    tokens = gen_tokens(DEV, dims.cfg_id, steps, 1, dims.n_vocab)
+    logits = torch.empty(1, dims.n_vocab, dtype=torch.float32, device=DEV)
+    gl, ga = [], []
+    for t in range(steps):
+        m.decode_step(state, tokens[t], logits)
+        torch.cuda.synchronize()
+        gl.append(host(logits))
+        ga.append(state.argmax.cpu().numpy().copy())
+    cache_gpu = state.kv_cache.cpu().numpy()
+    Wh = host_weights(W)
+    mref = O.log_mel(audio[0].cpu().numpy(), dims.n_mels)
+    assert rel_err(host(mel)[0], mref) < 1e-3
+    eref = O.encoder(mref, Wh, dims.n_heads, dims.n_enc_layers)
+    e = rel_err(host(enc)[0], eref)
+    say(f"  encoder rel err {e:.2e}")
+    assert e < TOL
+    cr = O.cross_kv(eref, Wh, dims.n_heads, dims.n_dec_layers)
+    cross = [({0: k}, {0: v}) for k, v in cr]
+    cache = [[{0: np.zeros((dims.n_heads, 448, 64), np.uint8)} for _ in range(2)] for _ in range(dims.n_dec_layers)]
+    sc = np.ones((dims.n_dec_layers, 2), np.float32)
+    tok = tokens.cpu().numpy()
+    flips = 0
+    for t in range(steps):
+        forced = [[{0: cache_gpu[l, kv, 0, :, t]} for kv in range(2)] for l in range(dims.n_dec_layers)]
+        lg, tr = O.decode_step(Wh, dims.n_heads, tok[t], np.array([t]), cache, sc, cross, forced_codes=forced)
+        check_logits_argmax(gl[t], ga[t], lg, [0], f"tiny step {t}")
+        for l in range(dims.n_dec_layers):
+            for kv in range(2):
+                own = tr["codes"][l, kv, 0]
+                ok, nf = code_mismatch_ok(cache_gpu[l, kv, 0, :, t], own, tr["pre_quant"][l, kv, 0])
+                assert ok, (t, l, kv, nf)
+                assert codec_on_oracle_values_bit_exact(tr["pre_quant"][l, kv, 0], own)
+                flips += nf
+    say(f"  tiny: code flips {flips}")
+
+
+# ------------------------------------------------------------------ decode-state semantics
+def test_decode_resume_and_capacity():
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=2)
+    say("decode resume through host copy, and capacity error, large-v3 shape 2 layers B=8")
+    B, cap = 8, 64
+    m, W = model_for(dims)
+    enc = gen_normal(DEV, (B, 1500, 1280), dims.cfg_id, 5, bf16=True).to(torch.bfloat16)
+    ckv = m.cross_kv(enc)
+    tokens = gen_tokens(DEV, dims.cfg_id, 6, B, dims.n_vocab)
+    sc = torch.full((2, 2), 0.01)
+    s1 = DecodeState(dims, B, cap, ckv, sc, torch.arange(B, dtype=torch.int32))
+    for t in range(6):
+        m.decode_step(s1, tokens[t])
+    s2 = DecodeState(dims, B, cap, ckv, sc, torch.arange(B, dtype=torch.int32))
+    for t in range(3):
+        m.decode_step(s2, tokens[t])
+    torch.cuda.synchronize()
+    saved = (s2.kv_cache.cpu(), s2.lengths.cpu())
+    s2.kv_cache.fill_(0x55)
+    s2.lengths.fill_(0)
+    s2.kv_cache.copy_(saved[0].to(DEV))
+    s2.lengths.copy_(saved[1].to(DEV))
+    for t in range(3, 6):
+        m.decode_step(s2, tokens[t])
+    torch.cuda.synchronize()
+    assert torch.equal(s1.kv_cache, s2.kv_cache) and torch.equal(s1.argmax, s2.argmax)
+    assert torch.equal(s1.lengths, s2.lengths)
+    # a row whose slot is past the cache: the device error word is set, its write skipped
+    s3 = DecodeState(dims, B, cap, ckv, sc, torch.tensor([0, 1, 2, 3, 4, 5, 6, cap], dtype=torch.int32))
+    m.decode_step(s3, tokens[0])
+    torch.cuda.synchronize()
+    assert int(s3.dev_error[0].item()) == 6
+    assert int(s3.kv_cache[:, :, 7].sum().item()) == 0

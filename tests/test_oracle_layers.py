@@ -295,3 +295,19 @@ def test_fp8_decode_position_zero_reads_its_own_value():
     x0 = W["decoder.token_embedding"][toks[0]] + W["decoder.positional_embedding"][0]
     v_hat = O.e4m3_dequantize(cache[0, 1, :, :, 0, :], scales[0, 1]).reshape(2, d)
     assert np.allclose(tr["x"], x0 + v_hat, atol=1e-12)
+
+
+def test_forced_codes_equal_to_own_codes_change_nothing():
+    W, H, L, ctx, cross, toks, scales, dh = _fp8_setup(seed=9, B=2, steps=3)
+    c1 = np.zeros((L, 2, 2, H, ctx, dh), np.uint8)
+    c2 = np.zeros_like(c1)
+    for t in range(3):
+        lg1, tr1 = O.decode_step(W, H, toks[t], np.full(2, t), c1, scales, cross)
+        forced = [[{b: tr1["codes"][l, kv, b] for b in range(2)} for kv in range(2)] for l in range(L)]
+        lg2, tr2 = O.decode_step(W, H, toks[t], np.full(2, t), c2, scales, cross, forced_codes=forced)
+        assert np.array_equal(lg1, lg2) and np.array_equal(c1, c2)
+    # a forced code different from the oracle's own is what the cache holds afterwards
+    forced = [[{b: np.full((H, dh), 0x38, np.uint8) for b in range(2)} for kv in range(2)] for l in range(L)]
+    lg3, tr3 = O.decode_step(W, H, toks[0], np.full(2, 3), c2, scales, cross, forced_codes=forced)
+    assert np.all(c2[:, :, :, :, 3, :] == 0x38)
+    assert np.array_equal(tr3["codes"][0, 0], O.e4m3_quantize(tr3["pre_quant"][0, 0] * 1.0, 1.0))
