@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of the Whisper large-v3 hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+64 chunks of 30 s of 16 kHz audio -> GPU log-mel -> 32-layer encoder ->
+cross-attention K/V of the 32 decoder layers -> 224 teacher-forced decoder
+steps at batch 64 over an fp8 e4m3 self-KV cache prefilled to seeded lengths
+U{1..448} (capacity 672). Random N(0, 0.02) weights, synthetic tones + noise;
+every input is resident in HBM before the timed region.
+
+Prints one JSON line: value = RTFx (audio seconds per wall second) of the
+whole step, plus decode tokens/s, per-stage times, the roofline of the
+dominant kernel (decoder cross-attention, HBM-bound) timed with HIP events on
+its own stream inside the timed region, and the CPU oracle timed on a bounded
+sample on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+AUDIO_S = 30.0
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--decode-steps", type=int, default=224)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-probes", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
+              "(the path shards by independent 30 s chunks with no exchange step)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from speech_recognition_amd import _lib as L
+    from speech_recognition_amd.runtime import DecodeState, Whisper
+    from workload import CONFIGS, gen_audio_tones, gen_prefill_kv, gen_prefill_lengths, gen_tokens, gen_weights
+
+    DEV = "cuda"
+    B, TD = args.batch, args.decode_steps
+    dims = CONFIGS["v3_decode"].with_(name="large_v3", n_enc_layers=32)
+    H, d, T, Ldec = dims.n_heads, dims.d_model, dims.n_audio_ctx, dims.n_dec_layers
+    cap, prefill_max = 672, 448
+
+    t0 = time.time()
+    W = gen_weights(DEV, dims)
+    model = Whisper(dims, list(W.values()))
+    torch.cuda.synchronize()
+    del W
+    torch.cuda.empty_cache()
+    log(f"weights packed ({L.whisper_packed_weights_size(dims) / 1e9:.2f} GB) in {time.time() - t0:.1f}s")
+
+    audio = gen_audio_tones(DEV, dims.cfg_id, B)
+    lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max)
+    tokens = gen_tokens(DEV, dims.cfg_id, TD, B, dims.n_vocab)
+    mel = torch.empty(B, dims.n_mels, 3000, dtype=torch.float32, device=DEV)
+    enc = torch.empty(B, T, d, dtype=torch.bfloat16, device=DEV)
+    ckv = torch.empty(Ldec, 2, B, H, T, 64, dtype=torch.bfloat16, device=DEV)
+    logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
+    state = DecodeState(dims, B, cap, ckv, torch.ones(Ldec, 2), lengths0)
+    fp8_ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=DEV)
+    for l in range(Ldec):
+        for kv in range(2):
+            x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, H, prefill_max)
+            codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+            # per-layer scale from the prefill maximum, computed on the device
+            L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), None, codes,
+                                   state.kv_scales[l, kv:kv + 1].data_ptr(), fp8_ws, fp8_ws.numel())
+            state.kv_cache[l, kv, :, :, :prefill_max, :] = codes
+            del x, codes
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s; cross K/V buffer {ckv.numel() * 2 / 1e9:.2f} GB, "
+        f"KV cache {state.kv_cache.numel() / 1e9:.2f} GB")
+
+    def run_step(ev=None):
+        if ev:
+            ev[0].record()
+        model.logmel(audio, out=mel)
+        if ev:
+            ev[1].record()
+        model.encode(mel, out=enc)
+        if ev:
+            ev[2].record()
+        model.cross_kv(enc, out=ckv)
+        if ev:
+            ev[3].record()
+        state.lengths.copy_(lengths0)
+        for t in range(TD):
+            model.decode_step(state, tokens[t], logits)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    assert int(state.dev_error[0].item()) == 0
+    log(f"warmup done at {time.time() - t0:.1f}s")
+
+    # dominant kernel: decoder cross-attention, events on the launch stream inside the timed region
+    n_ev = min(2048, Ldec * TD * args.steps)
+    k_start = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    k_stop = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in k_start + k_stop:
+        e.record()
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    L.whisper_profile_arm(L.PROF_DECODE_CROSS_ATTENTION, k_start, k_stop)
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for s in range(args.steps):
+        run_step(stage_ev[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    n_rec = L.whisper_profile_disarm()
+    elapsed = t_end - t_begin
+    ms_step = elapsed / args.steps * 1e3
+
+    stage_names = ["logmel", "encode", "cross_kv", "decode"]
+    stage_ms = {n: float(np.mean([stage_ev[s][i].elapsed_time(stage_ev[s][i + 1]) for s in range(args.steps)]))
+                for i, n in enumerate(stage_names)}
+    cross_ms = float(np.mean([k_start[i].elapsed_time(k_stop[i]) for i in range(n_rec)]))
+    cross_bytes = 2 * B * H * T * 64 * 2 + B * d * 2 + B * H * 4 * 66 * 4
+    cross_gbs = cross_bytes / (cross_ms * 1e-3) / 1e9
+    enc_flop = B * (2 * 3000 * 3 * dims.n_mels * d + 2 * 1500 * 3 * d * d) + B * 32 * (
+        2 * T * d * 3 * d + 2 * T * d * d + 2 * 2 * T * d * dims.d_ffn + 4 * T * T * d)
+    rtfx = B * AUDIO_S / (elapsed / args.steps)
+    decode_tok_s = B * TD / (stage_ms["decode"] * 1e-3)
+    log(f"timed {args.steps} steps: {ms_step:.1f} ms/step, RTFx {rtfx:.0f}, stages {stage_ms}")
+    log(f"cross-attention: {n_rec} launches timed, {cross_ms * 1e3:.1f} us avg, {cross_gbs:.0f} GB/s")
+
+    kernels = {}
+    if not args.no_kernel_probes:
+        kernels = kernel_probes(model, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np)
+
+    result = {
+        "metric": "RTFx and decode tok/s at Whisper large-v3 shape, fp8 KV, batch 64",
+        "value": round(rtfx, 2),
+        "unit": "x realtime (audio s / wall s)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded tones + noise audio, random N(0,0.02) weights, seeded token ids)",
+        "config": {"workload": f"large-v3 full path: {B} x 30 s chunks -> log-mel -> 32-layer encoder -> "
+                               f"cross K/V -> {TD} teacher-forced decode steps, batch {B}, fp8 e4m3 self-KV "
+                               f"prefilled U[1,448], cap {cap}",
+                   "batch": B, "decode_steps": TD, "audio_s_per_step": B * AUDIO_S},
+        "decode_tok_per_s": round(decode_tok_s, 1),
+        "encoder_tflops": round(enc_flop / (stage_ms["encode"] * 1e-3) / 1e12, 1),
+        "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "attn_decode_cross_kernel (decoder cross-attention, split-T partial)",
+                     "bound": "hbm", "achieved": round(cross_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(cross_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": cross_bytes, "avg_launch_us": round(cross_ms * 1e3, 2),
+                     "launches_timed": n_rec},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dims, audio, lengths0, tokens, state, np, torch)
+    print(json.dumps(result))
+
+
+def kernel_probes(model, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np):
+    """Per-kernel rooflines of the other hot kernels, each timed with the same
+    event hook in one extra (untimed) pass of the stage that launches it."""
+    out = {}
+    d, T, F, H = dims.d_model, dims.n_audio_ctx, dims.d_ffn, dims.n_heads
+    M = B * T
+
+    def timed(kind, fn, cap):
+        s = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(cap)]
+        for x in s + e:
+            x.record()
+        torch.cuda.synchronize()
+        L.whisper_profile_arm(kind, s, e)
+        fn()
+        torch.cuda.synchronize()
+        n = L.whisper_profile_disarm()
+        return float(np.mean([s[i].elapsed_time(e[i]) for i in range(n)])), n
+
+    ms, n = timed(L.PROF_ENCODER_FFN1, lambda: model.encode(mel, out=enc), 32)
+    fl = 2.0 * M * d * F
+    out["encoder_ffn1_gemm"] = {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                "avg_launch_us": round(ms * 1e3, 1), "launches": n,
+                                "shape": f"[{M},{d}]x[{d},{F}] + bias + GELU"}
+    ms, n = timed(L.PROF_ENCODER_ATTENTION, lambda: model.encode(mel, out=enc), 32)
+    fl = 4.0 * B * H * T * T * 64
+    out["encoder_attention"] = {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 1),
+                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                "avg_launch_us": round(ms * 1e3, 1), "launches": n}
+    ms, n = timed(L.PROF_ENCODER_LAYERNORM, lambda: model.encode(mel, out=enc), 32)
+    by = M * d * (2 + 4 + 4 + 2)
+    out["encoder_residual_layernorm"] = {"bound": "hbm", "achieved": round(by / (ms * 1e-3) / 1e9, 1),
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                         "avg_launch_us": round(ms * 1e3, 1), "launches": n,
+                                         "bytes_per_launch": by}
+    n_steps = 8
+
+    def dec():
+        state.lengths.copy_(lengths0)
+        for t in range(n_steps):
+            model.decode_step(state, tokens[t], logits)
+
+    mean_len = float(lengths0.float().mean().item()) + (n_steps - 1) / 2 + 1
+    ms, n = timed(L.PROF_DECODE_SELF_ATTENTION, dec, dims.n_dec_layers * n_steps)
+    by = 2 * B * H * mean_len * 64 + B * d * 4
+    out["decode_self_attention_fp8"] = {"bound": "hbm", "achieved": round(by / (ms * 1e-3) / 1e9, 1),
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                        "frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "avg_launch_us": round(ms * 1e3, 1), "launches": n,
+                                        "bytes_per_launch": round(by)}
+    return out
+
+
+def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch):
+    """The oracle, untouched, on a bounded sample of the same workload: chunk 0
+    through log-mel, the 32-layer encoder and cross K/V, then N_DEC of its 224
+    decode steps (batch 1); decode time is scaled to 224 steps."""
+    import importlib
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    O = importlib.import_module("oracle.whisper_oracle")
+    from workload import gen_weights
+    N_DEC = 8
+    W = {k: v.double().cpu().numpy() for k, v in gen_weights("cuda", dims).items()}
+    H, Ld = dims.n_heads, dims.n_dec_layers
+    a0 = audio[0].cpu().numpy()
+    t = time.perf_counter()
+    m = O.log_mel(a0, dims.n_mels)
+    e = O.encoder(m, W, H, dims.n_enc_layers)
+    cr = O.cross_kv(e, W, H, Ld)
+    t_front = time.perf_counter() - t
+    cross = [({0: k}, {0: v}) for k, v in cr]
+    codes = state.kv_cache[:, :, 0].cpu().numpy()
+    cache = [[{0: codes[l, kv].copy()} for kv in range(2)] for l in range(Ld)]
+    sc = state.kv_scales.cpu().numpy()
+    tok = tokens.cpu().numpy()
+    length = np.array([int(lengths0[0].item())])
+    t = time.perf_counter()
+    for s in range(N_DEC):
+        O.decode_step(W, H, tok[s, :1], length, cache, sc, cross)
+        length = length + 1
+    t_dec = (time.perf_counter() - t) * (tokens.shape[0] / N_DEC)
+    total = t_front + t_dec
+    return {"value": round(AUDIO_S / total, 3), "unit": "x realtime (audio s / wall s)", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"chunk 0 of the batch: log-mel + 32-layer encoder + cross K/V ({t_front:.1f} s) and "
+                      f"{N_DEC} of {tokens.shape[0]} decode steps at batch 1, scaled x{tokens.shape[0] / N_DEC:.0f} "
+                      f"({t_dec:.1f} s); fp64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

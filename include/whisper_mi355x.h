@@ -22,7 +22,7 @@
  *  - Every pointer argument is device memory owned by the caller unless
  *    stated otherwise; the library never allocates, frees or retains caller
  *    memory and keeps no state between calls apart from thread-local error
- *    text.
+ *    text and the optional measurement hook below.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream). Work
  *    is enqueued asynchronously; no call synchronises.
  *  - Argument, shape, dtype, alignment (16 bytes for tensors and workspaces;
@@ -212,6 +212,25 @@ size_t whisper_attention_decode_cross_workspace_size(int batch, int n_heads, int
 whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, const void* k, const void* v,
                                               int batch, int n_heads, int T, void* out, void* ws, size_t ws_bytes,
                                               void* stream);
+
+/* ------------------------------------------------------------------ measurement hook
+ * For measurement harnesses that need one kernel's own launch duration inside
+ * the composite calls, on the stream it runs on. While armed, every launch of
+ * the chosen kernel family is bracketed by hipEventRecord(start_events[i]) and
+ * hipEventRecord(stop_events[i]) on the call's stream, for the first
+ * `capacity` launches; events are hipEvent_t (passed as void*) created and
+ * owned by the caller. Process-wide, not thread-safe; the only state the
+ * library keeps besides error text. whisper_profile_disarm returns the number
+ * of event pairs recorded and clears the hook. */
+enum {
+  WHISPER_PROF_DECODE_CROSS_ATTENTION = 1, /* split-T partial kernel of the decoder cross-attention */
+  WHISPER_PROF_DECODE_SELF_ATTENTION = 2,  /* decoder self-attention over the fp8 cache */
+  WHISPER_PROF_ENCODER_ATTENTION = 3,      /* encoder flash attention */
+  WHISPER_PROF_ENCODER_FFN1 = 4,           /* encoder MLP up-projection GEMM (+GELU) */
+  WHISPER_PROF_ENCODER_LAYERNORM = 5       /* encoder fused residual + LayerNorm before the MLP */
+};
+whisper_status whisper_profile_arm(int kind, void* const* start_events, void* const* stop_events, int capacity);
+int whisper_profile_disarm(void);
 
 const char* whisper_status_string(whisper_status status);
 const char* whisper_last_error(void);

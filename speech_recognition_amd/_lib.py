@@ -22,8 +22,11 @@ EXPORTS = [
     "whisper_fp8_workspace_size", "whisper_fp8_quantize", "whisper_fp8_dequantize", "whisper_layernorm_fused",
     "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
-    "whisper_status_string", "whisper_last_error",
+    "whisper_profile_arm", "whisper_profile_disarm", "whisper_status_string", "whisper_last_error",
 ]
+
+PROF_DECODE_CROSS_ATTENTION, PROF_DECODE_SELF_ATTENTION, PROF_ENCODER_ATTENTION = 1, 2, 3
+PROF_ENCODER_FFN1, PROF_ENCODER_LAYERNORM = 4, 5
 
 
 class WhisperError(RuntimeError):
@@ -68,6 +71,8 @@ _SIG = {
     "whisper_attention_decode_self": (I, [I, P, I, I, I, P, P, P, P, P, P]),
     "whisper_attention_decode_cross_workspace_size": (Z, [I, I, I]),
     "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
+    "whisper_profile_arm": (I, [I, P, P, I]),
+    "whisper_profile_disarm": (I, []),
     "whisper_status_string": (ctypes.c_char_p, [I]),
     "whisper_last_error": (ctypes.c_char_p, []),
 }
@@ -208,6 +213,24 @@ def whisper_attention_decode_self(dt, q, batch, n_heads, cap, k_codes, v_codes, 
 def whisper_attention_decode_cross(dt, q, k, v, batch, n_heads, T, out, ws, ws_bytes, stream=None):
     _check(lib().whisper_attention_decode_cross(dt, _p(q), _p(k), _p(v), batch, n_heads, T, _p(out), _p(ws),
                                                 ws_bytes, _stream(stream)))
+
+
+def whisper_profile_arm(kind, start_events, stop_events):
+    """start_events / stop_events: sequences of torch.cuda.Event (recorded once
+    beforehand so the handles exist) or raw hipEvent_t ints; kept alive by
+    the caller until disarm."""
+    n = len(start_events)
+    h = lambda e: e if isinstance(e, int) else e.cuda_event  # noqa: E731
+    starts = (ctypes.c_void_p * n)(*[h(e) for e in start_events])
+    stops = (ctypes.c_void_p * n)(*[h(e) for e in stop_events])
+    whisper_profile_arm._keep = (starts, stops)
+    _check(lib().whisper_profile_arm(kind, starts, stops, n))
+
+
+def whisper_profile_disarm():
+    n = lib().whisper_profile_disarm()
+    whisper_profile_arm._keep = None
+    return n
 
 
 def whisper_status_string(status):

@@ -153,6 +153,29 @@ DecWS dec_ws(const whisper_dims* d, int B) {
 
 template <typename T> T* at(const void* base, size_t off) { return (T*)((char*)base + off); }
 
+// ------------------------------------------------------------------ measurement hook
+// Process-wide and not thread-safe by design: a measurement harness arms it,
+// runs its timed region, and disarms it.
+struct Profile {
+  int kind = 0;
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+  int cap = 0, n = 0;
+};
+Profile g_prof;
+
+struct ProfScope {
+  bool on;
+  hipStream_t s;
+  int i;
+  ProfScope(int kind, hipStream_t s_) : on(g_prof.kind == kind && g_prof.n < g_prof.cap), s(s_), i(g_prof.n) {
+    if (on) hipEventRecord(g_prof.start[i], s);
+  }
+  ~ProfScope() {
+    if (on) { hipEventRecord(g_prof.stop[i], s); g_prof.n = i + 1; }
+  }
+};
+
 // ------------------------------------------------------------------ GEMM helpers
 GemmParams gp(const void* A, long lda, const void* B, long ldb, int M, int N, int K, const float* bias, void* C,
               long ldc) {
@@ -191,10 +214,19 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
       WH_TRY(launch_layernorm(t, false, h_in, nullptr, g1, b1, 1e-5f, M, D, A, X, s));
     x_ready = true;
     WH_TRY(launch_gemm(t, EPI_STORE, gp(A, D, at<void>(packed, L.wqkv), D, M, 3 * D, D, at<float>(packed, L.bqkv), QKV, 3 * D), s));
-    WH_TRY(launch_attn_encoder(t, QKV, B, T, d->n_heads, ATT, s));
+    {
+      ProfScope ps(WHISPER_PROF_ENCODER_ATTENTION, s);
+      WH_TRY(launch_attn_encoder(t, QKV, B, T, d->n_heads, ATT, s));
+    }
     WH_TRY(launch_gemm(t, EPI_STORE, gp(ATT, D, at<void>(packed, L.wo), D, M, D, D, at<float>(packed, L.bo), Dl, D), s));
-    WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s));
-    WH_TRY(launch_gemm(t, EPI_GELU, gp(A, D, at<void>(packed, L.w1), D, M, F, D, at<float>(packed, L.b1), HF, F), s));
+    {
+      ProfScope ps(WHISPER_PROF_ENCODER_LAYERNORM, s);
+      WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s));
+    }
+    {
+      ProfScope ps(WHISPER_PROF_ENCODER_FFN1, s);
+      WH_TRY(launch_gemm(t, EPI_GELU, gp(A, D, at<void>(packed, L.w1), D, M, F, D, at<float>(packed, L.b1), HF, F), s));
+    }
     WH_TRY(launch_gemm(t, EPI_STORE, gp(HF, F, at<void>(packed, L.w2), F, M, D, F, at<float>(packed, L.b2), Dl, D), s));
     have_delta = true;
   }
@@ -256,6 +288,24 @@ const char* whisper_status_string(whisper_status st) {
 }
 
 const char* whisper_last_error(void) { return g_err.c_str(); }
+
+whisper_status whisper_profile_arm(int kind, void* const* start_events, void* const* stop_events, int capacity) {
+  if (kind < WHISPER_PROF_DECODE_CROSS_ATTENTION || kind > WHISPER_PROF_ENCODER_LAYERNORM)
+    return fail(WHISPER_ERR_INVALID_ARG, "profile_arm: unknown kernel kind");
+  if (!start_events || !stop_events || capacity <= 0) return fail(WHISPER_ERR_INVALID_ARG, "profile_arm: no events");
+  g_prof.kind = kind;
+  g_prof.start = (hipEvent_t*)start_events;
+  g_prof.stop = (hipEvent_t*)stop_events;
+  g_prof.cap = capacity;
+  g_prof.n = 0;
+  return WHISPER_OK;
+}
+
+int whisper_profile_disarm(void) {
+  const int n = g_prof.n;
+  g_prof = Profile();
+  return n;
+}
 
 int whisper_weight_count(const whisper_dims* d) {
   if (check_dims(d) != WHISPER_OK) return 0;
@@ -465,12 +515,19 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
     pq.kv_cap = cap; pq.kv_B = B; pq.kv_H = H; pq.kv_layer = l; pq.d_model = D;
     WH_TRY(launch_gemm_skinny(t, EPI_DEC_QKV, pq, s));
     const uint8_t* kc = kv_cache + l * kv_layer;
-    WH_TRY(launch_attn_decode_self(t, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap, ATT, s));
+    {
+      ProfScope ps(WHISPER_PROF_DECODE_SELF_ATTENTION, s);
+      WH_TRY(launch_attn_decode_self(t, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap, ATT, s));
+    }
     WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(ATT, D, at<void>(packed, Lw.wo), D, B, D, D, at<float>(packed, Lw.bo), Dl, D), s));
     WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln2g), at<float>(packed, Lw.ln2b), 1e-5f, B, D, A, X, s));
     WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(A, D, at<void>(packed, Lw.wqc), D, B, D, D, at<float>(packed, Lw.bqc), QC, D), s));
     const char* ck = (const char*)cross_kv + l * ckv_layer;
-    WH_TRY(launch_attn_decode_cross(t, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, CR, s));
+    {
+      ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
+      WH_TRY(launch_attn_decode_cross_partial(t, QC, ck, ck + ckv_layer / 2, B, H, T, CR, s));
+    }
+    WH_TRY(launch_attn_decode_cross_combine(t, CR, B, H, ATT, s));
     WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(ATT, D, at<void>(packed, Lw.woc), D, B, D, D, at<float>(packed, Lw.boc), Dl, D), s));
     WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln3g), at<float>(packed, Lw.ln3b), 1e-5f, B, D, A, X, s));
     WH_TRY(launch_gemm_skinny(t, EPI_GELU, gp(A, D, at<void>(packed, Lw.w1), D, B, F, D, at<float>(packed, Lw.b1), HF, F), s));

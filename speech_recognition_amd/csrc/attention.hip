@@ -409,20 +409,32 @@ __global__ __launch_bounds__(64) void attn_decode_cross_combine(const float* __r
   out[((long)b * H + h) * 64 + e] = Act<T>::st(num / den);
 }
 
-hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
-                                    void* out, float* ws, hipStream_t s) {
+hipError_t launch_attn_decode_cross_partial(ActType t, const void* q, const void* k, const void* v, int B, int H,
+                                            int T, float* ws, hipStream_t s) {
   if ((T + CROSS_SPLIT - 1) / CROSS_SPLIT > CROSS_MAX_CHUNK) return hipErrorInvalidValue;
   dim3 grid(CROSS_SPLIT, H, B);
-  if (t == ACT_BF16) {
+  if (t == ACT_BF16)
     hipLaunchKernelGGL(attn_decode_cross_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, (const u16*)k,
                        (const u16*)v, H, T, ws);
-    hipLaunchKernelGGL(attn_decode_cross_combine<u16>, dim3(H, B), dim3(64), 0, s, ws, H, (u16*)out);
-  } else {
+  else
     hipLaunchKernelGGL(attn_decode_cross_kernel<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)k,
                        (const float*)v, H, T, ws);
-    hipLaunchKernelGGL(attn_decode_cross_combine<float>, dim3(H, B), dim3(64), 0, s, ws, H, (float*)out);
-  }
   return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_cross_combine(ActType t, const float* ws, int B, int H, void* out, hipStream_t s) {
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(attn_decode_cross_combine<u16>, dim3(H, B), dim3(64), 0, s, ws, H, (u16*)out);
+  else
+    hipLaunchKernelGGL(attn_decode_cross_combine<float>, dim3(H, B), dim3(64), 0, s, ws, H, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
+                                    void* out, float* ws, hipStream_t s) {
+  hipError_t e = launch_attn_decode_cross_partial(t, q, k, v, B, H, T, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_attn_decode_cross_combine(t, ws, B, H, out, s);
 }
 
 }  // namespace wh

@@ -65,6 +65,9 @@ hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, cons
 size_t attn_decode_cross_ws(int B, int H, int T);
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
                                     void* out, float* ws, hipStream_t s);
+hipError_t launch_attn_decode_cross_partial(ActType t, const void* q, const void* k, const void* v, int B, int H,
+                                            int T, float* ws, hipStream_t s);
+hipError_t launch_attn_decode_cross_combine(ActType t, const float* ws, int B, int H, void* out, hipStream_t s);
 
 // ------------------------------------------------------------------ log-mel
 size_t logmel_ws(int B, int n_mels);
