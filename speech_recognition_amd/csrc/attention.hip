@@ -54,26 +54,29 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
   for (int s = 0; s < 4; ++s) qf[s] = bitcast<bf16x8>(*(const uint4*)(Qp + (long)qi * ld + s * 16 + g * 8));
 
   // tile loader: 64 keys x 64 dims of K and of V, 2 chunks of 16 B each per thread
-  int ld_row[2], ld_kc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) { const int c = tid + i * 256; ld_row[i] = c >> 3; ld_kc[i] = c & 7; }
-  uint4 rk[2], rv[2];
+  // thread stages chunk kc of keys row and row + 32 (8 dims = 16 bytes each)
+  const int row = tid >> 3, kc = tid & 7;
+  uint4 rk0, rk1, rv0, rv1;
   auto gload = [&](int kb) {
+    const int k0 = min(kb * 64 + row, T - 1), k1 = min(kb * 64 + row + 32, T - 1);
+    rk0 = *(const uint4*)(Kp + (long)k0 * ld + kc * 8);
+    rk1 = *(const uint4*)(Kp + (long)k1 * ld + kc * 8);
+    rv0 = *(const uint4*)(Vp + (long)k0 * ld + kc * 8);
+    rv1 = *(const uint4*)(Vp + (long)k1 * ld + kc * 8);
+  };
+  auto vt_store = [&](int buf, const uint4 v, int key) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = min(kb * 64 + ld_row[i], T - 1);
-      rk[i] = *(const uint4*)(Kp + (long)key * ld + ld_kc[i] * 8);
-      rv[i] = *(const uint4*)(Vp + (long)key * ld + ld_kc[i] * 8);
+    for (int j = 0; j < 4; ++j) {
+      sVt[buf][vt_swz(kc * 8 + 2 * j, key)] = (u16)(w[j] & 0xffffu);
+      sVt[buf][vt_swz(kc * 8 + 2 * j + 1, key)] = (u16)(w[j] >> 16);
     }
   };
   auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(uint4*)&sK[buf][k_swz(ld_row[i], ld_kc[i])] = rk[i];
-      const u16* v8 = (const u16*)&rv[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sVt[buf][vt_swz(ld_kc[i] * 8 + j, ld_row[i])] = v8[j];
-    }
+    *(uint4*)&sK[buf][k_swz(row, kc)] = rk0;
+    *(uint4*)&sK[buf][k_swz(row + 32, kc)] = rk1;
+    vt_store(buf, rv0, row);
+    vt_store(buf, rv1, row + 32);
   };
 
   f32x16 o[2];
@@ -223,9 +226,25 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 }
 
 // ------------------------------------------------------------------ decoder self-attention over e4m3 codes
-// One workgroup per (row, head). Keys 0..n-1 (n = lengths[b] + len_add) are
-// read as 64-byte code rows, 4 lanes x 16 codes per key; scores stay in LDS.
+// One workgroup per (head, row). Keys 0..n-1 (n = lengths[b] + len_add) are
+// 64-byte code rows read as 4 lanes x 16 codes. Each lane issues all of its
+// loads of a batch (8 keys, 128 B) before decoding any of them, so a whole
+// cache row of up to 512 keys is in flight at once; scores stay in LDS.
 constexpr int DEC_MAX_CAP = 4096;
+constexpr int SELF_BATCH = 8;
+
+__device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[4];
+    e4m3x4_decode(w[i], v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc = fmaf(q[4 * i + k], v[k], acc);
+  }
+  return acc;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restrict__ q, long q_stride,
@@ -251,15 +270,21 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
 #pragma unroll
   for (int i = 0; i < 16; ++i) qreg[i] = qs[part * 16 + i];
   const float sscale = sk * 0.125f;
-  for (int j = kg; j < n; j += 64) {
-    const uint4 c = *(const uint4*)(K + (long)j * 64 + part * 16);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float acc = 0.f;
+  for (int base = 0; base < n; base += 64 * SELF_BATCH) {
+    uint4 c[SELF_BATCH];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc = fmaf(qreg[i], e4m3_decode((w[i >> 2] >> ((i & 3) * 8)) & 0xffu), acc);
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    if (part == 0) sc[j] = acc * sscale;
+    for (int i = 0; i < SELF_BATCH; ++i) {
+      const int j = base + kg + 64 * i;
+      c[i] = j < n ? *(const uint4*)(K + (long)j * 64 + part * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SELF_BATCH; ++i) {
+      const int j = base + kg + 64 * i;
+      float acc = dot16_e4m3(c[i], qreg);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (part == 0 && j < n) sc[j] = acc * sscale;
+    }
   }
   __syncthreads();
   float mx = -INFINITY;
@@ -271,19 +296,32 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
   float sum = 0.f;
   for (int j = tid; j < n; j += 256) { const float p = expf(sc[j] - mx); sc[j] = p; sum += p; }
   sum = wave_sum(sum);
-  __syncthreads();
   if ((tid & 63) == 0) wred[4 + (tid >> 6)] = sum;
   __syncthreads();
   sum = wred[4] + wred[5] + wred[6] + wred[7];
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int j = kg; j < n; j += 64) {
-    const uint4 c = *(const uint4*)(V + (long)j * 64 + part * 16);
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    const float p = sc[j];
+  for (int base = 0; base < n; base += 64 * SELF_BATCH) {
+    uint4 c[SELF_BATCH];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = fmaf(p, e4m3_decode((w[i >> 2] >> ((i & 3) * 8)) & 0xffu), acc[i]);
+    for (int i = 0; i < SELF_BATCH; ++i) {
+      const int j = base + kg + 64 * i;
+      c[i] = j < n ? *(const uint4*)(V + (long)j * 64 + part * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SELF_BATCH; ++i) {
+      const int j = base + kg + 64 * i;
+      const float p = j < n ? sc[j] : 0.f;
+      const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        float v[4];
+        e4m3x4_decode(w[e4], v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[4 * e4 + k] = fmaf(p, v[k], acc[4 * e4 + k]);
+      }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) red[kg][part * 16 + i] = acc[i];

@@ -59,6 +59,16 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | (code > 0x7eu ? 0x7eu : code);
 }
 
+// Four codes packed in a word -> fp32 with the gfx950 converter (OCP E4M3FN,
+// NaN for S.1111.111), two codes per instruction.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e4m3x4_decode(uint32_t w, float o[4]) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// Scalar decode from the bit fields (reference form of the same mapping).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
   float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;

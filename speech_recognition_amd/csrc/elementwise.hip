@@ -142,8 +142,11 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* x, size_t n,
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_dequantize_kernel(const uint8_t* codes, size_t n, const float* scale, T* y) {
   const float s = scale[0];
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-    y[i] = Act<T>::st(e4m3_decode(codes[i]) * s);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float v[4];
+    e4m3x4_decode(codes[i], v);
+    y[i] = Act<T>::st(v[0] * s);
+  }
 }
 
 static int grid_for(size_t n) {
@@ -321,14 +324,25 @@ hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, con
 }
 
 // Greedy token per row: largest logit, lowest index on ties; then lengths[b] += 1.
-__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V, int32_t* out, int32_t* lengths) {
-  const int b = blockIdx.x;
+// 1024 lanes per row with 16-byte loads, so a 51866-wide row is one pass of
+// ~13 independent loads per lane.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out, int32_t* lengths) {
+  const int b = blockIdx.x, tid = threadIdx.x;
   const float* row = logits + (size_t)b * V;
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) {
+  const bool vec = ((((uintptr_t)row) & 15u) == 0);
+  const int nv = vec ? V / 4 : 0;
+  for (int i = tid; i < nv; i += 1024) {
+    const float4 v = *(const float4*)(row + 4 * i);
+    const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (a[k] > best) { best = a[k]; idx = 4 * i + k; }
+  }
+  for (int i = 4 * nv + tid; i < V; i += 1024) {
     const float v = row[i];
-    if (v > best) { best = v; idx = i; }
+    if (v > best || (v == best && i < idx)) { best = v; idx = i; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -336,12 +350,12 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V,
     const int oi = __shfl_xor(idx, o, 64);
     if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
   }
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = idx; }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  if ((tid & 63) == 0) { sv[tid >> 6] = best; si[tid >> 6] = idx; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+  if (tid == 0) {
+    for (int w = 1; w < 16; ++w)
       if (sv[w] > best || (sv[w] == best && si[w] < idx)) { best = sv[w]; idx = si[w]; }
     out[b] = idx == 0x7fffffff ? 0 : idx;
     if (lengths) lengths[b] += 1;
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int V,
 }
 
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(256), 0, s, logits, V, argmax, lengths);
+  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, s, logits, V, argmax, lengths);
   return hipGetLastError();
 }
 

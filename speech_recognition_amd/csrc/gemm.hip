@@ -51,9 +51,14 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, int z, int m, int
 }
 
 // ------------------------------------------------------------------ bf16 MFMA, 128x128x64
+// 256 threads = 2x2 waves, each wave a 64x64 sub-tile of 16x16x32 MFMAs with
+// fp32 accumulators. A and B tiles (128 rows x 64 k) are staged through
+// registers into double-buffered LDS. Rows are 128 B (8 chunks of 16 B); chunk
+// c of row r is stored at c ^ ((r >> 1) & 7), so the 16 rows one MFMA fragment
+// read touches (two rows per 256-byte bank line) land on distinct banks.
 constexpr int TB = 128, TK = 64;
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * TK + ((kc ^ (row & 7)) << 3); }
+__device__ __forceinline__ int swz(int row, int kc) { return row * TK + ((kc ^ ((row >> 1) & 7)) << 3); }
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_bf16_128(GemmParams p) {
@@ -74,18 +79,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_128(GemmParams p) {
   const u16* B = (const u16*)p.B;
   const int m0 = tm * TB, n0 = tn * TB;
 
-  const u16* a_ptr[4];
-  const u16* b_ptr[4];
-  int lds_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * 256, row = c >> 3, kc = c & 7;
-    const int ar = min(m0 + row, p.M - 1), br = min(n0 + row, p.N - 1);
-    a_ptr[i] = A + (long)ar * p.lda + kc * 8;
-    b_ptr[i] = B + (long)br * p.ldb + kc * 8;
-    lds_off[i] = swz(row, kc);
-  }
-  uint4 ra[4], rb[4];
+  // this thread stages chunk (row r0 + 32 i, kc) of each tile, i = 0..3
+  const int r0 = tid >> 3, kc0 = tid & 7;
+  const long la = p.lda, lb = p.ldb;
+  const u16* pa0 = A + (long)min(m0 + r0, p.M - 1) * la + kc0 * 8;
+  const u16* pa1 = A + (long)min(m0 + r0 + 32, p.M - 1) * la + kc0 * 8;
+  const u16* pa2 = A + (long)min(m0 + r0 + 64, p.M - 1) * la + kc0 * 8;
+  const u16* pa3 = A + (long)min(m0 + r0 + 96, p.M - 1) * la + kc0 * 8;
+  const u16* pb0 = B + (long)min(n0 + r0, p.N - 1) * lb + kc0 * 8;
+  const u16* pb1 = B + (long)min(n0 + r0 + 32, p.N - 1) * lb + kc0 * 8;
+  const u16* pb2 = B + (long)min(n0 + r0 + 64, p.N - 1) * lb + kc0 * 8;
+  const u16* pb3 = B + (long)min(n0 + r0 + 96, p.N - 1) * lb + kc0 * 8;
+  const int so = swz(r0, kc0);  // rows r0 + 32 i share the swizzle, so chunk i sits at so + 32*i*TK
+
+  uint4 ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
+#define WH_GLOAD(k)                                                                  \
+  ga0 = *(const uint4*)(pa0 + (k)); ga1 = *(const uint4*)(pa1 + (k));                 \
+  ga2 = *(const uint4*)(pa2 + (k)); ga3 = *(const uint4*)(pa3 + (k));                 \
+  gb0 = *(const uint4*)(pb0 + (k)); gb1 = *(const uint4*)(pb1 + (k));                 \
+  gb2 = *(const uint4*)(pb2 + (k)); gb3 = *(const uint4*)(pb3 + (k));
+#define WH_SSTORE(buf)                                                               \
+  *(uint4*)(&sA[buf][so]) = ga0; *(uint4*)(&sA[buf][so + 32 * TK]) = ga1;             \
+  *(uint4*)(&sA[buf][so + 64 * TK]) = ga2; *(uint4*)(&sA[buf][so + 96 * TK]) = ga3;   \
+  *(uint4*)(&sB[buf][so]) = gb0; *(uint4*)(&sB[buf][so + 32 * TK]) = gb1;             \
+  *(uint4*)(&sB[buf][so + 64 * TK]) = gb2; *(uint4*)(&sB[buf][so + 96 * TK]) = gb3;
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -93,51 +111,37 @@ __global__ __launch_bounds__(256) void gemm_bf16_128(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / TK;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *(const uint4*)a_ptr[i];
-    rb[i] = *(const uint4*)b_ptr[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *(uint4*)&sA[0][lds_off[i]] = ra[i];
-    *(uint4*)&sB[0][lds_off[i]] = rb[i];
-  }
+  WH_GLOAD(0)
+  WH_SSTORE(0)
   __syncthreads();
-
+  const int fr = lane & 15;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = *(const uint4*)(a_ptr[i] + (kt + 1) * TK);
-        rb[i] = *(const uint4*)(b_ptr[i] + (kt + 1) * TK);
-      }
-    }
+    const bool more = kt + 1 < nk;
+    if (more) { WH_GLOAD((kt + 1) * TK) }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[4], bfr[4];
       const int kc = s * 4 + (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 64 + i * 16 + (lane & 15), kc)]);
-        bfr[i] = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + i * 16 + (lane & 15), kc)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      bf16x8 af0 = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 64 + 0 + fr, kc)]);
+      bf16x8 af1 = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 64 + 16 + fr, kc)]);
+      bf16x8 af2 = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 64 + 32 + fr, kc)]);
+      bf16x8 af3 = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 64 + 48 + fr, kc)]);
+      bf16x8 bf0 = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + 0 + fr, kc)]);
+      bf16x8 bf1 = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + 16 + fr, kc)]);
+      bf16x8 bf2 = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + 32 + fr, kc)]);
+      bf16x8 bf3 = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + 48 + fr, kc)]);
+#define WH_MF(i, j, a, b) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i][j], 0, 0, 0)
+      WH_MF(0, 0, af0, bf0); WH_MF(0, 1, af0, bf1); WH_MF(0, 2, af0, bf2); WH_MF(0, 3, af0, bf3);
+      WH_MF(1, 0, af1, bf0); WH_MF(1, 1, af1, bf1); WH_MF(1, 2, af1, bf2); WH_MF(1, 3, af1, bf3);
+      WH_MF(2, 0, af2, bf0); WH_MF(2, 1, af2, bf1); WH_MF(2, 2, af2, bf2); WH_MF(2, 3, af2, bf3);
+      WH_MF(3, 0, af3, bf0); WH_MF(3, 1, af3, bf1); WH_MF(3, 2, af3, bf2); WH_MF(3, 3, af3, bf3);
+#undef WH_MF
     }
-    if (kt + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *(uint4*)&sA[cur ^ 1][lds_off[i]] = ra[i];
-        *(uint4*)&sB[cur ^ 1][lds_off[i]] = rb[i];
-      }
-    }
+    if (more) { WH_SSTORE(cur ^ 1) }
     __syncthreads();
   }
+#undef WH_GLOAD
+#undef WH_SSTORE
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -151,47 +155,71 @@ __global__ __launch_bounds__(256) void gemm_bf16_128(GemmParams p) {
 }
 
 // ------------------------------------------------------------------ bf16 skinny (decode rows)
-// One workgroup owns 16 output columns; its KS waves split K into contiguous
-// ranges and stream that slice of the weight exactly once; the activation
-// rows (<= 16*MB) are re-read from L2. Partials are summed through LDS.
-template <int EPI, int MB, int KS>
-__global__ __launch_bounds__(KS * 64) void gemm_bf16_skinny(GemmParams p) {
-  __shared__ float red[KS][MB * 16][17];
+// Decoder GEMMs have M = batch rows (<= 128) and stream their weight once, so
+// they are bound by bytes in flight, not by MFMA. One workgroup owns 16*CB
+// output columns; its WAVES waves split K into contiguous ranges, and each
+// wave issues all loads of a batch of SKB k-steps (weights from HBM,
+// activation rows from L2) before the MFMAs of that batch, so a whole
+// (N/16*CB) x K weight slice is requested at once. Partials meet in LDS.
+template <int EPI, int MB, int CB, int W>
+__global__ __launch_bounds__(W * 64) void gemm_bf16_skinny(GemmParams p) {
+  constexpr int SKB = MB >= 8 ? 3 : 5;  // k-steps whose loads are issued together
+  constexpr int RW = CB * 16 + 1;
+  __shared__ float red[W][MB * 16][RW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16;
-  const int kper = p.K / KS;
-  const int kb = wave * kper;
-  const int nrow = min(n0 + (lane & 15), p.N - 1);
-  const u16* wp = (const u16*)p.B + (long)nrow * p.ldb + kb + (lane >> 4) * 8;
+  const int n0 = blockIdx.x * 16 * CB;
+  const int kper = p.K / W;
+  const int kofs = wave * kper + (lane >> 4) * 8;
+  const u16* wp[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int nrow = min(n0 + cb * 16 + (lane & 15), p.N - 1);
+    wp[cb] = (const u16*)p.B + (long)nrow * p.ldb + kofs;
+  }
   const u16* ap[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int row = min(mb * 16 + (lane & 15), p.M - 1);
-    ap[mb] = (const u16*)p.A + (long)row * p.lda + kb + (lane >> 4) * 8;
+    ap[mb] = (const u16*)p.A + (long)row * p.lda + kofs;
   }
-  f32x4 acc[MB];
+  f32x4 acc[MB][CB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < kper; k += 32) {
-    const bf16x8 b = bitcast<bf16x8>(*(const uint4*)(wp + k));
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8 a = bitcast<bf16x8>(*(const uint4*)(ap[mb] + k));
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb], 0, 0, 0);
+    for (int cb = 0; cb < CB; ++cb) acc[mb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < kper; k0 += 32 * SKB) {
+    uint4 wv[SKB][CB], av[SKB][MB];
+#pragma unroll
+    for (int j = 0; j < SKB; ++j) {
+      const int k = k0 + j * 32;
+      const bool ok = k < kper;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) wv[j][cb] = ok ? *(const uint4*)(wp[cb] + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[j][mb] = ok ? *(const uint4*)(ap[mb] + k) : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int j = 0; j < SKB; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[j][mb]), bitcast<bf16x8>(wv[j][cb]),
+                                                                acc[mb][cb], 0, 0, 0);
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][mb * 16 + (lane >> 4) * 4 + r][lane & 15] = acc[mb][r];
-  __syncthreads();
-  for (int o = tid; o < MB * 16 * 16; o += KS * 64) {
-    const int m = o >> 4, c = o & 15;
-    float s = 0.f;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int w = 0; w < KS; ++w) s += red[w][m][c];
-    epi_store<u16, EPI>(p, 0, m, n0 + c, s);
+      for (int r = 0; r < 4; ++r) red[wave][mb * 16 + (lane >> 4) * 4 + r][cb * 16 + (lane & 15)] = acc[mb][cb][r];
+  __syncthreads();
+  for (int o = tid; o < MB * 16 * CB * 16; o += W * 64) {
+    const int m = o / (CB * 16), c = o - m * (CB * 16);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) sum += red[w][m][c];
+    epi_store<u16, EPI>(p, 0, m, n0 + c, sum);
   }
 }
 
@@ -265,33 +293,38 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, int KS>
+template <int EPI, int CB, int W>
 static void skinny_mb(const GemmParams& p, hipStream_t s) {
-  dim3 grid((p.N + 15) / 16);
+  dim3 grid((p.N + 16 * CB - 1) / (16 * CB)), block(W * 64);
   const int mb = (p.M + 15) / 16;
-  if (mb <= 1) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 1, KS>), grid, dim3(KS * 64), 0, s, p);
-  else if (mb <= 2) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 2, KS>), grid, dim3(KS * 64), 0, s, p);
-  else if (mb <= 4) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 4, KS>), grid, dim3(KS * 64), 0, s, p);
-  else if (mb <= 6) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 6, KS>), grid, dim3(KS * 64), 0, s, p);
-  else hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 8, KS>), grid, dim3(KS * 64), 0, s, p);
+  if (mb <= 1) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 1, CB, W>), grid, block, 0, s, p);
+  else if (mb <= 2) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 2, CB, W>), grid, block, 0, s, p);
+  else if (mb <= 4) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 4, CB, W>), grid, block, 0, s, p);
+  else if (mb <= 6) hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 6, CB, W>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gemm_bf16_skinny<EPI, 8, CB, W>), grid, block, 0, s, p);
 }
 
-template <int EPI>
-static void skinny_ks(const GemmParams& p, hipStream_t s) {
-  if (p.K % (32 * 8) == 0 && p.K >= 4096) skinny_mb<EPI, 8>(p, s);
-  else skinny_mb<EPI, 4>(p, s);
+// K is split over 8 waves when it divides into 32-wide steps, else over 4.
+template <int EPI, int CB>
+static bool skinny_w(const GemmParams& p, hipStream_t s) {
+  if (p.K % (32 * 8) == 0) { skinny_mb<EPI, CB, 8>(p, s); return true; }
+  if (p.K % (32 * 4) == 0) { skinny_mb<EPI, CB, 4>(p, s); return true; }
+  return false;
 }
 
 hipError_t launch_gemm_skinny(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  if (t != ACT_BF16 || p.M > 128 || p.batch != 1 || p.K % 128 != 0) return launch_gemm(t, epi, p, s);
+  if (t != ACT_BF16 || p.M > 128 || p.batch != 1) return launch_gemm(t, epi, p, s);
+  bool ok = false;
   switch (epi) {
-    case EPI_STORE: skinny_ks<EPI_STORE>(p, s); break;
-    case EPI_GELU: skinny_ks<EPI_GELU>(p, s); break;
-    case EPI_F32: skinny_ks<EPI_F32>(p, s); break;
-    case EPI_DEC_QKV: skinny_ks<EPI_DEC_QKV>(p, s); break;
-    default: return launch_gemm(t, epi, p, s);
+    case EPI_STORE: ok = skinny_w<EPI_STORE, 1>(p, s); break;
+    case EPI_GELU: ok = skinny_w<EPI_GELU, 1>(p, s); break;
+    case EPI_DEC_QKV: ok = skinny_w<EPI_DEC_QKV, 1>(p, s); break;
+    // the vocabulary projection: two column blocks per wave halve activation re-reads
+    case EPI_F32: ok = p.N >= 16384 ? skinny_w<EPI_F32, 2>(p, s) : skinny_w<EPI_F32, 1>(p, s); break;
+    default: break;
   }
+  if (!ok) return launch_gemm(t, epi, p, s);
   return hipGetLastError();
 }
 
