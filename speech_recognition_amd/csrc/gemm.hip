@@ -154,6 +154,461 @@ __global__ __launch_bounds__(256) void gemm_bf16_128(GemmParams p) {
       }
 }
 
+// ------------------------------------------------------------------ bf16 MFMA, 256x256x64
+// Large-M variant (the encoder projections, conv stem and cross K/V): 512
+// threads = 2x4 waves, each wave a 128x64 sub-tile (8x4 MFMA 16x16x32 tiles,
+// 128 fp32 accumulators), so each fragment read from LDS feeds twice as many
+// MFMAs as in the 64x64 sub-tile. 2 x (32 KB A + 32 KB B) of LDS per block;
+// same row swizzle and XCD-aware tile order as above.
+constexpr int TB2 = 256;
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_256(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) u16 sA[2][TB2 * TK];
+  __shared__ __attribute__((aligned(16))) u16 sB[2][TB2 * TK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles_n = (p.N + TB2 - 1) / TB2;
+  const int tiles_m = (p.M + TB2 - 1) / TB2;
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid / tiles_n, tn = bid - tm * tiles_n;
+  const int z = blockIdx.z;
+  const u16* A = (const u16*)p.A + (long)z * p.strideA;
+  const u16* B = (const u16*)p.B;
+  const int m0 = tm * TB2, n0 = tn * TB2;
+
+  // this thread stages chunk (row r0 + 64 i, kc0) of each tile, i = 0..3
+  const int r0 = tid >> 3, kc0 = tid & 7;
+  const long la = p.lda, lb = p.ldb;
+  const u16* pa0 = A + (long)min(m0 + r0, p.M - 1) * la + kc0 * 8;
+  const u16* pa1 = A + (long)min(m0 + r0 + 64, p.M - 1) * la + kc0 * 8;
+  const u16* pa2 = A + (long)min(m0 + r0 + 128, p.M - 1) * la + kc0 * 8;
+  const u16* pa3 = A + (long)min(m0 + r0 + 192, p.M - 1) * la + kc0 * 8;
+  const u16* pb0 = B + (long)min(n0 + r0, p.N - 1) * lb + kc0 * 8;
+  const u16* pb1 = B + (long)min(n0 + r0 + 64, p.N - 1) * lb + kc0 * 8;
+  const u16* pb2 = B + (long)min(n0 + r0 + 128, p.N - 1) * lb + kc0 * 8;
+  const u16* pb3 = B + (long)min(n0 + r0 + 192, p.N - 1) * lb + kc0 * 8;
+  const int so = swz(r0, kc0);  // rows r0 + 64 i share the swizzle
+
+  uint4 ga0, ga1, ga2, ga3, gb0, gb1, gb2, gb3;
+#define WH_GLOAD(k)                                                                  \
+  ga0 = *(const uint4*)(pa0 + (k)); ga1 = *(const uint4*)(pa1 + (k));                 \
+  ga2 = *(const uint4*)(pa2 + (k)); ga3 = *(const uint4*)(pa3 + (k));                 \
+  gb0 = *(const uint4*)(pb0 + (k)); gb1 = *(const uint4*)(pb1 + (k));                 \
+  gb2 = *(const uint4*)(pb2 + (k)); gb3 = *(const uint4*)(pb3 + (k));
+#define WH_SSTORE(buf)                                                                 \
+  *(uint4*)(&sA[buf][so]) = ga0; *(uint4*)(&sA[buf][so + 64 * TK]) = ga1;               \
+  *(uint4*)(&sA[buf][so + 128 * TK]) = ga2; *(uint4*)(&sA[buf][so + 192 * TK]) = ga3;   \
+  *(uint4*)(&sB[buf][so]) = gb0; *(uint4*)(&sB[buf][so + 64 * TK]) = gb1;               \
+  *(uint4*)(&sB[buf][so + 128 * TK]) = gb2; *(uint4*)(&sB[buf][so + 192 * TK]) = gb3;
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / TK;
+  WH_GLOAD(0)
+  WH_SSTORE(0)
+  __syncthreads();
+  const int fr = lane & 15;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) { WH_GLOAD((kt + 1) * TK) }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kc = s * 4 + (lane >> 4);
+      bf16x8 bf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bf[j] = bitcast<bf16x8>(*(const uint4*)&sB[cur][swz(wn * 64 + j * 16 + fr, kc)]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 af = bitcast<bf16x8>(*(const uint4*)&sA[cur][swz(wm * 128 + i * 16 + fr, kc)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    if (more) { WH_SSTORE(cur ^ 1) }
+    __syncthreads();
+  }
+#undef WH_GLOAD
+#undef WH_SSTORE
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 128 + i * 16 + (lane >> 4) * 4 + r;
+        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
+        epi_store<u16, EPI>(p, z, m, n, acc[i][j][r]);
+      }
+}
+
+// ------------------------------------------------------------------ vectorised epilogue
+// Eight consecutive columns n..n+7 of row m (n % 8 == 0, all < N) in one go:
+// bias read as two float4, one 16-byte store for bf16 outputs.
+template <int EPI>
+__device__ __forceinline__ void epi_store8(const GemmParams& p, int z, int m, int n, float v[8]) {
+  if (p.bias) {
+    const float4 b0 = *(const float4*)(p.bias + n), b1 = *(const float4*)(p.bias + n + 4);
+    v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+    v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+  }
+  if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_PE) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = gelu_erf(v[i]);
+  }
+  if constexpr (EPI == EPI_GELU_PE) {
+    const float* pe = p.pe + (long)m * p.N + n;
+    const float4 q0 = *(const float4*)pe, q1 = *(const float4*)(pe + 4);
+    float* c = (float*)p.C + (long)z * p.strideC + (long)m * p.ldc + n;
+    *(float4*)c = make_float4(v[0] + q0.x, v[1] + q0.y, v[2] + q0.z, v[3] + q0.w);
+    *(float4*)(c + 4) = make_float4(v[4] + q1.x, v[5] + q1.y, v[6] + q1.z, v[7] + q1.w);
+    return;
+  }
+  uint4 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  if constexpr (EPI == EPI_CROSSKV) {
+    const int d = p.ckv_d, T_ = p.ckv_T;
+    const int b = m / T_, t = m - b * T_;
+    const int l = n / (2 * d), r = n - l * 2 * d;
+    const int kv = r / d, c = r - kv * d;
+    const long idx = ((((long)(l * 2 + kv) * p.ckv_B + b) * p.ckv_H + (c >> 6)) * T_ + t) * 64 + (c & 63);
+    *(uint4*)((u16*)p.C + idx) = u;
+  } else {
+    *(uint4*)((u16*)p.C + (long)z * p.strideC + (long)m * p.ldc + n) = u;
+  }
+}
+
+// Four consecutive columns n..n+3 of row m (n % 4 == 0, all < N): bias as one
+// float4, one 8-byte store for bf16 outputs (16 bytes for the fp32 stream).
+template <int EPI>
+__device__ __forceinline__ void epi_store4(const GemmParams& p, int z, int m, int n, float v[4]) {
+  if (p.bias) {
+    const float4 b = *(const float4*)(p.bias + n);
+    v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+  }
+  if constexpr (EPI == EPI_GELU || EPI == EPI_GELU_PE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = gelu_erf(v[i]);
+  }
+  if constexpr (EPI == EPI_GELU_PE) {
+    const float4 q = *(const float4*)(p.pe + (long)m * p.N + n);
+    *(float4*)((float*)p.C + (long)z * p.strideC + (long)m * p.ldc + n) =
+        make_float4(v[0] + q.x, v[1] + q.y, v[2] + q.z, v[3] + q.w);
+    return;
+  }
+  uint2 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  if constexpr (EPI == EPI_CROSSKV) {
+    const int d = p.ckv_d, T_ = p.ckv_T;
+    const int b = m / T_, t = m - b * T_;
+    const int l = n / (2 * d), r = n - l * 2 * d;
+    const int kv = r / d, c = r - kv * d;
+    const long idx = ((((long)(l * 2 + kv) * p.ckv_B + b) * p.ckv_H + (c >> 6)) * T_ + t) * 64 + (c & 63);
+    *(uint2*)((u16*)p.C + idx) = u;
+  } else {
+    *(uint2*)((u16*)p.C + (long)z * p.strideC + (long)m * p.ldc + n) = u;
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, 256x256x64, 4 waves
+// 256 threads = 2x2 waves, each wave a 128x128 sub-tile (8x8 MFMA 16x16x32
+// tiles, 256 fp32 accumulators held in AGPRs), one wave per SIMD: per MFMA,
+// half the LDS fragment bytes of the 64x64 sub-tile. The accumulators leave
+// through LDS (bias/activation applied, packed to bf16) so C is written with
+// 16-byte row-contiguous stores.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_bf16_256w4(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) u16 smem[2 * 2 * TB2 * TK];  // [buf][A|B][256][64]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_n = (p.N + TB2 - 1) / TB2;
+  const int tiles_m = (p.M + TB2 - 1) / TB2;
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int tm = bid / tiles_n, tn = bid - tm * tiles_n;
+  const int z = blockIdx.z;
+  const u16* A = (const u16*)p.A + (long)z * p.strideA;
+  const u16* B = (const u16*)p.B;
+  const int m0 = tm * TB2, n0 = tn * TB2;
+  u16* sA0 = smem;
+  u16* sB0 = smem + TB2 * TK;
+  constexpr int BUF = 2 * TB2 * TK;
+
+  // staging: rows r0 + 32 i (i = 0..7) of A and of B, chunk kc0
+  const int r0 = tid >> 3, kc0 = tid & 7;
+  const long la = p.lda, lb = p.ldb;
+  const u16* pa = A + (long)min(m0 + r0, p.M - 1) * la + kc0 * 8;
+  const u16* pb = B + (long)min(n0 + r0, p.N - 1) * lb + kc0 * 8;
+  long oa[8], ob[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    oa[i] = ((long)min(m0 + r0 + 32 * i, p.M - 1) - min(m0 + r0, p.M - 1)) * la;
+    ob[i] = ((long)min(n0 + r0 + 32 * i, p.N - 1) - min(n0 + r0, p.N - 1)) * lb;
+  }
+  const int so = swz(r0, kc0);
+  uint4 ga[8], gb[8];
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / TK;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { ga[i] = *(const uint4*)(pa + oa[i]); gb[i] = *(const uint4*)(pb + ob[i]); }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    *(uint4*)(sA0 + so + 32 * i * TK) = ga[i];
+    *(uint4*)(sB0 + so + 32 * i * TK) = gb[i];
+  }
+  __syncthreads();
+  const int fr = lane & 15;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // next tile (the last iteration re-reads the last tile: in bounds, unused)
+    const int kn = min(kt + 1, nk - 1) * TK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { ga[i] = *(const uint4*)(pa + oa[i] + kn); gb[i] = *(const uint4*)(pb + ob[i] + kn); }
+    const u16* cA = sA0 + cur * BUF;
+    const u16* cB = sB0 + cur * BUF;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kc = s * 4 + (lane >> 4);
+      bf16x8 bf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bf[j] = bitcast<bf16x8>(*(const uint4*)(cB + swz(wn * 128 + j * 16 + fr, kc)));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8 af = bitcast<bf16x8>(*(const uint4*)(cA + swz(wm * 128 + i * 16 + fr, kc)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    u16* nA = sA0 + (cur ^ 1) * BUF;
+    u16* nB = sB0 + (cur ^ 1) * BUF;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *(uint4*)(nA + so + 32 * i * TK) = ga[i];
+      *(uint4*)(nB + so + 32 * i * TK) = gb[i];
+    }
+    __syncthreads();
+  }
+  // epilogue: each wave parks its fp32 128x128 sub-tile in LDS in two 64-row
+  // halves (32 KB each), then reads 8 consecutive columns per lane
+  float* wbuf = (float*)smem + wave * (64 * 128);
+  constexpr int WR = 128;  // row stride in floats
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = ii * 16 + (lane >> 4) * 4 + r;
+          const int col = j * 16 + (lane & 15);
+          wbuf[row * WR + (col ^ ((row & 7) << 2))] = acc[h * 4 + ii][j][r];
+        }
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int c8 = it * 64 + lane;   // 64 rows x 16 eight-column chunks
+      const int row = c8 >> 4, col = (c8 & 15) * 8;
+      const int m = m0 + wm * 128 + h * 64 + row;
+      const int n = n0 + wn * 128 + col;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = wbuf[row * WR + ((col + q) ^ ((row & 7) << 2))];
+      if (m < p.M) {
+        if (n + 8 <= p.N) {
+          epi_store8<EPI>(p, z, m, n, v);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) epi_store<u16, EPI>(p, z, m, n + q, v[q]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ bf16 MFMA, 256x256, LDS DMA pipeline
+// The encoder / cross-K/V GEMM at full size. Measured on the register-staged
+// kernels: no LDS bank conflicts and LDS only ~17% busy, but waves spent ~45%
+// of their time waiting for the next tile's global loads. Here tiles flow
+// through a 4-stage LDS ring (BK = 32, 32 KB per stage) filled by direct
+// global->LDS loads (16 bytes per lane, no staging registers) issued three
+// stages ahead, with one barrier per stage. 512 threads = 2x4 waves of 128x64
+// sub-tiles (8x4 MFMA 16x16x32). Each 1 KB DMA block is 16 rows x 64 bytes;
+// lane L fills row L/4, slot L%4 with global chunk (L%4) ^ ((L/16)%4), so a
+// fragment read (16 rows, one chunk) hits 16 distinct 16-byte bank groups.
+// The stages are separate LDS objects so the compiler's wait insertion can
+// tell a stage being read from the stages being filled.
+constexpr int DBK = 32;
+
+// Tile order for the large kernels. Blocks are dispatched round-robin over
+// the 8 XCDs, so XCD x runs blocks x, x+8, ...: each XCD gets a contiguous
+// run of logical tiles (tile-columns fastest), so tiles running together on
+// one XCD share A row-panels in its L2. (Grouping 8 tile-columns with
+// tile-rows fastest measured no better at these shapes.)
+__device__ __forceinline__ void tile_order(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nblk = tiles_m * tiles_n;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  tm = bid / tiles_n;
+  tn = bid - tm * tiles_n;
+}
+constexpr int DSTAGE = 2 * TB2 * DBK;  // u16 elements per stage (A then B)
+
+__device__ __forceinline__ int dswz(int row, int kc) { return row * DBK + ((kc ^ ((row >> 2) & 3)) << 3); }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
+#define WH_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// One 16-byte-per-lane direct global->LDS load into the 1 KB block at LDS
+// byte offset `lds` (wave-uniform): M0 holds the LDS base; one wait state is
+// required between writing M0 and the LDS-DMA load. Issued as inline assembly
+// so that the compiler's wait insertion leaves the ring's counting to us.
+typedef __attribute__((address_space(3))) u16* lds_u16_ptr;
+__device__ __forceinline__ uint32_t lds_addr(const u16* p) { return (uint32_t)(uintptr_t)(lds_u16_ptr)(p); }
+__device__ __forceinline__ void dma16(const u16* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) u16 st0[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st1[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st2[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st3[DSTAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles_n = (p.N + TB2 - 1) / TB2;
+  const int tiles_m = (p.M + TB2 - 1) / TB2;
+  int tm, tn;
+  tile_order(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int z = blockIdx.z;
+  const u16* A = (const u16*)p.A + (long)z * p.strideA;
+  const u16* B = (const u16*)p.B;
+  const int m0 = tm * TB2, n0 = tn * TB2;
+
+  // DMA: wave w fills A blocks w, w+8 and B blocks w, w+8 (16 rows each)
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const u16* ga0 = A + (long)min(m0 + wave * 16 + lr, p.M - 1) * p.lda + lc * 8;
+  const u16* ga1 = A + (long)min(m0 + (wave + 8) * 16 + lr, p.M - 1) * p.lda + lc * 8;
+  const u16* gb0 = B + (long)min(n0 + wave * 16 + lr, p.N - 1) * p.ldb + lc * 8;
+  const u16* gb1 = B + (long)min(n0 + (wave + 8) * 16 + lr, p.N - 1) * p.ldb + lc * 8;
+  const int la0 = wave * 16 * DBK, la1 = (wave + 8) * 16 * DBK;
+  const int lb0 = TB2 * DBK + wave * 16 * DBK, lb1 = TB2 * DBK + (wave + 8) * 16 * DBK;
+#define WH_ISSUE(S, k)                                                                         \
+  dma16(ga0 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + la0)));                        \
+  dma16(ga1 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + la1)));                        \
+  dma16(gb0 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + lb0)));                        \
+  dma16(gb1 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + lb1)));
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, kc = lane >> 4;
+  const int nk = p.K / DBK;
+  if (nk > 0) { WH_ISSUE(st0, 0) }
+  if (nk > 1) { WH_ISSUE(st1, DBK) }
+  if (nk > 2) { WH_ISSUE(st2, 2 * DBK) }
+
+#define WH_STEP(S, SN, t)                                                                             \
+  if ((t) < nk) {                                                                                     \
+    const int after = min(2, nk - 1 - (t));                                                           \
+    if (after == 2) { WH_WAIT_VM(8); } else if (after == 1) { WH_WAIT_VM(4); } else { WH_WAIT_VM(0); } \
+    __builtin_amdgcn_s_barrier();                                                                     \
+    if ((t) + 3 < nk) { WH_ISSUE(SN, ((t) + 3) * DBK) }                                               \
+    bf16x8 bf[4];                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                     \
+      bf[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + j * 16 + fr, kc)));   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                   \
+      const bf16x8 af = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                   \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);          \
+    }                                                                                                 \
+  }
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    WH_STEP(st0, st3, kt)
+    WH_STEP(st1, st0, kt + 1)
+    WH_STEP(st2, st1, kt + 2)
+    WH_STEP(st3, st2, kt + 3)
+  }
+#undef WH_STEP
+#undef WH_ISSUE
+  // epilogue straight from registers: with B as the first MFMA operand each
+  // lane holds C[m][n..n+3] for m = its fragment row, so it writes 4
+  // consecutive columns (the 4 lanes of a row cover 16 contiguous columns)
+  const int em = m0 + wm * 128 + (lane & 15), en = n0 + wn * 64 + (lane >> 4) * 4;
+  if constexpr (EPI == EPI_CROSSKV) {
+    // head-major scatter: destination offset = column part + row part
+    const int d = p.ckv_d, T_ = p.ckv_T, H_ = p.ckv_H;
+    long coff[4];
+    float4 cb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = min(en + j * 16, p.N - 4);
+      const int l = n / (2 * d), r = n - l * 2 * d;
+      const int kv = r / d, c = r - kv * d;
+      coff[j] = (((long)(l * 2 + kv) * p.ckv_B * H_ + (c >> 6)) * T_) * 64 + (c & 63);
+      cb[j] = p.bias ? *(const float4*)(p.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = em + i * 16;
+      if (m >= p.M) continue;
+      const int b = m / T_, t = m - b * T_;
+      const long roff = ((long)b * H_ * T_ + t) * 64;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (en + j * 16 + 4 > p.N) continue;
+        uint2 u;
+        u.x = (uint32_t)f2bf(acc[i][j][0] + cb[j].x) | ((uint32_t)f2bf(acc[i][j][1] + cb[j].y) << 16);
+        u.y = (uint32_t)f2bf(acc[i][j][2] + cb[j].z) | ((uint32_t)f2bf(acc[i][j][3] + cb[j].w) << 16);
+        *(uint2*)((u16*)p.C + coff[j] + roff) = u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = em + i * 16;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = en + j * 16;
+        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        if (n + 4 <= p.N) {
+          epi_store4<EPI>(p, z, m, n, v);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) epi_store<u16, EPI>(p, z, m, n + q, v[q]);
+        }
+      }
+    }
+  }
+}
+#undef WH_WAIT_VM
+
 // ------------------------------------------------------------------ bf16 skinny (decode rows)
 // Decoder GEMMs have M = batch rows (<= 128) and stream their weight once, so
 // they are bound by bytes in flight, not by MFMA. One workgroup owns 16*CB
@@ -278,11 +733,54 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
 hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (t == ACT_BF16) {
-    const int tiles = ((p.M + TB - 1) / TB) * ((p.N + TB - 1) / TB);
-    dim3 grid(tiles, 1, p.batch);
-#define CALL(E) hipLaunchKernelGGL(gemm_bf16_128<E>, grid, dim3(256), 0, s, p)
-    WH_EPI_SWITCH(epi, CALL)
+    const int tiles2 = ((p.M + TB2 - 1) / TB2) * ((p.N + TB2 - 1) / TB2);
+    const bool w4_ok = p.N % 8 == 0 &&
+                       (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_GELU_PE || epi == EPI_CROSSKV);
+    int v = p.variant;
+    if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (w4_ok ? 4 : 2) : 1;
+    if ((v == 3 || v == 4) && !w4_ok) v = 1;
+    if (v == 4) {
+      dim3 grid(tiles2, 1, p.batch);
+#define CALL(E) hipLaunchKernelGGL(gemm_bf16_dma<E>, grid, dim3(512), 0, s, p)
+      switch (epi) {
+        case EPI_STORE: CALL(EPI_STORE); break;
+        case EPI_GELU: CALL(EPI_GELU); break;
+        case EPI_GELU_PE: CALL(EPI_GELU_PE); break;
+        default: CALL(EPI_CROSSKV); break;
+      }
 #undef CALL
+      return hipGetLastError();
+    }
+    if (v == 2 && epi == EPI_DEC_QKV) v = 1;
+    if (v == 3) {
+      dim3 grid(tiles2, 1, p.batch);
+#define CALL(E) hipLaunchKernelGGL(gemm_bf16_256w4<E>, grid, dim3(256), 0, s, p)
+      switch (epi) {
+        case EPI_STORE: CALL(EPI_STORE); break;
+        case EPI_GELU: CALL(EPI_GELU); break;
+        case EPI_GELU_PE: CALL(EPI_GELU_PE); break;
+        default: CALL(EPI_CROSSKV); break;
+      }
+#undef CALL
+    } else if (v == 2) {
+      dim3 grid(tiles2, 1, p.batch);
+#define CALL(E) hipLaunchKernelGGL(gemm_bf16_256<E>, grid, dim3(512), 0, s, p)
+      switch (epi) {
+        case EPI_STORE: CALL(EPI_STORE); break;
+        case EPI_GELU: CALL(EPI_GELU); break;
+        case EPI_GELU_PE: CALL(EPI_GELU_PE); break;
+        case EPI_F32: CALL(EPI_F32); break;
+        case EPI_CROSSKV: CALL(EPI_CROSSKV); break;
+        default: return hipErrorInvalidValue;
+      }
+#undef CALL
+    } else {
+      const int tiles = ((p.M + TB - 1) / TB) * ((p.N + TB - 1) / TB);
+      dim3 grid(tiles, 1, p.batch);
+#define CALL(E) hipLaunchKernelGGL(gemm_bf16_128<E>, grid, dim3(256), 0, s, p)
+      WH_EPI_SWITCH(epi, CALL)
+#undef CALL
+    }
   } else {
     const int tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
     dim3 grid(tiles, 1, p.batch);

@@ -34,6 +34,9 @@ struct GemmParams {
   // EPI_DEC_QKV
   uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
   int kv_cap, kv_B, kv_H, kv_layer, d_model;
+  // tiled-kernel choice for measurement: 0 automatic, 1 128x128, 2 256x256/8 waves, 3 256x256/4 waves,
+  // 4 256x256 with the LDS DMA pipeline
+  int variant;
 };
 
 hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
