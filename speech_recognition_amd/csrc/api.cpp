@@ -57,11 +57,17 @@ whisper_status check_dims(const whisper_dims* d) {
 
 // ------------------------------------------------------------------ packed layout
 struct EncL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, w1, b1, w2, b2; };
-struct DecL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, wqc, bqc, woc, boc, ln3g, ln3b, w1, b1, w2, b2; };
+// In bf16 mode the LayerNorm-consumer weights of the decoder (wqkv, wqc, w1
+// and the vocabulary projection lmw) are stored gamma-folded, their biases
+// beta-folded, with the row sums c1* beside them (see decode_gemm.hip).
+struct DecL {
+  size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, wqc, bqc, woc, boc, ln3g, ln3b, w1, b1, w2, b2;
+  size_t c1qkv = 0, c1qc = 0, c1w1 = 0;
+};
 struct Packed {
   size_t conv1w = 0, conv1b = 0, conv2w = 0, conv2b = 0, pe = 0, lnpg = 0, lnpb = 0;
   std::vector<EncL> enc;
-  size_t tok = 0, pos = 0, ckvw = 0, ckvb = 0, lnfg = 0, lnfb = 0;
+  size_t tok = 0, pos = 0, ckvw = 0, ckvb = 0, lnfg = 0, lnfb = 0, lmw = 0, lmc1 = 0, lmb2 = 0;
   std::vector<DecL> dec;
   size_t total = 0;
 };
@@ -101,11 +107,19 @@ Packed layout(const whisper_dims* d) {
       L.ln3g = take(D * f4); L.ln3b = take(D * f4);
       L.w1 = take(F * D * e); L.b1 = take(F * f4);
       L.w2 = take(D * F * e); L.b2 = take(D * f4);
+      if (d->act == WHISPER_BF16) {
+        L.c1qkv = take(3 * D * f4); L.c1qc = take(D * f4); L.c1w1 = take(F * f4);
+      }
       P.dec.push_back(L);
     }
     P.ckvw = take((size_t)d->n_dec_layers * 2 * D * D * e);
     P.ckvb = take((size_t)d->n_dec_layers * 2 * D * f4);
     P.lnfg = take(D * f4); P.lnfb = take(D * f4);
+    if (d->act == WHISPER_BF16) {
+      P.lmw = take((size_t)d->n_vocab * D * e);
+      P.lmc1 = take((size_t)d->n_vocab * f4);
+      P.lmb2 = take((size_t)d->n_vocab * f4);
+    }
   }
   P.total = off;
   return P;
@@ -269,6 +283,66 @@ whisper_status check_ws(void* ws, size_t have, size_t need, const char* what) {
   return WHISPER_OK;
 }
 
+// Decoder step in bf16 with the residual + LayerNorm folded into the GEMMs:
+// 9 launches per layer (QKV + cache append, self-attention, out-proj +
+// residual, cross-query, cross-attention and its combine, cross-out +
+// residual, MLP up, MLP down + residual), then the vocabulary projection and
+// the argmax. The residual stream stays fp32.
+whisper_status decode_step_fused(const whisper_dims* d, const void* packed, const Packed& P, const DecWS& W, int B,
+                                 int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                 const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
+                                 int32_t* dev_error, void* ws, hipStream_t s) {
+  const int D = d->d_model, H = d->n_heads, T = d->n_audio_ctx, F = d->d_ffn, L = d->n_dec_layers;
+  float* X = at<float>(ws, W.x);
+  u16_t* Q = at<u16_t>(ws, W.q);
+  u16_t* ATT = at<u16_t>(ws, W.att);
+  u16_t* QC = at<u16_t>(ws, W.qc);
+  u16_t* HF = at<u16_t>(ws, W.hf);
+  float* CR = at<float>(ws, W.cross);
+  WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
+                      d->n_text_ctx, cap, X, dev_error, s));
+  auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
+                  u16_t* out, float* out_f32, int layer) {
+    DecGemmParams g{};
+    g.M = B; g.N = N; g.K = K;
+    g.W = at<u16_t>(packed, w_off);
+    g.bias = b_off ? at<float>(packed, b_off) : nullptr;
+    g.c1 = c1_off ? at<float>(packed, c1_off) : nullptr;
+    g.A = A; g.lda = K; g.X = X; g.out = out; g.out_f32 = out_f32;
+    g.kv_cache = kv_cache; g.kv_scales = kv_scales; g.lengths = lengths; g.dev_error = dev_error;
+    g.kv_cap = cap; g.kv_B = B; g.kv_H = H; g.kv_layer = layer; g.d_model = D;
+    int mb, cb;
+    dec_gemm_tiles(B, N, mb, cb);
+    return launch_gemm_dec(pro, epi, g, mb, cb, s);
+  };
+  const size_t kv_layer = (size_t)2 * B * H * cap * 64;
+  const size_t ckv_layer = (size_t)2 * B * H * T * 64 * 2;
+  for (int l = 0; l < L; ++l) {
+    const DecL& Lw = P.dec[l];
+    WH_TRY(gemm(PRO_X, DEPI_QKV, Lw.wqkv, Lw.bqkv, Lw.c1qkv, 3 * D, D, nullptr, Q, nullptr, l));
+    const uint8_t* kc = kv_cache + l * kv_layer;
+    {
+      ProfScope ps(WHISPER_PROF_DECODE_SELF_ATTENTION, s);
+      WH_TRY(launch_attn_decode_self(ACT_BF16, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap,
+                                     ATT, s));
+    }
+    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.wo, Lw.bo, 0, D, D, ATT, nullptr, nullptr, l));
+    WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));
+    const char* ck = (const char*)cross_kv + l * ckv_layer;
+    {
+      ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
+      WH_TRY(launch_attn_decode_cross_partial(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, CR, s));
+    }
+    WH_TRY(launch_attn_decode_cross_combine(ACT_BF16, CR, B, H, ATT, s));
+    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
+    WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
+    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l));
+  }
+  WH_TRY(gemm(PRO_X, DEPI_F32, P.lmw, P.lmb2, P.lmc1, d->n_vocab, D, nullptr, nullptr, LG, 0));
+  WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
+  return WHISPER_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -357,6 +431,7 @@ whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w
     WH_TRY(cpy(w[i++], P.lnpb, D));
   }
   if (d->n_dec_layers > 0) {
+    const float* tok_logical = w[i];
     WH_TRY(cvt(w[i++], P.tok, (size_t)d->n_vocab * D));
     WH_TRY(cvt(w[i++], P.pos, (size_t)d->n_text_ctx * D));
     for (int l = 0; l < d->n_dec_layers; ++l) {
@@ -377,8 +452,25 @@ whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w
       WH_TRY(cpy(w[i + 18], L.ln3g, D)); WH_TRY(cpy(w[i + 19], L.ln3b, D));
       WH_TRY(cvt(w[i + 20], L.w1, F * D)); WH_TRY(cpy(w[i + 21], L.b1, F));
       WH_TRY(cvt(w[i + 22], L.w2, D * F)); WH_TRY(cpy(w[i + 23], L.b2, D));
+      if (t == ACT_BF16) {  // fold ln1 into q/k/v, ln2 into the cross query, ln3 into the MLP up-projection
+        const size_t DD = D * D * e;
+        float* c1 = at<float>(packed, L.c1qkv);
+        float* bq = at<float>(packed, L.bqkv);
+        WH_TRY(launch_fold_ln(w[i + 2], w[i + 0], w[i + 1], w[i + 3], D, D, at<void>(packed, L.wqkv), c1, bq, s));
+        WH_TRY(launch_fold_ln(w[i + 4], w[i + 0], w[i + 1], nullptr, D, D, at<void>(packed, L.wqkv + DD), c1 + D,
+                              bq + D, s));
+        WH_TRY(launch_fold_ln(w[i + 5], w[i + 0], w[i + 1], w[i + 6], D, D, at<void>(packed, L.wqkv + 2 * DD),
+                              c1 + 2 * D, bq + 2 * D, s));
+        WH_TRY(launch_fold_ln(w[i + 11], w[i + 9], w[i + 10], w[i + 12], D, D, at<void>(packed, L.wqc),
+                              at<float>(packed, L.c1qc), at<float>(packed, L.bqc), s));
+        WH_TRY(launch_fold_ln(w[i + 20], w[i + 18], w[i + 19], w[i + 21], F, D, at<void>(packed, L.w1),
+                              at<float>(packed, L.c1w1), at<float>(packed, L.b1), s));
+      }
       i += 24;
     }
+    if (t == ACT_BF16)  // final LayerNorm folded into a copy of the (tied) token embedding
+      WH_TRY(launch_fold_ln(tok_logical, w[i], w[i + 1], nullptr, d->n_vocab, D, at<void>(packed, P.lmw),
+                            at<float>(packed, P.lmc1), at<float>(packed, P.lmb2), s));
     WH_TRY(cpy(w[i++], P.lnfg, D));
     WH_TRY(cpy(w[i++], P.lnfb, D));
   }
@@ -500,6 +592,8 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   void* HF = at<void>(ws, W.hf);
   float* LG = logits ? logits : at<float>(ws, W.logits);
   float* CR = at<float>(ws, W.cross);
+  if (t == ACT_BF16) return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv,
+                                              LG, argmax, dev_error, ws, s);
   WH_TRY(launch_embed(t, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s));
   const size_t kv_layer = (size_t)2 * B * H * cap * 64;

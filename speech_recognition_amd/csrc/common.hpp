@@ -25,6 +25,14 @@ __device__ __forceinline__ u16 f2bf(float f) {
   return (u16)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair with the gfx950 converter (round to nearest
+// even, like f2bf on non-NaN inputs): low half from a, high half from b.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // Storage type traits: activations are bf16 (u16 bits) or fp32.
 template <typename T> struct Act;
 template <> struct Act<u16> {

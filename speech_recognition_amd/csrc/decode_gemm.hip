@@ -1,0 +1,380 @@
+// GEMMs of the batched decoder step (M = batch rows <= 128), with the
+// residual + LayerNorm of the whisper_blaze showcase page's layernorm_fused.cu
+// card folded into them.
+//
+// At batch 64 each of these GEMMs streams a weight matrix once (3.3-13 MB)
+// against a small activation block, so its time is set by how many dependent
+// memory round trips a workgroup makes, not by bandwidth. The kernel is built
+// to make one:
+//  * a workgroup of 8 waves owns 16*CB output columns and 16*MB rows; the 8
+//    waves split K among themselves, and every wave issues all of its weight
+//    and activation loads (straight into MFMA operand registers) before its
+//    first MFMA;
+//  * the 8 partial tiles are summed through LDS in wave order (deterministic),
+//    and one wave runs the epilogue. No global partials, counters or fences.
+//
+// LayerNorm folding. For y = LN(x) W^T + b with LN(x)_k = (x_k - mu) r g_k + be_k:
+//    y_n = r * (sum_k x_k W'_nk - mu * c1_n) + b2_n,
+//    W'_nk = bf16(g_k W_nk),  c1_n = sum_k W'_nk,  b2_n = b_n + sum_k be_k W_nk.
+// W', c1 and b2 are made once when the weights are packed (fold_ln_kernel).
+// The GEMM then reads the fp32 residual stream x directly, splits each value
+// into bf16 hi + lo parts (two MFMAs, ~2^-17 relative error), and computes the
+// row mean mu and r = 1/sqrt(var + eps) itself: the workgroup holds whole rows
+// of x, so the statistics come from registers (per-lane sums shifted by the
+// lane's first value, turned into a mean and a sum of squared deviations and
+// merged across lanes and waves with the pairwise update of Chan, Golub and
+// LeVeque). Since c1
+// is summed from the rounded W', the fold cancels the mean exactly up to fp32
+// accumulation error.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace wh {
+
+constexpr int DG_WAVES = 8;
+constexpr int DG_REG_BUDGET = 176;  // VGPRs per lane for in-flight operand loads plus accumulators
+
+// Registers one k-step of operand loads takes per lane, and how many k-steps
+// fit in one batch of in-flight loads.
+template <int PRO, int MB, int CB>
+struct DecStep {
+  static constexpr int REGS = (PRO == PRO_X ? MB * 8 : MB * 4) + CB * 4;
+  static constexpr int FREE = DG_REG_BUDGET - 4 * MB * CB;
+  static constexpr bool fits(int nj) { return nj * REGS <= FREE; }
+};
+
+// NJ: k-steps per batch, fixed at compile time so that a batch is straight-line
+// code whose loads are all in flight together (a guarded, variable-length batch
+// makes the compiler wait for each step's loads before issuing the next).
+// Every wave runs a whole number of batches: the host picks NJ with
+// (K / 32) % (8 * NJ) == 0, or NJ = 1.
+template <int PRO, int EPI, int MB, int CB, int NJ>
+__global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
+  constexpr int MR = MB * 16;
+  constexpr bool XIN = PRO == PRO_X;
+  __shared__ f32x4 red[DG_WAVES - 1][MB * CB][64];
+  __shared__ float2 s_st[XIN ? DG_WAVES : 1][MR];
+  __shared__ float s_mu[MR], s_rs[MR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16 * CB, m0 = blockIdx.y * MR;
+  const int M = p.M, N = p.N, K = p.K;
+  const int S = K / 32;
+  const int s0 = wave * S / DG_WAVES, s1 = (wave + 1) * S / DG_WAVES;  // this wave's k-steps
+  const int nsteps = s1 - s0;
+  const int kq = (lane >> 4) * 8;
+
+  const u16* wrow[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) wrow[cb] = p.W + (long)min(n0 + cb * 16 + (lane & 15), N - 1) * K + kq;
+  long arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1);
+
+  // ---- epilogue operands, fetched before the main loads so that the epilogue
+  // (run by wave 0) makes no memory round trip of its own: its stores may
+  // alias these addresses, so loads left in the store loop would serialise.
+  constexpr bool RES = EPI == DEPI_RESID, QKV = EPI == DEPI_QKV;
+  float e_bias[CB], e_c1[CB];
+  float e_x[RES ? MB : 1][RES ? CB : 1][4];
+  int e_pos[QKV ? MB : 1][4];
+  float e_inv[2] = {0.f, 0.f};
+  if (wave == 0) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = min(n0 + cb * 16 + (lane & 15), N - 1);
+      e_bias[cb] = p.bias ? p.bias[n] : 0.f;
+      e_c1[cb] = XIN ? p.c1[n] : 0.f;
+      if constexpr (RES) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e_x[mb][cb][r] = p.X[(long)min(m0 + mb * 16 + (lane >> 4) * 4 + r, M - 1) * N + n];
+      }
+    }
+    if constexpr (QKV) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e_pos[mb][r] = p.lengths[min(m0 + mb * 16 + (lane >> 4) * 4 + r, M - 1)];
+      e_inv[0] = 1.0f / p.kv_scales[p.kv_layer * 2];
+      e_inv[1] = 1.0f / p.kv_scales[p.kv_layer * 2 + 1];
+    }
+  }
+
+  f32x4 acc[MB][CB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[mb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float st_c[MB], st_s1[MB], st_s2[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) st_c[mb] = st_s1[mb] = st_s2[mb] = 0.f;
+
+  for (int b0 = 0; b0 < nsteps; b0 += NJ) {
+    uint4 wv[NJ][CB];
+    float4 xa[XIN ? NJ : 1][MB], xb[XIN ? NJ : 1][MB];
+    uint4 av[XIN ? 1 : NJ][MB];
+    // ---- issue every load of the batch
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int k = (s0 + b0 + j) * 32;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) wv[j][cb] = *(const uint4*)(wrow[cb] + k);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (XIN) {
+          const float* x = p.X + arow[mb] * K + k + kq;
+          xa[j][mb] = *(const float4*)x;
+          xb[j][mb] = *(const float4*)(x + 4);
+        } else {
+          av[j][mb] = *(const uint4*)(p.A + arow[mb] * p.lda + k + kq);
+        }
+      }
+    }
+    // keep the scheduler from interleaving the loads with the MFMAs below (it
+    // would trade in-flight loads for registers and serialise the batch)
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- MFMAs (and, for the fp32 residual input, the row moments)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (XIN) {
+          const float v[8] = {xa[j][mb].x, xa[j][mb].y, xa[j][mb].z, xa[j][mb].w,
+                              xb[j][mb].x, xb[j][mb].y, xb[j][mb].z, xb[j][mb].w};
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hi[i] = f2bf2(v[2 * i], v[2 * i + 1]);
+            lo[i] = f2bf2(v[2 * i] - __uint_as_float(hi[i] << 16), v[2 * i + 1] - __uint_as_float(hi[i] & 0xffff0000u));
+          }
+          const bf16x8 ah = bitcast<bf16x8>(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+          const bf16x8 al = bitcast<bf16x8>(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bitcast<bf16x8>(wv[j][cb]), acc[mb][cb], 0, 0, 0);
+            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bitcast<bf16x8>(wv[j][cb]), acc[mb][cb], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[j][mb]), bitcast<bf16x8>(wv[j][cb]),
+                                                                  acc[mb][cb], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (XIN) {
+      // shifted sums: S1 += x - c, S2 += (x - c)^2 with c = this lane's first value of the row
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (b0 == 0) st_c[mb] = xa[0][mb].x;
+        const float c = st_c[mb];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const float4 a = xa[j][mb], e = xb[j][mb];
+          const float d[8] = {a.x - c, a.y - c, a.z - c, a.w - c, e.x - c, e.y - c, e.z - c, e.w - c};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            st_s1[mb] += d[i];
+            st_s2[mb] = fmaf(d[i], d[i], st_s2[mb]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- row moments: per lane (mean, M2) from the shifted sums, merged over the
+  // 4 lanes holding a row (equal counts), published per wave
+  if constexpr (XIN) {
+    const float n = 8.f * nsteps, inv_n = nsteps ? 1.f / n : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float mu = st_c[mb] + st_s1[mb] * inv_n;
+      float m2 = fmaxf(st_s2[mb] - st_s1[mb] * st_s1[mb] * inv_n, 0.f);
+      float cnt = n;
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float mu2 = __shfl_xor(mu, o, 64), m22 = __shfl_xor(m2, o, 64);
+        const float d = mu - mu2;
+        mu = 0.5f * (mu + mu2);
+        m2 = (m2 + m22) + d * d * (0.5f * cnt);
+        cnt *= 2.f;
+      }
+      if (lane < 16) s_st[wave][mb * 16 + lane] = make_float2(mu, m2);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) red[wave - 1][mb * CB + cb][lane] = acc[mb][cb];
+  }
+  __syncthreads();
+  if constexpr (XIN) {
+    if (tid < MR) {
+      float mu = 0.f, m2 = 0.f;
+#pragma unroll
+      for (int w = 0; w < DG_WAVES; ++w) mu += (32.f * ((w + 1) * S / DG_WAVES - w * S / DG_WAVES)) * s_st[w][tid].x;
+      mu *= 1.0f / (32.f * S);
+#pragma unroll
+      for (int w = 0; w < DG_WAVES; ++w) {
+        const float2 sw = s_st[w][tid];
+        const float d = sw.x - mu;
+        m2 += sw.y + (32.f * ((w + 1) * S / DG_WAVES - w * S / DG_WAVES)) * d * d;
+      }
+      s_mu[tid] = mu;
+      s_rs[tid] = 1.0f / sqrtf(m2 * (1.0f / (32.f * S)) + 1e-5f);
+    }
+    __syncthreads();
+  }
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < DG_WAVES - 1; ++w)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[mb][cb] += red[w][mb * CB + cb][lane];
+
+  // ---- epilogue: lane holds rows mb*16 + (lane>>4)*4 + r, column cb*16 + (lane&15)
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = n0 + cb * 16 + (lane & 15);
+    if (n >= N) continue;
+    const float bias = e_bias[cb], c1 = e_c1[cb];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ml = mb * 16 + (lane >> 4) * 4 + r, m = m0 + ml;
+        if (m >= M) continue;
+        float v = acc[mb][cb][r];
+        v = XIN ? s_rs[ml] * (v - s_mu[ml] * c1) + bias : v + bias;
+        if constexpr (EPI == DEPI_RESID) {
+          p.X[(long)m * N + n] = e_x[RES ? mb : 0][RES ? cb : 0][r] + v;
+        } else if constexpr (EPI == DEPI_F32) {
+          p.out_f32[(long)m * N + n] = v;
+        } else if constexpr (EPI == DEPI_STORE) {
+          p.out[(long)m * N + n] = f2bf(v);
+        } else if constexpr (EPI == DEPI_GELU) {
+          p.out[(long)m * N + n] = f2bf(gelu_erf(v));
+        } else if constexpr (EPI == DEPI_QKV) {
+          // q -> bf16; k, v -> e4m3 codes at cache slot lengths[m]
+          const int d = p.d_model;
+          if (n < d) {
+            p.out[(long)m * d + n] = f2bf(v);
+          } else {
+            const int kv = (n - d) / d, c = (n - d) - kv * d, pos = e_pos[QKV ? mb : 0][r];
+            if (pos >= 0 && pos < p.kv_cap) {
+              const long idx =
+                  ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
+              p.kv_cache[idx] = (uint8_t)e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
+            } else if (p.dev_error) {
+              *p.dev_error = 6;  // capacity exceeded: the write is skipped
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int PRO, int EPI, int MB, int CB, int NJ>
+static hipError_t dec_launch_nj(const DecGemmParams& p, hipStream_t s) {
+  if constexpr (!DecStep<PRO, MB, CB>::fits(NJ)) {
+    return hipErrorInvalidValue;
+  } else {
+    const dim3 grid((p.N + 16 * CB - 1) / (16 * CB), (p.M + 16 * MB - 1) / (16 * MB));
+    hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NJ>), grid, dim3(DG_WAVES * 64), 0, s, p);
+    return hipGetLastError();
+  }
+}
+
+// Largest batch (10 or 5 k-steps) that divides every wave's share of K and
+// fits the register budget; 1 otherwise.
+template <int PRO, int EPI, int MB, int CB>
+static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
+  const int S = p.K / 32;
+  if (S % (DG_WAVES * 10) == 0 && DecStep<PRO, MB, CB>::fits(10)) return dec_launch_nj<PRO, EPI, MB, CB, 10>(p, s);
+  if (S % (DG_WAVES * 5) == 0 && DecStep<PRO, MB, CB>::fits(5)) return dec_launch_nj<PRO, EPI, MB, CB, 5>(p, s);
+  return dec_launch_nj<PRO, EPI, MB, CB, 1>(p, s);
+}
+
+// Tile shapes with MB * CB <= 4 (larger ones run out of registers).
+template <int PRO, int EPI>
+static hipError_t dec_launch(const DecGemmParams& p, int mb, int cb, hipStream_t s) {
+  if (cb == 1 && mb == 1) return dec_launch_t<PRO, EPI, 1, 1>(p, s);
+  if (cb == 1 && mb == 2) return dec_launch_t<PRO, EPI, 2, 1>(p, s);
+  if (cb == 1 && mb == 4) return dec_launch_t<PRO, EPI, 4, 1>(p, s);
+  if (cb == 2 && mb == 1) return dec_launch_t<PRO, EPI, 1, 2>(p, s);
+  if (cb == 2 && mb == 2) return dec_launch_t<PRO, EPI, 2, 2>(p, s);
+  if (cb == 4 && mb == 1) return dec_launch_t<PRO, EPI, 1, 4>(p, s);
+  return hipErrorInvalidValue;
+}
+
+// Rows (16 * mb) and columns (16 * cb) per workgroup. One 16-row block per
+// workgroup keeps the activation slice a workgroup streams small (it is
+// re-read by every column tile); 64 columns for N of 2K-4K (about one
+// workgroup per CU at batch 64), 32 otherwise. Chosen by measurement at batch 64.
+void dec_gemm_tiles(int M, int N, int& mb, int& cb) {
+  (void)M;
+  mb = 1;
+  cb = (N >= 2048 && N <= 4096) || N > 16384 ? 4 : 2;
+}
+
+hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s) {
+  if (p.M <= 0 || p.M > 128 || p.N <= 0 || p.K <= 0 || p.K % 32) return hipErrorInvalidValue;
+  if (pro == PRO_X) {
+    switch (epi) {
+      case DEPI_QKV: return dec_launch<PRO_X, DEPI_QKV>(p, mb, cb, s);
+      case DEPI_STORE: return dec_launch<PRO_X, DEPI_STORE>(p, mb, cb, s);
+      case DEPI_GELU: return dec_launch<PRO_X, DEPI_GELU>(p, mb, cb, s);
+      case DEPI_F32: return dec_launch<PRO_X, DEPI_F32>(p, mb, cb, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (epi) {
+    case DEPI_RESID: return dec_launch<PRO_A, DEPI_RESID>(p, mb, cb, s);
+    case DEPI_STORE: return dec_launch<PRO_A, DEPI_STORE>(p, mb, cb, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Weight packing for a LayerNorm-consumer GEMM (one workgroup per output row
+// n): W'[n,k] = bf16(gamma_k W[n,k]), c1[n] = sum_k W'[n,k],
+// b2[n] = bias[n] + sum_k beta_k W[n,k]; sums in fp64.
+__global__ __launch_bounds__(256) void fold_ln_kernel(const float* W, const float* gamma, const float* beta,
+                                                      const float* bias, int K, u16* Wf, float* c1, float* b2) {
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const float* w = W + (long)n * K;
+  double s1 = 0.0, s2 = 0.0;
+  for (int k = tid; k < K; k += 256) {
+    const u16 f = f2bf(gamma[k] * w[k]);
+    Wf[(long)n * K + k] = f;
+    s1 += (double)bf2f(f);
+    s2 += (double)beta[k] * (double)w[k];
+  }
+  __shared__ double r1[256], r2[256];
+  r1[tid] = s1;
+  r2[tid] = s2;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) {
+      r1[tid] += r1[tid + o];
+      r2[tid] += r2[tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    c1[n] = (float)r1[0];
+    b2[n] = (float)((bias ? (double)bias[n] : 0.0) + r2[0]);
+  }
+}
+
+hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
+                          void* Wf, float* c1, float* b2, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_ln_kernel, dim3(N), dim3(256), 0, s, W, gamma, beta, bias, K, (u16*)Wf, c1, b2);
+  return hipGetLastError();
+}
+
+}  // namespace wh

@@ -478,6 +478,8 @@ __device__ __forceinline__ int dswz(int row, int kc) { return row * DBK + ((kc ^
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
 #define WH_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// the same, and lgkmcnt(0): this wave's LDS reads have completed
+#define WH_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
 // One 16-byte-per-lane direct global->LDS load into the 1 KB block at LDS
 // byte offset `lds` (wave-uniform): M0 holds the LDS base; one wait state is
@@ -528,32 +530,58 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
 
   const int fr = lane & 15, kc = lane >> 4;
   const int nk = p.K / DBK;
+  // fragment registers, two sets: stage t+1's fragments are read while stage
+  // t's MFMAs run from the other set
+  bf16x8 a0[8], b0[4], a1[8], b1[4];
+#define WH_READ(S, AF, BF)                                                                    \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+    BF[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + j * 16 + fr, kc))); \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+    AF[i] = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));
+#define WH_MFMA(AF, BF)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(BF[j], AF[i], acc[i][j], 0, 0, 0);
+  // wait until this wave's loads of stage `t` have landed (vmcnt counts the
+  // later stages' loads still allowed in flight) and its own LDS reads are
+  // complete, then meet the other waves
+#define WH_SYNC(t)                                                                            \
+  {                                                                                           \
+    const int after = min(2, nk - 1 - (t));                                                   \
+    if (after == 2) { WH_WAIT_VM_LGKM0(8); } else if (after == 1) { WH_WAIT_VM_LGKM0(4); }    \
+    else { WH_WAIT_VM_LGKM0(0); }                                                             \
+    __builtin_amdgcn_s_barrier();                                                             \
+  }
+
   if (nk > 0) { WH_ISSUE(st0, 0) }
   if (nk > 1) { WH_ISSUE(st1, DBK) }
   if (nk > 2) { WH_ISSUE(st2, 2 * DBK) }
+  WH_SYNC(0)
+  if (nk > 3) { WH_ISSUE(st3, 3 * DBK) }
+  WH_READ(st0, a0, b0)
 
-#define WH_STEP(S, SN, t)                                                                             \
-  if ((t) < nk) {                                                                                     \
-    const int after = min(2, nk - 1 - (t));                                                           \
-    if (after == 2) { WH_WAIT_VM(8); } else if (after == 1) { WH_WAIT_VM(4); } else { WH_WAIT_VM(0); } \
-    __builtin_amdgcn_s_barrier();                                                                     \
-    if ((t) + 3 < nk) { WH_ISSUE(SN, ((t) + 3) * DBK) }                                               \
-    bf16x8 bf[4];                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                     \
-      bf[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + j * 16 + fr, kc)));   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                   \
-      const bf16x8 af = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));    \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                   \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);          \
-    }                                                                                                 \
+  // step t: stage t's fragments are in (AC, BC); make stage t+1 ready, refill
+  // the buffer stage t came from with tile t+4, read stage t+1's fragments
+  // into (AN, BN), then run stage t's MFMAs
+#define WH_STEP(SN, SREFILL, AC, BC, AN, BN, t)                                               \
+  if ((t) < nk) {                                                                             \
+    if ((t) + 1 < nk) {                                                                       \
+      WH_SYNC((t) + 1)                                                                        \
+      if ((t) + 4 < nk) { WH_ISSUE(SREFILL, ((t) + 4) * DBK) }                                \
+      WH_READ(SN, AN, BN)                                                                     \
+    }                                                                                         \
+    WH_MFMA(AC, BC)                                                                           \
   }
 
   for (int kt = 0; kt < nk; kt += 4) {
-    WH_STEP(st0, st3, kt)
-    WH_STEP(st1, st0, kt + 1)
-    WH_STEP(st2, st1, kt + 2)
-    WH_STEP(st3, st2, kt + 3)
+    WH_STEP(st1, st0, a0, b0, a1, b1, kt)
+    WH_STEP(st2, st1, a1, b1, a0, b0, kt + 1)
+    WH_STEP(st3, st2, a0, b0, a1, b1, kt + 2)
+    WH_STEP(st0, st3, a1, b1, a0, b0, kt + 3)
   }
+#undef WH_READ
+#undef WH_MFMA
+#undef WH_SYNC
 #undef WH_STEP
 #undef WH_ISSUE
   // epilogue straight from registers: with B as the first MFMA operand each
@@ -608,6 +636,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
   }
 }
 #undef WH_WAIT_VM
+#undef WH_WAIT_VM_LGKM0
 
 // ------------------------------------------------------------------ bf16 skinny (decode rows)
 // Decoder GEMMs have M = batch rows (<= 128) and stream their weight once, so

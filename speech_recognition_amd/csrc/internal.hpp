@@ -9,6 +9,7 @@
 namespace wh {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+typedef uint16_t u16_t;
 
 // ------------------------------------------------------------------ GEMM
 // C = epilogue(A[M,K] . B[N,K]^T + bias); A rows may overlap (lda < K) for
@@ -42,6 +43,29 @@ struct GemmParams {
 hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
 // Skinny path for decode (M <= 128): weights streamed once, K split over waves.
 hipError_t launch_gemm_skinny(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
+
+// ------------------------------------------------------------------ decoder-step GEMMs (bf16, M <= 128)
+// PRO_A: A is a bf16 activation block. PRO_X: A = LayerNorm(X) of the fp32
+// residual stream, folded into W (gamma), c1 and the bias (beta).
+enum DecPro { PRO_A = 0, PRO_X = 1 };
+enum DecEpi { DEPI_STORE = 0, DEPI_GELU = 1, DEPI_RESID = 2, DEPI_QKV = 3, DEPI_F32 = 4 };
+struct DecGemmParams {
+  int M, N, K;
+  const u16_t* W;            // [N, K] bf16 (PRO_X: gamma-folded)
+  const float* bias;         // [N] or NULL (PRO_X: folded bias b + W beta)
+  const float* c1;           // PRO_X: [N] row sums of the folded W
+  const u16_t* A; long lda;  // PRO_A: [M, K] bf16, row stride lda
+  float* X;                  // residual stream [M, d] fp32: PRO_X input, DEPI_RESID in/out
+  u16_t* out;                // DEPI_STORE / GELU: [M, N] bf16; DEPI_QKV: q [M, d]
+  float* out_f32;            // DEPI_F32: [M, N]
+  // DEPI_QKV: k, v appended as e4m3 codes at slot lengths[m]
+  uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
+  int kv_cap, kv_B, kv_H, kv_layer, d_model;
+};
+void dec_gemm_tiles(int M, int N, int& mb, int& cb);
+hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
+hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
+                          void* Wf, float* c1, float* b2, hipStream_t s);
 
 // ------------------------------------------------------------------ LayerNorm
 // h is in the activation type (or fp32 when h_f32); residual and total are the
