@@ -43,6 +43,27 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def counted_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when that
+    summary is missing or the kernel's sources changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{kernel.split('_kernel')[0]}_hbm_counters.md")
+    try:
+        text = open(path).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            with open(os.path.join(here, f), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if rec.get("kernel") != kernel or h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -190,7 +211,8 @@ def main():
         "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
         "roofline": {"kernel": "attn_decode_cross_kernel (decoder cross-attention, split-T partial)",
                      "bound": "hbm", "achieved": round(cross_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(cross_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(cross_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic("attn_decode_cross_kernel"),
                      "bytes_per_launch": cross_bytes, "avg_launch_us": round(cross_ms * 1e3, 2),
                      "launches_timed": n_rec},
         "kernels": kernels,
