@@ -102,6 +102,17 @@ def _p(x):
     return x.data_ptr()
 
 
+def _dtype_check(name, t, dt):
+    """A torch tensor passed where the call's whisper_dtype fixes the element
+    type must have that type (a silent mismatch reinterprets the bytes)."""
+    if t is None or isinstance(t, int) or not hasattr(t, "dtype"):
+        return
+    import torch
+    want = {WHISPER_F32: torch.float32, WHISPER_BF16: torch.bfloat16}.get(dt)
+    if want is not None and t.dtype != want:
+        raise WhisperError(3, f"{name}: tensor dtype {t.dtype} does not match whisper dtype {want}")
+
+
 def _stream(s):
     if s is not None:
         return s if isinstance(s, int) else s.cuda_stream
@@ -183,11 +194,13 @@ def whisper_decode_step(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, 
 
 
 def whisper_fp8_quantize(x, dt, n, scale_in, codes, scale_out, ws=None, ws_bytes=0, stream=None):
+    _dtype_check("whisper_fp8_quantize x", x, dt)
     _check(lib().whisper_fp8_quantize(_p(x), dt, n, _p(scale_in), _p(codes), _p(scale_out), _p(ws), ws_bytes,
                                       _stream(stream)))
 
 
 def whisper_fp8_dequantize(codes, n, scale, y, dt, stream=None):
+    _dtype_check("whisper_fp8_dequantize y", y, dt)
     _check(lib().whisper_fp8_dequantize(_p(codes), n, _p(scale), _p(y), dt, _stream(stream)))
 
 
@@ -198,19 +211,27 @@ def whisper_layernorm_fused(dims, h, residual, gamma, beta, eps, M, normed, tota
 
 
 def whisper_linear(dt, x, lda, w, bias, M, N, K, act, y, path=0, stream=None):
+    for nm, t in (("x", x), ("w", w), ("y", y)):
+        _dtype_check("whisper_linear " + nm, t, dt)
     _check(lib().whisper_linear(dt, _p(x), lda, _p(w), _p(bias), M, N, K, act, _p(y), path, _stream(stream)))
 
 
 def whisper_attention_encoder(dt, qkv, batch, T, n_heads, out, stream=None):
+    _dtype_check("whisper_attention_encoder qkv", qkv, dt)
+    _dtype_check("whisper_attention_encoder out", out, dt)
     _check(lib().whisper_attention_encoder(dt, _p(qkv), batch, T, n_heads, _p(out), _stream(stream)))
 
 
 def whisper_attention_decode_self(dt, q, batch, n_heads, cap, k_codes, v_codes, scales, n_keys, out, stream=None):
+    _dtype_check("whisper_attention_decode_self q", q, dt)
+    _dtype_check("whisper_attention_decode_self out", out, dt)
     _check(lib().whisper_attention_decode_self(dt, _p(q), batch, n_heads, cap, _p(k_codes), _p(v_codes),
                                                _p(scales), _p(n_keys), _p(out), _stream(stream)))
 
 
 def whisper_attention_decode_cross(dt, q, k, v, batch, n_heads, T, out, ws, ws_bytes, stream=None):
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _dtype_check("whisper_attention_decode_cross " + nm, t, dt)
     _check(lib().whisper_attention_decode_cross(dt, _p(q), _p(k), _p(v), batch, n_heads, T, _p(out), _p(ws),
                                                 ws_bytes, _stream(stream)))
 

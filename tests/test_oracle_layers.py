@@ -8,7 +8,16 @@ import torch.nn.functional as F
 
 from oracle import whisper_oracle as O
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """torch CPU references in float64, restored afterwards (the GPU tests
+    collected in the same session build their inputs with torch defaults)."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def T(a):
