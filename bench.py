@@ -176,7 +176,7 @@ def main():
     stage_ms = {n: float(np.mean([stage_ev[s][i].elapsed_time(stage_ev[s][i + 1]) for s in range(args.steps)]))
                 for i, n in enumerate(stage_names)}
     cross_ms = float(np.mean([k_start[i].elapsed_time(k_stop[i]) for i in range(n_rec)]))
-    cross_bytes = 2 * B * H * T * 64 * 2 + B * d * 2 + B * H * 4 * 66 * 4
+    cross_bytes = 2 * B * H * T * 64 * 2 + 2 * B * d * 2  # K and V, q in, output out
     cross_gbs = cross_bytes / (cross_ms * 1e-3) / 1e9
     enc_flop = B * (2 * 3000 * 3 * dims.n_mels * d + 2 * 1500 * 3 * d * d) + B * 32 * (
         2 * T * d * 3 * d + 2 * T * d * d + 2 * 2 * T * d * dims.d_ffn + 4 * T * T * d)
@@ -209,7 +209,7 @@ def main():
         "decode_tok_per_s": round(decode_tok_s, 1),
         "encoder_tflops": round(enc_flop / (stage_ms["encode"] * 1e-3) / 1e12, 1),
         "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "attn_decode_cross_kernel (decoder cross-attention, split-T partial)",
+        "roofline": {"kernel": "attn_decode_cross_kernel (decoder cross-attention)",
                      "bound": "hbm", "achieved": round(cross_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(cross_gbs / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic("attn_decode_cross_kernel"),

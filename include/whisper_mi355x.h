@@ -209,8 +209,9 @@ whisper_status whisper_attention_decode_self(whisper_dtype dt, const void* q, in
                                              const int32_t* n_keys, void* out, void* stream);
 
 /* Decoder cross-attention: q [batch, n_heads*64], k and v head-major
- * [batch][n_heads][T][64] -> out [batch, n_heads*64]. Workspace:
- * whisper_attention_decode_cross_workspace_size(). */
+ * [batch][n_heads][T][64] -> out [batch, n_heads*64], one pass per (row,
+ * head). whisper_attention_decode_cross_workspace_size() returns 0: ws and
+ * ws_bytes are accepted for interface stability and not used (NULL is fine). */
 size_t whisper_attention_decode_cross_workspace_size(int batch, int n_heads, int T);
 whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, const void* k, const void* v,
                                               int batch, int n_heads, int T, void* out, void* ws, size_t ws_bytes,

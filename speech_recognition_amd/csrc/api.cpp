@@ -150,7 +150,7 @@ EncWS enc_ws(const whisper_dims* d, int B) {
   return W;
 }
 
-struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, cross, total; };
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, total; };
 DecWS dec_ws(const whisper_dims* d, int B) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
@@ -160,7 +160,6 @@ DecWS dec_ws(const whisper_dims* d, int B) {
   W.att = take(B * D * e); W.qc = take(B * D * e);
   W.hf = take((size_t)B * d->d_ffn * e);
   W.logits = take((size_t)B * d->n_vocab * 4);
-  W.cross = take(attn_decode_cross_ws(B, d->n_heads, d->n_audio_ctx));
   W.total = off;
   return W;
 }
@@ -298,7 +297,6 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* ATT = at<u16_t>(ws, W.att);
   u16_t* QC = at<u16_t>(ws, W.qc);
   u16_t* HF = at<u16_t>(ws, W.hf);
-  float* CR = at<float>(ws, W.cross);
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
@@ -331,9 +329,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     const char* ck = (const char*)cross_kv + l * ckv_layer;
     {
       ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
-      WH_TRY(launch_attn_decode_cross_partial(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, CR, s));
+      WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s));
     }
-    WH_TRY(launch_attn_decode_cross_combine(ACT_BF16, CR, B, H, ATT, s));
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l));
@@ -591,7 +588,6 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   void* QC = at<void>(ws, W.qc);
   void* HF = at<void>(ws, W.hf);
   float* LG = logits ? logits : at<float>(ws, W.logits);
-  float* CR = at<float>(ws, W.cross);
   if (t == ACT_BF16) return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv,
                                               LG, argmax, dev_error, ws, s);
   WH_TRY(launch_embed(t, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
@@ -619,9 +615,8 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
     const char* ck = (const char*)cross_kv + l * ckv_layer;
     {
       ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
-      WH_TRY(launch_attn_decode_cross_partial(t, QC, ck, ck + ckv_layer / 2, B, H, T, CR, s));
+      WH_TRY(launch_attn_decode_cross(t, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s));
     }
-    WH_TRY(launch_attn_decode_cross_combine(t, CR, B, H, ATT, s));
     WH_TRY(launch_gemm_skinny(t, EPI_STORE, gp(ATT, D, at<void>(packed, Lw.woc), D, B, D, D, at<float>(packed, Lw.boc), Dl, D), s));
     WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln3g), at<float>(packed, Lw.ln3b), 1e-5f, B, D, A, X, s));
     WH_TRY(launch_gemm_skinny(t, EPI_GELU, gp(A, D, at<void>(packed, Lw.w1), D, B, F, D, at<float>(packed, Lw.b1), HF, F), s));
@@ -730,8 +725,8 @@ whisper_status whisper_attention_decode_self(whisper_dtype dt, const void* q, in
 }
 
 size_t whisper_attention_decode_cross_workspace_size(int B, int H, int T) {
-  if (B <= 0 || H <= 0 || T <= 0) return 0;
-  return attn_decode_cross_ws(B, H, T);
+  (void)B; (void)H; (void)T;
+  return 0;  // single pass, no partials
 }
 
 whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, const void* k, const void* v, int B,
@@ -740,9 +735,9 @@ whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, c
   if (B <= 0 || H <= 0 || T <= 0) return fail(WHISPER_ERR_INVALID_ARG, "attention_decode_cross: sizes must be > 0");
   if (T > 4096) return fail(WHISPER_ERR_SHAPE, "attention_decode_cross: T must be <= 4096");
   WH_CHECK(check_ptrs({q, k, v, out}, "attention_decode_cross"));
-  WH_CHECK(check_ws(ws, ws_bytes, attn_decode_cross_ws(B, H, T), "attention_decode_cross"));
+  (void)ws; (void)ws_bytes;
   (void)hipGetLastError();
-  WH_TRY(launch_attn_decode_cross(act_of(dt), q, k, v, B, H, T, out, (float*)ws, S(stream)));
+  WH_TRY(launch_attn_decode_cross(act_of(dt), q, k, v, B, H, T, out, S(stream)));
   return WHISPER_OK;
 }
 

@@ -14,6 +14,8 @@
 // read (the Inference Endpoints post, "Inference Stack": K/V stored as float8,
 // compute in bfloat16). Decoder cross-attention streams head-major bf16 K/V,
 // split over the 1500 frames with a log-sum-exp combine.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -231,7 +233,6 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 // loads of a batch (8 keys, 128 B) before decoding any of them, so a whole
 // cache row of up to 512 keys is in flight at once; scores stay in LDS.
 constexpr int DEC_MAX_CAP = 4096;
-constexpr int SELF_BATCH = 8;
 
 __device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -246,6 +247,15 @@ __device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
   return acc;
 }
 
+// One workgroup per (row, head). Lane (part = tid & 3, kg = tid >> 2) owns 16
+// of the 64 dims of keys kg, kg + 64, ...; per batch of SELF_KB keys it loads
+// the K and V codes together (addresses clamped to the last valid key, so the
+// batch is straight-line code and all its loads are in flight at once), keeps
+// a private online softmax (running max, sum and 16 output dims), and the 256
+// private states are merged once at the end: block max, rescale, sum over
+// the 64 key groups through LDS. q goes straight from global to registers.
+constexpr int SELF_KB = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restrict__ q, long q_stride,
                                                                const uint8_t* __restrict__ kc,
@@ -253,67 +263,53 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
                                                                const float* __restrict__ scales,
                                                                const int32_t* __restrict__ lengths, int len_add, int H,
                                                                int cap, T* __restrict__ out) {
-  __shared__ float qs[64];
-  __shared__ float sc[DEC_MAX_CAP];
-  __shared__ float red[64][65];
-  __shared__ float wred[8];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[4][64];
+  __shared__ float wmax[4], wsum[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = max(0, min(lengths[b] + len_add, cap));
-  const float sk = scales[0], sv = scales[1];
-  if (tid < 64) qs[tid] = Act<T>::cvt(q[(long)b * q_stride + h * 64 + tid]);
-  __syncthreads();
-  const long head = ((long)b * H + h) * cap * 64;
-  const uint8_t* K = kc + head;
-  const uint8_t* V = vc + head;
   const int part = tid & 3, kg = tid >> 2;
   float qreg[16];
+  {
+    const T* qp = q + (long)b * q_stride + h * 64 + part * 16;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) qreg[i] = qs[part * 16 + i];
-  const float sscale = sk * 0.125f;
-  for (int base = 0; base < n; base += 64 * SELF_BATCH) {
-    uint4 c[SELF_BATCH];
-#pragma unroll
-    for (int i = 0; i < SELF_BATCH; ++i) {
-      const int j = base + kg + 64 * i;
-      c[i] = j < n ? *(const uint4*)(K + (long)j * 64 + part * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < SELF_BATCH; ++i) {
-      const int j = base + kg + 64 * i;
-      float acc = dot16_e4m3(c[i], qreg);
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (part == 0 && j < n) sc[j] = acc * sscale;
-    }
+    for (int i = 0; i < 16; ++i) qreg[i] = Act<T>::cvt(qp[i]);
   }
-  __syncthreads();
-  float mx = -INFINITY;
-  for (int j = tid; j < n; j += 256) mx = fmaxf(mx, sc[j]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) wred[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  float sum = 0.f;
-  for (int j = tid; j < n; j += 256) { const float p = expf(sc[j] - mx); sc[j] = p; sum += p; }
-  sum = wave_sum(sum);
-  if ((tid & 63) == 0) wred[4 + (tid >> 6)] = sum;
-  __syncthreads();
-  sum = wred[4] + wred[5] + wred[6] + wred[7];
-  float acc[16];
+  const float sscale = scales[0] * 0.125f, sv = scales[1];
+  const long head = ((long)b * H + h) * cap * 64 + part * 16;
+  const uint8_t* K = kc + head;
+  const uint8_t* V = vc + head;
+  float m = -INFINITY, l = 0.f, acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int base = 0; base < n; base += 64 * SELF_BATCH) {
-    uint4 c[SELF_BATCH];
+  for (int base = 0; base < n; base += 64 * SELF_KB) {
+    uint4 ck[SELF_KB], cv[SELF_KB];
 #pragma unroll
-    for (int i = 0; i < SELF_BATCH; ++i) {
-      const int j = base + kg + 64 * i;
-      c[i] = j < n ? *(const uint4*)(V + (long)j * 64 + part * 16) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < SELF_KB; ++i) {
+      const long j = min(base + kg + 64 * i, n - 1);
+      ck[i] = *(const uint4*)(K + j * 64);
+      cv[i] = *(const uint4*)(V + j * 64);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    float sj[SELF_KB];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < SELF_BATCH; ++i) {
-      const int j = base + kg + 64 * i;
-      const float p = j < n ? sc[j] : 0.f;
-      const uint32_t w[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+    for (int i = 0; i < SELF_KB; ++i) {
+      float d = dot16_e4m3(ck[i], qreg);
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      sj[i] = (base + kg + 64 * i < n) ? d * sscale : -INFINITY;
+      bm = fmaxf(bm, sj[i]);
+    }
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int i = 0; i < SELF_KB; ++i) {
+      const float p = (sj[i] == -INFINITY) ? 0.f : expf(sj[i] - mn);
+      l += p;
+      const uint32_t w[4] = {cv[i].x, cv[i].y, cv[i].z, cv[i].w};
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         float v[4];
@@ -322,13 +318,33 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
         for (int k = 0; k < 4; ++k) acc[4 * e4 + k] = fmaf(p, v[k], acc[4 * e4 + k]);
       }
     }
+    m = mn;
   }
+  // merge the private states: block max, rescale, sum over the 16 key groups of
+  // a wave with lane shuffles (lanes of equal part), then over the 4 waves in LDS
+  const float wm = wave_max(m);
+  if (lane == 0) wmax[wave] = wm;
+  __syncthreads();
+  const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float f = (m == -INFINITY) ? 0.f : expf(m - mx);
+  float ls = l * f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) red[kg][part * 16 + i] = acc[i];
+  for (int i = 0; i < 16; ++i) acc[i] *= f;
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) {
+    ls += __shfl_xor(ls, o, 64);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
+  }
+  if (lane < 4) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave][lane * 16 + i] = acc[i];
+    if (lane == 0) wsum[wave] = ls;
+  }
   __syncthreads();
   if (tid < 64) {
-    float s = 0.f;
-    for (int r = 0; r < 64; ++r) s += red[r][tid];
+    const float sum = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
     const float v = (n > 0) ? s * sv / sum : 0.f;
     out[(long)b * H * 64 + h * 64 + tid] = Act<T>::st(v);
   }
@@ -349,130 +365,132 @@ hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, cons
 }
 
 // ------------------------------------------------------------------ decoder cross-attention
-// Grid (split, head, row). Each split handles a contiguous range of frames,
-// keeps its scores in LDS and writes an unnormalised partial output with its
-// local max and sum; the combine kernel merges the splits.
-constexpr int CROSS_SPLIT = 4;
-constexpr int CROSS_MAX_CHUNK = 1024;
+// One workgroup per (row, head) streams that head's whole K and V slabs
+// (1500 x 64 each, head-major, so a wave's 16-byte loads cover 1 KB of
+// consecutive key rows). Lane (part, kg) owns EPT of the 64 dims of keys
+// kg, kg + KPP, ...; per batch of CROSS_NB passes it loads the K and V rows
+// together (addresses clamped to the last frame, so the batch is
+// straight-line code), keeps a private online softmax, and the private states
+// are merged once at the end and written as the final output: no partials, no
+// combine pass.
+constexpr int CROSS_NB = 8;
 
-size_t attn_decode_cross_ws(int B, int H, int T) { return (size_t)B * H * CROSS_SPLIT * 66 * sizeof(float); }
+// 16 bytes of a K or V row as fp32 (no address-taken register arrays)
+__device__ __forceinline__ void unpack16(const uint4 w, float o[8]) {
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(a[i] << 16);
+    o[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const float4 w, float o[4]) {
+  o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const T* __restrict__ v, int H, int T_,
-                                                                float* __restrict__ ws) {
+                                                                T* __restrict__ out) {
   constexpr int EPT = 16 / sizeof(T);   // elements per 16-byte chunk
-  constexpr int TPK = 64 / EPT;         // threads per key row
+  constexpr int TPK = 64 / EPT;         // lanes per key row
   constexpr int KPP = 256 / TPK;        // keys per pass
-  __shared__ float qs[64];
-  __shared__ float sc[CROSS_MAX_CHUNK];
-  __shared__ float red[KPP][65];
-  __shared__ float wred[8];
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int chunk = (T_ + CROSS_SPLIT - 1) / CROSS_SPLIT;
-  const int t0 = split * chunk, t1 = min(T_, t0 + chunk), n = max(0, t1 - t0);
-  if (tid < 64) qs[tid] = Act<T>::cvt(q[((long)b * H + h) * 64 + tid]);
-  __syncthreads();
-  const long head = (((long)b * H + h) * T_ + t0) * 64;
-  const T* K = k + head;
-  const T* V = v + head;
+  typedef typename std::conditional<sizeof(T) == 2, uint4, float4>::type V16;
+  __shared__ float red[4][64];
+  __shared__ float wmax[4], wsum[4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = tid % TPK, kg = tid / TPK;
   float qreg[EPT];
+  {
+    const T* qp = q + ((long)b * H + h) * 64 + part * EPT;
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) qreg[i] = qs[part * EPT + i];
-#pragma unroll 4
-  for (int j = kg; j < n; j += KPP) {
-    const uint4 c = *(const uint4*)(K + (long)j * 64 + part * EPT);
-    const T* e = (const T*)&c;
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) acc = fmaf(qreg[i], Act<T>::cvt(e[i]), acc);
-#pragma unroll
-    for (int o = 1; o < TPK; o <<= 1) acc += __shfl_xor(acc, o, 64);
-    if (part == 0) sc[j] = acc * 0.125f;
+    for (int i = 0; i < EPT; ++i) qreg[i] = Act<T>::cvt(qp[i]) * 0.125f;
   }
-  __syncthreads();
-  float mx = -INFINITY;
-  for (int j = tid; j < n; j += 256) mx = fmaxf(mx, sc[j]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) wred[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  float sum = 0.f;
-  for (int j = tid; j < n; j += 256) { const float p = expf(sc[j] - mx); sc[j] = p; sum += p; }
-  sum = wave_sum(sum);
-  __syncthreads();
-  if ((tid & 63) == 0) wred[4 + (tid >> 6)] = sum;
-  __syncthreads();
-  sum = wred[4] + wred[5] + wred[6] + wred[7];
-  float acc[EPT];
+  const long head = ((long)b * H + h) * T_ * 64 + part * EPT;
+  const T* K = k + head;
+  const T* V = v + head;
+  float m = -INFINITY, l = 0.f, acc[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int j = kg; j < n; j += KPP) {
-    const uint4 c = *(const uint4*)(V + (long)j * 64 + part * EPT);
-    const T* e = (const T*)&c;
-    const float p = sc[j];
+  for (int base = 0; base < T_; base += KPP * CROSS_NB) {
+    V16 ck[CROSS_NB], cv[CROSS_NB];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) acc[i] = fmaf(p, Act<T>::cvt(e[i]), acc[i]);
+    for (int i = 0; i < CROSS_NB; ++i) {
+      const long j = min(base + kg + KPP * i, T_ - 1);
+      ck[i] = *(const V16*)(K + j * 64);
+      cv[i] = *(const V16*)(V + j * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float sj[CROSS_NB];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CROSS_NB; ++i) {
+      float kk[EPT];
+      unpack16(ck[i], kk);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) d = fmaf(qreg[e], kk[e], d);
+#pragma unroll
+      for (int o = 1; o < TPK; o <<= 1) d += __shfl_xor(d, o, 64);
+      sj[i] = (base + kg + KPP * i < T_) ? d : -INFINITY;
+      bm = fmaxf(bm, sj[i]);
+    }
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < CROSS_NB; ++i) {
+      const float p = (sj[i] == -INFINITY) ? 0.f : expf(sj[i] - mn);
+      l += p;
+      float vv[EPT];
+      unpack16(cv[i], vv);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) acc[e] = fmaf(p, vv[e], acc[e]);
+    }
+    m = mn;
   }
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) red[kg][part * EPT + i] = acc[i];
+  // merge: block max, rescale, sum over the key groups of a wave with lane
+  // shuffles (lanes of equal part), then over the 4 waves in LDS
+  const float wm = wave_max(m);
+  if (lane == 0) wmax[wave] = wm;
   __syncthreads();
-  float* w = ws + (((long)b * H + h) * CROSS_SPLIT + split) * 66;
+  const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float f = (m == -INFINITY) ? 0.f : expf(m - mx);
+  float ls = l * f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] *= f;
+#pragma unroll
+  for (int o = TPK; o < 64; o <<= 1) {
+    ls += __shfl_xor(ls, o, 64);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+  if (lane < TPK) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) red[wave][lane * EPT + e] = acc[e];
+    if (lane == 0) wsum[wave] = ls;
+  }
+  __syncthreads();
   if (tid < 64) {
-    float s = 0.f;
-    for (int r = 0; r < KPP; ++r) s += red[r][tid];
-    w[tid] = s;
+    const float sum = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    out[((long)b * H + h) * 64 + tid] = Act<T>::st(T_ > 0 ? s / sum : 0.f);
   }
-  if (tid == 0) { w[64] = (n > 0) ? mx : -INFINITY; w[65] = (n > 0) ? sum : 0.f; }
-}
-
-template <typename T>
-__global__ __launch_bounds__(64) void attn_decode_cross_combine(const float* __restrict__ ws, int H,
-                                                                T* __restrict__ out) {
-  const int h = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
-  const float* w = ws + ((long)b * H + h) * CROSS_SPLIT * 66;
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < CROSS_SPLIT; ++s) M = fmaxf(M, w[s * 66 + 64]);
-  float num = 0.f, den = 0.f;
-#pragma unroll
-  for (int s = 0; s < CROSS_SPLIT; ++s) {
-    const float ms = w[s * 66 + 64];
-    const float f = (ms == -INFINITY) ? 0.f : expf(ms - M);
-    num += w[s * 66 + e] * f;
-    den += w[s * 66 + 65] * f;
-  }
-  out[((long)b * H + h) * 64 + e] = Act<T>::st(num / den);
-}
-
-hipError_t launch_attn_decode_cross_partial(ActType t, const void* q, const void* k, const void* v, int B, int H,
-                                            int T, float* ws, hipStream_t s) {
-  if ((T + CROSS_SPLIT - 1) / CROSS_SPLIT > CROSS_MAX_CHUNK) return hipErrorInvalidValue;
-  dim3 grid(CROSS_SPLIT, H, B);
-  if (t == ACT_BF16)
-    hipLaunchKernelGGL(attn_decode_cross_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, (const u16*)k,
-                       (const u16*)v, H, T, ws);
-  else
-    hipLaunchKernelGGL(attn_decode_cross_kernel<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, H, T, ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_decode_cross_combine(ActType t, const float* ws, int B, int H, void* out, hipStream_t s) {
-  if (t == ACT_BF16)
-    hipLaunchKernelGGL(attn_decode_cross_combine<u16>, dim3(H, B), dim3(64), 0, s, ws, H, (u16*)out);
-  else
-    hipLaunchKernelGGL(attn_decode_cross_combine<float>, dim3(H, B), dim3(64), 0, s, ws, H, (float*)out);
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
-                                    void* out, float* ws, hipStream_t s) {
-  hipError_t e = launch_attn_decode_cross_partial(t, q, k, v, B, H, T, ws, s);
-  if (e != hipSuccess) return e;
-  return launch_attn_decode_cross_combine(t, ws, B, H, out, s);
+                                    void* out, hipStream_t s) {
+  if (T <= 0) return hipErrorInvalidValue;
+  const dim3 grid(H, B);
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL(attn_decode_cross_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, (const u16*)k,
+                       (const u16*)v, H, T, (u16*)out);
+  else
+    hipLaunchKernelGGL(attn_decode_cross_kernel<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)k,
+                       (const float*)v, H, T, (float*)out);
+  return hipGetLastError();
 }
 
 }  // namespace wh

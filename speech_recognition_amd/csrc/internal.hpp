@@ -89,12 +89,8 @@ hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, cons
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths,
                                    int len_add, int B, int H, int cap, void* out, hipStream_t s);
 // Decode cross-attention over head-major K/V [B][H][T][64]; split over T.
-size_t attn_decode_cross_ws(int B, int H, int T);
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
-                                    void* out, float* ws, hipStream_t s);
-hipError_t launch_attn_decode_cross_partial(ActType t, const void* q, const void* k, const void* v, int B, int H,
-                                            int T, float* ws, hipStream_t s);
-hipError_t launch_attn_decode_cross_combine(ActType t, const float* ws, int B, int H, void* out, hipStream_t s);
+                                    void* out, hipStream_t s);
 
 // ------------------------------------------------------------------ log-mel
 size_t logmel_ws(int B, int n_mels);
