@@ -32,23 +32,16 @@
 namespace wh {
 
 constexpr int DG_WAVES = 8;
-constexpr int DG_REG_BUDGET = 176;  // VGPRs per lane for in-flight operand loads plus accumulators
+constexpr int DG_DEPTH = 1;         // k-steps of operand loads in flight per wave ahead of the MFMAs
 
-// Registers one k-step of operand loads takes per lane, and how many k-steps
-// fit in one batch of in-flight loads.
-template <int PRO, int MB, int CB>
-struct DecStep {
-  static constexpr int REGS = (PRO == PRO_X ? MB * 8 : MB * 4) + CB * 4;
-  static constexpr int FREE = DG_REG_BUDGET - 4 * MB * CB;
-  static constexpr bool fits(int nj) { return nj * REGS <= FREE; }
-};
-
-// NJ: k-steps per batch, fixed at compile time so that a batch is straight-line
-// code whose loads are all in flight together (a guarded, variable-length batch
-// makes the compiler wait for each step's loads before issuing the next).
-// Every wave runs a whole number of batches: the host picks NJ with
-// (K / 32) % (8 * NJ) == 0, or NJ = 1.
-template <int PRO, int EPI, int MB, int CB, int NJ>
+// NS: k-steps per wave, fixed at compile time (K / 256 for K = 1280 or 5120),
+// so the main loop is a straight-line software pipeline: the loads of step
+// s + DG_DEPTH are issued before step s is computed, which keeps a bounded
+// ~DG_DEPTH steps of operand bytes in flight per wave (streaming measured on
+// MI355X: ~4-8 KB in flight per wave sustains ~12 TB/s from the caches, while
+// issuing a wave's whole share at once congests and runs at about half that).
+// NS = 0 is the generic path (any K % 32 == 0): one step at a time.
+template <int PRO, int EPI, int MB, int CB, int NS>
 __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
   constexpr int MR = MB * 16;
   constexpr bool XIN = PRO == PRO_X;
@@ -110,78 +103,74 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) st_c[mb] = st_s1[mb] = st_s2[mb] = 0.f;
 
-  for (int b0 = 0; b0 < nsteps; b0 += NJ) {
-    uint4 wv[NJ][CB];
-    float4 xa[XIN ? NJ : 1][MB], xb[XIN ? NJ : 1][MB];
-    uint4 av[XIN ? 1 : NJ][MB];
-    // ---- issue every load of the batch
+  // operand slots: step j of this wave lives in slot j % NSLOT
+  constexpr int NSLOT = NS > 0 ? DG_DEPTH + 1 : 1;
+  uint4 wv[NSLOT][CB];
+  float4 xa[XIN ? NSLOT : 1][MB], xb[XIN ? NSLOT : 1][MB];
+  uint4 av[XIN ? 1 : NSLOT][MB];
+#define DG_ISSUE(J, SL)                                                                        \
+  {                                                                                            \
+    const int k_ = (s0 + (J)) * 32;                                                            \
+    _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) wv[SL][cb] = *(const uint4*)(wrow[cb] + k_); \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
+      if constexpr (XIN) {                                                                     \
+        const float* x_ = p.X + arow[mb] * K + k_ + kq;                                        \
+        xa[XIN ? SL : 0][mb] = *(const float4*)x_;                                             \
+        xb[XIN ? SL : 0][mb] = *(const float4*)(x_ + 4);                                       \
+      } else {                                                                                 \
+        av[XIN ? 0 : SL][mb] = *(const uint4*)(p.A + arow[mb] * p.lda + k_ + kq);              \
+      }                                                                                        \
+    }                                                                                          \
+  }
+#define DG_COMPUTE(J, SL)                                                                      \
+  {                                                                                            \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
+      if constexpr (XIN) {                                                                     \
+        const float4 a_ = xa[XIN ? SL : 0][mb], e_ = xb[XIN ? SL : 0][mb];                     \
+        const float v_[8] = {a_.x, a_.y, a_.z, a_.w, e_.x, e_.y, e_.z, e_.w};                  \
+        uint32_t hi_[4], lo_[4];                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
+          hi_[i] = f2bf2(v_[2 * i], v_[2 * i + 1]);                                            \
+          lo_[i] = f2bf2(v_[2 * i] - __uint_as_float(hi_[i] << 16),                            \
+                         v_[2 * i + 1] - __uint_as_float(hi_[i] & 0xffff0000u));               \
+        }                                                                                      \
+        const bf16x8 ah_ = bitcast<bf16x8>(make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]));        \
+        const bf16x8 al_ = bitcast<bf16x8>(make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]));        \
+        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) {                                    \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah_, bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al_, bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
+        }                                                                                      \
+        /* shifted sums: S1 += x - c, S2 += (x - c)^2, c = this lane's first value of the row */ \
+        if ((J) == 0) st_c[mb] = a_.x;                                                         \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+          const float d_ = v_[i] - st_c[mb];                                                   \
+          st_s1[mb] += d_;                                                                     \
+          st_s2[mb] = fmaf(d_, d_, st_s2[mb]);                                                 \
+        }                                                                                      \
+      } else {                                                                                 \
+        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb)                                      \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[XIN ? 0 : SL][mb]), \
+                                                                bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
+      }                                                                                        \
+    }                                                                                          \
+  }
+  if constexpr (NS > 0) {
+    // straight-line pipeline: issue step t, compute step t - DG_DEPTH
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int k = (s0 + b0 + j) * 32;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) wv[j][cb] = *(const uint4*)(wrow[cb] + k);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (XIN) {
-          const float* x = p.X + arow[mb] * K + k + kq;
-          xa[j][mb] = *(const float4*)x;
-          xb[j][mb] = *(const float4*)(x + 4);
-        } else {
-          av[j][mb] = *(const uint4*)(p.A + arow[mb] * p.lda + k + kq);
-        }
-      }
+    for (int t = 0; t < NS + DG_DEPTH; ++t) {
+      if (t < NS) DG_ISSUE(t, t % NSLOT)
+      __builtin_amdgcn_sched_barrier(0);
+      if (t >= DG_DEPTH) DG_COMPUTE(t - DG_DEPTH, (t - DG_DEPTH) % NSLOT)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // keep the scheduler from interleaving the loads with the MFMAs below (it
-    // would trade in-flight loads for registers and serialise the batch)
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- MFMAs (and, for the fp32 residual input, the row moments)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (XIN) {
-          const float v[8] = {xa[j][mb].x, xa[j][mb].y, xa[j][mb].z, xa[j][mb].w,
-                              xb[j][mb].x, xb[j][mb].y, xb[j][mb].z, xb[j][mb].w};
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hi[i] = f2bf2(v[2 * i], v[2 * i + 1]);
-            lo[i] = f2bf2(v[2 * i] - __uint_as_float(hi[i] << 16), v[2 * i + 1] - __uint_as_float(hi[i] & 0xffff0000u));
-          }
-          const bf16x8 ah = bitcast<bf16x8>(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-          const bf16x8 al = bitcast<bf16x8>(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bitcast<bf16x8>(wv[j][cb]), acc[mb][cb], 0, 0, 0);
-            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bitcast<bf16x8>(wv[j][cb]), acc[mb][cb], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[j][mb]), bitcast<bf16x8>(wv[j][cb]),
-                                                                  acc[mb][cb], 0, 0, 0);
-        }
-      }
-    }
-    if constexpr (XIN) {
-      // shifted sums: S1 += x - c, S2 += (x - c)^2 with c = this lane's first value of the row
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (b0 == 0) st_c[mb] = xa[0][mb].x;
-        const float c = st_c[mb];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const float4 a = xa[j][mb], e = xb[j][mb];
-          const float d[8] = {a.x - c, a.y - c, a.z - c, a.w - c, e.x - c, e.y - c, e.z - c, e.w - c};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            st_s1[mb] += d[i];
-            st_s2[mb] = fmaf(d[i], d[i], st_s2[mb]);
-          }
-        }
-      }
+  } else {
+    for (int j = 0; j < nsteps; ++j) {
+      DG_ISSUE(j, 0)
+      DG_COMPUTE(j, 0)
     }
   }
+#undef DG_ISSUE
+#undef DG_COMPUTE
 
   // ---- row moments: per lane (mean, M2) from the shifted sums, merged over the
   // 4 lanes holding a row (equal counts), published per wave
@@ -278,25 +267,21 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   }
 }
 
-template <int PRO, int EPI, int MB, int CB, int NJ>
-static hipError_t dec_launch_nj(const DecGemmParams& p, hipStream_t s) {
-  if constexpr (!DecStep<PRO, MB, CB>::fits(NJ)) {
-    return hipErrorInvalidValue;
-  } else {
-    const dim3 grid((p.N + 16 * CB - 1) / (16 * CB), (p.M + 16 * MB - 1) / (16 * MB));
-    hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NJ>), grid, dim3(DG_WAVES * 64), 0, s, p);
-    return hipGetLastError();
-  }
+template <int PRO, int EPI, int MB, int CB, int NS>
+static hipError_t dec_launch_ns(const DecGemmParams& p, hipStream_t s) {
+  const dim3 grid((p.N + 16 * CB - 1) / (16 * CB), (p.M + 16 * MB - 1) / (16 * MB));
+  hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NS>), grid, dim3(DG_WAVES * 64), 0, s, p);
+  return hipGetLastError();
 }
 
-// Largest batch (10 or 5 k-steps) that divides every wave's share of K and
-// fits the register budget; 1 otherwise.
+// The pipelined kernel for the two K of the model (d = 1280 -> 5 steps per
+// wave, 4d = 5120 -> 20), the generic one otherwise.
 template <int PRO, int EPI, int MB, int CB>
 static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
   const int S = p.K / 32;
-  if (S % (DG_WAVES * 10) == 0 && DecStep<PRO, MB, CB>::fits(10)) return dec_launch_nj<PRO, EPI, MB, CB, 10>(p, s);
-  if (S % (DG_WAVES * 5) == 0 && DecStep<PRO, MB, CB>::fits(5)) return dec_launch_nj<PRO, EPI, MB, CB, 5>(p, s);
-  return dec_launch_nj<PRO, EPI, MB, CB, 1>(p, s);
+  if (S == DG_WAVES * 5) return dec_launch_ns<PRO, EPI, MB, CB, 5>(p, s);
+  if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20>(p, s);
+  return dec_launch_ns<PRO, EPI, MB, CB, 0>(p, s);
 }
 
 // Tile shapes with MB * CB <= 4 (larger ones run out of registers).
