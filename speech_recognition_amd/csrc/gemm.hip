@@ -542,43 +542,43 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(BF[j], AF[i], acc[i][j], 0, 0, 0);
-  // wait until this wave's loads of stage `t` have landed (vmcnt counts the
-  // later stages' loads still allowed in flight) and its own LDS reads are
-  // complete, then meet the other waves
-#define WH_SYNC(t)                                                                            \
-  {                                                                                           \
-    const int after = min(2, nk - 1 - (t));                                                   \
-    if (after == 2) { WH_WAIT_VM_LGKM0(8); } else if (after == 1) { WH_WAIT_VM_LGKM0(4); }    \
-    else { WH_WAIT_VM_LGKM0(0); }                                                             \
-    __builtin_amdgcn_s_barrier();                                                             \
+  // Straight-line pipeline (K % 128 == 0): every wait is static, so the
+  // compiler keeps the two fragment sets in place and waits for LDS reads
+  // only where their registers are used. WH_SYNC(n): this wave's DMA loads of
+  // the stage being waited for have landed (n later loads may still be in
+  // flight) and its LDS reads are complete, then all waves meet.
+#define WH_SYNC(n)                                                                             \
+  {                                                                                            \
+    WH_WAIT_VM_LGKM0(n);                                                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
   }
+  // one k-step: make the next stage ready, optionally refill the buffer the
+  // current stage came from, read the next stage's fragments, then run the
+  // current stage's MFMAs
+#define WH_STEP(WAITN, REFILL, SREFILL, KREFILL, SN, AC, BC, AN, BN)                           \
+  WH_SYNC(WAITN)                                                                               \
+  if (REFILL) { WH_ISSUE(SREFILL, KREFILL) }                                                   \
+  WH_READ(SN, AN, BN)                                                                          \
+  WH_MFMA(AC, BC)
 
-  if (nk > 0) { WH_ISSUE(st0, 0) }
-  if (nk > 1) { WH_ISSUE(st1, DBK) }
-  if (nk > 2) { WH_ISSUE(st2, 2 * DBK) }
-  WH_SYNC(0)
-  if (nk > 3) { WH_ISSUE(st3, 3 * DBK) }
+  WH_ISSUE(st0, 0)
+  WH_ISSUE(st1, DBK)
+  WH_ISSUE(st2, 2 * DBK)
+  WH_SYNC(8)
+  WH_ISSUE(st3, 3 * DBK)
   WH_READ(st0, a0, b0)
-
-  // step t: stage t's fragments are in (AC, BC); make stage t+1 ready, refill
-  // the buffer stage t came from with tile t+4, read stage t+1's fragments
-  // into (AN, BN), then run stage t's MFMAs
-#define WH_STEP(SN, SREFILL, AC, BC, AN, BN, t)                                               \
-  if ((t) < nk) {                                                                             \
-    if ((t) + 1 < nk) {                                                                       \
-      WH_SYNC((t) + 1)                                                                        \
-      if ((t) + 4 < nk) { WH_ISSUE(SREFILL, ((t) + 4) * DBK) }                                \
-      WH_READ(SN, AN, BN)                                                                     \
-    }                                                                                         \
-    WH_MFMA(AC, BC)                                                                           \
+  int kt = 0;
+  for (; kt + 8 <= nk; kt += 4) {
+    WH_STEP(8, true, st0, (kt + 4) * DBK, st1, a0, b0, a1, b1)
+    WH_STEP(8, true, st1, (kt + 5) * DBK, st2, a1, b1, a0, b0)
+    WH_STEP(8, true, st2, (kt + 6) * DBK, st3, a0, b0, a1, b1)
+    WH_STEP(8, true, st3, (kt + 7) * DBK, st0, a1, b1, a0, b0)
   }
-
-  for (int kt = 0; kt < nk; kt += 4) {
-    WH_STEP(st1, st0, a0, b0, a1, b1, kt)
-    WH_STEP(st2, st1, a1, b1, a0, b0, kt + 1)
-    WH_STEP(st3, st2, a0, b0, a1, b1, kt + 2)
-    WH_STEP(st0, st3, a1, b1, a0, b0, kt + 3)
-  }
+  // last four k-steps (stages nk-4 .. nk-1 live in buffers 0 .. 3)
+  WH_STEP(8, false, st0, 0, st1, a0, b0, a1, b1)
+  WH_STEP(4, false, st0, 0, st2, a1, b1, a0, b0)
+  WH_STEP(0, false, st0, 0, st3, a0, b0, a1, b1)
+  WH_MFMA(a1, b1)
 #undef WH_READ
 #undef WH_MFMA
 #undef WH_SYNC
@@ -694,37 +694,35 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma4(GemmParams p) {
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
     _Pragma("unroll") for (int j = 0; j < 8; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(BF[j], AF[i], acc[i][j], 0, 0, 0);
-#define WH_SYNC(t)                                                                            \
-  {                                                                                           \
-    const int after = min(2, nk - 1 - (t));                                                   \
-    if (after == 2) { WH_WAIT_VM_LGKM0(16); } else if (after == 1) { WH_WAIT_VM_LGKM0(8); }   \
-    else { WH_WAIT_VM_LGKM0(0); }                                                             \
-    __builtin_amdgcn_s_barrier();                                                             \
+#define WH_SYNC(n)                                                                             \
+  {                                                                                            \
+    WH_WAIT_VM_LGKM0(n);                                                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
   }
+#define WH_STEP(WAITN, REFILL, SREFILL, KREFILL, SN, AC, BC, AN, BN)                           \
+  WH_SYNC(WAITN)                                                                               \
+  if (REFILL) { WH_ISSUE(SREFILL, KREFILL) }                                                   \
+  WH_READ(SN, AN, BN)                                                                          \
+  WH_MFMA(AC, BC)
 
-  if (nk > 0) { WH_ISSUE(st0, 0) }
-  if (nk > 1) { WH_ISSUE(st1, DBK) }
-  if (nk > 2) { WH_ISSUE(st2, 2 * DBK) }
-  WH_SYNC(0)
-  if (nk > 3) { WH_ISSUE(st3, 3 * DBK) }
+  // straight-line pipeline as in gemm_bf16_dma (K % 128 == 0); 8 DMA loads per wave per stage
+  WH_ISSUE(st0, 0)
+  WH_ISSUE(st1, DBK)
+  WH_ISSUE(st2, 2 * DBK)
+  WH_SYNC(16)
+  WH_ISSUE(st3, 3 * DBK)
   WH_READ(st0, a0, b0)
-
-#define WH_STEP(SN, SREFILL, AC, BC, AN, BN, t)                                               \
-  if ((t) < nk) {                                                                             \
-    if ((t) + 1 < nk) {                                                                       \
-      WH_SYNC((t) + 1)                                                                        \
-      if ((t) + 4 < nk) { WH_ISSUE(SREFILL, ((t) + 4) * DBK) }                                \
-      WH_READ(SN, AN, BN)                                                                     \
-    }                                                                                         \
-    WH_MFMA(AC, BC)                                                                           \
+  int kt = 0;
+  for (; kt + 8 <= nk; kt += 4) {
+    WH_STEP(16, true, st0, (kt + 4) * DBK, st1, a0, b0, a1, b1)
+    WH_STEP(16, true, st1, (kt + 5) * DBK, st2, a1, b1, a0, b0)
+    WH_STEP(16, true, st2, (kt + 6) * DBK, st3, a0, b0, a1, b1)
+    WH_STEP(16, true, st3, (kt + 7) * DBK, st0, a1, b1, a0, b0)
   }
-
-  for (int kt = 0; kt < nk; kt += 4) {
-    WH_STEP(st1, st0, a0, b0, a1, b1, kt)
-    WH_STEP(st2, st1, a1, b1, a0, b0, kt + 1)
-    WH_STEP(st3, st2, a0, b0, a1, b1, kt + 2)
-    WH_STEP(st0, st3, a1, b1, a0, b0, kt + 3)
-  }
+  WH_STEP(16, false, st0, 0, st1, a0, b0, a1, b1)
+  WH_STEP(8, false, st0, 0, st2, a1, b1, a0, b0)
+  WH_STEP(0, false, st0, 0, st3, a0, b0, a1, b1)
+  WH_MFMA(a1, b1)
 #undef WH_READ
 #undef WH_MFMA
 #undef WH_SYNC
@@ -906,10 +904,11 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
     const int tiles2 = ((p.M + TB2 - 1) / TB2) * ((p.N + TB2 - 1) / TB2);
     const bool w4_ok = p.N % 8 == 0 &&
                        (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_GELU_PE || epi == EPI_CROSSKV);
+    const bool dma_ok = w4_ok && p.K % (4 * DBK) == 0;  // the LDS-DMA kernels run whole 4-stage rounds
     int v = p.variant;
-    if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (w4_ok ? 4 : 2) : 1;
-    if ((v == 3 || v == 4) && !w4_ok) v = 1;
-    if (v == 5 && !w4_ok) v = 1;
+    if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (dma_ok ? 4 : 2) : 1;
+    if ((v == 3 && !w4_ok) || (v == 4 && !dma_ok)) v = 1;
+    if (v == 5 && !dma_ok) v = 1;
     if (v == 5) {
       dim3 grid(tiles2, 1, p.batch);
 #define CALL(E) hipLaunchKernelGGL(gemm_bf16_dma4<E>, grid, dim3(256), 0, s, p)
