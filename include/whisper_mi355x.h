@@ -189,9 +189,11 @@ whisper_status whisper_layernorm_fused(const whisper_dims* dims, const void* h, 
  * y [M, N]; act 0 = none, 1 = exact GELU. dt = WHISPER_BF16 needs K % 64 == 0
  * and lda % 8 == 0. path: 0 auto, 1 tiled MFMA (automatic tile), 2 skinny
  * (M <= 128, K % 128 == 0); 3, 4, 5, 6, 7 force the 128x128, 256x256 8-wave,
- * 256x256 4-wave, 256x256 LDS-DMA-pipelined 8-wave and 4-wave tiled kernels
- * (for measurement; 5, 6 and 7 need N % 8 == 0 and fall back to 128x128
- * otherwise). */
+ * 256x256 4-wave, 256x256 LDS-DMA-pipelined 8-wave and 4-wave tiled kernels;
+ * 8 is the 8-wave LDS-DMA kernel with the plain tile order (6 and the
+ * automatic choice use the weight-panel-grouped order) (for
+ * measurement; 5-8 need N % 8 == 0 and the DMA kernels K % 128 == 0, and
+ * fall back to 128x128 otherwise). */
 whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const void* w, const float* bias, int M,
                               int N, int K, int act, void* y, int path, void* stream);
 

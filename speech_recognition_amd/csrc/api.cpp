@@ -686,7 +686,7 @@ whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const vo
   if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "linear: bad dtype");
   if (M <= 0 || N <= 0 || K <= 0 || lda <= 0) return fail(WHISPER_ERR_INVALID_ARG, "linear: sizes must be > 0");
   if (act != 0 && act != 1) return fail(WHISPER_ERR_INVALID_ARG, "linear: act must be 0 or 1");
-  if (path < 0 || path > 7) return fail(WHISPER_ERR_INVALID_ARG, "linear: path must be in 0..7");
+  if (path < 0 || path > 8) return fail(WHISPER_ERR_INVALID_ARG, "linear: path must be in 0..8");
   WH_CHECK(check_ptrs({x, w, y}, "linear"));
   if (bias && !aligned16(bias)) return fail(WHISPER_ERR_ALIGN, "linear: bias not 16-byte aligned");
   if (dt == WHISPER_BF16 && (K % 64 || lda % 8)) return fail(WHISPER_ERR_SHAPE, "linear: bf16 needs K % 64 == 0 and lda % 8 == 0");

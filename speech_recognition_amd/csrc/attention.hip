@@ -37,18 +37,25 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return bitcast<bf16x8>(u);
 }
 
-__global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__ qkv, int T, int H,
+__global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__ qkv, int T, int H, int B,
                                                          u16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) u16 sK[2][64 * 64];
   __shared__ __attribute__((aligned(16))) u16 sVt[2][64 * 64];
   const int d = H * 64, ld = 3 * d;
-  const int b = blockIdx.z, h = blockIdx.y;
+  // XCD-aware order (block L runs on XCD L % 8): the query tiles of one
+  // (chunk, head) get consecutive slots on one XCD, so its K/V are fetched
+  // into that XCD's L2 once instead of once per query tile.
+  const int QT = (T + 127) / 128;
+  const int L = blockIdx.x, xcdi = L & 7, jj = L >> 3;
+  const int bh = (jj / QT) * 8 + xcdi, qtile = jj - (jj / QT) * QT;
+  if (bh >= B * H) return;  // padding blocks ((chunk, head) count rounded up to a multiple of 8)
+  const int b = bh / H, h = bh - (bh / H) * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const u16* Qp = qkv + (long)b * T * ld + h * 64;
   const u16* Kp = Qp + d;
   const u16* Vp = Qp + 2 * d;
-  const int q0 = blockIdx.x * 128 + wave * 32;
+  const int q0 = qtile * 128 + wave * 32;
   const int qi = min(q0 + l32, T - 1);
 
   bf16x8 qf[4];
@@ -219,8 +226,8 @@ __global__ __launch_bounds__(64) void attn_encoder_f32(const float* __restrict__
 
 hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, void* out, hipStream_t s) {
   if (t == ACT_BF16)
-    hipLaunchKernelGGL(attn_encoder_bf16, dim3((T + 127) / 128, H, B), dim3(256), 0, s, (const u16*)qkv, T, H,
-                       (u16*)out);
+    hipLaunchKernelGGL(attn_encoder_bf16, dim3((T + 127) / 128 * ((B * H + 7) / 8) * 8), dim3(256), 0, s,
+                       (const u16*)qkv, T, H, B, (u16*)out);
   else
     hipLaunchKernelGGL(attn_encoder_f32, dim3((T + 63) / 64, H, B), dim3(64), 0, s, (const float*)qkv, T, H,
                        (float*)out);
@@ -228,10 +235,8 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 }
 
 // ------------------------------------------------------------------ decoder self-attention over e4m3 codes
-// One workgroup per (head, row). Keys 0..n-1 (n = lengths[b] + len_add) are
-// 64-byte code rows read as 4 lanes x 16 codes. Each lane issues all of its
-// loads of a batch (8 keys, 128 B) before decoding any of them, so a whole
-// cache row of up to 512 keys is in flight at once; scores stay in LDS.
+// Keys 0..n-1 (n = lengths[b] + len_add) are 64-byte code rows read as 4
+// lanes x 16 codes.
 constexpr int DEC_MAX_CAP = 4096;
 
 __device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {

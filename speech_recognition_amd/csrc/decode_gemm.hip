@@ -49,7 +49,14 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   __shared__ float2 s_st[XIN ? DG_WAVES : 1][MR];
   __shared__ float s_mu[MR], s_rs[MR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16 * CB, m0 = blockIdx.y * MR;
+  // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs
+  // (block L on XCD L % 8), so the row tiles of one column tile are given
+  // consecutive slots on one XCD and share its L2 copy of the weight slice.
+  const int RT = (p.M + MR - 1) / MR, CT = (p.N + 16 * CB - 1) / (16 * CB);
+  const int L = blockIdx.x, xcd = L & 7, jj = L >> 3;
+  const int ct = (jj / RT) * 8 + xcd, rt = jj - (jj / RT) * RT;
+  if (ct >= CT) return;  // padding blocks (CT rounded up to a multiple of 8)
+  const int n0 = ct * 16 * CB, m0 = rt * MR;
   const int M = p.M, N = p.N, K = p.K;
   const int S = K / 32;
   const int s0 = wave * S / DG_WAVES, s1 = (wave + 1) * S / DG_WAVES;  // this wave's k-steps
@@ -269,7 +276,8 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 
 template <int PRO, int EPI, int MB, int CB, int NS>
 static hipError_t dec_launch_ns(const DecGemmParams& p, hipStream_t s) {
-  const dim3 grid((p.N + 16 * CB - 1) / (16 * CB), (p.M + 16 * MB - 1) / (16 * MB));
+  const int CT = (p.N + 16 * CB - 1) / (16 * CB), RT = (p.M + 16 * MB - 1) / (16 * MB);
+  const dim3 grid(((CT + 7) / 8) * 8 * RT);
   hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NS>), grid, dim3(DG_WAVES * 64), 0, s, p);
   return hipGetLastError();
 }

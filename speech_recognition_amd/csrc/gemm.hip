@@ -455,8 +455,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_256w4(GemmParams p) {
 // global->LDS loads (16 bytes per lane, no staging registers) issued three
 // stages ahead, with one barrier per stage. 512 threads = 2x4 waves of 128x64
 // sub-tiles (8x4 MFMA 16x16x32). Each 1 KB DMA block is 16 rows x 64 bytes;
-// lane L fills row L/4, slot L%4 with global chunk (L%4) ^ ((L/16)%4), so a
-// fragment read (16 rows, one chunk) hits 16 distinct 16-byte bank groups.
+// lane L fills row L/4, slot L%4 with global chunk (L%4) ^ ((L/8)%4), the
+// swizzle of dswz() below, so fragment reads are free of bank conflicts.
 // The stages are separate LDS objects so the compiler's wait insertion can
 // tell a stage being read from the stages being filled.
 constexpr int DBK = 32;
@@ -472,9 +472,29 @@ __device__ __forceinline__ void tile_order(int bid, int tiles_m, int tiles_n, in
   tm = bid / tiles_n;
   tn = bid - tm * tiles_n;
 }
+
+// Grouped order: each XCD walks a group of GN tile-columns down the tile-rows
+// before moving to the next group, so the GN weight panels it reads stay in
+// its L2 (the whole weight, 3-13 MB, does not fit in one XCD's 4 MB) while
+// the activation panels stream past once per group.
+template <int GN>
+__device__ __forceinline__ void tile_order_grouped(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nblk = tiles_m * tiles_n;
+  if ((nblk & 7) != 0) { tile_order(bid, tiles_m, tiles_n, tm, tn); return; }
+  const int t = (bid & 7) * (nblk >> 3) + (bid >> 3);  // contiguous logical range per XCD, as above
+  const int gsz = GN * tiles_m;                         // tiles per full column group
+  const int grp = t / gsz, r = t - grp * gsz;
+  const int gn = min(GN, tiles_n - grp * GN);           // width of this (possibly last, narrower) group
+  tm = r / gn;
+  tn = grp * GN + (r - tm * gn);
+}
 constexpr int DSTAGE = 2 * TB2 * DBK;  // u16 elements per stage (A then B)
 
-__device__ __forceinline__ int dswz(int row, int kc) { return row * DBK + ((kc ^ ((row >> 2) & 3)) << 3); }
+// LDS serves a 16-byte-per-lane read in groups of 8 lanes over a 128-byte
+// bank window (32 banks), so the 8 rows one group reads (64 B apart: two per
+// window) must land on 8 distinct 16-byte slots: chunk kc of row r is stored
+// at slot kc ^ ((r >> 1) & 3).
+__device__ __forceinline__ int dswz(int row, int kc) { return row * DBK + ((kc ^ ((row >> 1) & 3)) << 3); }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
 #define WH_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -491,7 +511,7 @@ __device__ __forceinline__ void dma16(const u16* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
-template <int EPI>
+template <int EPI, int ORDER>
 __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) u16 st0[DSTAGE];
   __shared__ __attribute__((aligned(1024))) u16 st1[DSTAGE];
@@ -502,14 +522,15 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
   const int tiles_n = (p.N + TB2 - 1) / TB2;
   const int tiles_m = (p.M + TB2 - 1) / TB2;
   int tm, tn;
-  tile_order(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  if constexpr (ORDER == 1) tile_order_grouped<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  else tile_order(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int z = blockIdx.z;
   const u16* A = (const u16*)p.A + (long)z * p.strideA;
   const u16* B = (const u16*)p.B;
   const int m0 = tm * TB2, n0 = tn * TB2;
 
   // DMA: wave w fills A blocks w, w+8 and B blocks w, w+8 (16 rows each)
-  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 3) & 3);  // global chunk for LDS slot lane & 3 of row lr
   const u16* ga0 = A + (long)min(m0 + wave * 16 + lr, p.M - 1) * p.lda + lc * 8;
   const u16* ga1 = A + (long)min(m0 + (wave + 8) * 16 + lr, p.M - 1) * p.lda + lc * 8;
   const u16* gb0 = B + (long)min(n0 + wave * 16 + lr, p.N - 1) * p.ldb + lc * 8;
@@ -658,7 +679,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dma4(GemmParams p) {
   const int m0 = tm * TB2, n0 = tn * TB2;
 
   // DMA: wave w fills A blocks w, w+4, w+8, w+12 and the same B blocks (16 rows each)
-  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 3) & 3);  // global chunk for LDS slot lane & 3 of row lr
   const u16* ga[4];
   const u16* gb[4];
   int la[4], lb[4];
@@ -921,9 +942,22 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
 #undef CALL
       return hipGetLastError();
     }
+    if (v == 6 && !dma_ok) v = 1;
+    if (v == 6) {  // plain (ungrouped) tile order, for comparison
+      dim3 grid(tiles2, 1, p.batch);
+#define CALL(E) hipLaunchKernelGGL((gemm_bf16_dma<E, 0>), grid, dim3(512), 0, s, p)
+      switch (epi) {
+        case EPI_STORE: CALL(EPI_STORE); break;
+        case EPI_GELU: CALL(EPI_GELU); break;
+        case EPI_GELU_PE: CALL(EPI_GELU_PE); break;
+        default: CALL(EPI_CROSSKV); break;
+      }
+#undef CALL
+      return hipGetLastError();
+    }
     if (v == 4) {
       dim3 grid(tiles2, 1, p.batch);
-#define CALL(E) hipLaunchKernelGGL(gemm_bf16_dma<E>, grid, dim3(512), 0, s, p)
+#define CALL(E) hipLaunchKernelGGL((gemm_bf16_dma<E, 1>), grid, dim3(512), 0, s, p)
       switch (epi) {
         case EPI_STORE: CALL(EPI_STORE); break;
         case EPI_GELU: CALL(EPI_GELU); break;

@@ -108,7 +108,8 @@ def test_layernorm_fused(act, d, M):
     ("bf16", 530, 264, 320, 1, 6), ("bf16", 1500, 1280, 1280, 0, 6), ("bf16", 3000, 640, 384, 1, 6),
     ("bf16", 257, 2056, 64, 0, 6), ("bf16", 700, 520, 192, 1, 6),
     ("bf16", 1500, 1280, 1280, 0, 7), ("bf16", 3000, 640, 384, 1, 7), ("bf16", 257, 2056, 64, 0, 7),
-    ("bf16", 700, 520, 192, 1, 7),
+    ("bf16", 700, 520, 192, 1, 7), ("bf16", 1500, 1280, 1280, 0, 8), ("bf16", 3000, 640, 384, 1, 8),
+    ("bf16", 700, 520, 256, 1, 8), ("bf16", 1024, 2560, 256, 0, 8),
     ("bf16", 64, 1280, 1280, 0, 2), ("bf16", 90, 200, 5120, 1, 2), ("bf16", 1, 51, 128, 0, 2),
     ("f32", 77, 130, 240, 1, 1)])
 def test_linear(act, M, N, K, gelu, path):
