@@ -190,10 +190,13 @@ whisper_status whisper_layernorm_fused(const whisper_dims* dims, const void* h, 
  * and lda % 8 == 0. path: 0 auto, 1 tiled MFMA (automatic tile), 2 skinny
  * (M <= 128, K % 128 == 0); 3, 4, 5, 6, 7 force the 128x128, 256x256 8-wave,
  * 256x256 4-wave, 256x256 LDS-DMA-pipelined 8-wave and 4-wave tiled kernels;
- * 8 is the 8-wave LDS-DMA kernel with the plain tile order (6 and the
- * automatic choice use the weight-panel-grouped order) (for
- * measurement; 5-8 need N % 8 == 0 and the DMA kernels K % 128 == 0, and
- * fall back to 128x128 otherwise). */
+ * 8 is the 8-wave LDS-DMA kernel with the plain tile order (6 uses the
+ * weight-panel-grouped order); 9 is the persistent 8-wave LDS-DMA kernel
+ * (one workgroup per compute unit, the ring running on across tiles), which
+ * the automatic choice takes for large bf16 GEMMs without activation or with
+ * GELU when N % 256 == 0, K % 128 == 0, K >= 256 and y is under 2 GB. 5-9
+ * are for measurement; 5-8 need N % 8 == 0 and the DMA kernels K % 128 == 0,
+ * and fall back to 128x128 otherwise; 9 falls back to 6. */
 whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const void* w, const float* bias, int M,
                               int N, int K, int act, void* y, int path, void* stream);
 

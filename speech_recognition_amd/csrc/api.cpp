@@ -686,14 +686,14 @@ whisper_status whisper_linear(whisper_dtype dt, const void* x, int lda, const vo
   if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "linear: bad dtype");
   if (M <= 0 || N <= 0 || K <= 0 || lda <= 0) return fail(WHISPER_ERR_INVALID_ARG, "linear: sizes must be > 0");
   if (act != 0 && act != 1) return fail(WHISPER_ERR_INVALID_ARG, "linear: act must be 0 or 1");
-  if (path < 0 || path > 8) return fail(WHISPER_ERR_INVALID_ARG, "linear: path must be in 0..8");
+  if (path < 0 || path > 9) return fail(WHISPER_ERR_INVALID_ARG, "linear: path must be in 0..9");
   WH_CHECK(check_ptrs({x, w, y}, "linear"));
   if (bias && !aligned16(bias)) return fail(WHISPER_ERR_ALIGN, "linear: bias not 16-byte aligned");
   if (dt == WHISPER_BF16 && (K % 64 || lda % 8)) return fail(WHISPER_ERR_SHAPE, "linear: bf16 needs K % 64 == 0 and lda % 8 == 0");
   if (path == 2 && (dt != WHISPER_BF16 || M > 128 || K % 128)) return fail(WHISPER_ERR_SHAPE, "linear: skinny path needs bf16, M <= 128, K % 128 == 0");
   (void)hipGetLastError();
   GemmParams p = gp(x, lda, w, K, M, N, K, bias, y, N);
-  p.variant = path >= 3 ? path - 2 : 0;
+  p.variant = path == 9 ? 9 : path >= 3 ? path - 2 : 0;
   const Epi epi = act ? EPI_GELU : EPI_STORE;
   const bool skinny = path == 2 || (path == 0 && dt == WHISPER_BF16 && M <= 128 && K % 128 == 0);
   WH_TRY(skinny ? launch_gemm_skinny(act_of(dt), epi, p, S(stream)) : launch_gemm(act_of(dt), epi, p, S(stream)));

@@ -656,6 +656,208 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
     }
   }
 }
+// ------------------------------------------------------------------ bf16 MFMA, 256x256, LDS DMA pipeline, persistent
+// The 8-wave LDS-DMA kernel above, run as one workgroup per CU that walks a
+// share of the tiles. The 4-stage ring runs on across tile boundaries: the
+// last four k-steps of a tile load the first four stages of the next one (and
+// its bias), so a tile's 32 stores per lane are issued with the next tile's
+// loads already in flight and drain behind its first k-steps instead of
+// stalling every CU at once. Loads use buffer addressing (scalar resource and
+// k offset, one 32-bit VGPR offset per stream); stores use the buffer range
+// check to drop rows past M, so every wave issues the same, fixed number of
+// memory operations per tile and the vmcnt waits below are exact:
+//   in-tile wait for stage s+1: the 2 younger stages (8 loads) may be in flight;
+//   first three waits of a tile: also the previous tile's 32 stores (40);
+//   tail waits: also the next tile's bias load (9);
+//   tile head (next tile's stage 0): its stages 1-3 and the 32 stores (44).
+// Requirements (checked by the launcher): batch 1, N % 256 == 0, K % 128 == 0,
+// K >= 256, operands and output under 2 GB.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);                             // range in bytes
+  r.w = 0x00020000;                                                             // gfx9 raw-buffer format word
+  return r;
+}
+// One 16-byte-per-lane buffer load straight into the 1 KB LDS block at `lds`
+// (lane L writes bytes 16L..16L+15): address = resource base + voff + soff.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rsrc),
+               "s"(soff)
+               : "memory", "m0");
+}
+
+// logical tile t -> (tm, tn) in column groups of 4 tile-columns, tile-rows within a group
+__device__ __forceinline__ void grouped_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int gsz = 4 * tiles_m, grp = t / gsz, r = t - grp * gsz;
+  const int gn = min(4, tiles_n - grp * 4);
+  tm = r / gn;
+  tn = grp * 4 + (r - tm * gn);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) u16 st0[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st1[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st2[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st3[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) float bsl[2][TB2];  // bias of the current / next tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles_m = (p.M + TB2 - 1) / TB2, tiles_n = p.N / TB2, T = tiles_m * tiles_n;
+  // XCD x (= blockIdx.x % 8) owns the logical tiles [lo, hi); its workgroups
+  // take every nslot-th one, so the tiles running together on one XCD are
+  // consecutive in the grouped order and share weight and activation panels.
+  const int x = blockIdx.x & 7, nslot = (gridDim.x - x + 7) >> 3;
+  const int lo = (int)(((long)T * x) >> 3), hi = (int)(((long)T * (x + 1)) >> 3);
+  int L = lo + (blockIdx.x >> 3);
+  if (L >= hi) return;
+  int tm, tn;
+  grouped_coords(L, tiles_m, tiles_n, tm, tn);
+
+  const i32x4 ra = buf_rsrc(p.A, (uint32_t)(((long)(p.M - 1) * p.lda + p.K) * 2));
+  const i32x4 rb = buf_rsrc(p.B, (uint32_t)(((long)(p.N - 1) * p.ldb + p.K) * 2));
+  const i32x4 rbias = buf_rsrc(p.bias ? (const void*)p.bias : p.A, p.bias ? (uint32_t)p.N * 4 : 0u);
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 3) & 3);  // global chunk for LDS slot lane & 3 of row lr
+  const uint32_t la0 = wave * 16 * DBK, la1 = (wave + 8) * 16 * DBK;
+  const uint32_t lb0 = TB2 * DBK + wave * 16 * DBK, lb1 = TB2 * DBK + (wave + 8) * 16 * DBK;
+  uint32_t oa0, oa1, ob0, ob1;  // byte offsets of this lane's 16-byte chunk in its four DMA rows
+#define WH_OFFS(TM, TN)                                                                              \
+  oa0 = ((uint32_t)min((TM) * TB2 + wave * 16 + lr, p.M - 1) * (uint32_t)p.lda + lc * 8) * 2;        \
+  oa1 = ((uint32_t)min((TM) * TB2 + (wave + 8) * 16 + lr, p.M - 1) * (uint32_t)p.lda + lc * 8) * 2;  \
+  ob0 = ((uint32_t)((TN) * TB2 + wave * 16 + lr) * (uint32_t)p.ldb + lc * 8) * 2;                    \
+  ob1 = ((uint32_t)((TN) * TB2 + (wave + 8) * 16 + lr) * (uint32_t)p.ldb + lc * 8) * 2;
+  WH_OFFS(tm, tn)
+#define WH_ISSUE(S, k)                                       \
+  dma16_buf(ra, oa0, (k) * 2, lds_addr((S) + la0));          \
+  dma16_buf(ra, oa1, (k) * 2, lds_addr((S) + la1));          \
+  dma16_buf(rb, ob0, (k) * 2, lds_addr((S) + lb0));          \
+  dma16_buf(rb, ob1, (k) * 2, lds_addr((S) + lb1));
+  // every wave loads the whole 1 KB bias row (identical bytes), so each
+  // wave's own wait covers it
+#define WH_BIAS(SLOT, TN) \
+  dma16_buf(rbias, lane * 16, (TN) * TB2 * 4, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)(bsl[SLOT]));
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, kc = lane >> 4;
+  const int nk = p.K / DBK;
+  bf16x8 a0[8], b0[4], a1[8], b1[4];
+#define WH_READ(S, AF, BF)                                                                    \
+  _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+    BF[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + j * 16 + fr, kc))); \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+    AF[i] = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));
+#define WH_MFMA(AF, BF)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(BF[j], AF[i], acc[i][j], 0, 0, 0);
+#define WH_SYNC(n)             \
+  {                            \
+    WH_WAIT_VM_LGKM0(n);       \
+    __builtin_amdgcn_s_barrier(); \
+  }
+  // one k-step: wait for the stage whose fragments are read next, refill the
+  // buffer the current stage came from, read the next fragments, then the
+  // current stage's MFMAs
+#define WH_STEP(WAITN, SREFILL, KREFILL, SN, AC, BC, AN, BN) \
+  WH_SYNC(WAITN)                                             \
+  WH_ISSUE(SREFILL, KREFILL)                                 \
+  WH_READ(SN, AN, BN)                                        \
+  WH_MFMA(AC, BC)
+#define WH_ROUND(W0, W1, W2, W3, KT)                                \
+  WH_STEP(W0, st0, ((KT) + 4) * DBK, st1, a0, b0, a1, b1)           \
+  WH_STEP(W1, st1, ((KT) + 5) * DBK, st2, a1, b1, a0, b0)           \
+  WH_STEP(W2, st2, ((KT) + 6) * DBK, st3, a0, b0, a1, b1)           \
+  WH_STEP(W3, st3, ((KT) + 7) * DBK, st0, a1, b1, a0, b0)
+
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)((long)p.M * p.ldc * 2), 0x00020000);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  // the first tile starts like every later one: bias and stages 0-3 in
+  // flight, then 32 stores (here out of range, so dropped) behind them
+  WH_BIAS(0, tn)
+  WH_ISSUE(st0, 0)
+  WH_ISSUE(st1, DBK)
+  WH_ISSUE(st2, 2 * DBK)
+  WH_ISSUE(st3, 3 * DBK)
+#pragma unroll
+  for (int q = 0; q < 32; ++q) __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rc, 0x80000000u, 0, 0);
+  asm volatile("" ::: "memory");
+  int par = 0;
+  for (;;) {
+    WH_SYNC(44)  // this tile's stage 0 (and bias) has landed
+    WH_READ(st0, a0, b0)
+    WH_ROUND(40, 40, 40, 8, 0)
+    for (int kt = 4; kt + 8 <= nk; kt += 4) {
+      WH_ROUND(8, 8, 8, 8, kt)
+    }
+    // tail: the next tile's bias and stages 0-3 (when there is no next tile,
+    // the same tile's are loaded again so that the wait counts stay exact)
+    const int Ln = L + nslot;
+    const bool more = Ln < hi;
+    int tmn = tm, tnn = tn;
+    if (more) grouped_coords(Ln, tiles_m, tiles_n, tmn, tnn);
+    const int m0 = tm * TB2, n0 = tn * TB2;
+    WH_OFFS(tmn, tnn)
+    WH_SYNC(8)
+    WH_BIAS(par ^ 1, tnn)
+    WH_ISSUE(st0, 0)
+    WH_READ(st1, a1, b1)
+    WH_MFMA(a0, b0)
+    WH_STEP(9, st1, DBK, st2, a1, b1, a0, b0)
+    WH_STEP(9, st2, 2 * DBK, st3, a0, b0, a1, b1)
+    WH_SYNC(63)  // all waves are done reading buffer 3; nothing to wait for in vmcnt
+    WH_ISSUE(st3, 3 * DBK)
+    WH_MFMA(a1, b1)
+    // epilogue: bias from LDS, activation, bf16 pairs, 32 buffer stores per lane;
+    // rows past M get an offset beyond the range and are dropped
+    {
+      const int en = wn * 64 + (lane >> 4) * 4;
+      float4 bj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bj[j] = p.bias ? *(const float4*)(&bsl[par][en + j * 16]) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + (lane & 15);
+        const uint32_t roff = m < p.M ? ((uint32_t)m * (uint32_t)p.ldc + (uint32_t)(n0 + en)) * 2 : 0x80000000u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v0 = acc[i][j][0] + bj[j].x, v1 = acc[i][j][1] + bj[j].y;
+          float v2 = acc[i][j][2] + bj[j].z, v3 = acc[i][j][3] + bj[j].w;
+          if constexpr (EPI == EPI_GELU) {
+            v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3);
+          }
+          const u32x2 u = {f2bf2(v0, v1), f2bf2(v2, v3)};
+          __builtin_amdgcn_raw_buffer_store_b64(u, rc, roff + j * 32, 0, 0);
+          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    // the 32 stores must all be issued before the next wait: its count includes them
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more) break;
+    L = Ln; tm = tmn; tn = tnn; par ^= 1;
+  }
+  WH_WAIT_VM(0);  // no LDS-DMA write may still be in flight when the workgroup ends
+#undef WH_READ
+#undef WH_MFMA
+#undef WH_SYNC
+#undef WH_STEP
+#undef WH_ROUND
+#undef WH_ISSUE
+#undef WH_BIAS
+#undef WH_OFFS
+}
+
 // ------------------------------------------------------------------ bf16 MFMA, 256x256, LDS DMA pipeline, 4 waves
 // The same 4-stage LDS ring (BK = 32) fed by direct global->LDS loads, with
 // 256 threads = 2x2 waves of 128x128 sub-tiles (8x8 MFMA 16x16x32, 256 fp32
@@ -919,6 +1121,19 @@ __global__ __launch_bounds__(256) void gemm_f32_simt(GemmParams p) {
     default: return hipErrorInvalidValue;           \
   }
 
+// compute units of the current device (one persistent workgroup each)
+static int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (t == ACT_BF16) {
@@ -926,8 +1141,12 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
     const bool w4_ok = p.N % 8 == 0 &&
                        (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_GELU_PE || epi == EPI_CROSSKV);
     const bool dma_ok = w4_ok && p.K % (4 * DBK) == 0;  // the LDS-DMA kernels run whole 4-stage rounds
+    // persistent variant: whole 256-column tiles, one workgroup per CU
+    const bool pers_ok = dma_ok && p.batch == 1 && p.N % TB2 == 0 && p.K >= 8 * DBK && (epi == EPI_STORE || epi == EPI_GELU) &&
+                         (long)p.M * p.ldc * 2 < (1L << 31) && ((long)(p.M - 1) * p.lda + p.K) * 2 < (1L << 32) &&
+                         ((long)(p.N - 1) * p.ldb + p.K) * 2 < (1L << 32) && p.ldc >= p.N;
     int v = p.variant;
-    if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (dma_ok ? 4 : 2) : 1;
+    if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (pers_ok ? 9 : dma_ok ? 4 : 2) : 1;
     if ((v == 3 && !w4_ok) || (v == 4 && !dma_ok)) v = 1;
     if (v == 5 && !dma_ok) v = 1;
     if (v == 5) {
@@ -940,6 +1159,13 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
         default: CALL(EPI_CROSSKV); break;
       }
 #undef CALL
+      return hipGetLastError();
+    }
+    if (v == 9 && !pers_ok) v = dma_ok ? 4 : 1;
+    if (v == 9) {
+      dim3 grid(min(num_cus(), ((p.M + TB2 - 1) / TB2) * (p.N / TB2) + 7));
+      if (epi == EPI_GELU) hipLaunchKernelGGL(gemm_bf16_persist<EPI_GELU>, grid, dim3(512), 0, s, p);
+      else hipLaunchKernelGGL(gemm_bf16_persist<EPI_STORE>, grid, dim3(512), 0, s, p);
       return hipGetLastError();
     }
     if (v == 6 && !dma_ok) v = 1;

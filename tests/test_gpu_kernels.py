@@ -110,19 +110,33 @@ def test_layernorm_fused(act, d, M):
     ("bf16", 1500, 1280, 1280, 0, 7), ("bf16", 3000, 640, 384, 1, 7), ("bf16", 257, 2056, 64, 0, 7),
     ("bf16", 700, 520, 192, 1, 7), ("bf16", 1500, 1280, 1280, 0, 8), ("bf16", 3000, 640, 384, 1, 8),
     ("bf16", 700, 520, 256, 1, 8), ("bf16", 1024, 2560, 256, 0, 8),
+    # persistent kernel: ragged M, more tiles than compute units (workgroups cross tile
+    # boundaries), the smallest K it takes (8 k-steps), GELU, a grid with empty XCD ranges,
+    # and a shape it does not take (falls back)
+    ("bf16", 1500, 1280, 1280, 0, 9), ("bf16", 4100, 5120, 384, 1, 9), ("bf16", 4096, 4608, 256, 0, 9),
+    ("bf16", 300, 256, 256, 1, 9), ("bf16", 3000, 1280, 5120, 0, 9), ("bf16", 700, 520, 256, 1, 9),
     ("bf16", 64, 1280, 1280, 0, 2), ("bf16", 90, 200, 5120, 1, 2), ("bf16", 1, 51, 128, 0, 2),
     ("f32", 77, 130, 240, 1, 1)])
 def test_linear(act, M, N, K, gelu, path):
-    say(f"linear act={act} M={M} N={N} K={K} gelu={gelu} path={path}")
+    _linear_case(act, M, N, K, gelu, path, True)
+
+
+@pytest.mark.parametrize("path", [0, 9])
+def test_linear_no_bias(path):
+    _linear_case("bf16", 1000, 2560, 512, 1, path, False)
+
+
+def _linear_case(act, M, N, K, gelu, path, with_bias):
+    say(f"linear act={act} M={M} N={N} K={K} gelu={gelu} path={path} bias={with_bias}")
     bf = act == "bf16"
     dt = torch.bfloat16 if bf else torch.float32
     x = gen_normal(DEV, (M, K), 9, 6, 10, bf16=bf).to(dt)
     w = gen_normal(DEV, (N, K), 9, 6, 11, std=0.05, bf16=bf).to(dt)
-    b = gen_normal(DEV, (N,), 9, 6, 12, std=0.5)
+    b = gen_normal(DEV, (N,), 9, 6, 12, std=0.5) if with_bias else None
     y = torch.empty(M, N, dtype=dt, device=DEV)
     L.whisper_linear(L.WHISPER_BF16 if bf else L.WHISPER_F32, x, K, w, b, M, N, K, gelu, y, path)
     torch.cuda.synchronize()
-    ref = O.linear(host(x), host(w), host(b))
+    ref = O.linear(host(x), host(w), host(b) if with_bias else np.zeros(N))
     if gelu:
         ref = O.gelu(ref)
     assert rel_err(host(y), ref) < TOL
