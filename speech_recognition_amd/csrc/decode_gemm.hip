@@ -292,7 +292,8 @@ static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
   return dec_launch_ns<PRO, EPI, MB, CB, 0>(p, s);
 }
 
-// Tile shapes with MB * CB <= 4 (larger ones run out of registers).
+// Tile shapes with MB * CB <= 4, and one 16-row block of 80 columns (larger
+// ones run out of registers).
 template <int PRO, int EPI>
 static hipError_t dec_launch(const DecGemmParams& p, int mb, int cb, hipStream_t s) {
   if (cb == 1 && mb == 1) return dec_launch_t<PRO, EPI, 1, 1>(p, s);
@@ -301,17 +302,25 @@ static hipError_t dec_launch(const DecGemmParams& p, int mb, int cb, hipStream_t
   if (cb == 2 && mb == 1) return dec_launch_t<PRO, EPI, 1, 2>(p, s);
   if (cb == 2 && mb == 2) return dec_launch_t<PRO, EPI, 2, 2>(p, s);
   if (cb == 4 && mb == 1) return dec_launch_t<PRO, EPI, 1, 4>(p, s);
+  if (cb == 5 && mb == 1) return dec_launch_t<PRO, EPI, 1, 5>(p, s);
   return hipErrorInvalidValue;
 }
 
 // Rows (16 * mb) and columns (16 * cb) per workgroup. One 16-row block per
 // workgroup keeps the activation slice a workgroup streams small (it is
 // re-read by every column tile); 64 columns for N of 2K-4K (about one
-// workgroup per CU at batch 64), 32 otherwise. Chosen by measurement at batch 64.
+// workgroup per CU at batch 64), 80 for N = 4d, 32 otherwise. Chosen by
+// measurement at batch 64: the time follows the bytes the busiest compute
+// unit streams (about 40 GB/s per unit), so the tile count is matched to the
+// 256 units.
 void dec_gemm_tiles(int M, int N, int& mb, int& cb) {
   (void)M;
   mb = 1;
   cb = (N >= 2048 && N <= 4096) || N > 16384 ? 4 : 2;
+  // the MLP up-projection (N = 4d): 80-column tiles give one workgroup per
+  // compute unit at batch <= 64 (5120 / 80 * 4 = 256) instead of 2.5, so no
+  // unit streams three tiles while others stream two
+  if (N % 80 == 0 && N > 4096 && N <= 8192) cb = 5;
 }
 
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s) {
