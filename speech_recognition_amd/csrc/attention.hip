@@ -27,14 +27,11 @@ __device__ __forceinline__ int vt_swz(int e, int key) {
   return e * 64 + ((((key >> 2) ^ (e & 15))) << 2) + (key & 3);
 }
 
+// eight fp32 -> bf16 with the gfx950 converter (round to nearest even; the
+// probabilities packed here are finite)
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                               float a7) {
-  uint4 u;
-  u.x = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
-  u.y = (uint32_t)f2bf(a2) | ((uint32_t)f2bf(a3) << 16);
-  u.z = (uint32_t)f2bf(a4) | ((uint32_t)f2bf(a5) << 16);
-  u.w = (uint32_t)f2bf(a6) | ((uint32_t)f2bf(a7) << 16);
-  return bitcast<bf16x8>(u);
+  return bitcast<bf16x8>(make_uint4(f2bf2(a0, a1), f2bf2(a2, a3), f2bf2(a4, a5), f2bf2(a6, a7)));
 }
 
 __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__ qkv, int T, int H, int B,
@@ -97,12 +94,12 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
   const float c = 1.4426950408889634f * 0.125f;  // log2(e) / sqrt(64)
   const int nkb = (T + 63) / 64;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One 64-key tile: S^T = K Q^T, online softmax (base-2 exponent with the
+  // 1/sqrt(64) scale folded in), O^T += V^T P^T. Only the last tile can run
+  // past T, so the key mask is compiled into that copy alone; the output rows
+  // are rescaled only when some lane's running max moved.
+  auto tile = [&](const int kb, const bool last) {
     const int cur = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
     f32x16 st[2];
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
@@ -114,7 +111,7 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
         st[j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[j2], 0, 0, 0);
       }
     }
-    if (kb * 64 + 64 > T) {
+    if (last) {
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2)
 #pragma unroll
@@ -130,23 +127,26 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[j2][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * c);
     const float mc = m_new * c;
     float psum = 0.f;
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(st[j2][i], c, -mc));
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[j2][i], c, -mc));
         st[j2][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
+    if (__any(m_new > m_run)) {  // wave-uniform: exp2(0) = 1 for the lanes whose max did not move
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[e][i] *= alpha;
+    }
+    l_run += psum;
     m_run = m_new;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[e][i] *= alpha;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int j2 = t >> 1, hs = (t & 1) * 8;
@@ -161,9 +161,20 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
         o[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(vv), pf, o[eb], 0, 0, 0);
       }
     }
-    if (kb + 1 < nkb) sstore(cur ^ 1);
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const bool ragged = nkb * 64 > T;
+  const int nfull = ragged ? nkb - 1 : nkb;
+  for (int kb = 0; kb < nfull; ++kb) {
+    if (kb + 1 < nkb) gload(kb + 1);
+    tile(kb, false);
+    if (kb + 1 < nkb) sstore((kb & 1) ^ 1);
     __syncthreads();
   }
+  if (ragged) tile(nkb - 1, true);
   const float l = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l;
   const int q = q0 + l32;
