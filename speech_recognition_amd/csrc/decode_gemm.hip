@@ -45,7 +45,7 @@ template <int PRO, int EPI, int MB, int CB, int NS>
 __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
   constexpr int MR = MB * 16;
   constexpr bool XIN = PRO == PRO_X;
-  __shared__ f32x4 red[DG_WAVES - 1][MB * CB][64];
+  __shared__ f32x4 red[DG_WAVES][MB * CB][64];
   __shared__ float2 s_st[XIN ? DG_WAVES : 1][MR];
   __shared__ float s_mu[MR], s_rs[MR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -70,32 +70,29 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1);
 
-  // ---- epilogue operands, fetched before the main loads so that the epilogue
-  // (run by wave 0) makes no memory round trip of its own: its stores may
-  // alias these addresses, so loads left in the store loop would serialise.
+  // ---- epilogue: the MB * CB output blocks (16 rows x 16 columns) go to waves
+  // 0 .. MB*CB-1, one each. A block's operands are fetched by its wave before
+  // the main loads, so the epilogue makes no memory round trip of its own
+  // (its stores may alias these addresses: loads left in the store loop would
+  // serialise).
   constexpr bool RES = EPI == DEPI_RESID, QKV = EPI == DEPI_QKV;
-  float e_bias[CB], e_c1[CB];
-  float e_x[RES ? MB : 1][RES ? CB : 1][4];
-  int e_pos[QKV ? MB : 1][4];
-  float e_inv[2] = {0.f, 0.f};
-  if (wave == 0) {
+  static_assert(MB * CB <= DG_WAVES, "one output block per wave");
+  const bool ewave = wave < MB * CB;
+  const int emb = ewave ? wave / CB : 0, ecb = ewave ? wave - (wave / CB) * CB : 0;
+  const int en = n0 + ecb * 16 + (lane & 15);  // this lane's output column
+  float e_bias = 0.f, e_c1 = 0.f, e_x[4] = {0.f, 0.f, 0.f, 0.f}, e_inv[2] = {0.f, 0.f};
+  int e_pos[4] = {0, 0, 0, 0};
+  if (ewave) {
+    const int n = min(en, N - 1);
+    e_bias = p.bias ? p.bias[n] : 0.f;
+    e_c1 = XIN ? p.c1[n] : 0.f;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int n = min(n0 + cb * 16 + (lane & 15), N - 1);
-      e_bias[cb] = p.bias ? p.bias[n] : 0.f;
-      e_c1[cb] = XIN ? p.c1[n] : 0.f;
-      if constexpr (RES) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) e_x[mb][cb][r] = p.X[(long)min(m0 + mb * 16 + (lane >> 4) * 4 + r, M - 1) * N + n];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int m = min(m0 + emb * 16 + (lane >> 4) * 4 + r, M - 1);
+      if constexpr (RES) e_x[r] = p.X[(long)m * N + n];
+      if constexpr (QKV) e_pos[r] = p.lengths[m];
     }
     if constexpr (QKV) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e_pos[mb][r] = p.lengths[min(m0 + mb * 16 + (lane >> 4) * 4 + r, M - 1)];
       e_inv[0] = 1.0f / p.kv_scales[p.kv_layer * 2];
       e_inv[1] = 1.0f / p.kv_scales[p.kv_layer * 2 + 1];
     }
@@ -199,12 +196,10 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
       if (lane < 16) s_st[wave][mb * 16 + lane] = make_float2(mu, m2);
     }
   }
-  if (wave > 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) red[wave - 1][mb * CB + cb][lane] = acc[mb][cb];
-  }
+    for (int cb = 0; cb < CB; ++cb) red[wave][mb * CB + cb][lane] = acc[mb][cb];
   __syncthreads();
   if constexpr (XIN) {
     if (tid < MR) {
@@ -223,51 +218,42 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     }
     __syncthreads();
   }
-  if (wave > 0) return;
+  if (!ewave) return;
+  // this wave's block, summed over the 8 partial tiles in wave order
+  f32x4 v4 = red[0][wave][lane];
 #pragma unroll
-  for (int w = 0; w < DG_WAVES - 1; ++w)
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[mb][cb] += red[w][mb * CB + cb][lane];
+  for (int w = 1; w < DG_WAVES; ++w) v4 += red[w][wave][lane];
 
-  // ---- epilogue: lane holds rows mb*16 + (lane>>4)*4 + r, column cb*16 + (lane&15)
+  // ---- epilogue: lane holds rows emb*16 + (lane>>4)*4 + r of column en
+  if (en >= N) return;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int n = n0 + cb * 16 + (lane & 15);
-    if (n >= N) continue;
-    const float bias = e_bias[cb], c1 = e_c1[cb];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ml = mb * 16 + (lane >> 4) * 4 + r, m = m0 + ml;
-        if (m >= M) continue;
-        float v = acc[mb][cb][r];
-        v = XIN ? s_rs[ml] * (v - s_mu[ml] * c1) + bias : v + bias;
-        if constexpr (EPI == DEPI_RESID) {
-          p.X[(long)m * N + n] = e_x[RES ? mb : 0][RES ? cb : 0][r] + v;
-        } else if constexpr (EPI == DEPI_F32) {
-          p.out_f32[(long)m * N + n] = v;
-        } else if constexpr (EPI == DEPI_STORE) {
-          p.out[(long)m * N + n] = f2bf(v);
-        } else if constexpr (EPI == DEPI_GELU) {
-          p.out[(long)m * N + n] = f2bf(gelu_erf(v));
-        } else if constexpr (EPI == DEPI_QKV) {
-          // q -> bf16; k, v -> e4m3 codes at cache slot lengths[m]
-          const int d = p.d_model;
-          if (n < d) {
-            p.out[(long)m * d + n] = f2bf(v);
-          } else {
-            const int kv = (n - d) / d, c = (n - d) - kv * d, pos = e_pos[QKV ? mb : 0][r];
-            if (pos >= 0 && pos < p.kv_cap) {
-              const long idx =
-                  ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
-              p.kv_cache[idx] = (uint8_t)e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
-            } else if (p.dev_error) {
-              *p.dev_error = 6;  // capacity exceeded: the write is skipped
-            }
-          }
+  for (int r = 0; r < 4; ++r) {
+    const int ml = emb * 16 + (lane >> 4) * 4 + r, m = m0 + ml;
+    if (m >= M) continue;
+    const int n = en;
+    float v = v4[r];
+    v = XIN ? s_rs[ml] * (v - s_mu[ml] * e_c1) + e_bias : v + e_bias;
+    if constexpr (EPI == DEPI_RESID) {
+      p.X[(long)m * N + n] = e_x[r] + v;
+    } else if constexpr (EPI == DEPI_F32) {
+      p.out_f32[(long)m * N + n] = v;
+    } else if constexpr (EPI == DEPI_STORE) {
+      p.out[(long)m * N + n] = f2bf(v);
+    } else if constexpr (EPI == DEPI_GELU) {
+      p.out[(long)m * N + n] = f2bf(gelu_erf(v));
+    } else if constexpr (EPI == DEPI_QKV) {
+      // q -> bf16; k, v -> e4m3 codes at cache slot lengths[m]
+      const int d = p.d_model;
+      if (n < d) {
+        p.out[(long)m * d + n] = f2bf(v);
+      } else {
+        const int kv = (n - d) / d, c = (n - d) - kv * d, pos = e_pos[r];
+        if (pos >= 0 && pos < p.kv_cap) {
+          const long idx =
+              ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
+          p.kv_cache[idx] = (uint8_t)e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
+        } else if (p.dev_error) {
+          *p.dev_error = 6;  // capacity exceeded: the write is skipped
         }
       }
     }
