@@ -250,6 +250,24 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 // lanes x 16 codes.
 constexpr int DEC_MAX_CAP = 4096;
 
+// Sums over 4 or 8 consecutive lanes with DPP lane permutes folded into the
+// adds (no trip through the LDS crossbar as a generic shuffle takes):
+// quad_perm(1,0,3,2) and (2,3,0,1) pair lanes within a quad, row_half_mirror
+// (lane i <-> 7 - i of each 8) pairs the two quads of an 8-lane group.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum4_lanes(float d) {
+  d += dpp_f<0xB1>(d);
+  return d + dpp_f<0x4E>(d);
+}
+__device__ __forceinline__ float sum8_lanes(float d) {
+  d = sum4_lanes(d);
+  return d + dpp_f<0x141>(d);
+}
+constexpr float LOG2E = 1.4426950408889634f;
+
 __device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float acc = 0.f;
@@ -290,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) qreg[i] = Act<T>::cvt(qp[i]);
   }
-  const float sscale = scales[0] * 0.125f, sv = scales[1];
+  const float sscale = scales[0] * (0.125f * LOG2E), sv = scales[1];  // scores in base-2 units
   const long head = ((long)b * H + h) * cap * 64 + part * 16;
   const uint8_t* K = kc + head;
   const uint8_t* V = vc + head;
@@ -306,24 +324,28 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
       cv[i] = *(const uint4*)(V + j * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // key slot i of this wave covers keys base + 64 i + 16 wave .. + 15: a slot
+    // wholly past n is skipped by the whole wave (its loads were clamped)
     float sj[SELF_KB];
     float bm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < SELF_KB; ++i) {
-      float d = dot16_e4m3(ck[i], qreg);
-      d += __shfl_xor(d, 1, 64);
-      d += __shfl_xor(d, 2, 64);
-      sj[i] = (base + kg + 64 * i < n) ? d * sscale : -INFINITY;
+      sj[i] = -INFINITY;
+      if (base + 64 * i + 16 * wave < n) {
+        const float d = sum4_lanes(dot16_e4m3(ck[i], qreg));
+        if (base + kg + 64 * i < n) sj[i] = d * sscale;
+      }
       bm = fmaxf(bm, sj[i]);
     }
     const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] *= alpha;
 #pragma unroll
     for (int i = 0; i < SELF_KB; ++i) {
-      const float p = (sj[i] == -INFINITY) ? 0.f : expf(sj[i] - mn);
+      if (!(base + 64 * i + 16 * wave < n)) continue;
+      const float p = (sj[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sj[i] - mn);
       l += p;
       const uint32_t w[4] = {cv[i].x, cv[i].y, cv[i].z, cv[i].w};
 #pragma unroll
@@ -342,7 +364,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
   if (lane == 0) wmax[wave] = wm;
   __syncthreads();
   const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float f = (m == -INFINITY) ? 0.f : expf(m - mx);
+  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
   float ls = l * f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] *= f;
@@ -420,7 +442,7 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
   {
     const T* qp = q + ((long)b * H + h) * 64 + part * EPT;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) qreg[i] = Act<T>::cvt(qp[i]) * 0.125f;
+    for (int i = 0; i < EPT; ++i) qreg[i] = Act<T>::cvt(qp[i]) * (0.125f * LOG2E);  // scores in base-2 units
   }
   const long head = ((long)b * H + h) * T_ * 64 + part * EPT;
   const T* K = k + head;
@@ -446,19 +468,23 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) d = fmaf(qreg[e], kk[e], d);
+      if constexpr (TPK == 8) d = sum8_lanes(d);
+      else if constexpr (TPK == 4) d = sum4_lanes(d);
+      else {
 #pragma unroll
-      for (int o = 1; o < TPK; o <<= 1) d += __shfl_xor(d, o, 64);
+        for (int o = 1; o < TPK; o <<= 1) d += __shfl_xor(d, o, 64);
+      }
       sj[i] = (base + kg + KPP * i < T_) ? d : -INFINITY;
       bm = fmaxf(bm, sj[i]);
     }
     const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int i = 0; i < CROSS_NB; ++i) {
-      const float p = (sj[i] == -INFINITY) ? 0.f : expf(sj[i] - mn);
+      const float p = (sj[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sj[i] - mn);
       l += p;
       float vv[EPT];
       unpack16(cv[i], vv);
@@ -473,7 +499,7 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
   if (lane == 0) wmax[wave] = wm;
   __syncthreads();
   const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float f = (m == -INFINITY) ? 0.f : expf(m - mx);
+  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
   float ls = l * f;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] *= f;
