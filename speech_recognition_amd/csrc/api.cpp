@@ -150,7 +150,10 @@ EncWS enc_ws(const whisper_dims* d, int B) {
   return W;
 }
 
-struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, total; };
+// The MLP down-projection (K = d_ffn) runs split-K over DEC_KSPLIT workgroups
+// per 16 x 80 output tile; its partials and tile counters live here.
+constexpr int DEC_KSPLIT = 4, DEC_SPLIT_COLS = 80;
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, total; };
 DecWS dec_ws(const whisper_dims* d, int B) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
@@ -160,6 +163,10 @@ DecWS dec_ws(const whisper_dims* d, int B) {
   W.att = take(B * D * e); W.qc = take(B * D * e);
   W.hf = take((size_t)B * d->d_ffn * e);
   W.logits = take((size_t)B * d->n_vocab * 4);
+  const size_t tiles = (size_t)((D + DEC_SPLIT_COLS - 1) / DEC_SPLIT_COLS) * ((B + 15) / 16);
+  W.part = take(tiles * DEC_KSPLIT * (DEC_SPLIT_COLS / 16) * 64 * 16);
+  W.n_cnt = tiles;
+  W.cnt = take(tiles * 4);
   W.total = off;
   return W;
 }
@@ -297,10 +304,11 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* ATT = at<u16_t>(ws, W.att);
   u16_t* QC = at<u16_t>(ws, W.qc);
   u16_t* HF = at<u16_t>(ws, W.hf);
+  int32_t* CNT = at<int32_t>(ws, W.cnt);
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
-                      d->n_text_ctx, cap, X, dev_error, s));
+                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
-                  u16_t* out, float* out_f32, int layer) {
+                  u16_t* out, float* out_f32, int layer, bool split = false) {
     DecGemmParams g{};
     g.M = B; g.N = N; g.K = K;
     g.W = at<u16_t>(packed, w_off);
@@ -311,6 +319,12 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     g.kv_cap = cap; g.kv_B = B; g.kv_H = H; g.kv_layer = layer; g.d_model = D;
     int mb, cb;
     dec_gemm_tiles(B, N, mb, cb);
+    // split-K where the long K would otherwise leave a third of the CUs idle
+    // with 490 KB per busy one (the MLP down-projection)
+    if (split && pro == PRO_A && N % DEC_SPLIT_COLS == 0 && (K / 32) % (DEC_KSPLIT * 8) == 0) {
+      g.ks = DEC_KSPLIT; g.part = at<float>(ws, W.part); g.cnt = CNT;
+      mb = 1; cb = DEC_SPLIT_COLS / 16;
+    }
     return launch_gemm_dec(pro, epi, g, mb, cb, s);
   };
   const size_t kv_layer = (size_t)2 * B * H * cap * 64;
@@ -333,7 +347,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
-    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l));
+    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l, true));
   }
   WH_TRY(gemm(PRO_X, DEPI_F32, P.lmw, P.lmb2, P.lmc1, d->n_vocab, D, nullptr, nullptr, LG, 0));
   WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));

@@ -52,14 +52,19 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   // XCD-aware order: blocks are dispatched round-robin over the 8 XCDs
   // (block L on XCD L % 8), so the row tiles of one column tile are given
   // consecutive slots on one XCD and share its L2 copy of the weight slice.
-  const int RT = (p.M + MR - 1) / MR, CT = (p.N + 16 * CB - 1) / (16 * CB);
+  // split-K (PRO_A only): the KS_ workgroups of an output tile take
+  // consecutive K slices and sit next to its row tiles in the order below
+  const int KS_ = p.ks > 1 ? p.ks : 1;
+  const int RT = (p.M + MR - 1) / MR, CT = (p.N + 16 * CB - 1) / (16 * CB), RTK = RT * KS_;
   const int L = blockIdx.x, xcd = L & 7, jj = L >> 3;
-  const int ct = (jj / RT) * 8 + xcd, rt = jj - (jj / RT) * RT;
+  const int ct = (jj / RTK) * 8 + xcd, rk = jj - (jj / RTK) * RTK;
+  const int rt = rk / KS_, ksl = rk - (rk / KS_) * KS_;  // row tile, K slice
   if (ct >= CT) return;  // padding blocks (CT rounded up to a multiple of 8)
   const int n0 = ct * 16 * CB, m0 = rt * MR;
   const int M = p.M, N = p.N, K = p.K;
-  const int S = K / 32;
-  const int s0 = wave * S / DG_WAVES, s1 = (wave + 1) * S / DG_WAVES;  // this wave's k-steps
+  const int S = K / 32;    // k-steps of a whole row (the LayerNorm statistics use these)
+  const int SK = S / KS_;  // k-steps of this workgroup's slice
+  const int s0 = ksl * SK + wave * SK / DG_WAVES, s1 = ksl * SK + (wave + 1) * SK / DG_WAVES;  // this wave's k-steps
   const int nsteps = s1 - s0;
   const int kq = (lane >> 4) * 8;
 
@@ -218,11 +223,38 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     }
     __syncthreads();
   }
-  if (!ewave) return;
   // this wave's block, summed over the 8 partial tiles in wave order
-  f32x4 v4 = red[0][wave][lane];
+  f32x4 v4 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ewave) {
+    v4 = red[0][wave][lane];
 #pragma unroll
-  for (int w = 1; w < DG_WAVES; ++w) v4 += red[w][wave][lane];
+    for (int w = 1; w < DG_WAVES; ++w) v4 += red[w][wave][lane];
+  }
+  if (KS_ > 1) {
+    // split-K: the blocks go out with device-scope stores (coherent across
+    // XCDs without an L2 write-back); once every wave's stores are
+    // acknowledged, a device-scope counter picks the tile's last workgroup,
+    // which sums the KS_ partials in slice order (device-scope loads) and runs
+    // the epilogue, then resets the counter
+    __shared__ int s_last;
+    const int tile = ct * RT + rt;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(p.part, (short)0, 0x7fffffff, 0x00020000);
+    if (ewave)
+      __builtin_amdgcn_raw_buffer_store_b128(v4, rp, (uint32_t)((((tile * KS_ + ksl) * (MB * CB) + wave) * 64 + lane) * 16),
+                                             0, 16);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(p.cnt + tile, 1) == KS_ - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (ewave) {
+      v4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < KS_; ++q)
+        v4 += __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)((((tile * KS_ + q) * (MB * CB) + wave) * 64 + lane) * 16), 0, 16);
+    }
+    if (tid == 0) p.cnt[tile] = 0;
+  }
+  if (!ewave) return;
 
   // ---- epilogue: lane holds rows emb*16 + (lane>>4)*4 + r of column en
   if (en >= N) return;
@@ -263,7 +295,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 template <int PRO, int EPI, int MB, int CB, int NS>
 static hipError_t dec_launch_ns(const DecGemmParams& p, hipStream_t s) {
   const int CT = (p.N + 16 * CB - 1) / (16 * CB), RT = (p.M + 16 * MB - 1) / (16 * MB);
-  const dim3 grid(((CT + 7) / 8) * 8 * RT);
+  const dim3 grid(((CT + 7) / 8) * 8 * RT * (p.ks > 1 ? p.ks : 1));
   hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NS>), grid, dim3(DG_WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -272,7 +304,7 @@ static hipError_t dec_launch_ns(const DecGemmParams& p, hipStream_t s) {
 // wave, 4d = 5120 -> 20), the generic one otherwise.
 template <int PRO, int EPI, int MB, int CB>
 static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
-  const int S = p.K / 32;
+  const int S = p.K / 32 / (p.ks > 1 ? p.ks : 1);  // k-steps of one workgroup's slice
   if (S == DG_WAVES * 5) return dec_launch_ns<PRO, EPI, MB, CB, 5>(p, s);
   if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20>(p, s);
   return dec_launch_ns<PRO, EPI, MB, CB, 0>(p, s);
@@ -311,6 +343,8 @@ void dec_gemm_tiles(int M, int N, int& mb, int& cb) {
 
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s) {
   if (p.M <= 0 || p.M > 128 || p.N <= 0 || p.K <= 0 || p.K % 32) return hipErrorInvalidValue;
+  if (p.ks > 1 && (pro != PRO_A || !p.part || !p.cnt || p.ks > 16 || (p.K / 32) % (p.ks * DG_WAVES)))
+    return hipErrorInvalidValue;  // split-K: bf16 activations, whole k-steps per wave, workspace given
   if (pro == PRO_X) {
     switch (epi) {
       case DEPI_QKV: return dec_launch<PRO_X, DEPI_QKV>(p, mb, cb, s);

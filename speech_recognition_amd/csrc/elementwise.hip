@@ -299,8 +299,10 @@ hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* pos_emb, const int32_t* tokens,
                                                     const int32_t* lengths, int d, int n_vocab, int n_ctx, int cap,
-                                                    float* x, int32_t* dev_error) {
+                                                    float* x, int32_t* dev_error, int32_t* zero, int n_zero) {
   const int b = blockIdx.x;
+  if (b == 0)  // the step's split-K counters start at zero
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   const int tok = tokens[b], pos = lengths[b];
   const bool ok = tok >= 0 && tok < n_vocab && pos >= 0 && pos < n_ctx && pos < cap;
   if (!ok && dev_error && threadIdx.x == 0) *dev_error = (pos >= cap) ? 6 : 1;
@@ -313,13 +315,13 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* p
 
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
-                        int32_t* dev_error, hipStream_t s) {
+                        int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero) {
   if (t == ACT_BF16)
     hipLaunchKernelGGL(embed_kernel<u16>, dim3(B), dim3(256), 0, s, (const u16*)tok_emb, (const u16*)pos_emb, tokens,
-                       lengths, d, n_vocab, n_ctx, cap, x, dev_error);
+                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(B), dim3(256), 0, s, (const float*)tok_emb, (const float*)pos_emb,
-                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error);
+                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero);
   return hipGetLastError();
 }
 

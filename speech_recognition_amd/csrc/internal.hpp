@@ -61,6 +61,10 @@ struct DecGemmParams {
   // DEPI_QKV: k, v appended as e4m3 codes at slot lengths[m]
   uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
   int kv_cap, kv_B, kv_H, kv_layer, d_model;
+  // split-K over ks workgroups per output tile (PRO_A only; ks <= 1: none):
+  // partial blocks [tiles][ks][MB*CB][64 lanes] f32x4 and one counter per tile,
+  // zero on entry (each launch leaves them zero)
+  int ks; float* part; int32_t* cnt;
 };
 void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
@@ -109,7 +113,7 @@ hipError_t launch_fill_f32(float* dst, float v, size_t n, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
-                        int32_t* dev_error, hipStream_t s);
+                        int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0);
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s);
 
 }  // namespace wh
