@@ -12,8 +12,8 @@
 //
 // Decoder self-attention reads the caller's e4m3 KV cache and dequantises on
 // read (the Inference Endpoints post, "Inference Stack": K/V stored as float8,
-// compute in bfloat16). Decoder cross-attention streams head-major bf16 K/V,
-// split over the 1500 frames with a log-sum-exp combine.
+// compute in bfloat16). Decoder cross-attention streams head-major bf16 K/V
+// in one pass per (row, head).
 #include <type_traits>
 
 #include "common.hpp"
