@@ -8,7 +8,8 @@
 // so the C layout puts one query per lane column: that query's running max,
 // sum and output rows all live in the same lane and the softmax needs a
 // single cross-lane exchange (lane ^ 32). P^T then feeds O^T = V^T P^T
-// directly from registers; V is transposed once per tile on its way into LDS.
+// directly from registers; V stays key-major in LDS (stored like K) and its
+// transposed fragments come from LDS transpose reads.
 //
 // Decoder self-attention reads the caller's e4m3 KV cache and dequantises on
 // read (the Inference Endpoints post, "Inference Stack": K/V stored as float8,
@@ -23,8 +24,16 @@ namespace wh {
 
 // ------------------------------------------------------------------ encoder, bf16 MFMA
 __device__ __forceinline__ int k_swz(int row, int kc) { return row * 64 + ((kc ^ (row & 7)) << 3); }
-__device__ __forceinline__ int vt_swz(int e, int key) {
-  return e * 64 + ((((key >> 2) ^ (e & 15))) << 2) + (key & 3);
+
+// V^T fragment straight from the key-major V tile with the gfx950 LDS
+// transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane j
+// names 4 consecutive 16-bit elements (8 bytes); the group's 16 x 4 elements,
+// in lane order, form a sequence E of 64, and lane i receives E[i], E[16+i],
+// E[32+i], E[48+i]. When lane j of the group points at key k0 + j/4, columns
+// e0 + 4(j%4) .. +3, lane i receives keys k0 .. k0+3 of column e0 + i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const u16* p) {
+  return bitcast<uint2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
 }
 
 // eight fp32 -> bf16 with the gfx950 converter (round to nearest even; the
@@ -37,7 +46,7 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
 __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__ qkv, int T, int H, int B,
                                                          u16* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) u16 sK[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) u16 sVt[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][64 * 64];
   const int d = H * 64, ld = 3 * d;
   // XCD-aware order (block L runs on XCD L % 8): the query tiles of one
   // (chunk, head) get consecutive slots on one XCD, so its K/V are fetched
@@ -70,20 +79,17 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
     rv0 = *(const uint4*)(Vp + (long)k0 * ld + kc * 8);
     rv1 = *(const uint4*)(Vp + (long)k1 * ld + kc * 8);
   };
-  auto vt_store = [&](int buf, const uint4 v, int key) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sVt[buf][vt_swz(kc * 8 + 2 * j, key)] = (u16)(w[j] & 0xffffu);
-      sVt[buf][vt_swz(kc * 8 + 2 * j + 1, key)] = (u16)(w[j] >> 16);
-    }
-  };
   auto sstore = [&](int buf) {
     *(uint4*)&sK[buf][k_swz(row, kc)] = rk0;
     *(uint4*)&sK[buf][k_swz(row + 32, kc)] = rk1;
-    vt_store(buf, rv0, row);
-    vt_store(buf, rv1, row + 32);
+    *(uint4*)&sV[buf][k_swz(row, kc)] = rv0;
+    *(uint4*)&sV[buf][k_swz(row + 32, kc)] = rv1;
   };
+  // this lane's part of the transpose reads: group G = lane / 16 serves columns
+  // 16 (G & 1) .. +15 of a 32-column block and key quad G >> 1 of each 8 keys
+  const int tr_key = ((lane >> 5) << 2) + ((lane & 15) >> 2);        // key offset within 8
+  const int tr_col = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);   // column offset within 32
+  auto v_addr = [&](int key, int col) { return key * 64 + ((((col >> 3) ^ (key & 7))) << 3) + (col & 7); };
 
   f32x16 o[2];
 #pragma unroll
@@ -154,9 +160,10 @@ __global__ __launch_bounds__(256) void attn_encoder_bf16(const u16* __restrict__
                                     st[j2][hs + 4], st[j2][hs + 5], st[j2][hs + 6], st[j2][hs + 7]);
 #pragma unroll
       for (int eb = 0; eb < 2; ++eb) {
-        const int e = eb * 32 + l32;
-        const uint2 lo = *(const uint2*)&sVt[cur][vt_swz(e, t * 16 + g * 4)];
-        const uint2 hi = *(const uint2*)&sVt[cur][vt_swz(e, t * 16 + 8 + g * 4)];
+        // V^T rows eb*32 + l32, keys t*16 + 4g + 0..3 and t*16 + 8 + 4g + 0..3 (the
+        // key order of the P^T fragment)
+        const uint2 lo = lds_read_tr16(&sV[cur][v_addr(t * 16 + tr_key, eb * 32 + tr_col)]);
+        const uint2 hi = lds_read_tr16(&sV[cur][v_addr(t * 16 + 8 + tr_key, eb * 32 + tr_col)]);
         const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(vv), pf, o[eb], 0, 0, 0);
       }
