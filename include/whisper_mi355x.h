@@ -93,7 +93,9 @@ enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WH
  * whisper_pack_weights converts them once into the library's packed buffer
  * (activation dtype for matrices, fp32 for biases and LayerNorm parameters;
  * fused QKV, tap-major conv filters, all decoder layers' cross K/V stacked,
- * encoder sinusoidal positions precomputed). The packed buffer is caller
+ * encoder sinusoidal positions precomputed; in bf16 the decoder's
+ * LayerNorm-consumer matrices are LayerNorm-folded and all decoder GEMM
+ * matrices are stored in MFMA fragment order). The packed buffer is caller
  * memory of whisper_packed_weights_size() bytes; the logical tensors may be
  * freed once the pack has completed on `stream`. */
 int whisper_weight_count(const whisper_dims* dims);

@@ -59,7 +59,9 @@ whisper_status check_dims(const whisper_dims* d) {
 struct EncL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, w1, b1, w2, b2; };
 // In bf16 mode the LayerNorm-consumer weights of the decoder (wqkv, wqc, w1
 // and the vocabulary projection lmw) are stored gamma-folded, their biases
-// beta-folded, with the row sums c1* beside them (see decode_gemm.hip).
+// beta-folded, with the row sums c1* beside them (see decode_gemm.hip), and
+// all decoder GEMM weights (those and wo, woc, w2) are in the MFMA fragment
+// order of decode_gemm.hip rather than row-major.
 struct DecL {
   size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, wqc, bqc, woc, boc, ln3g, ln3b, w1, b1, w2, b2;
   size_t c1qkv = 0, c1qc = 0, c1w1 = 0;
@@ -116,7 +118,7 @@ Packed layout(const whisper_dims* d) {
     P.ckvb = take((size_t)d->n_dec_layers * 2 * D * f4);
     P.lnfg = take(D * f4); P.lnfb = take(D * f4);
     if (d->act == WHISPER_BF16) {
-      P.lmw = take((size_t)d->n_vocab * D * e);
+      P.lmw = take((size_t)((d->n_vocab + 15) & ~15) * D * e);  // rows padded to the 16-row fragment
       P.lmc1 = take((size_t)d->n_vocab * f4);
       P.lmb2 = take((size_t)d->n_vocab * f4);
     }
@@ -419,6 +421,12 @@ whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w
   int i = 0;
   auto cvt = [&](const float* src, size_t off, size_t cnt) { return launch_convert(t, src, at<void>(packed, off), cnt, s); };
   auto cpy = [&](const float* src, size_t off, size_t cnt) { return launch_copy_f32(src, at<float>(packed, off), cnt, s); };
+  // decoder GEMM weights: in bf16 mode the fused decode step reads them in
+  // fragment order (decode_gemm.hip); the other dtypes keep them row-major
+  auto dw = [&](const float* src, size_t off, size_t n_rows, size_t k) {
+    return t == ACT_BF16 ? launch_pack_dec_weight(src, (int)n_rows, (int)k, at<void>(packed, off), s)
+                         : cvt(src, off, n_rows * k);
+  };
   if (d->n_enc_layers > 0) {
     WH_TRY(launch_pack_conv(t, w[i++], D, d->n_mels, 3, at<void>(packed, P.conv1w), s));
     WH_TRY(cpy(w[i++], P.conv1b, D));
@@ -453,16 +461,16 @@ whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w
       WH_TRY(cvt(w[i + 4], L.wqkv + D * D * e, D * D));
       WH_TRY(launch_fill_f32(at<float>(packed, L.bqkv + D * 4), 0.f, D, s));
       WH_TRY(cvt(w[i + 5], L.wqkv + 2 * D * D * e, D * D)); WH_TRY(cpy(w[i + 6], L.bqkv + 2 * D * 4, D));
-      WH_TRY(cvt(w[i + 7], L.wo, D * D)); WH_TRY(cpy(w[i + 8], L.bo, D));
+      WH_TRY(dw(w[i + 7], L.wo, D, D)); WH_TRY(cpy(w[i + 8], L.bo, D));
       WH_TRY(cpy(w[i + 9], L.ln2g, D)); WH_TRY(cpy(w[i + 10], L.ln2b, D));
       WH_TRY(cvt(w[i + 11], L.wqc, D * D)); WH_TRY(cpy(w[i + 12], L.bqc, D));
       WH_TRY(cvt(w[i + 13], ck, D * D));
       WH_TRY(launch_fill_f32(at<float>(packed, cb), 0.f, D, s));
       WH_TRY(cvt(w[i + 14], ck + D * D * e, D * D)); WH_TRY(cpy(w[i + 15], cb + D * 4, D));
-      WH_TRY(cvt(w[i + 16], L.woc, D * D)); WH_TRY(cpy(w[i + 17], L.boc, D));
+      WH_TRY(dw(w[i + 16], L.woc, D, D)); WH_TRY(cpy(w[i + 17], L.boc, D));
       WH_TRY(cpy(w[i + 18], L.ln3g, D)); WH_TRY(cpy(w[i + 19], L.ln3b, D));
       WH_TRY(cvt(w[i + 20], L.w1, F * D)); WH_TRY(cpy(w[i + 21], L.b1, F));
-      WH_TRY(cvt(w[i + 22], L.w2, D * F)); WH_TRY(cpy(w[i + 23], L.b2, D));
+      WH_TRY(dw(w[i + 22], L.w2, D, F)); WH_TRY(cpy(w[i + 23], L.b2, D));
       if (t == ACT_BF16) {  // fold ln1 into q/k/v, ln2 into the cross query, ln3 into the MLP up-projection
         const size_t DD = D * D * e;
         float* c1 = at<float>(packed, L.c1qkv);

@@ -32,6 +32,14 @@
 namespace wh {
 
 constexpr int DG_WAVES = 8;
+
+// Fragment order of a decoder weight W [N, K] (K % 32 == 0, rows padded to a
+// multiple of 16): block (n / 16, k / 32) is 512 contiguous elements, in which
+// lane l = 16 * ((k % 32) / 8) + n % 16 holds its 8 consecutive k values: the
+// B operand of one 16x16x32 MFMA, in lane order.
+__host__ __device__ inline long dec_frag_index(long n, long k, long K) {
+  return (((n >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k & 31) >> 3) * 16 + (n & 15)) * 8 + (k & 7);
+}
 constexpr int DG_DEPTH = 1;         // k-steps of operand loads in flight per wave ahead of the MFMAs
 
 // NS: k-steps per wave, fixed at compile time (K / 256 for K = 1280 or 5120),
@@ -68,9 +76,13 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   const int nsteps = s1 - s0;
   const int kq = (lane >> 4) * 8;
 
-  const u16* wrow[CB];
+  // W is stored in fragment order (dec_frag_index): the 16 x 32 block of a
+  // column group and k-step is 1 KB, lane-ordered, so each wave load is one
+  // contiguous 1 KB read of whole cache lines
+  const int NF = (N + 15) >> 4;
+  const u16* wfr[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) wrow[cb] = p.W + (long)min(n0 + cb * 16 + (lane & 15), N - 1) * K + kq;
+  for (int cb = 0; cb < CB; ++cb) wfr[cb] = p.W + (long)min((n0 >> 4) + cb, NF - 1) * S * 512 + lane * 8;
   long arow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1);
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #define DG_ISSUE(J, SL)                                                                        \
   {                                                                                            \
     const int k_ = (s0 + (J)) * 32;                                                            \
-    _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) wv[SL][cb] = *(const uint4*)(wrow[cb] + k_); \
+    _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) wv[SL][cb] = *(const uint4*)(wfr[cb] + k_ * 16); \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
       if constexpr (XIN) {                                                                     \
         const float* x_ = p.X + arow[mb] * K + k_ + kq;                                        \
@@ -363,15 +375,21 @@ hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int m
 
 // Weight packing for a LayerNorm-consumer GEMM (one workgroup per output row
 // n): W'[n,k] = bf16(gamma_k W[n,k]), c1[n] = sum_k W'[n,k],
-// b2[n] = bias[n] + sum_k beta_k W[n,k]; sums in fp64.
+// b2[n] = bias[n] + sum_k beta_k W[n,k]; sums in fp64. W' goes out in
+// fragment order; rows N .. 16*ceil(N/16) - 1 are zero padding.
 __global__ __launch_bounds__(256) void fold_ln_kernel(const float* W, const float* gamma, const float* beta,
-                                                      const float* bias, int K, u16* Wf, float* c1, float* b2) {
+                                                      const float* bias, int N, int K, u16* Wf, float* c1,
+                                                      float* b2) {
   const int n = blockIdx.x, tid = threadIdx.x;
+  if (n >= N) {
+    for (int k = tid; k < K; k += 256) Wf[dec_frag_index(n, k, K)] = 0;
+    return;
+  }
   const float* w = W + (long)n * K;
   double s1 = 0.0, s2 = 0.0;
   for (int k = tid; k < K; k += 256) {
     const u16 f = f2bf(gamma[k] * w[k]);
-    Wf[(long)n * K + k] = f;
+    Wf[dec_frag_index(n, k, K)] = f;
     s1 += (double)bf2f(f);
     s2 += (double)beta[k] * (double)w[k];
   }
@@ -395,7 +413,24 @@ __global__ __launch_bounds__(256) void fold_ln_kernel(const float* W, const floa
 hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
                           void* Wf, float* c1, float* b2, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_ln_kernel, dim3(N), dim3(256), 0, s, W, gamma, beta, bias, K, (u16*)Wf, c1, b2);
+  if (K <= 0 || K % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fold_ln_kernel, dim3((N + 15) & ~15), dim3(256), 0, s, W, gamma, beta, bias, N, K, (u16*)Wf,
+                     c1, b2);
+  return hipGetLastError();
+}
+
+// fp32 row-major [N, K] -> bf16 in fragment order, rows padded to a multiple
+// of 16 with zeros (weights read straight from the residual-free activations:
+// attention outputs and the MLP hidden layer)
+__global__ __launch_bounds__(256) void pack_frag_kernel(const float* W, int N, int K, u16* Wf) {
+  const int n = blockIdx.x, tid = threadIdx.x;
+  for (int k = tid; k < K; k += 256) Wf[dec_frag_index(n, k, K)] = n < N ? f2bf(W[(long)n * K + k]) : (u16)0;
+}
+
+hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (K <= 0 || K % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_frag_kernel, dim3((N + 15) & ~15), dim3(256), 0, s, W, N, K, (u16*)Wf);
   return hipGetLastError();
 }
 

@@ -51,7 +51,7 @@ enum DecPro { PRO_A = 0, PRO_X = 1 };
 enum DecEpi { DEPI_STORE = 0, DEPI_GELU = 1, DEPI_RESID = 2, DEPI_QKV = 3, DEPI_F32 = 4 };
 struct DecGemmParams {
   int M, N, K;
-  const u16_t* W;            // [N, K] bf16 (PRO_X: gamma-folded)
+  const u16_t* W;            // [N, K] bf16 in fragment order (PRO_X: gamma-folded)
   const float* bias;         // [N] or NULL (PRO_X: folded bias b + W beta)
   const float* c1;           // PRO_X: [N] row sums of the folded W
   const u16_t* A; long lda;  // PRO_A: [M, K] bf16, row stride lda
@@ -70,6 +70,7 @@ void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
 hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
                           void* Wf, float* c1, float* b2, hipStream_t s);
+hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStream_t s);
 
 // ------------------------------------------------------------------ LayerNorm
 // h is in the activation type (or fp32 when h_f32); residual and total are the
