@@ -161,7 +161,8 @@ DecWS dec_ws(const whisper_dims* d, int B) {
   const size_t e = esz(d->act), D = d->d_model;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
-  W.x = take(B * D * 4); W.a = take(B * D * e); W.dlt = take(B * D * e); W.q = take(B * D * e);
+  W.x = take((size_t)((B + 15) & ~15) * D * 4);  // bf16 path: 16-row tiles (dec_x_index)
+  W.a = take(B * D * e); W.dlt = take(B * D * e); W.q = take(B * D * e);
   W.att = take(B * D * e); W.qc = take(B * D * e);
   W.hf = take((size_t)B * d->d_ffn * e);
   W.logits = take((size_t)B * d->n_vocab * 4);
@@ -308,7 +309,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* HF = at<u16_t>(ws, W.hf);
   int32_t* CNT = at<int32_t>(ws, W.cnt);
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
-                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt));
+                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
                   u16_t* out, float* out_f32, int layer, bool split = false) {
     DecGemmParams g{};

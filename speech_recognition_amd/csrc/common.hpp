@@ -84,6 +84,16 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// ------------------------------------------------------------------ decoder residual tiles
+// The fused decode step keeps its fp32 residual stream x [M, d] (M padded to
+// a multiple of 16, d % 32 == 0) in 16-row tiles laid out for the A operand
+// of a 16x16x32 MFMA: per 16 rows and 32 columns a 2 KB block holding two
+// 1 KB halves, each lane-ordered (lane = 16 * ((k % 32) / 8) + m % 16, four
+// consecutive k), so a wave's operand load is one contiguous 1 KB read.
+__host__ __device__ __forceinline__ long dec_x_index(long m, long k, long d) {
+  return ((((m >> 4) * (d >> 5) + (k >> 5)) * 2 + ((k & 7) >> 2)) * 64 + ((k & 31) >> 3) * 16 + (m & 15)) * 4 + (k & 3);
+}
+
 // ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

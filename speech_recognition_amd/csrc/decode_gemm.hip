@@ -86,6 +86,11 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   long arow[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1);
+  // x tiles (dec_x_index): this lane's 4 + 4 values of k-step s sit at
+  // xoff + 512 s and 256 floats further
+  long xoff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) xoff[mb] = (arow[mb] >> 4) * S * 512 + ((lane >> 4) * 16 + (arow[mb] & 15)) * 4;
 
   // ---- epilogue: the MB * CB output blocks (16 rows x 16 columns) go to waves
   // 0 .. MB*CB-1, one each. A block's operands are fetched by its wave before
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = min(m0 + emb * 16 + (lane >> 4) * 4 + r, M - 1);
-      if constexpr (RES) e_x[r] = p.X[(long)m * N + n];
+      if constexpr (RES) e_x[r] = p.X[dec_x_index(m, n, N)];
       if constexpr (QKV) e_pos[r] = p.lengths[m];
     }
     if constexpr (QKV) {
@@ -135,9 +140,9 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) wv[SL][cb] = *(const uint4*)(wfr[cb] + k_ * 16); \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
       if constexpr (XIN) {                                                                     \
-        const float* x_ = p.X + arow[mb] * K + k_ + kq;                                        \
+        const float* x_ = p.X + xoff[mb] + k_ * 16;                                             \
         xa[XIN ? SL : 0][mb] = *(const float4*)x_;                                             \
-        xb[XIN ? SL : 0][mb] = *(const float4*)(x_ + 4);                                       \
+        xb[XIN ? SL : 0][mb] = *(const float4*)(x_ + 256);                                     \
       } else {                                                                                 \
         av[XIN ? 0 : SL][mb] = *(const uint4*)(p.A + arow[mb] * p.lda + k_ + kq);              \
       }                                                                                        \
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     float v = v4[r];
     v = XIN ? s_rs[ml] * (v - s_mu[ml] * e_c1) + e_bias : v + e_bias;
     if constexpr (EPI == DEPI_RESID) {
-      p.X[(long)m * N + n] = e_x[r] + v;
+      p.X[dec_x_index(m, n, N)] = e_x[r] + v;
     } else if constexpr (EPI == DEPI_F32) {
       p.out_f32[(long)m * N + n] = v;
     } else if constexpr (EPI == DEPI_STORE) {

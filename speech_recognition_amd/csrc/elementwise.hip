@@ -299,7 +299,8 @@ hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* pos_emb, const int32_t* tokens,
                                                     const int32_t* lengths, int d, int n_vocab, int n_ctx, int cap,
-                                                    float* x, int32_t* dev_error, int32_t* zero, int n_zero) {
+                                                    float* x, int32_t* dev_error, int32_t* zero, int n_zero,
+                                                    int x_tiled) {
   const int b = blockIdx.x;
   if (b == 0)  // the step's split-K counters start at zero
     for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
@@ -309,19 +310,20 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* p
   for (int c = threadIdx.x; c < d; c += 256) {
     float v = 0.f;
     if (ok) v = Act<T>::cvt(tok_emb[(size_t)tok * d + c]) + Act<T>::cvt(pos_emb[(size_t)pos * d + c]);
-    x[(size_t)b * d + c] = v;
+    x[x_tiled ? dec_x_index(b, c, d) : (long)b * d + c] = v;
   }
 }
 
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
-                        int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero) {
+                        int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero, int x_tiled) {
+  if (x_tiled && d % 32) return hipErrorInvalidValue;
   if (t == ACT_BF16)
     hipLaunchKernelGGL(embed_kernel<u16>, dim3(B), dim3(256), 0, s, (const u16*)tok_emb, (const u16*)pos_emb, tokens,
-                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero);
+                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(B), dim3(256), 0, s, (const float*)tok_emb, (const float*)pos_emb,
-                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero);
+                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled);
   return hipGetLastError();
 }
 

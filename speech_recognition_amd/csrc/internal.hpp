@@ -55,7 +55,7 @@ struct DecGemmParams {
   const float* bias;         // [N] or NULL (PRO_X: folded bias b + W beta)
   const float* c1;           // PRO_X: [N] row sums of the folded W
   const u16_t* A; long lda;  // PRO_A: [M, K] bf16, row stride lda
-  float* X;                  // residual stream [M, d] fp32: PRO_X input, DEPI_RESID in/out
+  float* X;                  // residual stream [M, d] fp32 in 16-row tiles (dec_x_index): PRO_X input, DEPI_RESID in/out
   u16_t* out;                // DEPI_STORE / GELU: [M, N] bf16; DEPI_QKV: q [M, d]
   float* out_f32;            // DEPI_F32: [M, N]
   // DEPI_QKV: k, v appended as e4m3 codes at slot lengths[m]
@@ -114,7 +114,8 @@ hipError_t launch_fill_f32(float* dst, float v, size_t n, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
-                        int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0);
+                        int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0,
+                        int x_tiled = 0);  // x_tiled: x in the 16-row tiles of dec_x_index
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s);
 
 }  // namespace wh
