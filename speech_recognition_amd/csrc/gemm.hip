@@ -661,15 +661,19 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
 // share of the tiles. The 4-stage ring runs on across tile boundaries: the
 // last four k-steps of a tile load the first four stages of the next one (and
 // its bias), so a tile's 32 stores per lane are issued with the next tile's
-// loads already in flight and drain behind its first k-steps instead of
-// stalling every CU at once. Loads use buffer addressing (scalar resource and
-// k offset, one 32-bit VGPR offset per stream); stores use the buffer range
-// check to drop rows past M, so every wave issues the same, fixed number of
-// memory operations per tile and the vmcnt waits below are exact:
-//   in-tile wait for stage s+1: the 2 younger stages (8 loads) may be in flight;
-//   first three waits of a tile: also the previous tile's 32 stores (40);
+// loads already in flight. Loads use buffer addressing (scalar resource and k
+// offset, one 32-bit VGPR offset per stream); stores use the buffer range
+// check to drop rows past M. Every wave issues the same, fixed number of loads
+// per tile, and each vmcnt wait allows exactly the loads issued after the
+// awaited stage to stay in flight. Loads retire in order among themselves,
+// but stores may retire before older loads (a dropped store at once), so a
+// pending store must never be counted as one of the operations allowed to
+// remain outstanding; the waits count loads only:
+//   in-tile wait for stage s+1: the 2 younger stages (8 loads);
 //   tail waits: also the next tile's bias load (9);
-//   tile head (next tile's stage 0): its stages 1-3 and the 32 stores (44).
+//   tile head (next tile's bias and stage 0): its stages 1-3 (12).
+// With the previous tile's stores younger than those loads, the head wait also
+// holds until most of those stores have retired.
 // Requirements (checked by the launcher): batch 1, N % 256 == 0, K % 128 == 0,
 // K >= 256, operands and output under 2 GB.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -780,21 +784,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)((long)p.M * p.ldc * 2), 0x00020000);
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  // the first tile starts like every later one: bias and stages 0-3 in
-  // flight, then 32 stores (here out of range, so dropped) behind them
+  // the first tile starts like every later one: bias and stages 0-3 in flight
   WH_BIAS(0, tn)
   WH_ISSUE(st0, 0)
   WH_ISSUE(st1, DBK)
   WH_ISSUE(st2, 2 * DBK)
   WH_ISSUE(st3, 3 * DBK)
-#pragma unroll
-  for (int q = 0; q < 32; ++q) __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rc, 0x80000000u, 0, 0);
   asm volatile("" ::: "memory");
   int par = 0;
   for (;;) {
-    WH_SYNC(44)  // this tile's stage 0 (and bias) has landed
+    WH_SYNC(12)  // this tile's bias and stage 0 have landed (stages 1-3 may be in flight)
     WH_READ(st0, a0, b0)
-    WH_ROUND(40, 40, 40, 8, 0)
+    WH_ROUND(8, 8, 8, 8, 0)
     for (int kt = 4; kt + 8 <= nk; kt += 4) {
       WH_ROUND(8, 8, 8, 8, kt)
     }
@@ -841,7 +842,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
         }
       }
     }
-    // the 32 stores must all be issued before the next wait: its count includes them
+    // the stores stay ahead of the next tile's waits in program order
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     if (!more) break;

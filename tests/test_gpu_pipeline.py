@@ -58,7 +58,10 @@ def _encoder_from_audio(dims, B, chunks):
     audio = gen_audio_tones(DEV, dims.cfg_id, B)
     mel = m.logmel(audio)
     enc = m.encode(mel)
+    enc2 = m.encode(mel)
     torch.cuda.synchronize()
+    same = [bool(torch.equal(enc[b], enc2[b])) for b in range(B)]
+    assert all(same), f"encoder is not deterministic: chunks equal across two runs {same}"
     Wh = host_weights(W, "encoder.")
     for b in chunks:
         mref = O.log_mel(audio[b].cpu().numpy(), dims.n_mels)
@@ -67,6 +70,22 @@ def _encoder_from_audio(dims, B, chunks):
         e = rel_err(host(enc)[b], ref)
         say(f"  chunk {b}: mel rel err {em:.2e}, encoder rel err {e:.3e}")
         assert em < 1e-3 and e < TOL
+
+
+def test_encoder_layers_deterministic_ragged_tiles():
+    """Repeated two-layer encodes at batch 3 (4500 rows: the last 256-row GEMM
+    tile is ragged, and one workgroup's epilogue stores overlap the next tile's
+    loads) must agree bit for bit with the first."""
+    dims = CONFIGS["v3_encoder"].with_(n_enc_layers=2)
+    say("encoder layers 0..2, B=3: five repeated runs bit-identical")
+    m, _ = model_for(dims)
+    h = gen_normal(DEV, (3, 1500, 1280), dims.cfg_id, 6, bf16=True).to(torch.bfloat16)
+    ref = m.encode_layers(h, 0, 2)
+    for i in range(4):
+        o = m.encode_layers(h, 0, 2)
+        torch.cuda.synchronize()
+        same = [bool(torch.equal(o[b], ref[b])) for b in range(3)]
+        assert all(same), f"run {i + 1}: chunks equal to the first run {same}"
 
 
 def test_encoder_from_audio_two_layers():
