@@ -660,7 +660,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
 // The 8-wave LDS-DMA kernel above, run as one workgroup per CU that walks a
 // share of the tiles. The 4-stage ring runs on across tile boundaries: the
 // last four k-steps of a tile load the first four stages of the next one (and
-// its bias), so a tile's 32 stores per lane are issued with the next tile's
+// its bias), so a tile's 16 stores per lane are issued with the next tile's
 // loads already in flight. Loads use buffer addressing (scalar resource and k
 // offset, one 32-bit VGPR offset per stream); stores use the buffer range
 // check to drop rows past M. Every wave issues the same, fixed number of loads
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_dma(GemmParams p) {
 // With the previous tile's stores younger than those loads, the head wait also
 // holds until most of those stores have retired.
 // Requirements (checked by the launcher): batch 1, N % 256 == 0, K % 128 == 0,
-// K >= 256, operands and output under 2 GB.
+// K >= 256, ldc % 8 == 0, operands and output under 2 GB.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
@@ -754,9 +754,11 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
   const int fr = lane & 15, kc = lane >> 4;
   const int nk = p.K / DBK;
   bf16x8 a0[8], b0[4], a1[8], b1[4];
+  // B fragment slot s of block j holds tile row 32 (j / 2) + 8 (s / 4) + 4 (j % 2) + s % 4, so a
+  // lane's outputs in blocks 2h and 2h+1 are 8 consecutive columns (one 16-byte store)
 #define WH_READ(S, AF, BF)                                                                    \
   _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
-    BF[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + j * 16 + fr, kc))); \
+    BF[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 64 + 32 * (j >> 1) + 8 * (fr >> 2) + 4 * (j & 1) + (fr & 3), kc))); \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
     AF[i] = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));
 #define WH_MFMA(AF, BF)                                                                       \
@@ -784,6 +786,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
 
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)((long)p.M * p.ldc * 2), 0x00020000);
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // the first tile starts like every later one: bias and stages 0-3 in flight
   WH_BIAS(0, tn)
   WH_ISSUE(st0, 0)
@@ -817,28 +820,36 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
     WH_SYNC(63)  // all waves are done reading buffer 3; nothing to wait for in vmcnt
     WH_ISSUE(st3, 3 * DBK)
     WH_MFMA(a1, b1)
-    // epilogue: bias from LDS, activation, bf16 pairs, 32 buffer stores per lane;
-    // rows past M get an offset beyond the range and are dropped
+    // epilogue: bias from LDS, activation, bf16, 16 buffer stores of 16 bytes per
+    // lane (each instruction writes 64 contiguous bytes of 16 rows); rows past M
+    // get an offset beyond the range and are dropped
     {
-      const int en = wn * 64 + (lane >> 4) * 4;
+      // lane columns: en + 32 h + 0..7 come from blocks 2h (first 4) and 2h + 1
+      const int en = wn * 64 + (lane >> 4) * 8;
       float4 bj[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bj[j] = p.bias ? *(const float4*)(&bsl[par][en + j * 16]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        bj[j] = p.bias ? *(const float4*)(&bsl[par][en + 32 * (j >> 1) + 4 * (j & 1)]) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int m = m0 + wm * 128 + i * 16 + (lane & 15);
         const uint32_t roff = m < p.M ? ((uint32_t)m * (uint32_t)p.ldc + (uint32_t)(n0 + en)) * 2 : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v0 = acc[i][j][0] + bj[j].x, v1 = acc[i][j][1] + bj[j].y;
-          float v2 = acc[i][j][2] + bj[j].z, v3 = acc[i][j][3] + bj[j].w;
-          if constexpr (EPI == EPI_GELU) {
-            v0 = gelu_erf(v0); v1 = gelu_erf(v1); v2 = gelu_erf(v2); v3 = gelu_erf(v3);
+        for (int h = 0; h < 2; ++h) {
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int j = 2 * h + q;
+            v[4 * q + 0] = acc[i][j][0] + bj[j].x; v[4 * q + 1] = acc[i][j][1] + bj[j].y;
+            v[4 * q + 2] = acc[i][j][2] + bj[j].z; v[4 * q + 3] = acc[i][j][3] + bj[j].w;
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          const u32x2 u = {f2bf2(v0, v1), f2bf2(v2, v3)};
-          __builtin_amdgcn_raw_buffer_store_b64(u, rc, roff + j * 32, 0, 0);
-          acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = gelu_erf(v[q]);
+          }
+          const u32x4 u = {f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(u, rc, roff + h * 64, 0, 0);
         }
       }
     }
@@ -1145,7 +1156,7 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
     // persistent variant: whole 256-column tiles, one workgroup per CU
     const bool pers_ok = dma_ok && p.batch == 1 && p.N % TB2 == 0 && p.K >= 8 * DBK && (epi == EPI_STORE || epi == EPI_GELU) &&
                          (long)p.M * p.ldc * 2 < (1L << 31) && ((long)(p.M - 1) * p.lda + p.K) * 2 < (1L << 32) &&
-                         ((long)(p.N - 1) * p.ldb + p.K) * 2 < (1L << 32) && p.ldc >= p.N;
+                         ((long)(p.N - 1) * p.ldb + p.K) * 2 < (1L << 32) && p.ldc >= p.N && p.ldc % 8 == 0;
     int v = p.variant;
     if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (pers_ok ? 9 : dma_ok ? 4 : 2) : 1;
     if ((v == 3 && !w4_ok) || (v == 4 && !dma_ok)) v = 1;
