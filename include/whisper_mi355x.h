@@ -162,6 +162,24 @@ whisper_status whisper_decode_step(const whisper_dims* dims, const void* packed,
                                    const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
                                    int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
+/* Decoder step with fp8 cross-attention K/V (the fp8 cross-attention site of
+ * the pages' precision presets; project page, "Direct Kernel API":
+ * quantise_e4m3 with a per-tensor scale). As whisper_decode_step, bf16 models
+ * only, except that the cross-attention keys and values are e4m3 codes:
+ * cross_codes:  [n_dec_layers][2][batch][n_heads][n_audio_ctx][64] uint8, the
+ *               bf16 whisper_cross_kv output of each (layer, K|V) slab
+ *               quantised with whisper_fp8_quantize (code = e4m3_rne_saturate(
+ *               fl32(x * fl32(1/scale)))), caller-owned;
+ * cross_scales: [n_dec_layers][2] fp32 device scales, K then V.
+ * The cross-attention reads half the bytes of the bf16 form and dequantises
+ * on read: score = (q . value(codes_k)) * scale_k / 8, output =
+ * sum p * value(codes_v) * scale_v. */
+whisper_status whisper_decode_step_xq(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
+                                      const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                      const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,
+                                      float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                      void* stream);
+
 /* ------------------------------------------------------------------ kernel-level calls
  * fp8 E4M3 codec with a per-tensor scale (project page quantise_e4m3 /
  * dequantise_e4m3). x: n values of dtype `dt`. With scale_in == NULL the scale

@@ -315,6 +315,25 @@ def cross_kv(enc, W, n_heads, n_layers):
     return out
 
 
+def cross_kv_fp8(cross, scales):
+    """fp8 cross-attention keys and values: each layer's K and V are
+    quantised on write with the caller's per-(layer, K|V) scale and read back
+    dequantised, so decode_step then attends over the fp8 values (whisper_blaze
+    showcase page, precision.py card and its preset table: the aggressive
+    preset puts the cross-attention site in fp8; fp8_quantize.cu card: E4M3
+    codes with a per-tensor scale). Reading: E4M3 with one scale per (layer,
+    K|V) tensor, which keeps the range by scaling instead of E5M2's exponent.
+
+    cross: list over layers of (K, V), each an array [B, H, T, dh] or a dict
+    b -> [H, T, dh]; scales: [L, 2]. Returns the same structure holding
+    e4m3_dequantize(e4m3_quantize(x, s), s)."""
+    def q(x, s):
+        if isinstance(x, dict):
+            return {b: e4m3_dequantize(e4m3_quantize(v, s), s) for b, v in x.items()}
+        return e4m3_dequantize(e4m3_quantize(x, s), s)
+    return [(q(k, scales[layer][0]), q(v, scales[layer][1])) for layer, (k, v) in enumerate(cross)]
+
+
 # =========================================================================== decoder step
 
 def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, forced_codes=None):

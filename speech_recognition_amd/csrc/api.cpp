@@ -300,7 +300,8 @@ whisper_status check_ws(void* ws, size_t have, size_t need, const char* what) {
 whisper_status decode_step_fused(const whisper_dims* d, const void* packed, const Packed& P, const DecWS& W, int B,
                                  int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
-                                 int32_t* dev_error, void* ws, hipStream_t s) {
+                                 int32_t* dev_error, void* ws, hipStream_t s, const uint8_t* xcodes = nullptr,
+                                 const float* xscales = nullptr) {
   const int D = d->d_model, H = d->n_heads, T = d->n_audio_ctx, F = d->d_ffn, L = d->n_dec_layers;
   float* X = at<float>(ws, W.x);
   u16_t* Q = at<u16_t>(ws, W.q);
@@ -343,10 +344,16 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.wo, Lw.bo, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));
-    const char* ck = (const char*)cross_kv + l * ckv_layer;
     {
       ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
-      WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s));
+      if (xcodes) {  // e4m3 cross K/V: the fp8 attention kernel over all T keys of each row
+        const uint8_t* xc = xcodes + l * (ckv_layer / 2);
+        WH_TRY(launch_attn_decode_self(ACT_BF16, QC, D, xc, xc + ckv_layer / 4, xscales + 2 * l, nullptr, 0, B, H, T,
+                                       ATT, s));
+      } else {
+        const char* ck = (const char*)cross_kv + l * ckv_layer;
+        WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s));
+      }
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
@@ -649,6 +656,30 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   WH_TRY(launch_gemm_skinny(t, EPI_F32, gp(A, D, at<void>(packed, P.tok), D, B, d->n_vocab, D, nullptr, LG, d->n_vocab), s));
   WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
   return WHISPER_OK;
+}
+
+whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed, int B, int cap,
+                                      const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                      const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,
+                                      float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  WH_CHECK(check_dims(d));
+  if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "decode_step_xq: bf16 models only");
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_step_xq: batch must be > 0");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_step_xq: no decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_step_xq: kv_cap must be in 1..4096");
+  if (d->n_audio_ctx > 4096) return fail(WHISPER_ERR_SHAPE, "decode_step_xq: n_audio_ctx must be <= 4096");
+  WH_CHECK(check_ptrs({packed, kv_cache, cross_codes}, "decode_step_xq"));
+  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, cross_scales, argmax}, "decode_step_xq"));
+  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, "decode_step_xq: logits not 16-byte aligned");
+  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_step_xq: dev_error not 4-byte aligned");
+  const DecWS W = dec_ws(d, B);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_step_xq"));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  float* LG = logits ? logits : at<float>(ws, W.logits);
+  return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, nullptr, LG, argmax,
+                           dev_error, ws, S(stream), cross_codes, cross_scales);
 }
 
 size_t whisper_fp8_workspace_size(void) { return 1024 * sizeof(float); }

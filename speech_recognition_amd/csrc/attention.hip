@@ -257,7 +257,8 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 }
 
 // ------------------------------------------------------------------ decoder self-attention over e4m3 codes
-// Keys 0..n-1 (n = lengths[b] + len_add) are 64-byte code rows read as 4
+// Keys 0..n-1 (n = lengths[b] + len_add, or all cap keys when lengths is
+// NULL, as for the fp8 cross-attention K/V) are 64-byte code rows read as 4
 // lanes x 16 codes.
 constexpr int DEC_MAX_CAP = 4096;
 
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
   __shared__ float red[4][64];
   __shared__ float wmax[4], wsum[4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = max(0, min(lengths[b] + len_add, cap));
+  const int n = lengths ? max(0, min(lengths[b] + len_add, cap)) : cap;
   const int part = tid & 3, kg = tid >> 2;
   float qreg[16];
   {

@@ -103,10 +103,34 @@ hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* r
 }
 
 // ------------------------------------------------------------------ e4m3 codec
+// 8 consecutive elements (16-byte aligned group) as fp32
+__device__ __forceinline__ void load8(const u16* p, float v[8]) {
+  const uint4 w = *(const uint4*)p;
+  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(a[i] << 16);
+    v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void amax_partial(const T* x, size_t n, float* partial) {
   float m = 0.f;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+  // 8 elements per lane per iteration from 16-byte-aligned groups (x is 16-byte
+  // aligned), then the tail one by one
+  const size_t n8 = n / 8, stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    float v[8];
+    load8(x + i * 8, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  }
+  for (size_t i = n8 * 8 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
     m = fmaxf(m, fabsf(Act<T>::cvt(x[i])));
   m = wave_max(m);
   __shared__ float sm[4];
@@ -135,7 +159,19 @@ hipError_t launch_amax(ActType t, const void* x, size_t n, float* partial, int n
 template <typename T>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* x, size_t n, const float* scale, uint8_t* codes) {
   const float inv = 1.0f / scale[0];
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+  // 8 elements per lane per iteration (x 16-byte and codes 8-byte aligned per
+  // group), then the tail one by one
+  const size_t n8 = n / 8, stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    float v[8];
+    load8(x + i * 8, v);
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(v[k] * inv);
+    *(uint2*)(codes + i * 8) = uint2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
+  }
+  for (size_t i = n8 * 8 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
     codes[i] = (uint8_t)e4m3_encode(Act<T>::cvt(x[i]) * inv);
 }
 

@@ -77,23 +77,52 @@ class Whisper:
         L.whisper_cross_kv(d, self.packed, enc, B, ckv)
         return ckv
 
+    def quantize_cross_kv(self, ckv, scales=None, codes=None):
+        """e4m3 codes of bf16 cross K/V [L, 2, B, H, T, 64], one scale per (layer,
+        K|V) slab: the given scales [L, 2], or amax / 448 of each slab when None.
+        Returns (codes uint8 of the same shape, scales fp32 [L, 2] on the device)."""
+        n_l = ckv.shape[0]
+        codes = codes if codes is not None else torch.empty(ckv.shape, dtype=torch.uint8, device=ckv.device)
+        sc = torch.zeros(n_l, 2, dtype=torch.float32, device=ckv.device)
+        if scales is not None:
+            sc.copy_(torch.as_tensor(scales, dtype=torch.float32))
+        ws = None if scales is not None else torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8,
+                                                         device=ckv.device)
+        n = ckv[0, 0].numel()
+        for l in range(n_l):
+            for kv in range(2):
+                if scales is not None:
+                    L.whisper_fp8_quantize(ckv[l, kv], L.WHISPER_BF16, n, sc[l, kv:kv + 1], codes[l, kv], None)
+                else:
+                    L.whisper_fp8_quantize(ckv[l, kv], L.WHISPER_BF16, n, None, codes[l, kv], sc[l, kv:kv + 1],
+                                           ws, ws.numel())
+        return codes, sc
+
     def decode_step(self, state, tokens, logits=None):
         B = state.batch
         ws, nb = self.workspace(B, L.WS_DECODE)
-        L.whisper_decode_step(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
-                              state.kv_scales, state.cross_kv, logits, state.argmax, state.dev_error, ws, nb)
+        if state.cross_codes is not None:
+            L.whisper_decode_step_xq(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
+                                     state.kv_scales, state.cross_codes, state.cross_scales, logits, state.argmax,
+                                     state.dev_error, ws, nb)
+        else:
+            L.whisper_decode_step(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
+                                  state.kv_scales, state.cross_kv, logits, state.argmax, state.dev_error, ws, nb)
         return state.argmax
 
 
 class DecodeState:
-    """Caller-owned decode state: fp8 self-KV cache, scales, lengths, cross K/V."""
+    """Caller-owned decode state: fp8 self-KV cache, scales, lengths, cross K/V
+    (bf16, or e4m3 codes with per-(layer, K|V) scales from quantize_cross_kv)."""
 
-    def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda"):
+    def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda", cross_codes=None,
+                 cross_scales=None):
         self.batch, self.cap = batch, cap
         self.kv_cache = torch.zeros(dims.n_dec_layers, 2, batch, dims.n_heads, cap, 64, dtype=torch.uint8,
                                     device=device)
         self.kv_scales = kv_scales.to(device=device, dtype=torch.float32).contiguous()
         self.lengths = lengths.to(device=device, dtype=torch.int32).contiguous().clone()
         self.cross_kv = cross_kv
+        self.cross_codes, self.cross_scales = cross_codes, cross_scales
         self.argmax = torch.zeros(batch, dtype=torch.int32, device=device)
         self.dev_error = torch.zeros(4, dtype=torch.int32, device=device)

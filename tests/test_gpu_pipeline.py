@@ -147,8 +147,11 @@ def check_logits_argmax(lg_gpu, am_gpu, lg_ref, rows, tag):
     return n_tied
 
 
-def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag):
-    """Teacher-forced decode on the GPU from a prefilled fp8 cache vs the oracle on `rows`."""
+def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None):
+    """Teacher-forced decode on the GPU from a prefilled fp8 cache vs the oracle on `rows`.
+    cross_fp8_scale: when given, the cross-attention K/V are e4m3 codes with that
+    scale for every (layer, K|V), on both sides (the GPU quantises its bf16
+    projections, the oracle its own fp64 ones)."""
     H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
     m, W = model_for(dims, ln_random=True)
     dt = act_dtype(dims)
@@ -164,7 +167,14 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag):
                 x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, H, prefill_max)
                 scales[l, kv] = float(O.e4m3_scale_from_amax(np.array([x.abs().max().item()], np.float32)))
                 prefill[(l, kv)] = x
-    state = DecodeState(dims, B, cap, ckv, scales, lengths0)
+    xscales = None
+    if cross_fp8_scale is not None:
+        xscales = np.full((Lyr, 2), np.float32(cross_fp8_scale), np.float32)
+        xcodes, xsc = m.quantize_cross_kv(ckv, scales=torch.from_numpy(xscales))
+        state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc)
+        del ckv
+    else:
+        state = DecodeState(dims, B, cap, ckv, scales, lengths0)
     for (l, kv), x in prefill.items():
         codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
         L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), state.kv_scales[l, kv:kv + 1].contiguous().clone(),
@@ -188,6 +198,8 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag):
     enc_h = {b: host(enc[b]) for b in rows}
     cross_rows = {b: O.cross_kv(enc_h[b], Wh, H, Lyr) for b in rows}
     cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
+    if xscales is not None:
+        cross = O.cross_kv_fp8(cross, xscales)
     cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
     lengths = lengths0.cpu().numpy().copy()
     for (l, kv), x in prefill.items():
@@ -242,6 +254,18 @@ def test_decode_turbo_shape_batch90_empty_cache():
     dims = CONFIGS["turbo_longform"]
     say("decode turbo shape, 4 layers, B=90, empty cache s=1, 3 steps")
     run_decode_case(dims, 90, 228, 0, 3, [0, 89], "turbo")
+
+
+def test_decode_fp8_cross_kv_large_v3_shape():
+    """fp8 e4m3 cross-attention K/V (one scale per layer and K|V) through
+    whisper_decode_step_xq, against the oracle attending over its own K/V
+    quantised with the same scale. The scale 5/448 covers the K/V range of
+    these inputs (std ~0.7)."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode large-v3 shape, 4 layers, B=64, fp8 cross K/V, cap 672, prefill U[1,448], 3 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 fp8 cross", cross_fp8_scale=5.0 / 448.0)
 
 
 # ------------------------------------------------------------------ tiny fp32 end to end

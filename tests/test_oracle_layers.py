@@ -320,3 +320,48 @@ def test_forced_codes_equal_to_own_codes_change_nothing():
     lg3, tr3 = O.decode_step(W, H, toks[0], np.full(2, 3), c2, scales, cross, forced_codes=forced)
     assert np.all(c2[:, :, :, :, 3, :] == 0x38)
     assert np.array_equal(tr3["codes"][0, 0], O.e4m3_quantize(tr3["pre_quant"][0, 0] * 1.0, 1.0))
+
+
+def test_fp8_cross_kv_grid_values_exact_and_error_bound():
+    """fp8 cross K/V: with power-of-two scales, values already on the scaled
+    e4m3 grid pass unchanged (so a decode step over such K/V equals the
+    unquantised step exactly);
+    others move by at most half an e4m3 step: 2^-4 of the value in the normal
+    range, 2^-10 * scale in the subnormal range; magnitudes past 448 * scale
+    saturate. Dict and array forms agree."""
+    W, H, L, ctx, cross, toks, scales, dh = _fp8_setup()
+    scales = np.array([[2.0 ** -5, 2.0 ** -4], [2.0 ** -6, 2.0 ** -3]], np.float32)  # exact in fp32 both ways
+    rng = np.random.default_rng(5)
+    # snap every K/V onto the scaled grid (finite codes only, within range)
+    grid = []
+    for layer, (k, v) in enumerate(cross):
+        pair = []
+        for kv, x in ((0, k), (1, v)):
+            codes = rng.integers(0, 256, x.shape).astype(np.uint8)
+            codes[(codes & 0x7F) == 0x7F] = 0
+            pair.append(O.e4m3_value(codes).astype(np.float64) * np.float64(np.float32(scales[layer][kv])))
+        grid.append(tuple(pair))
+    q = O.cross_kv_fp8(grid, scales)
+    for layer in range(L):
+        for kv in range(2):
+            assert np.array_equal(q[layer][kv], grid[layer][kv])
+    qd = O.cross_kv_fp8([({b: k[b] for b in range(k.shape[0])}, {b: v[b] for b in range(v.shape[0])})
+                         for k, v in grid], scales)
+    assert all(np.array_equal(qd[l][kv][b], q[l][kv][b]) for l in range(L) for kv in range(2) for b in range(2))
+    B = toks.shape[1]
+    c1 = np.zeros((L, 2, B, H, ctx, dh), np.uint8)
+    c2 = np.zeros_like(c1)
+    lg1, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c1, scales, grid)
+    lg2, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c2, scales, q)
+    assert np.array_equal(lg1, lg2)
+    # error bound on general values, with saturation past the range
+    s = np.float32(0.01)
+    x = rng.standard_normal(20000) * 1.5
+    x[:10] = [5.0, -5.0, 4.48, -4.48, 1e-6, -1e-6, 0.0, 3e-5, 100.0, -100.0]
+    y = O.cross_kv_fp8([(x, x)], np.array([[s, s]], np.float32))[0][0]
+    inr = np.abs(x) <= 448 * float(s)
+    normal = inr & (np.abs(x) >= 2.0 ** -6 * float(s))
+    assert np.all(np.abs(y - x)[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6))
+    sub = inr & ~normal
+    assert np.all(np.abs(y - x)[sub] <= 2.0 ** -10 * float(s) * (1 + 1e-6))
+    assert np.all(np.abs(y[~inr]) == np.float64(np.float32(448.0) * s))
