@@ -243,6 +243,19 @@ whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, c
                                               int batch, int n_heads, int T, void* out, void* ws, size_t ws_bytes,
                                               void* stream);
 
+/* ------------------------------------------------------------------ measured ceilings
+ * The rates this part sustains, for rooflines reported against measured as
+ * well as vendor peaks. whisper_peak_mfma runs n_wg workgroups of 4 waves,
+ * each `iters` rounds of 16 independent MFMA 16x16x32 bf16 on register
+ * operands, and writes n_wg * 4 floats to `out` (device, 4-byte aligned);
+ * its FLOP count is whisper_peak_mfma_flop(n_wg, iters). whisper_peak_read
+ * streams `bytes` (a positive multiple of 16) of the 16-byte-aligned device
+ * buffer `buf` with 16-byte loads over n_wg workgroups of 256 threads and
+ * writes n_wg floats to `out`. Time them with events on `stream`. */
+whisper_status whisper_peak_mfma(int n_wg, int iters, float* out, void* stream);
+double whisper_peak_mfma_flop(int n_wg, int iters);
+whisper_status whisper_peak_read(const void* buf, size_t bytes, int n_wg, float* out, void* stream);
+
 /* ------------------------------------------------------------------ measurement hook
  * For measurement harnesses that need one kernel's own launch duration inside
  * the composite calls, on the stream it runs on. While armed, every launch of

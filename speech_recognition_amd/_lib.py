@@ -24,6 +24,7 @@ EXPORTS = [
     "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
     "whisper_profile_arm", "whisper_profile_disarm", "whisper_status_string", "whisper_last_error",
+    "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read",
 ]
 
 PROF_DECODE_CROSS_ATTENTION, PROF_DECODE_SELF_ATTENTION, PROF_ENCODER_ATTENTION = 1, 2, 3
@@ -73,6 +74,9 @@ _SIG = {
     "whisper_attention_decode_self": (I, [I, P, I, I, I, P, P, P, P, P, P]),
     "whisper_attention_decode_cross_workspace_size": (Z, [I, I, I]),
     "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
+    "whisper_peak_mfma": (I, [I, I, P, P]),
+    "whisper_peak_mfma_flop": (ctypes.c_double, [I, I]),
+    "whisper_peak_read": (I, [P, Z, I, P, P]),
     "whisper_profile_arm": (I, [I, P, P, I]),
     "whisper_profile_disarm": (I, []),
     "whisper_status_string": (ctypes.c_char_p, [I]),
@@ -270,3 +274,16 @@ def whisper_status_string(status):
 
 def whisper_last_error():
     return lib().whisper_last_error().decode()
+
+
+# ------------------------------------------------------------------ measured ceilings
+def whisper_peak_mfma(n_wg, iters, out, stream=None):
+    _check(lib().whisper_peak_mfma(n_wg, iters, _p(out), _stream(stream)))
+
+
+def whisper_peak_mfma_flop(n_wg, iters):
+    return lib().whisper_peak_mfma_flop(n_wg, iters)
+
+
+def whisper_peak_read(buf, nbytes, n_wg, out, stream=None):
+    _check(lib().whisper_peak_read(_p(buf), nbytes, n_wg, _p(out), _stream(stream)))

@@ -682,6 +682,25 @@ whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed,
                            dev_error, ws, S(stream), cross_codes, cross_scales);
 }
 
+whisper_status whisper_peak_mfma(int n_wg, int iters, float* out, void* stream) {
+  if (n_wg <= 0 || iters <= 0) return fail(WHISPER_ERR_INVALID_ARG, "peak_mfma: n_wg and iters must be > 0");
+  WH_CHECK(check_ptrs4({out}, "peak_mfma"));
+  (void)hipGetLastError();
+  WH_TRY(launch_peak_mfma(n_wg, iters, out, S(stream)));
+  return WHISPER_OK;
+}
+
+double whisper_peak_mfma_flop(int n_wg, int iters) { return n_wg > 0 && iters > 0 ? peak_mfma_flop(n_wg, iters) : 0.0; }
+
+whisper_status whisper_peak_read(const void* buf, size_t bytes, int n_wg, float* out, void* stream) {
+  if (n_wg <= 0 || bytes < 16 || bytes % 16) return fail(WHISPER_ERR_INVALID_ARG, "peak_read: n_wg > 0, bytes a positive multiple of 16");
+  WH_CHECK(check_ptrs({buf}, "peak_read"));
+  WH_CHECK(check_ptrs4({out}, "peak_read"));
+  (void)hipGetLastError();
+  WH_TRY(launch_peak_read(buf, bytes, n_wg, out, S(stream)));
+  return WHISPER_OK;
+}
+
 size_t whisper_fp8_workspace_size(void) { return 1024 * sizeof(float); }
 
 whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, const float* scale_in, uint8_t* codes,

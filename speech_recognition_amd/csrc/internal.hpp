@@ -118,4 +118,9 @@ hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, con
                         int x_tiled = 0);  // x_tiled: x in the 16-row tiles of dec_x_index
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s);
 
+// measured ceilings (peak.hip)
+hipError_t launch_peak_mfma(int n_wg, int iters, float* out, hipStream_t s);
+hipError_t launch_peak_read(const void* buf, size_t bytes, int n_wg, float* out, hipStream_t s);
+double peak_mfma_flop(int n_wg, int iters);
+
 }  // namespace wh
