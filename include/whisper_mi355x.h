@@ -119,6 +119,24 @@ size_t whisper_workspace_size(const whisper_dims* dims, int batch, int which);
 whisper_status whisper_logmel(const whisper_dims* dims, const float* audio, int batch, int n_samples,
                               float* mel_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Overlapping-chunk log-mel for long recordings (showcase page,
+ * mel_spectrogram.cu card: overlapping-chunk support for long audio).
+ * Chunk i covers samples [i*stride, i*stride + 480000) of the one recording
+ * `audio` [n_samples] fp32, zero past its end, and is framed, clamped and
+ * scaled as a standalone 30 s clip (whisper_logmel). stride: 160..480000 and
+ * a multiple of the 160-sample hop (480000 = no overlap).
+ * whisper_chunk_plan (host only) returns the chunk count, and with `plan`
+ * non-NULL and max_chunks >= that count fills plan[4 i + 0..3] = {first
+ * sample, valid samples, first owned frame, end of owned frames}: owned
+ * frames (chunk-local, 10 ms each) split every overlap at its midpoint so
+ * each frame of the recording belongs to exactly one chunk, and end at the
+ * last frame centred on real audio in the final chunk. Returns 0 on invalid
+ * input (or too small a plan). mel_out: [count, n_mels, 3000] fp32; ws:
+ * whisper_workspace_size(dims, count, WHISPER_WS_LOGMEL) bytes. */
+int whisper_chunk_plan(int64_t n_samples, int stride, int32_t* plan, int max_chunks);
+whisper_status whisper_logmel_chunked(const whisper_dims* dims, const float* audio, int64_t n_samples, int stride,
+                                      float* mel_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ encoder
  * mel [batch, n_mels, 3000] fp32 -> enc_out [batch, n_audio_ctx, d] (act dtype):
  * conv k3 s1 + GELU, conv k3 s2 + GELU, + sinusoidal positions, n_enc_layers

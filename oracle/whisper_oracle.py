@@ -195,6 +195,43 @@ def log_mel(audio, n_mels):
     return (lg + 4.0) / 4.0
 
 
+def chunk_plan(n_samples, stride, window=480000, hop=160, n_frames=3000):
+    """Overlapping 30 s chunks of one long recording (showcase page,
+    mel_spectrogram.cu card: overlapping-chunk support for long audio).
+    Reading: chunk i covers samples [i*stride, i*stride + window), zero past
+    the end of the recording; the chunk count is the smallest that reaches
+    the last sample. Each shared span of (window - stride) / hop frames is
+    split at its midpoint (the earlier chunk keeps its first floor(span / 2)
+    frames, the later one the rest), so every frame of the recording belongs
+    to one chunk; the last chunk's owned frames end at its last frame centred
+    on real audio. Returns a list of (first sample, valid samples,
+    first owned frame, end of owned frames), frames chunk-local."""
+    assert n_samples > 0 and 0 < stride <= window and stride % hop == 0
+    n = 1 if n_samples <= window else 1 + -(-(n_samples - window) // stride)
+    overlap = n_frames - stride // hop
+    plan = []
+    for i in range(n):
+        start = i * stride
+        valid = min(window, n_samples - start)
+        begin = 0 if i == 0 else overlap // 2
+        end = min(n_frames, -(-valid // hop)) if i == n - 1 else n_frames - (overlap - overlap // 2)
+        plan.append((start, valid, begin, end))
+    return plan
+
+
+def log_mel_chunked(audio, stride, n_mels, window=480000):
+    """[n_chunks, n_mels, 3000] log-mel of the overlapping chunks of one
+    recording: each chunk sliced, zero-padded to 30 s and processed as a
+    standalone clip (its own max - 8 clamp)."""
+    audio = np.asarray(audio, dtype=np.float64)
+    out = []
+    for start, valid, _, _ in chunk_plan(len(audio), stride, window):
+        chunk = np.zeros(window)
+        chunk[:valid] = audio[start:start + valid]
+        out.append(log_mel(chunk, n_mels))
+    return np.stack(out)
+
+
 # =========================================================================== layers
 
 def gelu(x):

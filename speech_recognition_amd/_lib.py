@@ -24,7 +24,8 @@ EXPORTS = [
     "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
     "whisper_profile_arm", "whisper_profile_disarm", "whisper_status_string", "whisper_last_error",
-    "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read",
+    "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read", "whisper_chunk_plan",
+    "whisper_logmel_chunked",
 ]
 
 PROF_DECODE_CROSS_ATTENTION, PROF_DECODE_SELF_ATTENTION, PROF_ENCODER_ATTENTION = 1, 2, 3
@@ -74,6 +75,8 @@ _SIG = {
     "whisper_attention_decode_self": (I, [I, P, I, I, I, P, P, P, P, P, P]),
     "whisper_attention_decode_cross_workspace_size": (Z, [I, I, I]),
     "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
+    "whisper_chunk_plan": (I, [ctypes.c_int64, I, P, I]),
+    "whisper_logmel_chunked": (I, [P, P, ctypes.c_int64, I, P, P, Z, P]),
     "whisper_peak_mfma": (I, [I, I, P, P]),
     "whisper_peak_mfma_flop": (ctypes.c_double, [I, I]),
     "whisper_peak_read": (I, [P, Z, I, P, P]),
@@ -287,3 +290,20 @@ def whisper_peak_mfma_flop(n_wg, iters):
 
 def whisper_peak_read(buf, nbytes, n_wg, out, stream=None):
     _check(lib().whisper_peak_read(_p(buf), nbytes, n_wg, _p(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ overlapping chunks of a long recording
+def whisper_chunk_plan(n_samples, stride):
+    """(count, plan) with plan a list of (first sample, valid samples, first owned frame, end of owned frames)."""
+    n = lib().whisper_chunk_plan(n_samples, stride, None, 0)
+    if n <= 0:
+        raise WhisperError(1, "chunk_plan: need n_samples > 0 and stride in 160..480000, a multiple of 160")
+    buf = (ctypes.c_int32 * (4 * n))()
+    lib().whisper_chunk_plan(n_samples, stride, buf, n)
+    return n, [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def whisper_logmel_chunked(dims, audio, n_samples, stride, mel_out, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_logmel_chunked(dp, _p(audio), n_samples, stride, _p(mel_out), _p(ws), ws_bytes,
+                                        _stream(stream)))

@@ -3,6 +3,7 @@
 // All checks run before the first launch; nothing throws across the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -524,6 +525,38 @@ whisper_status whisper_logmel(const whisper_dims* d, const float* audio, int B, 
   WH_CHECK(check_ws(ws, ws_bytes, whisper_workspace_size(d, B, WHISPER_WS_LOGMEL), "logmel"));
   (void)hipGetLastError();
   WH_TRY(launch_logmel(audio, B, n_samples, d->n_mels, mel_out, ws, S(stream)));
+  return WHISPER_OK;
+}
+
+int whisper_chunk_plan(int64_t n_samples, int stride, int32_t* plan, int max_chunks) {
+  constexpr long W = 480000, HOP = 160, NFR = 3000;
+  if (n_samples <= 0 || stride <= 0 || stride > W || stride % HOP) return 0;
+  const long n = n_samples <= W ? 1 : 1 + (n_samples - W + stride - 1) / stride;
+  if (n > 0x7fffffff) return 0;
+  if (!plan) return (int)n;
+  if (max_chunks < n) return 0;
+  const long sf = stride / HOP, of = NFR - sf;  // frames per stride, frames of overlap
+  for (long i = 0; i < n; ++i) {
+    const long start = i * stride, valid = std::min(W, n_samples - start);
+    const long vf = std::min(NFR, (valid + HOP - 1) / HOP);  // frames centred on real audio
+    plan[4 * i + 0] = (int32_t)start;
+    plan[4 * i + 1] = (int32_t)valid;
+    plan[4 * i + 2] = (int32_t)(i == 0 ? 0 : of / 2);
+    plan[4 * i + 3] = (int32_t)(i == n - 1 ? vf : NFR - (of - of / 2));
+  }
+  return (int)n;
+}
+
+whisper_status whisper_logmel_chunked(const whisper_dims* d, const float* audio, int64_t n_samples, int stride,
+                                      float* mel_out, void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  const int n = whisper_chunk_plan(n_samples, stride, nullptr, 0);
+  if (n <= 0) return fail(WHISPER_ERR_SHAPE, "logmel_chunked: need n_samples > 0 and stride in 160..480000, a multiple of 160");
+  if (n_samples > (1L << 40)) return fail(WHISPER_ERR_SHAPE, "logmel_chunked: n_samples too large");
+  WH_CHECK(check_ptrs({audio, mel_out}, "logmel_chunked"));
+  WH_CHECK(check_ws(ws, ws_bytes, whisper_workspace_size(d, n, WHISPER_WS_LOGMEL), "logmel_chunked"));
+  (void)hipGetLastError();
+  WH_TRY(launch_logmel(audio, n, 480000, d->n_mels, mel_out, ws, S(stream), stride, n_samples));
   return WHISPER_OK;
 }
 

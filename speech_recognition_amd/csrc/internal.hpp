@@ -99,8 +99,10 @@ hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, con
 
 // ------------------------------------------------------------------ log-mel
 size_t logmel_ws(int B, int n_mels);
+// row_stride / total: chunk b starts at audio + b * row_stride, total samples
+// from audio[0] (row_stride <= 0: separate clips of n_samples each)
 hipError_t launch_logmel(const float* audio, int B, int n_samples, int n_mels, float* mel_out, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, long row_stride = 0, long total = 0);
 
 // ------------------------------------------------------------------ misc
 hipError_t launch_mel_to_conv_input(ActType t, const float* mel, int B, int n_mels, int n_frames, void* x0,

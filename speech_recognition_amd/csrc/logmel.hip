@@ -68,22 +68,27 @@ __global__ __launch_bounds__(256) void logmel_setup(float* ws, int n_mels) {
   }
 }
 
-__global__ __launch_bounds__(256) void logmel_frames(const float* __restrict__ audio, int n_samples, int n_mels,
-                                                     const float* __restrict__ ws, float* __restrict__ mel_out,
-                                                     float* __restrict__ bmax) {
+// Chunk b starts at audio + b * row_stride and holds n_valid(b) = min(n_samples,
+// total - b * row_stride) samples, zero beyond (row_stride = n_samples, total =
+// B * n_samples for separate clips; a stride below 30 s for overlapping chunks
+// of one long recording).
+__global__ __launch_bounds__(256) void logmel_frames(const float* __restrict__ audio, int n_samples, long row_stride,
+                                                     long total, int n_mels, const float* __restrict__ ws,
+                                                     float* __restrict__ mel_out, float* __restrict__ bmax) {
   __shared__ float xs[FT][NFFT];
   __shared__ float cs[NFFT], sn[NFFT];
   __shared__ float pw[FT][NBIN + 3];
   __shared__ float wm[4];
   const int b = blockIdx.y, f0 = blockIdx.x * FT, tid = threadIdx.x;
-  const float* a = audio + (size_t)b * n_samples;
+  const float* a = audio + (size_t)b * row_stride;
+  const long n_valid = min((long)n_samples, total - (long)b * row_stride);
   for (int i = tid; i < NFFT; i += 256) { cs[i] = ws[i]; sn[i] = ws[NFFT + i]; }
   for (int i = tid; i < FT * NFFT; i += 256) {
     const int f = i / NFFT, n = i - f * NFFT;
     int s = (f0 + f) * HOPL + n - NFFT / 2;
     if (s < 0) s = -s;
     if (s >= NSAMP) s = 2 * (NSAMP - 1) - s;
-    const float v = (s < n_samples) ? a[s] : 0.f;
+    const float v = (s < n_valid) ? a[s] : 0.f;
     xs[f][n] = v * ws[2 * NFFT + n];
   }
   __syncthreads();
@@ -146,11 +151,12 @@ __global__ __launch_bounds__(256) void logmel_finalize(float* __restrict__ mel_o
 }
 
 hipError_t launch_logmel(const float* audio, int B, int n_samples, int n_mels, float* mel_out, void* ws_,
-                         hipStream_t s) {
+                         hipStream_t s, long row_stride, long total) {
   float* ws = (float*)ws_;
+  if (row_stride <= 0) { row_stride = n_samples; total = (long)B * n_samples; }
   hipLaunchKernelGGL(logmel_setup, dim3((NFFT + 255) / 256), dim3(256), 0, s, ws, n_mels);
-  hipLaunchKernelGGL(logmel_frames, dim3(NBLK, B), dim3(256), 0, s, audio, n_samples, n_mels, ws, mel_out,
-                     ws + bmax_off(n_mels));
+  hipLaunchKernelGGL(logmel_frames, dim3(NBLK, B), dim3(256), 0, s, audio, n_samples, row_stride, total, n_mels, ws,
+                     mel_out, ws + bmax_off(n_mels));
   hipLaunchKernelGGL(logmel_finalize, dim3(64, B), dim3(256), 0, s, mel_out, ws + bmax_off(n_mels), n_mels);
   return hipGetLastError();
 }

@@ -97,3 +97,16 @@ def test_kernel_call_validation():
         L.whisper_attention_decode_self(L.WHISPER_BF16, 16, 4, 20, 5000, 16, 16, 16, 16, 16, stream=0)
     assert e.value.status == 2
     assert L.whisper_status_string(6) == "KV cache capacity exceeded"
+
+
+def test_chunk_plan_host_logic_matches_oracle():
+    """whisper_chunk_plan is host arithmetic: its plan equals the oracle's for
+    strides with and without overlap; invalid strides are rejected."""
+    from oracle import whisper_oracle as O
+    for n in (1, 479999, 480000, 480001, 1_200_000, 43_200_000):
+        for stride in (480000, 400000, 320000, 160160):
+            count, plan = L.whisper_chunk_plan(n, stride)
+            assert count == len(plan) and plan == O.chunk_plan(n, stride), (n, stride)
+    for bad in ((0, 400000), (1000, 0), (1000, 480160), (1000, 1000)):
+        with pytest.raises(L.WhisperError):
+            L.whisper_chunk_plan(*bad)

@@ -233,3 +233,27 @@ def test_logmel(n_mels, n_samples):
         e = rel_err(host(mel)[b], ref)
         say(f"  chunk {b}: rel err {e:.2e}")
         assert e < 1e-3
+
+
+@pytest.mark.parametrize("stride", [400000, 480000])
+def test_logmel_chunked_long_recording(stride):
+    """Overlapping (25 s stride) and back-to-back chunks of one 75.5 s
+    recording: each chunk's log-mel against the oracle's slice of the same
+    recording (the last chunk zero-padded)."""
+    from workload import gen_audio_longform
+    dims = CONFIGS["v3_encoder"]
+    n = 1_208_000
+    rec = gen_audio_longform(DEV, 9, minutes=3.0)[:3].reshape(-1)[:n].contiguous()
+    count, plan = L.whisper_chunk_plan(n, stride)
+    say(f"logmel_chunked n={n} stride={stride}: {count} chunks")
+    mel = torch.empty(count, 128, 3000, dtype=torch.float32, device=DEV)
+    nws = L.whisper_workspace_size(dims, count, L.WS_LOGMEL)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    L.whisper_logmel_chunked(dims, rec, n, stride, mel, ws, nws)
+    torch.cuda.synchronize()
+    ref = O.log_mel_chunked(rec.cpu().double().numpy(), stride, 128)
+    assert ref.shape[0] == count
+    for i in range(count):
+        e = rel_err(host(mel)[i], ref[i])
+        say(f"  chunk {i} (samples {plan[i][0]}..+{plan[i][1]}): rel err {e:.2e}")
+        assert e < 1e-3

@@ -106,3 +106,58 @@ def test_log_mel_composition():
     lg = np.log10(np.maximum(mel, 1e-10)).T
     assert np.allclose(out, (np.maximum(lg, lg.max() - 8) + 4) / 4)
     assert out.min() >= (lg.max() - 8 + 4) / 4 - 1e-12
+
+
+# ------------------------------------------------------------------ overlapping chunks of one recording
+def test_chunk_plan_owned_frames_partition_the_recording():
+    """Owned frames (chunk-local plus the chunk's first frame) tile the frames
+    of the recording exactly once, for strides with and without overlap and
+    lengths around the window edge; chunk starts step by the stride; the last
+    chunk reaches the last sample; valid counts are what is left."""
+    for n in (1, 1000, 479999, 480000, 480001, 880000, 1_200_000, 2_700_000 + 123):
+        for stride in (480000, 400000, 240000, 160160, 160):
+            if stride < 160000 and n > 1_000_000:
+                continue
+            plan = O.chunk_plan(n, stride)
+            owned = []
+            for i, (start, valid, b, e) in enumerate(plan):
+                assert start == i * stride and valid == min(480000, n - start) and valid > 0
+                assert 0 <= b <= e <= 3000
+                owned.extend(range(start // 160 + b, start // 160 + e))
+            assert plan[-1][0] + plan[-1][1] == n
+            assert owned == list(range(-(-n // 160))), (n, stride)
+
+
+def test_chunked_log_mel_without_overlap_is_the_per_chunk_log_mel():
+    """stride = 30 s: the chunks are the plain 30 s slices (the last one
+    zero-padded), so each chunk equals log_mel of its slice."""
+    rng = np.random.default_rng(9)
+    audio = rng.standard_normal(480000 * 2 + 123_456) * 0.1
+    got = O.log_mel_chunked(audio, 480000, 80)
+    assert got.shape == (3, 80, 3000)
+    for i in range(3):
+        clip = np.zeros(480000)
+        part = audio[i * 480000:(i + 1) * 480000]
+        clip[:len(part)] = part
+        assert np.array_equal(got[i], O.log_mel(clip, 80))
+
+
+def test_overlapping_chunks_share_interior_frames_before_the_clamp():
+    """With a stride of S samples (S / 160 frames), chunk i + 1's frame t
+    sees exactly the samples of chunk i's frame t + S / 160 wherever neither
+    window touches a chunk edge, so their unclamped log-mel columns agree."""
+    rng = np.random.default_rng(10)
+    stride = 400000
+    audio = rng.standard_normal(880000) * 0.1
+    plan = O.chunk_plan(len(audio), stride)
+    assert len(plan) == 2
+    c0 = audio[:480000]
+    c1 = np.zeros(480000)
+    c1[:plan[1][1]] = audio[stride:stride + plan[1][1]]
+    u0 = O.log_mel_unnormalised(c0, 80)
+    u1 = O.log_mel_unnormalised(c1, 80)
+    sf = stride // 160
+    ts = np.arange(2, 3000 - sf - 2)   # windows of 400 samples stay inside both chunks
+    assert np.allclose(u0[:, ts + sf], u1[:, ts], rtol=0, atol=1e-9)
+    # at the edges they do differ (reflection at a chunk's own start)
+    assert not np.allclose(u0[:, sf], u1[:, 0], rtol=0, atol=1e-9)
