@@ -180,6 +180,21 @@ whisper_status whisper_decode_step(const whisper_dims* dims, const void* packed,
                                    const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
                                    int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
+/* Causal prefill of n_tokens prompt tokens per row in one pass (the pages'
+ * decoder self-attention with multiple queries; showcase page,
+ * flash_attn_hopper.cu card: causal mask). bf16 models only. tokens:
+ * [batch, n_tokens] int32; row b's token p goes to cache slot and position
+ * lengths[b] + p and attends over slots 0 .. lengths[b] + p. The result
+ * equals n_tokens successive whisper_decode_step calls with those tokens:
+ * the same codes in kv_cache, and logits / argmax of each row's last
+ * token ([batch, n_vocab] / [batch]); lengths[b] += n_tokens. Requires
+ * batch * n_tokens <= 4096; ws: whisper_workspace_size(dims, batch *
+ * n_tokens, WHISPER_WS_DECODE) bytes. Other arguments as whisper_decode_step. */
+whisper_status whisper_decode_prefill(const whisper_dims* dims, const void* packed, int batch, int n_tokens,
+                                      int kv_cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                      const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
+                                      int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
 /* Decoder step with fp8 cross-attention K/V (the fp8 cross-attention site of
  * the pages' precision presets; project page, "Direct Kernel API":
  * quantise_e4m3 with a per-tensor scale). As whisper_decode_step, bf16 models

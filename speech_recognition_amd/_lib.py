@@ -19,7 +19,7 @@ WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE = 0, 1, 2, 3
 EXPORTS = [
     "whisper_weight_count", "whisper_packed_weights_size", "whisper_pack_weights", "whisper_workspace_size",
     "whisper_logmel", "whisper_encode", "whisper_encode_layers", "whisper_cross_kv", "whisper_decode_step",
-    "whisper_decode_step_xq",
+    "whisper_decode_step_xq", "whisper_decode_prefill",
     "whisper_fp8_workspace_size", "whisper_fp8_quantize", "whisper_fp8_dequantize", "whisper_layernorm_fused",
     "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
@@ -66,6 +66,7 @@ _SIG = {
     "whisper_cross_kv": (I, [P, P, P, I, P, P, Z, P]),
     "whisper_decode_step": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_decode_prefill": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_fp8_workspace_size": (Z, []),
     "whisper_fp8_quantize": (I, [P, I, Z, P, P, P, P, Z, P]),
     "whisper_fp8_dequantize": (I, [P, Z, P, P, I, P]),
@@ -200,6 +201,14 @@ def whisper_decode_step(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, 
     _check(lib().whisper_decode_step(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
                                      _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax), _p(dev_error), _p(ws),
                                      ws_bytes, _stream(stream)))
+
+
+def whisper_decode_prefill(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv,
+                           logits, argmax, dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_prefill(dp, _p(packed), batch, n_tokens, kv_cap, _p(tokens), _p(lengths),
+                                        _p(kv_cache), _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax),
+                                        _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
 
 
 def whisper_decode_step_xq(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_codes,

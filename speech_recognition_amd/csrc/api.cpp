@@ -156,7 +156,7 @@ EncWS enc_ws(const whisper_dims* d, int B) {
 // The MLP down-projection (K = d_ffn) runs split-K over DEC_KSPLIT workgroups
 // per 16 x 80 output tile; its partials and tile counters live here.
 constexpr int DEC_KSPLIT = 4, DEC_SPLIT_COLS = 80;
-struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, total; };
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, total; };
 DecWS dec_ws(const whisper_dims* d, int B) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
@@ -171,6 +171,7 @@ DecWS dec_ws(const whisper_dims* d, int B) {
   W.part = take(tiles * DEC_KSPLIT * (DEC_SPLIT_COLS / 16) * 64 * 16);
   W.n_cnt = tiles;
   W.cnt = take(tiles * 4);
+  W.xg = take((size_t)((B + 15) & ~15) * D * 4);  // prefill: the last position of each batch row, 16-row tiles
   W.total = off;
   return W;
 }
@@ -302,7 +303,11 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
                                  int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
                                  int32_t* dev_error, void* ws, hipStream_t s, const uint8_t* xcodes = nullptr,
-                                 const float* xscales = nullptr) {
+                                 const float* xscales = nullptr, int R = 1) {
+  // B batch rows of the cache; R tokens per row (a prefill when R > 1): the
+  // activations have B * R rows, row m being token m % R of batch row m / R
+  const int Bc = B;
+  B = Bc * R;
   const int D = d->d_model, H = d->n_heads, T = d->n_audio_ctx, F = d->d_ffn, L = d->n_dec_layers;
   float* X = at<float>(ws, W.x);
   u16_t* Q = at<u16_t>(ws, W.q);
@@ -311,7 +316,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* HF = at<u16_t>(ws, W.hf);
   int32_t* CNT = at<int32_t>(ws, W.cnt);
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
-                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1));
+                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
                   u16_t* out, float* out_f32, int layer, bool split = false) {
     DecGemmParams g{};
@@ -321,7 +326,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     g.c1 = c1_off ? at<float>(packed, c1_off) : nullptr;
     g.A = A; g.lda = K; g.X = X; g.out = out; g.out_f32 = out_f32;
     g.kv_cache = kv_cache; g.kv_scales = kv_scales; g.lengths = lengths; g.dev_error = dev_error;
-    g.kv_cap = cap; g.kv_B = B; g.kv_H = H; g.kv_layer = layer; g.d_model = D;
+    g.kv_cap = cap; g.kv_B = Bc; g.kv_H = H; g.kv_layer = layer; g.d_model = D; g.rows_per_b = R;
     int mb, cb;
     dec_gemm_tiles(B, N, mb, cb);
     // split-K where the long K would otherwise leave a third of the CUs idle
@@ -332,8 +337,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     }
     return launch_gemm_dec(pro, epi, g, mb, cb, s);
   };
-  const size_t kv_layer = (size_t)2 * B * H * cap * 64;
-  const size_t ckv_layer = (size_t)2 * B * H * T * 64 * 2;
+  const size_t kv_layer = (size_t)2 * Bc * H * cap * 64;
+  const size_t ckv_layer = (size_t)2 * Bc * H * T * 64 * 2;
   for (int l = 0; l < L; ++l) {
     const DecL& Lw = P.dec[l];
     WH_TRY(gemm(PRO_X, DEPI_QKV, Lw.wqkv, Lw.bqkv, Lw.c1qkv, 3 * D, D, nullptr, Q, nullptr, l));
@@ -341,7 +346,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     {
       ProfScope ps(WHISPER_PROF_DECODE_SELF_ATTENTION, s);
       WH_TRY(launch_attn_decode_self(ACT_BF16, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap,
-                                     ATT, s));
+                                     ATT, s, R));
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.wo, Lw.bo, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));
@@ -350,18 +355,24 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
       if (xcodes) {  // e4m3 cross K/V: the fp8 attention kernel over all T keys of each row
         const uint8_t* xc = xcodes + l * (ckv_layer / 2);
         WH_TRY(launch_attn_decode_self(ACT_BF16, QC, D, xc, xc + ckv_layer / 4, xscales + 2 * l, nullptr, 0, B, H, T,
-                                       ATT, s));
+                                       ATT, s, R));
       } else {
         const char* ck = (const char*)cross_kv + l * ckv_layer;
-        WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s));
+        WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s, R));
       }
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l, true));
   }
+  if (R > 1) {  // vocabulary projection and argmax of each batch row's last position only
+    float* XG = at<float>(ws, W.xg);
+    WH_TRY(launch_gather_last_rows(X, XG, Bc, R, D, s));
+    X = XG;
+    B = Bc;
+  }
   WH_TRY(gemm(PRO_X, DEPI_F32, P.lmw, P.lmb2, P.lmc1, d->n_vocab, D, nullptr, nullptr, LG, 0));
-  WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
+  WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s, R));
   return WHISPER_OK;
 }
 
@@ -689,6 +700,29 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   WH_TRY(launch_gemm_skinny(t, EPI_F32, gp(A, D, at<void>(packed, P.tok), D, B, d->n_vocab, D, nullptr, LG, d->n_vocab), s));
   WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
   return WHISPER_OK;
+}
+
+whisper_status whisper_decode_prefill(const whisper_dims* d, const void* packed, int B, int n_tokens, int cap,
+                                      const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                      const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
+                                      int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "decode_prefill: bf16 models only");
+  if (B <= 0 || n_tokens <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_prefill: batch and n_tokens must be > 0");
+  if ((long)B * n_tokens > 4096) return fail(WHISPER_ERR_SHAPE, "decode_prefill: batch * n_tokens must be <= 4096");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_prefill: no decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_prefill: kv_cap must be in 1..4096");
+  WH_CHECK(check_ptrs({packed, kv_cache, cross_kv}, "decode_prefill"));
+  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, "decode_prefill"));
+  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, "decode_prefill: logits not 16-byte aligned");
+  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_prefill: dev_error not 4-byte aligned");
+  const DecWS W = dec_ws(d, B * n_tokens);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_prefill"));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  float* LG = logits ? logits : at<float>(ws, W.logits);
+  return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, LG, argmax,
+                           dev_error, ws, S(stream), nullptr, nullptr, n_tokens);
 }
 
 whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed, int B, int cap,

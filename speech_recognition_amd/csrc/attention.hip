@@ -308,11 +308,12 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
                                                                const uint8_t* __restrict__ vc,
                                                                const float* __restrict__ scales,
                                                                const int32_t* __restrict__ lengths, int len_add, int H,
-                                                               int cap, T* __restrict__ out) {
+                                                               int cap, T* __restrict__ out, int rows_per_b) {
   __shared__ float red[4][64];
   __shared__ float wmax[4], wsum[4];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lengths ? max(0, min(lengths[b] + len_add, cap)) : cap;
+  const int bc = b / rows_per_b;  // cache batch row of query row b
+  const int n = lengths ? max(0, min(lengths[bc] + len_add + b % rows_per_b, cap)) : cap;
   const int part = tid & 3, kg = tid >> 2;
   float qreg[16];
   {
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
     for (int i = 0; i < 16; ++i) qreg[i] = Act<T>::cvt(qp[i]);
   }
   const float sscale = scales[0] * (0.125f * LOG2E), sv = scales[1];  // scores in base-2 units
-  const long head = ((long)b * H + h) * cap * 64 + part * 16;
+  const long head = ((long)bc * H + h) * cap * 64 + part * 16;
   const uint8_t* K = kc + head;
   const uint8_t* V = vc + head;
   float m = -INFINITY, l = 0.f, acc[16];
@@ -402,15 +403,15 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
 
 hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths, int len_add,
-                                   int B, int H, int cap, void* out, hipStream_t s) {
-  if (cap > DEC_MAX_CAP) return hipErrorInvalidValue;
+                                   int B, int H, int cap, void* out, hipStream_t s, int rows_per_b) {
+  if (cap > DEC_MAX_CAP || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
   dim3 grid(H, B);
   if (t == ACT_BF16)
     hipLaunchKernelGGL(attn_decode_self_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, q_stride, k_codes,
-                       v_codes, scales, lengths, len_add, H, cap, (u16*)out);
+                       v_codes, scales, lengths, len_add, H, cap, (u16*)out, rows_per_b);
   else
     hipLaunchKernelGGL(attn_decode_self_kernel<float>, grid, dim3(256), 0, s, (const float*)q, q_stride, k_codes,
-                       v_codes, scales, lengths, len_add, H, cap, (float*)out);
+                       v_codes, scales, lengths, len_add, H, cap, (float*)out, rows_per_b);
   return hipGetLastError();
 }
 
@@ -441,7 +442,7 @@ __device__ __forceinline__ void unpack16(const float4 w, float o[4]) {
 template <typename T>
 __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const T* __restrict__ v, int H, int T_,
-                                                                T* __restrict__ out) {
+                                                                T* __restrict__ out, int rows_per_b) {
   constexpr int EPT = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int TPK = 64 / EPT;         // lanes per key row
   constexpr int KPP = 256 / TPK;        // keys per pass
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
 #pragma unroll
     for (int i = 0; i < EPT; ++i) qreg[i] = Act<T>::cvt(qp[i]) * (0.125f * LOG2E);  // scores in base-2 units
   }
-  const long head = ((long)b * H + h) * T_ * 64 + part * EPT;
+  const long head = ((long)(b / rows_per_b) * H + h) * T_ * 64 + part * EPT;  // K/V of the query row's batch row
   const T* K = k + head;
   const T* V = v + head;
   float m = -INFINITY, l = 0.f, acc[EPT];
@@ -535,15 +536,15 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
 }
 
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
-                                    void* out, hipStream_t s) {
-  if (T <= 0) return hipErrorInvalidValue;
+                                    void* out, hipStream_t s, int rows_per_b) {
+  if (T <= 0 || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
   const dim3 grid(H, B);
   if (t == ACT_BF16)
     hipLaunchKernelGGL(attn_decode_cross_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, (const u16*)k,
-                       (const u16*)v, H, T, (u16*)out);
+                       (const u16*)v, H, T, (u16*)out, rows_per_b);
   else
     hipLaunchKernelGGL(attn_decode_cross_kernel<float>, grid, dim3(256), 0, s, (const float*)q, (const float*)k,
-                       (const float*)v, H, T, (float*)out);
+                       (const float*)v, H, T, (float*)out, rows_per_b);
   return hipGetLastError();
 }
 

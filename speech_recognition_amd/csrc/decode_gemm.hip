@@ -1,4 +1,5 @@
-// GEMMs of the batched decoder step (M = batch rows <= 128), with the
+// GEMMs of the batched decoder step (M = batch rows, or batch rows x prompt
+// tokens in a prefill; up to 4096), with the
 // residual + LayerNorm of the whisper_blaze showcase page's layernorm_fused.cu
 // card folded into them.
 //
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   // (its stores may alias these addresses: loads left in the store loop would
   // serialise).
   constexpr bool RES = EPI == DEPI_RESID, QKV = EPI == DEPI_QKV;
+  const int RPB = p.rows_per_b > 1 ? p.rows_per_b : 1;  // rows per batch row (prefill)
   static_assert(MB * CB <= DG_WAVES, "one output block per wave");
   const bool ewave = wave < MB * CB;
   const int emb = ewave ? wave / CB : 0, ecb = ewave ? wave - (wave / CB) * CB : 0;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     for (int r = 0; r < 4; ++r) {
       const int m = min(m0 + emb * 16 + (lane >> 4) * 4 + r, M - 1);
       if constexpr (RES) e_x[r] = p.X[dec_x_index(m, n, N)];
-      if constexpr (QKV) e_pos[r] = p.lengths[m];
+      if constexpr (QKV) e_pos[r] = p.lengths[m / RPB] + m % RPB;
     }
     if constexpr (QKV) {
       e_inv[0] = 1.0f / p.kv_scales[p.kv_layer * 2];
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
         const int kv = (n - d) / d, c = (n - d) - kv * d, pos = e_pos[r];
         if (pos >= 0 && pos < p.kv_cap) {
           const long idx =
-              ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
+              ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m / RPB) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
           p.kv_cache[idx] = (uint8_t)e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
         } else if (p.dev_error) {
           *p.dev_error = 6;  // capacity exceeded: the write is skipped
@@ -359,7 +361,7 @@ void dec_gemm_tiles(int M, int N, int& mb, int& cb) {
 }
 
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s) {
-  if (p.M <= 0 || p.M > 128 || p.N <= 0 || p.K <= 0 || p.K % 32) return hipErrorInvalidValue;
+  if (p.M <= 0 || p.M > 4096 || p.N <= 0 || p.K <= 0 || p.K % 32) return hipErrorInvalidValue;
   if (p.ks > 1 && (pro != PRO_A || !p.part || !p.cnt || p.ks > 16 || (p.K / 32) % (p.ks * DG_WAVES)))
     return hipErrorInvalidValue;  // split-K: bf16 activations, whole k-steps per wave, workspace given
   if (pro == PRO_X) {

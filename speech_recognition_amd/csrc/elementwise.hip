@@ -330,17 +330,19 @@ hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per
 }
 
 // ------------------------------------------------------------------ decoder embedding / argmax
-// x[b] = tok_emb[tokens[b]] + pos_emb[lengths[b]] into the fp32 residual stream.
+// x[b] = tok_emb[tokens[b]] + pos_emb[lengths[b]] into the fp32 residual stream
+// (in a prefill of R tokens per batch row, row b is token b % R of batch row
+// b / R, at position lengths[b / R] + b % R).
 // Out-of-range token ids or positions write zeros and raise the device error.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* pos_emb, const int32_t* tokens,
                                                     const int32_t* lengths, int d, int n_vocab, int n_ctx, int cap,
                                                     float* x, int32_t* dev_error, int32_t* zero, int n_zero,
-                                                    int x_tiled) {
+                                                    int x_tiled, int rows_per_b) {
   const int b = blockIdx.x;
   if (b == 0)  // the step's split-K counters start at zero
     for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
-  const int tok = tokens[b], pos = lengths[b];
+  const int tok = tokens[b], pos = lengths[b / rows_per_b] + b % rows_per_b;
   const bool ok = tok >= 0 && tok < n_vocab && pos >= 0 && pos < n_ctx && pos < cap;
   if (!ok && dev_error && threadIdx.x == 0) *dev_error = (pos >= cap) ? 6 : 1;
   for (int c = threadIdx.x; c < d; c += 256) {
@@ -352,21 +354,24 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* p
 
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
-                        int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero, int x_tiled) {
-  if (x_tiled && d % 32) return hipErrorInvalidValue;
+                        int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero, int x_tiled,
+                        int rows_per_b) {
+  if ((x_tiled && d % 32) || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
   if (t == ACT_BF16)
     hipLaunchKernelGGL(embed_kernel<u16>, dim3(B), dim3(256), 0, s, (const u16*)tok_emb, (const u16*)pos_emb, tokens,
-                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled);
+                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(B), dim3(256), 0, s, (const float*)tok_emb, (const float*)pos_emb,
-                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled);
+                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b);
   return hipGetLastError();
 }
 
-// Greedy token per row: largest logit, lowest index on ties; then lengths[b] += 1.
+// Greedy token per row: largest logit, lowest index on ties; then lengths[b] +=
+// len_inc (1 per decode step, the prompt length after a prefill).
 // 1024 lanes per row with 16-byte loads, so a 51866-wide row is one pass of
 // ~13 independent loads per lane.
-__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out, int32_t* lengths) {
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int32_t* out, int32_t* lengths,
+                                                     int len_inc) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const float* row = logits + (size_t)b * V;
   float best = -INFINITY;
@@ -398,12 +403,26 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V
     for (int w = 1; w < 16; ++w)
       if (sv[w] > best || (sv[w] == best && si[w] < idx)) { best = sv[w]; idx = si[w]; }
     out[b] = idx == 0x7fffffff ? 0 : idx;
-    if (lengths) lengths[b] += 1;
+    if (lengths) lengths[b] += len_inc;
   }
 }
 
-hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, s, logits, V, argmax, lengths);
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s,
+                         int len_inc) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, s, logits, V, argmax, lengths, len_inc);
+  return hipGetLastError();
+}
+
+// Last position of each batch row of a prefill: x_dst row b = x_src row
+// b * R + R - 1, both in the 16-row tiles of dec_x_index.
+__global__ __launch_bounds__(256) void gather_last_rows_kernel(const float* x_src, float* x_dst, int R, int d) {
+  const int b = blockIdx.x;
+  for (int c = threadIdx.x; c < d; c += 256) x_dst[dec_x_index(b, c, d)] = x_src[dec_x_index((long)b * R + R - 1, c, d)];
+}
+
+hipError_t launch_gather_last_rows(const float* x_src, float* x_dst, int B, int R, int d, hipStream_t s) {
+  if (B <= 0 || R < 1 || d % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_last_rows_kernel, dim3(B), dim3(256), 0, s, x_src, x_dst, R, d);
   return hipGetLastError();
 }
 

@@ -65,6 +65,9 @@ struct DecGemmParams {
   // partial blocks [tiles][ks][MB*CB][64 lanes] f32x4 and one counter per tile,
   // zero on entry (each launch leaves them zero)
   int ks; float* part; int32_t* cnt;
+  // rows per batch row (prefill of R tokens per row: row m is batch row m / R
+  // at position lengths[m / R] + m % R); 0 or 1 for one token per row
+  int rows_per_b;
 };
 void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
@@ -90,12 +93,15 @@ hipError_t launch_fp8_dequantize(ActType t, const uint8_t* codes, size_t n, cons
 // Encoder self-attention over the packed QKV [B*T, 3*H*64] -> out [B*T, H*64].
 hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, void* out, hipStream_t s);
 // Decode causal self-attention over e4m3 codes [B][H][cap][64]; n_keys[b] = lengths[b] + add.
+// rows_per_b (R): query row m reads cache batch row m / R and attends over
+// n = lengths[m / R] + len_add + m % R keys (B = query rows)
 hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths,
-                                   int len_add, int B, int H, int cap, void* out, hipStream_t s);
-// Decode cross-attention over head-major K/V [B][H][T][64]; split over T.
+                                   int len_add, int B, int H, int cap, void* out, hipStream_t s, int rows_per_b = 1);
+// Decode cross-attention over head-major K/V [B / R][H][T][64] (query row m
+// reads K/V batch row m / R, R = rows_per_b); one pass per (row, head).
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
-                                    void* out, hipStream_t s);
+                                    void* out, hipStream_t s, int rows_per_b = 1);
 
 // ------------------------------------------------------------------ log-mel
 size_t logmel_ws(int B, int n_mels);
@@ -117,8 +123,12 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
                         int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0,
-                        int x_tiled = 0);  // x_tiled: x in the 16-row tiles of dec_x_index
-hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s);
+                        int x_tiled = 0, int rows_per_b = 1);  // x_tiled: x in the 16-row tiles of dec_x_index;
+                        // rows_per_b (R): B rows, row m is token m of batch row m / R at lengths[m / R] + m % R
+hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s,
+                         int len_inc = 1);
+// x_dst row b = x_src row b * R + R - 1 (both in the 16-row tiles of dec_x_index)
+hipError_t launch_gather_last_rows(const float* x_src, float* x_dst, int B, int R, int d, hipStream_t s);
 
 // measured ceilings (peak.hip)
 hipError_t launch_peak_mfma(int n_wg, int iters, float* out, hipStream_t s);

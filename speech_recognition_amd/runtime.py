@@ -98,6 +98,16 @@ class Whisper:
                                            ws, ws.numel())
         return codes, sc
 
+    def decode_prefill(self, state, tokens, logits=None):
+        """tokens [B, P]: P prompt tokens per row in one pass (equal to P decode steps)."""
+        B, n_tok = tokens.shape
+        assert B == state.batch and state.cross_codes is None
+        ws, nb = self.workspace(B * n_tok, L.WS_DECODE)
+        L.whisper_decode_prefill(self.dims, self.packed, B, n_tok, state.cap, tokens.contiguous(), state.lengths,
+                                 state.kv_cache, state.kv_scales, state.cross_kv, logits, state.argmax,
+                                 state.dev_error, ws, nb)
+        return state.argmax
+
     def decode_step(self, state, tokens, logits=None):
         B = state.batch
         ws, nb = self.workspace(B, L.WS_DECODE)

@@ -348,3 +348,68 @@ def test_decode_resume_and_capacity():
     torch.cuda.synchronize()
     assert int(s3.dev_error[0].item()) == 6
     assert int(s3.kv_cache[:, :, 7].sum().item()) == 0
+
+
+def test_decode_prefill_equals_successive_steps_and_oracle():
+    """A causal prefill of P prompt tokens per row in one pass equals P
+    successive decode steps bit for bit (cache codes, lengths, logits and
+    argmax of the last token), and so does the step after it; its logits
+    match the oracle's P teacher-forced steps on two rows."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=2)
+    B, P, cap, prefill_max = 24, 4, 96, 40
+    say(f"decode prefill: large-v3 shape 2 layers, B={B}, {P} prompt tokens, prefill U[1,{prefill_max}]")
+    m, W = model_for(dims, ln_random=True)
+    H, Lyr = dims.n_heads, dims.n_dec_layers
+    enc = gen_normal(DEV, (B, 1500, 1280), dims.cfg_id, 8, bf16=True).to(torch.bfloat16)
+    ckv = m.cross_kv(enc)
+    lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max)
+    sc = torch.full((Lyr, 2), 0.02)
+    toks = gen_tokens(DEV, dims.cfg_id, P + 1, B, dims.n_vocab)   # [P + 1, B]
+    prefill = torch.randint(0, 256, (Lyr, 2, B, H, cap, 64), dtype=torch.uint8,
+                            generator=torch.Generator().manual_seed(12)).to(DEV)
+    prefill[(prefill & 0x7F) == 0x7F] = 0
+    s1 = DecodeState(dims, B, cap, ckv, sc, lengths0)
+    s2 = DecodeState(dims, B, cap, ckv, sc, lengths0)
+    s1.kv_cache.copy_(prefill)
+    s2.kv_cache.copy_(prefill)
+    lg1 = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
+    lg2 = torch.empty_like(lg1)
+    m.decode_prefill(s1, toks[:P].t().contiguous(), lg1)
+    for t in range(P):
+        m.decode_step(s2, toks[t], lg2)
+    torch.cuda.synchronize()
+    assert int(s1.dev_error[0].item()) == 0 and int(s2.dev_error[0].item()) == 0
+    assert torch.equal(s1.lengths, lengths0.to(DEV) + P) and torch.equal(s1.lengths, s2.lengths)
+    assert torch.equal(s1.kv_cache, s2.kv_cache), "cache codes differ"
+    assert torch.equal(lg1, lg2) and torch.equal(s1.argmax, s2.argmax), "last-token logits differ"
+    m.decode_step(s1, toks[P], lg1)
+    m.decode_step(s2, toks[P], lg2)
+    torch.cuda.synchronize()
+    assert torch.equal(lg1, lg2) and torch.equal(s1.kv_cache, s2.kv_cache)
+    # oracle: P teacher-forced steps on two rows, continuing from the GPU's checked codes
+    rows = [0, B - 1]
+    Wh = host_weights(W, "decoder.")
+    cross_rows = {b: O.cross_kv(host(enc[b]), Wh, H, Lyr) for b in rows}
+    cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
+    cache_gpu = s2.kv_cache.cpu().numpy()
+    pre = prefill.cpu().numpy()
+    cache = [[{b: pre[l, kv, b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)]
+    lengths = lengths0.cpu().numpy().copy()
+    tok = toks.cpu().numpy()
+    scn = sc.numpy()
+    for t in range(P):
+        forced = [[{b: cache_gpu[l, kv, b, :, int(lengths[b]), :] for b in rows} for kv in range(2)]
+                  for l in range(Lyr)]
+        lg_ref, tr = O.decode_step(Wh, H, tok[t], lengths, cache, scn, cross, rows=rows, forced_codes=forced)
+        for b in rows:
+            for l in range(Lyr):
+                for kv in range(2):
+                    ok, _ = code_mismatch_ok(forced[l][kv][b], tr["codes"][l, kv, b], tr["pre_quant"][l, kv, b])
+                    assert ok
+        lengths = lengths + 1
+    # the prefill's logits are those of token P - 1 (s1 has moved on one step: compare s2's copy taken above)
+    m2 = DecodeState(dims, B, cap, ckv, sc, lengths0)
+    m2.kv_cache.copy_(prefill)
+    m.decode_prefill(m2, toks[:P].t().contiguous(), lg1)
+    torch.cuda.synchronize()
+    check_logits_argmax(host(lg1), m2.argmax.cpu().numpy(), lg_ref, rows, "prefill")
