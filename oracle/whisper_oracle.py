@@ -12,8 +12,8 @@ Plain NumPy in float64 (floating point) with a library primitive per step
   128-bin mel filterbank, log-mel front end on the GPU), layernorm_fused.cu
   card (residual add + LayerNorm in one pass), flash_attn_hopper.cu card
   (encoder self, decoder causal self and decoder cross attention, online
-  softmax, no score matrix in memory), fp8_quantize.cu card (E4M3 with a
-  per-tensor scale from the activation maximum).
+  softmax, no score matrix in memory), fp8_quantize.cu card (E4M3, and
+  E5M2 for range, with a per-tensor scale from the activation maximum).
 * whisper-blaze project page, "Direct Kernel API": quantise_e4m3 returns codes
   plus a per-tensor scale; dequantise_e4m3 takes codes, scale and shape;
   layernorm_fused_residual returns (normed, total).
@@ -25,7 +25,8 @@ Plain NumPy in float64 (floating point) with a library primitive per step
 
 Where the pages are silent (STFT parameters, mel scale, log floor, layer
 structure, attention scale, GELU form, fp8 rounding) the oracle takes the
-public Whisper model definition and the OCP E4M3FN format definition; each
+public Whisper model definition and the OCP E4M3FN / E5M2 format
+definitions; each
 reading is stated at the function that uses it.
 """
 import numpy as np
@@ -108,6 +109,85 @@ def e4m3_scale_from_amax(x):
     if amax == 0:
         return np.float32(1.0)
     return np.float32(amax) / np.float32(E4M3_MAX)
+
+
+# =========================================================================== fp8 e5m2
+# OCP 8-bit float E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits. It is
+# laid out like IEEE binary16 cut to its top byte: exponent 31 holds +-inf
+# (mantissa 0) and NaN (mantissa != 0); largest finite magnitude
+# 1.75 * 2^15 = 57344; subnormal step 2^-16. The pages offer it beside E4M3
+# for its wider range (whisper_blaze showcase page: fp8_quantize.cu card and
+# the aggressive_fp8 preset of the precision.py card).
+
+E5M2_MAX = 57344.0
+
+
+def e5m2_value(code):
+    """Real value of each e5m2 code (+-inf for 0x7C / 0xFC, NaN for
+    0x7D..0x7F and 0xFD..0xFF)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 0x1F
+    m = c & 0x3
+    normal = (1.0 + m / 4.0) * np.exp2(e - 15.0)
+    sub = (m / 4.0) * 2.0 ** -14
+    v = s * np.where(e == 0, sub, normal)
+    return np.where(e == 31, np.where(m == 0, s * np.inf, np.nan), v)
+
+
+# The 124 non-negative finite values, ascending; index == code (0x7B = 57344).
+_E5M2_POS = e5m2_value(np.arange(124))
+
+
+def e5m2_encode(y):
+    """Code of the e5m2 value nearest to each fp32 input.
+
+    Ties go to the code with an even mantissa (round to nearest even);
+    magnitudes above 57344, infinities included, saturate to +-57344 (the
+    saturating conversion, as the e4m3 encoder does at 448, so no finite input
+    becomes inf); NaN maps to the NaN code 0x7F with the input's sign; the sign
+    bit of the input is kept (so -0 -> 0x80)."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y.astype(np.float64))
+    neg = np.signbit(y)
+    nan = np.isnan(y)
+    a_ = np.where(nan, 0.0, a)
+    i = np.clip(np.searchsorted(_E5M2_POS, a_, side="right") - 1, 0, 123)
+    j = np.minimum(i + 1, 123)
+    lo, hi = _E5M2_POS[i], _E5M2_POS[j]
+    d_lo, d_hi = a_ - lo, hi - a_
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (j % 2 == 0) & (j != i))
+    code = np.where(up, j, i)
+    code = np.where(a_ >= E5M2_MAX, 123, code)
+    code = np.where(nan, 127, code)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def e5m2_quantize(x, scale):
+    """code = e5m2(fl32(fl32(x) * fl32(1 / scale))), as e4m3_quantize."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = np.asarray(x, dtype=np.float64).astype(np.float32) * inv
+    return e5m2_encode(y)
+
+
+def e5m2_dequantize(codes, scale):
+    """Dequantise-on-read: fl32(value(code) * scale)."""
+    v = e5m2_value(codes).astype(np.float32)
+    return (v * np.float32(scale)).astype(np.float64)
+
+
+def e5m2_scale_from_amax(x):
+    """fl32(amax) / 57344 in fp32 (1.0 for an all-zero tensor)."""
+    amax = np.float32(np.max(np.abs(np.asarray(x, dtype=np.float64)))) if np.size(x) else np.float32(0)
+    if amax == 0:
+        return np.float32(1.0)
+    return np.float32(amax) / np.float32(E5M2_MAX)
+
+
+FP8_FORMATS = {
+    "e4m3": (e4m3_quantize, e4m3_dequantize, e4m3_scale_from_amax),
+    "e5m2": (e5m2_quantize, e5m2_dequantize, e5m2_scale_from_amax),
+}
 
 
 # =========================================================================== log-mel
@@ -352,22 +432,25 @@ def cross_kv(enc, W, n_heads, n_layers):
     return out
 
 
-def cross_kv_fp8(cross, scales):
+def cross_kv_fp8(cross, scales, fmt="e4m3"):
     """fp8 cross-attention keys and values: each layer's K and V are
     quantised on write with the caller's per-(layer, K|V) scale and read back
     dequantised, so decode_step then attends over the fp8 values (whisper_blaze
     showcase page, precision.py card and its preset table: the aggressive
-    preset puts the cross-attention site in fp8; fp8_quantize.cu card: E4M3
-    codes with a per-tensor scale). Reading: E4M3 with one scale per (layer,
-    K|V) tensor, which keeps the range by scaling instead of E5M2's exponent.
+    preset puts the cross-attention site in fp8, there in E5M2 for range;
+    fp8_quantize.cu card: E4M3 and E5M2 codes with a per-tensor scale).
+    fmt picks the format, "e4m3" or "e5m2", with one scale per (layer, K|V)
+    tensor either way.
 
     cross: list over layers of (K, V), each an array [B, H, T, dh] or a dict
     b -> [H, T, dh]; scales: [L, 2]. Returns the same structure holding
-    e4m3_dequantize(e4m3_quantize(x, s), s)."""
+    dequantize(quantize(x, s), s) in the chosen format."""
+    quant, dequant, _ = FP8_FORMATS[fmt]
+
     def q(x, s):
         if isinstance(x, dict):
-            return {b: e4m3_dequantize(e4m3_quantize(v, s), s) for b, v in x.items()}
-        return e4m3_dequantize(e4m3_quantize(x, s), s)
+            return {b: dequant(quant(v, s), s) for b, v in x.items()}
+        return dequant(quant(x, s), s)
     return [(q(k, scales[layer][0]), q(v, scales[layer][1])) for layer, (k, v) in enumerate(cross)]
 
 

@@ -365,3 +365,45 @@ def test_fp8_cross_kv_grid_values_exact_and_error_bound():
     sub = inr & ~normal
     assert np.all(np.abs(y - x)[sub] <= 2.0 ** -10 * float(s) * (1 + 1e-6))
     assert np.all(np.abs(y[~inr]) == np.float64(np.float32(448.0) * s))
+
+
+def test_fp8_cross_kv_e5m2_grid_values_exact_and_error_bound():
+    """fp8 cross K/V in E5M2 (the aggressive preset's cross-attention format):
+    with power-of-two scales, values on the scaled e5m2 grid pass unchanged,
+    so a decode step over them equals the unquantised step exactly; others
+    move by at most half an e5m2 step (2^-3 of the value in the normal range,
+    2^-17 * scale below it); past 57344 * scale they saturate."""
+    W, H, L, ctx, cross, toks, scales, dh = _fp8_setup()
+    scales = np.array([[2.0 ** -12, 2.0 ** -11], [2.0 ** -13, 2.0 ** -10]], np.float32)
+    rng = np.random.default_rng(6)
+    grid = []
+    for layer, (k, v) in enumerate(cross):
+        pair = []
+        for kv, x in ((0, k), (1, v)):
+            codes = rng.integers(0, 256, x.shape).astype(np.uint8)
+            codes[(codes & 0x7F) >= 0x7C] = 0
+            pair.append(O.e5m2_value(codes).astype(np.float64) * np.float64(np.float32(scales[layer][kv])))
+        grid.append(tuple(pair))
+    q = O.cross_kv_fp8(grid, scales, fmt="e5m2")
+    for layer in range(L):
+        for kv in range(2):
+            assert np.array_equal(q[layer][kv], grid[layer][kv])
+    # the E4M3 form of the same values is not exact (E5M2's exponent range)
+    q4 = O.cross_kv_fp8(grid, scales, fmt="e4m3")
+    assert not all(np.array_equal(q4[l][kv], grid[l][kv]) for l in range(L) for kv in range(2))
+    B = toks.shape[1]
+    c1 = np.zeros((L, 2, B, H, ctx, dh), np.uint8)
+    c2 = np.zeros_like(c1)
+    lg1, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c1, scales, grid)
+    lg2, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c2, scales, q)
+    assert np.array_equal(lg1, lg2)
+    s = np.float32(0.01)
+    x = rng.standard_normal(20000) * 50.0
+    x[:8] = [600.0, -600.0, 573.44, -573.44, 1e-9, 0.0, 1e4, -1e4]
+    y = O.cross_kv_fp8([(x, x)], np.array([[s, s]], np.float32), fmt="e5m2")[0][0]
+    inr = np.abs(x) <= 57344 * float(s)
+    normal = inr & (np.abs(x) >= 2.0 ** -14 * float(s))
+    assert np.all(np.abs(y - x)[normal] <= 2.0 ** -3 * np.abs(x[normal]) * (1 + 1e-6))
+    sub = inr & ~normal
+    assert np.all(np.abs(y - x)[sub] <= 2.0 ** -17 * float(s) * (1 + 1e-6))
+    assert np.all(np.abs(y[~inr]) == np.float64(np.float32(57344.0) * s))
