@@ -59,6 +59,15 @@ typedef enum {
   WHISPER_ERR_HIP = 7          /* a HIP launch failed */
 } whisper_status;
 
+/* fp8 code formats (OCP 8-bit floats; whisper_blaze showcase page,
+ * fp8_quantize.cu card: E4M3 for precision, E5M2 for range). Encoding rounds
+ * to nearest even and saturates at the largest finite magnitude (448 or
+ * 57344; infinities too); NaN maps to a NaN code of the input's sign. */
+typedef enum {
+  WHISPER_FP8_E4M3 = 0, /* E4M3FN: bias 7, no infinities, S.1111.111 is NaN */
+  WHISPER_FP8_E5M2 = 1  /* E5M2: bias 15, binary16's top byte (inf and NaN as IEEE) */
+} whisper_fp8_format;
+
 typedef enum { WHISPER_F32 = 0, WHISPER_BF16 = 1 } whisper_dtype;
 
 /* Model shape. head_dim must be 64 and n_heads*64 == d_model; n_audio_ctx is
@@ -196,35 +205,43 @@ whisper_status whisper_decode_prefill(const whisper_dims* dims, const void* pack
                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
 /* Decoder step with fp8 cross-attention K/V (the fp8 cross-attention site of
- * the pages' precision presets; project page, "Direct Kernel API":
- * quantise_e4m3 with a per-tensor scale). As whisper_decode_step, bf16 models
- * only, except that the cross-attention keys and values are e4m3 codes:
+ * the showcase page's precision presets, whose aggressive preset takes E5M2
+ * there for range; project page, "Direct Kernel API": quantise_e4m3 with a
+ * per-tensor scale). As whisper_decode_step, bf16 models only, except that
+ * the cross-attention keys and values are fp8 codes:
  * cross_codes:  [n_dec_layers][2][batch][n_heads][n_audio_ctx][64] uint8, the
  *               bf16 whisper_cross_kv output of each (layer, K|V) slab
- *               quantised with whisper_fp8_quantize (code = e4m3_rne_saturate(
- *               fl32(x * fl32(1/scale)))), caller-owned;
- * cross_scales: [n_dec_layers][2] fp32 device scales, K then V.
- * The cross-attention reads half the bytes of the bf16 form and dequantises
- * on read: score = (q . value(codes_k)) * scale_k / 8, output =
- * sum p * value(codes_v) * scale_v. */
+ *               quantised with whisper_fp8_quantize in cross_format
+ *               (code = fp8_rne_saturate(fl32(x * fl32(1/scale)))),
+ *               caller-owned;
+ * cross_scales: [n_dec_layers][2] fp32 device scales, K then V;
+ * cross_format: WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2 (else INVALID_ARG).
+ * The KV cache stays E4M3 either way. The cross-attention reads half the
+ * bytes of the bf16 form and dequantises on read: score =
+ * (q . value(codes_k)) * scale_k / 8, output = sum p * value(codes_v) * scale_v. */
 whisper_status whisper_decode_step_xq(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                       const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,
-                                      float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
-                                      void* stream);
+                                      whisper_fp8_format cross_format, float* logits, int32_t* argmax,
+                                      int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ kernel-level calls
- * fp8 E4M3 codec with a per-tensor scale (project page quantise_e4m3 /
- * dequantise_e4m3). x: n values of dtype `dt`. With scale_in == NULL the scale
- * is computed on the device as fl32(amax)/448 (1.0 if amax is 0) and written
- * to scale_out; this needs a workspace of whisper_fp8_workspace_size() bytes.
- * codes[i] = e4m3_rne_saturate(fl32(x[i] * fl32(1/scale))). */
+ * fp8 codec with a per-tensor scale (project page quantise_e4m3 /
+ * dequantise_e4m3; showcase page fp8_quantize.cu card: E4M3 and E5M2).
+ * x: n values of dtype `dt`; fmt: WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2 (else
+ * INVALID_ARG). With scale_in == NULL the scale is computed on the device as
+ * fl32(amax) / fmax (fmax = 448 for E4M3, 57344 for E5M2; 1.0 if amax is 0)
+ * and written to scale_out; this needs a workspace of
+ * whisper_fp8_workspace_size() bytes.
+ * codes[i] = fp8_rne_saturate(fl32(x[i] * fl32(1/scale))). */
 size_t whisper_fp8_workspace_size(void);
-whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, const float* scale_in,
-                                    uint8_t* codes, float* scale_out, void* ws, size_t ws_bytes, void* stream);
-/* y[i] = fl32(value(codes[i]) * scale[0]), stored in dtype dt. */
-whisper_status whisper_fp8_dequantize(const uint8_t* codes, size_t n, const float* scale, void* y,
-                                      whisper_dtype dt, void* stream);
+whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, whisper_fp8_format fmt, size_t n,
+                                    const float* scale_in, uint8_t* codes, float* scale_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+/* y[i] = fl32(value(codes[i]) * scale[0]) in format fmt, stored in dtype dt
+ * (E5M2 infinity codes give +-inf, NaN codes NaN). */
+whisper_status whisper_fp8_dequantize(const uint8_t* codes, whisper_fp8_format fmt, size_t n, const float* scale,
+                                      void* y, whisper_dtype dt, void* stream);
 
 /* Fused residual + LayerNorm (showcase page, layernorm_fused.cu card; project
  * page layernorm_fused_residual): total = fl32(h + residual) (h alone if

@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwhisper_mi355x.so")
 
 WHISPER_F32, WHISPER_BF16 = 0, 1
+WHISPER_FP8_E4M3, WHISPER_FP8_E5M2 = 0, 1
 WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE = 0, 1, 2, 3
 
 EXPORTS = [
@@ -65,11 +66,11 @@ _SIG = {
     "whisper_encode_layers": (I, [P, P, P, I, I, I, I, P, P, Z, P]),
     "whisper_cross_kv": (I, [P, P, P, I, P, P, Z, P]),
     "whisper_decode_step": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
-    "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, I, P, P, P, P, Z, P]),
     "whisper_decode_prefill": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_fp8_workspace_size": (Z, []),
-    "whisper_fp8_quantize": (I, [P, I, Z, P, P, P, P, Z, P]),
-    "whisper_fp8_dequantize": (I, [P, Z, P, P, I, P]),
+    "whisper_fp8_quantize": (I, [P, I, I, Z, P, P, P, P, Z, P]),
+    "whisper_fp8_dequantize": (I, [P, I, Z, P, P, I, P]),
     "whisper_layernorm_fused": (I, [P, P, P, P, P, F, I, P, P, P]),
     "whisper_linear": (I, [I, P, I, P, P, I, I, I, I, P, I, P]),
     "whisper_attention_encoder": (I, [I, P, I, I, I, P, P]),
@@ -212,22 +213,24 @@ def whisper_decode_prefill(dims, packed, batch, n_tokens, kv_cap, tokens, length
 
 
 def whisper_decode_step_xq(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_codes,
-                           cross_scales, logits, argmax, dev_error, ws, ws_bytes, stream=None):
+                           cross_scales, logits, argmax, dev_error, ws, ws_bytes, stream=None,
+                           cross_format=WHISPER_FP8_E4M3):
     dd, dp = _dims_ptr(dims)
     _check(lib().whisper_decode_step_xq(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
-                                        _p(kv_scales), _p(cross_codes), _p(cross_scales), _p(logits), _p(argmax),
-                                        _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
+                                        _p(kv_scales), _p(cross_codes), _p(cross_scales), cross_format,
+                                        _p(logits), _p(argmax), _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
 
 
-def whisper_fp8_quantize(x, dt, n, scale_in, codes, scale_out, ws=None, ws_bytes=0, stream=None):
+def whisper_fp8_quantize(x, dt, n, scale_in, codes, scale_out, ws=None, ws_bytes=0, stream=None,
+                         fmt=WHISPER_FP8_E4M3):
     _dtype_check("whisper_fp8_quantize x", x, dt)
-    _check(lib().whisper_fp8_quantize(_p(x), dt, n, _p(scale_in), _p(codes), _p(scale_out), _p(ws), ws_bytes,
+    _check(lib().whisper_fp8_quantize(_p(x), dt, fmt, n, _p(scale_in), _p(codes), _p(scale_out), _p(ws), ws_bytes,
                                       _stream(stream)))
 
 
-def whisper_fp8_dequantize(codes, n, scale, y, dt, stream=None):
+def whisper_fp8_dequantize(codes, n, scale, y, dt, stream=None, fmt=WHISPER_FP8_E4M3):
     _dtype_check("whisper_fp8_dequantize y", y, dt)
-    _check(lib().whisper_fp8_dequantize(_p(codes), n, _p(scale), _p(y), dt, _stream(stream)))
+    _check(lib().whisper_fp8_dequantize(_p(codes), fmt, n, _p(scale), _p(y), dt, _stream(stream)))
 
 
 def whisper_layernorm_fused(dims, h, residual, gamma, beta, eps, M, normed, total, stream=None):

@@ -10,6 +10,9 @@
 #include "internal.hpp"
 #include "whisper_mi355x.h"
 
+static_assert((int)WHISPER_FP8_E4M3 == (int)wh::FP8_E4M3 && (int)WHISPER_FP8_E5M2 == (int)wh::FP8_E5M2,
+              "public fp8 format values must match the kernels' template values");
+
 using namespace wh;
 
 namespace {
@@ -303,7 +306,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
                                  int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
                                  int32_t* dev_error, void* ws, hipStream_t s, const uint8_t* xcodes = nullptr,
-                                 const float* xscales = nullptr, int R = 1) {
+                                 const float* xscales = nullptr, int R = 1, int xfmt = FP8_E4M3) {
   // B batch rows of the cache; R tokens per row (a prefill when R > 1): the
   // activations have B * R rows, row m being token m % R of batch row m / R
   const int Bc = B;
@@ -352,10 +355,10 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));
     {
       ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
-      if (xcodes) {  // e4m3 cross K/V: the fp8 attention kernel over all T keys of each row
+      if (xcodes) {  // fp8 cross K/V: the fp8 attention kernel over all T keys of each row
         const uint8_t* xc = xcodes + l * (ckv_layer / 2);
         WH_TRY(launch_attn_decode_self(ACT_BF16, QC, D, xc, xc + ckv_layer / 4, xscales + 2 * l, nullptr, 0, B, H, T,
-                                       ATT, s, R));
+                                       ATT, s, R, xfmt));
       } else {
         const char* ck = (const char*)cross_kv + l * ckv_layer;
         WH_TRY(launch_attn_decode_cross(ACT_BF16, QC, ck, ck + ckv_layer / 2, B, H, T, ATT, s, R));
@@ -728,9 +731,11 @@ whisper_status whisper_decode_prefill(const whisper_dims* d, const void* packed,
 whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed, int B, int cap,
                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                       const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,
-                                      float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
-                                      void* stream) {
+                                      whisper_fp8_format cross_format, float* logits, int32_t* argmax,
+                                      int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
   WH_CHECK(check_dims(d));
+  if (cross_format != WHISPER_FP8_E4M3 && cross_format != WHISPER_FP8_E5M2)
+    return fail(WHISPER_ERR_INVALID_ARG, "decode_step_xq: cross_format must be WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2");
   if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "decode_step_xq: bf16 models only");
   if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_step_xq: batch must be > 0");
   if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_step_xq: no decoder layers");
@@ -746,7 +751,7 @@ whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed,
   const Packed P = layout(d);
   float* LG = logits ? logits : at<float>(ws, W.logits);
   return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, nullptr, LG, argmax,
-                           dev_error, ws, S(stream), cross_codes, cross_scales);
+                           dev_error, ws, S(stream), cross_codes, cross_scales, 1, (int)cross_format);
 }
 
 whisper_status whisper_peak_mfma(int n_wg, int iters, float* out, void* stream) {
@@ -770,9 +775,12 @@ whisper_status whisper_peak_read(const void* buf, size_t bytes, int n_wg, float*
 
 size_t whisper_fp8_workspace_size(void) { return 1024 * sizeof(float); }
 
-whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, const float* scale_in, uint8_t* codes,
-                                    float* scale_out, void* ws, size_t ws_bytes, void* stream) {
+whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, whisper_fp8_format fmt, size_t n,
+                                    const float* scale_in, uint8_t* codes, float* scale_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
   if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "fp8_quantize: dtype must be F32 or BF16");
+  if (fmt != WHISPER_FP8_E4M3 && fmt != WHISPER_FP8_E5M2)
+    return fail(WHISPER_ERR_INVALID_ARG, "fp8_quantize: fmt must be WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2");
   if (n == 0) return fail(WHISPER_ERR_INVALID_ARG, "fp8_quantize: n must be > 0");
   WH_CHECK(check_ptrs({x, codes}, "fp8_quantize"));
   if (!scale_in && !scale_out) return fail(WHISPER_ERR_INVALID_ARG, "fp8_quantize: need scale_in or scale_out");
@@ -785,23 +793,25 @@ whisper_status whisper_fp8_quantize(const void* x, whisper_dtype dt, size_t n, c
   if (!scale_in) {
     size_t blocks = (n + 255) / 256;
     const int np = (int)(blocks > 1024 ? 1024 : blocks);
-    WH_TRY(launch_amax(act_of(dt), x, n, (float*)ws, np, scale_out, s));
+    WH_TRY(launch_amax(act_of(dt), (int)fmt, x, n, (float*)ws, np, scale_out, s));
     sc = scale_out;
   } else if (scale_out) {
     WH_TRY(launch_copy_f32(scale_in, scale_out, 1, s));
   }
-  WH_TRY(launch_fp8_quantize(act_of(dt), x, n, sc, codes, s));
+  WH_TRY(launch_fp8_quantize(act_of(dt), (int)fmt, x, n, sc, codes, s));
   return WHISPER_OK;
 }
 
-whisper_status whisper_fp8_dequantize(const uint8_t* codes, size_t n, const float* scale, void* y, whisper_dtype dt,
-                                      void* stream) {
+whisper_status whisper_fp8_dequantize(const uint8_t* codes, whisper_fp8_format fmt, size_t n, const float* scale,
+                                      void* y, whisper_dtype dt, void* stream) {
   if (dt != WHISPER_F32 && dt != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "fp8_dequantize: dtype must be F32 or BF16");
+  if (fmt != WHISPER_FP8_E4M3 && fmt != WHISPER_FP8_E5M2)
+    return fail(WHISPER_ERR_INVALID_ARG, "fp8_dequantize: fmt must be WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2");
   if (n == 0) return fail(WHISPER_ERR_INVALID_ARG, "fp8_dequantize: n must be > 0");
   WH_CHECK(check_ptrs({codes, y}, "fp8_dequantize"));
   WH_CHECK(check_ptrs4({scale}, "fp8_dequantize"));
   (void)hipGetLastError();
-  WH_TRY(launch_fp8_dequantize(act_of(dt), codes, n, scale, y, S(stream)));
+  WH_TRY(launch_fp8_dequantize(act_of(dt), (int)fmt, codes, n, scale, y, S(stream)));
   return WHISPER_OK;
 }
 

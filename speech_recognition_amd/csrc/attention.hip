@@ -14,7 +14,9 @@
 // Decoder self-attention reads the caller's e4m3 KV cache and dequantises on
 // read (the Inference Endpoints post, "Inference Stack": K/V stored as float8,
 // compute in bfloat16). Decoder cross-attention streams head-major bf16 K/V
-// in one pass per (row, head).
+// in one pass per (row, head); its fp8 form (E4M3 or E5M2 codes with
+// per-tensor scales, the showcase page's precision presets) runs through the
+// fp8 decode kernel over all frames.
 #include <type_traits>
 
 #include "common.hpp"
@@ -256,10 +258,11 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ decoder self-attention over e4m3 codes
+// ------------------------------------------------------------------ decoder attention over fp8 codes
 // Keys 0..n-1 (n = lengths[b] + len_add, or all cap keys when lengths is
 // NULL, as for the fp8 cross-attention K/V) are 64-byte code rows read as 4
-// lanes x 16 codes.
+// lanes x 16 codes, in E4M3 (the KV cache) or E5M2 (an option for the
+// cross-attention K/V, for range), decoded by the gfx950 converters.
 constexpr int DEC_MAX_CAP = 4096;
 
 // Sums over 4 or 8 consecutive lanes with DPP lane permutes folded into the
@@ -280,13 +283,14 @@ __device__ __forceinline__ float sum8_lanes(float d) {
 }
 constexpr float LOG2E = 1.4426950408889634f;
 
-__device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
+template <int FMT>
+__device__ __forceinline__ float dot16_fp8(const uint4 c, const float* q) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float v[4];
-    e4m3x4_decode(w[i], v);
+    fp8x4_decode<FMT>(w[i], v);
 #pragma unroll
     for (int k = 0; k < 4; ++k) acc = fmaf(q[4 * i + k], v[k], acc);
   }
@@ -302,7 +306,7 @@ __device__ __forceinline__ float dot16_e4m3(const uint4 c, const float* q) {
 // the 64 key groups through LDS. q goes straight from global to registers.
 constexpr int SELF_KB = 8;
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restrict__ q, long q_stride,
                                                                const uint8_t* __restrict__ kc,
                                                                const uint8_t* __restrict__ vc,
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
     for (int i = 0; i < SELF_KB; ++i) {
       sj[i] = -INFINITY;
       if (base + 64 * i + 16 * wave < n) {
-        const float d = sum4_lanes(dot16_e4m3(ck[i], qreg));
+        const float d = sum4_lanes(dot16_fp8<FMT>(ck[i], qreg));
         if (base + kg + 64 * i < n) sj[i] = d * sscale;
       }
       bm = fmaxf(bm, sj[i]);
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         float v[4];
-        e4m3x4_decode(w[e4], v);
+        fp8x4_decode<FMT>(w[e4], v);
 #pragma unroll
         for (int k = 0; k < 4; ++k) acc[4 * e4 + k] = fmaf(p, v[k], acc[4 * e4 + k]);
       }
@@ -401,17 +405,29 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
   }
 }
 
-hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
-                                   const uint8_t* v_codes, const float* scales, const int32_t* lengths, int len_add,
-                                   int B, int H, int cap, void* out, hipStream_t s, int rows_per_b) {
-  if (cap > DEC_MAX_CAP || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
+template <int FMT>
+static void decode_self_fmt(ActType t, const void* q, long q_stride, const uint8_t* k_codes, const uint8_t* v_codes,
+                            const float* scales, const int32_t* lengths, int len_add, int B, int H, int cap,
+                            void* out, hipStream_t s, int rows_per_b) {
   dim3 grid(H, B);
   if (t == ACT_BF16)
-    hipLaunchKernelGGL(attn_decode_self_kernel<u16>, grid, dim3(256), 0, s, (const u16*)q, q_stride, k_codes,
+    hipLaunchKernelGGL((attn_decode_self_kernel<u16, FMT>), grid, dim3(256), 0, s, (const u16*)q, q_stride, k_codes,
                        v_codes, scales, lengths, len_add, H, cap, (u16*)out, rows_per_b);
   else
-    hipLaunchKernelGGL(attn_decode_self_kernel<float>, grid, dim3(256), 0, s, (const float*)q, q_stride, k_codes,
-                       v_codes, scales, lengths, len_add, H, cap, (float*)out, rows_per_b);
+    hipLaunchKernelGGL((attn_decode_self_kernel<float, FMT>), grid, dim3(256), 0, s, (const float*)q, q_stride,
+                       k_codes, v_codes, scales, lengths, len_add, H, cap, (float*)out, rows_per_b);
+}
+
+hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
+                                   const uint8_t* v_codes, const float* scales, const int32_t* lengths, int len_add,
+                                   int B, int H, int cap, void* out, hipStream_t s, int rows_per_b, int fmt) {
+  if (cap > DEC_MAX_CAP || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
+  if (fmt == FP8_E5M2)
+    decode_self_fmt<FP8_E5M2>(t, q, q_stride, k_codes, v_codes, scales, lengths, len_add, B, H, cap, out, s,
+                              rows_per_b);
+  else
+    decode_self_fmt<FP8_E4M3>(t, q, q_stride, k_codes, v_codes, scales, lengths, len_add, B, H, cap, out, s,
+                              rows_per_b);
   return hipGetLastError();
 }
 

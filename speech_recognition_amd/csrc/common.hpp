@@ -1,9 +1,11 @@
 // Device helpers shared by the gfx950 kernels of the Whisper hot path:
-// bf16 / OCP-e4m3 conversions done on bits, MFMA operand vector types and
-// wave64 reductions.
+// bf16 / OCP fp8 (E4M3, E5M2) conversions done on bits, MFMA operand vector
+// types and wave64 reductions.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "internal.hpp"
 
 namespace wh {
 
@@ -83,6 +85,46 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   if ((c & 0x7fu) == 0x7fu) v = __uint_as_float(0x7fc00000u);
   return (c & 0x80u) ? -v : v;
 }
+
+// ------------------------------------------------------------------ OCP E5M2
+// 1 sign, 5 exponent bits (bias 15), 2 mantissa bits: IEEE binary16's top
+// byte, with +-inf (S.11111.00) and NaN (S.11111.xx, xx != 0); largest finite
+// magnitude 57344. Encoding rounds to nearest even and saturates magnitudes
+// >= 57344, infinities included, to +-57344; the sign bit is always kept.
+__device__ __forceinline__ uint32_t e5m2_encode(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+  if (a >= 0x47600000u) return sign | 0x7bu;         // |y| >= 57344: saturate
+  if (a < 0x38800000u) {                             // |y| < 2^-14: subnormal, step 2^-16
+    const float s = __uint_as_float(a) * 65536.0f;   // exact scaling by a power of two
+    return sign | (uint32_t)__builtin_rintf(s);      // 0..4 (4 is the smallest normal)
+  }
+  const uint32_t r = a + 0xfffffu + ((a >> 21) & 1u);  // round 23 -> 2 mantissa bits, ties to even
+  uint32_t code = (((r >> 23) - 112u) << 2) | ((r >> 21) & 3u);
+  return sign | (code > 0x7bu ? 0x7bu : code);
+}
+
+// Four E5M2 codes packed in a word -> fp32 with the gfx950 converter.
+__device__ __forceinline__ void e5m2x4_decode(uint32_t w, float o[4]) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+}
+
+// The two fp8 formats as one template parameter (Fp8Fmt, internal.hpp).
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode(float y) {
+  return FMT == FP8_E5M2 ? e5m2_encode(y) : e4m3_encode(y);
+}
+template <int FMT>
+__device__ __forceinline__ void fp8x4_decode(uint32_t w, float o[4]) {
+  if (FMT == FP8_E5M2) e5m2x4_decode(w, o);
+  else e4m3x4_decode(w, o);
+}
+template <int FMT>
+constexpr float fp8_max() { return FMT == FP8_E5M2 ? 57344.0f : 448.0f; }
 
 // ------------------------------------------------------------------ decoder residual tiles
 // The fused decode step keeps its fp32 residual stream x [M, d] (M padded to

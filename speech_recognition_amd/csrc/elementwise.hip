@@ -1,9 +1,9 @@
 // Memory-bound kernels of the hot path: fused residual + LayerNorm (the
 // whisper_blaze showcase page's layernorm_fused.cu card: residual add and
 // LayerNorm in one pass; the project page's "Direct Kernel API" returns both
-// the normalised value and the pre-norm sum), the e4m3 codec with a
-// per-tensor scale (fp8_quantize.cu card; project page quantise_e4m3 /
-// dequantise_e4m3), weight packing, decoder embeddings and the greedy argmax.
+// the normalised value and the pre-norm sum), the fp8 codec (E4M3, and E5M2
+// for range) with a per-tensor scale (fp8_quantize.cu card; project page
+// quantise_e4m3 / dequantise_e4m3), weight packing, decoder embeddings and the greedy argmax.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -102,7 +102,7 @@ hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* r
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ e4m3 codec
+// ------------------------------------------------------------------ fp8 codec (E4M3, E5M2)
 // 8 consecutive elements (16-byte aligned group) as fp32
 __device__ __forceinline__ void load8(const u16* p, float v[8]) {
   const uint4 w = *(const uint4*)p;
@@ -139,24 +139,26 @@ __global__ __launch_bounds__(256) void amax_partial(const T* x, size_t n, float*
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
 }
 
-__global__ __launch_bounds__(64) void amax_final(const float* partial, int n, float* scale_out) {
+// scale = fl32(amax) / (largest finite magnitude of the format), 1 for amax 0
+__global__ __launch_bounds__(64) void amax_final(const float* partial, int n, float fmax, float* scale_out) {
   float m = 0.f;
   for (int i = threadIdx.x; i < n; i += 64) m = fmaxf(m, partial[i]);
   m = wave_max(m);
-  if (threadIdx.x == 0) scale_out[0] = (m > 0.f) ? m / 448.0f : 1.0f;
+  if (threadIdx.x == 0) scale_out[0] = (m > 0.f) ? m / fmax : 1.0f;
 }
 
-hipError_t launch_amax(ActType t, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
+hipError_t launch_amax(ActType t, int fmt, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
                        hipStream_t s) {
   if (t == ACT_BF16)
     hipLaunchKernelGGL(amax_partial<u16>, dim3(n_partial), dim3(256), 0, s, (const u16*)x, n, partial);
   else
     hipLaunchKernelGGL(amax_partial<float>, dim3(n_partial), dim3(256), 0, s, (const float*)x, n, partial);
-  hipLaunchKernelGGL(amax_final, dim3(1), dim3(64), 0, s, partial, n_partial, scale_out);
+  const float fmax = fmt == FP8_E5M2 ? fp8_max<FP8_E5M2>() : fp8_max<FP8_E4M3>();
+  hipLaunchKernelGGL(amax_final, dim3(1), dim3(64), 0, s, partial, n_partial, fmax, scale_out);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* x, size_t n, const float* scale, uint8_t* codes) {
   const float inv = 1.0f / scale[0];
   // 8 elements per lane per iteration (x 16-byte and codes 8-byte aligned per
@@ -167,20 +169,20 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(const T* x, size_t n,
     load8(x + i * 8, v);
     uint32_t c[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(v[k] * inv);
+    for (int k = 0; k < 8; ++k) c[k] = fp8_encode<FMT>(v[k] * inv);
     *(uint2*)(codes + i * 8) = uint2{c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)};
   }
   for (size_t i = n8 * 8 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
-    codes[i] = (uint8_t)e4m3_encode(Act<T>::cvt(x[i]) * inv);
+    codes[i] = (uint8_t)fp8_encode<FMT>(Act<T>::cvt(x[i]) * inv);
 }
 
-template <typename T>
+template <typename T, int FMT>
 __global__ __launch_bounds__(256) void fp8_dequantize_kernel(const uint8_t* codes, size_t n, const float* scale, T* y) {
   const float s = scale[0];
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     float v[4];
-    e4m3x4_decode(codes[i], v);
+    fp8x4_decode<FMT>(codes[i], v);
     y[i] = Act<T>::st(v[0] * s);
   }
 }
@@ -190,24 +192,39 @@ static int grid_for(size_t n) {
   return (int)(g > 8192 ? 8192 : (g < 1 ? 1 : g));
 }
 
-hipError_t launch_fp8_quantize(ActType t, const void* x, size_t n, const float* scale, uint8_t* codes,
+template <int FMT>
+static void quantize_fmt(ActType t, const void* x, size_t n, const float* scale, uint8_t* codes, hipStream_t s) {
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL((fp8_quantize_kernel<u16, FMT>), dim3(grid_for(n)), dim3(256), 0, s, (const u16*)x, n, scale,
+                       codes);
+  else
+    hipLaunchKernelGGL((fp8_quantize_kernel<float, FMT>), dim3(grid_for(n)), dim3(256), 0, s, (const float*)x, n,
+                       scale, codes);
+}
+
+hipError_t launch_fp8_quantize(ActType t, int fmt, const void* x, size_t n, const float* scale, uint8_t* codes,
                                hipStream_t s) {
   if (!n) return hipSuccess;
-  if (t == ACT_BF16)
-    hipLaunchKernelGGL(fp8_quantize_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, (const u16*)x, n, scale, codes);
-  else
-    hipLaunchKernelGGL(fp8_quantize_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, (const float*)x, n, scale,
-                       codes);
+  if (fmt == FP8_E5M2) quantize_fmt<FP8_E5M2>(t, x, n, scale, codes, s);
+  else quantize_fmt<FP8_E4M3>(t, x, n, scale, codes, s);
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_dequantize(ActType t, const uint8_t* codes, size_t n, const float* scale, void* y,
+template <int FMT>
+static void dequantize_fmt(ActType t, const uint8_t* codes, size_t n, const float* scale, void* y, hipStream_t s) {
+  if (t == ACT_BF16)
+    hipLaunchKernelGGL((fp8_dequantize_kernel<u16, FMT>), dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale,
+                       (u16*)y);
+  else
+    hipLaunchKernelGGL((fp8_dequantize_kernel<float, FMT>), dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale,
+                       (float*)y);
+}
+
+hipError_t launch_fp8_dequantize(ActType t, int fmt, const uint8_t* codes, size_t n, const float* scale, void* y,
                                  hipStream_t s) {
   if (!n) return hipSuccess;
-  if (t == ACT_BF16)
-    hipLaunchKernelGGL(fp8_dequantize_kernel<u16>, dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale, (u16*)y);
-  else
-    hipLaunchKernelGGL(fp8_dequantize_kernel<float>, dim3(grid_for(n)), dim3(256), 0, s, codes, n, scale, (float*)y);
+  if (fmt == FP8_E5M2) dequantize_fmt<FP8_E5M2>(t, codes, n, scale, y, s);
+  else dequantize_fmt<FP8_E4M3>(t, codes, n, scale, y, s);
   return hipGetLastError();
 }
 

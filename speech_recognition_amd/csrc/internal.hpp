@@ -9,6 +9,8 @@
 namespace wh {
 
 enum ActType { ACT_F32 = 0, ACT_BF16 = 1 };
+// fp8 code formats (values match the public whisper_fp8_format enum)
+enum Fp8Fmt { FP8_E4M3 = 0, FP8_E5M2 = 1 };
 typedef uint16_t u16_t;
 
 // ------------------------------------------------------------------ GEMM
@@ -82,11 +84,13 @@ hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* r
                             float eps, int M, int d, void* normed, float* total, hipStream_t s);
 
 // ------------------------------------------------------------------ fp8 codec
-hipError_t launch_amax(ActType t, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
+// fmt: FP8_E4M3 or FP8_E5M2 (common.hpp); the amax scale divides by that
+// format's largest finite magnitude (448 or 57344).
+hipError_t launch_amax(ActType t, int fmt, const void* x, size_t n, float* partial, int n_partial, float* scale_out,
                        hipStream_t s);
-hipError_t launch_fp8_quantize(ActType t, const void* x, size_t n, const float* scale, uint8_t* codes,
+hipError_t launch_fp8_quantize(ActType t, int fmt, const void* x, size_t n, const float* scale, uint8_t* codes,
                                hipStream_t s);
-hipError_t launch_fp8_dequantize(ActType t, const uint8_t* codes, size_t n, const float* scale, void* y,
+hipError_t launch_fp8_dequantize(ActType t, int fmt, const uint8_t* codes, size_t n, const float* scale, void* y,
                                  hipStream_t s);
 
 // ------------------------------------------------------------------ attention
@@ -95,9 +99,12 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 // Decode causal self-attention over e4m3 codes [B][H][cap][64]; n_keys[b] = lengths[b] + add.
 // rows_per_b (R): query row m reads cache batch row m / R and attends over
 // n = lengths[m / R] + len_add + m % R keys (B = query rows)
+// fmt: code format of k_codes / v_codes (FP8_E4M3 for the KV cache; either
+// format for fp8 cross-attention K/V).
 hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths,
-                                   int len_add, int B, int H, int cap, void* out, hipStream_t s, int rows_per_b = 1);
+                                   int len_add, int B, int H, int cap, void* out, hipStream_t s, int rows_per_b = 1,
+                                   int fmt = 0);
 // Decode cross-attention over head-major K/V [B / R][H][T][64] (query row m
 // reads K/V batch row m / R, R = rows_per_b); one pass per (row, head).
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,

@@ -77,9 +77,10 @@ class Whisper:
         L.whisper_cross_kv(d, self.packed, enc, B, ckv)
         return ckv
 
-    def quantize_cross_kv(self, ckv, scales=None, codes=None):
-        """e4m3 codes of bf16 cross K/V [L, 2, B, H, T, 64], one scale per (layer,
-        K|V) slab: the given scales [L, 2], or amax / 448 of each slab when None.
+    def quantize_cross_kv(self, ckv, scales=None, codes=None, fmt=L.WHISPER_FP8_E4M3):
+        """fp8 codes (fmt: WHISPER_FP8_E4M3 or WHISPER_FP8_E5M2) of bf16 cross K/V
+        [L, 2, B, H, T, 64], one scale per (layer, K|V) slab: the given scales
+        [L, 2], or amax / (448 or 57344) of each slab when None.
         Returns (codes uint8 of the same shape, scales fp32 [L, 2] on the device)."""
         n_l = ckv.shape[0]
         codes = codes if codes is not None else torch.empty(ckv.shape, dtype=torch.uint8, device=ckv.device)
@@ -92,10 +93,11 @@ class Whisper:
         for l in range(n_l):
             for kv in range(2):
                 if scales is not None:
-                    L.whisper_fp8_quantize(ckv[l, kv], L.WHISPER_BF16, n, sc[l, kv:kv + 1], codes[l, kv], None)
+                    L.whisper_fp8_quantize(ckv[l, kv], L.WHISPER_BF16, n, sc[l, kv:kv + 1], codes[l, kv], None,
+                                           fmt=fmt)
                 else:
                     L.whisper_fp8_quantize(ckv[l, kv], L.WHISPER_BF16, n, None, codes[l, kv], sc[l, kv:kv + 1],
-                                           ws, ws.numel())
+                                           ws, ws.numel(), fmt=fmt)
         return codes, sc
 
     def decode_prefill(self, state, tokens, logits=None):
@@ -114,7 +116,7 @@ class Whisper:
         if state.cross_codes is not None:
             L.whisper_decode_step_xq(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
                                      state.kv_scales, state.cross_codes, state.cross_scales, logits, state.argmax,
-                                     state.dev_error, ws, nb)
+                                     state.dev_error, ws, nb, cross_format=state.cross_format)
         else:
             L.whisper_decode_step(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
                                   state.kv_scales, state.cross_kv, logits, state.argmax, state.dev_error, ws, nb)
@@ -123,10 +125,11 @@ class Whisper:
 
 class DecodeState:
     """Caller-owned decode state: fp8 self-KV cache, scales, lengths, cross K/V
-    (bf16, or e4m3 codes with per-(layer, K|V) scales from quantize_cross_kv)."""
+    (bf16, or fp8 codes in cross_format with per-(layer, K|V) scales from
+    quantize_cross_kv)."""
 
     def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda", cross_codes=None,
-                 cross_scales=None):
+                 cross_scales=None, cross_format=L.WHISPER_FP8_E4M3):
         self.batch, self.cap = batch, cap
         self.kv_cache = torch.zeros(dims.n_dec_layers, 2, batch, dims.n_heads, cap, 64, dtype=torch.uint8,
                                     device=device)
@@ -134,5 +137,6 @@ class DecodeState:
         self.lengths = lengths.to(device=device, dtype=torch.int32).contiguous().clone()
         self.cross_kv = cross_kv
         self.cross_codes, self.cross_scales = cross_codes, cross_scales
+        self.cross_format = cross_format
         self.argmax = torch.zeros(batch, dtype=torch.int32, device=device)
         self.dev_error = torch.zeros(4, dtype=torch.int32, device=device)

@@ -93,6 +93,17 @@ def test_kernel_call_validation():
     with pytest.raises(L.WhisperError) as e:
         L.whisper_fp8_quantize(16, L.WHISPER_BF16, 10, None, 16, 16, 16, 100, stream=0)
     assert e.value.status == 5
+    with pytest.raises(L.WhisperError) as e:  # unknown fp8 format
+        L.whisper_fp8_quantize(16, L.WHISPER_BF16, 10, 16, 16, None, stream=0, fmt=2)
+    assert e.value.status == 1
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_fp8_dequantize(16, 10, 16, 16, L.WHISPER_F32, stream=0, fmt=-1)
+    assert e.value.status == 1
+    d = CONFIGS["v3_decode"]
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_decode_step_xq(d, 16, 64, 672, 16, 16, 16, 16, 16, 16, None, 16, None, 16, 1 << 40, stream=0,
+                                 cross_format=7)
+    assert e.value.status == 1
     with pytest.raises(L.WhisperError) as e:
         L.whisper_attention_decode_self(L.WHISPER_BF16, 16, 4, 20, 5000, 16, 16, 16, 16, 16, stream=0)
     assert e.value.status == 2

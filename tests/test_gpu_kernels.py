@@ -18,47 +18,60 @@ def _gpu():
 
 
 # ------------------------------------------------------------------ fp8 codec
-def test_fp8_quantize_all_bf16_patterns_bit_exact():
-    say("fp8 quantize: all 65536 bf16 bit patterns, scale 1")
+FMTS = {"e4m3": L.WHISPER_FP8_E4M3, "e5m2": L.WHISPER_FP8_E5M2}
+
+
+@pytest.mark.parametrize("fmt", list(FMTS))
+def test_fp8_quantize_all_bf16_patterns_bit_exact(fmt):
+    say(f"fp8 quantize {fmt}: all 65536 bf16 bit patterns, scale 1")
+    quant = O.FP8_FORMATS[fmt][0]
     bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
     x = bits.view(torch.bfloat16).to(DEV)
     scale = torch.ones(4, dtype=torch.float32, device=DEV)
     codes = torch.empty(65536, dtype=torch.uint8, device=DEV)
-    L.whisper_fp8_quantize(x, L.WHISPER_BF16, 65536, scale, codes, None)
+    L.whisper_fp8_quantize(x, L.WHISPER_BF16, 65536, scale, codes, None, fmt=FMTS[fmt])
     torch.cuda.synchronize()
-    ref = O.e4m3_quantize(x.float().cpu().numpy(), 1.0)
+    ref = quant(x.float().cpu().numpy(), 1.0)
     assert np.array_equal(codes.cpu().numpy(), ref)
 
 
-def test_fp8_quantize_fp32_scaled_bit_exact_and_amax_scale():
-    say("fp8 quantize: 1M fp32 values, device amax scale")
+@pytest.mark.parametrize("fmt", list(FMTS))
+def test_fp8_quantize_fp32_scaled_bit_exact_and_amax_scale(fmt):
+    say(f"fp8 quantize {fmt}: 1M fp32 values, device amax scale")
+    quant, _, amax_scale = O.FP8_FORMATS[fmt]
     g = torch.Generator().manual_seed(3)
     x = (torch.randn(1 << 20, generator=g) * 3.7).to(DEV)
     codes = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
     scale = torch.zeros(4, dtype=torch.float32, device=DEV)
     ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=DEV)
-    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), None, codes, scale, ws, ws.numel())
+    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), None, codes, scale, ws, ws.numel(), fmt=FMTS[fmt])
     torch.cuda.synchronize()
     xs = x.cpu().numpy()
-    s_ref = O.e4m3_scale_from_amax(xs)
+    s_ref = amax_scale(xs)
     assert scale[0].item() == float(s_ref)
-    assert np.array_equal(codes.cpu().numpy(), O.e4m3_quantize(xs, s_ref))
+    assert np.array_equal(codes.cpu().numpy(), quant(xs, s_ref))
     # a scale that is not a power of two and saturates part of the range
-    s2 = torch.full((4,), 0.0123, dtype=torch.float32, device=DEV)
-    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), s2, codes, None)
+    s_fix = 0.0123 if fmt == "e4m3" else 0.0123 / 128
+    s2 = torch.full((4,), s_fix, dtype=torch.float32, device=DEV)
+    L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), s2, codes, None, fmt=FMTS[fmt])
     torch.cuda.synchronize()
-    assert np.array_equal(codes.cpu().numpy(), O.e4m3_quantize(xs, np.float32(0.0123)))
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, quant(xs, np.float32(s_fix)))
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    assert np.count_nonzero((got & 0x7F) == top) > 0, "the fixed scale should saturate part of the range"
 
 
-def test_fp8_dequantize_all_codes():
-    say("fp8 dequantize: all 256 codes")
+@pytest.mark.parametrize("fmt", list(FMTS))
+def test_fp8_dequantize_all_codes(fmt):
+    say(f"fp8 dequantize {fmt}: all 256 codes")
+    dequant = O.FP8_FORMATS[fmt][1]
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(DEV)
     for s in (1.0, 0.0123):
         scale = torch.full((4,), s, dtype=torch.float32, device=DEV)
         y = torch.empty(256, dtype=torch.float32, device=DEV)
-        L.whisper_fp8_dequantize(codes, 256, scale, y, L.WHISPER_F32)
+        L.whisper_fp8_dequantize(codes, 256, scale, y, L.WHISPER_F32, fmt=FMTS[fmt])
         torch.cuda.synchronize()
-        ref = O.e4m3_dequantize(np.arange(256), np.float32(s)).astype(np.float32)
+        ref = dequant(np.arange(256), np.float32(s)).astype(np.float32)
         got = y.cpu().numpy()
         assert np.array_equal(np.isnan(got), np.isnan(ref))
         ok = ~np.isnan(ref)

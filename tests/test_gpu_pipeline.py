@@ -147,11 +147,12 @@ def check_logits_argmax(lg_gpu, am_gpu, lg_ref, rows, tag):
     return n_tied
 
 
-def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None):
+def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None, cross_fmt="e4m3"):
     """Teacher-forced decode on the GPU from a prefilled fp8 cache vs the oracle on `rows`.
-    cross_fp8_scale: when given, the cross-attention K/V are e4m3 codes with that
-    scale for every (layer, K|V), on both sides (the GPU quantises its bf16
-    projections, the oracle its own fp64 ones)."""
+    cross_fp8_scale: when given, the cross-attention K/V are fp8 codes in
+    cross_fmt ("e4m3" or "e5m2") with that scale for every (layer, K|V), on
+    both sides (the GPU quantises its bf16 projections, the oracle its own
+    fp64 ones)."""
     H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
     m, W = model_for(dims, ln_random=True)
     dt = act_dtype(dims)
@@ -170,8 +171,10 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale
     xscales = None
     if cross_fp8_scale is not None:
         xscales = np.full((Lyr, 2), np.float32(cross_fp8_scale), np.float32)
-        xcodes, xsc = m.quantize_cross_kv(ckv, scales=torch.from_numpy(xscales))
-        state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc)
+        fmt = {"e4m3": L.WHISPER_FP8_E4M3, "e5m2": L.WHISPER_FP8_E5M2}[cross_fmt]
+        xcodes, xsc = m.quantize_cross_kv(ckv, scales=torch.from_numpy(xscales), fmt=fmt)
+        state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc,
+                            cross_format=fmt)
         del ckv
     else:
         state = DecodeState(dims, B, cap, ckv, scales, lengths0)
@@ -199,7 +202,7 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale
     cross_rows = {b: O.cross_kv(enc_h[b], Wh, H, Lyr) for b in rows}
     cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
     if xscales is not None:
-        cross = O.cross_kv_fp8(cross, xscales)
+        cross = O.cross_kv_fp8(cross, xscales, fmt=cross_fmt)
     cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
     lengths = lengths0.cpu().numpy().copy()
     for (l, kv), x in prefill.items():
@@ -266,6 +269,18 @@ def test_decode_fp8_cross_kv_large_v3_shape():
     lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
     rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
     run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 fp8 cross", cross_fp8_scale=5.0 / 448.0)
+
+
+def test_decode_fp8_e5m2_cross_kv_large_v3_shape():
+    """The E5M2 form of the fp8 cross-attention K/V (the aggressive preset's
+    format, chosen for range) with unit scales: E5M2 spans these K/V values
+    without per-tensor scaling. Against the oracle attending over its own K/V
+    quantised to E5M2 with the same scales."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode large-v3 shape, 4 layers, B=64, E5M2 cross K/V scale 1, cap 672, prefill U[1,448], 3 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 7, 40})
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 e5m2 cross", cross_fp8_scale=1.0, cross_fmt="e5m2")
 
 
 # ------------------------------------------------------------------ tiny fp32 end to end
