@@ -116,6 +116,43 @@ whisper_status whisper_pack_weights(const whisper_dims* dims, const float* const
  * chunks (LOGMEL, ENCODE, CROSS_KV) or rows (DECODE). 0 on invalid input. */
 size_t whisper_workspace_size(const whisper_dims* dims, int batch, int which);
 
+/* Batch sizing under a device-memory budget (whisper_blaze showcase page,
+ * "VRAM capping": a VRAM limit on a shared card sizes each GPU batch to fit;
+ * the project page's batcher caps the batch to the budget). Host arithmetic
+ * only, from the size queries above; nothing is allocated or launched.
+ * Fills *plan for the largest batch B in 1..max_batch (and B * max(1,
+ * prompt_tokens) <= 4096) whose peak footprint fits in budget_bytes, for one
+ * pass of B 30 s chunks: log-mel, encoder, cross K/V, an optional fp8
+ * quantisation of the cross K/V (cross_fp8 != 0), then decoding with a
+ * kv_cap-slot fp8 KV cache (prompt_tokens > 1: one causal prefill first).
+ * Every buffer is rounded up to 256 bytes. The schedule keeps the packed
+ * weights and ONE workspace of the largest size any call of the pass needs
+ * alive throughout, and each stage's buffers only while a stage reads or
+ * writes them:
+ *   logmel:   audio [B, 480000] fp32 + mel [B, n_mels, 3000] fp32
+ *   encode:   mel + encoder output [B, 1500, d] (act dtype)
+ *   cross_kv: encoder output + cross K/V [L, 2, B, H, 1500, 64] (act dtype)
+ *   quantise: cross K/V + codes (1 byte each) + scales [L, 2] fp32 (fp8 only)
+ *   decode:   cross K/V (or codes + scales) + KV cache [L, 2, B, H, kv_cap, 64]
+ *             uint8 + its scales + tokens, lengths, argmax [B] int32 + prompt
+ *             [B, prompt_tokens] int32 + error word + logits [B, n_vocab] fp32
+ *             when want_logits;
+ * total = weights + workspace + the largest stage. Returns WHISPER_OK, or
+ * WHISPER_ERR_CAPACITY when even B = 1 does not fit (plan then describes
+ * B = 1 with plan->batch = 0), WHISPER_ERR_SHAPE for dims without both
+ * encoder and decoder or kv_cap outside 1..4096, WHISPER_ERR_INVALID_ARG for
+ * a NULL plan or max_batch < 1. */
+typedef struct {
+  int batch;                 /* planned batch (0: one chunk does not fit) */
+  int peak_stage;            /* 0 logmel, 1 encode, 2 cross_kv, 3 quantise, 4 decode */
+  size_t weights, workspace; /* packed weights; the one shared workspace */
+  size_t audio, mel, encoder_out, cross_kv, cross_codes, kv_cache, decode_state, logits;
+  size_t stage[5];           /* live stage buffers of each stage (without weights, workspace) */
+  size_t total;              /* weights + workspace + max(stage) */
+} whisper_batch_plan;
+whisper_status whisper_plan_batch(const whisper_dims* dims, size_t budget_bytes, int kv_cap, int prompt_tokens,
+                                  int cross_fp8, int want_logits, int max_batch, whisper_batch_plan* plan);
+
 /* ------------------------------------------------------------------ front end
  * Log-mel features of `batch` chunks (showcase page, mel_spectrogram.cu card;
  * direct kernel call mel_spectrogram(audio) -> [1, 128, T]).

@@ -25,7 +25,7 @@ EXPORTS = [
     "whisper_linear", "whisper_attention_encoder", "whisper_attention_decode_self",
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
     "whisper_profile_arm", "whisper_profile_disarm", "whisper_status_string", "whisper_last_error",
-    "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read", "whisper_chunk_plan",
+    "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read", "whisper_chunk_plan", "whisper_plan_batch",
     "whisper_logmel_chunked",
 ]
 
@@ -43,6 +43,16 @@ class WhisperDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "n_mels", "n_audio_ctx", "d_model", "n_heads", "head_dim", "d_ffn",
         "n_enc_layers", "n_dec_layers", "n_vocab", "n_text_ctx", "act")]
+
+
+class WhisperBatchPlan(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int), ("peak_stage", ctypes.c_int)] + [
+        (n, ctypes.c_size_t) for n in ("weights", "workspace", "audio", "mel", "encoder_out", "cross_kv",
+                                       "cross_codes", "kv_cache", "decode_state", "logits")] + [
+        ("stage", ctypes.c_size_t * 5), ("total", ctypes.c_size_t)]
+
+
+PLAN_STAGES = ("logmel", "encode", "cross_kv", "quantise", "decode")
 
 
 def make_dims(d):
@@ -78,6 +88,7 @@ _SIG = {
     "whisper_attention_decode_cross_workspace_size": (Z, [I, I, I]),
     "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
     "whisper_chunk_plan": (I, [ctypes.c_int64, I, P, I]),
+    "whisper_plan_batch": (I, [P, Z, I, I, I, I, I, P]),
     "whisper_logmel_chunked": (I, [P, P, ctypes.c_int64, I, P, P, Z, P]),
     "whisper_peak_mfma": (I, [I, I, P, P]),
     "whisper_peak_mfma_flop": (ctypes.c_double, [I, I]),
@@ -313,6 +324,21 @@ def whisper_chunk_plan(n_samples, stride):
     buf = (ctypes.c_int32 * (4 * n))()
     lib().whisper_chunk_plan(n_samples, stride, buf, n)
     return n, [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def whisper_plan_batch(dims, budget_bytes, kv_cap, prompt_tokens=0, cross_fp8=False, want_logits=False,
+                       max_batch=4096):
+    """Largest batch whose one-pass footprint fits budget_bytes, with the
+    footprint breakdown, as a dict (raises WhisperError with status 6 when one
+    chunk does not fit)."""
+    dd, dp = _dims_ptr(dims)
+    plan = WhisperBatchPlan()
+    _check(lib().whisper_plan_batch(dp, budget_bytes, kv_cap, prompt_tokens, int(bool(cross_fp8)),
+                                    int(bool(want_logits)), max_batch, ctypes.byref(plan)))
+    out = {n: getattr(plan, n) for n, _ in WhisperBatchPlan._fields_ if n != "stage"}
+    out["stage"] = dict(zip(PLAN_STAGES, list(plan.stage)))
+    out["peak_stage"] = PLAN_STAGES[plan.peak_stage]
+    return out
 
 
 def whisper_logmel_chunked(dims, audio, n_samples, stride, mel_out, ws, ws_bytes, stream=None):

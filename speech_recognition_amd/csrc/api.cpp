@@ -530,6 +530,63 @@ size_t whisper_workspace_size(const whisper_dims* d, int batch, int which) {
   return 0;
 }
 
+// Peak device footprint of one pass of B chunks under the stage schedule the
+// header documents.
+static void batch_footprint(const whisper_dims* d, int B, int cap, int P, bool fp8, bool logits,
+                            whisper_batch_plan* p) {
+  const size_t e = esz(d->act), b = (size_t)B, L = d->n_dec_layers, H = d->n_heads, T = d->n_audio_ctx;
+  const size_t D = d->d_model;
+  *p = whisper_batch_plan{};
+  p->weights = al256(whisper_packed_weights_size(d));
+  p->workspace = std::max({al256(logmel_ws(B, d->n_mels)), enc_ws(d, B).total, dec_ws(d, B).total,
+                           dec_ws(d, B * std::max(P, 1)).total, fp8 ? al256(whisper_fp8_workspace_size()) : 0});
+  p->audio = al256(b * 480000 * 4);
+  p->mel = al256(b * d->n_mels * N_FRAMES * 4);
+  p->encoder_out = al256(b * T * D * e);
+  p->cross_kv = al256(L * 2 * b * H * T * 64 * e);
+  p->cross_codes = fp8 ? al256(L * 2 * b * H * T * 64) + al256(L * 2 * 4) : 0;
+  p->kv_cache = al256(L * 2 * b * H * (size_t)cap * 64);
+  p->decode_state = al256(L * 2 * 4) + 3 * al256(b * 4) + al256(b * std::max(P, 1) * 4) + al256(16);
+  p->logits = logits ? al256(b * d->n_vocab * 4) : 0;
+  p->stage[0] = p->audio + p->mel;
+  p->stage[1] = p->mel + p->encoder_out;
+  p->stage[2] = p->encoder_out + p->cross_kv;
+  p->stage[3] = fp8 ? p->cross_kv + p->cross_codes : 0;
+  p->stage[4] = (fp8 ? p->cross_codes : p->cross_kv) + p->kv_cache + p->decode_state + p->logits;
+  for (int i = 0; i < 5; ++i)
+    if (p->stage[i] > p->stage[p->peak_stage]) p->peak_stage = i;
+  p->total = p->weights + p->workspace + p->stage[p->peak_stage];
+}
+
+whisper_status whisper_plan_batch(const whisper_dims* d, size_t budget, int cap, int P, int cross_fp8,
+                                  int want_logits, int max_batch, whisper_batch_plan* plan) {
+  WH_CHECK(check_dims(d));
+  if (!plan) return fail(WHISPER_ERR_INVALID_ARG, "plan_batch: plan is NULL");
+  if (max_batch < 1) return fail(WHISPER_ERR_INVALID_ARG, "plan_batch: max_batch must be >= 1");
+  if (d->n_enc_layers <= 0 || d->n_dec_layers <= 0)
+    return fail(WHISPER_ERR_SHAPE, "plan_batch: needs both encoder and decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "plan_batch: kv_cap must be in 1..4096");
+  if (P < 0 || P > cap) return fail(WHISPER_ERR_SHAPE, "plan_batch: prompt_tokens must be in 0..kv_cap");
+  const bool fp8 = cross_fp8 != 0, lg = want_logits != 0;
+  int hi = std::min(max_batch, 4096 / std::max(P, 1));
+  batch_footprint(d, 1, cap, P, fp8, lg, plan);
+  if (plan->total > budget) {
+    plan->batch = 0;
+    return fail(WHISPER_ERR_CAPACITY, "plan_batch: one chunk does not fit in the budget");
+  }
+  int lo = 1;  // footprint is non-decreasing in B: the largest fitting B by bisection
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    whisper_batch_plan t;
+    batch_footprint(d, mid, cap, P, fp8, lg, &t);
+    if (t.total <= budget) lo = mid;
+    else hi = mid - 1;
+  }
+  batch_footprint(d, lo, cap, P, fp8, lg, plan);
+  plan->batch = lo;
+  return WHISPER_OK;
+}
+
 whisper_status whisper_logmel(const whisper_dims* d, const float* audio, int B, int n_samples, float* mel_out,
                               void* ws, size_t ws_bytes, void* stream) {
   WH_CHECK(check_dims(d));

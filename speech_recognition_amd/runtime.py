@@ -34,16 +34,29 @@ class Whisper:
                 raise ValueError("logical weights must be contiguous fp32 device tensors")
         self.packed = _empty_bytes(L.whisper_packed_weights_size(dims), self.device)
         L.whisper_pack_weights(dims, logical_weights, self.packed)
-        self._ws = {}
+        self._ws = None
 
     def workspace(self, batch, which):
+        """The model's one workspace, grown to the largest size asked so far.
+        Calls are ordered on one stream, so every stage reuses the same
+        buffer (the schedule whisper_plan_batch sizes)."""
         nbytes = L.whisper_workspace_size(self.dims, batch, which)
-        key = which
-        ws = self._ws.get(key)
-        if ws is None or ws.numel() < nbytes:
-            ws = _empty_bytes(nbytes, self.device)
-            self._ws[key] = ws
-        return ws, nbytes
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = None
+            self._ws = _empty_bytes(nbytes, self.device)
+        return self._ws, nbytes
+
+    def reserve_workspace(self, nbytes):
+        """Allocate the shared workspace up front (e.g. a plan's workspace size)."""
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = None
+            self._ws = _empty_bytes(nbytes, self.device)
+
+    def plan_batch(self, budget_bytes, kv_cap, prompt_tokens=0, cross_fp8=False, want_logits=False,
+                   max_batch=4096):
+        """Largest batch of 30 s chunks whose pass fits budget_bytes (whisper_plan_batch)."""
+        return L.whisper_plan_batch(self.dims, budget_bytes, kv_cap, prompt_tokens, cross_fp8, want_logits,
+                                    max_batch)
 
     # ---------------------------------------------------------------- stages
     def logmel(self, audio, out=None):

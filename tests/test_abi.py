@@ -121,3 +121,64 @@ def test_chunk_plan_host_logic_matches_oracle():
     for bad in ((0, 400000), (1000, 0), (1000, 480160), (1000, 1000)):
         with pytest.raises(L.WhisperError):
             L.whisper_chunk_plan(*bad)
+
+
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def test_plan_batch_host_logic():
+    """whisper_plan_batch is host arithmetic over the size queries: the plan
+    fits the budget, one more chunk does not, the stage sums follow the
+    documented schedule, and the footprint grows with the batch."""
+    G = 1 << 30
+    full = CONFIGS["v3_decode"].with_(n_enc_layers=32)
+    # the showcase page's example cap: 24 GB on a shared card; this footprint
+    # admits exactly the 64-chunk batch of the large-v3 decode workload
+    assert L.whisper_plan_batch(full, 24 * G, 672, 4, False, True)["batch"] == 64
+    prev = 0
+    for budget in (6 * G, 24 * G, 80 * G, 288 * G):
+        for fp8 in (False, True):
+            for P, logits in ((0, False), (4, True)):
+                p = L.whisper_plan_batch(full, budget, 672, P, fp8, logits)
+                B = p["batch"]
+                assert 1 <= B and p["total"] <= budget
+                nxt = L.whisper_plan_batch(full, 1 << 62, 672, P, fp8, logits, max_batch=B + 1)
+                assert nxt["batch"] == B + 1 and nxt["total"] > budget
+                Lh, H, T, D, e = 32, 20, 1500, 1280, 2
+                assert p["weights"] == _al(L.whisper_packed_weights_size(full))
+                ws = max(L.whisper_workspace_size(full, B, k) for k in (L.WS_LOGMEL, L.WS_ENCODE, L.WS_DECODE))
+                ws = max(ws, L.whisper_workspace_size(full, B * max(P, 1), L.WS_DECODE))
+                if fp8:
+                    ws = max(ws, _al(L.whisper_fp8_workspace_size()))
+                assert p["workspace"] == ws
+                assert p["audio"] == _al(B * 480000 * 4) and p["mel"] == _al(B * 128 * 3000 * 4)
+                assert p["encoder_out"] == _al(B * T * D * e)
+                assert p["cross_kv"] == _al(Lh * 2 * B * H * T * 64 * e)
+                assert p["cross_codes"] == (_al(Lh * 2 * B * H * T * 64) + _al(Lh * 2 * 4) if fp8 else 0)
+                assert p["kv_cache"] == _al(Lh * 2 * B * H * 672 * 64)
+                assert p["logits"] == (_al(B * 51866 * 4) if logits else 0)
+                st = p["stage"]
+                assert st["logmel"] == p["audio"] + p["mel"]
+                assert st["encode"] == p["mel"] + p["encoder_out"]
+                assert st["cross_kv"] == p["encoder_out"] + p["cross_kv"]
+                assert st["quantise"] == (p["cross_kv"] + p["cross_codes"] if fp8 else 0)
+                assert st["decode"] == ((p["cross_codes"] if fp8 else p["cross_kv"]) + p["kv_cache"]
+                                        + p["decode_state"] + p["logits"])
+                assert p["total"] == p["weights"] + p["workspace"] + max(st.values())
+                assert st[p["peak_stage"]] == max(st.values())
+        b24 = L.whisper_plan_batch(full, budget, 672)["batch"]
+        assert b24 > prev
+        prev = b24
+    # the prefill bound B * P <= 4096 and max_batch cap
+    assert L.whisper_plan_batch(full, 1 << 62, 672, 64)["batch"] == 64
+    assert L.whisper_plan_batch(full, 1 << 62, 672, 0, max_batch=7)["batch"] == 7
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_plan_batch(full, 3 * G, 672)
+    assert e.value.status == 6
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_plan_batch(CONFIGS["v3_decode"], 24 * G, 672)
+    assert e.value.status == 2
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_plan_batch(full, 24 * G, 5000)
+    assert e.value.status == 2

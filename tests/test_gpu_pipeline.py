@@ -428,3 +428,62 @@ def test_decode_prefill_equals_successive_steps_and_oracle():
     m.decode_prefill(m2, toks[:P].t().contiguous(), lg1)
     torch.cuda.synchronize()
     check_logits_argmax(host(lg1), m2.argmax.cpu().numpy(), lg_ref, rows, "prefill")
+
+
+@pytest.mark.parametrize("cross_fp8", [False, True])
+def test_plan_batch_pass_fits_its_budget(cross_fp8):
+    """A batch sized by whisper_plan_batch runs the whole pass (log-mel,
+    encoder, cross K/V, [fp8 quantisation], 4-token prefill, one decode step)
+    with torch's peak device allocation inside the plan's total; the plan for
+    one more chunk exceeds the budget. Turbo shape, 6 GiB budget."""
+    dims = CONFIGS["turbo_longform"]
+    budget, cap, P = 6 << 30, 228, 4
+    m, W = model_for(dims)
+    del W
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    plan = m.plan_batch(budget, cap, P, cross_fp8=cross_fp8, want_logits=True)
+    B = plan["batch"]
+    say(f"plan_batch turbo, 6 GiB, fp8 cross {cross_fp8}: B={B}, peak stage {plan['peak_stage']}, "
+        f"total {plan['total'] / 2**30:.2f} GiB")
+    assert B >= 2
+    assert m.plan_batch(1 << 62, cap, P, cross_fp8=cross_fp8, want_logits=True, max_batch=B + 1)["total"] > budget
+    base = torch.cuda.memory_allocated()
+    assert base - plan["weights"] < (1 << 20), "only the packed weights should be live"
+    torch.cuda.reset_peak_memory_stats()
+    m.reserve_workspace(plan["workspace"])
+    audio = gen_audio_tones("cpu", dims.cfg_id, B).to(DEV)  # no device temporaries beside the pass
+    mel = m.logmel(audio)
+    del audio
+    enc = m.encode(mel)
+    del mel
+    ckv = m.cross_kv(enc)
+    del enc
+    kv_scales = torch.full((dims.n_dec_layers, 2), 0.05, dtype=torch.float32)
+    lengths = torch.zeros(B, dtype=torch.int32)
+    if cross_fp8:
+        xcodes, xsc = m.quantize_cross_kv(ckv, scales=torch.full((dims.n_dec_layers, 2), 0.01))
+        del ckv
+        state = DecodeState(dims, B, cap, None, kv_scales, lengths, cross_codes=xcodes, cross_scales=xsc)
+    else:
+        state = DecodeState(dims, B, cap, ckv, kv_scales, lengths)
+        del ckv
+    prompt = gen_tokens("cpu", dims.cfg_id, P, B, dims.n_vocab).t().contiguous().to(DEV)
+    logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
+    if cross_fp8:  # the prefill takes bf16 cross K/V; fp8 feeds the prompt step by step
+        for t in range(P):
+            m.decode_step(state, prompt[:, t].contiguous(), logits)
+    else:
+        m.decode_prefill(state, prompt)
+    tok = state.argmax.clone()
+    m.decode_step(state, tok, logits)
+    torch.cuda.synchronize()
+    assert int(state.dev_error[0].item()) == 0
+    assert np.array_equal(state.lengths.cpu().numpy(), np.full(B, P + 1))
+    am = state.argmax.cpu().numpy()
+    assert am.min() >= 0 and am.max() < dims.n_vocab
+    peak = torch.cuda.max_memory_allocated() - base
+    need = plan["total"] - plan["weights"]
+    say(f"  peak {peak / 2**30:.3f} GiB of planned {need / 2**30:.3f} GiB beyond the weights")
+    assert peak <= need + (16 << 20)
+    assert peak >= 0.9 * need
