@@ -417,6 +417,57 @@ def encoder(mel, W, n_heads, n_layers):
     return encoder_layers(conv_stem(mel, W), W, n_heads, range(n_layers), ln_post=True)
 
 
+# =========================================================================== mixed_fp8 encoder
+# Reading of the whisper_blaze showcase page's precision.py card (the
+# mixed_fp8 preset's table of layer sites): the encoder FFN (both matmuls)
+# and the encoder attention's query/key/value projections take fp8 E4M3
+# weights and activations; the attention itself, its output projection and
+# the conv stem keep the activation precision. Scales, after the
+# fp8_quantize.cu card and "Learnings" (per-tensor scales from maxima):
+# one per weight tensor (query, key, value, fc1, fc2: fl32(amax) / 448), and
+# one per activation tensor at each site, taken over one chunk's activation
+# (one 30 s clip, so a chunk's result does not depend on the batch it runs
+# in): fl32(amax) / 448. The product sums value(code_x) * value(code_w) and
+# multiplies by both scales; the bias is added after.
+
+def fp8_linear(x, w, b, sx, sw):
+    """y = sx * sw * (value(e4m3(x / sx)) @ value(e4m3(w / sw))^T) + b."""
+    cx = e4m3_quantize(x, sx)
+    cw = e4m3_quantize(w, sw)
+    y = (e4m3_value(cx) @ e4m3_value(cw).T) * (float(np.float32(sx)) * float(np.float32(sw)))
+    return y if b is None else y + b
+
+
+def _site(x, w, b, fp8):
+    """One mixed_fp8 matmul site: fp8 with amax scales, or the plain linear."""
+    if not fp8:
+        return linear(x, w, b)
+    return fp8_linear(x, w, b, e4m3_scale_from_amax(x), e4m3_scale_from_amax(w))
+
+
+def encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8=True):
+    """encoder_layer with the mixed_fp8 sites (query, key, value, fc1, fc2)
+    in fp8 E4M3 for one chunk x [1500, d]; with fp8=False it is
+    encoder_layer."""
+    p = f"encoder.blocks.{layer}."
+    a = layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
+    q = _site(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], fp8)
+    k = _site(a, W[p + "attn.key.weight"], None, fp8)
+    v = _site(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], fp8)
+    x = x + linear(attention(q, k, v, n_heads), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
+    m = layer_norm(x, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
+    hdn = gelu(_site(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], fp8))
+    return x + _site(hdn, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], fp8)
+
+
+def encoder_layers_mixed_fp8(x, W, n_heads, layers, ln_post=True, fp8=True):
+    for layer in layers:
+        x = encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8)
+    if ln_post:
+        x = layer_norm(x, W["encoder.ln_post.weight"], W["encoder.ln_post.bias"])
+    return x
+
+
 def cross_kv(enc, W, n_heads, n_layers):
     """Per decoder layer the cross-attention keys and values of one chunk's
     encoder output enc [T, d]: K = enc Wk^T, V = enc Wv^T + bv, each returned

@@ -1,0 +1,86 @@
+"""Pins of the oracle's mixed_fp8 encoder sites (fp8 E4M3 weights and
+activations with per-tensor amax scales at the query/key/value and FFN
+matmuls): grid values pass exactly, an independent library quantiser
+(torch.float8_e4m3fn) gives the same product, the error stays inside the
+half-step bound, and with fp8 off the layer is the plain encoder layer."""
+import numpy as np
+import torch
+
+from oracle import whisper_oracle as O
+from tests.test_oracle_layers import _tiny_weights
+
+
+def _grid(rng, shape, s):
+    codes = rng.integers(0, 256, shape).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    return O.e4m3_value(codes) * s
+
+
+def test_fp8_linear_exact_on_scaled_grid():
+    rng = np.random.default_rng(0)
+    sx, sw = 2.0 ** -5, 2.0 ** -7
+    x, w, b = _grid(rng, (37, 96), sx), _grid(rng, (40, 96), sw), rng.standard_normal(40)
+    assert np.array_equal(O.fp8_linear(x, w, b, sx, sw), O.linear(x, w, b))
+    assert np.array_equal(O.fp8_linear(x, w, None, sx, sw), O.linear(x, w))
+
+
+def test_fp8_linear_matches_torch_quantiser():
+    rng = np.random.default_rng(1)
+    x, w, b = rng.standard_normal((33, 128)) * 2.0, rng.standard_normal((24, 128)) * 0.05, rng.standard_normal(24)
+    sx, sw = O.e4m3_scale_from_amax(x), O.e4m3_scale_from_amax(w)
+
+    def tq(a, s):  # fl32(a * fl32(1/s)) rounded by torch's float8_e4m3fn conversion
+        y = torch.from_numpy(a.astype(np.float32)) * torch.tensor(np.float32(1.0) / np.float32(s))
+        return y.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    ref = (tq(x, sx) @ tq(w, sw).T) * (float(sx) * float(sw)) + b
+    assert np.allclose(O.fp8_linear(x, w, b, sx, sw), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_fp8_linear_error_within_half_step_bound():
+    rng = np.random.default_rng(2)
+    x, w = rng.standard_normal((50, 64)), rng.standard_normal((30, 64)) * 0.1
+    sx, sw = O.e4m3_scale_from_amax(x), O.e4m3_scale_from_amax(w)
+
+    def half_step(a, s):  # 2^-4 relative in the normal range, 2^-10 * s below it
+        return np.maximum(np.abs(a) * 2.0 ** -4, 2.0 ** -10 * float(s)) * (1 + 1e-6)
+
+    dx, dw = half_step(x, sx), half_step(w, sw)
+    bound = np.abs(x) @ dw.T + dx @ np.abs(w).T + dx @ dw.T
+    err = np.abs(O.fp8_linear(x, w, None, sx, sw) - O.linear(x, w))
+    assert np.all(err <= bound)
+    assert err.max() > 0
+
+
+def test_mixed_fp8_layer_off_is_the_plain_layer_and_on_stays_close():
+    rng = np.random.default_rng(3)
+    W = _tiny_weights(rng, d=64, f=256)
+    x = rng.standard_normal((40, 64))
+    assert np.array_equal(O.encoder_layer_mixed_fp8(x, W, 0, 2, fp8=False), O.encoder_layer(x, W, 0, 2))
+    assert np.array_equal(O.encoder_layers_mixed_fp8(x, W, 2, [0, 1], fp8=False),
+                          O.encoder_layers(x, W, 2, [0, 1]))
+    y8 = O.encoder_layer_mixed_fp8(x, W, 0, 2)
+    y = O.encoder_layer(x, W, 0, 2)
+    # e4m3 keeps 3 mantissa bits (a rounding error of up to 2^-4 per operand),
+    # so the layer moves by some per cent, not by its own size
+    rel = np.linalg.norm(y8 - y) / np.linalg.norm(y)
+    assert 0 < rel < 0.15
+
+
+def test_mixed_fp8_sites_use_per_tensor_amax_scales():
+    """The layer's fp8 sites equal fp8_linear with amax scales of exactly the
+    site's input (one chunk) and weight: recompute the layer from its parts."""
+    rng = np.random.default_rng(4)
+    W = _tiny_weights(rng, d=64, f=256)
+    x = rng.standard_normal((30, 64))
+    p = "encoder.blocks.1."
+    a = O.layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
+    s = O.e4m3_scale_from_amax
+    q = O.fp8_linear(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], s(a), s(W[p + "attn.query.weight"]))
+    k = O.fp8_linear(a, W[p + "attn.key.weight"], None, s(a), s(W[p + "attn.key.weight"]))
+    v = O.fp8_linear(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], s(a), s(W[p + "attn.value.weight"]))
+    h = x + O.linear(O.attention(q, k, v, 2), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
+    m = O.layer_norm(h, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
+    g = O.gelu(O.fp8_linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], s(m), s(W[p + "mlp.0.weight"])))
+    out = h + O.fp8_linear(g, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], s(g), s(W[p + "mlp.2.weight"]))
+    assert np.array_equal(O.encoder_layer_mixed_fp8(x, W, 1, 2), out)
