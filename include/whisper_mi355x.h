@@ -79,7 +79,8 @@ typedef struct {
   whisper_dtype act;
 } whisper_dims;
 
-enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3 };
+enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3,
+       WHISPER_WS_ENCODE_FP8 = 4 /* whisper_encode_fp8 / whisper_encode_layers_fp8 */ };
 
 /* ------------------------------------------------------------------ weights
  * Logical weights are fp32 device tensors in PyTorch layout, passed as an
@@ -261,6 +262,52 @@ whisper_status whisper_decode_step_xq(const whisper_dims* dims, const void* pack
                                       const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,
                                       whisper_fp8_format cross_format, float* logits, int32_t* argmax,
                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ mixed_fp8 encoder
+ * The showcase page's mixed_fp8 precision preset (precision.py card, its
+ * table of layer sites): the encoder FFN (fc1, fc2) and the attention's
+ * query/key/value projections take fp8 E4M3 weights and activations; the
+ * attention, its output projection, the conv stem and everything in the
+ * decoder keep bf16. Scales (fp8_quantize.cu card; "Learnings": per-tensor
+ * scales from activation maxima): one per weight tensor, fl32(amax) / 448,
+ * computed at pack time; one per activation tensor at each site and chunk
+ * (the 1500 x d or 1500 x d_ffn activation of one 30 s clip, so a chunk's
+ * output does not depend on its batch), fl32(amax) / 448, computed on the
+ * device before each site. A site computes
+ *   y = fl32(sum value(code_x) value(code_w)) * s_x * s_w + bias
+ * with fp32 accumulation, then its epilogue (GELU for fc1) in bf16.
+ * Only for bf16 models with d_model and d_ffn multiples of 256.
+ *
+ * whisper_pack_weights_fp8 quantises the encoder's query, key, value, fc1 and
+ * fc2 weights from the same logical fp32 tensors whisper_pack_weights takes
+ * (16-byte aligned) into caller memory `packed8` of
+ * whisper_packed_weights_fp8_size() bytes; ws: whisper_fp8_workspace_size()
+ * bytes. The bf16 `packed` buffer is still needed (biases, LayerNorms, stem,
+ * out-projection). whisper_encode_fp8 and whisper_encode_layers_fp8 are
+ * whisper_encode and whisper_encode_layers with the fp8 sites; ws:
+ * whisper_workspace_size(dims, batch, WHISPER_WS_ENCODE_FP8) bytes. */
+size_t whisper_packed_weights_fp8_size(const whisper_dims* dims);
+whisper_status whisper_pack_weights_fp8(const whisper_dims* dims, const float* const* logical, void* packed8,
+                                        void* ws, size_t ws_bytes, void* stream);
+whisper_status whisper_encode_fp8(const whisper_dims* dims, const void* packed, const void* packed8,
+                                  const float* mel, int batch, void* enc_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+whisper_status whisper_encode_layers_fp8(const whisper_dims* dims, const void* packed, const void* packed8,
+                                         const void* h_in, int batch, int layer_begin, int layer_end,
+                                         int apply_ln_post, void* h_out, void* ws, size_t ws_bytes, void* stream);
+
+/* One fp8 site as a kernel call (showcase page, gemm_hopper.cu card: FP8
+ * E4M3 GEMM). a: E4M3 codes [M, K] row-major; w: E4M3 codes [N, K] (PyTorch
+ * weight layout); a_scales: one fp32 scale per group of rows_per_scale rows
+ * (row m uses a_scales[m / rows_per_scale]); w_scale: one fp32 scale; bias:
+ * [N] fp32 or NULL; gelu != 0 applies exact GELU. c: bf16 [M, ldc], columns
+ * 0..N-1 written: c[m][n] = bf16(epi(acc * a_scales[m / rows_per_scale] *
+ * w_scale[0] + bias[n])), acc the fp32 sum of value(a[m][k]) * value(w[n][k]).
+ * Requires K % 256 == 0, K >= 512, N % 256 == 0, ldc % 8 == 0, ldc >= N,
+ * rows_per_scale >= 256, every operand under 2 GB (else WHISPER_ERR_SHAPE). */
+whisper_status whisper_gemm_fp8(const uint8_t* a, int M, int K, const float* a_scales, int rows_per_scale,
+                                const uint8_t* w, int N, const float* w_scale, const float* bias, int gelu, void* c,
+                                long ldc, void* stream);
 
 /* ------------------------------------------------------------------ kernel-level calls
  * fp8 codec with a per-tensor scale (project page quantise_e4m3 /

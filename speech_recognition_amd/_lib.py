@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libwhisper_mi355x.so")
 
 WHISPER_F32, WHISPER_BF16 = 0, 1
 WHISPER_FP8_E4M3, WHISPER_FP8_E5M2 = 0, 1
-WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE = 0, 1, 2, 3
+WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE, WS_ENCODE_FP8 = 0, 1, 2, 3, 4
 
 EXPORTS = [
     "whisper_weight_count", "whisper_packed_weights_size", "whisper_pack_weights", "whisper_workspace_size",
@@ -26,6 +26,8 @@ EXPORTS = [
     "whisper_attention_decode_cross_workspace_size", "whisper_attention_decode_cross",
     "whisper_profile_arm", "whisper_profile_disarm", "whisper_status_string", "whisper_last_error",
     "whisper_peak_mfma", "whisper_peak_mfma_flop", "whisper_peak_read", "whisper_chunk_plan", "whisper_plan_batch",
+    "whisper_packed_weights_fp8_size", "whisper_pack_weights_fp8", "whisper_encode_fp8", "whisper_encode_layers_fp8",
+    "whisper_gemm_fp8",
     "whisper_logmel_chunked",
 ]
 
@@ -89,6 +91,11 @@ _SIG = {
     "whisper_attention_decode_cross": (I, [I, P, P, P, I, I, I, P, P, Z, P]),
     "whisper_chunk_plan": (I, [ctypes.c_int64, I, P, I]),
     "whisper_plan_batch": (I, [P, Z, I, I, I, I, I, P]),
+    "whisper_packed_weights_fp8_size": (Z, [P]),
+    "whisper_pack_weights_fp8": (I, [P, P, P, P, Z, P]),
+    "whisper_encode_fp8": (I, [P, P, P, P, I, P, P, Z, P]),
+    "whisper_encode_layers_fp8": (I, [P, P, P, P, I, I, I, I, P, P, Z, P]),
+    "whisper_gemm_fp8": (I, [P, I, I, P, I, P, I, P, P, I, P, ctypes.c_long, P]),
     "whisper_logmel_chunked": (I, [P, P, ctypes.c_int64, I, P, P, Z, P]),
     "whisper_peak_mfma": (I, [I, I, P, P]),
     "whisper_peak_mfma_flop": (ctypes.c_double, [I, I]),
@@ -324,6 +331,35 @@ def whisper_chunk_plan(n_samples, stride):
     buf = (ctypes.c_int32 * (4 * n))()
     lib().whisper_chunk_plan(n_samples, stride, buf, n)
     return n, [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def whisper_packed_weights_fp8_size(dims):
+    dd, dp = _dims_ptr(dims)
+    return lib().whisper_packed_weights_fp8_size(dp)
+
+
+def whisper_pack_weights_fp8(dims, logical, packed8, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    arr = (ctypes.c_void_p * len(logical))(*[_p(t) for t in logical])
+    _check(lib().whisper_pack_weights_fp8(dp, arr, _p(packed8), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_encode_fp8(dims, packed, packed8, mel, batch, enc_out, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_encode_fp8(dp, _p(packed), _p(packed8), _p(mel), batch, _p(enc_out), _p(ws), ws_bytes,
+                                    _stream(stream)))
+
+
+def whisper_encode_layers_fp8(dims, packed, packed8, h_in, batch, l0, l1, ln_post, h_out, ws, ws_bytes,
+                              stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_encode_layers_fp8(dp, _p(packed), _p(packed8), _p(h_in), batch, l0, l1, int(bool(ln_post)),
+                                           _p(h_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_gemm_fp8(a, M, K, a_scales, rows_per_scale, w, N, w_scale, bias, gelu, c, ldc, stream=None):
+    _check(lib().whisper_gemm_fp8(_p(a), M, K, _p(a_scales), rows_per_scale, _p(w), N, _p(w_scale), _p(bias),
+                                  int(bool(gelu)), _p(c), ldc, _stream(stream)))
 
 
 def whisper_plan_batch(dims, budget_bytes, kv_cap, prompt_tokens=0, cross_fp8=False, want_logits=False,

@@ -136,9 +136,9 @@ int weight_count(const whisper_dims* d) {
 }
 
 // ------------------------------------------------------------------ workspace layout
-struct EncWS { size_t x0, g1, x, a, dlt, qkv, att, hf, total; };
-EncWS enc_ws(const whisper_dims* d, int B) {
-  EncWS W;
+struct EncWS { size_t x0, g1, x, a, dlt, qkv, att, hf, codes, part, ascale, total; };
+EncWS enc_ws(const whisper_dims* d, int B, bool fp8 = false) {
+  EncWS W{};
   const size_t e = esz(d->act), D = d->d_model, T = d->n_audio_ctx, rows = (size_t)B * T;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
@@ -152,8 +152,32 @@ EncWS enc_ws(const whisper_dims* d, int B) {
   const size_t hf_b = std::max(rows * d->d_ffn * e, (size_t)B * (N_FRAMES + 2) * D * e);
   W.hf = take(hf_b);
   W.g1 = W.hf;   // conv1 output lives in the MLP buffer before the first block
+  if (fp8) {     // E4M3 codes of the activation entering an fp8 site, per-chunk amax partials and scales
+    W.codes = take(rows * std::max((size_t)d->d_ffn, D));
+    W.part = take((size_t)B * 64 * 4);
+    W.ascale = take((size_t)B * 4);
+  }
   W.total = off;
   return W;
+}
+
+// E4M3 weights of the mixed_fp8 encoder sites, per layer: query, key, value
+// codes [3d, d] (one block, as the fused QKV), fc1 [f, d], fc2 [d, f]; then
+// per layer 8 fp32 scales (query, key, value, fc1, fc2, 3 unused).
+struct Packed8 { std::vector<size_t> qkv, w1, w2; size_t scales = 0, total = 0; };
+Packed8 layout8(const whisper_dims* d) {
+  Packed8 P;
+  const size_t D = d->d_model, F = d->d_ffn;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  for (int l = 0; l < d->n_enc_layers; ++l) {
+    P.qkv.push_back(take(3 * D * D));
+    P.w1.push_back(take(F * D));
+    P.w2.push_back(take(D * F));
+  }
+  P.scales = take((size_t)d->n_enc_layers * 8 * 4);
+  P.total = off;
+  return P;
 }
 
 // The MLP down-projection (K = d_ffn) runs split-K over DEC_KSPLIT workgroups
@@ -217,9 +241,11 @@ GemmParams gp(const void* A, long lda, const void* B, long ldb, int M, int N, in
 // The residual stream X is fp32 in the workspace. `h_in` is either that
 // buffer already holding the stem output (in_is_x) or caller hidden states in
 // the activation type, which the first LayerNorm copies into X.
+// packed8 non-NULL: the mixed_fp8 sites (query, key, value, fc1, fc2) run as
+// E4M3 GEMMs on the per-chunk quantised activation (W from enc_ws(d, B, true)).
 whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const Packed& P, const EncWS& W,
                               const void* h_in, bool in_is_x, int B, int l0, int l1, bool ln_post, void* out,
-                              void* ws, hipStream_t s) {
+                              void* ws, hipStream_t s, const void* packed8 = nullptr) {
   const ActType t = act_of(d->act);
   const int D = d->d_model, T = d->n_audio_ctx, M = B * T, F = d->d_ffn;
   float* X = at<float>(ws, W.x);
@@ -228,6 +254,7 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
   void* QKV = at<void>(ws, W.qkv);
   void* ATT = at<void>(ws, W.att);
   void* HF = at<void>(ws, W.hf);
+  const Packed8 P8 = packed8 ? layout8(d) : Packed8{};
   bool x_ready = in_is_x;  // X holds the residual stream
   bool have_delta = false; // Dl holds a block output not yet added to X
   for (int l = l0; l < l1; ++l) {
@@ -241,7 +268,26 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
     else
       WH_TRY(launch_layernorm(t, false, h_in, nullptr, g1, b1, 1e-5f, M, D, A, X, s));
     x_ready = true;
-    WH_TRY(launch_gemm(t, EPI_STORE, gp(A, D, at<void>(packed, L.wqkv), D, M, 3 * D, D, at<float>(packed, L.bqkv), QKV, 3 * D), s));
+    const float* sc8 = packed8 ? at<float>(packed8, P8.scales) + 8 * l : nullptr;
+    uint8_t* CODES = packed8 ? at<uint8_t>(ws, W.codes) : nullptr;
+    float* PART = packed8 ? at<float>(ws, W.part) : nullptr;
+    float* ASC = packed8 ? at<float>(ws, W.ascale) : nullptr;
+    // one fp8 site: C[:, col0:col0+N] = epi(e4m3(A) . W8^T * sa * sw + bias)
+    auto fp8_site = [&](Epi epi, const uint8_t* w8, const float* sw, int N, int K, const float* bias, void* C,
+                        long ldc) -> hipError_t {
+      GemmParams g = gp(CODES, K, w8, K, M, N, K, bias, C, ldc);
+      g.a_scale = ASC; g.a_rows_per_scale = T; g.b_scale = sw;
+      return launch_gemm_fp8(epi, g, s);
+    };
+    if (packed8) {
+      const uint8_t* q8 = at<uint8_t>(packed8, P8.qkv[l]);
+      const float* bq = at<float>(packed, L.bqkv);
+      WH_TRY(launch_chunk_quant_fp8(A, M, D, T, PART, ASC, CODES, s));
+      for (int r = 0; r < 3; ++r)  // query, key, value: one weight scale each
+        WH_TRY(fp8_site(EPI_STORE, q8 + (size_t)r * D * D, sc8 + r, D, D, bq + r * D, (u16_t*)QKV + r * D, 3 * D));
+    } else {
+      WH_TRY(launch_gemm(t, EPI_STORE, gp(A, D, at<void>(packed, L.wqkv), D, M, 3 * D, D, at<float>(packed, L.bqkv), QKV, 3 * D), s));
+    }
     {
       ProfScope ps(WHISPER_PROF_ENCODER_ATTENTION, s);
       WH_TRY(launch_attn_encoder(t, QKV, B, T, d->n_heads, ATT, s));
@@ -251,11 +297,21 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
       ProfScope ps(WHISPER_PROF_ENCODER_LAYERNORM, s);
       WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s));
     }
-    {
-      ProfScope ps(WHISPER_PROF_ENCODER_FFN1, s);
-      WH_TRY(launch_gemm(t, EPI_GELU, gp(A, D, at<void>(packed, L.w1), D, M, F, D, at<float>(packed, L.b1), HF, F), s));
+    if (packed8) {
+      WH_TRY(launch_chunk_quant_fp8(A, M, D, T, PART, ASC, CODES, s));
+      {
+        ProfScope ps(WHISPER_PROF_ENCODER_FFN1, s);
+        WH_TRY(fp8_site(EPI_GELU, at<uint8_t>(packed8, P8.w1[l]), sc8 + 3, F, D, at<float>(packed, L.b1), HF, F));
+      }
+      WH_TRY(launch_chunk_quant_fp8(HF, M, F, T, PART, ASC, CODES, s));
+      WH_TRY(fp8_site(EPI_STORE, at<uint8_t>(packed8, P8.w2[l]), sc8 + 4, D, F, at<float>(packed, L.b2), Dl, D));
+    } else {
+      {
+        ProfScope ps(WHISPER_PROF_ENCODER_FFN1, s);
+        WH_TRY(launch_gemm(t, EPI_GELU, gp(A, D, at<void>(packed, L.w1), D, M, F, D, at<float>(packed, L.b1), HF, F), s));
+      }
+      WH_TRY(launch_gemm(t, EPI_STORE, gp(HF, F, at<void>(packed, L.w2), F, M, D, F, at<float>(packed, L.b2), Dl, D), s));
     }
-    WH_TRY(launch_gemm(t, EPI_STORE, gp(HF, F, at<void>(packed, L.w2), F, M, D, F, at<float>(packed, L.b2), Dl, D), s));
     have_delta = true;
   }
   const float* gp_ = at<float>(packed, P.lnpg);
@@ -526,6 +582,7 @@ size_t whisper_workspace_size(const whisper_dims* d, int batch, int which) {
     case WHISPER_WS_ENCODE: return enc_ws(d, batch).total;
     case WHISPER_WS_CROSS_KV: return 0;
     case WHISPER_WS_DECODE: return dec_ws(d, batch).total;
+    case WHISPER_WS_ENCODE_FP8: return enc_ws(d, batch, true).total;
   }
   return 0;
 }
@@ -645,14 +702,15 @@ whisper_status whisper_encode_layers(const whisper_dims* d, const void* packed, 
   return run_enc_layers(d, packed, layout(d), W, h_in, false, B, l0, l1, apply_ln_post != 0, h_out, ws, S(stream));
 }
 
-whisper_status whisper_encode(const whisper_dims* d, const void* packed, const float* mel, int B, void* enc_out,
-                              void* ws, size_t ws_bytes, void* stream) {
+static whisper_status encode_impl(const whisper_dims* d, const void* packed, const void* packed8, const float* mel,
+                                  int B, void* enc_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = packed8 ? "encode_fp8" : "encode";
   WH_CHECK(check_dims(d));
-  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "encode: batch must be > 0");
-  if (d->n_enc_layers <= 0) return fail(WHISPER_ERR_SHAPE, "encode: no encoder layers");
-  WH_CHECK(check_ptrs({packed, mel, enc_out}, "encode"));
-  const EncWS W = enc_ws(d, B);
-  WH_CHECK(check_ws(ws, ws_bytes, W.total, "encode"));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, std::string(who) + ": batch must be > 0");
+  if (d->n_enc_layers <= 0) return fail(WHISPER_ERR_SHAPE, std::string(who) + ": no encoder layers");
+  WH_CHECK(check_ptrs({packed, mel, enc_out}, who));
+  const EncWS W = enc_ws(d, B, packed8 != nullptr);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, who));
   (void)hipGetLastError();
   const Packed P = layout(d);
   const ActType t = act_of(d->act);
@@ -674,7 +732,99 @@ whisper_status whisper_encode(const whisper_dims* d, const void* packed, const f
   GemmParams c2 = gp(G1, 2 * D, at<void>(packed, P.conv2w), 3 * D, T, D, 3 * D, at<float>(packed, P.conv2b), X, D);
   c2.batch = B; c2.strideA = R * D; c2.strideC = (long)T * D; c2.pe = at<float>(packed, P.pe);
   WH_TRY(launch_gemm(t, EPI_GELU_PE, c2, s));
-  return run_enc_layers(d, packed, P, W, X, true, B, 0, d->n_enc_layers, true, enc_out, ws, s);
+  return run_enc_layers(d, packed, P, W, X, true, B, 0, d->n_enc_layers, true, enc_out, ws, s, packed8);
+}
+
+whisper_status whisper_encode(const whisper_dims* d, const void* packed, const float* mel, int B, void* enc_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return encode_impl(d, packed, nullptr, mel, B, enc_out, ws, ws_bytes, stream);
+}
+
+static whisper_status check_fp8_model(const whisper_dims* d, const void* packed8, const char* who) {
+  if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, std::string(who) + ": bf16 models only");
+  if (d->d_model % 256 || d->d_ffn % 256 || d->d_model < 512)
+    return fail(WHISPER_ERR_SHAPE, std::string(who) + ": d_model and d_ffn must be multiples of 256, d_model >= 512");
+  return check_ptrs({packed8}, who);
+}
+
+whisper_status whisper_encode_fp8(const whisper_dims* d, const void* packed, const void* packed8, const float* mel,
+                                  int B, void* enc_out, void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  WH_CHECK(check_fp8_model(d, packed8, "encode_fp8"));
+  return encode_impl(d, packed, packed8, mel, B, enc_out, ws, ws_bytes, stream);
+}
+
+whisper_status whisper_encode_layers_fp8(const whisper_dims* d, const void* packed, const void* packed8,
+                                         const void* h_in, int B, int l0, int l1, int apply_ln_post, void* h_out,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  WH_CHECK(check_fp8_model(d, packed8, "encode_layers_fp8"));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "encode_layers_fp8: batch must be > 0");
+  if (d->n_enc_layers <= 0 || l0 < 0 || l1 < l0 || l1 > d->n_enc_layers)
+    return fail(WHISPER_ERR_SHAPE, "encode_layers_fp8: layer range outside the encoder");
+  WH_CHECK(check_ptrs({packed, h_in, h_out}, "encode_layers_fp8"));
+  const EncWS W = enc_ws(d, B, true);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "encode_layers_fp8"));
+  (void)hipGetLastError();
+  return run_enc_layers(d, packed, layout(d), W, h_in, false, B, l0, l1, apply_ln_post != 0, h_out, ws, S(stream),
+                        packed8);
+}
+
+size_t whisper_packed_weights_fp8_size(const whisper_dims* d) {
+  if (check_dims(d) != WHISPER_OK || d->n_enc_layers <= 0) return 0;
+  return layout8(d).total;
+}
+
+whisper_status whisper_pack_weights_fp8(const whisper_dims* d, const float* const* w, void* packed8, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  WH_CHECK(check_dims(d));
+  WH_CHECK(check_fp8_model(d, packed8, "pack_fp8"));
+  if (d->n_enc_layers <= 0) return fail(WHISPER_ERR_SHAPE, "pack_fp8: no encoder layers");
+  if (!w) return fail(WHISPER_ERR_INVALID_ARG, "pack_fp8: weight table is NULL");
+  WH_CHECK(check_ws(ws, ws_bytes, whisper_fp8_workspace_size(), "pack_fp8"));
+  const int n = weight_count(d);
+  for (int i = 0; i < n; ++i)
+    if (!w[i] || ((uintptr_t)w[i] & 15u)) return fail(WHISPER_ERR_ALIGN, "pack_fp8: weight " + std::to_string(i) + " NULL or not 16-byte aligned");
+  (void)hipGetLastError();
+  const Packed8 P8 = layout8(d);
+  const hipStream_t s = S(stream);
+  const size_t D = d->d_model, F = d->d_ffn;
+  float* sc = at<float>(packed8, P8.scales);
+  // per weight tensor: amax scale (fl32(amax) / 448), then E4M3 codes
+  auto q = [&](const float* src, size_t n_el, uint8_t* dst, float* scale) -> hipError_t {
+    const size_t blocks = (n_el + 255) / 256;
+    hipError_t e = launch_amax(ACT_F32, FP8_E4M3, src, n_el, (float*)ws, (int)std::min<size_t>(blocks, 1024), scale, s);
+    if (e != hipSuccess) return e;
+    return launch_fp8_quantize(ACT_F32, FP8_E4M3, src, n_el, scale, dst, s);
+  };
+  for (int l = 0; l < d->n_enc_layers; ++l) {
+    const int i = 4 + 15 * l;  // logical order: conv1.{w,b}, conv2.{w,b}, then 15 tensors per layer
+    uint8_t* qkv = at<uint8_t>(packed8, P8.qkv[l]);
+    WH_TRY(q(w[i + 2], D * D, qkv, sc + 8 * l + 0));          // attn.query.weight
+    WH_TRY(q(w[i + 4], D * D, qkv + D * D, sc + 8 * l + 1));  // attn.key.weight
+    WH_TRY(q(w[i + 5], D * D, qkv + 2 * D * D, sc + 8 * l + 2));  // attn.value.weight
+    WH_TRY(q(w[i + 11], F * D, at<uint8_t>(packed8, P8.w1[l]), sc + 8 * l + 3));  // mlp.0.weight
+    WH_TRY(q(w[i + 13], D * F, at<uint8_t>(packed8, P8.w2[l]), sc + 8 * l + 4));  // mlp.2.weight
+  }
+  return WHISPER_OK;
+}
+
+whisper_status whisper_gemm_fp8(const uint8_t* a, int M, int K, const float* a_scales, int rows_per_scale,
+                                const uint8_t* w, int N, const float* w_scale, const float* bias, int gelu, void* c,
+                                long ldc, void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(WHISPER_ERR_INVALID_ARG, "gemm_fp8: sizes must be > 0");
+  if (K % 256 || K < 512 || N % 256 || ldc < N || ldc % 8 || rows_per_scale < 256)
+    return fail(WHISPER_ERR_SHAPE, "gemm_fp8: K % 256 == 0, K >= 512, N % 256 == 0, ldc >= N and % 8 == 0, rows_per_scale >= 256");
+  if ((long)M * K > (1L << 31) || (long)N * K > (1L << 31) || (long)M * ldc * 2 > (1L << 31))
+    return fail(WHISPER_ERR_SHAPE, "gemm_fp8: operands and output must be under 2 GB");
+  WH_CHECK(check_ptrs({a, w, c}, "gemm_fp8"));
+  WH_CHECK(check_ptrs4({a_scales, w_scale}, "gemm_fp8"));
+  if (bias && !aligned16(bias)) return fail(WHISPER_ERR_ALIGN, "gemm_fp8: bias not 16-byte aligned");
+  (void)hipGetLastError();
+  GemmParams g = gp(a, K, w, K, M, N, K, bias, c, ldc);
+  g.a_scale = a_scales; g.a_rows_per_scale = rows_per_scale; g.b_scale = w_scale;
+  WH_TRY(launch_gemm_fp8(gelu ? EPI_GELU : EPI_STORE, g, S(stream)));
+  return WHISPER_OK;
 }
 
 whisper_status whisper_cross_kv(const whisper_dims* d, const void* packed, const void* enc_out, int B, void* cross_kv,

@@ -187,6 +187,74 @@ __global__ __launch_bounds__(256) void fp8_dequantize_kernel(const uint8_t* code
   }
 }
 
+// ------------------------------------------------------------------ per-chunk activation quantisation
+// The activation entering an fp8 GEMM site, bf16 [rows, K] with rows in
+// chunks of rows_per_chunk (one 30 s clip each), becomes E4M3 codes with one
+// scale per chunk: scale = fl32(amax of the chunk) / 448 (1 if the chunk is
+// all zero), code = e4m3(fl32(x * fl32(1 / scale))). Pass 1 writes CQ_PARTS
+// partial maxima per chunk; pass 2 reduces them in every workgroup, quantises
+// its slice and the chunk's first workgroup stores the scale.
+constexpr int CQ_PARTS = 64;
+
+__global__ __launch_bounds__(256) void chunk_amax_kernel(const u16* __restrict__ x, long chunk_elems, long total,
+                                                         float* __restrict__ partial) {
+  const int c = blockIdx.y;
+  const long begin = (long)c * chunk_elems, end = min(begin + chunk_elems, total);
+  const long n8 = (end - begin) / 8;
+  float m = 0.f;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)CQ_PARTS * 256) {
+    float v[8];
+    load8(x + begin + i * 8, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  }
+  m = wave_max(m);
+  __shared__ float sm[4];
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[c * CQ_PARTS + blockIdx.x] = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+}
+
+__global__ __launch_bounds__(256) void chunk_quant_kernel(const u16* __restrict__ x, long chunk_elems, long total,
+                                                          const float* __restrict__ partial,
+                                                          float* __restrict__ scales, uint8_t* __restrict__ codes) {
+  const int c = blockIdx.y;
+  __shared__ float s_inv;
+  if (threadIdx.x < 64) {
+    const float m = wave_max(partial[c * CQ_PARTS + threadIdx.x]);
+    if (threadIdx.x == 0) {
+      const float sc = (m > 0.f) ? m / 448.0f : 1.0f;
+      s_inv = 1.0f / sc;
+      if (blockIdx.x == 0) scales[c] = sc;
+    }
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  const long begin = (long)c * chunk_elems, end = min(begin + chunk_elems, total);
+  const long n8 = (end - begin) / 8;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)CQ_PARTS * 256) {
+    float v[8];
+    load8(x + begin + i * 8, v);
+    uint32_t q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = e4m3_encode(v[k] * inv);
+    *(uint2*)(codes + begin + i * 8) = uint2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+  }
+}
+
+hipError_t launch_chunk_quant_fp8(const void* x, long rows, int K, int rows_per_chunk, float* partial,
+                                  float* scales, uint8_t* codes, hipStream_t s) {
+  if (rows <= 0 || K % 8 || rows_per_chunk <= 0) return hipErrorInvalidValue;
+  const int n_chunks = (int)((rows + rows_per_chunk - 1) / rows_per_chunk);
+  const long chunk_elems = (long)rows_per_chunk * K, total = rows * K;
+  dim3 grid(CQ_PARTS, n_chunks);
+  hipLaunchKernelGGL(chunk_amax_kernel, grid, dim3(256), 0, s, (const u16*)x, chunk_elems, total, partial);
+  hipLaunchKernelGGL(chunk_quant_kernel, grid, dim3(256), 0, s, (const u16*)x, chunk_elems, total, partial, scales,
+                     codes);
+  return hipGetLastError();
+}
+
 static int grid_for(size_t n) {
   size_t g = (n + 255) / 256;
   return (int)(g > 8192 ? 8192 : (g < 1 ? 1 : g));

@@ -870,6 +870,171 @@ __global__ __launch_bounds__(512) void gemm_bf16_persist(GemmParams p) {
 #undef WH_OFFS
 }
 
+// ------------------------------------------------------------------ fp8 E4M3 MFMA, 256x256, LDS DMA pipeline
+// The mixed_fp8 sites (showcase page, precision.py card: encoder QKV and FFN
+// in fp8 E4M3; gemm_hopper.cu card: FP8 E4M3 GEMM). A [M, K] and B [N, K] are
+// E4M3 codes, K-contiguous; C = epi(acc * sa[m / a_rows_per_scale] * sb + bias)
+// in bf16. The memory pipeline is the bf16 LDS-DMA kernel's byte for byte
+// (one 256x256 tile per workgroup, 8 waves, 4-stage ring): a stage holds 64
+// bytes of every tile row, which is 64 fp8 values instead of 32 bf16, and one
+// 32x32x64 fp8 MFMA per 32x32 block consumes exactly one stage in the MFMA
+// time the bf16 kernel spends on one stage, so the same traffic feeds twice
+// the FLOPs. The launcher passes K and the row strides in 2-byte units
+// (bytes / 2) so that the address computations are the bf16 kernel's.
+// A lane's MFMA operand is 32 bytes of one row: chunks 2g, 2g+1 (g = lane / 32)
+// of row lane % 32, for A and B alike; the K order inside the MFMA is the same
+// for both operands, so any K permutation it applies cancels in the products.
+// B row slot i of a 32-row block holds tile column 16 ((i / 4) % 2) + 4 (i / 8)
+// + i % 4, so the 16 outputs a lane holds (rows 8 (v / 4) + 4 g + v % 4 of the
+// MFMA result) are 16 consecutive columns g*16 .. g*16 + 15: two 16-byte stores.
+// Requirements (checked by the launcher): K % 256 == 0, K >= 512, N % 256 == 0,
+// lda, ldb % 2 == 0, ldc % 8 == 0, a_rows_per_scale >= 256.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ int fp8_bcol(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_fp8_dma(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) u16 st0[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st1[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st2[DSTAGE];
+  __shared__ __attribute__((aligned(1024))) u16 st3[DSTAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int tiles_n = p.N / TB2;
+  const int tiles_m = (p.M + TB2 - 1) / TB2;
+  int tm, tn;
+  tile_order_grouped<4>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const u16* A = (const u16*)p.A;
+  const u16* B = (const u16*)p.B;
+  const int m0 = tm * TB2, n0 = tn * TB2;
+
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 3) & 3);
+  const u16* ga0 = A + (long)min(m0 + wave * 16 + lr, p.M - 1) * p.lda + lc * 8;
+  const u16* ga1 = A + (long)min(m0 + (wave + 8) * 16 + lr, p.M - 1) * p.lda + lc * 8;
+  const u16* gb0 = B + (long)(n0 + wave * 16 + lr) * p.ldb + lc * 8;
+  const u16* gb1 = B + (long)(n0 + (wave + 8) * 16 + lr) * p.ldb + lc * 8;
+  const int la0 = wave * 16 * DBK, la1 = (wave + 8) * 16 * DBK;
+  const int lb0 = TB2 * DBK + wave * 16 * DBK, lb1 = TB2 * DBK + (wave + 8) * 16 * DBK;
+#define WH_ISSUE(S, k)                                                                         \
+  dma16(ga0 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + la0)));                        \
+  dma16(ga1 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + la1)));                        \
+  dma16(gb0 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + lb0)));                        \
+  dma16(gb1 + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + lb1)));
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int fr = lane & 31, g = lane >> 5;
+  const int nk = p.K / DBK;
+  i32x8 a0[4], b0[2], a1[4], b1[2];
+#define WH_FRAG(S, ROW, DST)                                                       \
+  {                                                                                \
+    const uint4 lo_ = *(const uint4*)((S) + dswz((ROW), 2 * g));                   \
+    const uint4 hi_ = *(const uint4*)((S) + dswz((ROW), 2 * g + 1));               \
+    DST = i32x8{(int)lo_.x, (int)lo_.y, (int)lo_.z, (int)lo_.w,                     \
+                (int)hi_.x, (int)hi_.y, (int)hi_.z, (int)hi_.w};                    \
+  }
+#define WH_READ(S, AF, BF)                                                                 \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                            \
+    WH_FRAG((S) + TB2 * DBK, wn * 64 + 32 * j + fp8_bcol(fr), BF[j])                        \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
+    WH_FRAG((S), wm * 128 + i * 32 + fr, AF[i])
+  // E4M3 both operands (format 0), unit block scales (E8M0 127 = 2^0)
+#define WH_MFMA(AF, BF)                                                                    \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                          \
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(BF[j], AF[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+#define WH_SYNC(n)                                                                             \
+  {                                                                                            \
+    WH_WAIT_VM_LGKM0(n);                                                                       \
+    __builtin_amdgcn_s_barrier();                                                              \
+  }
+#define WH_STEP(WAITN, REFILL, SREFILL, KREFILL, SN, AC, BC, AN, BN)                           \
+  WH_SYNC(WAITN)                                                                               \
+  if (REFILL) { WH_ISSUE(SREFILL, KREFILL) }                                                   \
+  WH_READ(SN, AN, BN)                                                                          \
+  WH_MFMA(AC, BC)
+
+  WH_ISSUE(st0, 0)
+  WH_ISSUE(st1, DBK)
+  WH_ISSUE(st2, 2 * DBK)
+  WH_SYNC(8)
+  WH_ISSUE(st3, 3 * DBK)
+  WH_READ(st0, a0, b0)
+  int kt = 0;
+  for (; kt + 8 <= nk; kt += 4) {
+    WH_STEP(8, true, st0, (kt + 4) * DBK, st1, a0, b0, a1, b1)
+    WH_STEP(8, true, st1, (kt + 5) * DBK, st2, a1, b1, a0, b0)
+    WH_STEP(8, true, st2, (kt + 6) * DBK, st3, a0, b0, a1, b1)
+    WH_STEP(8, true, st3, (kt + 7) * DBK, st0, a1, b1, a0, b0)
+  }
+  WH_STEP(8, false, st0, 0, st1, a0, b0, a1, b1)
+  WH_STEP(4, false, st0, 0, st2, a1, b1, a0, b0)
+  WH_STEP(0, false, st0, 0, st3, a0, b0, a1, b1)
+  WH_MFMA(a1, b1)
+#undef WH_FRAG
+#undef WH_READ
+#undef WH_MFMA
+#undef WH_SYNC
+#undef WH_STEP
+#undef WH_ISSUE
+  // epilogue: per-row activation scale (a tile spans at most two scale
+  // groups), weight scale, bias, activation, bf16, two 16-byte stores per
+  // 32x32 block
+  const int rps = p.a_rows_per_scale;
+  const int c0 = m0 / rps, c1 = min(m0 + TB2 - 1, p.M - 1) / rps, mb = (c0 + 1) * rps;
+  const float s_w = p.b_scale[0], s_lo = p.a_scale[c0] * s_w, s_hi = p.a_scale[c1] * s_w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + fr;
+    if (m >= p.M) continue;
+    const float sm = (m >= mb) ? s_hi : s_lo;
+    u16* crow = (u16*)p.C + (long)m * p.ldc + n0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cl = wn * 64 + 32 * j + 16 * g;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float4 bq = p.bias ? *(const float4*)(p.bias + n0 + cl + 8 * h + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+          v[4 * q + 0] = acc[i][j][8 * h + 4 * q + 0] * sm + bq.x;
+          v[4 * q + 1] = acc[i][j][8 * h + 4 * q + 1] * sm + bq.y;
+          v[4 * q + 2] = acc[i][j][8 * h + 4 * q + 2] * sm + bq.z;
+          v[4 * q + 3] = acc[i][j][8 * h + 4 * q + 3] * sm + bq.w;
+        }
+        if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = gelu_erf(v[q]);
+        }
+        *(uint4*)(crow + cl + 8 * h) = uint4{f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7])};
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_fp8(Epi epi, const GemmParams& q, hipStream_t s) {
+  // K and strides in bytes here; the kernel takes them in 2-byte units
+  if (q.K % 256 || q.K < 512 || q.N % TB2 || q.lda % 2 || q.ldb % 2 || q.ldc % 8 || q.batch != 1 ||
+      q.a_rows_per_scale < TB2 || !q.a_scale || !q.b_scale || q.M <= 0)
+    return hipErrorInvalidValue;
+  if ((long)q.M * q.lda > (1L << 31) || (long)q.N * q.ldb > (1L << 31) || (long)q.M * q.ldc * 2 > (1L << 31))
+    return hipErrorInvalidValue;
+  if (epi != EPI_STORE && epi != EPI_GELU) return hipErrorInvalidValue;
+  GemmParams p = q;
+  p.K = q.K / 2; p.lda = q.lda / 2; p.ldb = q.ldb / 2;
+  dim3 grid(((p.M + TB2 - 1) / TB2) * (p.N / TB2));
+  if (epi == EPI_GELU) hipLaunchKernelGGL(gemm_fp8_dma<EPI_GELU>, grid, dim3(512), 0, s, p);
+  else hipLaunchKernelGGL(gemm_fp8_dma<EPI_STORE>, grid, dim3(512), 0, s, p);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ bf16 MFMA, 256x256, LDS DMA pipeline, 4 waves
 // The same 4-stage LDS ring (BK = 32) fed by direct global->LDS loads, with
 // 256 threads = 2x2 waves of 128x128 sub-tiles (8x8 MFMA 16x16x32, 256 fp32

@@ -40,9 +40,14 @@ struct GemmParams {
   // tiled-kernel choice for measurement: 0 automatic, 1 128x128, 2 256x256/8 waves, 3 256x256/4 waves,
   // 4 256x256 with the LDS DMA pipeline
   int variant;
+  // fp8 GEMM (launch_gemm_fp8): C = epi(acc * a_scale[m / a_rows_per_scale] * b_scale[0] + bias)
+  const float* a_scale; int a_rows_per_scale; const float* b_scale;
 };
 
 hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
+// fp8 E4M3 A [M, K] and B [N, K] codes (K, lda, ldb in bytes), bf16 C;
+// EPI_STORE or EPI_GELU.
+hipError_t launch_gemm_fp8(Epi epi, const GemmParams& p, hipStream_t s);
 // Skinny path for decode (M <= 128): weights streamed once, K split over waves.
 hipError_t launch_gemm_skinny(ActType t, Epi epi, const GemmParams& p, hipStream_t s);
 
@@ -92,6 +97,10 @@ hipError_t launch_fp8_quantize(ActType t, int fmt, const void* x, size_t n, cons
                                hipStream_t s);
 hipError_t launch_fp8_dequantize(ActType t, int fmt, const uint8_t* codes, size_t n, const float* scale, void* y,
                                  hipStream_t s);
+// bf16 x [rows, K] -> E4M3 codes with one amax scale per chunk of
+// rows_per_chunk rows; partial: 64 floats per chunk; scales: one per chunk.
+hipError_t launch_chunk_quant_fp8(const void* x, long rows, int K, int rows_per_chunk, float* partial,
+                                  float* scales, uint8_t* codes, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 // Encoder self-attention over the packed QKV [B*T, 3*H*64] -> out [B*T, H*64].

@@ -22,8 +22,10 @@ def _empty_bytes(n, device):
 class Whisper:
     """Packed weights plus per-call workspaces for one model shape."""
 
-    def __init__(self, dims, logical_weights, device="cuda"):
-        """logical_weights: fp32 device tensors in the ABI's canonical order."""
+    def __init__(self, dims, logical_weights, device="cuda", fp8_encoder=False):
+        """logical_weights: fp32 device tensors in the ABI's canonical order.
+        fp8_encoder: also pack the E4M3 weights of the mixed_fp8 encoder sites
+        (encode_fp8 / encode_layers_fp8)."""
         self.dims = dims
         self.device = torch.device(device)
         n = L.whisper_weight_count(dims)
@@ -34,6 +36,11 @@ class Whisper:
                 raise ValueError("logical weights must be contiguous fp32 device tensors")
         self.packed = _empty_bytes(L.whisper_packed_weights_size(dims), self.device)
         L.whisper_pack_weights(dims, logical_weights, self.packed)
+        self.packed8 = None
+        if fp8_encoder:
+            self.packed8 = _empty_bytes(L.whisper_packed_weights_fp8_size(dims), self.device)
+            ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=self.device)
+            L.whisper_pack_weights_fp8(dims, logical_weights, self.packed8, ws, ws.numel())
         self._ws = None
 
     def workspace(self, batch, which):
@@ -74,6 +81,23 @@ class Whisper:
         ws, nb = self.workspace(B, L.WS_ENCODE)
         L.whisper_encode(self.dims, self.packed, mel, B, enc, ws, nb)
         return enc
+
+    def encode_fp8(self, mel, out=None):
+        """encode with the mixed_fp8 sites in E4M3 (needs fp8_encoder=True)."""
+        B = mel.shape[0]
+        enc = out if out is not None else torch.empty(B, self.dims.n_audio_ctx, self.dims.d_model,
+                                                      dtype=act_dtype(self.dims), device=self.device)
+        ws, nb = self.workspace(B, L.WS_ENCODE_FP8)
+        L.whisper_encode_fp8(self.dims, self.packed, self.packed8, mel, B, enc, ws, nb)
+        return enc
+
+    def encode_layers_fp8(self, h, layer_begin, layer_end, ln_post=False, out=None):
+        B = h.shape[0]
+        o = out if out is not None else torch.empty_like(h)
+        ws, nb = self.workspace(B, L.WS_ENCODE_FP8)
+        L.whisper_encode_layers_fp8(self.dims, self.packed, self.packed8, h, B, layer_begin, layer_end, ln_post, o,
+                                    ws, nb)
+        return o
 
     def encode_layers(self, h, layer_begin, layer_end, ln_post=False, out=None):
         B = h.shape[0]

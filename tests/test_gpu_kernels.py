@@ -270,3 +270,45 @@ def test_logmel_chunked_long_recording(stride):
         e = rel_err(host(mel)[i], ref[i])
         say(f"  chunk {i} (samples {plan[i][0]}..+{plan[i][1]}): rel err {e:.2e}")
         assert e < 1e-3
+
+
+# ------------------------------------------------------------------ fp8 GEMM (mixed_fp8 sites)
+@pytest.mark.parametrize("gelu", [False, True])
+def test_gemm_fp8_codes_against_exact_products(gelu):
+    """whisper_gemm_fp8 on seeded E4M3 codes: 700 rows (3 row tiles, ragged),
+    512 columns (2 tiles), K = 1280, row scales in groups of 300 rows (groups
+    cross tile edges), a weight scale and a bias, against the exact products
+    of the codes' values (fp64), scaled, biased, GELU'd, then bf16."""
+    say(f"fp8 GEMM 700x512x1280, gelu={gelu}")
+    M, N, K, rps = 700, 512, 1280, 300
+    g = torch.Generator().manual_seed(11)
+    a = torch.randint(0, 256, (M, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    w = torch.randint(0, 256, (N, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    a[(a & 0x7F) == 0x7F] = 0  # no NaN codes
+    w[(w & 0x7F) == 0x7F] = 0
+    sa = (torch.rand(3, generator=g) * 0.01 + 0.001).float()
+    sw = (torch.rand(1, generator=g) * 0.01 + 0.001).float()
+    bias = torch.randn(N, generator=g).float()
+    c = torch.full((M, N + 8), float("nan"), dtype=torch.bfloat16)
+    dev = [t.to(DEV) for t in (a, w, sa, sw, bias, c)]
+    L.whisper_gemm_fp8(dev[0], M, K, dev[2], rps, dev[1], N, dev[3], dev[4], gelu, dev[5], N + 8)
+    torch.cuda.synchronize()
+    got = dev[5].float().cpu().numpy()
+    va, vw = O.e4m3_value(a.numpy()), O.e4m3_value(w.numpy())
+    scale = np.float32(sa.numpy()[np.arange(M) // rps])[:, None].astype(np.float64) * float(sw[0])
+    ref = (va @ vw.T) * scale + bias.numpy().astype(np.float64)
+    if gelu:
+        ref = O.gelu(ref)
+    assert np.all(np.isnan(got[:, N:])), "columns past N must stay untouched"
+    err = np.abs(got[:, :N] - ref)
+    # fp32 summation of K exact products: |error| <= K 2^-24 sum |terms| (the
+    # textbook bound for any order), doubled for the scale and bias roundings
+    # and GELU's slope; then one bf16 rounding of the result
+    terms = (np.abs(va) @ np.abs(vw).T) * scale
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * K * 2.0 ** -24 * (terms + np.abs(bias.numpy())) + 1e-6
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{len(bad)} outputs beyond the bound, first {bad[:3].tolist()}: "
+                           f"got {got[tuple(bad[0])]}, ref {ref[tuple(bad[0])]}, bound {bound[tuple(bad[0])]}")
+    # typical error is far inside the worst-case bound
+    assert np.median(err / (np.abs(ref) + 1e-3)) < 2.0 ** -8
+

@@ -24,9 +24,9 @@ def _gpu():
     need_gpu()
 
 
-def model_for(dims, ln_random=False):
+def model_for(dims, ln_random=False, fp8_encoder=False):
     W = gen_weights(DEV, dims, ln_random=ln_random)
-    m = Whisper(dims, list(W.values()))
+    m = Whisper(dims, list(W.values()), fp8_encoder=fp8_encoder)
     torch.cuda.synchronize()
     return m, W
 
@@ -51,6 +51,34 @@ def test_encoder_layer_large_v3(ln_post):
     e = rel_err(host(out)[0], ref)
     say(f"  rel err {e:.3e}")
     assert e < TOL
+
+
+def test_encoder_layer_mixed_fp8_large_v3_two_chunks():
+    """One large-v3 encoder layer with the mixed_fp8 sites (query, key, value,
+    fc1, fc2 in E4M3; per-tensor weight scales, per-chunk activation scales)
+    through whisper_encode_layers_fp8, two chunks (the 1500-row chunks cross
+    256-row tiles), against the oracle's mixed_fp8 layer on each chunk. The
+    two sides quantise activations that differ by bf16 rounding, so some codes
+    differ by one step; the tolerance is the fp8 one of the decode tests."""
+    dims = CONFIGS["v3_layer"]
+    say("mixed_fp8 encoder layer large-v3 B=2")
+    m, W = model_for(dims, ln_random=True, fp8_encoder=True)
+    h = gen_normal(DEV, (2, 1500, 1280), dims.cfg_id, 7, bf16=True).to(torch.bfloat16)
+    out = m.encode_layers_fp8(h, 0, 1)
+    out2 = m.encode_layers_fp8(h, 0, 1)
+    bf = m.encode_layers(h, 0, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "fp8 encoder layer is not deterministic"
+    Wh = host_weights(W)
+    for b in range(2):
+        x = host(h)[b]
+        ref = O.encoder_layers_mixed_fp8(x, Wh, dims.n_heads, [0], ln_post=False)
+        e = rel_err(host(out)[b], ref)
+        # the fp8 result differs from the bf16 layer by the fp8 rounding, not more
+        e_bf = rel_err(host(out)[b], host(bf)[b])
+        say(f"  chunk {b}: rel err vs oracle {e:.3e}, vs bf16 path {e_bf:.3e}")
+        assert e < TOL
+        assert e_bf < 0.1
 
 
 def _encoder_from_audio(dims, B, chunks):
