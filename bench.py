@@ -22,6 +22,7 @@ import time
 
 AUDIO_S = 30.0
 HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -37,6 +38,8 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring the MFMA and HBM ceilings")
     ap.add_argument("--no-long-form", action="store_true",
                     help="skip the 45-minute long-form leg (turbo shape, batch 90; reported apart from value)")
+    ap.add_argument("--no-fp8-encoder", action="store_true",
+                    help="skip the extra step with the mixed_fp8 encoder sites (E4M3 QKV and FFN GEMMs)")
     ap.add_argument("--no-fp8-cross", action="store_true",
                     help="skip the extra step with fp8 e4m3 cross-attention K/V (reported apart from value)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -105,7 +108,7 @@ def main():
 
     t0 = time.time()
     W = gen_weights(DEV, dims)
-    model = Whisper(dims, list(W.values()))
+    model = Whisper(dims, list(W.values()), fp8_encoder=not args.no_fp8_encoder)
     torch.cuda.synchronize()
     del W
     torch.cuda.empty_cache()
@@ -193,6 +196,10 @@ def main():
     peaks = None if args.no_peaks else measured_peaks(L, torch)
     lf = None if args.no_long_form else long_form(L, torch, Whisper, DecodeState)
 
+    fp8e = None
+    if not args.no_fp8_encoder:
+        fp8e = fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch,
+                                np)
     fp8x = {}
     if not args.no_fp8_cross:
         for fmt in ("e4m3", "e5m2"):
@@ -240,6 +247,11 @@ def main():
             k["peak_measured"], k["frac_of_measured"] = ref, round(k["achieved"] / ref, 4)
     if lf is not None:
         result["long_form"] = lf
+    if fp8e is not None:
+        if peaks is not None:
+            k = fp8e["encoder_ffn1_gemm_fp8"]
+            k["peak_measured_bf16"] = peaks["mfma_bf16_tflops"]
+        result["fp8_encoder"] = fp8e
     for fmt, leg in fp8x.items():
         if peaks is not None:
             xc = leg["cross_attention"]
@@ -402,6 +414,60 @@ def measured_peaks(L, torch):
     log(f"measured peaks: bf16 MFMA {mfma:.0f} TFLOP/s, HBM read {read:.0f} GB/s")
     return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(read, 1),
             "how": "register-resident MFMA 16x16x32 bf16 loop, 16384 waves; 16-byte streaming read of 4 GiB"}
+
+
+def fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np):
+    """One more full step with the encoder's mixed_fp8 sites (query, key,
+    value, fc1, fc2 as E4M3 GEMMs with per-tensor weight and per-chunk
+    activation amax scales), the rest unchanged. Reported apart from `value`:
+    the configured workload is bf16."""
+    def step(ev=None):
+        if ev: ev[0].record()
+        model.logmel(audio, out=mel)
+        model.encode_fp8(mel, out=enc)
+        if ev: ev[1].record()
+        model.cross_kv(enc, out=ckv)
+        state.lengths.copy_(lengths0)
+        for t in range(TD):
+            model.decode_step(state, tokens[t], logits)
+        if ev: ev[2].record()
+
+    step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t0 = time.perf_counter()
+    step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(state.dev_error[0].item()) == 0
+    # the fc1 site (E4M3 GEMM + bias + GELU) with the event hook, in one more encoder pass
+    n = 32
+    s = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for x in s + e:
+        x.record()
+    torch.cuda.synchronize()
+    L.whisper_profile_arm(L.PROF_ENCODER_FFN1, s, e)
+    t1 = time.perf_counter()
+    model.encode_fp8(mel, out=enc)
+    torch.cuda.synchronize()
+    enc_wall = time.perf_counter() - t1
+    n_rec = L.whisper_profile_disarm()
+    ms = float(np.mean([s[i].elapsed_time(e[i]) for i in range(n_rec)]))
+    M, d, F = B * dims.n_audio_ctx, dims.d_model, dims.d_ffn
+    fl = 2.0 * M * d * F
+    tf = fl / (ms * 1e-3) / 1e12
+    log(f"fp8 encoder step: {wall * 1e3:.1f} ms, encode {ev[0].elapsed_time(ev[1]):.1f} ms, "
+        f"fc1 fp8 GEMM {ms * 1e3:.0f} us ({tf:.0f} TFLOP/s)")
+    return {"ms_per_step": round(wall * 1e3, 3), "rtfx": round(B * AUDIO_S / wall, 2),
+            "stage_ms": {"logmel_encode": round(ev[0].elapsed_time(ev[1]), 3),
+                         "cross_kv_decode": round(ev[1].elapsed_time(ev[2]), 3)},
+            "encode_only_ms": round(enc_wall * 1e3, 3),
+            "encoder_ffn1_gemm_fp8": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                                      "avg_launch_us": round(ms * 1e3, 1), "launches": n_rec,
+                                      "shape": f"[{M},{d}]x[{d},{F}] E4M3 + scales + bias + GELU"},
+            "note": "mixed_fp8 preset sites in E4M3 (encoder query/key/value, fc1, fc2); not the configured workload"}
 
 
 def fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np,
