@@ -182,3 +182,38 @@ def test_plan_batch_host_logic():
     with pytest.raises(L.WhisperError) as e:
         L.whisper_plan_batch(full, 24 * G, 5000)
     assert e.value.status == 2
+
+
+def test_fp8_encoder_entry_validation():
+    """Host checks of the mixed_fp8 entry points (no launch happens)."""
+    v3 = CONFIGS["v3_decode"].with_(n_enc_layers=32)
+    tiny = CONFIGS["tiny_f32"]
+    # packed size: per layer 3 d^2 + 2 d f bytes of codes (256-aligned), then 8 scales per layer
+    d, f = 1280, 5120
+    per = [(3 * d * d + 255) // 256 * 256, (f * d + 255) // 256 * 256, (d * f + 255) // 256 * 256]
+    assert L.whisper_packed_weights_fp8_size(v3) == 32 * sum(per) + (32 * 8 * 4 + 255) // 256 * 256
+    assert L.whisper_packed_weights_fp8_size(CONFIGS["v3_decode"]) == 0  # no encoder
+    ws = L.whisper_workspace_size(v3, 2, L.WS_ENCODE_FP8)
+    assert ws > L.whisper_workspace_size(v3, 2, L.WS_ENCODE)
+    with pytest.raises(L.WhisperError) as e:  # fp32 model
+        L.whisper_encode_fp8(tiny, 16, 16, 16, 1, 16, 16, 1 << 40, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(L.WhisperError) as e:  # workspace too small
+        L.whisper_encode_fp8(v3, 16, 16, 16, 2, 16, 16, ws - 1, stream=0)
+    assert e.value.status == 5
+    with pytest.raises(L.WhisperError) as e:  # layer range
+        L.whisper_encode_layers_fp8(v3, 16, 16, 16, 1, 3, 40, False, 16, 16, 1 << 40, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(L.WhisperError) as e:  # pack workspace below whisper_fp8_workspace_size()
+        L.whisper_pack_weights_fp8(v3, [16] * L.whisper_weight_count(v3), 16, 16, 8, stream=0)
+    assert e.value.status == 5
+    # whisper_gemm_fp8 shape rules: K % 256, K >= 512, N % 256, ldc, rows_per_scale
+    ok = dict(M=100, K=512, rps=256, N=256, ldc=256)
+    for bad in (dict(K=384), dict(K=256), dict(N=200), dict(ldc=200), dict(ldc=260), dict(rps=100)):
+        a = {**ok, **bad}
+        with pytest.raises(L.WhisperError) as e:
+            L.whisper_gemm_fp8(16, a["M"], a["K"], 16, a["rps"], 16, a["N"], 16, None, False, 16, a["ldc"], stream=0)
+        assert e.value.status == 2, bad
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_gemm_fp8(16, 0, 512, 16, 256, 16, 256, 16, None, False, 16, 256, stream=0)
+    assert e.value.status == 1
