@@ -312,3 +312,35 @@ def test_gemm_fp8_codes_against_exact_products(gelu):
     # typical error is far inside the worst-case bound
     assert np.median(err / (np.abs(ref) + 1e-3)) < 2.0 ** -8
 
+
+
+@pytest.mark.parametrize("N,K,gelu", [(5120, 1280, True), (1280, 5120, False)])
+def test_gemm_fp8_full_encoder_shape_sampled_rows(N, K, gelu):
+    """whisper_gemm_fp8 at the encoder's full batch-64 shapes (96000 rows:
+    fc1 5120x1280 + GELU, fc2 1280x5120), one scale per 1500-row chunk as the
+    encoder runs it; one sampled row per chunk checked against the exact
+    products of its codes, inside the fp32 summation bound."""
+    say(f"fp8 GEMM 96000x{N}x{K}, gelu={gelu}, sampled rows")
+    M, rps = 96000, 1500
+    g = torch.Generator().manual_seed(12)
+    a = torch.randint(0, 256, (M, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    w = torch.randint(0, 256, (N, K), generator=g, dtype=torch.int32).to(torch.uint8)
+    a[(a & 0x7F) == 0x7F] = 0
+    w[(w & 0x7F) == 0x7F] = 0
+    sa = (torch.rand(M // rps, generator=g) * 0.01 + 0.001).float()
+    sw = (torch.rand(1, generator=g) * 0.01 + 0.001).float()
+    bias = torch.randn(N, generator=g).float()
+    dev = [t.to(DEV) for t in (a, w, sa, sw, bias)]
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    L.whisper_gemm_fp8(dev[0], M, K, dev[2], rps, dev[1], N, dev[3], dev[4], gelu, c, N)
+    torch.cuda.synchronize()
+    rows = np.array([ch * rps + (ch * 37) % rps for ch in range(M // rps)] + [M - 1])
+    got = c[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    va, vw = O.e4m3_value(a.numpy()[rows]), O.e4m3_value(w.numpy())
+    scale = np.float32(sa.numpy()[rows // rps])[:, None].astype(np.float64) * float(sw[0])
+    ref = (va @ vw.T) * scale + bias.numpy().astype(np.float64)
+    if gelu:
+        ref = O.gelu(ref)
+    terms = (np.abs(va) @ np.abs(vw).T) * scale
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * K * 2.0 ** -24 * (terms + np.abs(bias.numpy())) + 1e-6
+    assert np.all(np.abs(got - ref) <= bound)
