@@ -427,7 +427,8 @@ def encoder(mel, W, n_heads, n_layers):
 # one per weight tensor (query, key, value, fc1, fc2: fl32(amax) / 448), and
 # one per activation tensor at each site, taken over one chunk's activation
 # (one 30 s clip, so a chunk's result does not depend on the batch it runs
-# in): fl32(amax) / 448. The product sums value(code_x) * value(code_w) and
+# in): fl32(amax) / 448. That activation is the bfloat16 tensor the
+# Endpoints post's inference stack computes ("Inference Stack"). The product sums value(code_x) * value(code_w) and
 # multiplies by both scales; the bias is added after.
 
 def fp8_linear(x, w, b, sx, sw):
@@ -438,11 +439,23 @@ def fp8_linear(x, w, b, sx, sw):
     return y if b is None else y + b
 
 
+def bf16_round(x):
+    """x rounded to bfloat16 (through fp32, round to nearest even), as float64."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
 def _site(x, w, b, fp8):
-    """One mixed_fp8 matmul site: fp8 with amax scales, or the plain linear."""
+    """One mixed_fp8 matmul site: fp8 with amax scales, or the plain linear.
+    The activation that reaches a site is a bfloat16 tensor (Endpoints post,
+    "Inference Stack": activations are computed in bfloat16), so the fp8 form
+    takes its amax and codes from x rounded to bf16; the weights are quantised
+    from their fp32 values."""
     if not fp8:
         return linear(x, w, b)
-    return fp8_linear(x, w, b, e4m3_scale_from_amax(x), e4m3_scale_from_amax(w))
+    xb = bf16_round(x)
+    return fp8_linear(xb, w, b, e4m3_scale_from_amax(xb), e4m3_scale_from_amax(w))
 
 
 def encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8=True):

@@ -74,13 +74,24 @@ def test_mixed_fp8_sites_use_per_tensor_amax_scales():
     W = _tiny_weights(rng, d=64, f=256)
     x = rng.standard_normal((30, 64))
     p = "encoder.blocks.1."
-    a = O.layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
+    a = O.bf16_round(O.layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"]))
     s = O.e4m3_scale_from_amax
     q = O.fp8_linear(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], s(a), s(W[p + "attn.query.weight"]))
     k = O.fp8_linear(a, W[p + "attn.key.weight"], None, s(a), s(W[p + "attn.key.weight"]))
     v = O.fp8_linear(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], s(a), s(W[p + "attn.value.weight"]))
     h = x + O.linear(O.attention(q, k, v, 2), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
-    m = O.layer_norm(h, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
-    g = O.gelu(O.fp8_linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], s(m), s(W[p + "mlp.0.weight"])))
+    m = O.bf16_round(O.layer_norm(h, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"]))
+    g = O.bf16_round(O.gelu(O.fp8_linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], s(m),
+                                         s(W[p + "mlp.0.weight"]))))
     out = h + O.fp8_linear(g, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], s(g), s(W[p + "mlp.2.weight"]))
     assert np.array_equal(O.encoder_layer_mixed_fp8(x, W, 1, 2), out)
+
+
+def test_bf16_round_matches_torch_and_keeps_grid_values():
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(100000) * sc for sc in (1e-3, 1.0, 300.0)])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(x), ref)
+    g = O.e4m3_value(np.arange(127))  # every e4m3 value is a bf16 value
+    assert np.array_equal(O.bf16_round(g), g)
+
