@@ -504,17 +504,19 @@ def cross_kv_fp8(cross, scales, fmt="e4m3"):
     preset puts the cross-attention site in fp8, there in E5M2 for range;
     fp8_quantize.cu card: E4M3 and E5M2 codes with a per-tensor scale).
     fmt picks the format, "e4m3" or "e5m2", with one scale per (layer, K|V)
-    tensor either way.
+    tensor either way. The K and V being quantised are the bfloat16 tensors
+    the inference stack computes (Endpoints post, "Inference Stack":
+    activations in bfloat16), so they are rounded to bf16 first.
 
     cross: list over layers of (K, V), each an array [B, H, T, dh] or a dict
     b -> [H, T, dh]; scales: [L, 2]. Returns the same structure holding
-    dequantize(quantize(x, s), s) in the chosen format."""
+    dequantize(quantize(bf16(x), s), s) in the chosen format."""
     quant, dequant, _ = FP8_FORMATS[fmt]
 
     def q(x, s):
         if isinstance(x, dict):
-            return {b: dequant(quant(v, s), s) for b, v in x.items()}
-        return dequant(quant(x, s), s)
+            return {b: dequant(quant(bf16_round(v), s), s) for b, v in x.items()}
+        return dequant(quant(bf16_round(x), s), s)
     return [(q(k, scales[layer][0]), q(v, scales[layer][1])) for layer, (k, v) in enumerate(cross)]
 
 
