@@ -81,6 +81,24 @@ def test_encoder_layer_mixed_fp8_large_v3_two_chunks():
         assert e_bf < 0.1
 
 
+def test_encoder_layer_mixed_fp8_full_batch_sampled_chunks():
+    """The mixed_fp8 layer at the bench's batch of 64 chunks (the per-chunk
+    amax and quantisation grids at full size, 96000-row fp8 GEMMs), the first
+    and last chunk against the oracle's mixed_fp8 layer."""
+    dims = CONFIGS["v3_layer"]
+    say("mixed_fp8 encoder layer large-v3 B=64, chunks 0 and 63")
+    m, W = model_for(dims, ln_random=True, fp8_encoder=True)
+    h = gen_normal(DEV, (64, 1500, 1280), dims.cfg_id, 8, bf16=True).to(torch.bfloat16)
+    out = m.encode_layers_fp8(h, 0, 1)
+    torch.cuda.synchronize()
+    Wh = host_weights(W)
+    for b in (0, 63):
+        ref = O.encoder_layers_mixed_fp8(host(h[b]), Wh, dims.n_heads, [0], ln_post=False)
+        e = rel_err(host(out[b]), ref)
+        say(f"  chunk {b}: rel err vs oracle {e:.3e}")
+        assert e < TOL
+
+
 def _encoder_from_audio(dims, B, chunks):
     m, W = model_for(dims)
     audio = gen_audio_tones(DEV, dims.cfg_id, B)
