@@ -259,7 +259,7 @@ def main():
             xc["frac_of_measured"] = round(xc["achieved"] / peaks["hbm_read_gbs"], 4)
         result["fp8_cross_kv" if fmt == "e4m3" else "fp8_cross_kv_e5m2"] = leg
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(dims, audio, lengths0, tokens, state, np, torch)
+        result["cpu_baseline"] = cpu_baseline(dims, audio, lengths0, tokens, state, np, torch, prefill_max)
     print(json.dumps(result))
 
 
@@ -530,7 +530,7 @@ def fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0,
             "note": f"{fmt} cross-attention K/V, one amax scale per layer and K|V; not the configured workload"}
 
 
-def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch):
+def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch, prefill_max):
     """The oracle, untouched, on a bounded sample of the same workload: chunk 0
     through log-mel, the 32-layer encoder and cross K/V, then N_DEC of its 224
     decode steps (batch 1); decode time is scaled to 224 steps."""
@@ -541,7 +541,7 @@ def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     O = importlib.import_module("oracle.whisper_oracle")
-    from workload import gen_weights
+    from workload import gen_prefill_kv, gen_weights
     N_DEC = 8
     W = {k: v.double().cpu().numpy() for k, v in gen_weights("cuda", dims).items()}
     H, Ld = dims.n_heads, dims.n_dec_layers
@@ -552,9 +552,17 @@ def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch):
     cr = O.cross_kv(e, W, H, Ld)
     t_front = time.perf_counter() - t
     cross = [({0: k}, {0: v}) for k, v in cr]
-    codes = state.kv_cache[:, :, 0].cpu().numpy()
-    cache = [[{0: codes[l, kv].copy()} for kv in range(2)] for l in range(Ld)]
-    sc = state.kv_scales.cpu().numpy()
+    # row 0's prefilled cache from the seeded prefill values, through the
+    # oracle's own scale and codec
+    cap = state.kv_cache.shape[4]
+    cache = [[{0: np.zeros((H, cap, 64), np.uint8)} for kv in range(2)] for l in range(Ld)]
+    sc = np.ones((Ld, 2), np.float32)
+    for l in range(Ld):
+        for kv in range(2):
+            x = gen_prefill_kv("cuda", dims.cfg_id, l, kv, audio.shape[0], H, prefill_max)
+            sc[l, kv] = O.e4m3_scale_from_amax(np.array([x.abs().max().item()], np.float32))
+            cache[l][kv][0][:, :prefill_max] = O.e4m3_quantize(x[0].cpu().numpy(), sc[l, kv])
+            del x
     tok = tokens.cpu().numpy()
     length = np.array([int(lengths0[0].item())])
     t = time.perf_counter()
@@ -564,7 +572,7 @@ def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch):
     t_dec = (time.perf_counter() - t) * (tokens.shape[0] / N_DEC)
     total = t_front + t_dec
     return {"value": round(AUDIO_S / total, 3), "unit": "x realtime (audio s / wall s)", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "dtype": "f64",
             "sample": f"chunk 0 of the batch: log-mel + 32-layer encoder + cross K/V ({t_front:.1f} s) and "
                       f"{N_DEC} of {tokens.shape[0]} decode steps at batch 1, scaled x{tokens.shape[0] / N_DEC:.0f} "
                       f"({t_dec:.1f} s); fp64 NumPy"}

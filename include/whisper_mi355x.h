@@ -22,7 +22,7 @@
  *  - Every pointer argument is device memory owned by the caller unless
  *    stated otherwise; the library never allocates, frees or retains caller
  *    memory and keeps no state between calls apart from thread-local error
- *    text and the optional measurement hook below.
+ *    text and the optional measurement and K/V debug hooks below.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream). Work
  *    is enqueued asynchronously; no call synchronises.
  *  - Argument, shape, dtype, alignment (16 bytes for tensors and workspaces;
@@ -178,17 +178,28 @@ whisper_status whisper_logmel(const whisper_dims* dims, const float* audio, int 
  * frames (chunk-local, 10 ms each) split every overlap at its midpoint so
  * each frame of the recording belongs to exactly one chunk, and end at the
  * last frame centred on real audio in the final chunk. Returns 0 on invalid
- * input (or too small a plan). mel_out: [count, n_mels, 3000] fp32; ws:
+ * input (or too small a plan), and for recordings of more than 2^31 - 1
+ * samples (about 37 h at 16 kHz), whose chunk starts would not fit the int32
+ * plan entries. mel_out: [count, n_mels, 3000] fp32; ws:
  * whisper_workspace_size(dims, count, WHISPER_WS_LOGMEL) bytes. */
 int whisper_chunk_plan(int64_t n_samples, int stride, int32_t* plan, int max_chunks);
 whisper_status whisper_logmel_chunked(const whisper_dims* dims, const float* audio, int64_t n_samples, int stride,
                                       float* mel_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ encoder
+ * The encoder transformer of the showcase page ("The Approach": the encoder's
+ * attention and its FFN matmuls; "The Solution": gemm_hopper.cu for the
+ * projections, flash_attn_hopper.cu for encoder self-attention,
+ * layernorm_fused.cu for every residual + LayerNorm; the project page's
+ * fused-kernel list counts 162 LayerNorms in large-v3, i.e. pre-LN blocks plus
+ * a final LayerNorm per stack).
  * mel [batch, n_mels, 3000] fp32 -> enc_out [batch, n_audio_ctx, d] (act dtype):
  * conv k3 s1 + GELU, conv k3 s2 + GELU, + sinusoidal positions, n_enc_layers
  * pre-LN blocks (fused residual+LayerNorm, bidirectional attention, GELU MLP),
- * final LayerNorm. */
+ * final LayerNorm. packed: whisper_pack_weights output; ws:
+ * whisper_workspace_size(dims, batch, WHISPER_WS_ENCODE) bytes (16-byte
+ * aligned). Errors: INVALID_ARG (batch <= 0, NULL), SHAPE (no encoder layers),
+ * ALIGN, WORKSPACE, HIP; nothing is launched unless all checks pass. */
 whisper_status whisper_encode(const whisper_dims* dims, const void* packed, const float* mel, int batch,
                               void* enc_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -199,14 +210,28 @@ whisper_status whisper_encode_layers(const whisper_dims* dims, const void* packe
                                      int layer_begin, int layer_end, int apply_ln_post, void* h_out, void* ws,
                                      size_t ws_bytes, void* stream);
 
-/* Cross-attention keys/values of every decoder layer, once per chunk batch:
+/* Cross-attention keys/values of every decoder layer, once per chunk batch
+ * (the decoder cross-attention over the encoder output of the showcase page's
+ * flash_attn_hopper.cu card; the keys and values depend only on the encoder
+ * output, so they are projected once for all decode steps):
  * K = enc W_k^T, V = enc W_v^T + b_v, written head-major as
- * cross_kv [n_dec_layers][2][batch][n_heads][n_audio_ctx][64] (act dtype). */
+ * cross_kv [n_dec_layers][2][batch][n_heads][n_audio_ctx][64] (act dtype),
+ * caller-owned. enc_out: [batch, n_audio_ctx, d] from whisper_encode. ws and
+ * ws_bytes are not used (NULL is fine). Errors: INVALID_ARG, SHAPE (no
+ * decoder layers), ALIGN, HIP; nothing is launched unless all checks pass. */
 whisper_status whisper_cross_kv(const whisper_dims* dims, const void* packed, const void* enc_out, int batch,
                                 void* cross_kv, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------ decoder step
- * One batched decoder step with given tokens (teacher forcing or greedy).
+ * One batched decoder step with given tokens (teacher forcing or greedy): the
+ * autoregressive decoder of the showcase page (flash_attn_hopper.cu card:
+ * causal self-attention and cross-attention) over the KV cache of the
+ * Endpoints post's inference stack ("Inference Stack": compute in bfloat16,
+ * keys and values stored as float8, one byte per element, quantised on the
+ * way in). Errors: INVALID_ARG, SHAPE (no decoder layers, kv_cap outside
+ * 1..4096), ALIGN, WORKSPACE (ws smaller than whisper_workspace_size(dims,
+ * batch, WHISPER_WS_DECODE), or an armed K/V debug buffer too small), HIP;
+ * nothing is launched unless all checks pass.
  * tokens:    [batch] int32 token ids.
  * lengths:   [batch] int32, in/out. lengths[b] is the cache slot the new token's
  *            K/V go to and its position; +1 on return.
@@ -377,6 +402,66 @@ whisper_status whisper_attention_decode_cross(whisper_dtype dt, const void* q, c
                                               int batch, int n_heads, int T, void* out, void* ws, size_t ws_bytes,
                                               void* stream);
 
+/* One projection of the batched decoder step, as the fused step runs it
+ * (kernel-level call for tests and measurement; the decoder GEMMs of the
+ * showcase page's gemm_hopper.cu card with the residual + LayerNorm of its
+ * layernorm_fused.cu card folded in). bf16 weights, fp32 accumulation,
+ * M <= 4096 rows, K % 32 == 0. The LN modes compute LN(x) . W^T + bias with
+ * LN(x) = (x - mean) / sqrt(var + 1e-5) * gamma + beta over the K values of a
+ * row (biased variance), folded into the weights: y = r (x . W'^T - mean c1) +
+ * b2, W' = bf16(gamma * W), c1 = sum_k W'[., k], b2 = bias + W . beta,
+ * r = 1 / sqrt(var + 1e-5), with x entering the MFMA as bf16 hi + lo parts.
+ *   WHISPER_DEC_LN_STORE  y [M, N] bf16                           (cross-attention query)
+ *   WHISPER_DEC_LN_GELU   y [M, N] bf16 = gelu(.)                 (MLP up-projection)
+ *   WHISPER_DEC_LN_F32    y [M, N] fp32, unrounded                (vocabulary projection)
+ *   WHISPER_DEC_LN_QKV    N == 3 K, K % 64 == 0: columns [0, K) -> y [M, K] bf16
+ *                         (query); key and value columns appended as e4m3 codes
+ *                         code = e4m3_rne_saturate(fl32(v * fl32(1/scale))) to
+ *                         kv_cache [2][M][K/64][kv_cap][64] at slot lengths[m]
+ *                         (scales kv_scales[2], K then V; a slot outside
+ *                         0..kv_cap-1 skips the write and sets *dev_error = 6)
+ *   WHISPER_DEC_RESID     x [M, N] fp32 += a . bf16(W)^T + bias, a [M, K] bf16 (N % 32 == 0)
+ *   WHISPER_DEC_RESID_SPLITK  the same with K split over 4 workgroups per
+ *                         16 x 80 tile (N % 80 == 0, K % 1024 == 0), as the
+ *                         step's MLP down-projection
+ * x: LN modes [M, K] fp32 (read); residual modes [M, N] fp32 (read and
+ * written). w: [N, K] fp32 logical weight and bias [N] fp32 or NULL; each
+ * call rounds and re-lays them out into ws (whisper_decode_linear_workspace_size
+ * bytes, 0 for invalid arguments). gamma, beta: [K] fp32 (LN modes).
+ * Errors: INVALID_ARG (mode, sizes, NULL), SHAPE, ALIGN, WORKSPACE, HIP;
+ * nothing is launched unless all checks pass. */
+enum {
+  WHISPER_DEC_LN_STORE = 0, WHISPER_DEC_LN_GELU = 1, WHISPER_DEC_LN_F32 = 2, WHISPER_DEC_LN_QKV = 3,
+  WHISPER_DEC_RESID = 4, WHISPER_DEC_RESID_SPLITK = 5
+};
+size_t whisper_decode_linear_workspace_size(int mode, int M, int N, int K);
+whisper_status whisper_decode_linear(int mode, int M, int N, int K, float* x, const void* a, const float* w,
+                                     const float* bias, const float* gamma, const float* beta, void* y,
+                                     uint8_t* kv_cache, const float* kv_scales, const int32_t* lengths, int kv_cap,
+                                     int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ K/V append debug hooks
+ * For parity tests of the fp8 KV append (quantise on write, Endpoints post,
+ * "Inference Stack"). While armed, every whisper_decode_step,
+ * whisper_decode_step_xq, whisper_decode_prefill and WHISPER_DEC_LN_QKV call
+ * uses two optional caller buffers of [n_layers][2][rows][d_model] elements
+ * (rows = batch * n_tokens; one layer for whisper_decode_linear), indexed by
+ * (layer, K|V, activation row, channel):
+ *   kv_pre   (fp32, may be NULL): receives the key and value of each appended
+ *            token as the projection computes them, the value the codec
+ *            multiplies by fl32(1/scale) and rounds;
+ *   kv_force (int16, may be NULL): an entry >= 0 is the code written to the
+ *            cache for that value instead of the kernel's own (so a test can
+ *            give the GPU another implementation's codes, and the GPU's later
+ *            reads see them); a negative entry keeps the kernel's code.
+ * A call whose rows would not fit in n_elems returns WHISPER_ERR_WORKSPACE
+ * before launching anything. The buffers are caller device memory that must
+ * stay valid until disarm. Process-wide, not thread-safe (like the
+ * measurement hook below); disarmed, the hooks cost one pointer test per
+ * appended value. */
+whisper_status whisper_debug_kv_arm(float* kv_pre, const int16_t* kv_force, size_t n_elems);
+void whisper_debug_kv_disarm(void);
+
 /* ------------------------------------------------------------------ measured ceilings
  * The rates this part sustains, for rooflines reported against measured as
  * well as vendor peaks. whisper_peak_mfma runs n_wg workgroups of 4 waves,
@@ -398,7 +483,8 @@ whisper_status whisper_peak_read(const void* buf, size_t bytes, int n_wg, float*
  * `capacity` launches; events are hipEvent_t (passed as void*) created and
  * owned by the caller. Process-wide, not thread-safe; the only state the
  * library keeps besides error text. whisper_profile_disarm returns the number
- * of event pairs recorded and clears the hook. */
+ * of event pairs recorded and clears the hook. Disarmed, the hook costs one
+ * flag test per launch of the measured kernels, nothing on the device. */
 enum {
   WHISPER_PROF_DECODE_CROSS_ATTENTION = 1, /* split-T partial kernel of the decoder cross-attention */
   WHISPER_PROF_DECODE_SELF_ATTENTION = 2,  /* decoder self-attention over the fp8 cache */

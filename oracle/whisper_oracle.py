@@ -522,7 +522,7 @@ def cross_kv_fp8(cross, scales, fmt="e4m3"):
 
 # =========================================================================== decoder step
 
-def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, forced_codes=None):
+def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None):
     """One batched decoder step with teacher-forced tokens.
 
     tokens, lengths: [B] ints; lengths[b] is both the cache slot the new
@@ -530,24 +530,22 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, fo
     cache: indexable as cache[layer][kv][b] -> [H, cap, dh] (an array
         [L, 2, B, H, cap, dh] or nested containers holding only the rows
         used); uint8 e4m3 codes when scales is given (updated in place at
-        slot lengths[b]), or float values when scales is None (exact cache,
-        used to pin the step against a full causal pass).
+        slot lengths[b] with this step's own codes), or float values when
+        scales is None (exact cache, used to pin the step against a full
+        causal pass).
     scales: [L, 2] fp32 per-layer K and V scales, or None.
     cross: list over layers of (K_c, V_c), each indexable as K_c[b] -> [H, T, dh].
     rows: optional list of batch rows to compute (others are skipped);
         rows are independent, so a subset gives exactly those rows' results.
-    forced_codes: optional forced_codes[layer][kv][b] -> [H, dh] uint8 codes
-        stored in the new slot instead of the oracle's own quantisation. A
-        value close to a rounding boundary has two valid codes; once another
-        implementation's choice has been checked against the oracle's own code
-        and pre-quantisation value (both returned in the trace), the oracle can
-        continue from the same cache contents.
+    kv_transform: optional function applied to the new token's K and V before
+        the codec (sensitivity analysis: how far the step moves when the
+        quantised values change by a rounding, e.g. bf16_round). None: off.
 
     The new token's K and V are written first and then read back from the
     cache with the rest (quantise-on-write, dequantise-on-read).
-    Returns (logits [B, V] float64, trace dict with the fp32 pre-quantisation
-    K/V values [L, 2, B, H, dh], the oracle's own codes [L, 2, B, H, dh] and
-    the last residual stream).
+    Returns (logits [B, V] float64, trace dict: "kv" the new token's K and V
+    before quantisation [L, 2, B, H, dh] float64, "codes" the codes written
+    for them [L, 2, B, H, dh] uint8, "x" the last residual stream).
     """
     n_layers = len(cross)
     bsz = len(tokens)
@@ -557,8 +555,8 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, fo
     x = np.zeros((bsz, d))
     for b in rows:
         x[b] = W["decoder.token_embedding"][tokens[b]] + W["decoder.positional_embedding"][lengths[b]]
-    pre = np.zeros((n_layers, 2, bsz, n_heads, dh), dtype=np.float32)
-    own = np.zeros((n_layers, 2, bsz, n_heads, dh), dtype=np.uint8)
+    kv_new = np.zeros((n_layers, 2, bsz, n_heads, dh))
+    codes = np.zeros((n_layers, 2, bsz, n_heads, dh), dtype=np.uint8)
     for layer in range(n_layers):
         p = f"decoder.blocks.{layer}."
         a = layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
@@ -571,13 +569,13 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, fo
             for kv, val in ((0, k), (1, v)):
                 vb = val[b].reshape(n_heads, dh)
                 slot = cache[layer][kv][b]
+                kv_new[layer, kv, b] = vb
                 if scales is None:
                     slot[:, pos, :] = vb
                 else:
-                    pre[layer, kv, b] = e4m3_pre_quant(vb, scales[layer][kv])
-                    own[layer, kv, b] = e4m3_quantize(vb, scales[layer][kv])
-                    forced = None if forced_codes is None else forced_codes[layer][kv][b]
-                    slot[:, pos, :] = own[layer, kv, b] if forced is None else forced
+                    xq = vb if kv_transform is None else kv_transform(vb)
+                    codes[layer, kv, b] = e4m3_quantize(xq, scales[layer][kv])
+                    slot[:, pos, :] = codes[layer, kv, b]
             for h in range(n_heads):
                 kc_ = cache[layer][0][b][h, :pos + 1, :]
                 vc_ = cache[layer][1][b][h, :pos + 1, :]
@@ -603,9 +601,34 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, fo
                        W[p + "mlp.2.weight"], W[p + "mlp.2.bias"])
     y = layer_norm(x, W["decoder.ln.weight"], W["decoder.ln.bias"])
     logits = y @ W["decoder.token_embedding"].T
-    return logits, {"pre_quant": pre, "codes": own, "x": x}
+    return logits, {"kv": kv_new, "codes": codes, "x": x}
+
+
+def decode_prefill(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None):
+    """P prompt tokens per row fed causally: token p of row b goes to slot and
+    position lengths[b] + p and attends over slots 0 .. lengths[b] + p, which is
+    P successive teacher-forced steps (the decoder's causal self-attention
+    with several queries, flash_attn_hopper.cu card of the whisper_blaze
+    showcase page). tokens: [B, P]. Returns (logits of each row's last
+    token, list of the P steps' traces)."""
+    tokens = np.asarray(tokens)
+    lengths = np.asarray(lengths).copy()
+    traces = []
+    logits = None
+    for p in range(tokens.shape[1]):
+        logits, tr = decode_step(W, n_heads, tokens[:, p], lengths, cache, scales, cross, rows=rows,
+                                 kv_transform=kv_transform)
+        traces.append(tr)
+        lengths = lengths + 1
+    return logits, traces
 
 
 def greedy_token(logits):
     """Argmax over the vocabulary, lowest index on ties."""
     return np.argmax(logits, axis=-1)
+
+
+def top2_gap(logits):
+    """Per row, the largest logit minus the second largest (0 on a tie)."""
+    s = np.sort(np.asarray(logits, dtype=np.float64), axis=-1)
+    return s[..., -1] - s[..., -2]

@@ -29,8 +29,11 @@ EXPORTS = [
     "whisper_packed_weights_fp8_size", "whisper_pack_weights_fp8", "whisper_encode_fp8", "whisper_encode_layers_fp8",
     "whisper_gemm_fp8",
     "whisper_logmel_chunked",
+    "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
+    "whisper_debug_kv_disarm",
 ]
 
+DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
 PROF_DECODE_CROSS_ATTENTION, PROF_DECODE_SELF_ATTENTION, PROF_ENCODER_ATTENTION = 1, 2, 3
 PROF_ENCODER_FFN1, PROF_ENCODER_LAYERNORM = 4, 5
 
@@ -100,6 +103,10 @@ _SIG = {
     "whisper_peak_mfma": (I, [I, I, P, P]),
     "whisper_peak_mfma_flop": (ctypes.c_double, [I, I]),
     "whisper_peak_read": (I, [P, Z, I, P, P]),
+    "whisper_decode_linear_workspace_size": (Z, [I, I, I, I]),
+    "whisper_decode_linear": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]),
+    "whisper_debug_kv_arm": (I, [P, P, Z]),
+    "whisper_debug_kv_disarm": (None, []),
     "whisper_profile_arm": (I, [I, P, P, I]),
     "whisper_profile_disarm": (I, []),
     "whisper_status_string": (ctypes.c_char_p, [I]),
@@ -299,6 +306,27 @@ def whisper_profile_disarm():
     n = lib().whisper_profile_disarm()
     whisper_profile_arm._keep = None
     return n
+
+
+def whisper_decode_linear_workspace_size(mode, M, N, K):
+    return lib().whisper_decode_linear_workspace_size(mode, M, N, K)
+
+
+def whisper_decode_linear(mode, M, N, K, x, a, w, bias, gamma, beta, y, kv_cache=None, kv_scales=None,
+                          lengths=None, kv_cap=0, dev_error=None, ws=None, ws_bytes=0, stream=None):
+    _check(lib().whisper_decode_linear(mode, M, N, K, _p(x), _p(a), _p(w), _p(bias), _p(gamma), _p(beta), _p(y),
+                                       _p(kv_cache), _p(kv_scales), _p(lengths), kv_cap, _p(dev_error), _p(ws),
+                                       ws_bytes, _stream(stream)))
+
+
+def whisper_debug_kv_arm(kv_pre, kv_force, n_elems):
+    """kv_pre (fp32) and kv_force (int16): device tensors or None, kept alive
+    by the caller until disarm."""
+    _check(lib().whisper_debug_kv_arm(_p(kv_pre), _p(kv_force), n_elems))
+
+
+def whisper_debug_kv_disarm():
+    lib().whisper_debug_kv_disarm()
 
 
 def whisper_status_string(status):

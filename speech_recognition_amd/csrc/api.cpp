@@ -228,6 +228,28 @@ struct ProfScope {
   }
 };
 
+// ------------------------------------------------------------------ KV-append debug hook
+// While armed, the QKV epilogue of every decode call also stores the fp32 K / V
+// values its fp8 codec is applied to (parity tests check the codec bit for bit
+// on them). Process-wide and not thread-safe, like the measurement hook.
+struct KvTrace {
+  float* buf = nullptr;          // fp32 values the codec is applied to
+  const int16_t* force = nullptr;  // codes written instead of the kernel's own (>= 0)
+  size_t cap = 0;                // elements of each buffer
+};
+KvTrace g_kvtrace;
+
+// The hook's buffers must hold [n_layers][2][rows][d_model] elements; checked
+// before the first launch of a call.
+whisper_status kvtrace_check(int n_layers, long rows, int d_model, const char* who) {
+  if (!g_kvtrace.buf && !g_kvtrace.force) return WHISPER_OK;
+  const size_t need = (size_t)n_layers * 2 * rows * d_model;
+  if (need > g_kvtrace.cap)
+    return fail(WHISPER_ERR_WORKSPACE, std::string(who) + ": the armed K/V debug buffers hold " +
+                                           std::to_string(g_kvtrace.cap) + " elements, need " + std::to_string(need));
+  return WHISPER_OK;
+}
+
 // ------------------------------------------------------------------ GEMM helpers
 GemmParams gp(const void* A, long lda, const void* B, long ldb, int M, int N, int K, const float* bias, void* C,
               long ldc) {
@@ -374,6 +396,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* QC = at<u16_t>(ws, W.qc);
   u16_t* HF = at<u16_t>(ws, W.hf);
   int32_t* CNT = at<int32_t>(ws, W.cnt);
+  WH_CHECK(kvtrace_check(L, B, D, "decode"));
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
@@ -386,6 +409,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     g.A = A; g.lda = K; g.X = X; g.out = out; g.out_f32 = out_f32;
     g.kv_cache = kv_cache; g.kv_scales = kv_scales; g.lengths = lengths; g.dev_error = dev_error;
     g.kv_cap = cap; g.kv_B = Bc; g.kv_H = H; g.kv_layer = layer; g.d_model = D; g.rows_per_b = R;
+    g.kv_pre = epi == DEPI_QKV ? g_kvtrace.buf : nullptr;
+    g.kv_force = epi == DEPI_QKV ? g_kvtrace.force : nullptr;
     int mb, cb;
     dec_gemm_tiles(B, N, mb, cb);
     // split-K where the long K would otherwise leave a third of the CUs idle
@@ -472,6 +497,19 @@ int whisper_profile_disarm(void) {
   g_prof = Profile();
   return n;
 }
+
+whisper_status whisper_debug_kv_arm(float* kv_pre, const int16_t* kv_force, size_t n_elems) {
+  if ((!kv_pre && !kv_force) || n_elems == 0)
+    return fail(WHISPER_ERR_INVALID_ARG, "debug_kv_arm: no buffer or zero size");
+  if (((uintptr_t)kv_pre & 3u) || ((uintptr_t)kv_force & 1u))
+    return fail(WHISPER_ERR_ALIGN, "debug_kv_arm: buffer not aligned to its element");
+  g_kvtrace.buf = kv_pre;
+  g_kvtrace.force = kv_force;
+  g_kvtrace.cap = n_elems;
+  return WHISPER_OK;
+}
+
+void whisper_debug_kv_disarm(void) { g_kvtrace = KvTrace(); }
 
 int whisper_weight_count(const whisper_dims* d) {
   if (check_dims(d) != WHISPER_OK) return 0;
@@ -660,7 +698,8 @@ int whisper_chunk_plan(int64_t n_samples, int stride, int32_t* plan, int max_chu
   constexpr long W = 480000, HOP = 160, NFR = 3000;
   if (n_samples <= 0 || stride <= 0 || stride > W || stride % HOP) return 0;
   const long n = n_samples <= W ? 1 : 1 + (n_samples - W + stride - 1) / stride;
-  if (n > 0x7fffffff) return 0;
+  // plan entries are int32: every chunk's first sample must fit
+  if (n_samples > 0x7fffffffL || (n - 1) * (long)stride > 0x7fffffffL) return 0;
   if (!plan) return (int)n;
   if (max_chunks < n) return 0;
   const long sf = stride / HOP, of = NFR - sf;  // frames per stride, frames of overlap
@@ -874,6 +913,7 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   float* LG = logits ? logits : at<float>(ws, W.logits);
   if (t == ACT_BF16) return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv,
                                               LG, argmax, dev_error, ws, s);
+  WH_CHECK(kvtrace_check(L, B, D, "decode_step"));
   WH_TRY(launch_embed(t, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s));
   const size_t kv_layer = (size_t)2 * B * H * cap * 64;
@@ -886,7 +926,8 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
       WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, Lw.ln1g), at<float>(packed, Lw.ln1b), 1e-5f, B, D, A, X, s));
     GemmParams pq = gp(A, D, at<void>(packed, Lw.wqkv), D, B, 3 * D, D, at<float>(packed, Lw.bqkv), Q, D);
     pq.kv_cache = kv_cache; pq.kv_scales = kv_scales; pq.lengths = lengths; pq.dev_error = dev_error;
-    pq.kv_cap = cap; pq.kv_B = B; pq.kv_H = H; pq.kv_layer = l; pq.d_model = D;
+    pq.kv_cap = cap; pq.kv_B = B; pq.kv_H = H; pq.kv_layer = l; pq.d_model = D; pq.kv_pre = g_kvtrace.buf;
+    pq.kv_force = g_kvtrace.force;
     WH_TRY(launch_gemm_skinny(t, EPI_DEC_QKV, pq, s));
     const uint8_t* kc = kv_cache + l * kv_layer;
     {
@@ -959,6 +1000,101 @@ whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed,
   float* LG = logits ? logits : at<float>(ws, W.logits);
   return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, nullptr, LG, argmax,
                            dev_error, ws, S(stream), cross_codes, cross_scales, 1, (int)cross_format);
+}
+
+// ------------------------------------------------------------------ one decoder projection
+namespace {
+struct DecLinWS { size_t wf, c1, b2, xt, part, cnt, n_cnt, total; };
+bool declin_ln(int mode) { return mode <= WHISPER_DEC_LN_QKV; }
+bool declin_split(int mode) { return mode == WHISPER_DEC_RESID_SPLITK; }
+DecLinWS declin_ws(int mode, int M, int N, int K) {
+  DecLinWS W{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  const size_t Mp = (size_t)((M + 15) & ~15), Np = (size_t)((N + 15) & ~15);
+  W.wf = take(Np * K * 2);
+  W.c1 = take((size_t)N * 4);
+  W.b2 = take((size_t)N * 4);
+  W.xt = take(Mp * (declin_ln(mode) ? K : N) * 4);
+  if (declin_split(mode)) {
+    const size_t tiles = (size_t)((N + DEC_SPLIT_COLS - 1) / DEC_SPLIT_COLS) * ((M + 15) / 16);
+    W.part = take(tiles * DEC_KSPLIT * (DEC_SPLIT_COLS / 16) * 64 * 16);
+    W.cnt = take(tiles * 4);
+    W.n_cnt = tiles;
+  }
+  W.total = off;
+  return W;
+}
+}  // namespace
+
+size_t whisper_decode_linear_workspace_size(int mode, int M, int N, int K) {
+  if (mode < WHISPER_DEC_LN_STORE || mode > WHISPER_DEC_RESID_SPLITK || M <= 0 || M > 4096 || N <= 0 || K <= 0 ||
+      K % 32)
+    return 0;
+  return declin_ws(mode, M, N, K).total;
+}
+
+whisper_status whisper_decode_linear(int mode, int M, int N, int K, float* x, const void* a, const float* w,
+                                     const float* bias, const float* gamma, const float* beta, void* y,
+                                     uint8_t* kv_cache, const float* kv_scales, const int32_t* lengths, int kv_cap,
+                                     int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  if (mode < WHISPER_DEC_LN_STORE || mode > WHISPER_DEC_RESID_SPLITK)
+    return fail(WHISPER_ERR_INVALID_ARG, "decode_linear: unknown mode");
+  if (M <= 0 || M > 4096 || N <= 0 || K <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_linear: need 1 <= M <= 4096, N, K > 0");
+  if (K % 32) return fail(WHISPER_ERR_SHAPE, "decode_linear: K must be a multiple of 32");
+  const bool ln = declin_ln(mode), split = declin_split(mode);
+  if (!ln && N % 32) return fail(WHISPER_ERR_SHAPE, "decode_linear: residual modes need N % 32 == 0");
+  if (split && (N % DEC_SPLIT_COLS || K % (DEC_KSPLIT * 8 * 32)))
+    return fail(WHISPER_ERR_SHAPE, "decode_linear: split-K needs N % 80 == 0 and K % 1024 == 0");
+  if (mode == WHISPER_DEC_LN_QKV && (N != 3 * K || K % 64))
+    return fail(WHISPER_ERR_SHAPE, "decode_linear: QKV needs N == 3 K and K % 64 == 0");
+  WH_CHECK(check_ptrs({x, w}, "decode_linear"));
+  if (ln) {
+    WH_CHECK(check_ptrs({gamma, beta, y}, "decode_linear"));
+  } else {
+    WH_CHECK(check_ptrs({a}, "decode_linear"));
+  }
+  if (bias && !aligned16(bias)) return fail(WHISPER_ERR_ALIGN, "decode_linear: bias not 16-byte aligned");
+  if (mode == WHISPER_DEC_LN_QKV) {
+    if (kv_cap <= 0 || kv_cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_linear: kv_cap must be in 1..4096");
+    WH_CHECK(check_ptrs({kv_cache}, "decode_linear"));
+    WH_CHECK(check_ptrs4({kv_scales, lengths}, "decode_linear"));
+    if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_linear: dev_error not 4-byte aligned");
+    WH_CHECK(kvtrace_check(1, M, K, "decode_linear"));
+  }
+  const DecLinWS W = declin_ws(mode, M, N, K);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_linear"));
+  (void)hipGetLastError();
+  const hipStream_t s = S(stream);
+  u16_t* Wf = at<u16_t>(ws, W.wf);
+  float* C1 = at<float>(ws, W.c1);
+  float* B2 = at<float>(ws, W.b2);
+  float* XT = at<float>(ws, W.xt);
+  if (ln) WH_TRY(launch_fold_ln(w, gamma, beta, bias, N, K, Wf, C1, B2, s));
+  else WH_TRY(launch_pack_dec_weight(w, N, K, Wf, s));
+  WH_TRY(launch_x_tiles(x, XT, M, ln ? K : N, 1, s));
+  DecGemmParams g{};
+  g.M = M; g.N = N; g.K = K; g.W = Wf;
+  g.bias = ln ? B2 : bias;
+  g.c1 = ln ? C1 : nullptr;
+  g.A = (const u16_t*)a; g.lda = K; g.X = XT;
+  g.out = (u16_t*)y; g.out_f32 = (float*)y;
+  if (mode == WHISPER_DEC_LN_QKV) {
+    g.kv_cache = kv_cache; g.kv_scales = kv_scales; g.lengths = lengths; g.dev_error = dev_error;
+    g.kv_cap = kv_cap; g.kv_B = M; g.kv_H = K / 64; g.kv_layer = 0; g.d_model = K; g.kv_pre = g_kvtrace.buf;
+    g.kv_force = g_kvtrace.force;
+  }
+  int mb, cb;
+  dec_gemm_tiles(M, N, mb, cb);
+  if (split) {
+    g.ks = DEC_KSPLIT; g.part = at<float>(ws, W.part); g.cnt = at<int32_t>(ws, W.cnt);
+    mb = 1; cb = DEC_SPLIT_COLS / 16;
+    WH_TRY(launch_fill_f32((float*)g.cnt, 0.f, W.n_cnt, s));  // the tile counters start at zero
+  }
+  static const DecEpi epis[] = {DEPI_STORE, DEPI_GELU, DEPI_F32, DEPI_QKV, DEPI_RESID, DEPI_RESID};
+  WH_TRY(launch_gemm_dec(ln ? PRO_X : PRO_A, epis[mode], g, mb, cb, s));
+  if (!ln) WH_TRY(launch_x_tiles(XT, x, M, N, 0, s));
+  return WHISPER_OK;
 }
 
 whisper_status whisper_peak_mfma(int n_wg, int iters, float* out, void* stream) {

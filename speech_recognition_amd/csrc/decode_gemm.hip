@@ -299,10 +299,14 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
         p.out[(long)m * d + n] = f2bf(v);
       } else {
         const int kv = (n - d) / d, c = (n - d) - kv * d, pos = e_pos[r];
+        const long dbg = ((long)(p.kv_layer * 2 + kv) * M + m) * d + c;
+        if (p.kv_pre) p.kv_pre[dbg] = v;
         if (pos >= 0 && pos < p.kv_cap) {
           const long idx =
               ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m / RPB) * p.kv_H + (c >> 6)) * p.kv_cap + pos) * 64 + (c & 63);
-          p.kv_cache[idx] = (uint8_t)e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
+          uint32_t code = e4m3_encode(v * (kv ? e_inv[1] : e_inv[0]));
+          if (p.kv_force && p.kv_force[dbg] >= 0) code = (uint32_t)p.kv_force[dbg];
+          p.kv_cache[idx] = (uint8_t)code;
         } else if (p.dev_error) {
           *p.dev_error = 6;  // capacity exceeded: the write is skipped
         }

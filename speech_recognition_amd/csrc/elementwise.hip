@@ -498,6 +498,21 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int
   return hipGetLastError();
 }
 
+// Row-major fp32 rows <-> the 16-row tiles of dec_x_index (one workgroup per row).
+__global__ __launch_bounds__(256) void x_tiles_kernel(const float* src, float* dst, int d, int to_tiles) {
+  const long m = blockIdx.x;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    if (to_tiles) dst[dec_x_index(m, c, d)] = src[m * d + c];
+    else dst[m * d + c] = src[dec_x_index(m, c, d)];
+  }
+}
+
+hipError_t launch_x_tiles(const float* src, float* dst, int M, int d, int to_tiles, hipStream_t s) {
+  if (M <= 0 || d <= 0 || d % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(x_tiles_kernel, dim3(M), dim3(256), 0, s, src, dst, d, to_tiles);
+  return hipGetLastError();
+}
+
 // Last position of each batch row of a prefill: x_dst row b = x_src row
 // b * R + R - 1, both in the 16-row tiles of dec_x_index.
 __global__ __launch_bounds__(256) void gather_last_rows_kernel(const float* x_src, float* x_dst, int R, int d) {

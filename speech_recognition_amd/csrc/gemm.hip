@@ -39,10 +39,14 @@ __device__ __forceinline__ void epi_store(const GemmParams& p, int z, int m, int
       const int kv = (n - d) / d, c = (n - d) - kv * d;
       const int h = c >> 6, e = c & 63;
       const int pos = p.lengths[m];
+      const long dbg = ((long)(p.kv_layer * 2 + kv) * p.M + m) * d + c;
+      if (p.kv_pre) p.kv_pre[dbg] = v;
       if (pos >= 0 && pos < p.kv_cap) {
         const float inv = 1.0f / p.kv_scales[p.kv_layer * 2 + kv];
         const long idx = ((((long)(p.kv_layer * 2 + kv) * p.kv_B + m) * p.kv_H + h) * p.kv_cap + pos) * 64 + e;
-        p.kv_cache[idx] = (uint8_t)e4m3_encode(v * inv);
+        uint32_t code = e4m3_encode(v * inv);
+        if (p.kv_force && p.kv_force[dbg] >= 0) code = (uint32_t)p.kv_force[dbg];
+        p.kv_cache[idx] = (uint8_t)code;
       } else if (p.dev_error && n == d) {
         *p.dev_error = 6;  // capacity exceeded: the write is skipped
       }

@@ -37,6 +37,11 @@ struct GemmParams {
   // EPI_DEC_QKV
   uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
   int kv_cap, kv_B, kv_H, kv_layer, d_model;
+  // EPI_DEC_QKV debug hooks (NULL: off): kv_pre receives the fp32 K / V values
+  // the codec is applied to; a non-negative kv_force entry is written to the
+  // cache instead of the kernel's own code. Both [n_layers][2][M][d_model].
+  float* kv_pre;
+  const int16_t* kv_force;
   // tiled-kernel choice for measurement: 0 automatic, 1 128x128, 2 256x256/8 waves, 3 256x256/4 waves,
   // 4 256x256 with the LDS DMA pipeline
   int variant;
@@ -68,6 +73,11 @@ struct DecGemmParams {
   // DEPI_QKV: k, v appended as e4m3 codes at slot lengths[m]
   uint8_t* kv_cache; const float* kv_scales; const int32_t* lengths; int32_t* dev_error;
   int kv_cap, kv_B, kv_H, kv_layer, d_model;
+  // DEPI_QKV debug hooks (NULL: off): kv_pre receives the fp32 K / V values
+  // the codec is applied to; a non-negative kv_force entry is written to the
+  // cache instead of the kernel's own code. Both [n_layers][2][M][d_model].
+  float* kv_pre;
+  const int16_t* kv_force;
   // split-K over ks workgroups per output tile (PRO_A only; ks <= 1: none):
   // partial blocks [tiles][ks][MB*CB][64 lanes] f32x4 and one counter per tile,
   // zero on entry (each launch leaves them zero)
@@ -143,6 +153,9 @@ hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, con
                         // rows_per_b (R): B rows, row m is token m of batch row m / R at lengths[m / R] + m % R
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s,
                          int len_inc = 1);
+// fp32 rows [M, d] (row-major) to the 16-row tiles of dec_x_index (to_tiles
+// != 0), or back; d % 32 == 0
+hipError_t launch_x_tiles(const float* src, float* dst, int M, int d, int to_tiles, hipStream_t s);
 // x_dst row b = x_src row b * R + R - 1 (both in the 16-row tiles of dec_x_index)
 hipError_t launch_gather_last_rows(const float* x_src, float* x_dst, int B, int R, int d, hipStream_t s);
 

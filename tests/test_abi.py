@@ -121,6 +121,12 @@ def test_chunk_plan_host_logic_matches_oracle():
     for bad in ((0, 400000), (1000, 0), (1000, 480160), (1000, 1000)):
         with pytest.raises(L.WhisperError):
             L.whisper_chunk_plan(*bad)
+    # plan entries are int32: the longest recording whose chunk starts fit is
+    # accepted, one sample more is rejected (about 37 h at 16 kHz)
+    lib = L.lib()
+    assert lib.whisper_chunk_plan(2**31 - 1, 480000, None, 0) == 1 + -(-(2**31 - 1 - 480000) // 480000)
+    assert lib.whisper_chunk_plan(2**31, 480000, None, 0) == 0
+    assert lib.whisper_chunk_plan(2**40, 160, None, 0) == 0
 
 
 def _al(n):
@@ -217,3 +223,63 @@ def test_fp8_encoder_entry_validation():
     with pytest.raises(L.WhisperError) as e:
         L.whisper_gemm_fp8(16, 0, 512, 16, 256, 16, 256, 16, None, False, 16, 256, stream=0)
     assert e.value.status == 1
+
+
+def test_decode_linear_validation():
+    """Host checks of whisper_decode_linear (no launch happens): modes, shape
+    rules of the split-K and QKV forms, workspace size."""
+    M, N, K = 64, 1280, 1280
+    ws = L.whisper_decode_linear_workspace_size(L.DEC_LN_STORE, M, N, K)
+    # packed weight (rows padded to 16), c1, b2 and the 16-row x tiles
+    assert ws >= N * K * 2 + 2 * N * 4 + M * K * 4
+    assert L.whisper_decode_linear_workspace_size(L.DEC_RESID_SPLITK, M, 1280, 5120) > \
+        L.whisper_decode_linear_workspace_size(L.DEC_RESID, M, 1280, 5120)  # + partials and counters
+    assert L.whisper_decode_linear_workspace_size(7, M, N, K) == 0
+    assert L.whisper_decode_linear_workspace_size(L.DEC_LN_STORE, 5000, N, K) == 0
+    assert L.whisper_decode_linear_workspace_size(L.DEC_LN_STORE, M, N, 100) == 0
+
+    def call(mode, M=64, N=1280, K=1280, ws_bytes=1 << 40, **kw):
+        args = dict(x=16, a=16, w=16, bias=None, gamma=16, beta=16, y=16, kv_cache=16, kv_scales=16, lengths=16,
+                    kv_cap=672, dev_error=None, ws=16)
+        args.update(kw)
+        L.whisper_decode_linear(mode, M, N, K, args["x"], args["a"], args["w"], args["bias"], args["gamma"],
+                                args["beta"], args["y"], args["kv_cache"], args["kv_scales"], args["lengths"],
+                                args["kv_cap"], args["dev_error"], args["ws"], ws_bytes, stream=0)
+
+    for kw, status in ((dict(mode=9), 1), (dict(mode=0, M=0), 1), (dict(mode=0, M=4097), 1),
+                       (dict(mode=0, K=100), 2), (dict(mode=4, N=1000), 2),
+                       (dict(mode=5, N=1280, K=1280), 2), (dict(mode=5, N=1200, K=5120), 2),
+                       (dict(mode=3, N=3000), 2), (dict(mode=3, N=3840, kv_cap=0), 2),
+                       (dict(mode=0, gamma=None), 1), (dict(mode=4, a=None), 1), (dict(mode=0, x=24), 4),
+                       (dict(mode=3, N=3840, lengths=None), 1), (dict(mode=0, ws_bytes=1024), 5)):
+        with pytest.raises(L.WhisperError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+
+
+def test_debug_kv_hook_checked_before_launch():
+    """The K/V debug hook: NULL or misaligned buffers are rejected, and a call
+    whose trace would overflow the armed buffer fails with WORKSPACE before
+    launching anything; disarming restores normal validation."""
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_debug_kv_arm(None, None, 10)
+    assert e.value.status == 1
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_debug_kv_arm(18, None, 10)
+    assert e.value.status == 4
+    with pytest.raises(L.WhisperError) as e:
+        L.whisper_debug_kv_arm(None, 17, 10)
+    assert e.value.status == 4
+    d = CONFIGS["v3_decode"]
+    ws = L.whisper_workspace_size(d, 4, L.WS_DECODE)
+    L.whisper_debug_kv_arm(16, 32, 32 * 2 * 4 * 1280 - 1)  # one element short of 32 layers x K, V x 4 rows
+    try:
+        with pytest.raises(L.WhisperError) as e:
+            L.whisper_decode_step(d, 16, 4, 672, 16, 16, 16, 16, 16, None, 16, None, 16, ws, stream=0)
+        assert e.value.status == 5 and "debug" in str(e.value)
+        with pytest.raises(L.WhisperError) as e:
+            L.whisper_decode_linear(L.DEC_LN_QKV, 4096, 3840, 1280, 16, 16, 16, None, 16, 16, 16, 16, 16, 16, 672,
+                                    None, 16, 1 << 40, stream=0)
+        assert e.value.status == 5
+    finally:
+        L.whisper_debug_kv_disarm()

@@ -175,15 +175,23 @@ def test_attention_encoder(act, B, T, H):
         assert rel_err(host(out)[b], ref) < TOL
 
 
-def test_attention_decode_self_fp8():
-    B, H, cap = 5, 3, 100
-    say(f"attention_decode_self B={B} H={H} cap={cap}")
-    g = torch.Generator().manual_seed(5)
+@pytest.mark.parametrize("cap,n_keys", [
+    (100, [1, 17, 64, 99, 100]),
+    # the kernel walks keys in batches of 512: one key, both sides of the batch
+    # boundary, and the capacity of the batch-64 decode workload (448 + 224)
+    (672, [1, 511, 512, 513, 671, 672]),
+    # every frame of a 30 s chunk: the fp8 cross-attention form of the kernel
+    (1500, [1500, 1024, 1499]),
+])
+def test_attention_decode_self_fp8(cap, n_keys):
+    B, H = len(n_keys), 3
+    say(f"attention_decode_self B={B} H={H} cap={cap} n_keys={n_keys}")
+    g = torch.Generator().manual_seed(5 + cap)
     kc = torch.randint(0, 256, (B, H, cap, 64), generator=g, dtype=torch.int32)
     vc = torch.randint(0, 256, (B, H, cap, 64), generator=g, dtype=torch.int32)
     kc[(kc & 0x7F) == 0x7F] = 0x40   # no NaN codes among the keys
     vc[(vc & 0x7F) == 0x7F] = 0x41
-    n_keys = torch.tensor([1, 17, 64, 99, 100], dtype=torch.int32)
+    n_keys = torch.tensor(n_keys, dtype=torch.int32)
     # poison every slot past n_keys with NaN codes: causality means they are never read
     for b in range(B):
         kc[b, :, n_keys[b]:] = 0x7F
@@ -191,10 +199,13 @@ def test_attention_decode_self_fp8():
     kc, vc = kc.to(torch.uint8), vc.to(torch.uint8)
     q = gen_normal(DEV, (B, H * 64), 9, 6, 30, bf16=True).to(torch.bfloat16)
     scales = torch.tensor([0.004, 0.01, 0, 0], dtype=torch.float32, device=DEV)
-    out = torch.empty(B, H * 64, dtype=torch.bfloat16, device=DEV)
+    # canary bytes around the output: only the B x H*64 outputs are written
+    buf = torch.full((B * H * 64 + 2 * 64,), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[64:64 + B * H * 64].view(B, H * 64)
     L.whisper_attention_decode_self(L.WHISPER_BF16, q, B, H, cap, kc.to(DEV), vc.to(DEV), scales,
                                     n_keys.to(DEV), out)
     torch.cuda.synchronize()
+    assert torch.all(buf[:64] == -7.0) and torch.all(buf[64 + B * H * 64:] == -7.0), "write outside the output"
     got = host(out)
     assert np.isfinite(got).all()
     qh = host(q)

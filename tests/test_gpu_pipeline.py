@@ -1,6 +1,8 @@
 """GPU parity of the composed hot path against the oracle (teacher forcing),
 through the C ABI: encoder layer, full encoder from audio, the tiny fp32
-model end to end, and the batched large-v3 decoder step over an fp8 KV cache.
+model end to end, the long-form turbo pipeline end to end, and the batched
+large-v3 decoder step over an fp8 KV cache. The GPU and the oracle each keep
+their own KV cache; the oracle never reads a value the GPU produced.
 
 Batch rows and chunks are independent, so at the large shapes the oracle runs
 on a few rows/chunks only and those rows must match."""
@@ -11,9 +13,11 @@ import torch
 from oracle import whisper_oracle as O
 from speech_recognition_amd import _lib as L
 from speech_recognition_amd.runtime import DecodeState, Whisper, act_dtype
+from tests.decode_check import (KvTrace, check_codec_exact, check_kv_against_oracle, check_logits_argmax,
+                                gpu_codec_on_oracle_values)
 from tests.gpu_util import TOL, host, need_gpu, rel_err, say
-from workload import (CONFIGS, gen_audio_tones, gen_normal, gen_prefill_kv, gen_prefill_lengths, gen_tokens,
-                      gen_weights)
+from workload import (CONFIGS, gen_audio_longform, gen_audio_tones, gen_normal, gen_prefill_kv, gen_prefill_lengths,
+                      gen_tokens, gen_weights)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -147,140 +151,184 @@ def test_encoder_full_large_v3_from_audio():
 
 
 # ------------------------------------------------------------------ decoder helpers
-def code_mismatch_ok(g, o, pre):
-    """End-to-end fp8 codes (teacher forced): a GPU code equal to the oracle's
-    passes; a differing one must be the e4m3 rounding of some value within
-    delta = TOL * max|y| of the oracle's pre-quantisation value y, i.e. within
-    the same tolerance the activations are held to (max over the layer's K or
-    V row). pre: [H, 64] oracle pre-quantisation values.
-    Returns (ok, n_differing)."""
-    g = np.asarray(g, np.int64)
-    o = np.asarray(o, np.int64)
-    diff = g != o
-    if not diff.any():
-        return True, 0
-    y = pre.astype(np.float64)
-    delta = TOL * np.abs(y).max()
-    vlo = O.e4m3_value(O.e4m3_encode((y - delta).astype(np.float32)))
-    vhi = O.e4m3_value(O.e4m3_encode((y + delta).astype(np.float32)))
-    vg = O.e4m3_value(g)
-    ok = (~diff) | ((vg >= vlo) & (vg <= vhi))
-    return bool(ok.all()), int(diff.sum())
+def prefill_both(state, dims, B, prefill_max, rows, sc):
+    """Prefill the GPU cache (library codec) and the oracle's cache for `rows`
+    (oracle codec) from the same seeded K/V values; the two codecs must agree
+    code for code. Returns the oracle cache (rows only)."""
+    H, Lyr, cap = dims.n_heads, dims.n_dec_layers, state.cap
+    cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
+    for l in range(Lyr):
+        for kv in range(2):
+            x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, H, prefill_max)
+            codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+            L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), state.kv_scales[l, kv:kv + 1].contiguous().clone(),
+                                   codes, None)
+            state.kv_cache[l, kv, :, :, :prefill_max, :] = codes
+            xh = x.cpu().numpy()
+            ch = codes.cpu().numpy()
+            for b in rows:
+                ref = O.e4m3_quantize(xh[b], sc[l, kv])
+                assert np.array_equal(ref, ch[b]), "prefill codes differ between the GPU codec and the oracle codec"
+                cache[l][kv][b][:, :prefill_max, :] = ref
+            del x, codes
+    return cache
 
 
-def codec_on_oracle_values_bit_exact(pre, codes_ref):
-    """The GPU codec fed the oracle's own pre-quantisation values (scale 1)
-    must reproduce the oracle's codes bit for bit."""
-    y = torch.from_numpy(np.ascontiguousarray(pre, dtype=np.float32)).to(DEV)
-    one = torch.ones(4, dtype=torch.float32, device=DEV)
-    c = torch.empty(y.numel(), dtype=torch.uint8, device=DEV)
-    L.whisper_fp8_quantize(y, L.WHISPER_F32, y.numel(), one, c, None)
-    torch.cuda.synchronize()
-    return np.array_equal(c.cpu().numpy(), np.asarray(codes_ref).reshape(-1))
+def prefill_scales(dims, B, prefill_max):
+    """Per-layer K and V scales from the seeded prefill values (amax / 448)."""
+    sc = torch.ones(dims.n_dec_layers, 2, dtype=torch.float32)
+    for l in range(dims.n_dec_layers):
+        for kv in range(2):
+            x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, dims.n_heads, prefill_max)
+            sc[l, kv] = float(O.e4m3_scale_from_amax(np.array([x.abs().max().item()], np.float32)))
+            del x
+    return sc
 
 
-def check_logits_argmax(lg_gpu, am_gpu, lg_ref, rows, tag):
-    n_tied = 0
-    for b in rows:
-        e = rel_err(lg_gpu[b], lg_ref[b])
-        assert e < TOL, f"{tag} row {b}: logits rel err {e:.3e}"
-        top2 = np.sort(lg_ref[b])[-2:]
-        bound = 2 * np.abs(lg_gpu[b] - lg_ref[b]).max()
-        if top2[1] - top2[0] <= bound:
-            n_tied += 1
-            continue
-        assert am_gpu[b] == int(np.argmax(lg_ref[b])), f"{tag} row {b}: argmax differs"
-    return n_tied
+def new_stats():
+    return {"flips": 0, "codes": 0, "kv_err": 0.0, "tied": 0, "logit_err": 0.0, "sens": 0.0, "ops": 0}
 
 
-def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None, cross_fmt="e4m3"):
-    """Teacher-forced decode on the GPU from a prefilled fp8 cache vs the oracle on `rows`.
-    cross_fp8_scale: when given, the cross-attention K/V are fp8 codes in
-    cross_fmt ("e4m3" or "e5m2") with that scale for every (layer, K|V), on
-    both sides (the GPU quantises its bf16 projections, the oracle its own
-    fp64 ones)."""
+def report(tag, st):
+    say(f"  {tag}: logits max rel err {st['logit_err']:.2e}"
+        + (f" (oracle's own bf16 sensitivity {st['sens']:.2e})" if st["sens"] else "")
+        + f"; K/V before quantisation max rel err {st['kv_err']:.2e}; kernel codes differing from the oracle's "
+        f"{st['flips']}/{st['codes']} ({100.0 * st['flips'] / max(st['codes'], 1):.3f}%); tied argmax rows "
+        f"excluded {st['tied']}")
+
+
+def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
+    """Run `ops` (("step", tokens [B]) or ("prefill", tokens [B, P]), device
+    int32) on the GPU and on the oracle, comparing after each.
+
+    oracle: dict(W=host weights, H=heads, cross=oracle cross K/V, cache=oracle
+    cache (rows only, updated in place), sc=[L, 2] scales).
+    independent=False: the oracle runs each op first and its codes are forced
+    into the GPU's appends for `rows` (see tests/decode_check.py); extra_rows
+    are batch rows left to the kernel's own codes, whose codec is checked.
+    independent=True: no forcing; the oracle also runs a copy of its cache
+    with its quantised K/V rounded to bf16, which sets the logits bar."""
+    W, H, cross, cache, sc = oracle["W"], oracle["H"], oracle["cross"], oracle["cache"], oracle["sc"]
+    Lyr, B, d = len(cross), state.batch, H * 64
+    cache_n = [[{b: cache[l][kv][b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)] \
+        if independent else None
+    lengths = state.lengths.cpu().numpy().copy()
+    p_max = max(1 if k == "step" else t.shape[1] for k, t in ops)
+    st = new_stats()
+    logits = torch.empty(B, oracle["n_vocab"], dtype=torch.float32, device=DEV)
+    with KvTrace(Lyr, B * p_max, d, force=not independent) as trace:
+        for kind, tok in ops:
+            P = 1 if kind == "step" else tok.shape[1]
+            th = tok.cpu().numpy()
+            if kind == "step":
+                lg_ref, tr = O.decode_step(W, H, th, lengths, cache, sc, cross, rows=rows)
+                trs = [tr]
+                if independent:
+                    lg_n, _ = O.decode_step(W, H, th, lengths, cache_n, sc, cross, rows=rows,
+                                            kv_transform=O.bf16_round)
+            else:
+                lg_ref, trs = O.decode_prefill(W, H, th, lengths, cache, sc, cross, rows=rows)
+                if independent:
+                    lg_n, _ = O.decode_prefill(W, H, th, lengths, cache_n, sc, cross, rows=rows,
+                                               kv_transform=O.bf16_round)
+            if not independent:
+                trace.set_force({b * P + p: trs[p]["codes"][:, :, b] for b in rows for p in range(P)}, B * P)
+            if kind == "step":
+                m.decode_step(state, tok, logits)
+            else:
+                m.decode_prefill(state, tok.contiguous(), logits)
+            kv_g = trace.take(B * P)
+            lg_g, am_g = host(logits), state.argmax.cpu().numpy().copy()
+            slots = {b: state.kv_cache[:, :, b, :, int(lengths[b]):int(lengths[b]) + P, :].cpu().numpy()
+                     for b in list(rows) + list(extra_rows)}
+            where = f"{tag} {kind} {st['ops']}"
+            if independent:
+                for b in rows:
+                    sens = rel_err(lg_n[b], lg_ref[b])
+                    st["sens"] = max(st["sens"], sens)
+                    st["tied"] += check_logits_argmax(lg_g, am_g, lg_ref, [b], where, tol=max(TOL, 2 * sens))
+            else:
+                st["tied"] += check_logits_argmax(lg_g, am_g, lg_ref, rows, where)
+            st["logit_err"] = max([st["logit_err"]] + [rel_err(lg_g[b], lg_ref[b]) for b in rows])
+            for p in range(P):
+                tr = trs[p]
+                for l in range(Lyr):
+                    for kv in range(2):
+                        for b in rows:
+                            w = f"{where} token {p} row {b} layer {l} kv {kv}"
+                            got = slots[b][l, kv, :, p, :]
+                            if independent:
+                                check_codec_exact(kv_g[l, kv, b * P + p], got, sc[l, kv], w)
+                                st["flips"] += int((got != tr["codes"][l, kv, b]).sum())
+                                st["codes"] += got.size
+                            else:
+                                assert np.array_equal(got, tr["codes"][l, kv, b]), f"{w}: forced codes not in the cache"
+                                nd, e = check_kv_against_oracle(kv_g[l, kv, b * P + p], tr["kv"][l, kv, b],
+                                                                tr["codes"][l, kv, b], sc[l, kv], w, layer=l)
+                                st["flips"] += nd
+                                st["codes"] += got.size
+                                st["kv_err"] = max(st["kv_err"], e)
+                        for b in extra_rows:
+                            check_codec_exact(kv_g[l, kv, b * P + p], slots[b][l, kv, :, p, :], sc[l, kv],
+                                              f"{where} token {p} row {b} layer {l} kv {kv} (own codes)")
+                assert gpu_codec_on_oracle_values([tr["kv"][l, kv, b] for b in rows for l in range(Lyr) for kv in (0, 1)],
+                                                  [sc[l, kv] for b in rows for l in range(Lyr) for kv in (0, 1)],
+                                                  [tr["codes"][l, kv, b] for b in rows for l in range(Lyr) for kv in (0, 1)])
+            lengths = lengths + P
+            st["ops"] += 1
+    assert int(state.dev_error[0].item()) == 0
+    assert np.array_equal(state.lengths.cpu().numpy(), lengths)
+    report(tag + (" (independent caches)" if independent else " (oracle codes forced)"), st)
+    return st
+
+
+def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None, cross_fmt="e4m3",
+                    lengths0=None, modes=("forced",)):
+    """Teacher-forced decode on the GPU from a prefilled fp8 cache against the
+    oracle on `rows`, in each of `modes` ("forced", "independent"; each from
+    the same initial state). lengths0: prefill lengths [B] (default
+    U{1..prefill_max}). cross_fp8_scale: when given, the cross-attention K/V
+    are fp8 codes in cross_fmt ("e4m3" or "e5m2") with that scale for every
+    (layer, K|V), on both sides (the GPU quantises its bf16 projections, the
+    oracle its own fp64 ones)."""
     H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
     m, W = model_for(dims, ln_random=True)
     dt = act_dtype(dims)
     enc = gen_normal(DEV, (B, T, d), dims.cfg_id, 5, bf16=dims.act == "bf16").to(dt)
     ckv = m.cross_kv(enc)
-    lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max) if prefill_max else torch.zeros(
-        B, dtype=torch.int32, device=DEV)
-    scales = torch.ones(Lyr, 2, dtype=torch.float32)
-    prefill = {}
-    if prefill_max:
-        for l in range(Lyr):
-            for kv in range(2):
-                x = gen_prefill_kv(DEV, dims.cfg_id, l, kv, B, H, prefill_max)
-                scales[l, kv] = float(O.e4m3_scale_from_amax(np.array([x.abs().max().item()], np.float32)))
-                prefill[(l, kv)] = x
-    xscales = None
+    if lengths0 is None:
+        lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max) if prefill_max else torch.zeros(
+            B, dtype=torch.int32, device=DEV)
+    lengths0 = lengths0.to(DEV)
+    scales = prefill_scales(dims, B, prefill_max) if prefill_max else torch.ones(Lyr, 2, dtype=torch.float32)
+    sc = scales.numpy()
+    xscales = xcodes = xsc = fmt = None
     if cross_fp8_scale is not None:
         xscales = np.full((Lyr, 2), np.float32(cross_fp8_scale), np.float32)
         fmt = {"e4m3": L.WHISPER_FP8_E4M3, "e5m2": L.WHISPER_FP8_E5M2}[cross_fmt]
         xcodes, xsc = m.quantize_cross_kv(ckv, scales=torch.from_numpy(xscales), fmt=fmt)
-        state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc,
-                            cross_format=fmt)
         del ckv
-    else:
-        state = DecodeState(dims, B, cap, ckv, scales, lengths0)
-    for (l, kv), x in prefill.items():
-        codes = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
-        L.whisper_fp8_quantize(x, L.WHISPER_F32, x.numel(), state.kv_scales[l, kv:kv + 1].contiguous().clone(),
-                               codes, None)
-        state.kv_cache[l, kv, :, :, :prefill_max, :] = codes
-    tokens = gen_tokens(DEV, dims.cfg_id, steps, B, dims.n_vocab)
-    logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
-    gpu_steps = []
-    for t in range(steps):
-        pos = state.lengths.clone()
-        m.decode_step(state, tokens[t], logits)
-        torch.cuda.synchronize()
-        gpu_steps.append((host(logits), state.argmax.cpu().numpy().copy(), pos.cpu().numpy()))
-    assert int(state.dev_error[0].item()) == 0
-    assert np.array_equal(state.lengths.cpu().numpy(), lengths0.cpu().numpy() + steps)
-    cache_gpu = state.kv_cache.cpu().numpy()
-
-    # ---- oracle on the chosen rows
+        ckv = None
     Wh = host_weights(W, "decoder.")
-    sc = scales.numpy()
-    enc_h = {b: host(enc[b]) for b in rows}
-    cross_rows = {b: O.cross_kv(enc_h[b], Wh, H, Lyr) for b in rows}
+    cross_rows = {b: O.cross_kv(host(enc[b]), Wh, H, Lyr) for b in rows}
     cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
     if xscales is not None:
         cross = O.cross_kv_fp8(cross, xscales, fmt=cross_fmt)
-    cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
-    lengths = lengths0.cpu().numpy().copy()
-    for (l, kv), x in prefill.items():
-        xh = x.cpu().numpy()
-        for b in rows:
-            cache[l][kv][b][:, :prefill_max, :] = O.e4m3_quantize(xh[b], sc[l, kv])
-            n0 = int(lengths[b])  # later slots were overwritten by the decode steps
-            assert np.array_equal(cache[l][kv][b][:, :n0], cache_gpu[l, kv, b, :, :n0]), \
-                "prefill codes differ between the GPU codec and the oracle codec"
-    tok = tokens.cpu().numpy()
-    n_flips = n_codes = n_tied = 0
-    for t in range(steps):
-        # the oracle continues from the GPU's codes for the new slot; they are
-        # checked against the oracle's own codes right after
-        forced = [[{b: cache_gpu[l, kv, b, :, int(lengths[b]), :] for b in rows} for kv in range(2)]
-                  for l in range(Lyr)]
-        lg_ref, tr = O.decode_step(Wh, H, tok[t], lengths, cache, sc, cross, rows=rows, forced_codes=forced)
-        lg_g, am_g, pos = gpu_steps[t]
-        n_tied += check_logits_argmax(lg_g, am_g, lg_ref, rows, f"{tag} step {t}")
-        for b in rows:
-            for l in range(Lyr):
-                for kv in range(2):
-                    own = tr["codes"][l, kv, b]
-                    ok, nf = code_mismatch_ok(forced[l][kv][b], own, tr["pre_quant"][l, kv, b])
-                    assert ok, f"{tag} step {t} row {b} layer {l} kv {kv}: {nf} fp8 codes differ beyond the band"
-                    assert codec_on_oracle_values_bit_exact(tr["pre_quant"][l, kv, b], own)
-                    n_flips += nf
-                    n_codes += H * 64
-        lengths = lengths + 1
-    say(f"  {tag}: code flips {n_flips}/{n_codes} ({100.0 * n_flips / max(n_codes, 1):.3f}%), "
-        f"tied argmax rows excluded {n_tied}/{steps * len(rows)}")
-    assert n_flips <= 0.25 * n_codes
+    tokens = gen_tokens(DEV, dims.cfg_id, steps, B, dims.n_vocab)
+    extra = [r for r in (1, B - 2) if r not in rows]
+    for mode in modes:
+        if xcodes is not None:
+            state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc,
+                                cross_format=fmt)
+        else:
+            state = DecodeState(dims, B, cap, ckv, scales, lengths0)
+        cache = prefill_both(state, dims, B, prefill_max, rows, sc) if prefill_max else \
+            [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
+        oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc, n_vocab=dims.n_vocab)
+        drive(m, state, oracle, [("step", tokens[t]) for t in range(steps)], rows, tag, mode == "independent",
+              extra_rows=extra if mode == "forced" else ())
+        del state
+        torch.cuda.empty_cache()
 
 
 def test_decode_large_v3_shape_4_layers():
@@ -288,21 +336,34 @@ def test_decode_large_v3_shape_4_layers():
     say("decode large-v3 shape, 4 layers, B=64, cap 672, prefill U[1,448], 3 steps")
     lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
     rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
-    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4")
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4", modes=("forced", "independent"))
 
 
 def test_decode_large_v3_full():
     dims = CONFIGS["v3_decode"]
-    say("decode large-v3, 32 layers, B=64, cap 672, prefill U[1,448], 2 steps")
+    say("decode large-v3, 32 layers, B=64, cap 672, prefill U[1,448], 3 steps")
     lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
     rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0))})
-    run_decode_case(dims, 64, 672, 448, 2, rows, "v3x32")
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x32", modes=("forced", "independent"))
+
+
+def test_decode_long_rows_to_capacity():
+    """Cache lengths past the self-attention kernel's first 512-key batch, up
+    to the capacity: prefill lengths U{513..670} with one row at 670, so two
+    steps write slots 670 and 671 and that row ends at exactly cap = 672."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    B, cap = 64, 672
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, B, 670, low=513)
+    lengths0[17] = 670
+    rows = sorted({17, int(np.argmin(lengths0.numpy())), 40})
+    say(f"decode large-v3 shape, 4 layers, B=64, cap 672, prefill U[513,670] (row 17 at 670), 2 steps, rows {rows}")
+    run_decode_case(dims, B, cap, 670, 2, rows, "v3x4 long", lengths0=lengths0, modes=("forced", "independent"))
 
 
 def test_decode_turbo_shape_batch90_empty_cache():
     dims = CONFIGS["turbo_longform"]
     say("decode turbo shape, 4 layers, B=90, empty cache s=1, 3 steps")
-    run_decode_case(dims, 90, 228, 0, 3, [0, 89], "turbo")
+    run_decode_case(dims, 90, 228, 0, 3, [0, 89], "turbo", modes=("forced", "independent"))
 
 
 def test_decode_fp8_cross_kv_large_v3_shape():
@@ -329,6 +390,26 @@ def test_decode_fp8_e5m2_cross_kv_large_v3_shape():
     run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 e5m2 cross", cross_fp8_scale=1.0, cross_fmt="e5m2")
 
 
+def test_cross_kv_against_oracle_sampled_rows():
+    """whisper_cross_kv's head-major output [L, 2, B, H, T, 64] against the
+    oracle's per-chunk projection K = E Wk^T, V = E Wv^T + bv, on the first and
+    last chunk of a batch of 64, all layers, every frame."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("cross K/V large-v3 shape, 4 layers, B=64, chunks 0 and 63 against the oracle")
+    m, W = model_for(dims, ln_random=True)
+    enc = gen_normal(DEV, (64, 1500, 1280), dims.cfg_id, 5, bf16=True).to(torch.bfloat16)
+    ckv = m.cross_kv(enc)
+    torch.cuda.synchronize()
+    Wh = host_weights(W, "decoder.")
+    for b in (0, 63):
+        ref = O.cross_kv(host(enc[b]), Wh, dims.n_heads, dims.n_dec_layers)
+        for l in range(dims.n_dec_layers):
+            for kv in range(2):
+                e = rel_err(host(ckv[l, kv, b]), ref[l][kv])
+                assert e < TOL, (b, l, kv, e)
+        say(f"  chunk {b}: every layer's K and V within {TOL}")
+
+
 # ------------------------------------------------------------------ tiny fp32 end to end
 def test_tiny_fp32_end_to_end():
     dims = CONFIGS["tiny_f32"]
@@ -338,17 +419,7 @@ def test_tiny_fp32_end_to_end():
     mel = m.logmel(audio)
     enc = m.encode(mel)
     ckv = m.cross_kv(enc)
-    steps = 16
-    state = DecodeState(dims, 1, 448, ckv, torch.ones(dims.n_dec_layers, 2), torch.zeros(1, dtype=torch.int32))
-    tokens = gen_tokens(DEV, dims.cfg_id, steps, 1, dims.n_vocab)
-    logits = torch.empty(1, dims.n_vocab, dtype=torch.float32, device=DEV)
-    gl, ga = [], []
-    for t in range(steps):
-        m.decode_step(state, tokens[t], logits)
-        torch.cuda.synchronize()
-        gl.append(host(logits))
-        ga.append(state.argmax.cpu().numpy().copy())
-    cache_gpu = state.kv_cache.cpu().numpy()
+    steps, cap, Lyr = 16, 448, dims.n_dec_layers
     Wh = host_weights(W)
     mref = O.log_mel(audio[0].cpu().numpy(), dims.n_mels)
     assert rel_err(host(mel)[0], mref) < 1e-3
@@ -356,24 +427,60 @@ def test_tiny_fp32_end_to_end():
     e = rel_err(host(enc)[0], eref)
     say(f"  encoder rel err {e:.2e}")
     assert e < TOL
-    cr = O.cross_kv(eref, Wh, dims.n_heads, dims.n_dec_layers)
+    cr = O.cross_kv(eref, Wh, dims.n_heads, Lyr)
     cross = [({0: k}, {0: v}) for k, v in cr]
-    cache = [[{0: np.zeros((dims.n_heads, 448, 64), np.uint8)} for _ in range(2)] for _ in range(dims.n_dec_layers)]
-    sc = np.ones((dims.n_dec_layers, 2), np.float32)
-    tok = tokens.cpu().numpy()
-    flips = 0
-    for t in range(steps):
-        forced = [[{0: cache_gpu[l, kv, 0, :, t]} for kv in range(2)] for l in range(dims.n_dec_layers)]
-        lg, tr = O.decode_step(Wh, dims.n_heads, tok[t], np.array([t]), cache, sc, cross, forced_codes=forced)
-        check_logits_argmax(gl[t], ga[t], lg, [0], f"tiny step {t}")
-        for l in range(dims.n_dec_layers):
-            for kv in range(2):
-                own = tr["codes"][l, kv, 0]
-                ok, nf = code_mismatch_ok(cache_gpu[l, kv, 0, :, t], own, tr["pre_quant"][l, kv, 0])
-                assert ok, (t, l, kv, nf)
-                assert codec_on_oracle_values_bit_exact(tr["pre_quant"][l, kv, 0], own)
-                flips += nf
-    say(f"  tiny: code flips {flips}")
+    tokens = gen_tokens(DEV, dims.cfg_id, steps, 1, dims.n_vocab)
+    sc = np.ones((Lyr, 2), np.float32)
+    for mode in ("forced", "independent"):
+        state = DecodeState(dims, 1, cap, ckv, torch.ones(Lyr, 2), torch.zeros(1, dtype=torch.int32))
+        cache = [[{0: np.zeros((dims.n_heads, cap, 64), np.uint8)} for _ in range(2)] for _ in range(Lyr)]
+        oracle = dict(W=Wh, H=dims.n_heads, cross=cross, cache=cache, sc=sc, n_vocab=dims.n_vocab)
+        drive(m, state, oracle, [("step", tokens[t]) for t in range(steps)], [0], "tiny", mode == "independent")
+
+
+def test_longform_turbo_end_to_end_first_and_last_chunk():
+    """The long-form workload end to end at the large-v3-turbo shape: 45 min of
+    piecewise tone / noise audio as 90 chunks -> log-mel -> 32-layer encoder ->
+    cross K/V (4 decoder layers) -> 4 prompt tokens in one causal prefill ->
+    3 teacher-forced steps at batch 90 from an empty fp8 cache. The oracle runs
+    chunks 0 and 89 through the same pipeline on its own."""
+    dims = CONFIGS["turbo_longform"]
+    B, P, steps, cap, Lyr, H = 90, 4, 3, 228, dims.n_dec_layers, dims.n_heads
+    rows = [0, B - 1]
+    say("long form, turbo shape: 90 chunks from 45 min of audio -> prefill 4 -> 3 steps; oracle on chunks 0, 89")
+    m, W = model_for(dims, ln_random=True)
+    audio = gen_audio_longform(DEV, dims.cfg_id, 45.0)
+    assert audio.shape[0] == B
+    mel = m.logmel(audio)
+    enc = m.encode(mel)
+    ckv = m.cross_kv(enc)
+    torch.cuda.synchronize()
+    mel_h, enc_h = {b: host(mel[b]) for b in rows}, {b: host(enc[b]) for b in rows}
+    audio_h = {b: audio[b].cpu().numpy() for b in rows}
+    del enc, mel, audio
+    torch.cuda.empty_cache()
+    Wh = host_weights(W)
+    cross_rows = {}
+    for b in rows:
+        mref = O.log_mel(audio_h[b], dims.n_mels)
+        em = rel_err(mel_h[b], mref)
+        eref = O.encoder(mref, Wh, H, dims.n_enc_layers)
+        e = rel_err(enc_h[b], eref)
+        say(f"  chunk {b}: log-mel rel err {em:.2e}, encoder rel err {e:.3e}")
+        assert em < 1e-3 and e < TOL
+        cross_rows[b] = O.cross_kv(eref, Wh, H, Lyr)
+    cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
+    toks = gen_tokens(DEV, dims.cfg_id, P + steps, B, dims.n_vocab)
+    ops = [("prefill", toks[:P].t().contiguous())] + [("step", toks[P + t]) for t in range(steps)]
+    sc = np.ones((Lyr, 2), np.float32)
+    for mode in ("forced", "independent"):
+        state = DecodeState(dims, B, cap, ckv, torch.ones(Lyr, 2), torch.zeros(B, dtype=torch.int32))
+        cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for _ in range(2)] for _ in range(Lyr)]
+        oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc, n_vocab=dims.n_vocab)
+        drive(m, state, oracle, ops, rows, "long form", mode == "independent",
+              extra_rows=[45] if mode == "forced" else ())
+        del state
+        torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ decode-state semantics
@@ -447,33 +554,20 @@ def test_decode_prefill_equals_successive_steps_and_oracle():
     m.decode_step(s2, toks[P], lg2)
     torch.cuda.synchronize()
     assert torch.equal(lg1, lg2) and torch.equal(s1.kv_cache, s2.kv_cache)
-    # oracle: P teacher-forced steps on two rows, continuing from the GPU's checked codes
+    # oracle: the same prefill on two rows from the same prefilled codes, its
+    # codes forced into the GPU's appends (tests/decode_check.py)
     rows = [0, B - 1]
     Wh = host_weights(W, "decoder.")
     cross_rows = {b: O.cross_kv(host(enc[b]), Wh, H, Lyr) for b in rows}
     cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
-    cache_gpu = s2.kv_cache.cpu().numpy()
     pre = prefill.cpu().numpy()
-    cache = [[{b: pre[l, kv, b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)]
-    lengths = lengths0.cpu().numpy().copy()
-    tok = toks.cpu().numpy()
-    scn = sc.numpy()
-    for t in range(P):
-        forced = [[{b: cache_gpu[l, kv, b, :, int(lengths[b]), :] for b in rows} for kv in range(2)]
-                  for l in range(Lyr)]
-        lg_ref, tr = O.decode_step(Wh, H, tok[t], lengths, cache, scn, cross, rows=rows, forced_codes=forced)
-        for b in rows:
-            for l in range(Lyr):
-                for kv in range(2):
-                    ok, _ = code_mismatch_ok(forced[l][kv][b], tr["codes"][l, kv, b], tr["pre_quant"][l, kv, b])
-                    assert ok
-        lengths = lengths + 1
-    # the prefill's logits are those of token P - 1 (s1 has moved on one step: compare s2's copy taken above)
-    m2 = DecodeState(dims, B, cap, ckv, sc, lengths0)
-    m2.kv_cache.copy_(prefill)
-    m.decode_prefill(m2, toks[:P].t().contiguous(), lg1)
-    torch.cuda.synchronize()
-    check_logits_argmax(host(lg1), m2.argmax.cpu().numpy(), lg_ref, rows, "prefill")
+    for mode in ("forced", "independent"):
+        st = DecodeState(dims, B, cap, ckv, sc, lengths0)
+        st.kv_cache.copy_(prefill)
+        cache = [[{b: pre[l, kv, b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)]
+        oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc.numpy(), n_vocab=dims.n_vocab)
+        drive(m, st, oracle, [("prefill", toks[:P].t().contiguous()), ("step", toks[P])], rows, "prefill",
+              mode == "independent", extra_rows=[5] if mode == "forced" else ())
 
 
 @pytest.mark.parametrize("cross_fp8", [False, True])

@@ -272,10 +272,12 @@ def test_fp8_decode_properties():
         lg_exact, _ = O.decode_step(W, H, toks[t], lengths, exact, None, cross)
         # causal: slots beyond the current position are never read
         assert np.array_equal(lg, lg_nan)
-        # the stored codes are the codec applied to the recorded pre-quantisation values
+        # the stored codes are the codec applied to the new token's K / V, and
+        # those K / V are the exact-cache step's
         for l in range(L):
             for kv in range(2):
-                assert np.array_equal(cache[l, kv, :, :, t, :], O.e4m3_encode(tr["pre_quant"][l, kv]))
+                assert np.array_equal(cache[l, kv, :, :, t, :], O.e4m3_quantize(tr["kv"][l, kv], scales[l, kv]))
+                assert np.array_equal(cache[l, kv, :, :, t, :], tr["codes"][l, kv])
         # quantisation noise is small next to the logits
         assert np.abs(lg - lg_exact).max() < 0.1 * np.abs(lg_exact).max()
     # rows are independent: computing a subset gives the same rows
@@ -306,20 +308,55 @@ def test_fp8_decode_position_zero_reads_its_own_value():
     assert np.allclose(tr["x"], x0 + v_hat, atol=1e-12)
 
 
-def test_forced_codes_equal_to_own_codes_change_nothing():
-    W, H, L, ctx, cross, toks, scales, dh = _fp8_setup(seed=9, B=2, steps=3)
-    c1 = np.zeros((L, 2, 2, H, ctx, dh), np.uint8)
+def test_prefill_matches_torch_causal_decoder():
+    """A causal prefill of P tokens per row from an exact cache gives the last
+    position's logits of the full causal torch decoder over those P tokens, and
+    with an fp8 cache it equals P single steps code for code."""
+    rng = np.random.default_rng(10)
+    d, H, L, V, ctx, Tenc, B, P = 64, 2, 2, 50, 12, 7, 2, 5
+    W = _tiny_weights(rng, d=d, n_dec=L, vocab=V, ctx=ctx)
+    enc = rng.standard_normal((B, Tenc, d))
+    toks = rng.integers(0, V, (B, P))
+    cross_b = [O.cross_kv(enc[b], W, H, L) for b in range(B)]
+    cross = [(np.stack([cross_b[b][l][0] for b in range(B)]), np.stack([cross_b[b][l][1] for b in range(B)]))
+             for l in range(L)]
+    exact = np.zeros((L, 2, B, H, ctx, d // H))
+    logits, traces = O.decode_prefill(W, H, toks, np.zeros(B, int), exact, None, cross)
+    assert len(traces) == P
+    x = T(W["decoder.token_embedding"][toks] + W["decoder.positional_embedding"][:P][None])
+    mask = torch.nn.Transformer.generate_square_subsequent_mask(P)
+    with torch.no_grad():
+        for l in range(L):
+            layer = torch.nn.TransformerDecoderLayer(d, H, 256, dropout=0.0, activation="gelu",
+                                                     batch_first=True, norm_first=True)
+            p = f"decoder.blocks.{l}."
+            _load_mha(layer.self_attn, W, p + "attn.", d)
+            _load_mha(layer.multihead_attn, W, p + "cross_attn.", d)
+            _load_ln(layer.norm1, W, p + "attn_ln")
+            _load_ln(layer.norm2, W, p + "cross_attn_ln")
+            _load_ln(layer.norm3, W, p + "mlp_ln")
+            _load_mlp(layer, W, p)
+            layer.eval()
+            x = layer(x, T(enc), tgt_mask=mask)
+        y = F.layer_norm(x[:, -1], (d,), T(W["decoder.ln.weight"]), T(W["decoder.ln.bias"]), 1e-5)
+        ref = (y @ T(W["decoder.token_embedding"]).T).numpy()
+    assert np.allclose(logits, ref, atol=1e-9)
+    # fp8 cache: the prefill is P steps in a row, code for code
+    scales = np.full((L, 2), np.float32(0.03), np.float32)
+    c1 = np.zeros((L, 2, B, H, ctx, d // H), np.uint8)
     c2 = np.zeros_like(c1)
-    for t in range(3):
-        lg1, tr1 = O.decode_step(W, H, toks[t], np.full(2, t), c1, scales, cross)
-        forced = [[{b: tr1["codes"][l, kv, b] for b in range(2)} for kv in range(2)] for l in range(L)]
-        lg2, tr2 = O.decode_step(W, H, toks[t], np.full(2, t), c2, scales, cross, forced_codes=forced)
-        assert np.array_equal(lg1, lg2) and np.array_equal(c1, c2)
-    # a forced code different from the oracle's own is what the cache holds afterwards
-    forced = [[{b: np.full((H, dh), 0x38, np.uint8) for b in range(2)} for kv in range(2)] for l in range(L)]
-    lg3, tr3 = O.decode_step(W, H, toks[0], np.full(2, 3), c2, scales, cross, forced_codes=forced)
-    assert np.all(c2[:, :, :, :, 3, :] == 0x38)
-    assert np.array_equal(tr3["codes"][0, 0], O.e4m3_quantize(tr3["pre_quant"][0, 0] * 1.0, 1.0))
+    lg1, _ = O.decode_prefill(W, H, toks, np.array([0, 3]), c1, scales, cross)
+    lengths = np.array([0, 3])
+    for p in range(P):
+        lg2, _ = O.decode_step(W, H, toks[:, p], lengths, c2, scales, cross)
+        lengths = lengths + 1
+    assert np.array_equal(lg1, lg2) and np.array_equal(c1, c2)
+
+
+def test_top2_gap_and_greedy_token():
+    lg = np.array([[0.0, 3.0, 1.0, 3.0], [5.0, -1.0, 2.5, 0.0]])
+    assert list(O.greedy_token(lg)) == [1, 0]  # lowest index among equal maxima
+    assert np.allclose(O.top2_gap(lg), [0.0, 2.5])
 
 
 def test_fp8_cross_kv_grid_values_exact_and_error_bound():

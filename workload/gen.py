@@ -189,10 +189,10 @@ def gen_tokens(device, cfg_id, steps, batch, n_vocab):
     return torch.randint(0, n_vocab, (steps, batch), generator=g, device=device, dtype=torch.int32)
 
 
-def gen_prefill_lengths(device, cfg_id, batch, max_len):
-    """Prefilled cache lengths [batch] int32, uniform over {1..max_len}."""
-    g = rng_for("cpu", cfg_id, 3)
-    return torch.randint(1, max_len + 1, (batch,), generator=g, dtype=torch.int32).to(device)
+def gen_prefill_lengths(device, cfg_id, batch, max_len, low=1):
+    """Prefilled cache lengths [batch] int32, uniform over {low..max_len}."""
+    g = rng_for("cpu", cfg_id, 3) if low == 1 else rng_for("cpu", cfg_id, 3, low)
+    return torch.randint(low, max_len + 1, (batch,), generator=g, dtype=torch.int32).to(device)
 
 
 def gen_prefill_kv(device, cfg_id, layer, kv, batch, heads, n, head_dim=64):
