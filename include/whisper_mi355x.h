@@ -252,6 +252,26 @@ whisper_status whisper_decode_step(const whisper_dims* dims, const void* packed,
                                    const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
                                    int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
+/* whisper_decode_step for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace: the step's activations, split-K partials and tile counters live
+ * in a library-owned static device array of WHISPER_NOALLOC_SCRATCH_BYTES
+ * (8 MiB) per GPU, set up on the first call on that device and held until the
+ * process ends; the call itself allocates nothing. Arguments and results are
+ * those of whisper_decode_step, except that logits must be given (non-NULL).
+ * A batch whose workspace without logits (whisper_workspace_size(dims, batch,
+ * WHISPER_WS_DECODE) less batch * n_vocab * 4 bytes, about 54 KB per row at
+ * the large-v3 shape: up to ~150 rows) exceeds the array returns
+ * WHISPER_ERR_WORKSPACE before launching anything. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller; the
+ * split-K tile counters are cleared at the start of every call. */
+#define WHISPER_NOALLOC_SCRATCH_BYTES (8u << 20)
+whisper_status whisper_decode_step_noalloc(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
+                                           const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                           const float* kv_scales, const void* cross_kv, float* logits,
+                                           int32_t* argmax, int32_t* dev_error, void* stream);
+
 /* Causal prefill of n_tokens prompt tokens per row in one pass (the pages'
  * decoder self-attention with multiple queries; showcase page,
  * flash_attn_hopper.cu card: causal mask). bf16 models only. tokens:

@@ -30,7 +30,7 @@ EXPORTS = [
     "whisper_gemm_fp8",
     "whisper_logmel_chunked",
     "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
-    "whisper_debug_kv_disarm",
+    "whisper_debug_kv_disarm", "whisper_decode_step_noalloc",
 ]
 
 DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
@@ -82,6 +82,7 @@ _SIG = {
     "whisper_cross_kv": (I, [P, P, P, I, P, P, Z, P]),
     "whisper_decode_step": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, I, P, P, P, P, Z, P]),
+    "whisper_decode_step_noalloc": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P]),
     "whisper_decode_prefill": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_fp8_workspace_size": (Z, []),
     "whisper_fp8_quantize": (I, [P, I, I, Z, P, P, P, P, Z, P]),
@@ -227,6 +228,14 @@ def whisper_decode_step(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, 
     _check(lib().whisper_decode_step(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
                                      _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax), _p(dev_error), _p(ws),
                                      ws_bytes, _stream(stream)))
+
+
+def whisper_decode_step_noalloc(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits,
+                                argmax, dev_error, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_step_noalloc(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
+                                             _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax), _p(dev_error),
+                                             _stream(stream)))
 
 
 def whisper_decode_prefill(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -184,7 +185,7 @@ Packed8 layout8(const whisper_dims* d) {
 // per 16 x 80 output tile; its partials and tile counters live here.
 constexpr int DEC_KSPLIT = 4, DEC_SPLIT_COLS = 80;
 struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, total; };
-DecWS dec_ws(const whisper_dims* d, int B) {
+DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
   size_t off = 0;
@@ -193,7 +194,7 @@ DecWS dec_ws(const whisper_dims* d, int B) {
   W.a = take(B * D * e); W.dlt = take(B * D * e); W.q = take(B * D * e);
   W.att = take(B * D * e); W.qc = take(B * D * e);
   W.hf = take((size_t)B * d->d_ffn * e);
-  W.logits = take((size_t)B * d->n_vocab * 4);
+  W.logits = with_logits ? take((size_t)B * d->n_vocab * 4) : 0;
   const size_t tiles = (size_t)((D + DEC_SPLIT_COLS - 1) / DEC_SPLIT_COLS) * ((B + 15) / 16);
   W.part = take(tiles * DEC_KSPLIT * (DEC_SPLIT_COLS / 16) * 64 * 16);
   W.n_cnt = tiles;
@@ -883,24 +884,40 @@ whisper_status whisper_cross_kv(const whisper_dims* d, const void* packed, const
   return WHISPER_OK;
 }
 
-whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, int B, int cap, const int32_t* tokens,
-                                   int32_t* lengths, uint8_t* kv_cache, const float* kv_scales, const void* cross_kv,
-                                   float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
-                                   void* stream) {
+}  // extern "C"
+
+// Allocation-free decoder step: its workspace (activations, split-K partials
+// and tile counters) lives in this file-scope device array, one copy per GPU,
+// held until the process ends. Host code uses the per-device address from
+// hipGetSymbolAddress, never the array's name.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)8 << 20;
+static_assert(NOALLOC_SCRATCH_BYTES == (size_t)WHISPER_NOALLOC_SCRATCH_BYTES, "header and library limits agree");
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+whisper_status decode_step_checks(const whisper_dims* d, const void* packed, int B, int cap, const int32_t* tokens,
+                                  int32_t* lengths, uint8_t* kv_cache, const float* kv_scales, const void* cross_kv,
+                                  const float* logits, int32_t* argmax, int32_t* dev_error, const char* who) {
   WH_CHECK(check_dims(d));
-  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_step: batch must be > 0");
-  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_step: no decoder layers");
-  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_step: kv_cap must be in 1..4096");
-  WH_CHECK(check_ptrs({packed, kv_cache, cross_kv}, "decode_step"));
-  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, "decode_step"));
-  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, "decode_step: logits not 16-byte aligned");
-  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_step: dev_error not 4-byte aligned");
-  const DecWS W = dec_ws(d, B);
-  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_step"));
+  if (B <= 0) return fail(WHISPER_ERR_INVALID_ARG, std::string(who) + ": batch must be > 0");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, std::string(who) + ": no decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, std::string(who) + ": kv_cap must be in 1..4096");
+  WH_CHECK(check_ptrs({packed, kv_cache, cross_kv}, who));
+  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, who));
+  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, std::string(who) + ": logits not 16-byte aligned");
+  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, std::string(who) + ": dev_error not 4-byte aligned");
+  return WHISPER_OK;
+}
+
+// The decoder step over workspace `ws` laid out as W (arguments checked).
+whisper_status decode_step_run(const whisper_dims* d, const void* packed, const DecWS& W, int B, int cap,
+                               const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache, const float* kv_scales,
+                               const void* cross_kv, float* logits, int32_t* argmax, int32_t* dev_error, void* ws,
+                               hipStream_t s) {
   (void)hipGetLastError();
   const Packed P = layout(d);
   const ActType t = act_of(d->act);
-  const hipStream_t s = S(stream);
   const int D = d->d_model, H = d->n_heads, T = d->n_audio_ctx, F = d->d_ffn, L = d->n_dec_layers;
   const size_t e = esz(d->act);
   float* X = at<float>(ws, W.x);
@@ -951,6 +968,64 @@ whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, in
   WH_TRY(launch_gemm_skinny(t, EPI_F32, gp(A, D, at<void>(packed, P.tok), D, B, d->n_vocab, D, nullptr, LG, d->n_vocab), s));
   WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s));
   return WHISPER_OK;
+}
+
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {nullptr};
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current.
+whisper_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WHISPER_ERR_HIP, std::string("decode_step_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(WHISPER_ERR_HIP, "decode_step_noalloc: device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(WHISPER_ERR_HIP, std::string("decode_step_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WHISPER_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+whisper_status whisper_decode_step(const whisper_dims* d, const void* packed, int B, int cap, const int32_t* tokens,
+                                   int32_t* lengths, uint8_t* kv_cache, const float* kv_scales, const void* cross_kv,
+                                   float* logits, int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  WH_CHECK(decode_step_checks(d, packed, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits, argmax,
+                              dev_error, "decode_step"));
+  const DecWS W = dec_ws(d, B);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_step"));
+  return decode_step_run(d, packed, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits, argmax,
+                         dev_error, ws, S(stream));
+}
+
+whisper_status whisper_decode_step_noalloc(const whisper_dims* d, const void* packed, int B, int cap,
+                                           const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                           const float* kv_scales, const void* cross_kv, float* logits,
+                                           int32_t* argmax, int32_t* dev_error, void* stream) {
+  WH_CHECK(decode_step_checks(d, packed, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits, argmax,
+                              dev_error, "decode_step_noalloc"));
+  if (!logits) return fail(WHISPER_ERR_INVALID_ARG, "decode_step_noalloc: logits must be given (no workspace holds them)");
+  const DecWS W = dec_ws(d, B, false);
+  if (W.total > NOALLOC_SCRATCH_BYTES)
+    return fail(WHISPER_ERR_WORKSPACE, "decode_step_noalloc: batch " + std::to_string(B) + " needs " +
+                                           std::to_string(W.total) + " bytes of scratch, the library holds " +
+                                           std::to_string(NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  WH_CHECK(scratch_for_current_device(&ws));
+  return decode_step_run(d, packed, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, logits, argmax,
+                         dev_error, ws, S(stream));
 }
 
 whisper_status whisper_decode_prefill(const whisper_dims* d, const void* packed, int B, int n_tokens, int cap,

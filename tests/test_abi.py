@@ -283,3 +283,15 @@ def test_debug_kv_hook_checked_before_launch():
         assert e.value.status == 5
     finally:
         L.whisper_debug_kv_disarm()
+
+
+def test_decode_step_noalloc_host_checks():
+    """The allocation-free step needs logits and a batch whose workspace fits
+    the library's scratch; both are checked before any launch."""
+    d = CONFIGS["v3_decode"]
+    with pytest.raises(L.WhisperError) as e:  # logits NULL
+        L.whisper_decode_step_noalloc(d, 16, 64, 672, 16, 16, 16, 16, 16, None, 16, None, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.WhisperError) as e:  # 160 rows need more than the 8 MiB scratch
+        L.whisper_decode_step_noalloc(d, 16, 160, 672, 16, 16, 16, 16, 16, 16, 16, None, stream=0)
+    assert e.value.status == 5 and "scratch" in str(e.value)
