@@ -80,7 +80,8 @@ typedef struct {
 } whisper_dims;
 
 enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3,
-       WHISPER_WS_ENCODE_FP8 = 4 /* whisper_encode_fp8 / whisper_encode_layers_fp8 */ };
+       WHISPER_WS_ENCODE_FP8 = 4 /* whisper_encode_fp8 / whisper_encode_layers_fp8 */,
+       WHISPER_WS_DECODE_ENC = 5 /* whisper_decode_step_enc / whisper_decode_prefill_enc, batch = query rows */ };
 
 /* ------------------------------------------------------------------ weights
  * Logical weights are fp32 device tensors in PyTorch layout, passed as an
@@ -286,6 +287,28 @@ whisper_status whisper_decode_prefill(const whisper_dims* dims, const void* pack
                                       int kv_cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                       const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/* Decoder step and causal prefill with the cross-attention read straight
+ * from the encoder output (the decoder cross-attention over the encoder
+ * output of the showcase page's flash_attn_hopper.cu card). As
+ * whisper_decode_step / whisper_decode_prefill, bf16 models with d_model in
+ * {512, 768, 1024, 1280}, except that enc_out [batch][n_audio_ctx][d] bf16
+ * (whisper_encode's output) replaces cross_kv. Since K = E W_k^T and
+ * V = E W_v^T + b_v are linear in E and the softmax weights sum to one, each
+ * head computes softmax((W_k,h^T q_h) . E^T / 8) over the frames, u_h =
+ * sum_t p_t E_t, and W_v,h u_h + b_v,h: the same attention, reading E once per
+ * layer (half the bytes of K and V) and never forming K or V, so no
+ * whisper_cross_kv pass is needed. ws: whisper_workspace_size(dims, batch *
+ * n_tokens, WHISPER_WS_DECODE_ENC) bytes. Errors as whisper_decode_prefill. */
+whisper_status whisper_decode_step_enc(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
+                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                       const float* kv_scales, const void* enc_out, float* logits, int32_t* argmax,
+                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+whisper_status whisper_decode_prefill_enc(const whisper_dims* dims, const void* packed, int batch, int n_tokens,
+                                          int kv_cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                          const float* kv_scales, const void* enc_out, float* logits,
+                                          int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                          void* stream);
 
 /* Decoder step with fp8 cross-attention K/V (the fp8 cross-attention site of
  * the showcase page's precision presets, whose aggressive preset takes E5M2

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libwhisper_mi355x.so")
 
 WHISPER_F32, WHISPER_BF16 = 0, 1
 WHISPER_FP8_E4M3, WHISPER_FP8_E5M2 = 0, 1
-WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE, WS_ENCODE_FP8 = 0, 1, 2, 3, 4
+WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE, WS_ENCODE_FP8, WS_DECODE_ENC = 0, 1, 2, 3, 4, 5
 
 EXPORTS = [
     "whisper_weight_count", "whisper_packed_weights_size", "whisper_pack_weights", "whisper_workspace_size",
@@ -30,7 +30,7 @@ EXPORTS = [
     "whisper_gemm_fp8",
     "whisper_logmel_chunked",
     "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
-    "whisper_debug_kv_disarm", "whisper_decode_step_noalloc",
+    "whisper_debug_kv_disarm", "whisper_decode_step_noalloc", "whisper_decode_step_enc", "whisper_decode_prefill_enc",
 ]
 
 DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
@@ -83,6 +83,8 @@ _SIG = {
     "whisper_decode_step": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, I, P, P, P, P, Z, P]),
     "whisper_decode_step_noalloc": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P]),
+    "whisper_decode_step_enc": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_decode_prefill_enc": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_prefill": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_fp8_workspace_size": (Z, []),
     "whisper_fp8_quantize": (I, [P, I, I, Z, P, P, P, P, Z, P]),
@@ -236,6 +238,22 @@ def whisper_decode_step_noalloc(dims, packed, batch, kv_cap, tokens, lengths, kv
     _check(lib().whisper_decode_step_noalloc(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
                                              _p(kv_scales), _p(cross_kv), _p(logits), _p(argmax), _p(dev_error),
                                              _stream(stream)))
+
+
+def whisper_decode_step_enc(dims, packed, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, enc_out, logits, argmax,
+                            dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_step_enc(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
+                                         _p(kv_scales), _p(enc_out), _p(logits), _p(argmax), _p(dev_error), _p(ws),
+                                         ws_bytes, _stream(stream)))
+
+
+def whisper_decode_prefill_enc(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, enc_out,
+                               logits, argmax, dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_prefill_enc(dp, _p(packed), batch, n_tokens, kv_cap, _p(tokens), _p(lengths),
+                                            _p(kv_cache), _p(kv_scales), _p(enc_out), _p(logits), _p(argmax),
+                                            _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
 
 
 def whisper_decode_prefill(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv,

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libwhisper_mi355x.so")
-SOURCES = ["gemm.hip", "decode_gemm.hip", "attention.hip", "elementwise.hip", "logmel.hip", "peak.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "decode_gemm.hip", "attention.hip", "cross_enc.hip", "elementwise.hip", "logmel.hip", "peak.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -67,9 +67,12 @@ struct EncL { size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, w1, b1, w2, b2;
 // beta-folded, with the row sums c1* beside them (see decode_gemm.hip), and
 // all decoder GEMM weights (those and wo, woc, w2) are in the MFMA fragment
 // order of decode_gemm.hip rather than row-major.
+// bf16 mode also keeps, per layer, the cross-attention key weight transposed
+// per head (wkt, [H][d][64]) and the value weight in fragment order (wvf), for
+// the cross-attention over the encoder output (cross_enc.hip).
 struct DecL {
   size_t ln1g, ln1b, wqkv, bqkv, wo, bo, ln2g, ln2b, wqc, bqc, woc, boc, ln3g, ln3b, w1, b1, w2, b2;
-  size_t c1qkv = 0, c1qc = 0, c1w1 = 0;
+  size_t c1qkv = 0, c1qc = 0, c1w1 = 0, wkt = 0, wvf = 0;
 };
 struct Packed {
   size_t conv1w = 0, conv1b = 0, conv2w = 0, conv2b = 0, pe = 0, lnpg = 0, lnpb = 0;
@@ -116,6 +119,7 @@ Packed layout(const whisper_dims* d) {
       L.w2 = take(D * F * e); L.b2 = take(D * f4);
       if (d->act == WHISPER_BF16) {
         L.c1qkv = take(3 * D * f4); L.c1qc = take(D * f4); L.c1w1 = take(F * f4);
+        L.wkt = take(D * D * e); L.wvf = take(D * D * e);
       }
       P.dec.push_back(L);
     }
@@ -200,6 +204,26 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   W.n_cnt = tiles;
   W.cnt = take(tiles * 4);
   W.xg = take((size_t)((B + 15) & ~15) * D * 4);  // prefill: the last position of each batch row, 16-row tiles
+  W.total = off;
+  return W;
+}
+
+// Cross-attention over the encoder output (decode_step_enc): q' [M][H][d],
+// chunk partials U [M][NC][H][d] bf16 and (max, sum) [M][NC][H][2] fp32, and
+// the combined u [M][H][d], after the step's own workspace.
+constexpr int XE_CU = 256;  // compute units the frame chunking balances for
+struct DecEncWS { DecWS base; size_t qp, upart, ml, u, total; int NC, SPC; };
+DecEncWS dec_ws_enc(const whisper_dims* d, int M) {
+  DecEncWS W;
+  W.base = dec_ws(d, M);
+  size_t off = W.base.total;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  cross_enc_chunks(M, d->n_audio_ctx, XE_CU, W.NC, W.SPC);
+  const size_t rows = (size_t)M * d->n_heads * d->d_model;
+  W.qp = take(rows * 2);
+  W.upart = take(rows * W.NC * 2);
+  W.ml = take((size_t)M * W.NC * d->n_heads * 2 * 4);
+  W.u = take(rows * 2);
   W.total = off;
   return W;
 }
@@ -385,7 +409,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
                                  int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
                                  int32_t* dev_error, void* ws, hipStream_t s, const uint8_t* xcodes = nullptr,
-                                 const float* xscales = nullptr, int R = 1, int xfmt = FP8_E4M3) {
+                                 const float* xscales = nullptr, int R = 1, int xfmt = FP8_E4M3,
+                                 const void* enc = nullptr, const DecEncWS* XW = nullptr) {
   // B batch rows of the cache; R tokens per row (a prefill when R > 1): the
   // activations have B * R rows, row m being token m % R of batch row m / R
   const int Bc = B;
@@ -401,13 +426,16 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
-                  u16_t* out, float* out_f32, int layer, bool split = false) {
+                  u16_t* out, float* out_f32, int layer, bool split = false, int a_group = 0) {
     DecGemmParams g{};
     g.M = B; g.N = N; g.K = K;
     g.W = at<u16_t>(packed, w_off);
     g.bias = b_off ? at<float>(packed, b_off) : nullptr;
     g.c1 = c1_off ? at<float>(packed, c1_off) : nullptr;
     g.A = A; g.lda = K; g.X = X; g.out = out; g.out_f32 = out_f32;
+    if (a_group) {  // A is u [M][H][d]: output column n reads head n / a_group's row
+      g.a_group = a_group; g.a_group_stride = K; g.lda = (long)H * K;
+    }
     g.kv_cache = kv_cache; g.kv_scales = kv_scales; g.lengths = lengths; g.dev_error = dev_error;
     g.kv_cap = cap; g.kv_B = Bc; g.kv_H = H; g.kv_layer = layer; g.d_model = D; g.rows_per_b = R;
     g.kv_pre = epi == DEPI_QKV ? g_kvtrace.buf : nullptr;
@@ -435,7 +463,20 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.wo, Lw.bo, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));
-    {
+    if (enc) {  // cross-attention over the encoder output: q' = W_k^T q per head, attention over E, W_v u + b_v
+      WH_TRY(launch_absorb_q(QC, at<void>(packed, Lw.wkt), B, H, D, at<void>(ws, XW->qp), s));
+      {
+        ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
+        // odd layers walk the frames backwards: a layer first re-reads the part of E
+        // the previous layer read last
+        WH_TRY(launch_attn_cross_enc(at<void>(ws, XW->qp), enc, B, H, T, D, R, XW->NC, XW->SPC, l & 1,
+                                     at<void>(ws, XW->upart), at<float>(ws, XW->ml), s));
+      }
+      WH_TRY(launch_absorb_combine(at<void>(ws, XW->upart), at<float>(ws, XW->ml), B, H, D, XW->NC,
+                                   at<void>(ws, XW->u), s));
+      WH_TRY(gemm(PRO_A, DEPI_STORE, Lw.wvf, P.ckvb + ((size_t)l * 2 + 1) * D * 4, 0, D, D, at<u16_t>(ws, XW->u),
+                  ATT, nullptr, l, false, 64));
+    } else {
       ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
       if (xcodes) {  // fp8 cross K/V: the fp8 attention kernel over all T keys of each row
         const uint8_t* xc = xcodes + l * (ckv_layer / 2);
@@ -602,6 +643,8 @@ whisper_status whisper_pack_weights(const whisper_dims* d, const float* const* w
                               at<float>(packed, L.c1qc), at<float>(packed, L.bqc), s));
         WH_TRY(launch_fold_ln(w[i + 20], w[i + 18], w[i + 19], w[i + 21], F, D, at<void>(packed, L.w1),
                               at<float>(packed, L.c1w1), at<float>(packed, L.b1), s));
+        WH_TRY(launch_pack_kt(w[i + 13], D, at<void>(packed, L.wkt), s));
+        WH_TRY(launch_pack_dec_weight(w[i + 14], D, D, at<void>(packed, L.wvf), s));
       }
       i += 24;
     }
@@ -622,6 +665,7 @@ size_t whisper_workspace_size(const whisper_dims* d, int batch, int which) {
     case WHISPER_WS_CROSS_KV: return 0;
     case WHISPER_WS_DECODE: return dec_ws(d, batch).total;
     case WHISPER_WS_ENCODE_FP8: return enc_ws(d, batch, true).total;
+    case WHISPER_WS_DECODE_ENC: return dec_ws_enc(d, batch).total;
   }
   return 0;
 }
@@ -1028,27 +1072,62 @@ whisper_status whisper_decode_step_noalloc(const whisper_dims* d, const void* pa
                          dev_error, ws, S(stream));
 }
 
+}  // extern "C"
+
+// Prefill of n_tokens per row (n_tokens = 1: one decode step) through the
+// fused bf16 step, with the cross-attention over precomputed K/V (cross_kv)
+// or over the encoder output (enc).
+static whisper_status prefill_impl(const char* who, const whisper_dims* d, const void* packed, int B, int n_tokens,
+                                   int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                   const float* kv_scales, const void* cross_kv, const void* enc, float* logits,
+                                   int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  const std::string w(who);
+  WH_CHECK(check_dims(d));
+  if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, w + ": bf16 models only");
+  if (B <= 0 || n_tokens <= 0) return fail(WHISPER_ERR_INVALID_ARG, w + ": batch and n_tokens must be > 0");
+  if ((long)B * n_tokens > 4096) return fail(WHISPER_ERR_SHAPE, w + ": batch * n_tokens must be <= 4096");
+  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, w + ": no decoder layers");
+  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, w + ": kv_cap must be in 1..4096");
+  if (enc && d->d_model != 512 && d->d_model != 768 && d->d_model != 1024 && d->d_model != 1280)
+    return fail(WHISPER_ERR_SHAPE, w + ": d_model must be 512, 768, 1024 or 1280");
+  WH_CHECK(check_ptrs({packed, kv_cache, enc ? enc : cross_kv}, who));
+  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, who));
+  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, w + ": logits not 16-byte aligned");
+  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, w + ": dev_error not 4-byte aligned");
+  const int M = B * n_tokens;
+  const DecEncWS XW = enc ? dec_ws_enc(d, M) : DecEncWS{dec_ws(d, M)};
+  WH_CHECK(check_ws(ws, ws_bytes, enc ? XW.total : XW.base.total, who));
+  (void)hipGetLastError();
+  const Packed P = layout(d);
+  float* LG = logits ? logits : at<float>(ws, XW.base.logits);
+  return decode_step_fused(d, packed, P, XW.base, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, LG, argmax,
+                           dev_error, ws, S(stream), nullptr, nullptr, n_tokens, FP8_E4M3, enc, enc ? &XW : nullptr);
+}
+
+extern "C" {
+
 whisper_status whisper_decode_prefill(const whisper_dims* d, const void* packed, int B, int n_tokens, int cap,
                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                       const float* kv_scales, const void* cross_kv, float* logits, int32_t* argmax,
                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
-  WH_CHECK(check_dims(d));
-  if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, "decode_prefill: bf16 models only");
-  if (B <= 0 || n_tokens <= 0) return fail(WHISPER_ERR_INVALID_ARG, "decode_prefill: batch and n_tokens must be > 0");
-  if ((long)B * n_tokens > 4096) return fail(WHISPER_ERR_SHAPE, "decode_prefill: batch * n_tokens must be <= 4096");
-  if (d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "decode_prefill: no decoder layers");
-  if (cap <= 0 || cap > 4096) return fail(WHISPER_ERR_SHAPE, "decode_prefill: kv_cap must be in 1..4096");
-  WH_CHECK(check_ptrs({packed, kv_cache, cross_kv}, "decode_prefill"));
-  WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, "decode_prefill"));
-  if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, "decode_prefill: logits not 16-byte aligned");
-  if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, "decode_prefill: dev_error not 4-byte aligned");
-  const DecWS W = dec_ws(d, B * n_tokens);
-  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_prefill"));
-  (void)hipGetLastError();
-  const Packed P = layout(d);
-  float* LG = logits ? logits : at<float>(ws, W.logits);
-  return decode_step_fused(d, packed, P, W, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, LG, argmax,
-                           dev_error, ws, S(stream), nullptr, nullptr, n_tokens);
+  return prefill_impl("decode_prefill", d, packed, B, n_tokens, cap, tokens, lengths, kv_cache, kv_scales, cross_kv,
+                      nullptr, logits, argmax, dev_error, ws, ws_bytes, stream);
+}
+
+whisper_status whisper_decode_step_enc(const whisper_dims* d, const void* packed, int B, int cap,
+                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                       const float* kv_scales, const void* enc_out, float* logits, int32_t* argmax,
+                                       int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl("decode_step_enc", d, packed, B, 1, cap, tokens, lengths, kv_cache, kv_scales, nullptr, enc_out,
+                      logits, argmax, dev_error, ws, ws_bytes, stream);
+}
+
+whisper_status whisper_decode_prefill_enc(const whisper_dims* d, const void* packed, int B, int n_tokens, int cap,
+                                          const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                          const float* kv_scales, const void* enc_out, float* logits, int32_t* argmax,
+                                          int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl("decode_prefill_enc", d, packed, B, n_tokens, cap, tokens, lengths, kv_cache, kv_scales,
+                      nullptr, enc_out, logits, argmax, dev_error, ws, ws_bytes, stream);
 }
 
 whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed, int B, int cap,

@@ -85,13 +85,18 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) wfr[cb] = p.W + (long)min((n0 >> 4) + cb, NF - 1) * S * 512 + lane * 8;
   long arow[MB];
+  // grouped A: this column tile's rows of A start at its group's offset
+  const long agoff = p.a_group > 0 ? (long)(n0 / p.a_group) * p.a_group_stride : 0;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1);
+  for (int mb = 0; mb < MB; ++mb) arow[mb] = (long)min(m0 + mb * 16 + (lane & 15), M - 1) * p.lda + agoff;
   // x tiles (dec_x_index): this lane's 4 + 4 values of k-step s sit at
   // xoff + 512 s and 256 floats further
   long xoff[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) xoff[mb] = (arow[mb] >> 4) * S * 512 + ((lane >> 4) * 16 + (arow[mb] & 15)) * 4;
+  for (int mb = 0; mb < MB; ++mb) {
+    const long r = min(m0 + mb * 16 + (lane & 15), M - 1);
+    xoff[mb] = (r >> 4) * S * 512 + ((lane >> 4) * 16 + (r & 15)) * 4;
+  }
 
   // ---- epilogue: the MB * CB output blocks (16 rows x 16 columns) go to waves
   // 0 .. MB*CB-1, one each. A block's operands are fetched by its wave before
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
         xa[XIN ? SL : 0][mb] = *(const float4*)x_;                                             \
         xb[XIN ? SL : 0][mb] = *(const float4*)(x_ + 256);                                     \
       } else {                                                                                 \
-        av[XIN ? 0 : SL][mb] = *(const uint4*)(p.A + arow[mb] * p.lda + k_ + kq);              \
+        av[XIN ? 0 : SL][mb] = *(const uint4*)(p.A + arow[mb] + k_ + kq);                      \
       }                                                                                        \
     }                                                                                          \
   }
@@ -368,6 +373,7 @@ hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int m
   if (p.M <= 0 || p.M > 4096 || p.N <= 0 || p.K <= 0 || p.K % 32) return hipErrorInvalidValue;
   if (p.ks > 1 && (pro != PRO_A || !p.part || !p.cnt || p.ks > 16 || (p.K / 32) % (p.ks * DG_WAVES)))
     return hipErrorInvalidValue;  // split-K: bf16 activations, whole k-steps per wave, workspace given
+  if (p.a_group > 0 && (pro != PRO_A || p.a_group % (16 * cb))) return hipErrorInvalidValue;
   if (pro == PRO_X) {
     switch (epi) {
       case DEPI_QKV: return dec_launch<PRO_X, DEPI_QKV>(p, mb, cb, s);

@@ -85,12 +85,33 @@ struct DecGemmParams {
   // rows per batch row (prefill of R tokens per row: row m is batch row m / R
   // at position lengths[m / R] + m % R); 0 or 1 for one token per row
   int rows_per_b;
+  // PRO_A with one A row per group of a_group output columns (0: off): the A
+  // row of output column n starts a_group_stride elements further per group
+  // (A + m * lda + (n / a_group) * a_group_stride); a_group must be a
+  // multiple of the workgroup's column tile
+  int a_group; long a_group_stride;
 };
 void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
 hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
                           void* Wf, float* c1, float* b2, hipStream_t s);
 hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStream_t s);
+
+// ------------------------------------------------------------------ cross-attention over the encoder output (cross_enc.hip)
+// W_kT[h][n][j] = bf16(W_k[h * 64 + j][n]) from the fp32 [d, d] key weight
+hipError_t launch_pack_kt(const float* wk, int d, void* wkt, hipStream_t s);
+// q'[m][h][:] = W_k,h^T q[m][h*64 : h*64+64] (bf16 in and out)
+hipError_t launch_absorb_q(const void* q, const void* wkt, int M, int H, int d, void* qp, hipStream_t s);
+// frame chunks per query row and sub-tiles (32 frames) per chunk
+void cross_enc_chunks(int M, int T, int n_cu, int& NC, int& SPC);
+// per (row m, chunk c): unnormalised U [M][NC][H][d] bf16 and (max, sum) [M][NC][H][2];
+// query row m reads encoder row m / rows_per_b of E [B][T][d]
+// reverse != 0: each chunk's sub-tiles are walked last to first
+hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, int T, int d, int rows_per_b, int NC,
+                                 int SPC, int reverse, void* upart, float* ml, hipStream_t s);
+// u [M][H][d] bf16 = the chunks' U combined with their softmax weights
+hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int H, int d, int NC, void* u,
+                                 hipStream_t s);
 
 // ------------------------------------------------------------------ LayerNorm
 // h is in the activation type (or fp32 when h_f32); residual and total are the

@@ -141,6 +141,12 @@ class Whisper:
         """tokens [B, P]: P prompt tokens per row in one pass (equal to P decode steps)."""
         B, n_tok = tokens.shape
         assert B == state.batch and state.cross_codes is None
+        if state.enc is not None:
+            ws, nb = self.workspace(B * n_tok, L.WS_DECODE_ENC)
+            L.whisper_decode_prefill_enc(self.dims, self.packed, B, n_tok, state.cap, tokens.contiguous(),
+                                         state.lengths, state.kv_cache, state.kv_scales, state.enc, logits,
+                                         state.argmax, state.dev_error, ws, nb)
+            return state.argmax
         ws, nb = self.workspace(B * n_tok, L.WS_DECODE)
         L.whisper_decode_prefill(self.dims, self.packed, B, n_tok, state.cap, tokens.contiguous(), state.lengths,
                                  state.kv_cache, state.kv_scales, state.cross_kv, logits, state.argmax,
@@ -149,6 +155,11 @@ class Whisper:
 
     def decode_step(self, state, tokens, logits=None):
         B = state.batch
+        if state.enc is not None:
+            ws, nb = self.workspace(B, L.WS_DECODE_ENC)
+            L.whisper_decode_step_enc(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
+                                      state.kv_scales, state.enc, logits, state.argmax, state.dev_error, ws, nb)
+            return state.argmax
         ws, nb = self.workspace(B, L.WS_DECODE)
         if state.cross_codes is not None:
             L.whisper_decode_step_xq(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
@@ -161,18 +172,20 @@ class Whisper:
 
 
 class DecodeState:
-    """Caller-owned decode state: fp8 self-KV cache, scales, lengths, cross K/V
-    (bf16, or fp8 codes in cross_format with per-(layer, K|V) scales from
-    quantize_cross_kv)."""
+    """Caller-owned decode state: fp8 self-KV cache, scales, lengths, and the
+    cross-attention source: cross K/V (bf16, or fp8 codes in cross_format
+    with per-(layer, K|V) scales from quantize_cross_kv), or the encoder
+    output itself (enc, [B, 1500, d] bf16: decode_step_enc)."""
 
     def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda", cross_codes=None,
-                 cross_scales=None, cross_format=L.WHISPER_FP8_E4M3):
+                 cross_scales=None, cross_format=L.WHISPER_FP8_E4M3, enc=None):
         self.batch, self.cap = batch, cap
         self.kv_cache = torch.zeros(dims.n_dec_layers, 2, batch, dims.n_heads, cap, 64, dtype=torch.uint8,
                                     device=device)
         self.kv_scales = kv_scales.to(device=device, dtype=torch.float32).contiguous()
         self.lengths = lengths.to(device=device, dtype=torch.int32).contiguous().clone()
         self.cross_kv = cross_kv
+        self.enc = enc
         self.cross_codes, self.cross_scales = cross_codes, cross_scales
         self.cross_format = cross_format
         self.argmax = torch.zeros(batch, dtype=torch.int32, device=device)

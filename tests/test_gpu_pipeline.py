@@ -283,14 +283,15 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
 
 
 def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None, cross_fmt="e4m3",
-                    lengths0=None, modes=("forced",)):
+                    lengths0=None, modes=("forced",), from_enc=False):
     """Teacher-forced decode on the GPU from a prefilled fp8 cache against the
     oracle on `rows`, in each of `modes` ("forced", "independent"; each from
     the same initial state). lengths0: prefill lengths [B] (default
     U{1..prefill_max}). cross_fp8_scale: when given, the cross-attention K/V
     are fp8 codes in cross_fmt ("e4m3" or "e5m2") with that scale for every
     (layer, K|V), on both sides (the GPU quantises its bf16 projections, the
-    oracle its own fp64 ones)."""
+    oracle its own fp64 ones). from_enc: the GPU attends over the encoder
+    output itself (whisper_decode_step_enc) instead of projected K/V."""
     H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
     m, W = model_for(dims, ln_random=True)
     dt = act_dtype(dims)
@@ -320,6 +321,8 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale
         if xcodes is not None:
             state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc,
                                 cross_format=fmt)
+        elif from_enc:
+            state = DecodeState(dims, B, cap, None, scales, lengths0, enc=enc)
         else:
             state = DecodeState(dims, B, cap, ckv, scales, lengths0)
         cache = prefill_both(state, dims, B, prefill_max, rows, sc) if prefill_max else \
@@ -358,6 +361,30 @@ def test_decode_long_rows_to_capacity():
     rows = sorted({17, int(np.argmin(lengths0.numpy())), 40})
     say(f"decode large-v3 shape, 4 layers, B=64, cap 672, prefill U[513,670] (row 17 at 670), 2 steps, rows {rows}")
     run_decode_case(dims, B, cap, 670, 2, rows, "v3x4 long", lengths0=lengths0, modes=("forced", "independent"))
+
+
+def test_decode_from_encoder_output_large_v3_shape():
+    """The cross-attention read straight from the encoder output
+    (whisper_decode_step_enc: q' = W_k,h^T q_h, attention over E, W_v u + b_v)
+    against the oracle, which forms K and V and attends over them."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode from the encoder output, large-v3 shape, 4 layers, B=64, cap 672, prefill U[1,448], 3 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 enc", modes=("forced", "independent"), from_enc=True)
+
+
+def test_decode_from_encoder_output_full_and_ragged_batch():
+    """The same at 32 layers and batch 64, and at a batch of 37 rows (another
+    frame chunking: the chunk count follows the batch)."""
+    dims = CONFIGS["v3_decode"]
+    say("decode from the encoder output, large-v3, 32 layers, B=64, 2 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0))})
+    run_decode_case(dims, 64, 672, 448, 2, rows, "v3x32 enc", from_enc=True)
+    dims4 = dims.with_(n_dec_layers=4)
+    say("decode from the encoder output, large-v3 shape, 4 layers, B=37, 2 steps")
+    run_decode_case(dims4, 37, 672, 448, 2, [0, 36], "v3x4 enc B=37", from_enc=True)
 
 
 def test_decode_turbo_shape_batch90_empty_cache():
@@ -457,7 +484,7 @@ def test_longform_turbo_end_to_end_first_and_last_chunk():
     torch.cuda.synchronize()
     mel_h, enc_h = {b: host(mel[b]) for b in rows}, {b: host(enc[b]) for b in rows}
     audio_h = {b: audio[b].cpu().numpy() for b in rows}
-    del enc, mel, audio
+    del mel, audio
     torch.cuda.empty_cache()
     Wh = host_weights(W)
     cross_rows = {}
@@ -473,12 +500,13 @@ def test_longform_turbo_end_to_end_first_and_last_chunk():
     toks = gen_tokens(DEV, dims.cfg_id, P + steps, B, dims.n_vocab)
     ops = [("prefill", toks[:P].t().contiguous())] + [("step", toks[P + t]) for t in range(steps)]
     sc = np.ones((Lyr, 2), np.float32)
-    for mode in ("forced", "independent"):
-        state = DecodeState(dims, B, cap, ckv, torch.ones(Lyr, 2), torch.zeros(B, dtype=torch.int32))
+    for mode, src in (("forced", "kv"), ("independent", "kv"), ("forced", "enc")):
+        state = DecodeState(dims, B, cap, ckv if src == "kv" else None, torch.ones(Lyr, 2),
+                            torch.zeros(B, dtype=torch.int32), enc=enc if src == "enc" else None)
         cache = [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for _ in range(2)] for _ in range(Lyr)]
         oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc, n_vocab=dims.n_vocab)
-        drive(m, state, oracle, ops, rows, "long form", mode == "independent",
-              extra_rows=[45] if mode == "forced" else ())
+        drive(m, state, oracle, ops, rows, "long form" + (" from the encoder output" if src == "enc" else ""),
+              mode == "independent", extra_rows=[45] if mode == "forced" else ())
         del state
         torch.cuda.empty_cache()
 
