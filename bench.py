@@ -3,16 +3,18 @@
 
 One step is one pass of the whole path over one batch of synthetic input:
 64 chunks of 30 s of 16 kHz audio -> GPU log-mel -> 32-layer encoder ->
-cross-attention K/V of the 32 decoder layers -> 224 teacher-forced decoder
-steps at batch 64 over an fp8 e4m3 self-KV cache prefilled to seeded lengths
-U{1..448} (capacity 672). Random N(0, 0.02) weights, synthetic tones + noise;
-every input is resident in HBM before the timed region.
+224 teacher-forced decoder steps at batch 64 over an fp8 e4m3 self-KV cache
+prefilled to seeded lengths U{1..448} (capacity 672), the cross-attention of
+each decoder layer computed from the encoder output in its absorbed form
+(whisper_decode_step_enc: no cross K/V are formed). Random N(0, 0.02)
+weights, synthetic tones + noise; every input is resident in HBM before the
+timed region.
 
 Prints one JSON line: value = RTFx (audio seconds per wall second) of the
 whole step, plus decode tokens/s, per-stage times, the roofline of the
-dominant kernel (decoder cross-attention, HBM-bound) timed with HIP events on
-its own stream inside the timed region, and the CPU oracle timed on a bounded
-sample on the host cores.
+dominant kernel (decoder cross-attention over the encoder output,
+HBM-bound) timed with HIP events on its own stream inside the timed region,
+and the CPU oracle timed on a bounded sample on the host cores.
 """
 import argparse
 import json
@@ -41,7 +43,8 @@ def parse():
     ap.add_argument("--no-fp8-encoder", action="store_true",
                     help="skip the extra step with the mixed_fp8 encoder sites (E4M3 QKV and FFN GEMMs)")
     ap.add_argument("--no-fp8-cross", action="store_true",
-                    help="skip the extra step with fp8 e4m3 cross-attention K/V (reported apart from value)")
+                    help="skip the extra steps through explicit cross-attention K/V (bf16, fp8 e4m3, fp8 e5m2; "
+                         "reported apart from value)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -119,9 +122,8 @@ def main():
     tokens = gen_tokens(DEV, dims.cfg_id, TD, B, dims.n_vocab)
     mel = torch.empty(B, dims.n_mels, 3000, dtype=torch.float32, device=DEV)
     enc = torch.empty(B, T, d, dtype=torch.bfloat16, device=DEV)
-    ckv = torch.empty(Ldec, 2, B, H, T, 64, dtype=torch.bfloat16, device=DEV)
     logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
-    state = DecodeState(dims, B, cap, ckv, torch.ones(Ldec, 2), lengths0)
+    state = DecodeState(dims, B, cap, None, torch.ones(Ldec, 2), lengths0, enc=enc)
     fp8_ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=DEV)
     for l in range(Ldec):
         for kv in range(2):
@@ -133,7 +135,7 @@ def main():
             state.kv_cache[l, kv, :, :, :prefill_max, :] = codes
             del x, codes
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f}s; cross K/V buffer {ckv.numel() * 2 / 1e9:.2f} GB, "
+    log(f"inputs ready in {time.time() - t0:.1f}s; encoder output {enc.numel() * 2 / 1e9:.2f} GB, "
         f"KV cache {state.kv_cache.numel() / 1e9:.2f} GB")
 
     def run_step(ev=None):
@@ -145,14 +147,11 @@ def main():
         model.encode(mel, out=enc)
         if ev:
             ev[2].record()
-        model.cross_kv(enc, out=ckv)
-        if ev:
-            ev[3].record()
         state.lengths.copy_(lengths0)
         for t in range(TD):
             model.decode_step(state, tokens[t], logits)
         if ev:
-            ev[4].record()
+            ev[3].record()
 
     for _ in range(args.warmup):
         run_step()
@@ -160,13 +159,14 @@ def main():
     assert int(state.dev_error[0].item()) == 0
     log(f"warmup done at {time.time() - t0:.1f}s")
 
-    # dominant kernel: decoder cross-attention, events on the launch stream inside the timed region
+    # dominant kernel: decoder cross-attention over the encoder output, events
+    # on the launch stream inside the timed region
     n_ev = min(2048, Ldec * TD * args.steps)
     k_start = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     k_stop = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in k_start + k_stop:
         e.record()
-    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
 
     L.whisper_profile_arm(L.PROF_DECODE_CROSS_ATTENTION, k_start, k_stop)
@@ -180,11 +180,13 @@ def main():
     elapsed = t_end - t_begin
     ms_step = elapsed / args.steps * 1e3
 
-    stage_names = ["logmel", "encode", "cross_kv", "decode"]
+    stage_names = ["logmel", "encode", "decode"]
     stage_ms = {n: float(np.mean([stage_ev[s][i].elapsed_time(stage_ev[s][i + 1]) for s in range(args.steps)]))
                 for i, n in enumerate(stage_names)}
     cross_ms = float(np.mean([k_start[i].elapsed_time(k_stop[i]) for i in range(n_rec)]))
-    cross_bytes = 2 * B * H * T * 64 * 2 + 2 * B * d * 2  # K and V, q in, output out
+    # per batch row and layer: the encoder output (T x d bf16) read once, the
+    # absorbed query q' (H x d bf16) in, the per-head weighted sum u (H x d bf16) out
+    cross_bytes = B * (T * d * 2 + 2 * H * d * 2)
     cross_gbs = cross_bytes / (cross_ms * 1e-3) / 1e9
     enc_flop = B * (2 * 3000 * 3 * dims.n_mels * d + 2 * 1500 * 3 * d * d) + B * 32 * (
         2 * T * d * 3 * d + 2 * T * d * d + 2 * 2 * T * d * dims.d_ffn + 4 * T * T * d)
@@ -198,13 +200,15 @@ def main():
 
     fp8e = None
     if not args.no_fp8_encoder:
-        fp8e = fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch,
-                                np)
+        fp8e = fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np)
     fp8x = {}
     if not args.no_fp8_cross:
-        for fmt in ("e4m3", "e5m2"):
-            fp8x[fmt] = fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L,
-                                       torch, np, DecodeState, fmt)
+        ckv = torch.empty(Ldec, 2, B, H, T, 64, dtype=torch.bfloat16, device=DEV)
+        for fmt in (None, "e4m3", "e5m2"):
+            fp8x[fmt] = cross_kv_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L,
+                                      torch, np, DecodeState, fmt)
+        del ckv
+        torch.cuda.empty_cache()
 
     kernels = {}
     if not args.no_kernel_probes:
@@ -224,16 +228,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded tones + noise audio, random N(0,0.02) weights, seeded token ids)",
         "config": {"workload": f"large-v3 full path: {B} x 30 s chunks -> log-mel -> 32-layer encoder -> "
-                               f"cross K/V -> {TD} teacher-forced decode steps, batch {B}, fp8 e4m3 self-KV "
-                               f"prefilled U[1,448], cap {cap}",
+                               f"{TD} teacher-forced decode steps, batch {B}, fp8 e4m3 self-KV "
+                               f"prefilled U[1,448], cap {cap}; cross-attention over the encoder output "
+                               f"in absorbed form",
                    "batch": B, "decode_steps": TD, "audio_s_per_step": B * AUDIO_S},
         "decode_tok_per_s": round(decode_tok_s, 1),
         "encoder_tflops": round(enc_flop / (stage_ms["encode"] * 1e-3) / 1e12, 1),
         "stage_ms": {k: round(v, 3) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "attn_decode_cross_kernel (decoder cross-attention)",
+        "roofline": {"kernel": "attn_cross_enc_kernel (decoder cross-attention over the encoder output)",
                      "bound": "hbm", "achieved": round(cross_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(cross_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic("attn_decode_cross_kernel"),
+                     "traffic": counted_traffic("attn_cross_enc_kernel"),
                      "bytes_per_launch": cross_bytes, "avg_launch_us": round(cross_ms * 1e3, 2),
                      "launches_timed": n_rec},
         "kernels": kernels,
@@ -257,7 +262,7 @@ def main():
             xc = leg["cross_attention"]
             xc["peak_measured"] = peaks["hbm_read_gbs"]
             xc["frac_of_measured"] = round(xc["achieved"] / peaks["hbm_read_gbs"], 4)
-        result["fp8_cross_kv" if fmt == "e4m3" else "fp8_cross_kv_e5m2"] = leg
+        result[{None: "bf16_cross_kv", "e4m3": "fp8_cross_kv", "e5m2": "fp8_cross_kv_e5m2"}[fmt]] = leg
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dims, audio, lengths0, tokens, state, np, torch, prefill_max)
     print(json.dumps(result))
@@ -322,10 +327,10 @@ def kernel_probes(model, mel, enc, state, tokens, logits, lengths0, dims, B, TD,
 def long_form(L, torch, Whisper, DecodeState):
     """The pages' long-form workload, end to end: 45 min of 16 kHz synthetic
     audio (piecewise 2-8 s tone / noise segments) as 90 x 30 s chunks -> GPU
-    log-mel -> 32-layer encoder -> cross K/V of the 4 decoder layers -> 4
-    prompt + 224 teacher-forced decode steps at batch 90, fp8 KV cache from
-    empty (cap 228; the prompt fed by one causal prefill), at the
-    large-v3-turbo shape with random weights. One
+    log-mel -> 32-layer encoder -> 4 prompt + 224 teacher-forced decode steps
+    of the 4 decoder layers at batch 90 (cross-attention over the encoder
+    output), fp8 KV cache from empty (cap 228; the prompt fed by one causal
+    prefill), at the large-v3-turbo shape with random weights. One
     warm-up pass, then one timed pass; RTFx = 2700 s of audio / wall time."""
     from workload import CONFIGS, gen_audio_longform, gen_tokens, gen_weights
     from workload.configs import RUN
@@ -341,10 +346,10 @@ def long_form(L, torch, Whisper, DecodeState):
     tokens = gen_tokens("cuda", dims.cfg_id, n_tok, B, dims.n_vocab)
     mel = torch.empty(B, dims.n_mels, 3000, dtype=torch.float32, device="cuda")
     enc = torch.empty(B, dims.n_audio_ctx, dims.d_model, dtype=torch.bfloat16, device="cuda")
-    ckv = torch.empty(dims.n_dec_layers, 2, B, dims.n_heads, dims.n_audio_ctx, 64, dtype=torch.bfloat16, device="cuda")
     logits = torch.empty(B, dims.n_vocab, dtype=torch.float32, device="cuda")
-    state = DecodeState(dims, B, cap, ckv, torch.ones(dims.n_dec_layers, 2), torch.zeros(B, dtype=torch.int32))
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    state = DecodeState(dims, B, cap, None, torch.ones(dims.n_dec_layers, 2), torch.zeros(B, dtype=torch.int32),
+                        enc=enc)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     prompt = tokens[:run["prompt"]].t().contiguous()
 
     def once(record):
@@ -353,14 +358,12 @@ def long_form(L, torch, Whisper, DecodeState):
         if record: ev[1].record()
         m.encode(mel, out=enc)
         if record: ev[2].record()
-        m.cross_kv(enc, out=ckv)
-        if record: ev[3].record()
         state.lengths.zero_()
         m.decode_prefill(state, prompt, logits)   # the prompt tokens in one causal pass
-        if record: ev[4].record()
+        if record: ev[3].record()
         for t in range(run["prompt"], n_tok):
             m.decode_step(state, tokens[t], logits)
-        if record: ev[5].record()
+        if record: ev[4].record()
 
     once(False)
     torch.cuda.synchronize()
@@ -371,17 +374,17 @@ def long_form(L, torch, Whisper, DecodeState):
     assert int(state.dev_error[0].item()) == 0
     audio_s = run["minutes"] * 60.0
     st = {n: round(ev[i].elapsed_time(ev[i + 1]), 3)
-          for i, n in enumerate(["logmel", "encode", "cross_kv", "prefill", "decode"])}
+          for i, n in enumerate(["logmel", "encode", "prefill", "decode"])}
     log(f"long form: {audio_s:.0f} s of audio in {wall * 1e3:.1f} ms, RTFx {audio_s / wall:.0f}, stages {st}")
     out = {"workload": f"large-v3-turbo shape (32 encoder, 4 decoder layers): {run['minutes']:.0f} min of 16 kHz "
-                       f"synthetic audio -> {B} x 30 s chunks -> log-mel -> encoder -> cross K/V -> "
+                       f"synthetic audio -> {B} x 30 s chunks -> log-mel -> encoder -> "
                        f"{run['prompt']} prompt tokens in one causal prefill + {run['steps']} teacher-forced "
-                       f"decode steps, batch {B}, "
+                       f"decode steps (cross-attention over the encoder output), batch {B}, "
                        f"fp8 e4m3 self-KV from empty, cap {cap}",
            "rtfx": round(audio_s / wall, 1), "ms": round(wall * 1e3, 3), "stage_ms": st,
            "decode_tok_per_s": round(B * run["steps"] / (st["decode"] * 1e-3), 1),
            "data": "synthetic (seeded piecewise tone/noise audio, random N(0,0.02) weights, seeded token ids)"}
-    del m, audio, mel, enc, ckv, logits, state
+    del m, audio, mel, enc, logits, state
     torch.cuda.empty_cache()
     return out
 
@@ -416,7 +419,7 @@ def measured_peaks(L, torch):
             "how": "register-resident MFMA 16x16x32 bf16 loop, 16384 waves; 16-byte streaming read of 4 GiB"}
 
 
-def fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np):
+def fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np):
     """One more full step with the encoder's mixed_fp8 sites (query, key,
     value, fc1, fc2 as E4M3 GEMMs with per-tensor weight and per-chunk
     activation amax scales), the rest unchanged. Reported apart from `value`:
@@ -426,7 +429,6 @@ def fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths
         model.logmel(audio, out=mel)
         model.encode_fp8(mel, out=enc)
         if ev: ev[1].record()
-        model.cross_kv(enc, out=ckv)
         state.lengths.copy_(lengths0)
         for t in range(TD):
             model.decode_step(state, tokens[t], logits)
@@ -461,7 +463,7 @@ def fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths
         f"fc1 fp8 GEMM {ms * 1e3:.0f} us ({tf:.0f} TFLOP/s)")
     return {"ms_per_step": round(wall * 1e3, 3), "rtfx": round(B * AUDIO_S / wall, 2),
             "stage_ms": {"logmel_encode": round(ev[0].elapsed_time(ev[1]), 3),
-                         "cross_kv_decode": round(ev[1].elapsed_time(ev[2]), 3)},
+                         "decode": round(ev[1].elapsed_time(ev[2]), 3)},
             "encode_only_ms": round(enc_wall * 1e3, 3),
             "encoder_ffn1_gemm_fp8": {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
@@ -470,18 +472,20 @@ def fp8_encoder_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths
             "note": "mixed_fp8 preset sites in E4M3 (encoder query/key/value, fc1, fc2); not the configured workload"}
 
 
-def fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np,
-                   DecodeState, fmt="e4m3"):
-    """One more full step with the cross-attention K/V held as fp8 codes in
-    `fmt` ("e4m3", or "e5m2" as the aggressive preset has it; one amax scale
-    per layer and K|V, quantised from the bf16 K/V inside the step), decoded
-    through whisper_decode_step_xq. Reported apart from `value`: the
-    configured workload keeps bf16 cross K/V."""
-    code = {"e4m3": L.WHISPER_FP8_E4M3, "e5m2": L.WHISPER_FP8_E5M2}[fmt]
+def cross_kv_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np,
+                  DecodeState, fmt=None):
+    """One more full step through explicit cross-attention K/V: the K/V of
+    every decoder layer projected once per batch (whisper_cross_kv), then the
+    decode reads them, as bf16 (fmt None, whisper_decode_step) or as fp8 codes
+    in `fmt` ("e4m3", or "e5m2" as the aggressive preset has it; one amax
+    scale per layer and K|V, quantised inside the step; whisper_decode_step_xq).
+    Reported apart from `value`: the configured workload reads the encoder
+    output in absorbed form instead."""
     H, T = dims.n_heads, dims.n_audio_ctx
-    xcodes = torch.empty(ckv.shape, dtype=torch.uint8, device=ckv.device)
-    sx = DecodeState(dims, 1, 1, None, state.kv_scales, lengths0[:1],
-                     cross_format=code)  # small placeholder cache, replaced below
+    code = None if fmt is None else {"e4m3": L.WHISPER_FP8_E4M3, "e5m2": L.WHISPER_FP8_E5M2}[fmt]
+    xcodes = None if fmt is None else torch.empty(ckv.shape, dtype=torch.uint8, device=ckv.device)
+    sx = DecodeState(dims, 1, 1, None if fmt else ckv, state.kv_scales, lengths0[:1],
+                     cross_format=code if fmt else L.WHISPER_FP8_E4M3)  # small placeholder cache, replaced below
     sx.batch, sx.cap, sx.kv_cache, sx.lengths = B, state.cap, state.kv_cache, state.lengths
     sx.argmax, sx.dev_error = state.argmax, state.dev_error
 
@@ -491,7 +495,8 @@ def fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0,
         model.encode(mel, out=enc)
         model.cross_kv(enc, out=ckv)
         if ev: ev[1].record()
-        sx.cross_codes, sx.cross_scales = model.quantize_cross_kv(ckv, codes=xcodes, fmt=code)
+        if fmt is not None:
+            sx.cross_codes, sx.cross_scales = model.quantize_cross_kv(ckv, codes=xcodes, fmt=code)
         if ev: ev[2].record()
         state.lengths.copy_(lengths0)
         for t in range(TD):
@@ -515,19 +520,23 @@ def fp8_cross_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0,
     n_rec = L.whisper_profile_disarm()
     assert int(state.dev_error[0].item()) == 0
     x_ms = float(np.mean([ks[i].elapsed_time(ke[i]) for i in range(n_rec)]))
-    x_bytes = 2 * B * H * T * 64 + 2 * B * dims.d_model * 2  # K and V codes, q in, output out
+    elt = 2 if fmt is None else 1
+    x_bytes = 2 * B * H * T * 64 * elt + 2 * B * dims.d_model * 2  # K and V, q in, output out
     dec_ms = ev[2].elapsed_time(ev[3])
-    log(f"fp8 {fmt} cross K/V step: {wall * 1e3:.1f} ms, decode {dec_ms:.1f} ms, cross-attention {x_ms * 1e3:.1f} us "
+    name = fmt or "bf16"
+    log(f"{name} cross K/V step: {wall * 1e3:.1f} ms, decode {dec_ms:.1f} ms, cross-attention {x_ms * 1e3:.1f} us "
         f"({x_bytes / (x_ms * 1e-3) / 1e9:.0f} GB/s)")
+    stage = {"logmel_encode_cross_kv": round(ev[0].elapsed_time(ev[1]), 3), "decode": round(dec_ms, 3)}
+    if fmt is not None:
+        stage["quantize_cross_kv"] = round(ev[1].elapsed_time(ev[2]), 3)
     return {"ms_per_step": round(wall * 1e3, 3), "rtfx": round(B * AUDIO_S / wall, 2),
-            "decode_tok_per_s": round(B * TD / (dec_ms * 1e-3), 1),
-            "stage_ms": {"logmel_encode_cross_kv": round(ev[0].elapsed_time(ev[1]), 3),
-                         "quantize_cross_kv": round(ev[1].elapsed_time(ev[2]), 3), "decode": round(dec_ms, 3)},
+            "decode_tok_per_s": round(B * TD / (dec_ms * 1e-3), 1), "stage_ms": stage,
             "cross_attention": {"bound": "hbm", "bytes_per_launch": x_bytes, "avg_launch_us": round(x_ms * 1e3, 2),
                                 "achieved": round(x_bytes / (x_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(x_bytes / (x_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                 "launches_timed": n_rec},
-            "note": f"{fmt} cross-attention K/V, one amax scale per layer and K|V; not the configured workload"}
+            "note": (f"{fmt} cross-attention K/V, one amax scale per layer and K|V" if fmt else
+                     "bf16 cross-attention K/V projected once per batch") + "; not the configured workload"}
 
 
 def cpu_baseline(dims, audio, lengths0, tokens, state, np, torch, prefill_max):

@@ -188,7 +188,7 @@ Packed8 layout8(const whisper_dims* d) {
 // The MLP down-projection (K = d_ffn) runs split-K over DEC_KSPLIT workgroups
 // per 16 x 80 output tile; its partials and tile counters live here.
 constexpr int DEC_KSPLIT = 4, DEC_SPLIT_COLS = 80;
-struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, total; };
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, amx, total; };
 DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
@@ -204,6 +204,7 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   W.n_cnt = tiles;
   W.cnt = take(tiles * 4);
   W.xg = take((size_t)((B + 15) & ~15) * D * 4);  // prefill: the last position of each batch row, 16-row tiles
+  W.amx = take((size_t)B * ((d->n_vocab + 15) / 16) * 8);  // argmax: per-row maxima of 16-column blocks
   W.total = off;
   return W;
 }
@@ -401,10 +402,12 @@ whisper_status check_ws(void* ws, size_t have, size_t need, const char* what) {
 }
 
 // Decoder step in bf16 with the residual + LayerNorm folded into the GEMMs:
-// 9 launches per layer (QKV + cache append, self-attention, out-proj +
-// residual, cross-query, cross-attention and its combine, cross-out +
-// residual, MLP up, MLP down + residual), then the vocabulary projection and
-// the argmax. The residual stream stays fp32.
+// per layer QKV + cache append, self-attention, out-proj + residual,
+// cross-query, cross-attention (over cross K/V: one launch; over the encoder
+// output: query absorption, attention, combine, value projection), cross-out
+// + residual, MLP up, MLP down + residual; then the vocabulary projection,
+// whose epilogue also takes per-block row maxima, and the argmax over those.
+// The residual stream stays fp32.
 whisper_status decode_step_fused(const whisper_dims* d, const void* packed, const Packed& P, const DecWS& W, int B,
                                  int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
@@ -440,6 +443,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     g.kv_cap = cap; g.kv_B = Bc; g.kv_H = H; g.kv_layer = layer; g.d_model = D; g.rows_per_b = R;
     g.kv_pre = epi == DEPI_QKV ? g_kvtrace.buf : nullptr;
     g.kv_force = epi == DEPI_QKV ? g_kvtrace.force : nullptr;
+    g.amax_part = epi == DEPI_F32 ? at<int2>(ws, W.amx) : nullptr;  // the vocabulary projection
     int mb, cb;
     dec_gemm_tiles(B, N, mb, cb);
     // split-K where the long K would otherwise leave a third of the CUs idle
@@ -498,7 +502,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     B = Bc;
   }
   WH_TRY(gemm(PRO_X, DEPI_F32, P.lmw, P.lmb2, P.lmc1, d->n_vocab, D, nullptr, nullptr, LG, 0));
-  WH_TRY(launch_argmax(LG, B, d->n_vocab, argmax, lengths, s, R));
+  WH_TRY(launch_argmax_part(at<int2>(ws, W.amx), B, (d->n_vocab + 15) / 16, argmax, lengths, s, R));
   return WHISPER_OK;
 }
 

@@ -281,14 +281,48 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   if (!ewave) return;
 
   // ---- epilogue: lane holds rows emb*16 + (lane>>4)*4 + r of column en
+  float vr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ml = emb * 16 + (lane >> 4) * 4 + r;
+    vr[r] = XIN ? s_rs[ml] * (v4[r] - s_mu[ml] * e_c1) + e_bias : v4[r] + e_bias;
+  }
+  if constexpr (EPI == DEPI_F32) {
+    if (p.amax_part) {
+      // greedy argmax, first stage: each row's largest value over this block's
+      // 16 columns (the 16 lanes of a row group), lowest column on ties, NaN
+      // and columns past N never chosen
+      const int NB = (N + 15) >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = vr[r];
+        int idx = en;
+        if (en >= N || !(v == v)) {
+          v = -INFINITY;
+          idx = 0x7fffffff;
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float ov = __shfl_xor(v, o, 64);
+          const int oi = __shfl_xor(idx, o, 64);
+          if (ov > v || (ov == v && oi < idx)) {
+            v = ov;
+            idx = oi;
+          }
+        }
+        // blocks wholly past N (the last column tile's tail) have no entry
+        const int m = m0 + emb * 16 + (lane >> 4) * 4 + r, blk = (n0 >> 4) + ecb;
+        if ((lane & 15) == 0 && m < M && blk < NB) p.amax_part[(long)m * NB + blk] = make_int2(__float_as_int(v), idx);
+      }
+    }
+  }
   if (en >= N) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int ml = emb * 16 + (lane >> 4) * 4 + r, m = m0 + ml;
     if (m >= M) continue;
     const int n = en;
-    float v = v4[r];
-    v = XIN ? s_rs[ml] * (v - s_mu[ml] * e_c1) + e_bias : v + e_bias;
+    const float v = vr[r];
     if constexpr (EPI == DEPI_RESID) {
       p.X[dec_x_index(m, n, N)] = e_x[r] + v;
     } else if constexpr (EPI == DEPI_F32) {

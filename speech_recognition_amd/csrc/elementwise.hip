@@ -498,6 +498,46 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int
   return hipGetLastError();
 }
 
+// Second stage of the greedy argmax over the per-block maxima the vocabulary
+// projection writes ([B][NB] as (float bits, column)): the same rule as
+// argmax_kernel (largest value, lowest column on ties, NaN never chosen, 0 for
+// a row with no candidate). One workgroup per row.
+__global__ __launch_bounds__(256) void argmax_part_kernel(const int2* part, int NB, int32_t* out, int32_t* lengths,
+                                                          int len_inc) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int2* row = part + (size_t)b * NB;
+  float best = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int i = tid; i < NB; i += 256) {
+    const int2 e = row[i];
+    const float v = __int_as_float(e.x);
+    if (v > best || (v == best && e.y < idx)) { best = v; idx = e.y; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((tid & 63) == 0) { sv[tid >> 6] = best; si[tid >> 6] = idx; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (sv[w] > best || (sv[w] == best && si[w] < idx)) { best = sv[w]; idx = si[w]; }
+    out[b] = idx == 0x7fffffff ? 0 : idx;
+    if (lengths) lengths[b] += len_inc;
+  }
+}
+
+hipError_t launch_argmax_part(const int2* part, int B, int NB, int32_t* argmax, int32_t* lengths, hipStream_t s,
+                              int len_inc) {
+  if (B <= 0 || NB <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_part_kernel, dim3(B), dim3(256), 0, s, part, NB, argmax, lengths, len_inc);
+  return hipGetLastError();
+}
+
 // Row-major fp32 rows <-> the 16-row tiles of dec_x_index (one workgroup per row).
 __global__ __launch_bounds__(256) void x_tiles_kernel(const float* src, float* dst, int d, int to_tiles) {
   const long m = blockIdx.x;

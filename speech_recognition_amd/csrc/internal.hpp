@@ -90,6 +90,10 @@ struct DecGemmParams {
   // (A + m * lda + (n / a_group) * a_group_stride); a_group must be a
   // multiple of the workgroup's column tile
   int a_group; long a_group_stride;
+  // DEPI_F32 (NULL: off): per row, the largest value of each 16-column block
+  // and its column (lowest on ties; NaN never chosen), [M][ceil(N / 16)] as
+  // (float bits, column); argmax_part reduces them
+  int2* amax_part;
 };
 void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
@@ -172,6 +176,8 @@ hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, con
                         int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0,
                         int x_tiled = 0, int rows_per_b = 1);  // x_tiled: x in the 16-row tiles of dec_x_index;
                         // rows_per_b (R): B rows, row m is token m of batch row m / R at lengths[m / R] + m % R
+hipError_t launch_argmax_part(const int2* part, int B, int NB, int32_t* argmax, int32_t* lengths, hipStream_t s,
+                              int len_inc = 1);
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s,
                          int len_inc = 1);
 // fp32 rows [M, d] (row-major) to the 16-row tiles of dec_x_index (to_tiles

@@ -132,9 +132,12 @@ def gpu_codec_on_oracle_values(kv_ref_list, scale_list, codes_ref_list, device="
 def check_logits_argmax(lg_gpu, am_gpu, lg_ref, rows, tag, tol=TOL):
     """Per row: logits within tol (max-normalised); argmax equal to the
     oracle's unless the row is tied (oracle top-1 - top-2 gap at most twice
-    the row's largest logit difference). Returns the number of tied rows."""
+    the row's largest logit difference). The argmax is also checked exactly
+    against the GPU's own logits: the first largest value of the row.
+    Returns the number of tied rows."""
     n_tied = 0
     for b in rows:
+        assert am_gpu[b] == int(np.argmax(lg_gpu[b])), f"{tag} row {b}: argmax is not the first max of its logits"
         e = rel_err(lg_gpu[b], lg_ref[b])
         assert e < tol, f"{tag} row {b}: logits rel err {e:.3e} (bar {tol:.3e})"
         if O.top2_gap(lg_ref[b]) <= 2 * np.abs(lg_gpu[b] - lg_ref[b]).max():

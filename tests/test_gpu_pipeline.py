@@ -239,6 +239,8 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
                 m.decode_prefill(state, tok.contiguous(), logits)
             kv_g = trace.take(B * P)
             lg_g, am_g = host(logits), state.argmax.cpu().numpy().copy()
+            # the fused argmax of every row is the first largest value of the logits it returned
+            assert np.array_equal(am_g, np.argmax(lg_g, axis=1)), f"{tag}: argmax is not the first max of its logits"
             slots = {b: state.kv_cache[:, :, b, :, int(lengths[b]):int(lengths[b]) + P, :].cpu().numpy()
                      for b in list(rows) + list(extra_rows)}
             where = f"{tag} {kind} {st['ops']}"
