@@ -210,20 +210,22 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
 }
 
 // Cross-attention over the encoder output (decode_step_enc): q' [M][H][d],
-// chunk partials U [M][NC][H][d] bf16 and (max, sum) [M][NC][H][2] fp32, and
-// the combined u [M][H][d], after the step's own workspace.
-constexpr int XE_CU = 256;  // compute units the frame chunking balances for
-struct DecEncWS { DecWS base; size_t qp, upart, ml, u, total; int NC, SPC; };
+// the row-segment partials U [n_wg * kmax][H][d] bf16 and (max, sum)
+// [n_wg * kmax][H][2] fp32, and the combined u [M][H][d], after the step's own
+// workspace.
+constexpr int XE_CU = 256;  // compute units the frame sequence is shared over
+struct DecEncWS { DecWS base; size_t qp, upart, ml, u, total; XePlan plan; };
 DecEncWS dec_ws_enc(const whisper_dims* d, int M) {
   DecEncWS W;
   W.base = dec_ws(d, M);
   size_t off = W.base.total;
   auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
-  cross_enc_chunks(M, d->n_audio_ctx, XE_CU, W.NC, W.SPC);
+  cross_enc_plan(M, d->n_audio_ctx, XE_CU, W.plan);
   const size_t rows = (size_t)M * d->n_heads * d->d_model;
+  const size_t slots = (size_t)W.plan.n_wg * W.plan.kmax;
   W.qp = take(rows * 2);
-  W.upart = take(rows * W.NC * 2);
-  W.ml = take((size_t)M * W.NC * d->n_heads * 2 * 4);
+  W.upart = take(slots * d->n_heads * d->d_model * 2);
+  W.ml = take(slots * d->n_heads * 2 * 4);
   W.u = take(rows * 2);
   W.total = off;
   return W;
@@ -473,10 +475,10 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
         ProfScope ps(WHISPER_PROF_DECODE_CROSS_ATTENTION, s);
         // odd layers walk the frames backwards: a layer first re-reads the part of E
         // the previous layer read last
-        WH_TRY(launch_attn_cross_enc(at<void>(ws, XW->qp), enc, B, H, T, D, R, XW->NC, XW->SPC, l & 1,
+        WH_TRY(launch_attn_cross_enc(at<void>(ws, XW->qp), enc, B, H, T, D, R, XW->plan, l & 1,
                                      at<void>(ws, XW->upart), at<float>(ws, XW->ml), s));
       }
-      WH_TRY(launch_absorb_combine(at<void>(ws, XW->upart), at<float>(ws, XW->ml), B, H, D, XW->NC,
+      WH_TRY(launch_absorb_combine(at<void>(ws, XW->upart), at<float>(ws, XW->ml), B, H, D, XW->plan,
                                    at<void>(ws, XW->u), s));
       WH_TRY(gemm(PRO_A, DEPI_STORE, Lw.wvf, P.ckvb + ((size_t)l * 2 + 1) * D * 4, 0, D, D, at<u16_t>(ws, XW->u),
                   ATT, nullptr, l, false, 64));

@@ -12,9 +12,10 @@
 //
 // Per layer:
 //   absorb_q_kernel       q'[m][h][:] = W_k,h^T q_h       (W_k packed per head, transposed)
-//   attn_cross_enc_kernel  per (query row, frame chunk): scores S = E q'^T, online
-//                          softmax per head, U = P^T E; unnormalised U and the
-//                          chunk's (max, sum) per head
+//   attn_cross_enc_kernel  per workgroup, an even share of all rows' frames: scores
+//                          S = E q'^T, online softmax per head, U = P^T E;
+//                          unnormalised U and (max, sum) per head for each row
+//                          segment of the share
 //   absorb_combine_kernel u[m][h][:] = sum_c w_c U_c / sum_c w_c l_c
 //   value projection      the decoder GEMM with one A row per head group
 //                          (decode_gemm.hip), + b_v
@@ -88,33 +89,40 @@ hipError_t launch_absorb_q(const void* q, const void* wkt, int M, int H, int d, 
 }
 
 // ------------------------------------------------------------------ attention over E
-// One workgroup per (query row m, chunk c of the frames); NW waves, wave w
-// owning CB blocks of 32 columns of E (d = NW * CB * 32). Frames go in
-// sub-tiles of 32:
-//  * S^T [32 frames x 32 heads] = E_sub q'^T with MFMA 32x32x16 (heads padded
-//    to 32 with zero rows of q'); each wave contracts its own columns, and the
-//    NW partial tiles are summed through LDS;
-//  * online softmax per head: in the S^T layout lane l holds head l % 32 for 16
-//    of the frames (the other 16 in lane l ^ 32), so its max, sum and rescale
-//    factor are per lane;
-//  * U^T [32 CB columns x 32 heads] += E_sub^T P^T, the E^T fragments read from
-//    the wave's LDS slice with the gfx950 LDS transpose read.
-// Streaming: E is read once and decode is bound by HBM, so each wave keeps two
-// sub-tiles of loads in flight (two register stages, 2 x 10 KB per wave at
-// d = 1280) while it computes on a third held in LDS.
-// LDS slice of a wave: 2 CB k-blocks (16 columns each) of 32 frame rows x 32
-// bytes; frame f of k-block kb sits at row f ^ (kb & 3), so the fragment reads
-// stay conflict-free (a permutation within aligned groups of 4 rows). Each wave
-// reads only its own slice.
-constexpr int XE_SUB = 32;
-// q' rows in LDS are padded by 16 bytes so the 20 rows a fragment read touches
-// (one per head, same columns) spread over the banks; partial scores are kept
-// for the real heads only: element (i, g, head) of a wave's 32x32 tile at
-// i * 2 XE_MAXH + g XE_MAXH + head.
-constexpr int XE_MAXH = 20;
+// The frames of all query rows form one sequence of sub-tiles of 16 frames,
+// G = M * nsub long (row-major: row m's sub-tiles are m * nsub .. m * nsub +
+// nsub - 1). Workgroup w takes the contiguous share [w G / n_wg, (w + 1) G /
+// n_wg), so every compute unit gets the same number of sub-tiles whatever
+// the batch; a share may begin or end inside a row, and each row segment it
+// covers leaves one partial (unnormalised U, running max, sum) in slot
+// w * kmax + (row - first row of the share).
+//
+// In a workgroup, NW waves each own CB blocks of 32 columns of E (d = NW CB
+// 32). Per sub-tile:
+//  * S [16 frames x 32 heads] partial over the wave's columns with MFMA
+//    16x16x32 (E and q' from registers; heads past H are zero rows of q'),
+//    summed over the waves through LDS;
+//  * online softmax per head (the U layout: lane l holds head l % 32 for 8 of
+//    the frames, the other 8 in lane l ^ 32);
+//  * U^T [32 columns x 32 heads] += E^T P^T with MFMA 32x32x16, the E^T
+//    fragments read from LDS with the gfx950 transpose read.
+// Software pipeline per row segment, one barrier per sub-tile. The global
+// loads put E straight into the A operand of the score MFMAs (lane l: frame
+// l % 16, eight columns), XR sub-tiles ahead. In step i a wave computes the
+// partial scores of sub-tile i + 1 from those registers, stores the same
+// registers into its LDS slice (two stages) for the transposed reads of U, and
+// issues the loads of sub-tile i + 1 + XR into them; after the barrier it
+// takes the summed scores of sub-tile i through softmax into U while a few
+// threads sum the partials of sub-tile i + 1. A share that crosses a row
+// boundary runs one pipeline per row (q' is loaded once per row segment).
+constexpr int XE_F = 16;      // frames per sub-tile
+constexpr int XE_MAXH = 20;   // heads (real ones are stored, padded ones are zero)
+constexpr int XE_HS = 20;     // floats per head in a score tile (16 frames + 4 pad: conflict-free rows)
+constexpr int XE_XR = 2;      // register stages of global loads in flight
+constexpr int XE_MIN_PER_WG = 4;
 
-__device__ __forceinline__ int xe_off(int kb, int f, int col) {  // u16 offset in a wave's slice
-  return kb * 512 + ((f ^ (kb & 3)) << 4) + col;
+__device__ __forceinline__ int xe_off(int kb, int f, int col) {  // u16 offset in a wave's slice of one stage
+  return kb * (XE_F * 16) + ((f ^ (kb & 3)) << 4) + col;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -122,168 +130,138 @@ __device__ __forceinline__ uint2 xe_read_tr16(const u16* p) {
   return bitcast<uint2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p));
 }
 
-// NW waves x CB column blocks; QREG: q' held in registers for the whole chunk
-// (else in LDS, re-read per sub-tile); STAGES: sub-tiles of loads in flight
-// in registers (1 or 2). reverse != 0 walks the chunk's sub-tiles last to
-// first (alternate layers reverse, so a layer first re-reads the part of E the
-// previous layer read last, while it may still sit in the last-level cache).
-template <int NW, int CB, bool QREG, int STAGES>
+template <int NW, int CB>
 __global__ __launch_bounds__(NW * 64) void attn_cross_enc_kernel(const u16* __restrict__ qp, const u16* __restrict__ E,
-                                                                 int H, int T, int NC, int SPC, int rows_per_b,
-                                                                 int reverse, u16* __restrict__ upart,
+                                                                 int H, int T, int nsub, long G, int n_wg, int kmax,
+                                                                 int rows_per_b, int reverse, u16* __restrict__ upart,
                                                                  float* __restrict__ ml) {
-  constexpr int WC = CB * 32;        // columns per wave
+  constexpr int WC = CB * 32;         // columns per wave
   constexpr int d = NW * WC;
-  constexpr int NCH = WC / 8;        // 16-byte chunks per frame row of a wave's slice
-  constexpr int QS = WC + 8;         // q' row stride in LDS (u16)
-  constexpr int SN = 32 * XE_MAXH;   // stored score elements per wave tile
-  constexpr int KS = 2 * CB;         // 16-column k-steps per wave
-  __shared__ __attribute__((aligned(16))) u16 sE[NW][2 * CB * 512];
-  __shared__ __attribute__((aligned(16))) u16 sQ[QREG ? 1 : NW][QREG ? 8 : XE_MAXH * QS];
-  __shared__ __attribute__((aligned(16))) float sS[NW][SN];
-  __shared__ __attribute__((aligned(16))) float sSum[SN];
-  const int m = blockIdx.x / NC, c = blockIdx.x - (blockIdx.x / NC) * NC;
-  // the wave index is uniform across the wave: keep it (and the slice base and
-  // buffer resource derived from it) in scalar registers
+  constexpr int SLICE = 2 * CB * XE_F * 16;  // u16 per wave per stage
+  constexpr int SN = XE_MAXH * XE_HS; // floats per score tile
+  __shared__ __attribute__((aligned(16))) u16 sE[2][NW][SLICE];
+  __shared__ __attribute__((aligned(16))) float sS[2][NW][SN];
+  __shared__ __attribute__((aligned(16))) float sSum[2][SN];
+
+  const int w = blockIdx.x;
+  const long g0 = (long)w * G / n_wg, g1 = (long)(w + 1) * G / n_wg;
+  const int n = (int)(g1 - g0);
+  const int row0 = (int)(g0 / nsub);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
   const int col0 = wave * WC;
-  const bool hv = l32 < H;  // this lane's head is real (H <= XE_MAXH)
-  const u16* Eb = E + (long)(m / rows_per_b) * T * d + col0;
-  const int t_begin = c * SPC * XE_SUB, t_end = min(T, t_begin + SPC * XE_SUB);
-  const int nsub = (t_end - t_begin + XE_SUB - 1) / XE_SUB;
-  u16* sw = sE[wave];
-  // lane-major score tiles: a real-head lane's 16 values (frames of its half g)
-  // are 16 consecutive floats at (g * XE_MAXH + l32) * 16
-  const int so = (g * XE_MAXH + l32) * 16;
+  // sub-tile i of this share: global index, its row and first frame
+  auto gidx = [&](int i) -> long { return reverse ? g1 - 1 - i : g0 + i; };
+  auto row_of = [&](int i) -> int { return (int)(gidx(i) / nsub); };
+  auto t0_of = [&](int i) -> int { return (int)(gidx(i) - (gidx(i) / nsub) * nsub) * XE_F; };
 
-  // q' of this row and this wave's columns (the B operand of the score MFMAs:
-  // lane holds head l32, columns ks*16 + g*8 .. +7)
-  bf16x8 qreg[QREG ? KS : 1];
-  u16* sq = sQ[QREG ? 0 : wave];
-  if constexpr (QREG) {
+  // ---- E of one sub-tile in the score MFMAs' A layout: register ks of lane
+  // l holds frame l % 16, columns 32 ks + 8 (l / 16) .. +7 of the wave's
+  // columns; frames past T read frame T - 1 (their scores are masked)
+  const int fl = lane & 15, kk = lane >> 4;
+  uint4 rg[XE_XR][CB];
+  auto gload = [&](int slot, int i) {
+    const int r = row_of(i), fr = min(t0_of(i) + fl, T - 1);
+    const u16* base = E + (long)(r / rows_per_b) * T * d;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+    const uint32_t off = (uint32_t)(fr * d + col0 + kk * 8) * 2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (hv) v = *(const uint4*)(qp + ((long)m * H + l32) * d + col0 + ks * 16 + g * 8);
-      qreg[ks] = bitcast<bf16x8>(v);
-    }
-  } else {
-    for (int e = lane; e < H * NCH; e += 64) {
-      const int h = e / NCH, k = e - (e / NCH) * NCH;
-      *(uint4*)&sq[h * QS + k * 8] = *(const uint4*)(qp + ((long)m * H + h) * d + col0 + k * 8);
-    }
-  }
+    for (int ks = 0; ks < CB; ++ks)
+      rg[slot][ks] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rc, off + ks * 64, 0, 0));
+  };
+  // into the wave's LDS slice: k-block 2 ks + kk / 2, frame fl, column 8 (kk % 2)
+  auto sstore = [&](int slot, int stage) {
+    u16* sw = sE[stage][wave];
+#pragma unroll
+    for (int ks = 0; ks < CB; ++ks) *(uint4*)&sw[xe_off(2 * ks + (kk >> 1), fl, (kk & 1) * 8)] = rg[slot][ks];
+  };
 
-  // staging of a sub-tile (32 frames x WC columns): loads 0..7 of a lane take
-  // frame 4 i + lane / 16, 16-byte chunk lane % 16 of the first 128 columns
-  // (4 frames x 256 bytes per instruction); for CB = 5, loads 8, 9 take frame
-  // lane / 4 + 16 j, chunk 16 + lane % 4 of the last 32 columns. Every LDS
-  // store of a lane is its base plus a constant. Frames past T read frame
-  // T - 1 (their scores are masked). Buffer loads take a 32-bit byte offset
-  // from the wave's base.
-  static_assert(CB == 4 || CB == 5, "128 or 160 columns per wave");
-  constexpr int NLD = CB == 5 ? 10 : 8;
-  const __amdgpu_buffer_rsrc_t erc = __builtin_amdgcn_make_buffer_rsrc((void*)Eb, (short)0, 0x7fffffff, 0x00020000);
-  const int ka = lane & 15, fa = lane >> 4;       // pattern A
-  const int kb4 = 16 + (lane & 3), fb = lane >> 2;  // pattern B (CB = 5)
-  u16* const sta = &sw[xe_off(ka >> 1, fa, (ka & 1) * 8)];   // + 64 i
-  u16* const stb = &sw[xe_off(kb4 >> 1, fb, (kb4 & 1) * 8)];  // + 256 j
-  uint4 ra[NLD], rb[STAGES == 2 ? NLD : 1];
-  auto tsub = [&](int s_) { return t_begin + (reverse ? nsub - 1 - s_ : s_) * XE_SUB; };
-  auto gload = [&](uint4* rg, int t0) {
+  // ---- q' of one row for this wave's columns: the B operand of the score
+  // MFMAs, lane l holding head 16 hb + l % 16, columns 32 ks + 8 (l / 16) ..+7
+  uint4 qreg[2][CB];
+  auto qload = [&](int r) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int fr = min(t0 + i * 4 + fa, T - 1);
-      rg[i] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(erc, (uint32_t)(fr * d * 2 + ka * 16), 0, 0));
-    }
-    if constexpr (CB == 5) {
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = hb * 16 + fl;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int fr = min(t0 + j * 16 + fb, T - 1);
-        rg[8 + j] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(erc, (uint32_t)(fr * d * 2 + kb4 * 16), 0, 0));
+      for (int ks = 0; ks < CB; ++ks) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (h < H) v = *(const uint4*)(qp + ((long)r * H + h) * d + col0 + ks * 32 + kk * 8);
+        qreg[hb][ks] = v;
       }
     }
   };
-  auto sstore = [&](const uint4* rg) {
+
+  // ---- partial scores of the sub-tile in register stage slot, into
+  // sS[buf][wave]: element (frame f, head h) at h * XE_HS + f, real heads only
+  auto scores = [&](int slot, int buf) {
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *(uint4*)(sta + i * 64) = rg[i];
-    if constexpr (CB == 5) {
+    for (int ks = 0; ks < CB; ++ks)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) *(uint4*)(stb + j * 256) = rg[8 + j];
+      for (int hb = 0; hb < 2; ++hb)
+        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(rg[slot][ks]), bitcast<bf16x8>(qreg[hb][ks]),
+                                                          acc[hb], 0, 0, 0);
+    // output lane l, element e: frame 4 (l / 16) + e, head 16 hb + l % 16
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = hb * 16 + fl;
+      if (h < H) *(f32x4*)&sS[buf][wave][h * XE_HS + kk * 4] = acc[hb];
+    }
+  };
+  // the waves' partials of a score tile summed in wave order (threads < 4 H)
+  auto reduce = [&](int buf) {
+    if (tid < H * 4) {
+      const int e = (tid >> 2) * XE_HS + (tid & 3) * 4;
+      f32x4 v = *(const f32x4*)&sS[buf][0][e];
+#pragma unroll
+      for (int w_ = 1; w_ < NW; ++w_) v += *(const f32x4*)&sS[buf][w_][e];
+      *(f32x4*)&sSum[buf][e] = v;
     }
   };
 
+  // ---- softmax state and U accumulators of the current row segment
+  const int g = lane >> 5, l32 = lane & 31, jl = lane & 15;
+  const bool hv = l32 < H;
   f32x16 o[CB];
+  float m_run = -INFINITY, l_run = 0.f;  // running max in base-2 units (score * log2(e) / 8)
+  auto reset = [&]() {
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;  // running max in base-2 units (score * log2(e) / 8), per head
+      for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  reset();
   const float cs = 1.4426950408889634f * 0.125f;
-  // E^T fragment addressing (see xe_read_tr16): group G = lane / 16 serves
-  // k-block cb*2 + (G & 1) and frame quad G >> 1 of each 8 frames
-  const int G = lane >> 4, jl = lane & 15;
-
-  // one sub-tile held in LDS, starting at frame t0
-  auto compute = [&](const int t0) {
-    // ---- partial scores over this wave's columns
-    f32x16 st;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st[i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ef = bitcast<bf16x8>(*(const uint4*)&sw[xe_off(ks, l32, g * 8)]);
-      bf16x8 qf;
-      if constexpr (QREG) {
-        qf = qreg[ks];
-      } else {
-        uint4 qv = make_uint4(0u, 0u, 0u, 0u);
-        if (hv) qv = *(const uint4*)&sq[l32 * QS + ks * 16 + g * 8];
-        qf = bitcast<bf16x8>(qv);
-      }
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef, qf, st, 0, 0, 0);
-    }
+  // softmax of sub-tile i's summed scores, then U += E^T P^T from LDS stage st.
+  // This lane's frames (in the P fragment's order): 4 g .. 4 g + 3, 8 + 4 g .. 8 + 4 g + 3
+  auto softmax_u = [&](int i, int st, int buf) {
+    const int t0 = t0_of(i);
+    float sc[8];
     if (hv) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *(f32x4*)&sS[wave][so + i4 * 4] = f32x4{st[i4 * 4], st[i4 * 4 + 1], st[i4 * 4 + 2], st[i4 * 4 + 3]};
-    }
-    __syncthreads();
-    for (int e = tid * 4; e < SN; e += NW * 64 * 4) {
-      f32x4 v = *(const f32x4*)&sS[0][e];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) v += *(const f32x4*)&sS[w][e];
-      *(f32x4*)&sSum[e] = v;
-    }
-    __syncthreads();
-    // ---- online softmax of this lane's head over the sub-tile's frames
-    float sc[16];
-    if (hv) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 v = *(const f32x4*)&sSum[so + i4 * 4];
-        sc[i4 * 4] = v[0]; sc[i4 * 4 + 1] = v[1]; sc[i4 * 4 + 2] = v[2]; sc[i4 * 4 + 3] = v[3];
-      }
+      const f32x4 a = *(const f32x4*)&sSum[buf][l32 * XE_HS + 4 * g];
+      const f32x4 b = *(const f32x4*)&sSum[buf][l32 * XE_HS + 8 + 4 * g];
+      sc[0] = a[0]; sc[1] = a[1]; sc[2] = a[2]; sc[3] = a[3];
+      sc[4] = b[0]; sc[5] = b[1]; sc[6] = b[2]; sc[7] = b[3];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int fr = t0 + (i >> 2) * 8 + g * 4 + (i & 3);
+    for (int e = 0; e < 8; ++e) {
+      const int fr = t0 + (e >> 2) * 8 + 4 * g + (e & 3);
       // a padded head (not stored) gets zero scores, so its lanes stay finite
-      sc[i] = hv ? (fr < t_end ? sc[i] * cs : -INFINITY) : 0.f;
-      mx = fmaxf(mx, sc[i]);
+      sc[e] = hv ? (fr < T ? sc[e] * cs : -INFINITY) : 0.f;
+      mx = fmaxf(mx, sc[e]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    // probabilities, packed to bf16 at once: P^T fragment t holds sc[8 t .. 8 t + 7]
     float psum = 0.f;
-    uint32_t pk[8];
+    uint32_t pk[4];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[i] - m_new), p1 = __builtin_amdgcn_exp2f(sc[i + 1] - m_new);
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[e] - m_new), p1 = __builtin_amdgcn_exp2f(sc[e + 1] - m_new);
       psum += p0 + p1;
-      pk[i >> 1] = f2bf2(p0, p1);
+      pk[e >> 1] = f2bf2(p0, p1);
     }
     if (__any(m_new > m_run)) {  // exp2(0) = 1 for the lanes whose max did not move
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -291,105 +269,124 @@ __global__ __launch_bounds__(NW * 64) void attn_cross_enc_kernel(const u16* __re
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
+        for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
     }
     l_run += psum;
     m_run = m_new;
-    // ---- U^T += E^T P^T over the two 16-frame k-blocks of the sub-tile
+    const bf16x8 pf = bitcast<bf16x8>(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    const u16* sw = sE[st][wave];
+    // transposed reads: the 16 lanes of group lane / 16 read a 4-frame x 16-column
+    // block; lane jl gets column jl of it
+    const int G4 = lane >> 4, fr = (G4 >> 1) * 4 + (jl >> 2);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 pf = bitcast<bf16x8>(make_uint4(pk[t * 4 + 0], pk[t * 4 + 1], pk[t * 4 + 2], pk[t * 4 + 3]));
-      const int fr = t * 16 + (G >> 1) * 4 + (jl >> 2);
+    for (int cb = 0; cb < CB; ++cb) {
+      const int kb = cb * 2 + (G4 & 1);
+      const uint2 lo = xe_read_tr16(&sw[xe_off(kb, fr, (jl & 3) * 4)]);
+      const uint2 hi = xe_read_tr16(&sw[xe_off(kb, fr + 8, (jl & 3) * 4)]);
+      o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, o[cb], 0,
+                                                      0, 0);
+    }
+  };
+  // the segment of row r ends: its unnormalised U, max and sum to its slot
+  auto flush = [&](int r) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (hv) {
+      const long slot = ((long)w * kmax + (r - row0)) * H + l32;
+      u16* up = upart + slot * d + col0;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int kb = cb * 2 + (G & 1);
-        const uint2 lo = xe_read_tr16(&sw[xe_off(kb, fr, (jl & 3) * 4)]);
-        const uint2 hi = xe_read_tr16(&sw[xe_off(kb, fr + 8, (jl & 3) * 4)]);
-        o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, o[cb],
-                                                        0, 0, 0);
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          uint2 u;
+          u.x = f2bf2(o[cb][e4 * 4 + 0], o[cb][e4 * 4 + 1]);
+          u.y = f2bf2(o[cb][e4 * 4 + 2], o[cb][e4 * 4 + 3]);
+          *(uint2*)(up + cb * 32 + e4 * 8 + g * 4) = u;
+        }
+      if (wave == 0 && g == 0) {
+        ml[slot * 2 + 0] = m_run;
+        ml[slot * 2 + 1] = l_tot;
       }
     }
   };
 
-  // Pipeline: sub-tile s in LDS, the next STAGES in flight in registers. The
-  // slice is private to the wave and its own reads of s have completed (their
-  // values fed the MFMAs) before s + 1 is stored over it.
-  gload(ra, tsub(0));
-  sstore(ra);
-  if (nsub > 1) gload(ra, tsub(1));
-  if constexpr (STAGES == 2) {
-    if (nsub > 2) gload(rb, tsub(2));
-    for (int s = 0; s < nsub; s += 2) {
-      compute(tsub(s));
-      if (s + 1 >= nsub) break;
-      sstore(ra);
-      if (s + 3 < nsub) gload(ra, tsub(s + 3));
-      compute(tsub(s + 1));
-      if (s + 2 >= nsub) break;
-      sstore(rb);
-      if (s + 4 < nsub) gload(rb, tsub(s + 4));
-    }
-  } else {
-    for (int s = 0; s < nsub; ++s) {
-      compute(tsub(s));
-      if (s + 1 < nsub) sstore(ra);
-      if (s + 2 < nsub) gload(ra, tsub(s + 2));
-    }
-  }
-  // ---- this chunk's unnormalised U, max and sum per head
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (hv) {
-    const long row = ((long)m * NC + c) * H + l32;
-    u16* up = upart + row * d + col0;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        uint2 u;
-        u.x = f2bf2(o[cb][i4 * 4 + 0], o[cb][i4 * 4 + 1]);
-        u.y = f2bf2(o[cb][i4 * 4 + 2], o[cb][i4 * 4 + 3]);
-        *(uint2*)(up + cb * 32 + i4 * 8 + g * 4) = u;
+  // ---- pipeline over one row segment [i0, i1) of the share (q' loaded
+  // once). Register stage of sub-tile i0 + j: j % XR; LDS stage and score
+  // buffers: j % 2. Prologue: loads of the first XR sub-tiles issued, scores
+  // of the first summed, its E in LDS, the next loads issued.
+  static_assert(XE_XR == 2, "the prologue and the unrolled loop assume two register stages");
+  auto segment = [&](const int i0, const int i1) {
+    const int ns = i1 - i0;
+    gload(0, i0);
+    if (ns > 1) gload(1, i0 + 1);
+    qload(row_of(i0));
+    scores(0, 0);
+    sstore(0, 0);
+    if (XE_XR < ns) gload(0, i0 + XE_XR);
+    __syncthreads();
+    reduce(0);
+    // step j with k = (j + 1) % XR, the register stage of sub-tile j + 1,
+    // given as a constant (registers cannot be indexed at run time)
+    auto step = [&](int j, const int k) __attribute__((always_inline)) {
+      // (a) partial scores of sub-tile j + 1, its E into LDS, the loads of
+      // sub-tile j + 1 + XR into the freed registers
+      if (j + 1 < ns) {
+        scores(k, (j + 1) & 1);
+        sstore(k, (j + 1) & 1);
+        if (j + 1 + XE_XR < ns) gload(k, i0 + j + 1 + XE_XR);
       }
-    if (wave == 0 && g == 0) {
-      ml[row * 2 + 0] = m_run;
-      ml[row * 2 + 1] = l_tot;
+      __syncthreads();
+      // (b) softmax and U of sub-tile j; the partials of j + 1 summed
+      softmax_u(i0 + j, j & 1, j & 1);
+      if (j + 1 < ns) reduce((j + 1) & 1);
+    };
+    for (int j = 0; j < ns; j += 2) {
+      step(j, 1);
+      if (j + 1 < ns) step(j + 1, 0);
     }
+    flush(row_of(i0));
+    reset();
+    __syncthreads();  // the next segment reuses the LDS stages and score buffers
+  };
+  if (n <= 0) return;
+  for (int i0 = 0; i0 < n;) {
+    const int r = row_of(i0);
+    // the segment runs to the share's end or the row's end
+    const long lim = reverse ? g1 - (long)r * nsub : (long)(r + 1) * nsub - g0;
+    const int i1 = (int)(lim < n ? lim : n);
+    segment(i0, i1);
+    i0 = i1;
   }
 }
 
-// Frame chunks per query row: the count that balances rounds of workgroups
-// (one per compute unit) against sub-tiles per workgroup; no chunk is empty.
-void cross_enc_chunks(int M, int T, int n_cu, int& NC, int& SPC) {
-  const int nsub = (T + XE_SUB - 1) / XE_SUB;
-  long best = -1;
-  NC = 1;
-  SPC = nsub;
-  for (int nc = 1; nc <= nsub; ++nc) {
-    const int spc = (nsub + nc - 1) / nc;
-    const int nc_eff = (nsub + spc - 1) / spc;
-    const long rounds = ((long)M * nc_eff + n_cu - 1) / n_cu;
-    const long cost = rounds * spc;
-    if (best < 0 || cost < best) {
-      best = cost;
-      NC = nc_eff;
-      SPC = spc;
-    }
+// The workgroup count of the plan: one per compute unit, fewer when that
+// would give a workgroup fewer than XE_MIN_PER_WG sub-tiles; kmax = the most
+// rows one share touches.
+void cross_enc_plan(int M, int T, int n_cu, XePlan& p) {
+  p.nsub = (T + XE_F - 1) / XE_F;
+  p.G = (long)M * p.nsub;
+  const long want = (p.G + XE_MIN_PER_WG - 1) / XE_MIN_PER_WG;
+  p.n_wg = (int)(want < n_cu ? (want > 1 ? want : 1) : n_cu);
+  p.kmax = 1;
+  for (int w = 0; w < p.n_wg; ++w) {
+    const long a = (long)w * p.G / p.n_wg, b = (long)(w + 1) * p.G / p.n_wg;
+    const int k = (int)((b - 1) / p.nsub - a / p.nsub + 1);
+    if (k > p.kmax) p.kmax = k;
   }
 }
 
-hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, int T, int d, int rows_per_b, int NC,
-                                 int SPC, int reverse, void* upart, float* ml, hipStream_t s) {
-  if (M <= 0 || T <= 0 || NC <= 0 || SPC <= 0 || rows_per_b < 1 || M % rows_per_b || H * 64 != d || H > XE_MAXH)
+hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, int T, int d, int rows_per_b,
+                                 const XePlan& pl, int reverse, void* upart, float* ml, hipStream_t s) {
+  if (M <= 0 || T <= 0 || rows_per_b < 1 || M % rows_per_b || H * 64 != d || H > XE_MAXH) return hipErrorInvalidValue;
+  if (pl.nsub != (T + XE_F - 1) / XE_F || pl.G != (long)M * pl.nsub || pl.n_wg <= 0 || pl.kmax <= 0)
     return hipErrorInvalidValue;
-  if ((long)(NC - 1) * SPC * XE_SUB >= T) return hipErrorInvalidValue;  // an empty chunk
-#define XE_LAUNCH(NWV, CBV, QR, ST)                                                                              \
-  hipLaunchKernelGGL((attn_cross_enc_kernel<NWV, CBV, QR, ST>), dim3(M * NC), dim3(NWV * 64), 0, s, (const u16*)qp, \
-                     (const u16*)E, H, T, NC, SPC, rows_per_b, reverse, (u16*)upart, ml)
+#define XE_LAUNCH(NWV, CBV)                                                                                       \
+  hipLaunchKernelGGL((attn_cross_enc_kernel<NWV, CBV>), dim3(pl.n_wg), dim3(NWV * 64), 0, s, (const u16*)qp,       \
+                     (const u16*)E, H, T, pl.nsub, pl.G, pl.n_wg, pl.kmax, rows_per_b, reverse, (u16*)upart, ml)
   switch (d) {
-    case 1280: XE_LAUNCH(8, 5, true, 1); break;
-    case 1024: XE_LAUNCH(8, 4, true, 1); break;
-    case 768: XE_LAUNCH(6, 4, true, 1); break;
-    case 512: XE_LAUNCH(4, 4, true, 1); break;
+    case 1280: XE_LAUNCH(8, 5); break;
+    case 1024: XE_LAUNCH(8, 4); break;
+    case 768: XE_LAUNCH(6, 4); break;
+    case 512: XE_LAUNCH(4, 4); break;
     default: return hipErrorInvalidValue;
   }
 #undef XE_LAUNCH
@@ -397,31 +394,55 @@ hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, in
 }
 
 // ------------------------------------------------------------------ combine
-// u[m][h][:] = sum_c w_c U_c[m][h][:] / sum_c w_c l_c,  w_c = exp2(max_c - max).
-// One workgroup of 256 threads per (row, head); 8 columns per thread and pass.
+// u[m][h][:] = sum_s w_s U_s[h][:] / sum_s w_s l_s over the segments s of row
+// m (w_s = exp2(max_s - max)): the shares of workgroups w_first .. w_last,
+// in the slot of row m within each share. One workgroup of 256 threads per
+// (row, head): the first threads find the segments' slots and weights
+// (at most 256 segments: one per workgroup of the attention), then every
+// thread combines 8 columns per pass.
 __global__ __launch_bounds__(256) void absorb_combine_kernel(const u16* __restrict__ upart,
-                                                             const float* __restrict__ ml, int H, int d, int NC,
-                                                             u16* __restrict__ u) {
-  const int mh = blockIdx.x, m = mh / H, h = mh - (mh / H) * H;
-  float mx = -INFINITY;
-  for (int c = 0; c < NC; ++c) mx = fmaxf(mx, ml[(((long)m * NC + c) * H + h) * 2]);
-  float den = 0.f;
-  for (int c = 0; c < NC; ++c) {
-    const long r = ((long)m * NC + c) * H + h;
-    den += __builtin_amdgcn_exp2f(ml[r * 2] - mx) * ml[r * 2 + 1];
+                                                             const float* __restrict__ ml, int H, int d, int nsub,
+                                                             long G, int n_wg, int kmax, u16* __restrict__ u) {
+  __shared__ long s_slot[256];
+  __shared__ float s_w[256];
+  __shared__ float s_inv;
+  const int mh = blockIdx.x, m = mh / H, h = mh - (mh / H) * H, tid = threadIdx.x;
+  auto wg_of = [&](long g_) { return (int)(((g_ + 1) * n_wg - 1) / G); };
+  const int wf = wg_of((long)m * nsub), ns = wg_of((long)(m + 1) * nsub - 1) - wf + 1;
+  float mseg = -INFINITY;
+  if (tid < ns) {
+    const int w_ = wf + tid;
+    const int r0 = (int)(((long)w_ * G / n_wg) / nsub);
+    const long slot = ((long)w_ * kmax + (m - r0)) * H + h;
+    s_slot[tid] = slot;
+    mseg = ml[slot * 2];
   }
-  const float inv = 1.0f / den;
-  for (int ch = threadIdx.x; ch < d / 8; ch += 256) {
+  // the row's max over its segments, then each segment's weight
+  float mx = mseg;
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  __shared__ float s_mx[4];
+  if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+  if (tid < ns) s_w[tid] = __builtin_amdgcn_exp2f(mseg - mx);
+  __syncthreads();
+  if (tid == 0) {
+    float den = 0.f;
+    for (int k = 0; k < ns; ++k) den += s_w[k] * ml[s_slot[k] * 2 + 1];
+    s_inv = 1.0f / den;
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  for (int ch = tid; ch < d / 8; ch += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < NC; ++c) {
-      const long r = ((long)m * NC + c) * H + h;
-      const float w = __builtin_amdgcn_exp2f(ml[r * 2] - mx);
-      const uint4 v = *(const uint4*)(upart + r * d + ch * 8);
+    for (int k = 0; k < ns; ++k) {
+      const float wt = s_w[k];
+      const uint4 v = *(const uint4*)(upart + s_slot[k] * d + ch * 8);
       const uint32_t a[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[2 * k] = fmaf(w, __uint_as_float(a[k] << 16), acc[2 * k]);
-        acc[2 * k + 1] = fmaf(w, __uint_as_float(a[k] & 0xffff0000u), acc[2 * k + 1]);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wt, __uint_as_float(a[q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wt, __uint_as_float(a[q] & 0xffff0000u), acc[2 * q + 1]);
       }
     }
     *(uint4*)(u + ((long)m * H + h) * d + ch * 8) =
@@ -430,10 +451,12 @@ __global__ __launch_bounds__(256) void absorb_combine_kernel(const u16* __restri
   }
 }
 
-hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int H, int d, int NC, void* u,
+hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int H, int d, const XePlan& pl, void* u,
                                  hipStream_t s) {
-  if (M <= 0 || H <= 0 || NC <= 0 || d % 8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_combine_kernel, dim3(M * H), dim3(256), 0, s, (const u16*)upart, ml, H, d, NC, (u16*)u);
+  if (M <= 0 || H <= 0 || d % 8 || pl.G != (long)M * pl.nsub || pl.n_wg <= 0 || pl.n_wg > 256)
+    return hipErrorInvalidValue;  // a row has at most one segment per attention workgroup
+  hipLaunchKernelGGL(absorb_combine_kernel, dim3(M * H), dim3(256), 0, s, (const u16*)upart, ml, H, d, pl.nsub, pl.G,
+                     pl.n_wg, pl.kmax, (u16*)u);
   return hipGetLastError();
 }
 

@@ -106,15 +106,19 @@ hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStr
 hipError_t launch_pack_kt(const float* wk, int d, void* wkt, hipStream_t s);
 // q'[m][h][:] = W_k,h^T q[m][h*64 : h*64+64] (bf16 in and out)
 hipError_t launch_absorb_q(const void* q, const void* wkt, int M, int H, int d, void* qp, hipStream_t s);
-// frame chunks per query row and sub-tiles (32 frames) per chunk
-void cross_enc_chunks(int M, int T, int n_cu, int& NC, int& SPC);
-// per (row m, chunk c): unnormalised U [M][NC][H][d] bf16 and (max, sum) [M][NC][H][2];
-// query row m reads encoder row m / rows_per_b of E [B][T][d]
-// reverse != 0: each chunk's sub-tiles are walked last to first
-hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, int T, int d, int rows_per_b, int NC,
-                                 int SPC, int reverse, void* upart, float* ml, hipStream_t s);
-// u [M][H][d] bf16 = the chunks' U combined with their softmax weights
-hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int H, int d, int NC, void* u,
+// Work split of the attention over E: the M rows' frames as one sequence of
+// G = M * nsub sub-tiles of 16 frames, cut into n_wg even shares (one per
+// workgroup); a share touches at most kmax rows and leaves one partial per row
+// segment, in slot w * kmax + (row - the share's first row).
+struct XePlan { int nsub; long G; int n_wg, kmax; };
+void cross_enc_plan(int M, int T, int n_cu, XePlan& p);
+// unnormalised U [n_wg * kmax][H][d] bf16 and (max, sum) [n_wg * kmax][H][2];
+// query row m reads encoder row m / rows_per_b of E [B][T][d]; reverse != 0:
+// each share is walked last sub-tile first
+hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, int T, int d, int rows_per_b,
+                                 const XePlan& plan, int reverse, void* upart, float* ml, hipStream_t s);
+// u [M][H][d] bf16 = each row's segments combined with their softmax weights
+hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int H, int d, const XePlan& plan, void* u,
                                  hipStream_t s);
 
 // ------------------------------------------------------------------ LayerNorm
