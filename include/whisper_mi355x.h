@@ -410,10 +410,12 @@ whisper_status whisper_layernorm_fused(const whisper_dims* dims, const void* h, 
  * with x [M, K] (row stride lda elements), w [N, K], bias [N] fp32 or NULL,
  * y [M, N]; act 0 = none, 1 = exact GELU. dt = WHISPER_BF16 needs K % 64 == 0
  * and lda % 8 == 0. path: 0 auto, 1 tiled MFMA (automatic tile), 2 skinny
- * (M <= 128, K % 128 == 0); 3, 4, 5, 6, 7 force the 128x128, 256x256 8-wave,
- * 256x256 4-wave, 256x256 LDS-DMA-pipelined 8-wave and 4-wave tiled kernels;
- * 8 is the 8-wave LDS-DMA kernel with the plain tile order (6 uses the
- * weight-panel-grouped order); 9 is the persistent 8-wave LDS-DMA kernel
+ * (M <= 128, K % 128 == 0); 3, 4, 5, 6 force the 128x128, 256x256 8-wave,
+ * 256x256 4-wave and 256x256 LDS-DMA-pipelined 8-wave tiled kernels; 8 is
+ * the 8-wave LDS-DMA kernel with the plain tile order (6 uses the
+ * weight-panel-grouped order), and 7 (once a 4-wave LDS-DMA kernel, retired:
+ * its accumulators did not fit the register file) runs 8's kernel; 9 is the
+ * persistent 8-wave LDS-DMA kernel
  * (one workgroup per compute unit, the ring running on across tiles), which
  * the automatic choice takes for large bf16 GEMMs without activation or with
  * GELU when N % 256 == 0, K % 128 == 0, K >= 256 and y is under 2 GB. 5-9

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libwhisper_mi355x.so")
+# WHISPER_MI355X_LIB selects another build of the same library (the host
+# AddressSanitizer build the CPU tests use)
+LIB_PATH = os.environ.get("WHISPER_MI355X_LIB") or os.path.join(_HERE, "libwhisper_mi355x.so")
 
 WHISPER_F32, WHISPER_BF16 = 0, 1
 WHISPER_FP8_E4M3, WHISPER_FP8_E5M2 = 0, 1

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int bh = (jj / QT) * 8 + xcdi, qtile = jj - (jj / QT) * QT;
   if (bh >= B * H) return;  // padding blocks ((chunk, head) count rounded up to a multiple of 8)
   const int b = bh / H, h = bh - (bh / H) * H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const u16* Qp = qkv + (long)b * T * ld + h * 64;
   const u16* Kp = Qp + d;
@@ -190,9 +190,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (ragged) tile(nkb - 1, true);
   const float l = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l;
-  const int q = q0 + l32;
+  // the output row and column group from the lane id again (mbcnt needs no
+  // input register), so nothing address-like stays live across the key loop
+  const int lane_o = __lane_id(), go = lane_o >> 5;
+  const int q = q0 + (lane_o & 31);
   if (q < T) {
-    u16* op = out + ((long)b * T + q) * d + h * 64;
+    u16* op = out + (long)(b * T) * d + h * 64 + (uint32_t)(q * d);
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         uint2 u;
         u.x = (uint32_t)f2bf(o[eb][i4 * 4 + 0] * inv) | ((uint32_t)f2bf(o[eb][i4 * 4 + 1] * inv) << 16);
         u.y = (uint32_t)f2bf(o[eb][i4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[eb][i4 * 4 + 3] * inv) << 16);
-        *(uint2*)(op + eb * 32 + i4 * 8 + g * 4) = u;
+        *(uint2*)(op + eb * 32 + i4 * 8 + go * 4) = u;
       }
   }
 }

@@ -1039,148 +1039,6 @@ hipError_t launch_gemm_fp8(Epi epi, const GemmParams& q, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ bf16 MFMA, 256x256, LDS DMA pipeline, 4 waves
-// The same 4-stage LDS ring (BK = 32) fed by direct global->LDS loads, with
-// 256 threads = 2x2 waves of 128x128 sub-tiles (8x8 MFMA 16x16x32, 256 fp32
-// accumulators per lane): per MFMA a third less LDS fragment traffic than the
-// 128x64 sub-tiles, and 64 MFMAs per wave between barriers instead of 32.
-template <int EPI>
-__global__ __launch_bounds__(256) void gemm_bf16_dma4(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) u16 st0[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) u16 st1[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) u16 st2[DSTAGE];
-  __shared__ __attribute__((aligned(1024))) u16 st3[DSTAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_n = (p.N + TB2 - 1) / TB2;
-  const int tiles_m = (p.M + TB2 - 1) / TB2;
-  int tm, tn;
-  tile_order(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int z = blockIdx.z;
-  const u16* A = (const u16*)p.A + (long)z * p.strideA;
-  const u16* B = (const u16*)p.B;
-  const int m0 = tm * TB2, n0 = tn * TB2;
-
-  // DMA: wave w fills A blocks w, w+4, w+8, w+12 and the same B blocks (16 rows each)
-  const int lr = lane >> 2, lc = (lane & 3) ^ ((lane >> 3) & 3);  // global chunk for LDS slot lane & 3 of row lr
-  const u16* ga[4];
-  const u16* gb[4];
-  int la[4], lb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int blk = wave + 4 * q;
-    ga[q] = A + (long)min(m0 + blk * 16 + lr, p.M - 1) * p.lda + lc * 8;
-    gb[q] = B + (long)min(n0 + blk * 16 + lr, p.N - 1) * p.ldb + lc * 8;
-    la[q] = blk * 16 * DBK;
-    lb[q] = TB2 * DBK + blk * 16 * DBK;
-  }
-#define WH_ISSUE(S, k)                                                                         \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
-    dma16(ga[q] + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + la[q])));                 \
-    dma16(gb[q] + (k), __builtin_amdgcn_readfirstlane(lds_addr((S) + lb[q])));                 \
-  }
-
-  f32x4 acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int fr = lane & 15, kc = lane >> 4;
-  const int nk = p.K / DBK;
-  bf16x8 a0[8], b0[8], a1[8], b1[8];
-#define WH_READ(S, AF, BF)                                                                    \
-  _Pragma("unroll") for (int j = 0; j < 8; ++j)                                               \
-    BF[j] = bitcast<bf16x8>(*(const uint4*)((S) + TB2 * DBK + dswz(wn * 128 + j * 16 + fr, kc))); \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
-    AF[i] = bitcast<bf16x8>(*(const uint4*)((S) + dswz(wm * 128 + i * 16 + fr, kc)));
-#define WH_MFMA(AF, BF)                                                                       \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                               \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                             \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(BF[j], AF[i], acc[i][j], 0, 0, 0);
-#define WH_SYNC(n)                                                                             \
-  {                                                                                            \
-    WH_WAIT_VM_LGKM0(n);                                                                       \
-    __builtin_amdgcn_s_barrier();                                                              \
-  }
-#define WH_STEP(WAITN, REFILL, SREFILL, KREFILL, SN, AC, BC, AN, BN)                           \
-  WH_SYNC(WAITN)                                                                               \
-  if (REFILL) { WH_ISSUE(SREFILL, KREFILL) }                                                   \
-  WH_READ(SN, AN, BN)                                                                          \
-  WH_MFMA(AC, BC)
-
-  // straight-line pipeline as in gemm_bf16_dma (K % 128 == 0); 8 DMA loads per wave per stage
-  WH_ISSUE(st0, 0)
-  WH_ISSUE(st1, DBK)
-  WH_ISSUE(st2, 2 * DBK)
-  WH_SYNC(16)
-  WH_ISSUE(st3, 3 * DBK)
-  WH_READ(st0, a0, b0)
-  int kt = 0;
-  for (; kt + 8 <= nk; kt += 4) {
-    WH_STEP(16, true, st0, (kt + 4) * DBK, st1, a0, b0, a1, b1)
-    WH_STEP(16, true, st1, (kt + 5) * DBK, st2, a1, b1, a0, b0)
-    WH_STEP(16, true, st2, (kt + 6) * DBK, st3, a0, b0, a1, b1)
-    WH_STEP(16, true, st3, (kt + 7) * DBK, st0, a1, b1, a0, b0)
-  }
-  WH_STEP(16, false, st0, 0, st1, a0, b0, a1, b1)
-  WH_STEP(8, false, st0, 0, st2, a1, b1, a0, b0)
-  WH_STEP(0, false, st0, 0, st3, a0, b0, a1, b1)
-  WH_MFMA(a1, b1)
-#undef WH_READ
-#undef WH_MFMA
-#undef WH_SYNC
-#undef WH_STEP
-#undef WH_ISSUE
-  // epilogue straight from registers: lane holds C[m][n..n+3]
-  const int em = m0 + wm * 128 + (lane & 15), en = n0 + wn * 128 + (lane >> 4) * 4;
-  if constexpr (EPI == EPI_CROSSKV) {
-    const int d = p.ckv_d, T_ = p.ckv_T, H_ = p.ckv_H;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (en + j * 16 + 4 > p.N) continue;
-      const int n = en + j * 16;
-      const int l = n / (2 * d), r = n - l * 2 * d;
-      const int kv = r / d, c = r - kv * d;
-      const long coff = (((long)(l * 2 + kv) * p.ckv_B * H_ + (c >> 6)) * T_) * 64 + (c & 63);
-      const float4 cb = p.bias ? *(const float4*)(p.bias + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = em + i * 16;
-        if (m >= p.M) continue;
-        const int b = m / T_, t = m - b * T_;
-        uint2 u;
-        u.x = (uint32_t)f2bf(acc[i][j][0] + cb.x) | ((uint32_t)f2bf(acc[i][j][1] + cb.y) << 16);
-        u.y = (uint32_t)f2bf(acc[i][j][2] + cb.z) | ((uint32_t)f2bf(acc[i][j][3] + cb.w) << 16);
-        *(uint2*)((u16*)p.C + coff + ((long)b * H_ * T_ + t) * 64) = u;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // one output row block at a time (keeps the epilogue's registers bounded)
-      __builtin_amdgcn_sched_barrier(0);
-      const int m = em + i * 16;
-      if (m >= p.M) continue;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = en + j * 16;
-        float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-        if (n + 4 <= p.N) {
-          epi_store4<EPI>(p, z, m, n, v);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < p.N) epi_store<u16, EPI>(p, z, m, n + q, v[q]);
-        }
-      }
-    }
-  }
-}
-
-#undef WH_WAIT_VM
-#undef WH_WAIT_VM_LGKM0
-
 // ------------------------------------------------------------------ bf16 skinny (decode rows)
 // Decoder GEMMs have M = batch rows (<= 128) and stream their weight once, so
 // they are bound by bytes in flight, not by MFMA. One workgroup owns 16*CB
@@ -1329,19 +1187,7 @@ hipError_t launch_gemm(ActType t, Epi epi, const GemmParams& p, hipStream_t s) {
     int v = p.variant;
     if (v == 0) v = (tiles2 * p.batch >= 192 && epi != EPI_DEC_QKV) ? (pers_ok ? 9 : dma_ok ? 4 : 2) : 1;
     if ((v == 3 && !w4_ok) || (v == 4 && !dma_ok)) v = 1;
-    if (v == 5 && !dma_ok) v = 1;
-    if (v == 5) {
-      dim3 grid(tiles2, 1, p.batch);
-#define CALL(E) hipLaunchKernelGGL(gemm_bf16_dma4<E>, grid, dim3(256), 0, s, p)
-      switch (epi) {
-        case EPI_STORE: CALL(EPI_STORE); break;
-        case EPI_GELU: CALL(EPI_GELU); break;
-        case EPI_GELU_PE: CALL(EPI_GELU_PE); break;
-        default: CALL(EPI_CROSSKV); break;
-      }
-#undef CALL
-      return hipGetLastError();
-    }
+    if (v == 5) v = 6;  // the 4-wave 256x256 form is retired (its 256 accumulators per lane do not fit)
     if (v == 9 && !pers_ok) v = dma_ok ? 4 : 1;
     if (v == 9) {
       dim3 grid(min(num_cus(), ((p.M + TB2 - 1) / TB2) * (p.N / TB2) + 7));
