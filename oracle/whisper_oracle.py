@@ -427,9 +427,9 @@ def encoder(mel, W, n_heads, n_layers):
 # one per weight tensor (query, key, value, fc1, fc2: fl32(amax) / 448), and
 # one per activation tensor at each site, taken over one chunk's activation
 # (one 30 s clip, so a chunk's result does not depend on the batch it runs
-# in): fl32(amax) / 448. That activation is the bfloat16 tensor the
-# Endpoints post's inference stack computes ("Inference Stack"). The product sums value(code_x) * value(code_w) and
-# multiplies by both scales; the bias is added after.
+# in): fl32(amax) / 448, of the oracle's own activation values. The product
+# sums value(code_x) * value(code_w) and multiplies by both scales; the bias
+# is added after.
 
 def fp8_linear(x, w, b, sx, sw):
     """y = sx * sw * (value(e4m3(x / sx)) @ value(e4m3(w / sw))^T) + b."""
@@ -446,39 +446,48 @@ def bf16_round(x):
     return r.view(np.float32).astype(np.float64)
 
 
-def _site(x, w, b, fp8):
-    """One mixed_fp8 matmul site: fp8 with amax scales, or the plain linear.
-    The activation that reaches a site is a bfloat16 tensor (Endpoints post,
-    "Inference Stack": activations are computed in bfloat16), so the fp8 form
-    takes its amax and codes from x rounded to bf16; the weights are quantised
-    from their fp32 values."""
+def _site(x, w, b, fp8, act_transform=None):
+    """One mixed_fp8 matmul site: fp8 with amax scales of exactly the site's
+    input and weight, or the plain linear. The oracle quantises its own
+    activation values (no intermediate rounding). act_transform, when given,
+    is applied to the activation before its scale and codes are taken:
+    bf16_round there gives the activation as an inference stack that computes
+    in bfloat16 holds it (Endpoints post, "Inference Stack"), which is how the
+    oracle's sensitivity to that rounding is measured."""
     if not fp8:
         return linear(x, w, b)
-    xb = bf16_round(x)
-    return fp8_linear(xb, w, b, e4m3_scale_from_amax(xb), e4m3_scale_from_amax(w))
+    xq = x if act_transform is None else act_transform(x)
+    return fp8_linear(xq, w, b, e4m3_scale_from_amax(xq), e4m3_scale_from_amax(w))
 
 
-def encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8=True):
+def encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8=True, act_transform=None):
     """encoder_layer with the mixed_fp8 sites (query, key, value, fc1, fc2)
     in fp8 E4M3 for one chunk x [1500, d]; with fp8=False it is
-    encoder_layer."""
+    encoder_layer. act_transform: see _site."""
     p = f"encoder.blocks.{layer}."
     a = layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"])
-    q = _site(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], fp8)
-    k = _site(a, W[p + "attn.key.weight"], None, fp8)
-    v = _site(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], fp8)
+    q = _site(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], fp8, act_transform)
+    k = _site(a, W[p + "attn.key.weight"], None, fp8, act_transform)
+    v = _site(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], fp8, act_transform)
     x = x + linear(attention(q, k, v, n_heads), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
     m = layer_norm(x, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
-    hdn = gelu(_site(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], fp8))
-    return x + _site(hdn, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], fp8)
+    hdn = gelu(_site(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], fp8, act_transform))
+    return x + _site(hdn, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], fp8, act_transform)
 
 
-def encoder_layers_mixed_fp8(x, W, n_heads, layers, ln_post=True, fp8=True):
+def encoder_layers_mixed_fp8(x, W, n_heads, layers, ln_post=True, fp8=True, act_transform=None):
     for layer in layers:
-        x = encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8)
+        x = encoder_layer_mixed_fp8(x, W, layer, n_heads, fp8, act_transform)
     if ln_post:
         x = layer_norm(x, W["encoder.ln_post.weight"], W["encoder.ln_post.bias"])
     return x
+
+
+def encoder_mixed_fp8(mel, W, n_heads, n_layers, act_transform=None):
+    """One chunk with the mixed_fp8 sites: mel [n_mels, 3000] -> [1500, d]
+    (the conv stem keeps the activation precision)."""
+    return encoder_layers_mixed_fp8(conv_stem(mel, W), W, n_heads, range(n_layers), ln_post=True,
+                                    act_transform=act_transform)
 
 
 def cross_kv(enc, W, n_heads, n_layers):
@@ -496,7 +505,7 @@ def cross_kv(enc, W, n_heads, n_layers):
     return out
 
 
-def cross_kv_fp8(cross, scales, fmt="e4m3"):
+def cross_kv_fp8(cross, scales, fmt="e4m3", kv_transform=None):
     """fp8 cross-attention keys and values: each layer's K and V are
     quantised on write with the caller's per-(layer, K|V) scale and read back
     dequantised, so decode_step then attends over the fp8 values (whisper_blaze
@@ -504,19 +513,21 @@ def cross_kv_fp8(cross, scales, fmt="e4m3"):
     preset puts the cross-attention site in fp8, there in E5M2 for range;
     fp8_quantize.cu card: E4M3 and E5M2 codes with a per-tensor scale).
     fmt picks the format, "e4m3" or "e5m2", with one scale per (layer, K|V)
-    tensor either way. The K and V being quantised are the bfloat16 tensors
-    the inference stack computes (Endpoints post, "Inference Stack":
-    activations in bfloat16), so they are rounded to bf16 first.
+    tensor either way. The oracle quantises its own K and V values;
+    kv_transform, when given, is applied to them first (bf16_round: the
+    tensors as a bfloat16 inference stack holds them, for measuring the
+    oracle's sensitivity to that rounding).
 
     cross: list over layers of (K, V), each an array [B, H, T, dh] or a dict
     b -> [H, T, dh]; scales: [L, 2]. Returns the same structure holding
-    dequantize(quantize(bf16(x), s), s) in the chosen format."""
+    dequantize(quantize(x, s), s) in the chosen format."""
     quant, dequant, _ = FP8_FORMATS[fmt]
+    tr = (lambda a: a) if kv_transform is None else kv_transform
 
     def q(x, s):
         if isinstance(x, dict):
-            return {b: dequant(quant(bf16_round(v), s), s) for b, v in x.items()}
-        return dequant(quant(bf16_round(x), s), s)
+            return {b: dequant(quant(tr(v), s), s) for b, v in x.items()}
+        return dequant(quant(tr(x), s), s)
     return [(q(k, scales[layer][0]), q(v, scales[layer][1])) for layer, (k, v) in enumerate(cross)]
 
 

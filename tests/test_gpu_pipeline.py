@@ -6,6 +6,9 @@ their own KV cache; the oracle never reads a value the GPU produced.
 
 Batch rows and chunks are independent, so at the large shapes the oracle runs
 on a few rows/chunks only and those rows must match."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -57,13 +60,22 @@ def test_encoder_layer_large_v3(ln_post):
     assert e < TOL
 
 
+def fp8_bar(ref, ref_rounded):
+    """Bar for a GPU mixed_fp8 result against the oracle's: TOL, or twice the
+    oracle's own sensitivity to rounding the fp8 sites' inputs to bf16 (the
+    kernels quantise bf16 activations; a value within that rounding of an
+    e4m3 midpoint takes the neighbouring code), whichever is larger.
+    Returns (bar, sensitivity)."""
+    sens = rel_err(ref_rounded, ref)
+    return max(TOL, 2.0 * sens), sens
+
+
 def test_encoder_layer_mixed_fp8_large_v3_two_chunks():
     """One large-v3 encoder layer with the mixed_fp8 sites (query, key, value,
     fc1, fc2 in E4M3; per-tensor weight scales, per-chunk activation scales)
     through whisper_encode_layers_fp8, two chunks (the 1500-row chunks cross
-    256-row tiles), against the oracle's mixed_fp8 layer on each chunk. The
-    two sides quantise activations that differ by bf16 rounding, so some codes
-    differ by one step; the tolerance is the fp8 one of the decode tests."""
+    256-row tiles), against the oracle's mixed_fp8 layer on each chunk, which
+    quantises its own fp64 activations (bar: fp8_bar)."""
     dims = CONFIGS["v3_layer"]
     say("mixed_fp8 encoder layer large-v3 B=2")
     m, W = model_for(dims, ln_random=True, fp8_encoder=True)
@@ -77,11 +89,14 @@ def test_encoder_layer_mixed_fp8_large_v3_two_chunks():
     for b in range(2):
         x = host(h)[b]
         ref = O.encoder_layers_mixed_fp8(x, Wh, dims.n_heads, [0], ln_post=False)
+        bar, sens = fp8_bar(ref, O.encoder_layers_mixed_fp8(x, Wh, dims.n_heads, [0], ln_post=False,
+                                                            act_transform=O.bf16_round))
         e = rel_err(host(out)[b], ref)
         # the fp8 result differs from the bf16 layer by the fp8 rounding, not more
         e_bf = rel_err(host(out)[b], host(bf)[b])
-        say(f"  chunk {b}: rel err vs oracle {e:.3e}, vs bf16 path {e_bf:.3e}")
-        assert e < TOL
+        say(f"  chunk {b}: rel err vs oracle {e:.3e} (bar {bar:.3e}, oracle sensitivity {sens:.3e}), "
+            f"vs bf16 path {e_bf:.3e}")
+        assert e < bar
         assert e_bf < 0.1
 
 
@@ -98,9 +113,59 @@ def test_encoder_layer_mixed_fp8_full_batch_sampled_chunks():
     Wh = host_weights(W)
     for b in (0, 63):
         ref = O.encoder_layers_mixed_fp8(host(h[b]), Wh, dims.n_heads, [0], ln_post=False)
+        bar, sens = fp8_bar(ref, O.encoder_layers_mixed_fp8(host(h[b]), Wh, dims.n_heads, [0], ln_post=False,
+                                                            act_transform=O.bf16_round))
         e = rel_err(host(out[b]), ref)
-        say(f"  chunk {b}: rel err vs oracle {e:.3e}")
-        assert e < TOL
+        say(f"  chunk {b}: rel err vs oracle {e:.3e} (bar {bar:.3e}, oracle sensitivity {sens:.3e})")
+        assert e < bar
+
+
+def test_encoder_mixed_fp8_32_layers_per_layer_and_end_to_end():
+    """The whole 32-layer large-v3 encoder with the mixed_fp8 sites.
+
+    The oracle runs its mixed_fp8 encoder on chunk 0 of the audio (its own
+    log-mel), layer by layer. Per layer (sampled: 0, 11, 21, 31) the GPU runs
+    that one layer on the oracle's own input to it (bf16, as the GPU holds
+    activations; the oracle layer takes the same bf16 input) and must match
+    the oracle's layer within fp8_bar. Free-running over 32 layers the code
+    flips at near-ties compound chaotically: from bf16 rounding of its site
+    inputs alone the oracle moves by about 2e-2 after one layer and 8e-2
+    after 32, close to the whole fp8 effect (about 1e-1;
+    tests/golden/fp8_encoder_sensitivity.json), so the end-to-end result is
+    reported and only held to twice that whole-encoder sensitivity."""
+    dims = CONFIGS["v3_encoder"]
+    H = dims.n_heads
+    say("mixed_fp8 encoder, 32 layers, large-v3: per layer on the oracle's inputs, and end to end from audio")
+    m, W = model_for(dims, fp8_encoder=True)
+    audio = gen_audio_tones(DEV, dims.cfg_id, 2)
+    enc = m.encode_fp8(m.logmel(audio))
+    torch.cuda.synchronize()
+    Wh = host_weights(W, "encoder.")
+    del W
+    x = O.conv_stem(O.log_mel(audio[0].cpu().numpy(), dims.n_mels), Wh)
+    sampled = (0, 11, 21, 31)
+    for layer in range(dims.n_enc_layers):
+        if layer in sampled:
+            xb = O.bf16_round(x)
+            h = torch.from_numpy(xb.astype(np.float32)).to(DEV).to(torch.bfloat16)[None]
+            out = m.encode_layers_fp8(h, layer, layer + 1)
+            torch.cuda.synchronize()
+            ref = O.encoder_layer_mixed_fp8(xb, Wh, layer, H)
+            bar, sens = fp8_bar(ref, O.encoder_layer_mixed_fp8(xb, Wh, layer, H, act_transform=O.bf16_round))
+            e = rel_err(host(out)[0], ref)
+            say(f"  layer {layer} on the oracle's input: rel err {e:.3e} (bar {bar:.3e}, oracle sensitivity "
+                f"{sens:.3e})")
+            assert e < bar, f"layer {layer}"
+        x = O.encoder_layer_mixed_fp8(x, Wh, layer, H)
+    ref = O.layer_norm(x, Wh["encoder.ln_post.weight"], Wh["encoder.ln_post.bias"])
+    e = rel_err(host(enc)[0], ref)
+    # the oracle's whole-encoder sensitivity at this shape, from
+    # tests/golden/make_fp8_encoder_sensitivity.py (same generators, on the CPU)
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_encoder_sensitivity.json")))
+    bar = 2.0 * rec["sensitivity"]["32"]
+    say(f"  end to end, 32 layers from audio: rel err {e:.3e} (bar {bar:.3e}: twice the oracle's own "
+        f"whole-encoder sensitivity; the whole fp8 effect is {rec['fp8_vs_plain_32']:.3e})")
+    assert e < bar
 
 
 def _encoder_from_audio(dims, B, chunks):

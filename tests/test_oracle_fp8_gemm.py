@@ -69,22 +69,38 @@ def test_mixed_fp8_layer_off_is_the_plain_layer_and_on_stays_close():
 
 def test_mixed_fp8_sites_use_per_tensor_amax_scales():
     """The layer's fp8 sites equal fp8_linear with amax scales of exactly the
-    site's input (one chunk) and weight: recompute the layer from its parts."""
+    site's input (one chunk, the oracle's own values, no rounding) and
+    weight: recompute the layer from its parts. With act_transform the same
+    holds for the transformed inputs (bf16_round: the sensitivity runs)."""
     rng = np.random.default_rng(4)
     W = _tiny_weights(rng, d=64, f=256)
     x = rng.standard_normal((30, 64))
     p = "encoder.blocks.1."
-    a = O.bf16_round(O.layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"]))
     s = O.e4m3_scale_from_amax
-    q = O.fp8_linear(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], s(a), s(W[p + "attn.query.weight"]))
-    k = O.fp8_linear(a, W[p + "attn.key.weight"], None, s(a), s(W[p + "attn.key.weight"]))
-    v = O.fp8_linear(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], s(a), s(W[p + "attn.value.weight"]))
-    h = x + O.linear(O.attention(q, k, v, 2), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
-    m = O.bf16_round(O.layer_norm(h, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"]))
-    g = O.bf16_round(O.gelu(O.fp8_linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], s(m),
-                                         s(W[p + "mlp.0.weight"]))))
-    out = h + O.fp8_linear(g, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], s(g), s(W[p + "mlp.2.weight"]))
-    assert np.array_equal(O.encoder_layer_mixed_fp8(x, W, 1, 2), out)
+    for tr in (lambda a: a, O.bf16_round):
+        a = tr(O.layer_norm(x, W[p + "attn_ln.weight"], W[p + "attn_ln.bias"]))
+        q = O.fp8_linear(a, W[p + "attn.query.weight"], W[p + "attn.query.bias"], s(a), s(W[p + "attn.query.weight"]))
+        k = O.fp8_linear(a, W[p + "attn.key.weight"], None, s(a), s(W[p + "attn.key.weight"]))
+        v = O.fp8_linear(a, W[p + "attn.value.weight"], W[p + "attn.value.bias"], s(a),
+                         s(W[p + "attn.value.weight"]))
+        h = x + O.linear(O.attention(q, k, v, 2), W[p + "attn.out.weight"], W[p + "attn.out.bias"])
+        m = tr(O.layer_norm(h, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"]))
+        g = tr(O.gelu(O.fp8_linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], s(m), s(W[p + "mlp.0.weight"]))))
+        out = h + O.fp8_linear(g, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], s(g), s(W[p + "mlp.2.weight"]))
+        got = O.encoder_layer_mixed_fp8(x, W, 1, 2, act_transform=None if tr is not O.bf16_round else O.bf16_round)
+        assert np.array_equal(got, out)
+    # the rounding moves some codes, so the layer differs
+    y0 = O.encoder_layer_mixed_fp8(x, W, 1, 2)
+    y1 = O.encoder_layer_mixed_fp8(x, W, 1, 2, act_transform=O.bf16_round)
+    assert np.abs(y1 - y0).max() > 0
+
+
+def test_mixed_fp8_encoder_from_mel_is_stem_then_layers():
+    rng = np.random.default_rng(5)
+    W = _tiny_weights(rng, d=64, f=256)
+    mel = rng.standard_normal((16, 3000)) * 0.3
+    want = O.encoder_layers_mixed_fp8(O.conv_stem(mel, W), W, 2, [0, 1], ln_post=True)
+    assert np.array_equal(O.encoder_mixed_fp8(mel, W, 2, 2), want)
 
 
 def test_bf16_round_matches_torch_and_keeps_grid_values():

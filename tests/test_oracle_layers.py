@@ -363,10 +363,11 @@ def test_fp8_cross_kv_grid_values_exact_and_error_bound():
     """fp8 cross K/V: with power-of-two scales, values already on the scaled
     e4m3 grid pass unchanged (so a decode step over such K/V equals the
     unquantised step exactly);
-    others move by at most their bf16 rounding (2^-9, the K/V are bf16
-    tensors) plus half an e4m3 step: 2^-4 of the value in the normal range,
-    2^-10 * scale in the subnormal range; magnitudes past 448 * scale
-    saturate. Dict and array forms agree."""
+    others move by at most half an e4m3 step: 2^-4 of the value in the
+    normal range, 2^-10 * scale in the subnormal range; magnitudes past
+    448 * scale saturate. Dict and array forms agree. With kv_transform =
+    bf16_round the bf16 rounding (2^-9) adds to the bound, and the result is
+    the quantisation of the rounded values."""
     W, H, L, ctx, cross, toks, scales, dh = _fp8_setup()
     scales = np.array([[2.0 ** -5, 2.0 ** -4], [2.0 ** -6, 2.0 ** -3]], np.float32)  # exact in fp32 both ways
     rng = np.random.default_rng(5)
@@ -399,21 +400,24 @@ def test_fp8_cross_kv_grid_values_exact_and_error_bound():
     y = O.cross_kv_fp8([(x, x)], np.array([[s, s]], np.float32))[0][0]
     inr = np.abs(x) <= 448 * float(s)
     normal = inr & (np.abs(x) >= 2.0 ** -6 * float(s))
-    # half an e4m3 step of the bf16-rounded value plus that rounding (2^-9)
-    bf = 2.0 ** -9
-    assert np.all(np.abs(y - x)[normal] <= (2.0 ** -4 * (1 + bf) + bf) * np.abs(x[normal]) * (1 + 1e-6))
+    # half an e4m3 step: 2^-4 of the value in the normal range, 2^-10 * scale below
+    assert np.all(np.abs(y - x)[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6))
     sub = inr & ~normal
-    assert np.all(np.abs(y - x)[sub] <= (2.0 ** -10 * float(s) + bf * np.abs(x[sub])) * (1 + 1e-6))
+    assert np.all(np.abs(y - x)[sub] <= 2.0 ** -10 * float(s) * (1 + 1e-6))
     assert np.all(np.abs(y[~inr]) == np.float64(np.float32(448.0) * s))
+    # with the values rounded to bf16 first: that rounding (2^-9) on top
+    yb = O.cross_kv_fp8([(x, x)], np.array([[s, s]], np.float32), kv_transform=O.bf16_round)[0][0]
+    bf = 2.0 ** -9
+    assert np.all(np.abs(yb - x)[normal] <= (2.0 ** -4 * (1 + bf) + bf) * np.abs(x[normal]) * (1 + 1e-6))
+    assert np.array_equal(yb, O.cross_kv_fp8([(O.bf16_round(x), x)], np.array([[s, s]], np.float32))[0][0])
 
 
 def test_fp8_cross_kv_e5m2_grid_values_exact_and_error_bound():
     """fp8 cross K/V in E5M2 (the aggressive preset's cross-attention format):
     with power-of-two scales, values on the scaled e5m2 grid pass unchanged,
     so a decode step over them equals the unquantised step exactly; others
-    move by at most their bf16 rounding (2^-9) plus half an e5m2 step (2^-3
-    of the value in the normal range, 2^-17 * scale below it); past
-    57344 * scale they saturate."""
+    move by at most half an e5m2 step (2^-3 of the value in the normal
+    range, 2^-17 * scale below it); past 57344 * scale they saturate."""
     W, H, L, ctx, cross, toks, scales, dh = _fp8_setup()
     scales = np.array([[2.0 ** -12, 2.0 ** -11], [2.0 ** -13, 2.0 ** -10]], np.float32)
     rng = np.random.default_rng(6)
@@ -444,8 +448,7 @@ def test_fp8_cross_kv_e5m2_grid_values_exact_and_error_bound():
     y = O.cross_kv_fp8([(x, x)], np.array([[s, s]], np.float32), fmt="e5m2")[0][0]
     inr = np.abs(x) <= 57344 * float(s)
     normal = inr & (np.abs(x) >= 2.0 ** -14 * float(s))
-    bf = 2.0 ** -9  # the bf16 rounding before quantisation
-    assert np.all(np.abs(y - x)[normal] <= (2.0 ** -3 * (1 + bf) + bf) * np.abs(x[normal]) * (1 + 1e-6))
+    assert np.all(np.abs(y - x)[normal] <= 2.0 ** -3 * np.abs(x[normal]) * (1 + 1e-6))
     sub = inr & ~normal
-    assert np.all(np.abs(y - x)[sub] <= (2.0 ** -17 * float(s) + bf * np.abs(x[sub])) * (1 + 1e-6))
+    assert np.all(np.abs(y - x)[sub] <= 2.0 ** -17 * float(s) * (1 + 1e-6))
     assert np.all(np.abs(y[~inr]) == np.float64(np.float32(57344.0) * s))
