@@ -50,6 +50,18 @@ constexpr int DG_DEPTH = 1;         // k-steps of operand loads in flight per wa
 // MI355X: ~4-8 KB in flight per wave sustains ~12 TB/s from the caches, while
 // issuing a wave's whole share at once congests and runs at about half that).
 // NS = 0 is the generic path (any K % 32 == 0): one step at a time.
+// One step of a (value, column) max across lanes: the partner lane's pair
+// through the DPP control CTRL; larger value wins, the lower column on ties.
+template <int CTRL>
+__device__ __forceinline__ void amax_step(float& v, int& idx) {
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+  const int oi = __builtin_amdgcn_mov_dpp(idx, CTRL, 0xF, 0xF, true);
+  if (ov > v || (ov == v && oi < idx)) {
+    v = ov;
+    idx = oi;
+  }
+}
+
 template <int PRO, int EPI, int MB, int CB, int NS>
 __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
   constexpr int MR = MB * 16;
@@ -301,15 +313,14 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
           v = -INFINITY;
           idx = 0x7fffffff;
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float ov = __shfl_xor(v, o, 64);
-          const int oi = __shfl_xor(idx, o, 64);
-          if (ov > v || (ov == v && oi < idx)) {
-            v = ov;
-            idx = oi;
-          }
-        }
+        // across the 16 lanes of the row group with DPP lane permutes (no trip
+        // through the LDS crossbar): quad_perm(1,0,3,2), quad_perm(2,3,0,1),
+        // then row_half_mirror (lane i <-> 7 - i of each 8) and row_mirror
+        // (lane i <-> 15 - i): after the four steps every lane holds the max
+        amax_step<0xB1>(v, idx);
+        amax_step<0x4E>(v, idx);
+        amax_step<0x141>(v, idx);
+        amax_step<0x140>(v, idx);
         // blocks wholly past N (the last column tile's tail) have no entry
         const int m = m0 + emb * 16 + (lane >> 4) * 4 + r, blk = (n0 >> 4) + ecb;
         if ((lane & 15) == 0 && m < M && blk < NB) p.amax_part[(long)m * NB + blk] = make_int2(__float_as_int(v), idx);

@@ -502,16 +502,24 @@ hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int
 // projection writes ([B][NB] as (float bits, column)): the same rule as
 // argmax_kernel (largest value, lowest column on ties, NaN never chosen, 0 for
 // a row with no candidate). One workgroup per row.
-__global__ __launch_bounds__(256) void argmax_part_kernel(const int2* part, int NB, int32_t* out, int32_t* lengths,
-                                                          int len_inc) {
+__global__ __launch_bounds__(1024) void argmax_part_kernel(const int2* part, int NB, int32_t* out, int32_t* lengths,
+                                                           int len_inc) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int2* row = part + (size_t)b * NB;
   float best = -INFINITY;
   int idx = 0x7fffffff;
-  for (int i = tid; i < NB; i += 256) {
-    const int2 e = row[i];
-    const float v = __int_as_float(e.x);
-    if (v > best || (v == best && e.y < idx)) { best = v; idx = e.y; }
+  for (int i0 = 0; i0 < NB; i0 += 4096) {
+    int2 e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // four loads in flight per thread
+      const int i = i0 + k * 1024 + tid;
+      e[k] = i < NB ? row[i] : make_int2(__float_as_int(-INFINITY), 0x7fffffff);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = __int_as_float(e[k].x);
+      if (v > best || (v == best && e[k].y < idx)) { best = v; idx = e[k].y; }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -519,12 +527,12 @@ __global__ __launch_bounds__(256) void argmax_part_kernel(const int2* part, int 
     const int oi = __shfl_xor(idx, o, 64);
     if (ov > best || (ov == best && oi < idx)) { best = ov; idx = oi; }
   }
-  __shared__ float sv[4];
-  __shared__ int si[4];
+  __shared__ float sv[16];
+  __shared__ int si[16];
   if ((tid & 63) == 0) { sv[tid >> 6] = best; si[tid >> 6] = idx; }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < 16; ++w)
       if (sv[w] > best || (sv[w] == best && si[w] < idx)) { best = sv[w]; idx = si[w]; }
     out[b] = idx == 0x7fffffff ? 0 : idx;
     if (lengths) lengths[b] += len_inc;
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(256) void argmax_part_kernel(const int2* part, int 
 hipError_t launch_argmax_part(const int2* part, int B, int NB, int32_t* argmax, int32_t* lengths, hipStream_t s,
                               int len_inc) {
   if (B <= 0 || NB <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(argmax_part_kernel, dim3(B), dim3(256), 0, s, part, NB, argmax, lengths, len_inc);
+  hipLaunchKernelGGL(argmax_part_kernel, dim3(B), dim3(1024), 0, s, part, NB, argmax, lengths, len_inc);
   return hipGetLastError();
 }
 
