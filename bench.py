@@ -111,7 +111,7 @@ def main():
 
     t0 = time.time()
     W = gen_weights(DEV, dims)
-    model = Whisper(dims, list(W.values()), fp8_encoder=not args.no_fp8_encoder)
+    model = Whisper(dims, list(W.values()), mixed_fp8=not args.no_fp8_encoder)
     torch.cuda.synchronize()
     del W
     torch.cuda.empty_cache()

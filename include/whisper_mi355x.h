@@ -81,7 +81,8 @@ typedef struct {
 
 enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3,
        WHISPER_WS_ENCODE_FP8 = 4 /* whisper_encode_fp8 / whisper_encode_layers_fp8 */,
-       WHISPER_WS_DECODE_ENC = 5 /* whisper_decode_step_enc / whisper_decode_prefill_enc, batch = query rows */ };
+       WHISPER_WS_DECODE_ENC = 5 /* whisper_decode_step_enc / whisper_decode_prefill_enc, batch = query rows */,
+       WHISPER_WS_DECODE_ENC_FP8 = 6 /* whisper_decode_step_enc_fp8 */ };
 
 /* ------------------------------------------------------------------ weights
  * Logical weights are fp32 device tensors in PyTorch layout, passed as an
@@ -304,6 +305,25 @@ whisper_status whisper_decode_step_enc(const whisper_dims* dims, const void* pac
                                        const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                        const float* kv_scales, const void* enc_out, float* logits, int32_t* argmax,
                                        int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/* whisper_decode_step_enc with the decoder MLP as mixed_fp8 sites (the
+ * showcase page's precision.py card: in the mixed_fp8 preset the decoder FFN
+ * runs in fp8 E4M3, weights and activations). packed8: whisper_pack_weights_fp8
+ * output, which holds E4M3 codes of each decoder layer's fc1 and fc2 with one
+ * amax scale per tensor (fl32(amax) / 448). Per layer: a = LayerNorm(x) of
+ * each row in fp32 is quantised with its own scale (fl32(amax |a|) / 448,
+ * code = e4m3(fl32(a * fl32(1 / s)))); fc1 sums code values times weight code
+ * values in fp32, times the two scales, + bias, GELU, stored bf16; each
+ * hidden row is quantised the same way with its own scale; fc2 likewise,
+ * + bias, added to the residual stream. The rest of the step is
+ * whisper_decode_step_enc. Requires d_model and d_ffn multiples of 256 (and of
+ * 80), d_ffn a multiple of 1024. ws: whisper_workspace_size(dims, batch,
+ * WHISPER_WS_DECODE_ENC_FP8) bytes. Errors as whisper_decode_step_enc. */
+whisper_status whisper_decode_step_enc_fp8(const whisper_dims* dims, const void* packed, const void* packed8,
+                                           int batch, int kv_cap, const int32_t* tokens, int32_t* lengths,
+                                           uint8_t* kv_cache, const float* kv_scales, const void* enc_out,
+                                           float* logits, int32_t* argmax, int32_t* dev_error, void* ws,
+                                           size_t ws_bytes, void* stream);
 whisper_status whisper_decode_prefill_enc(const whisper_dims* dims, const void* packed, int batch, int n_tokens,
                                           int kv_cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                           const float* kv_scales, const void* enc_out, float* logits,
@@ -334,9 +354,10 @@ whisper_status whisper_decode_step_xq(const whisper_dims* dims, const void* pack
 /* ------------------------------------------------------------------ mixed_fp8 encoder
  * The showcase page's mixed_fp8 precision preset (precision.py card, its
  * table of layer sites): the encoder FFN (fc1, fc2) and the attention's
- * query/key/value projections take fp8 E4M3 weights and activations; the
- * attention, its output projection, the conv stem and everything in the
- * decoder keep bf16. Scales (fp8_quantize.cu card; "Learnings": per-tensor
+ * query/key/value projections take fp8 E4M3 weights and activations, and so
+ * does the decoder FFN (whisper_decode_step_enc_fp8, one activation scale per
+ * row there: a row is one token of one chunk); the attention, its output
+ * projection, the conv stem and the rest of the decoder keep bf16. Scales (fp8_quantize.cu card; "Learnings": per-tensor
  * scales from activation maxima): one per weight tensor, fl32(amax) / 448,
  * computed at pack time; one per activation tensor at each site and chunk
  * (the 1500 x d or 1500 x d_ffn activation of one 30 s clip, so a chunk's
@@ -347,10 +368,10 @@ whisper_status whisper_decode_step_xq(const whisper_dims* dims, const void* pack
  * Only for bf16 models with d_model and d_ffn multiples of 256.
  *
  * whisper_pack_weights_fp8 quantises the encoder's query, key, value, fc1 and
- * fc2 weights from the same logical fp32 tensors whisper_pack_weights takes
- * (16-byte aligned) into caller memory `packed8` of
- * whisper_packed_weights_fp8_size() bytes; ws: whisper_fp8_workspace_size()
- * bytes. The bf16 `packed` buffer is still needed (biases, LayerNorms, stem,
+ * fc2 weights and the decoder's fc1 and fc2 weights from the same logical
+ * fp32 tensors whisper_pack_weights takes (16-byte aligned) into caller
+ * memory `packed8` of whisper_packed_weights_fp8_size() bytes (0 for a model
+ * with no layers); ws: whisper_fp8_workspace_size() bytes. The bf16 `packed` buffer is still needed (biases, LayerNorms, stem,
  * out-projection). whisper_encode_fp8 and whisper_encode_layers_fp8 are
  * whisper_encode and whisper_encode_layers with the fp8 sites; ws:
  * whisper_workspace_size(dims, batch, WHISPER_WS_ENCODE_FP8) bytes. */

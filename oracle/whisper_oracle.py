@@ -17,8 +17,8 @@ Plain NumPy in float64 (floating point) with a library primitive per step
 * whisper-blaze project page, "Direct Kernel API": quantise_e4m3 returns codes
   plus a per-tensor scale; dequantise_e4m3 takes codes, scale and shape;
   layernorm_fused_residual returns (normed, total).
-* whisper_blaze showcase page, "Learnings": E4M3 saturates at 448; scales come
-  from activation maxima.
+* whisper_blaze showcase page, "Learnings": the largest E4M3 magnitude is
+  448, and the scales follow the activations' maxima.
 * "Blazingly fast whisper transcriptions with Inference Endpoints", section
   "Inference Stack": activations computed in bfloat16, KV cache stored as
   float8 (one byte per element), quantised dynamically on the way in.
@@ -35,7 +35,7 @@ from scipy.special import erf
 # =========================================================================== fp8 e4m3
 # OCP 8-bit float E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no
 # infinities, S.1111.111 is NaN, largest finite magnitude 1.75 * 2^8 = 448
-# ("E4M3 saturates at 448", whisper_blaze showcase page, "Learnings").
+# (the bound the whisper_blaze showcase page's "Learnings" gives for E4M3).
 
 E4M3_MAX = 448.0
 
@@ -533,7 +533,49 @@ def cross_kv_fp8(cross, scales, fmt="e4m3", kv_transform=None):
 
 # =========================================================================== decoder step
 
-def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None):
+_WEIGHT_CODES = {}
+
+
+def _quantised_weight(w):
+    """(scale, dequantised codes) of a weight with its per-tensor scale. The
+    result is kept per weight array (keyed by identity, checked by a weak
+    reference and the array's sum) since a decoder step quantises the same
+    weights at every step; it is the same computation each time."""
+    import weakref
+    key = id(w)
+    fp = float(np.sum(w))
+    hit = _WEIGHT_CODES.get(key)
+    if hit is not None and hit[0]() is w and hit[1] == fp and hit[2] == w.shape:
+        return hit[3], hit[4]
+    sw = e4m3_scale_from_amax(w)
+    wv = e4m3_value(e4m3_quantize(w, sw))
+    try:
+        ref = weakref.ref(w)
+    except TypeError:  # an array that takes no weak reference is not kept
+        return sw, wv
+    _WEIGHT_CODES[key] = (ref, fp, w.shape, sw, wv)
+    return sw, wv
+
+
+def fp8_linear_rows(x, w, b, rows=None, act_transform=None):
+    """A mixed_fp8 site with one activation scale per row of x: row r is
+    fp8_linear(x[r], w, b, fl32(amax(x[r])) / 448, fl32(amax(w)) / 448)
+    (per-tensor weight scale). Rows outside `rows` are left zero.
+    act_transform: as at the encoder sites (see _site)."""
+    n = x.shape[0]
+    out = np.zeros((n, w.shape[0]))
+    sw, wv = _quantised_weight(w)
+    for r in (range(n) if rows is None else rows):
+        xr = x[r] if act_transform is None else act_transform(x[r])
+        sx = e4m3_scale_from_amax(xr)
+        out[r] = (e4m3_value(e4m3_quantize(xr, sx)) @ wv.T) * (float(np.float32(sx)) * float(np.float32(sw)))
+        if b is not None:
+            out[r] += b
+    return out
+
+
+def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None, mixed_fp8=False,
+                act_transform=None):
     """One batched decoder step with teacher-forced tokens.
 
     tokens, lengths: [B] ints; lengths[b] is both the cache slot the new
@@ -551,6 +593,11 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv
     kv_transform: optional function applied to the new token's K and V before
         the codec (sensitivity analysis: how far the step moves when the
         quantised values change by a rounding, e.g. bf16_round). None: off.
+    mixed_fp8: the decoder MLP's two matmuls as mixed_fp8 sites (the
+        showcase page's precision.py card: decoder FFN in fp8 E4M3, weights
+        and activations): fp8_linear_rows, a per-tensor weight scale and one
+        activation scale per row (one token of one chunk). act_transform
+        applies to those sites' inputs (sensitivity runs).
 
     The new token's K and V are written first and then read back from the
     cache with the rest (quantise-on-write, dequantise-on-read).
@@ -608,14 +655,19 @@ def decode_step(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv
                 oc[b, h * dh:(h + 1) * dh] = softmax(kc[b][h] @ qh / np.sqrt(dh)) @ vc[b][h]
         x = x + linear(oc, W[p + "cross_attn.out.weight"], W[p + "cross_attn.out.bias"])
         m = layer_norm(x, W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
-        x = x + linear(gelu(linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"])),
-                       W[p + "mlp.2.weight"], W[p + "mlp.2.bias"])
+        if mixed_fp8:
+            hdn = gelu(fp8_linear_rows(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"], rows, act_transform))
+            x = x + fp8_linear_rows(hdn, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"], rows, act_transform)
+        else:
+            x = x + linear(gelu(linear(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"])),
+                           W[p + "mlp.2.weight"], W[p + "mlp.2.bias"])
     y = layer_norm(x, W["decoder.ln.weight"], W["decoder.ln.bias"])
     logits = y @ W["decoder.token_embedding"].T
     return logits, {"kv": kv_new, "codes": codes, "x": x}
 
 
-def decode_prefill(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None):
+def decode_prefill(W, n_heads, tokens, lengths, cache, scales, cross, rows=None, kv_transform=None, mixed_fp8=False,
+                   act_transform=None):
     """P prompt tokens per row fed causally: token p of row b goes to slot and
     position lengths[b] + p and attends over slots 0 .. lengths[b] + p, which is
     P successive teacher-forced steps (the decoder's causal self-attention
@@ -628,7 +680,7 @@ def decode_prefill(W, n_heads, tokens, lengths, cache, scales, cross, rows=None,
     logits = None
     for p in range(tokens.shape[1]):
         logits, tr = decode_step(W, n_heads, tokens[:, p], lengths, cache, scales, cross, rows=rows,
-                                 kv_transform=kv_transform)
+                                 kv_transform=kv_transform, mixed_fp8=mixed_fp8, act_transform=act_transform)
         traces.append(tr)
         lengths = lengths + 1
     return logits, traces

@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("WHISPER_MI355X_LIB") or os.path.join(_HERE, "libwhisp
 
 WHISPER_F32, WHISPER_BF16 = 0, 1
 WHISPER_FP8_E4M3, WHISPER_FP8_E5M2 = 0, 1
-WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE, WS_ENCODE_FP8, WS_DECODE_ENC = 0, 1, 2, 3, 4, 5
+WS_LOGMEL, WS_ENCODE, WS_CROSS_KV, WS_DECODE, WS_ENCODE_FP8, WS_DECODE_ENC, WS_DECODE_ENC_FP8 = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = [
     "whisper_weight_count", "whisper_packed_weights_size", "whisper_pack_weights", "whisper_workspace_size",
@@ -33,6 +33,7 @@ EXPORTS = [
     "whisper_logmel_chunked",
     "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
     "whisper_debug_kv_disarm", "whisper_decode_step_noalloc", "whisper_decode_step_enc", "whisper_decode_prefill_enc",
+    "whisper_decode_step_enc_fp8",
 ]
 
 DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
@@ -86,6 +87,7 @@ _SIG = {
     "whisper_decode_step_xq": (I, [P, P, I, I, P, P, P, P, P, P, I, P, P, P, P, Z, P]),
     "whisper_decode_step_noalloc": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P]),
     "whisper_decode_step_enc": (I, [P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_decode_step_enc_fp8": (I, [P, P, P, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_prefill_enc": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_decode_prefill": (I, [P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_fp8_workspace_size": (Z, []),
@@ -248,6 +250,14 @@ def whisper_decode_step_enc(dims, packed, batch, kv_cap, tokens, lengths, kv_cac
     _check(lib().whisper_decode_step_enc(dp, _p(packed), batch, kv_cap, _p(tokens), _p(lengths), _p(kv_cache),
                                          _p(kv_scales), _p(enc_out), _p(logits), _p(argmax), _p(dev_error), _p(ws),
                                          ws_bytes, _stream(stream)))
+
+
+def whisper_decode_step_enc_fp8(dims, packed, packed8, batch, kv_cap, tokens, lengths, kv_cache, kv_scales, enc_out,
+                                logits, argmax, dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_step_enc_fp8(dp, _p(packed), _p(packed8), batch, kv_cap, _p(tokens), _p(lengths),
+                                             _p(kv_cache), _p(kv_scales), _p(enc_out), _p(logits), _p(argmax),
+                                             _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
 
 
 def whisper_decode_prefill_enc(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, enc_out,

@@ -166,10 +166,16 @@ EncWS enc_ws(const whisper_dims* d, int B, bool fp8 = false) {
   return W;
 }
 
-// E4M3 weights of the mixed_fp8 encoder sites, per layer: query, key, value
+// E4M3 weights of the mixed_fp8 sites. Encoder, per layer: query, key, value
 // codes [3d, d] (one block, as the fused QKV), fc1 [f, d], fc2 [d, f]; then
-// per layer 8 fp32 scales (query, key, value, fc1, fc2, 3 unused).
-struct Packed8 { std::vector<size_t> qkv, w1, w2; size_t scales = 0, total = 0; };
+// per layer 8 fp32 scales (query, key, value, fc1, fc2, 3 unused). Decoder
+// MLP, per layer: fc1 codes [f, d] and fc2 codes [d, f] in the decode GEMM's
+// fragment order, fc1's bias [f] fp32 (unfolded: the fp8 site takes LN(x)
+// explicitly); then per layer 2 fp32 scales (fc1, fc2).
+struct Packed8 {
+  std::vector<size_t> qkv, w1, w2, dw1, dw2, db1;
+  size_t scales = 0, dscales = 0, total = 0;
+};
 Packed8 layout8(const whisper_dims* d) {
   Packed8 P;
   const size_t D = d->d_model, F = d->d_ffn;
@@ -180,7 +186,14 @@ Packed8 layout8(const whisper_dims* d) {
     P.w1.push_back(take(F * D));
     P.w2.push_back(take(D * F));
   }
-  P.scales = take((size_t)d->n_enc_layers * 8 * 4);
+  P.scales = take((size_t)std::max(d->n_enc_layers, 1) * 8 * 4);
+  const size_t F16 = (F + 15) & ~(size_t)15, D16 = (D + 15) & ~(size_t)15;  // whole 16-row fragments
+  for (int l = 0; l < d->n_dec_layers; ++l) {
+    P.dw1.push_back(take(F16 * D));
+    P.dw2.push_back(take(D16 * F));
+    P.db1.push_back(take(F * 4));
+  }
+  P.dscales = take((size_t)std::max(d->n_dec_layers, 1) * 2 * 4);
   P.total = off;
   return P;
 }
@@ -214,8 +227,10 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
 // [n_wg * kmax][H][2] fp32, and the combined u [M][H][d], after the step's own
 // workspace.
 constexpr int XE_CU = 256;  // compute units the frame sequence is shared over
-struct DecEncWS { DecWS base; size_t qp, upart, ml, u, total; XePlan plan; };
-DecEncWS dec_ws_enc(const whisper_dims* d, int M) {
+// With the decoder MLP as mixed_fp8 sites (fp8): the quantised LN(x) rows
+// [M][d] bf16, their scales [M], and per layer the hidden rows' amax [L][M].
+struct DecEncWS { DecWS base; size_t qp, upart, ml, u, aq = 0, srow = 0, amx8 = 0, total; XePlan plan; };
+DecEncWS dec_ws_enc(const whisper_dims* d, int M, bool fp8 = false) {
   DecEncWS W;
   W.base = dec_ws(d, M);
   size_t off = W.base.total;
@@ -227,6 +242,11 @@ DecEncWS dec_ws_enc(const whisper_dims* d, int M) {
   W.upart = take(slots * d->n_heads * d->d_model * 2);
   W.ml = take(slots * d->n_heads * 2 * 4);
   W.u = take(rows * 2);
+  if (fp8) {
+    W.aq = take((size_t)M * d->d_model * 2);
+    W.srow = take((size_t)M * 4);
+    W.amx8 = take((size_t)d->n_dec_layers * M * 4);
+  }
   W.total = off;
   return W;
 }
@@ -415,7 +435,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
                                  const float* kv_scales, const void* cross_kv, float* LG, int32_t* argmax,
                                  int32_t* dev_error, void* ws, hipStream_t s, const uint8_t* xcodes = nullptr,
                                  const float* xscales = nullptr, int R = 1, int xfmt = FP8_E4M3,
-                                 const void* enc = nullptr, const DecEncWS* XW = nullptr) {
+                                 const void* enc = nullptr, const DecEncWS* XW = nullptr,
+                                 const void* packed8 = nullptr) {
   // B batch rows of the cache; R tokens per row (a prefill when R > 1): the
   // activations have B * R rows, row m being token m % R of batch row m / R
   const int Bc = B;
@@ -430,6 +451,8 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   WH_CHECK(kvtrace_check(L, B, D, "decode"));
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
+  const Packed8 P8 = packed8 ? layout8(d) : Packed8{};
+  if (packed8) WH_TRY(launch_fill_f32(at<float>(ws, XW->amx8), 0.f, (size_t)L * B, s));  // the rows' amax start at 0
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
                   u16_t* out, float* out_f32, int layer, bool split = false, int a_group = 0) {
     DecGemmParams g{};
@@ -494,8 +517,30 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
       }
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.woc, Lw.boc, 0, D, D, ATT, nullptr, nullptr, l));
-    WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
-    WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l, true));
+    if (packed8) {
+      // the MLP as mixed_fp8 sites: LN(x) quantised per row, fc1 with E4M3
+      // weights + GELU (recording each hidden row's amax), fc2 quantising its
+      // input rows in registers, split-K + residual
+      u16_t* AQ = at<u16_t>(ws, XW->aq);
+      float* SROW = at<float>(ws, XW->srow);
+      uint32_t* AMX = at<uint32_t>(ws, XW->amx8) + (size_t)l * B;
+      const float* dsc = at<float>(packed8, P8.dscales) + 2 * l;
+      WH_TRY(launch_ln_quant_rows(X, at<float>(packed, Lw.ln3g), at<float>(packed, Lw.ln3b), B, D, AQ, SROW, s));
+      DecGemmParams g1{};
+      g1.M = B; g1.N = F; g1.K = D; g1.A = AQ; g1.lda = D; g1.X = X; g1.out = HF;
+      g1.W8 = at<uint8_t>(packed8, P8.dw1[l]); g1.w_scale8 = dsc; g1.row_scale = SROW; g1.amax_out = AMX;
+      g1.bias = at<float>(packed8, P8.db1[l]);
+      WH_TRY(launch_gemm_dec_fp8(DEPI_GELU, g1, s));
+      DecGemmParams g2{};
+      g2.M = B; g2.N = D; g2.K = F; g2.A = HF; g2.lda = F; g2.X = X;
+      g2.W8 = at<uint8_t>(packed8, P8.dw2[l]); g2.w_scale8 = dsc + 1; g2.aq_amax = AMX;
+      g2.bias = at<float>(packed, Lw.b2);
+      g2.ks = DEC_KSPLIT; g2.part = at<float>(ws, W.part); g2.cnt = CNT;
+      WH_TRY(launch_gemm_dec_fp8(DEPI_RESID, g2, s));
+    } else {
+      WH_TRY(gemm(PRO_X, DEPI_GELU, Lw.w1, Lw.b1, Lw.c1w1, F, D, nullptr, HF, nullptr, l));
+      WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.w2, Lw.b2, 0, D, F, HF, nullptr, nullptr, l, true));
+    }
   }
   if (R > 1) {  // vocabulary projection and argmax of each batch row's last position only
     float* XG = at<float>(ws, W.xg);
@@ -672,6 +717,7 @@ size_t whisper_workspace_size(const whisper_dims* d, int batch, int which) {
     case WHISPER_WS_DECODE: return dec_ws(d, batch).total;
     case WHISPER_WS_ENCODE_FP8: return enc_ws(d, batch, true).total;
     case WHISPER_WS_DECODE_ENC: return dec_ws_enc(d, batch).total;
+    case WHISPER_WS_DECODE_ENC_FP8: return dec_ws_enc(d, batch, true).total;
   }
   return 0;
 }
@@ -861,7 +907,7 @@ whisper_status whisper_encode_layers_fp8(const whisper_dims* d, const void* pack
 }
 
 size_t whisper_packed_weights_fp8_size(const whisper_dims* d) {
-  if (check_dims(d) != WHISPER_OK || d->n_enc_layers <= 0) return 0;
+  if (check_dims(d) != WHISPER_OK || (d->n_enc_layers <= 0 && d->n_dec_layers <= 0)) return 0;
   return layout8(d).total;
 }
 
@@ -869,7 +915,7 @@ whisper_status whisper_pack_weights_fp8(const whisper_dims* d, const float* cons
                                         size_t ws_bytes, void* stream) {
   WH_CHECK(check_dims(d));
   WH_CHECK(check_fp8_model(d, packed8, "pack_fp8"));
-  if (d->n_enc_layers <= 0) return fail(WHISPER_ERR_SHAPE, "pack_fp8: no encoder layers");
+  if (d->n_enc_layers <= 0 && d->n_dec_layers <= 0) return fail(WHISPER_ERR_SHAPE, "pack_fp8: no layers");
   if (!w) return fail(WHISPER_ERR_INVALID_ARG, "pack_fp8: weight table is NULL");
   WH_CHECK(check_ws(ws, ws_bytes, whisper_fp8_workspace_size(), "pack_fp8"));
   const int n = weight_count(d);
@@ -895,6 +941,20 @@ whisper_status whisper_pack_weights_fp8(const whisper_dims* d, const float* cons
     WH_TRY(q(w[i + 5], D * D, qkv + 2 * D * D, sc + 8 * l + 2));  // attn.value.weight
     WH_TRY(q(w[i + 11], F * D, at<uint8_t>(packed8, P8.w1[l]), sc + 8 * l + 3));  // mlp.0.weight
     WH_TRY(q(w[i + 13], D * F, at<uint8_t>(packed8, P8.w2[l]), sc + 8 * l + 4));  // mlp.2.weight
+  }
+  // decoder MLP: per tensor amax scale, then codes in the decode GEMM's fragment order
+  const int dec0 = (d->n_enc_layers > 0 ? 4 + 15 * d->n_enc_layers + 2 : 0) + 2;  // after the token and position tables
+  float* dsc = at<float>(packed8, P8.dscales);
+  for (int l = 0; l < d->n_dec_layers; ++l) {
+    const int i = dec0 + 24 * l;
+    const size_t blocks1 = (F * D + 255) / 256;
+    WH_TRY(launch_amax(ACT_F32, FP8_E4M3, w[i + 20], F * D, (float*)ws, (int)std::min<size_t>(blocks1, 1024),
+                       dsc + 2 * l, s));  // mlp.0.weight
+    WH_TRY(launch_pack_dec_weight_fp8(w[i + 20], (int)F, (int)D, dsc + 2 * l, at<void>(packed8, P8.dw1[l]), s));
+    WH_TRY(launch_amax(ACT_F32, FP8_E4M3, w[i + 22], D * F, (float*)ws, (int)std::min<size_t>(blocks1, 1024),
+                       dsc + 2 * l + 1, s));  // mlp.2.weight
+    WH_TRY(launch_pack_dec_weight_fp8(w[i + 22], (int)D, (int)F, dsc + 2 * l + 1, at<void>(packed8, P8.dw2[l]), s));
+    WH_TRY(launch_copy_f32(w[i + 21], at<float>(packed8, P8.db1[l]), F, s));  // mlp.0.bias, unfolded
   }
   return WHISPER_OK;
 }
@@ -1086,7 +1146,8 @@ whisper_status whisper_decode_step_noalloc(const whisper_dims* d, const void* pa
 static whisper_status prefill_impl(const char* who, const whisper_dims* d, const void* packed, int B, int n_tokens,
                                    int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                    const float* kv_scales, const void* cross_kv, const void* enc, float* logits,
-                                   int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+                                   int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes, void* stream,
+                                   const void* packed8 = nullptr) {
   const std::string w(who);
   WH_CHECK(check_dims(d));
   if (d->act != WHISPER_BF16) return fail(WHISPER_ERR_DTYPE, w + ": bf16 models only");
@@ -1100,14 +1161,21 @@ static whisper_status prefill_impl(const char* who, const whisper_dims* d, const
   WH_CHECK(check_ptrs4({tokens, lengths, kv_scales, argmax}, who));
   if (logits && !aligned16(logits)) return fail(WHISPER_ERR_ALIGN, w + ": logits not 16-byte aligned");
   if (dev_error && ((uintptr_t)dev_error & 3u)) return fail(WHISPER_ERR_ALIGN, w + ": dev_error not 4-byte aligned");
+  if (packed8) {
+    WH_CHECK(check_fp8_model(d, packed8, who));
+    if (!enc) return fail(WHISPER_ERR_INVALID_ARG, w + ": the fp8 MLP sites run with the encoder output");
+    if (d->d_ffn % 80 || d->d_ffn % (32 * 8 * DEC_KSPLIT) || d->d_model % 80)
+      return fail(WHISPER_ERR_SHAPE, w + ": d_model and d_ffn must be multiples of 80, d_ffn of 1024");
+  }
   const int M = B * n_tokens;
-  const DecEncWS XW = enc ? dec_ws_enc(d, M) : DecEncWS{dec_ws(d, M)};
+  const DecEncWS XW = enc ? dec_ws_enc(d, M, packed8 != nullptr) : DecEncWS{dec_ws(d, M)};
   WH_CHECK(check_ws(ws, ws_bytes, enc ? XW.total : XW.base.total, who));
   (void)hipGetLastError();
   const Packed P = layout(d);
   float* LG = logits ? logits : at<float>(ws, XW.base.logits);
   return decode_step_fused(d, packed, P, XW.base, B, cap, tokens, lengths, kv_cache, kv_scales, cross_kv, LG, argmax,
-                           dev_error, ws, S(stream), nullptr, nullptr, n_tokens, FP8_E4M3, enc, enc ? &XW : nullptr);
+                           dev_error, ws, S(stream), nullptr, nullptr, n_tokens, FP8_E4M3, enc, enc ? &XW : nullptr,
+                           packed8);
 }
 
 extern "C" {
@@ -1126,6 +1194,15 @@ whisper_status whisper_decode_step_enc(const whisper_dims* d, const void* packed
                                        int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
   return prefill_impl("decode_step_enc", d, packed, B, 1, cap, tokens, lengths, kv_cache, kv_scales, nullptr, enc_out,
                       logits, argmax, dev_error, ws, ws_bytes, stream);
+}
+
+whisper_status whisper_decode_step_enc_fp8(const whisper_dims* d, const void* packed, const void* packed8, int B,
+                                           int cap, const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
+                                           const float* kv_scales, const void* enc_out, float* logits,
+                                           int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  return prefill_impl("decode_step_enc_fp8", d, packed, B, 1, cap, tokens, lengths, kv_cache, kv_scales, nullptr,
+                      enc_out, logits, argmax, dev_error, ws, ws_bytes, stream, packed8);
 }
 
 whisper_status whisper_decode_prefill_enc(const whisper_dims* d, const void* packed, int B, int n_tokens, int cap,

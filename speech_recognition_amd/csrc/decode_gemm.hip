@@ -62,7 +62,21 @@ __device__ __forceinline__ void amax_step(float& v, int& idx) {
   }
 }
 
-template <int PRO, int EPI, int MB, int CB, int NS>
+// Eight E4M3 codes -> eight bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(const uint2 w) {
+  float a[4], b[4];
+  e4m3x4_decode(w.x, a);
+  e4m3x4_decode(w.y, b);
+  auto pk = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
+  return make_uint4(pk(a[0], a[1]), pk(a[2], a[3]), pk(b[0], b[1]), pk(b[2], b[3]));
+}
+// The E4M3 scale of an amax (fp32 bits): fl32(amax) / 448, 1 for 0.
+__device__ __forceinline__ float e4m3_scale_of(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? a / 448.0f : 1.0f;
+}
+
+template <int PRO, int EPI, int MB, int CB, int NS, bool F8 = false>
 __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
   constexpr int MR = MB * 16;
   constexpr bool XIN = PRO == PRO_X;
@@ -94,8 +108,21 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   // contiguous 1 KB read of whole cache lines
   const int NF = (N + 15) >> 4;
   const u16* wfr[CB];
+  const uint8_t* wfr8[CB];  // F8: the same element offsets, one byte each
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) wfr[cb] = p.W + (long)min((n0 >> 4) + cb, NF - 1) * S * 512 + lane * 8;
+  for (int cb = 0; cb < CB; ++cb) {
+    const long fo = (long)min((n0 >> 4) + cb, NF - 1) * S * 512 + lane * 8;
+    if constexpr (F8) wfr8[cb] = p.W8 + fo;
+    else wfr[cb] = p.W + fo;
+  }
+  // F8 with aq_amax: the reciprocal scale of this lane's A row (in-register quantisation)
+  float aq_inv[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    aq_inv[mb] = 1.f;
+    if constexpr (F8)
+      if (p.aq_amax) aq_inv[mb] = 1.0f / e4m3_scale_of(p.aq_amax[min(m0 + mb * 16 + (lane & 15), M - 1)]);
+  }
   long arow[MB];
   // grouped A: this column tile's rows of A start at its group's offset
   const long agoff = p.a_group > 0 ? (long)(n0 / p.a_group) * p.a_group_stride : 0;
@@ -122,6 +149,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   const int emb = ewave ? wave / CB : 0, ecb = ewave ? wave - (wave / CB) * CB : 0;
   const int en = n0 + ecb * 16 + (lane & 15);  // this lane's output column
   float e_bias = 0.f, e_c1 = 0.f, e_x[4] = {0.f, 0.f, 0.f, 0.f}, e_inv[2] = {0.f, 0.f};
+  float e_rs[4] = {1.f, 1.f, 1.f, 1.f};  // F8: row scale x weight scale
   int e_pos[4] = {0, 0, 0, 0};
   if (ewave) {
     const int n = min(en, N - 1);
@@ -132,6 +160,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
       const int m = min(m0 + emb * 16 + (lane >> 4) * 4 + r, M - 1);
       if constexpr (RES) e_x[r] = p.X[dec_x_index(m, n, N)];
       if constexpr (QKV) e_pos[r] = p.lengths[m / RPB] + m % RPB;
+      if constexpr (F8) e_rs[r] = (p.aq_amax ? e4m3_scale_of(p.aq_amax[m]) : p.row_scale[m]) * p.w_scale8[0];
     }
     if constexpr (QKV) {
       e_inv[0] = 1.0f / p.kv_scales[p.kv_layer * 2];
@@ -150,13 +179,17 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 
   // operand slots: step j of this wave lives in slot j % NSLOT
   constexpr int NSLOT = NS > 0 ? DG_DEPTH + 1 : 1;
-  uint4 wv[NSLOT][CB];
+  uint4 wv[F8 ? 1 : NSLOT][CB];
+  uint2 w8[F8 ? NSLOT : 1][CB];  // F8: eight codes per lane and fragment
   float4 xa[XIN ? NSLOT : 1][MB], xb[XIN ? NSLOT : 1][MB];
   uint4 av[XIN ? 1 : NSLOT][MB];
 #define DG_ISSUE(J, SL)                                                                        \
   {                                                                                            \
     const int k_ = (s0 + (J)) * 32;                                                            \
-    _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) wv[SL][cb] = *(const uint4*)(wfr[cb] + k_ * 16); \
+    _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) {                                        \
+      if constexpr (F8) w8[F8 ? SL : 0][cb] = *(const uint2*)(wfr8[cb] + k_ * 16);              \
+      else wv[F8 ? 0 : SL][cb] = *(const uint4*)(wfr[cb] + k_ * 16);                            \
+    }                                                                                          \
     _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                        \
       if constexpr (XIN) {                                                                     \
         const float* x_ = p.X + xoff[mb] + k_ * 16;                                             \
@@ -182,8 +215,8 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
         const bf16x8 ah_ = bitcast<bf16x8>(make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]));        \
         const bf16x8 al_ = bitcast<bf16x8>(make_uint4(lo_[0], lo_[1], lo_[2], lo_[3]));        \
         _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) {                                    \
-          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah_, bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
-          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al_, bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah_, bitcast<bf16x8>(wv[F8 ? 0 : SL][cb]), acc[mb][cb], 0, 0, 0); \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al_, bitcast<bf16x8>(wv[F8 ? 0 : SL][cb]), acc[mb][cb], 0, 0, 0); \
         }                                                                                      \
         /* shifted sums: S1 += x - c, S2 += (x - c)^2, c = this lane's first value of the row */ \
         if ((J) == 0) st_c[mb] = a_.x;                                                         \
@@ -193,9 +226,26 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
           st_s2[mb] = fmaf(d_, d_, st_s2[mb]);                                                 \
         }                                                                                      \
       } else {                                                                                 \
-        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb)                                      \
-          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[XIN ? 0 : SL][mb]), \
-                                                                bitcast<bf16x8>(wv[SL][cb]), acc[mb][cb], 0, 0, 0); \
+        uint4 a8_ = av[XIN ? 0 : SL][mb];                                                       \
+        if constexpr (F8) {                                                                    \
+          if (p.aq_amax) { /* quantise the bf16 row in registers: the code values, as bf16 */  \
+            const uint32_t q_[4] = {a8_.x, a8_.y, a8_.z, a8_.w};                                \
+            uint32_t o_[4];                                                                    \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
+              const float lo_ = e4m3_decode(e4m3_encode(__uint_as_float(q_[i] << 16) * aq_inv[mb]));        \
+              const float hi_ = e4m3_decode(e4m3_encode(__uint_as_float(q_[i] & 0xffff0000u) * aq_inv[mb])); \
+              o_[i] = (__float_as_uint(lo_) >> 16) | (__float_as_uint(hi_) & 0xffff0000u);     \
+            }                                                                                  \
+            a8_ = make_uint4(o_[0], o_[1], o_[2], o_[3]);                                      \
+          }                                                                                    \
+        }                                                                                      \
+        _Pragma("unroll") for (int cb = 0; cb < CB; ++cb) {                                    \
+          uint4 wb_;                                                                           \
+          if constexpr (F8) wb_ = fp8x8_to_bf16x8(w8[F8 ? SL : 0][cb]);                         \
+          else wb_ = wv[F8 ? 0 : SL][cb];                                                      \
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a8_), bitcast<bf16x8>(wb_), \
+                                                                acc[mb][cb], 0, 0, 0);         \
+        }                                                                                      \
       }                                                                                        \
     }                                                                                          \
   }
@@ -297,7 +347,23 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int ml = emb * 16 + (lane >> 4) * 4 + r;
-    vr[r] = XIN ? s_rs[ml] * (v4[r] - s_mu[ml] * e_c1) + e_bias : v4[r] + e_bias;
+    vr[r] = XIN ? s_rs[ml] * (v4[r] - s_mu[ml] * e_c1) + e_bias : (F8 ? v4[r] * e_rs[r] : v4[r]) + e_bias;
+  }
+  if constexpr (F8 && EPI == DEPI_GELU) {
+    if (p.amax_out) {
+      // the next site's scale: each row's max |stored bf16 value| over the
+      // block's 16 columns (DPP permutes as in the argmax), joined by atomic max
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = en < N ? fabsf(__uint_as_float((uint32_t)f2bf(gelu_erf(vr[r])) << 16)) : 0.f;
+        a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, true)));
+        a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, true)));
+        a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x141, 0xF, 0xF, true)));
+        a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x140, 0xF, 0xF, true)));
+        const int m = m0 + emb * 16 + (lane >> 4) * 4 + r;
+        if ((lane & 15) == 0 && m < M) atomicMax(p.amax_out + m, __float_as_uint(a));
+      }
+    }
   }
   if constexpr (EPI == DEPI_F32) {
     if (p.amax_part) {
@@ -365,22 +431,33 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   }
 }
 
-template <int PRO, int EPI, int MB, int CB, int NS>
+template <int PRO, int EPI, int MB, int CB, int NS, bool F8 = false>
 static hipError_t dec_launch_ns(const DecGemmParams& p, hipStream_t s) {
   const int CT = (p.N + 16 * CB - 1) / (16 * CB), RT = (p.M + 16 * MB - 1) / (16 * MB);
   const dim3 grid(((CT + 7) / 8) * 8 * RT * (p.ks > 1 ? p.ks : 1));
-  hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NS>), grid, dim3(DG_WAVES * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_dec_kernel<PRO, EPI, MB, CB, NS, F8>), grid, dim3(DG_WAVES * 64), 0, s, p);
   return hipGetLastError();
 }
 
 // The pipelined kernel for the two K of the model (d = 1280 -> 5 steps per
 // wave, 4d = 5120 -> 20), the generic one otherwise.
-template <int PRO, int EPI, int MB, int CB>
+template <int PRO, int EPI, int MB, int CB, bool F8 = false>
 static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
   const int S = p.K / 32 / (p.ks > 1 ? p.ks : 1);  // k-steps of one workgroup's slice
-  if (S == DG_WAVES * 5) return dec_launch_ns<PRO, EPI, MB, CB, 5>(p, s);
-  if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20>(p, s);
-  return dec_launch_ns<PRO, EPI, MB, CB, 0>(p, s);
+  if (S == DG_WAVES * 5) return dec_launch_ns<PRO, EPI, MB, CB, 5, F8>(p, s);
+  if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20, F8>(p, s);
+  return dec_launch_ns<PRO, EPI, MB, CB, 0, F8>(p, s);
+}
+
+hipError_t launch_gemm_dec_fp8(DecEpi epi, const DecGemmParams& p, hipStream_t s) {
+  if (p.M <= 0 || p.M > 4096 || p.N <= 0 || p.K <= 0 || p.K % 32 || !p.W8 || !p.w_scale8 || !p.A)
+    return hipErrorInvalidValue;
+  if (!p.row_scale == !p.aq_amax) return hipErrorInvalidValue;  // exactly one source of the row scale
+  if (p.N % 80) return hipErrorInvalidValue;                     // 16 x 80 tiles
+  if (epi == DEPI_GELU && p.ks <= 1) return dec_launch_t<PRO_A, DEPI_GELU, 1, 5, true>(p, s);
+  if (epi == DEPI_RESID && p.ks > 1 && p.part && p.cnt && p.ks <= 16 && (p.K / 32) % (p.ks * DG_WAVES) == 0)
+    return dec_launch_t<PRO_A, DEPI_RESID, 1, 5, true>(p, s);
+  return hipErrorInvalidValue;
 }
 
 // Tile shapes with MB * CB <= 4, and one 16-row block of 80 columns (larger
@@ -493,6 +570,89 @@ hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStr
   if (N <= 0) return hipSuccess;
   if (K <= 0 || K % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack_frag_kernel, dim3((N + 15) & ~15), dim3(256), 0, s, W, N, K, (u16*)Wf);
+  return hipGetLastError();
+}
+
+// E4M3 codes of a decoder weight W [N, K] with the per-tensor scale
+// scale[0] (code = e4m3(fl32(w * fl32(1 / s)))), in the fragment order of
+// dec_frag_index, one byte per element; rows N .. 16*ceil(N/16) - 1 are zero.
+__global__ __launch_bounds__(256) void pack_frag8_kernel(const float* W, int N, int K, const float* scale,
+                                                         uint8_t* Wf) {
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const float inv = 1.0f / scale[0];
+  for (int k = tid; k < K; k += 256)
+    Wf[dec_frag_index(n, k, K)] = n < N ? (uint8_t)e4m3_encode(W[(long)n * K + k] * inv) : (uint8_t)0;
+}
+
+hipError_t launch_pack_dec_weight_fp8(const float* W, int N, int K, const float* scale, void* Wf, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (K <= 0 || K % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_frag8_kernel, dim3((N + 15) & ~15), dim3(256), 0, s, W, N, K, scale, (uint8_t*)Wf);
+  return hipGetLastError();
+}
+
+// The decoder MLP's fp8 input site: per row m of the fp32 residual stream X
+// (16-row tiles, dec_x_index), a = LayerNorm(x) (fp32 two-pass statistics,
+// biased variance, eps 1e-5), its scale s = fl32(amax |a|) / 448 (1 for an
+// all-zero row), and the values of the codes e4m3(fl32(a * fl32(1 / s))),
+// stored as bf16 (every E4M3 value is a bf16 value) in A [M, K]; s to
+// srow[m]. One workgroup of 256 threads per row, K <= 2048.
+__global__ __launch_bounds__(256) void ln_quant_rows_kernel(const float* __restrict__ X, const float* __restrict__ g,
+                                                            const float* __restrict__ b, int K, u16* __restrict__ A,
+                                                            float* __restrict__ srow) {
+  constexpr int PER = 8;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  __shared__ float red[8];
+  float v[PER];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int k = tid + i * 256;
+    v[i] = k < K ? X[dec_x_index(m, k, K)] : 0.f;
+    sum += v[i];
+  }
+  auto block_sum = [&](float x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = x;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+  };
+  const float mu = block_sum(sum) / (float)K;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int k = tid + i * 256;
+    const float dlt = k < K ? v[i] - mu : 0.f;
+    sq = fmaf(dlt, dlt, sq);
+  }
+  const float r = 1.0f / sqrtf(block_sum(sq) / (float)K + 1e-5f);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int k = tid + i * 256;
+    v[i] = k < K ? (v[i] - mu) * r * g[k] + b[k] : 0.f;
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  __syncthreads();
+  if ((tid & 63) == 0) red[4 + (tid >> 6)] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float inv = 1.0f / sc;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int k = tid + i * 256;
+    if (k < K) A[(long)m * K + k] = (u16)(__float_as_uint(e4m3_decode(e4m3_encode(v[i] * inv))) >> 16);
+  }
+  if (tid == 0) srow[m] = sc;
+}
+
+hipError_t launch_ln_quant_rows(const float* X, const float* g, const float* b, int M, int K, void* A, float* srow,
+                                hipStream_t s) {
+  if (M <= 0 || K <= 0 || K > 2048 || K % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ln_quant_rows_kernel, dim3(M), dim3(256), 0, s, X, g, b, K, (u16*)A, srow);
   return hipGetLastError();
 }
 

@@ -90,6 +90,15 @@ struct DecGemmParams {
   // (A + m * lda + (n / a_group) * a_group_stride); a_group must be a
   // multiple of the workgroup's column tile
   int a_group; long a_group_stride;
+  // fp8 weights (launch_gemm_dec_fp8): W8 E4M3 codes [N, K] in fragment order
+  // with the per-tensor scale w_scale8[0]; the products are the codes' values,
+  // and the epilogue multiplies by (row scale) * w_scale8[0] before the bias.
+  // Row scale: row_scale[m] (A already holds code values), or, with aq_amax,
+  // fl32(amax) / 448 of aq_amax[m] (fp32 bits; 1 for 0), the A row being
+  // quantised in registers as e4m3(fl32(a * fl32(1 / s))). amax_out (DEPI_GELU,
+  // NULL: off): each row's max |stored bf16 output| joins amax_out[m] (fp32
+  // bits, atomic max; the caller zeroes it).
+  const uint8_t* W8; const float* w_scale8; const float* row_scale; const uint32_t* aq_amax; uint32_t* amax_out;
   // DEPI_F32 (NULL: off): per row, the largest value of each 16-column block
   // and its column (lowest on ties; NaN never chosen), [M][ceil(N / 16)] as
   // (float bits, column); argmax_part reduces them
@@ -97,6 +106,13 @@ struct DecGemmParams {
 };
 void dec_gemm_tiles(int M, int N, int& mb, int& cb);
 hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int mb, int cb, hipStream_t s);
+// The decoder MLP as mixed_fp8 sites (bf16 activations A, fp8 weights W8):
+// DEPI_GELU (up-projection, 80-column tiles) or DEPI_RESID with split-K over
+// DEC_KSPLIT workgroups (down-projection).
+hipError_t launch_gemm_dec_fp8(DecEpi epi, const DecGemmParams& p, hipStream_t s);
+hipError_t launch_pack_dec_weight_fp8(const float* W, int N, int K, const float* scale, void* Wf, hipStream_t s);
+hipError_t launch_ln_quant_rows(const float* X, const float* g, const float* b, int M, int K, void* A, float* srow,
+                                hipStream_t s);
 hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,
                           void* Wf, float* c1, float* b2, hipStream_t s);
 hipError_t launch_pack_dec_weight(const float* W, int N, int K, void* Wf, hipStream_t s);

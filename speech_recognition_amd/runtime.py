@@ -22,10 +22,11 @@ def _empty_bytes(n, device):
 class Whisper:
     """Packed weights plus per-call workspaces for one model shape."""
 
-    def __init__(self, dims, logical_weights, device="cuda", fp8_encoder=False):
+    def __init__(self, dims, logical_weights, device="cuda", mixed_fp8=False):
         """logical_weights: fp32 device tensors in the ABI's canonical order.
-        fp8_encoder: also pack the E4M3 weights of the mixed_fp8 encoder sites
-        (encode_fp8 / encode_layers_fp8)."""
+        mixed_fp8: also pack the E4M3 weights of the mixed_fp8 sites (encoder
+        query/key/value and MLP: encode_fp8 / encode_layers_fp8; decoder MLP:
+        decode_step with a DecodeState made with ffn_fp8=True)."""
         self.dims = dims
         self.device = torch.device(device)
         n = L.whisper_weight_count(dims)
@@ -37,7 +38,7 @@ class Whisper:
         self.packed = _empty_bytes(L.whisper_packed_weights_size(dims), self.device)
         L.whisper_pack_weights(dims, logical_weights, self.packed)
         self.packed8 = None
-        if fp8_encoder:
+        if mixed_fp8:
             self.packed8 = _empty_bytes(L.whisper_packed_weights_fp8_size(dims), self.device)
             ws = torch.empty(L.whisper_fp8_workspace_size(), dtype=torch.uint8, device=self.device)
             L.whisper_pack_weights_fp8(dims, logical_weights, self.packed8, ws, ws.numel())
@@ -83,7 +84,7 @@ class Whisper:
         return enc
 
     def encode_fp8(self, mel, out=None):
-        """encode with the mixed_fp8 sites in E4M3 (needs fp8_encoder=True)."""
+        """encode with the mixed_fp8 sites in E4M3 (needs mixed_fp8=True)."""
         B = mel.shape[0]
         enc = out if out is not None else torch.empty(B, self.dims.n_audio_ctx, self.dims.d_model,
                                                       dtype=act_dtype(self.dims), device=self.device)
@@ -155,6 +156,14 @@ class Whisper:
 
     def decode_step(self, state, tokens, logits=None):
         B = state.batch
+        if state.ffn_fp8:
+            if self.packed8 is None or state.enc is None:
+                raise ValueError("the fp8 MLP sites need mixed_fp8=True and a state over the encoder output")
+            ws, nb = self.workspace(B, L.WS_DECODE_ENC_FP8)
+            L.whisper_decode_step_enc_fp8(self.dims, self.packed, self.packed8, B, state.cap, tokens, state.lengths,
+                                          state.kv_cache, state.kv_scales, state.enc, logits, state.argmax,
+                                          state.dev_error, ws, nb)
+            return state.argmax
         if state.enc is not None:
             ws, nb = self.workspace(B, L.WS_DECODE_ENC)
             L.whisper_decode_step_enc(self.dims, self.packed, B, state.cap, tokens, state.lengths, state.kv_cache,
@@ -175,10 +184,11 @@ class DecodeState:
     """Caller-owned decode state: fp8 self-KV cache, scales, lengths, and the
     cross-attention source: cross K/V (bf16, or fp8 codes in cross_format
     with per-(layer, K|V) scales from quantize_cross_kv), or the encoder
-    output itself (enc, [B, 1500, d] bf16: decode_step_enc)."""
+    output itself (enc, [B, 1500, d] bf16: decode_step_enc). ffn_fp8: the
+    decoder MLP as mixed_fp8 sites (decode_step_enc_fp8; needs enc)."""
 
     def __init__(self, dims, batch, cap, cross_kv, kv_scales, lengths, device="cuda", cross_codes=None,
-                 cross_scales=None, cross_format=L.WHISPER_FP8_E4M3, enc=None):
+                 cross_scales=None, cross_format=L.WHISPER_FP8_E4M3, enc=None, ffn_fp8=False):
         self.batch, self.cap = batch, cap
         self.kv_cache = torch.zeros(dims.n_dec_layers, 2, batch, dims.n_heads, cap, 64, dtype=torch.uint8,
                                     device=device)
@@ -186,6 +196,7 @@ class DecodeState:
         self.lengths = lengths.to(device=device, dtype=torch.int32).contiguous().clone()
         self.cross_kv = cross_kv
         self.enc = enc
+        self.ffn_fp8 = ffn_fp8
         self.cross_codes, self.cross_scales = cross_codes, cross_scales
         self.cross_format = cross_format
         self.argmax = torch.zeros(batch, dtype=torch.int32, device=device)

@@ -194,11 +194,16 @@ def test_fp8_encoder_entry_validation():
     """Host checks of the mixed_fp8 entry points (no launch happens)."""
     v3 = CONFIGS["v3_decode"].with_(n_enc_layers=32)
     tiny = CONFIGS["tiny_f32"]
-    # packed size: per layer 3 d^2 + 2 d f bytes of codes (256-aligned), then 8 scales per layer
+    # packed size: per encoder layer 3 d^2 + 2 d f bytes of codes (256-aligned),
+    # then 8 scales per encoder layer; per decoder layer the MLP's two weights
+    # as codes and its first bias as fp32, then 2 scales per decoder layer
     d, f = 1280, 5120
-    per = [(3 * d * d + 255) // 256 * 256, (f * d + 255) // 256 * 256, (d * f + 255) // 256 * 256]
-    assert L.whisper_packed_weights_fp8_size(v3) == 32 * sum(per) + (32 * 8 * 4 + 255) // 256 * 256
-    assert L.whisper_packed_weights_fp8_size(CONFIGS["v3_decode"]) == 0  # no encoder
+    al = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    enc = 32 * (al(3 * d * d) + al(f * d) + al(d * f)) + al(32 * 8 * 4)
+    dec = 32 * (al(f * d) + al(d * f) + al(f * 4)) + al(32 * 2 * 4)
+    assert L.whisper_packed_weights_fp8_size(v3) == enc + dec
+    # no encoder layers: the scale block keeps one layer's slot
+    assert L.whisper_packed_weights_fp8_size(CONFIGS["v3_decode"]) == al(8 * 4) + dec
     ws = L.whisper_workspace_size(v3, 2, L.WS_ENCODE_FP8)
     assert ws > L.whisper_workspace_size(v3, 2, L.WS_ENCODE)
     with pytest.raises(L.WhisperError) as e:  # fp32 model

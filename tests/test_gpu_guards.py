@@ -45,12 +45,12 @@ def intact(whole, fill, lead=True):
 def decoder():
     dims = CONFIGS["v3_decode"].with_(n_dec_layers=2)
     W = gen_weights(DEV, dims)
-    m = Whisper(dims, list(W.values()))
+    m = Whisper(dims, list(W.values()), mixed_fp8=True)
     del W
     return dims, m
 
 
-@pytest.mark.parametrize("kind", ["step", "step_enc", "prefill_enc", "step_xq"])
+@pytest.mark.parametrize("kind", ["step", "step_enc", "prefill_enc", "step_xq", "step_enc_fp8"])
 def test_decode_poisoned_workspace_and_canaries(decoder, kind):
     dims, m = decoder
     B, cap, P = 37, 64, 3
@@ -65,7 +65,8 @@ def test_decode_poisoned_workspace_and_canaries(decoder, kind):
     sc = torch.full((Ly, 2), 0.02, device=DEV)
     toks = gen_tokens(DEV, dims.cfg_id, P, B, V)
     rows = B * P if kind == "prefill_enc" else B
-    which = L.WS_DECODE_ENC if kind in ("step_enc", "prefill_enc") else L.WS_DECODE
+    which = {"step_enc": L.WS_DECODE_ENC, "prefill_enc": L.WS_DECODE_ENC,
+             "step_enc_fp8": L.WS_DECODE_ENC_FP8}.get(kind, L.WS_DECODE)
     nbytes = L.whisper_workspace_size(dims, rows, which)
 
     def run(byte):
@@ -89,6 +90,9 @@ def test_decode_poisoned_workspace_and_canaries(decoder, kind):
                 elif kind == "step_enc":
                     L.whisper_decode_step_enc(dims, m.packed, B, cap, toks[t], lengths, kv, sc, enc, lg, am, err, ws,
                                               nbytes)
+                elif kind == "step_enc_fp8":
+                    L.whisper_decode_step_enc_fp8(dims, m.packed, m.packed8, B, cap, toks[t], lengths, kv, sc, enc,
+                                                  lg, am, err, ws, nbytes)
                 else:
                     L.whisper_decode_step_xq(dims, m.packed, B, cap, toks[t], lengths, kv, sc, xq[0], xq[1], lg, am,
                                              err, ws, nbytes)

@@ -33,7 +33,7 @@ def _gpu():
 
 def model_for(dims, ln_random=False, fp8_encoder=False):
     W = gen_weights(DEV, dims, ln_random=ln_random)
-    m = Whisper(dims, list(W.values()), fp8_encoder=fp8_encoder)
+    m = Whisper(dims, list(W.values()), mixed_fp8=fp8_encoder)
     torch.cuda.synchronize()
     return m, W
 
@@ -262,7 +262,7 @@ def report(tag, st):
         f"excluded {st['tied']}")
 
 
-def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
+def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=(), mixed_fp8=False):
     """Run `ops` (("step", tokens [B]) or ("prefill", tokens [B, P]), device
     int32) on the GPU and on the oracle, comparing after each.
 
@@ -272,11 +272,18 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
     into the GPU's appends for `rows` (see tests/decode_check.py); extra_rows
     are batch rows left to the kernel's own codes, whose codec is checked.
     independent=True: no forcing; the oracle also runs a copy of its cache
-    with its quantised K/V rounded to bf16, which sets the logits bar."""
+    with its quantised K/V rounded to bf16, which sets the logits bar.
+    mixed_fp8: the decoder MLP runs as fp8 sites on both sides (the state
+    was made with ffn_fp8=True); the oracle's copy also rounds those sites'
+    inputs to bf16, and in both modes the logits bar is max(TOL, twice that
+    run's distance) and its K/V widen the code band (check_kv_against_oracle)."""
     W, H, cross, cache, sc = oracle["W"], oracle["H"], oracle["cross"], oracle["cache"], oracle["sc"]
     Lyr, B, d = len(cross), state.batch, H * 64
+    moved = independent or mixed_fp8  # the oracle also runs a perturbed copy
     cache_n = [[{b: cache[l][kv][b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)] \
-        if independent else None
+        if moved else None
+    kv_tf = O.bf16_round if independent else None
+    act_tf = O.bf16_round if mixed_fp8 else None
     lengths = state.lengths.cpu().numpy().copy()
     p_max = max(1 if k == "step" else t.shape[1] for k, t in ops)
     st = new_stats()
@@ -286,16 +293,17 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
             P = 1 if kind == "step" else tok.shape[1]
             th = tok.cpu().numpy()
             if kind == "step":
-                lg_ref, tr = O.decode_step(W, H, th, lengths, cache, sc, cross, rows=rows)
+                lg_ref, tr = O.decode_step(W, H, th, lengths, cache, sc, cross, rows=rows, mixed_fp8=mixed_fp8)
                 trs = [tr]
-                if independent:
-                    lg_n, _ = O.decode_step(W, H, th, lengths, cache_n, sc, cross, rows=rows,
-                                            kv_transform=O.bf16_round)
+                if moved:
+                    lg_n, tr_n = O.decode_step(W, H, th, lengths, cache_n, sc, cross, rows=rows, kv_transform=kv_tf,
+                                               mixed_fp8=mixed_fp8, act_transform=act_tf)
+                    trs_n = [tr_n]
             else:
-                lg_ref, trs = O.decode_prefill(W, H, th, lengths, cache, sc, cross, rows=rows)
-                if independent:
-                    lg_n, _ = O.decode_prefill(W, H, th, lengths, cache_n, sc, cross, rows=rows,
-                                               kv_transform=O.bf16_round)
+                lg_ref, trs = O.decode_prefill(W, H, th, lengths, cache, sc, cross, rows=rows, mixed_fp8=mixed_fp8)
+                if moved:
+                    lg_n, trs_n = O.decode_prefill(W, H, th, lengths, cache_n, sc, cross, rows=rows,
+                                                   kv_transform=kv_tf, mixed_fp8=mixed_fp8, act_transform=act_tf)
             if not independent:
                 trace.set_force({b * P + p: trs[p]["codes"][:, :, b] for b in rows for p in range(P)}, B * P)
             if kind == "step":
@@ -309,7 +317,7 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
             slots = {b: state.kv_cache[:, :, b, :, int(lengths[b]):int(lengths[b]) + P, :].cpu().numpy()
                      for b in list(rows) + list(extra_rows)}
             where = f"{tag} {kind} {st['ops']}"
-            if independent:
+            if moved:
                 for b in rows:
                     sens = rel_err(lg_n[b], lg_ref[b])
                     st["sens"] = max(st["sens"], sens)
@@ -331,7 +339,9 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
                             else:
                                 assert np.array_equal(got, tr["codes"][l, kv, b]), f"{w}: forced codes not in the cache"
                                 nd, e = check_kv_against_oracle(kv_g[l, kv, b * P + p], tr["kv"][l, kv, b],
-                                                                tr["codes"][l, kv, b], sc[l, kv], w, layer=l)
+                                                                tr["codes"][l, kv, b], sc[l, kv], w, layer=l,
+                                                                kv_moved=trs_n[p]["kv"][l, kv, b] if mixed_fp8
+                                                                else None)
                                 st["flips"] += nd
                                 st["codes"] += got.size
                                 st["kv_err"] = max(st["kv_err"], e)
@@ -345,12 +355,13 @@ def drive(m, state, oracle, ops, rows, tag, independent, extra_rows=()):
             st["ops"] += 1
     assert int(state.dev_error[0].item()) == 0
     assert np.array_equal(state.lengths.cpu().numpy(), lengths)
-    report(tag + (" (independent caches)" if independent else " (oracle codes forced)"), st)
+    report(tag + (" (independent caches)" if independent else " (oracle codes forced)")
+           + (", fp8 MLP" if mixed_fp8 else ""), st)
     return st
 
 
 def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale=None, cross_fmt="e4m3",
-                    lengths0=None, modes=("forced",), from_enc=False):
+                    lengths0=None, modes=("forced",), from_enc=False, mixed_fp8=False):
     """Teacher-forced decode on the GPU from a prefilled fp8 cache against the
     oracle on `rows`, in each of `modes` ("forced", "independent"; each from
     the same initial state). lengths0: prefill lengths [B] (default
@@ -358,9 +369,12 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale
     are fp8 codes in cross_fmt ("e4m3" or "e5m2") with that scale for every
     (layer, K|V), on both sides (the GPU quantises its bf16 projections, the
     oracle its own fp64 ones). from_enc: the GPU attends over the encoder
-    output itself (whisper_decode_step_enc) instead of projected K/V."""
+    output itself (whisper_decode_step_enc) instead of projected K/V.
+    mixed_fp8: from_enc with the decoder MLP as fp8 sites
+    (whisper_decode_step_enc_fp8) against the oracle's mixed_fp8 step."""
     H, d, Lyr, T = dims.n_heads, dims.d_model, dims.n_dec_layers, dims.n_audio_ctx
-    m, W = model_for(dims, ln_random=True)
+    from_enc = from_enc or mixed_fp8
+    m, W = model_for(dims, ln_random=True, fp8_encoder=mixed_fp8)
     dt = act_dtype(dims)
     enc = gen_normal(DEV, (B, T, d), dims.cfg_id, 5, bf16=dims.act == "bf16").to(dt)
     ckv = m.cross_kv(enc)
@@ -389,14 +403,14 @@ def run_decode_case(dims, B, cap, prefill_max, steps, rows, tag, cross_fp8_scale
             state = DecodeState(dims, B, cap, None, scales, lengths0, cross_codes=xcodes, cross_scales=xsc,
                                 cross_format=fmt)
         elif from_enc:
-            state = DecodeState(dims, B, cap, None, scales, lengths0, enc=enc)
+            state = DecodeState(dims, B, cap, None, scales, lengths0, enc=enc, ffn_fp8=mixed_fp8)
         else:
             state = DecodeState(dims, B, cap, ckv, scales, lengths0)
         cache = prefill_both(state, dims, B, prefill_max, rows, sc) if prefill_max else \
             [[{b: np.zeros((H, cap, 64), np.uint8) for b in rows} for kv in range(2)] for l in range(Lyr)]
         oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc, n_vocab=dims.n_vocab)
         drive(m, state, oracle, [("step", tokens[t]) for t in range(steps)], rows, tag, mode == "independent",
-              extra_rows=extra if mode == "forced" else ())
+              extra_rows=extra if mode == "forced" else (), mixed_fp8=mixed_fp8)
         del state
         torch.cuda.empty_cache()
 
@@ -452,6 +466,30 @@ def test_decode_from_encoder_output_full_and_ragged_batch():
     dims4 = dims.with_(n_dec_layers=4)
     say("decode from the encoder output, large-v3 shape, 4 layers, B=37, 2 steps")
     run_decode_case(dims4, 37, 672, 448, 2, [0, 36], "v3x4 enc B=37", from_enc=True)
+
+
+def test_decode_mixed_fp8_mlp_large_v3_shape():
+    """The decoder MLP as mixed_fp8 sites (whisper_decode_step_enc_fp8: fc1
+    and fc2 in E4M3, per-tensor weight scales, one activation scale per
+    token) against the oracle's mixed_fp8 step, which quantises its own fp64
+    activations; 4 layers at batch 64 (forced and independent caches) and at
+    a ragged batch of 37."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode, fp8 MLP sites, large-v3 shape, 4 layers, B=64, cap 672, prefill U[1,448], 3 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0)), 5, 33})
+    run_decode_case(dims, 64, 672, 448, 3, rows, "v3x4 fp8 mlp", modes=("forced", "independent"), mixed_fp8=True)
+    say("decode, fp8 MLP sites, large-v3 shape, 4 layers, B=37, 2 steps")
+    run_decode_case(dims, 37, 672, 448, 2, [0, 36], "v3x4 fp8 mlp B=37", mixed_fp8=True)
+
+
+def test_decode_mixed_fp8_mlp_large_v3_full():
+    """The same through all 32 decoder layers at batch 64."""
+    dims = CONFIGS["v3_decode"]
+    say("decode, fp8 MLP sites, large-v3, 32 layers, B=64, 2 steps")
+    lengths0 = gen_prefill_lengths("cpu", dims.cfg_id, 64, 448).numpy()
+    rows = sorted({int(np.argmin(lengths0)), int(np.argmax(lengths0))})
+    run_decode_case(dims, 64, 672, 448, 2, rows, "v3x32 fp8 mlp", mixed_fp8=True)
 
 
 def test_decode_turbo_shape_batch90_empty_cache():

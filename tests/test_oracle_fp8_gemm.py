@@ -111,3 +111,41 @@ def test_bf16_round_matches_torch_and_keeps_grid_values():
     g = O.e4m3_value(np.arange(127))  # every e4m3 value is a bf16 value
     assert np.array_equal(O.bf16_round(g), g)
 
+
+
+def test_fp8_linear_rows_per_row_scales_match_torch_quantiser():
+    """The decoder FFN site: each row quantised with its own amax scale
+    (fl32(amax) / 448), the weight with its tensor's, against torch's
+    float8_e4m3fn conversion of fl32(v * fl32(1/s)); rows are independent."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 96)) * np.array([0.01, 1.0, 30.0, 0.5, 2.0, 200.0])[:, None]
+    w, b = rng.standard_normal((40, 96)) * 0.05, rng.standard_normal(40)
+
+    def tq(a, s):
+        y = torch.from_numpy(np.asarray(a, np.float32)) * torch.tensor(np.float32(1.0) / np.float32(s))
+        return y.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    sw = O.e4m3_scale_from_amax(w)
+    got = O.fp8_linear_rows(x, w, b)
+    for r in range(x.shape[0]):
+        sx = np.float32(np.float32(np.abs(x[r]).max()) / np.float32(448.0))
+        ref = (tq(x[r], sx) @ tq(w, sw).T) * (float(sx) * float(sw)) + b
+        assert np.allclose(got[r], ref, rtol=1e-13, atol=1e-13), r
+    part = O.fp8_linear_rows(x, w, b, rows=[1, 4])
+    assert np.array_equal(part[[1, 4]], got[[1, 4]]) and not part[[0, 2, 3, 5]].any()
+
+
+def test_decode_step_mixed_fp8_ffn_site():
+    """decode_step with the decoder FFN in fp8: off is the plain step; on, the
+    logits move by the fp8 rounding (some per cent), and rows are
+    independent (a subset gives exactly those rows)."""
+    from tests.test_oracle_layers import _fp8_setup
+    W, H, L, ctx, cross, toks, scales, dh = _fp8_setup()
+    B = toks.shape[1]
+    c0 = np.zeros((L, 2, B, H, ctx, dh), np.uint8)
+    lg, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c0.copy(), scales, cross)
+    lg8, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c0.copy(), scales, cross, mixed_fp8=True)
+    lg8r, _ = O.decode_step(W, H, toks[0], np.zeros(B, int), c0.copy(), scales, cross, rows=[1], mixed_fp8=True)
+    rel = np.abs(lg8 - lg).max() / np.abs(lg).max()
+    assert 0 < rel < 0.15
+    assert np.array_equal(lg8r[1], lg8[1])
