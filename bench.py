@@ -40,8 +40,8 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring the MFMA and HBM ceilings")
     ap.add_argument("--no-long-form", action="store_true",
                     help="skip the 45-minute long-form leg (turbo shape, batch 90; reported apart from value)")
-    ap.add_argument("--no-fp8-encoder", action="store_true",
-                    help="skip the extra step with the mixed_fp8 encoder sites (E4M3 QKV and FFN GEMMs)")
+    ap.add_argument("--no-fp8-encoder", "--no-mixed-fp8", action="store_true", dest="no_fp8_encoder",
+                    help="skip the extra step with the mixed_fp8 sites (encoder QKV and FFN, decoder FFN in E4M3)")
     ap.add_argument("--no-fp8-cross", action="store_true",
                     help="skip the extra steps through explicit cross-attention K/V (bf16, fp8 e4m3, fp8 e5m2; "
                          "reported apart from value)")
@@ -256,7 +256,7 @@ def main():
         if peaks is not None:
             k = fp8e["encoder_ffn1_gemm_fp8"]
             k["peak_measured_bf16"] = peaks["mfma_bf16_tflops"]
-        result["fp8_encoder"] = fp8e
+        result["mixed_fp8"] = fp8e
     for fmt, leg in fp8x.items():
         if peaks is not None:
             xc = leg["cross_attention"]
@@ -420,10 +420,11 @@ def measured_peaks(L, torch):
 
 
 def fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np):
-    """One more full step with the encoder's mixed_fp8 sites (query, key,
-    value, fc1, fc2 as E4M3 GEMMs with per-tensor weight and per-chunk
-    activation amax scales), the rest unchanged. Reported apart from `value`:
-    the configured workload is bf16."""
+    """One more full step with the mixed_fp8 preset's sites in E4M3: the
+    encoder's query, key, value, fc1, fc2 (per-tensor weight and per-chunk
+    activation amax scales) and the decoder MLP's fc1, fc2 (per-tensor weight
+    and per-token activation scales), the rest unchanged. Reported apart from
+    `value`: the configured workload is bf16."""
     def step(ev=None):
         if ev: ev[0].record()
         model.logmel(audio, out=mel)
@@ -434,13 +435,17 @@ def fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, di
             model.decode_step(state, tokens[t], logits)
         if ev: ev[2].record()
 
-    step()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    t0 = time.perf_counter()
-    step(ev)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    state.ffn_fp8 = True
+    try:
+        step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t0 = time.perf_counter()
+        step(ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        state.ffn_fp8 = False
     assert int(state.dev_error[0].item()) == 0
     # the fc1 site (E4M3 GEMM + bias + GELU) with the event hook, in one more encoder pass
     n = 32
@@ -459,8 +464,8 @@ def fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, di
     M, d, F = B * dims.n_audio_ctx, dims.d_model, dims.d_ffn
     fl = 2.0 * M * d * F
     tf = fl / (ms * 1e-3) / 1e12
-    log(f"fp8 encoder step: {wall * 1e3:.1f} ms, encode {ev[0].elapsed_time(ev[1]):.1f} ms, "
-        f"fc1 fp8 GEMM {ms * 1e3:.0f} us ({tf:.0f} TFLOP/s)")
+    log(f"mixed_fp8 step: {wall * 1e3:.1f} ms, encode {ev[0].elapsed_time(ev[1]):.1f} ms, decode "
+        f"{ev[1].elapsed_time(ev[2]):.1f} ms, encoder fc1 fp8 GEMM {ms * 1e3:.0f} us ({tf:.0f} TFLOP/s)")
     return {"ms_per_step": round(wall * 1e3, 3), "rtfx": round(B * AUDIO_S / wall, 2),
             "stage_ms": {"logmel_encode": round(ev[0].elapsed_time(ev[1]), 3),
                          "decode": round(ev[1].elapsed_time(ev[2]), 3)},
@@ -469,7 +474,8 @@ def fp8_encoder_step(model, audio, mel, enc, state, tokens, logits, lengths0, di
                                       "unit": "TFLOP/s", "frac": round(tf / FP8_PEAK_TFLOPS, 4),
                                       "avg_launch_us": round(ms * 1e3, 1), "launches": n_rec,
                                       "shape": f"[{M},{d}]x[{d},{F}] E4M3 + scales + bias + GELU"},
-            "note": "mixed_fp8 preset sites in E4M3 (encoder query/key/value, fc1, fc2); not the configured workload"}
+            "note": "mixed_fp8 preset sites in E4M3 (encoder query/key/value, fc1, fc2; decoder fc1, fc2); "
+                    "not the configured workload"}
 
 
 def cross_kv_step(model, audio, mel, enc, ckv, state, tokens, logits, lengths0, dims, B, TD, L, torch, np,

@@ -506,6 +506,35 @@ whisper_status whisper_decode_linear(int mode, int M, int N, int K, float* x, co
                                      uint8_t* kv_cache, const float* kv_scales, const int32_t* lengths, int kv_cap,
                                      int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
+/* One decoder MLP sublayer with the mixed_fp8 sites (the showcase page's
+ * precision.py card: decoder FFN in fp8 E4M3), as whisper_decode_step_enc_fp8
+ * runs it (kernel-level call for tests and measurement):
+ *   a   = bf16(LN(x))                     LN as in whisper_decode_linear
+ *   h   = bf16(gelu(site(a, w1) + b1))    (the hidden rows, bf16)
+ *   x  += site(h, w2) + b2
+ * where site(a, w) = e4m3(a / s_a) . e4m3(w / s_w)^T * s_a * s_w with one
+ * activation scale per row, s_a = fl32(amax |a_row|) / 448 (1 for a zero
+ * row), and a per-tensor weight scale s_w = fl32(amax |w|) / 448; codes are
+ * e4m3_rne_saturate(fl32(v * fl32(1 / s))), products exact, fp32
+ * accumulation. x: [M, d] fp32 row-major, read and written. gamma, beta,
+ * b2: [d] fp32; w1 [f, d], b1 [f], w2 [d, f] fp32 logical weights, which
+ * each call quantises into ws (whisper_decode_mlp_fp8_workspace_size bytes,
+ * 0 for invalid sizes). hidden: optional [M, f] bf16 output, the GELU rows
+ * as stored (the second site's input). hidden_amax: optional [M] fp32
+ * output, amax |h_row| (the second site's s_a is hidden_amax / 448).
+ * Sizes: 1 <= M <= 4096, d % 80 == 0, d <= 2048, f % 80 == 0, f % 1024 == 0.
+ * Errors: SHAPE, INVALID_ARG (NULL), ALIGN, WORKSPACE, HIP; nothing is
+ * launched unless all checks pass. */
+size_t whisper_decode_mlp_fp8_workspace_size(int M, int d, int f);
+/* Host evaluation (no GPU) of the rounding the second site applies to its
+ * bf16 input in registers: y[i] = the value of e4m3_rne_saturate(x[i]) for
+ * finite x[i] (the code is not formed; host and device run the same fp32
+ * arithmetic). x, y: n host floats. Errors: INVALID_ARG (NULL with n > 0). */
+whisper_status whisper_e4m3_round_host(const float* x, float* y, size_t n);
+whisper_status whisper_decode_mlp_fp8(int M, int d, int f, float* x, const float* gamma, const float* beta,
+                                      const float* w1, const float* b1, const float* w2, const float* b2,
+                                      void* hidden, float* hidden_amax, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ K/V append debug hooks
  * For parity tests of the fp8 KV append (quantise on write, Endpoints post,
  * "Inference Stack"). While armed, every whisper_decode_step,

@@ -33,7 +33,8 @@ EXPORTS = [
     "whisper_logmel_chunked",
     "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
     "whisper_debug_kv_disarm", "whisper_decode_step_noalloc", "whisper_decode_step_enc", "whisper_decode_prefill_enc",
-    "whisper_decode_step_enc_fp8",
+    "whisper_decode_step_enc_fp8", "whisper_decode_mlp_fp8_workspace_size", "whisper_decode_mlp_fp8",
+    "whisper_e4m3_round_host",
 ]
 
 DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
@@ -112,6 +113,9 @@ _SIG = {
     "whisper_peak_read": (I, [P, Z, I, P, P]),
     "whisper_decode_linear_workspace_size": (Z, [I, I, I, I]),
     "whisper_decode_linear": (I, [I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, P, P, Z, P]),
+    "whisper_decode_mlp_fp8_workspace_size": (Z, [I, I, I]),
+    "whisper_decode_mlp_fp8": (I, [I, I, I, P, P, P, P, P, P, P, P, P, P, Z, P]),
+    "whisper_e4m3_round_host": (I, [P, P, Z]),
     "whisper_debug_kv_arm": (I, [P, P, Z]),
     "whisper_debug_kv_disarm": (None, []),
     "whisper_profile_arm": (I, [I, P, P, I]),
@@ -356,6 +360,25 @@ def whisper_decode_linear(mode, M, N, K, x, a, w, bias, gamma, beta, y, kv_cache
     _check(lib().whisper_decode_linear(mode, M, N, K, _p(x), _p(a), _p(w), _p(bias), _p(gamma), _p(beta), _p(y),
                                        _p(kv_cache), _p(kv_scales), _p(lengths), kv_cap, _p(dev_error), _p(ws),
                                        ws_bytes, _stream(stream)))
+
+
+def whisper_decode_mlp_fp8_workspace_size(M, d, f):
+    return lib().whisper_decode_mlp_fp8_workspace_size(M, d, f)
+
+
+def whisper_decode_mlp_fp8(M, d, f, x, gamma, beta, w1, b1, w2, b2, hidden=None, hidden_amax=None, ws=None,
+                           ws_bytes=0, stream=None):
+    _check(lib().whisper_decode_mlp_fp8(M, d, f, _p(x), _p(gamma), _p(beta), _p(w1), _p(b1), _p(w2), _p(b2),
+                                        _p(hidden), _p(hidden_amax), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_e4m3_round_host(x):
+    """x: a C-contiguous float32 numpy array; returns the rounded values."""
+    import numpy as np
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    _check(lib().whisper_e4m3_round_host(x.ctypes.data, y.ctypes.data, x.size))
+    return y
 
 
 def whisper_debug_kv_arm(kv_pre, kv_force, n_elems):

@@ -228,7 +228,8 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
 // workspace.
 constexpr int XE_CU = 256;  // compute units the frame sequence is shared over
 // With the decoder MLP as mixed_fp8 sites (fp8): the quantised LN(x) rows
-// [M][d] bf16, their scales [M], and per layer the hidden rows' amax [L][M].
+// [M][d] bf16, their scales [M], and the hidden rows' 16-column block maxima
+// [M][f / 16] (rewritten by each layer's up-projection).
 struct DecEncWS { DecWS base; size_t qp, upart, ml, u, aq = 0, srow = 0, amx8 = 0, total; XePlan plan; };
 DecEncWS dec_ws_enc(const whisper_dims* d, int M, bool fp8 = false) {
   DecEncWS W;
@@ -245,7 +246,7 @@ DecEncWS dec_ws_enc(const whisper_dims* d, int M, bool fp8 = false) {
   if (fp8) {
     W.aq = take((size_t)M * d->d_model * 2);
     W.srow = take((size_t)M * 4);
-    W.amx8 = take((size_t)d->n_dec_layers * M * 4);
+    W.amx8 = take((size_t)M * (d->d_ffn / 16) * 4);
   }
   W.total = off;
   return W;
@@ -452,7 +453,6 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
                       d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
   const Packed8 P8 = packed8 ? layout8(d) : Packed8{};
-  if (packed8) WH_TRY(launch_fill_f32(at<float>(ws, XW->amx8), 0.f, (size_t)L * B, s));  // the rows' amax start at 0
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
                   u16_t* out, float* out_f32, int layer, bool split = false, int a_group = 0) {
     DecGemmParams g{};
@@ -523,17 +523,18 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
       // input rows in registers, split-K + residual
       u16_t* AQ = at<u16_t>(ws, XW->aq);
       float* SROW = at<float>(ws, XW->srow);
-      uint32_t* AMX = at<uint32_t>(ws, XW->amx8) + (size_t)l * B;
+      float* AMX = at<float>(ws, XW->amx8);
       const float* dsc = at<float>(packed8, P8.dscales) + 2 * l;
       WH_TRY(launch_ln_quant_rows(X, at<float>(packed, Lw.ln3g), at<float>(packed, Lw.ln3b), B, D, AQ, SROW, s));
       DecGemmParams g1{};
       g1.M = B; g1.N = F; g1.K = D; g1.A = AQ; g1.lda = D; g1.X = X; g1.out = HF;
       g1.W8 = at<uint8_t>(packed8, P8.dw1[l]); g1.w_scale8 = dsc; g1.row_scale = SROW; g1.amax_out = AMX;
+      g1.amax_nblk = F / 16;
       g1.bias = at<float>(packed8, P8.db1[l]);
       WH_TRY(launch_gemm_dec_fp8(DEPI_GELU, g1, s));
       DecGemmParams g2{};
       g2.M = B; g2.N = D; g2.K = F; g2.A = HF; g2.lda = F; g2.X = X;
-      g2.W8 = at<uint8_t>(packed8, P8.dw2[l]); g2.w_scale8 = dsc + 1; g2.aq_amax = AMX;
+      g2.W8 = at<uint8_t>(packed8, P8.dw2[l]); g2.w_scale8 = dsc + 1; g2.aq_part = AMX; g2.amax_nblk = F / 16;
       g2.bias = at<float>(packed, Lw.b2);
       g2.ks = DEC_KSPLIT; g2.part = at<float>(ws, W.part); g2.cnt = CNT;
       WH_TRY(launch_gemm_dec_fp8(DEPI_RESID, g2, s));
@@ -1331,6 +1332,95 @@ whisper_status whisper_decode_linear(int mode, int M, int N, int K, float* x, co
   static const DecEpi epis[] = {DEPI_STORE, DEPI_GELU, DEPI_F32, DEPI_QKV, DEPI_RESID, DEPI_RESID};
   WH_TRY(launch_gemm_dec(ln ? PRO_X : PRO_A, epis[mode], g, mb, cb, s));
   if (!ln) WH_TRY(launch_x_tiles(XT, x, M, N, 0, s));
+  return WHISPER_OK;
+}
+
+// Workspace of whisper_decode_mlp_fp8: the two weights' codes in fragment
+// order and their scales, amax partials, x in 16-row tiles, the quantised
+// LN(x) rows and their scales, the hidden rows (when the caller takes none),
+// the hidden rows' 16-column block maxima, split-K partials and tile
+// counters.
+struct DecMlp8WS { size_t w1, w2, sc, part_amax, xt, aq, srow, hf, amx, part, cnt, n_cnt, total; };
+DecMlp8WS decmlp8_ws(int M, int D, int F) {
+  DecMlp8WS W{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = al256(off + bytes); return o; };
+  const size_t Mp = (size_t)((M + 15) & ~15), F16 = (size_t)((F + 15) & ~15), D16 = (size_t)((D + 15) & ~15);
+  W.w1 = take(F16 * D);
+  W.w2 = take(D16 * F);
+  W.sc = take(2 * 4);
+  W.part_amax = take(1024 * 4);
+  W.xt = take(Mp * D * 4);
+  W.aq = take((size_t)M * D * 2);
+  W.srow = take((size_t)M * 4);
+  W.hf = take((size_t)M * F * 2);
+  W.amx = take((size_t)M * (F / 16) * 4);
+  const size_t tiles = (size_t)((D + DEC_SPLIT_COLS - 1) / DEC_SPLIT_COLS) * ((M + 15) / 16);
+  W.part = take(tiles * DEC_KSPLIT * (DEC_SPLIT_COLS / 16) * 64 * 16);
+  W.cnt = take(tiles * 4);
+  W.n_cnt = tiles;
+  W.total = off;
+  return W;
+}
+bool decmlp8_shape_ok(int M, int D, int F) {
+  return M > 0 && M <= 4096 && D > 0 && F > 0 && D % DEC_SPLIT_COLS == 0 && D <= 2048 && F % DEC_SPLIT_COLS == 0 &&
+         F % (DEC_KSPLIT * 8 * 32) == 0;
+}
+
+whisper_status whisper_e4m3_round_host(const float* x, float* y, size_t n) {
+  if (n && (!x || !y)) return fail(WHISPER_ERR_INVALID_ARG, "e4m3_round_host: NULL buffer");
+  e4m3_round_host(x, y, n);
+  return WHISPER_OK;
+}
+
+size_t whisper_decode_mlp_fp8_workspace_size(int M, int d, int f) {
+  return decmlp8_shape_ok(M, d, f) ? decmlp8_ws(M, d, f).total : 0;
+}
+
+whisper_status whisper_decode_mlp_fp8(int M, int d, int f, float* x, const float* gamma, const float* beta,
+                                      const float* w1, const float* b1, const float* w2, const float* b2,
+                                      void* hidden, float* hidden_amax, void* ws, size_t ws_bytes, void* stream) {
+  if (!decmlp8_shape_ok(M, d, f))
+    return fail(WHISPER_ERR_SHAPE, "decode_mlp_fp8: need 1 <= M <= 4096, d % 80 == 0, d <= 2048, f % 80 == 0, "
+                                   "f % 1024 == 0");
+  WH_CHECK(check_ptrs({x, w1, w2}, "decode_mlp_fp8"));
+  WH_CHECK(check_ptrs4({gamma, beta, b1, b2}, "decode_mlp_fp8"));
+  if (hidden && !aligned16(hidden)) return fail(WHISPER_ERR_ALIGN, "decode_mlp_fp8: hidden not 16-byte aligned");
+  if (hidden_amax && ((uintptr_t)hidden_amax & 3u))
+    return fail(WHISPER_ERR_ALIGN, "decode_mlp_fp8: hidden_amax not 4-byte aligned");
+  const DecMlp8WS W = decmlp8_ws(M, d, f);
+  WH_CHECK(check_ws(ws, ws_bytes, W.total, "decode_mlp_fp8"));
+  (void)hipGetLastError();
+  const hipStream_t s = S(stream);
+  const size_t D = d, F = f;
+  float* sc = at<float>(ws, W.sc);
+  float* pa = at<float>(ws, W.part_amax);
+  const size_t blocks = (F * D + 255) / 256;
+  const int np = (int)std::min<size_t>(blocks, 1024);
+  WH_TRY(launch_amax(ACT_F32, FP8_E4M3, w1, F * D, pa, np, sc, s));
+  WH_TRY(launch_pack_dec_weight_fp8(w1, f, d, sc, at<void>(ws, W.w1), s));
+  WH_TRY(launch_amax(ACT_F32, FP8_E4M3, w2, D * F, pa, np, sc + 1, s));
+  WH_TRY(launch_pack_dec_weight_fp8(w2, d, f, sc + 1, at<void>(ws, W.w2), s));
+  float* XT = at<float>(ws, W.xt);
+  WH_TRY(launch_x_tiles(x, XT, M, d, 1, s));
+  float* AMX = at<float>(ws, W.amx);
+  WH_TRY(launch_fill_f32(at<float>(ws, W.cnt), 0.f, W.n_cnt, s));  // the tile counters start at 0
+  u16_t* AQ = at<u16_t>(ws, W.aq);
+  float* SROW = at<float>(ws, W.srow);
+  u16_t* HF = hidden ? (u16_t*)hidden : at<u16_t>(ws, W.hf);
+  WH_TRY(launch_ln_quant_rows(XT, gamma, beta, M, d, AQ, SROW, s));
+  DecGemmParams g1{};
+  g1.M = M; g1.N = f; g1.K = d; g1.A = AQ; g1.lda = d; g1.X = XT; g1.out = HF;
+  g1.W8 = at<uint8_t>(ws, W.w1); g1.w_scale8 = sc; g1.row_scale = SROW; g1.amax_out = AMX; g1.amax_nblk = f / 16;
+  g1.bias = b1;
+  WH_TRY(launch_gemm_dec_fp8(DEPI_GELU, g1, s));
+  DecGemmParams g2{};
+  g2.M = M; g2.N = d; g2.K = f; g2.A = HF; g2.lda = f; g2.X = XT;
+  g2.W8 = at<uint8_t>(ws, W.w2); g2.w_scale8 = sc + 1; g2.aq_part = AMX; g2.amax_nblk = f / 16; g2.bias = b2;
+  g2.ks = DEC_KSPLIT; g2.part = at<float>(ws, W.part); g2.cnt = at<int32_t>(ws, W.cnt);
+  WH_TRY(launch_gemm_dec_fp8(DEPI_RESID, g2, s));
+  WH_TRY(launch_x_tiles(XT, x, M, d, 0, s));
+  if (hidden_amax) WH_TRY(launch_rows_max(AMX, M, f / 16, hidden_amax, s));
   return WHISPER_OK;
 }
 

@@ -62,6 +62,23 @@ __device__ __forceinline__ void amax_step(float& v, int& idx) {
   }
 }
 
+// The value of the E4M3 code of y, e4m3_decode(e4m3_encode(y)), computed
+// without forming the code, for finite y: normal magnitudes (>= 2^-6) keep 3
+// mantissa bits (round to nearest even on the fp32 bits) and saturate at
+// 448; smaller ones round to a multiple of 2^-9 (the subnormal step) by
+// adding and removing 1.5 * 2^14, whose fp32 spacing is 2^-9; the sign is
+// kept. Branch-free, so a wave whose lanes straddle the two ranges runs one
+// path. Host and device evaluate it identically (plain fp32 adds).
+__host__ __device__ __forceinline__ float e4m3_round(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sgn = u & 0x80000000u, a = u & 0x7fffffffu;
+  const uint32_t rn = (a + 0x7ffffu + ((a >> 20) & 1u)) & 0xfff00000u;
+  const float vn = fminf(__builtin_bit_cast(float, rn), 448.0f);
+  const float vs = (__builtin_bit_cast(float, a) + 24576.0f) - 24576.0f;
+  const float v = a < 0x3c800000u ? vs : vn;
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) | sgn);
+}
+
 // Eight E4M3 codes -> eight bf16 (exact: every E4M3 value is a bf16 value).
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(const uint2 w) {
   float a[4], b[4];
@@ -70,11 +87,8 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(const uint2 w) {
   auto pk = [](float lo, float hi) { return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u); };
   return make_uint4(pk(a[0], a[1]), pk(a[2], a[3]), pk(b[0], b[1]), pk(b[2], b[3]));
 }
-// The E4M3 scale of an amax (fp32 bits): fl32(amax) / 448, 1 for 0.
-__device__ __forceinline__ float e4m3_scale_of(uint32_t amax_bits) {
-  const float a = __uint_as_float(amax_bits);
-  return a > 0.f ? a / 448.0f : 1.0f;
-}
+// The E4M3 scale of an amax: fl32(amax) / 448, 1 for 0.
+__device__ __forceinline__ float e4m3_scale_of(float a) { return a > 0.f ? a / 448.0f : 1.0f; }
 
 template <int PRO, int EPI, int MB, int CB, int NS, bool F8 = false>
 __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p) {
@@ -115,14 +129,53 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     if constexpr (F8) wfr8[cb] = p.W8 + fo;
     else wfr[cb] = p.W + fo;
   }
-  // F8 with aq_amax: the reciprocal scale of this lane's A row (in-register quantisation)
+  // F8 with aq_part: each A row's amax is the largest of its amax_nblk
+  // partials (the 16-column block maxima the producing GEMM stored), reduced
+  // once per workgroup into s_aq; then the reciprocal scale of this lane's A
+  // row (in-register quantisation) and the epilogue's row scales. Run by
+  // every wave once the first weight loads are in flight (it ends in a
+  // barrier), so its loads overlap theirs.
+  __shared__ float s_aq[MR];
   float aq_inv[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    aq_inv[mb] = 1.f;
-    if constexpr (F8)
-      if (p.aq_amax) aq_inv[mb] = 1.0f / e4m3_scale_of(p.aq_amax[min(m0 + mb * 16 + (lane & 15), M - 1)]);
-  }
+  for (int mb = 0; mb < MB; ++mb) aq_inv[mb] = 1.f;
+  float e_rs[4] = {1.f, 1.f, 1.f, 1.f};  // F8: row scale x weight scale
+  auto aq_reduce = [&]() {
+    if constexpr (F8) {
+      if (p.aq_part) {
+        constexpr int TPR = DG_WAVES * 64 / MR;  // threads per row, a power of two <= 64
+        static_assert(TPR * MR == DG_WAVES * 64 && TPR <= 64 && (TPR & (TPR - 1)) == 0, "row split");
+        const int row = tid / TPR, j0 = tid - row * TPR;
+        // float4 loads (amax_nblk % 4 == 0), four in flight per thread
+        const float4* pr = (const float4*)(p.aq_part + (long)min(m0 + row, M - 1) * p.amax_nblk);
+        const int n4 = p.amax_nblk >> 2;
+        float a = 0.f;
+        for (int base = 0; base < n4; base += 4 * TPR) {
+          float4 v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = base + j0 + i * TPR;
+            v[i] = j < n4 ? pr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a = fmaxf(a, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+        }
+        for (int o = TPR / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+        if (j0 == 0) s_aq[row] = a;
+        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) aq_inv[mb] = 1.0f / e4m3_scale_of(s_aq[mb * 16 + (lane & 15)]);
+      }
+      if (wave < MB * CB) {
+        const int emb_ = wave / CB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ml = emb_ * 16 + (lane >> 4) * 4 + r;
+          e_rs[r] = (p.aq_part ? e4m3_scale_of(s_aq[ml]) : p.row_scale[min(m0 + ml, M - 1)]) * p.w_scale8[0];
+        }
+      }
+    }
+  };
   long arow[MB];
   // grouped A: this column tile's rows of A start at its group's offset
   const long agoff = p.a_group > 0 ? (long)(n0 / p.a_group) * p.a_group_stride : 0;
@@ -149,7 +202,6 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   const int emb = ewave ? wave / CB : 0, ecb = ewave ? wave - (wave / CB) * CB : 0;
   const int en = n0 + ecb * 16 + (lane & 15);  // this lane's output column
   float e_bias = 0.f, e_c1 = 0.f, e_x[4] = {0.f, 0.f, 0.f, 0.f}, e_inv[2] = {0.f, 0.f};
-  float e_rs[4] = {1.f, 1.f, 1.f, 1.f};  // F8: row scale x weight scale
   int e_pos[4] = {0, 0, 0, 0};
   if (ewave) {
     const int n = min(en, N - 1);
@@ -160,7 +212,6 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
       const int m = min(m0 + emb * 16 + (lane >> 4) * 4 + r, M - 1);
       if constexpr (RES) e_x[r] = p.X[dec_x_index(m, n, N)];
       if constexpr (QKV) e_pos[r] = p.lengths[m / RPB] + m % RPB;
-      if constexpr (F8) e_rs[r] = (p.aq_amax ? e4m3_scale_of(p.aq_amax[m]) : p.row_scale[m]) * p.w_scale8[0];
     }
     if constexpr (QKV) {
       e_inv[0] = 1.0f / p.kv_scales[p.kv_layer * 2];
@@ -228,12 +279,12 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
       } else {                                                                                 \
         uint4 a8_ = av[XIN ? 0 : SL][mb];                                                       \
         if constexpr (F8) {                                                                    \
-          if (p.aq_amax) { /* quantise the bf16 row in registers: the code values, as bf16 */  \
+          if (p.aq_part) { /* quantise the bf16 row in registers: the code values, as bf16 */  \
             const uint32_t q_[4] = {a8_.x, a8_.y, a8_.z, a8_.w};                                \
             uint32_t o_[4];                                                                    \
             _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
-              const float lo_ = e4m3_decode(e4m3_encode(__uint_as_float(q_[i] << 16) * aq_inv[mb]));        \
-              const float hi_ = e4m3_decode(e4m3_encode(__uint_as_float(q_[i] & 0xffff0000u) * aq_inv[mb])); \
+              const float lo_ = e4m3_round(__uint_as_float(q_[i] << 16) * aq_inv[mb]);          \
+              const float hi_ = e4m3_round(__uint_as_float(q_[i] & 0xffff0000u) * aq_inv[mb]);  \
               o_[i] = (__float_as_uint(lo_) >> 16) | (__float_as_uint(hi_) & 0xffff0000u);     \
             }                                                                                  \
             a8_ = make_uint4(o_[0], o_[1], o_[2], o_[3]);                                      \
@@ -255,10 +306,12 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
     for (int t = 0; t < NS + DG_DEPTH; ++t) {
       if (t < NS) DG_ISSUE(t, t % NSLOT)
       __builtin_amdgcn_sched_barrier(0);
+      if (t == DG_DEPTH) aq_reduce();
       if (t >= DG_DEPTH) DG_COMPUTE(t - DG_DEPTH, (t - DG_DEPTH) % NSLOT)
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
+    aq_reduce();
     for (int j = 0; j < nsteps; ++j) {
       DG_ISSUE(j, 0)
       DG_COMPUTE(j, 0)
@@ -352,7 +405,9 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
   if constexpr (F8 && EPI == DEPI_GELU) {
     if (p.amax_out) {
       // the next site's scale: each row's max |stored bf16 value| over the
-      // block's 16 columns (DPP permutes as in the argmax), joined by atomic max
+      // block's 16 columns (DPP permutes as in the argmax), stored as that
+      // row's partial for this 16-column block
+      const int blk = (n0 >> 4) + ecb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float a = en < N ? fabsf(__uint_as_float((uint32_t)f2bf(gelu_erf(vr[r])) << 16)) : 0.f;
@@ -361,7 +416,7 @@ __global__ __launch_bounds__(DG_WAVES * 64) void gemm_dec_kernel(DecGemmParams p
         a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x141, 0xF, 0xF, true)));
         a = fmaxf(a, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), 0x140, 0xF, 0xF, true)));
         const int m = m0 + emb * 16 + (lane >> 4) * 4 + r;
-        if ((lane & 15) == 0 && m < M) atomicMax(p.amax_out + m, __float_as_uint(a));
+        if ((lane & 15) == 0 && m < M && blk < p.amax_nblk) p.amax_out[(long)m * p.amax_nblk + blk] = a;
       }
     }
   }
@@ -445,14 +500,17 @@ template <int PRO, int EPI, int MB, int CB, bool F8 = false>
 static hipError_t dec_launch_t(const DecGemmParams& p, hipStream_t s) {
   const int S = p.K / 32 / (p.ks > 1 ? p.ks : 1);  // k-steps of one workgroup's slice
   if (S == DG_WAVES * 5) return dec_launch_ns<PRO, EPI, MB, CB, 5, F8>(p, s);
-  if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20, F8>(p, s);
+  if constexpr (!F8)  // (the fp8 kernel's 20-step form spills; the model's fp8 sites run 5 steps per wave)
+    if (S == DG_WAVES * 20) return dec_launch_ns<PRO, EPI, MB, CB, 20, F8>(p, s);
   return dec_launch_ns<PRO, EPI, MB, CB, 0, F8>(p, s);
 }
 
 hipError_t launch_gemm_dec_fp8(DecEpi epi, const DecGemmParams& p, hipStream_t s) {
   if (p.M <= 0 || p.M > 4096 || p.N <= 0 || p.K <= 0 || p.K % 32 || !p.W8 || !p.w_scale8 || !p.A)
     return hipErrorInvalidValue;
-  if (!p.row_scale == !p.aq_amax) return hipErrorInvalidValue;  // exactly one source of the row scale
+  if (!p.row_scale == !p.aq_part) return hipErrorInvalidValue;  // exactly one source of the row scale
+  if (p.aq_part && (p.amax_nblk <= 0 || p.amax_nblk % 4 || ((uintptr_t)p.aq_part & 15))) return hipErrorInvalidValue;
+  if (p.amax_out && (epi != DEPI_GELU || p.amax_nblk != p.N / 16)) return hipErrorInvalidValue;
   if (p.N % 80) return hipErrorInvalidValue;                     // 16 x 80 tiles
   if (epi == DEPI_GELU && p.ks <= 1) return dec_launch_t<PRO_A, DEPI_GELU, 1, 5, true>(p, s);
   if (epi == DEPI_RESID && p.ks > 1 && p.part && p.cnt && p.ks <= 16 && (p.K / 32) % (p.ks * DG_WAVES) == 0)
@@ -592,11 +650,13 @@ hipError_t launch_pack_dec_weight_fp8(const float* W, int N, int K, const float*
 }
 
 // The decoder MLP's fp8 input site: per row m of the fp32 residual stream X
-// (16-row tiles, dec_x_index), a = LayerNorm(x) (fp32 two-pass statistics,
-// biased variance, eps 1e-5), its scale s = fl32(amax |a|) / 448 (1 for an
-// all-zero row), and the values of the codes e4m3(fl32(a * fl32(1 / s))),
-// stored as bf16 (every E4M3 value is a bf16 value) in A [M, K]; s to
-// srow[m]. One workgroup of 256 threads per row, K <= 2048.
+// (16-row tiles, dec_x_index), a = bf16(LayerNorm(x)) (fp32 two-pass
+// statistics, biased variance, eps 1e-5; rounded to bf16 as every activation
+// of the step is, so the code decisions are taken on bf16 values), its scale
+// s = fl32(amax |a|) / 448 (1 for an all-zero row), and the values of the
+// codes e4m3(fl32(a * fl32(1 / s))), stored as bf16 (every E4M3 value is a
+// bf16 value) in A [M, K]; s to srow[m]. One workgroup of 256 threads per
+// row, K <= 2048.
 __global__ __launch_bounds__(256) void ln_quant_rows_kernel(const float* __restrict__ X, const float* __restrict__ g,
                                                             const float* __restrict__ b, int K, u16* __restrict__ A,
                                                             float* __restrict__ srow) {
@@ -631,7 +691,7 @@ __global__ __launch_bounds__(256) void ln_quant_rows_kernel(const float* __restr
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int k = tid + i * 256;
-    v[i] = k < K ? (v[i] - mu) * r * g[k] + b[k] : 0.f;
+    v[i] = k < K ? bf2f(f2bf((v[i] - mu) * r * g[k] + b[k])) : 0.f;
     amax = fmaxf(amax, fabsf(v[i]));
   }
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -647,6 +707,26 @@ __global__ __launch_bounds__(256) void ln_quant_rows_kernel(const float* __restr
     if (k < K) A[(long)m * K + k] = (u16)(__float_as_uint(e4m3_decode(e4m3_encode(v[i] * inv))) >> 16);
   }
   if (tid == 0) srow[m] = sc;
+}
+
+// The in-register rounding of the fp8 decode GEMM, evaluated on the host.
+void e4m3_round_host(const float* x, float* y, size_t n) {
+  for (size_t i = 0; i < n; ++i) y[i] = e4m3_round(x[i]);
+}
+
+// out[m] = max over j of part[m][j], j < nblk (one wave per row).
+__global__ __launch_bounds__(64) void rows_max_kernel(const float* part, int nblk, float* out) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  float a = 0.f;
+  for (int j = lane; j < nblk; j += 64) a = fmaxf(a, part[(long)m * nblk + j]);
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  if (lane == 0) out[m] = a;
+}
+
+hipError_t launch_rows_max(const float* part, int M, int nblk, float* out, hipStream_t s) {
+  if (M <= 0 || nblk <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_max_kernel, dim3(M), dim3(64), 0, s, part, nblk, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_ln_quant_rows(const float* X, const float* g, const float* b, int M, int K, void* A, float* srow,

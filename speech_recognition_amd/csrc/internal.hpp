@@ -93,12 +93,15 @@ struct DecGemmParams {
   // fp8 weights (launch_gemm_dec_fp8): W8 E4M3 codes [N, K] in fragment order
   // with the per-tensor scale w_scale8[0]; the products are the codes' values,
   // and the epilogue multiplies by (row scale) * w_scale8[0] before the bias.
-  // Row scale: row_scale[m] (A already holds code values), or, with aq_amax,
-  // fl32(amax) / 448 of aq_amax[m] (fp32 bits; 1 for 0), the A row being
-  // quantised in registers as e4m3(fl32(a * fl32(1 / s))). amax_out (DEPI_GELU,
-  // NULL: off): each row's max |stored bf16 output| joins amax_out[m] (fp32
-  // bits, atomic max; the caller zeroes it).
-  const uint8_t* W8; const float* w_scale8; const float* row_scale; const uint32_t* aq_amax; uint32_t* amax_out;
+  // Row scale: row_scale[m] (A already holds code values), or, with aq_part,
+  // fl32(amax) / 448 (1 for 0) where amax is the largest of the row's
+  // amax_nblk partials aq_part[m][0 .. amax_nblk) (amax_nblk % 4 == 0, aq_part
+  // 16-byte aligned), the A row being quantised
+  // in registers as e4m3(fl32(a * fl32(1 / s))). amax_out (DEPI_GELU, NULL:
+  // off; amax_nblk == N / 16): amax_out[m][j] = max |stored bf16 output| of
+  // row m over columns 16 j .. 16 j + 15, every entry of rows < M written.
+  const uint8_t* W8; const float* w_scale8; const float* row_scale; const float* aq_part; float* amax_out;
+  int amax_nblk;
   // DEPI_F32 (NULL: off): per row, the largest value of each 16-column block
   // and its column (lowest on ties; NaN never chosen), [M][ceil(N / 16)] as
   // (float bits, column); argmax_part reduces them
@@ -111,6 +114,8 @@ hipError_t launch_gemm_dec(DecPro pro, DecEpi epi, const DecGemmParams& p, int m
 // DEC_KSPLIT workgroups (down-projection).
 hipError_t launch_gemm_dec_fp8(DecEpi epi, const DecGemmParams& p, hipStream_t s);
 hipError_t launch_pack_dec_weight_fp8(const float* W, int N, int K, const float* scale, void* Wf, hipStream_t s);
+void e4m3_round_host(const float* x, float* y, size_t n);
+hipError_t launch_rows_max(const float* part, int M, int nblk, float* out, hipStream_t s);
 hipError_t launch_ln_quant_rows(const float* X, const float* g, const float* b, int M, int K, void* A, float* srow,
                                 hipStream_t s);
 hipError_t launch_fold_ln(const float* W, const float* gamma, const float* beta, const float* bias, int N, int K,

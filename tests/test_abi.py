@@ -230,6 +230,25 @@ def test_fp8_encoder_entry_validation():
     assert e.value.status == 1
 
 
+def test_decode_mlp_fp8_validation():
+    """Host checks of whisper_decode_mlp_fp8 (no launch happens)."""
+    ws = L.whisper_decode_mlp_fp8_workspace_size(64, 1280, 5120)
+    # at least both weights' codes, x tiles, quantised rows and hidden rows
+    assert ws >= 2 * 1280 * 5120 + 64 * 1280 * 4 + 64 * 1280 * 2 + 64 * 5120 * 2
+    for bad in ((0, 1280, 5120), (4097, 1280, 5120), (64, 1000, 5120), (64, 2080, 5120), (64, 1280, 5000),
+                (64, 1280, 4080)):
+        assert L.whisper_decode_mlp_fp8_workspace_size(*bad) == 0, bad
+        with pytest.raises(L.WhisperError) as e:
+            L.whisper_decode_mlp_fp8(*bad, 16, 16, 16, 16, 16, 16, 16, ws=16, ws_bytes=1 << 40, stream=0)
+        assert e.value.status == 2, bad
+    with pytest.raises(L.WhisperError) as e:  # workspace too small
+        L.whisper_decode_mlp_fp8(64, 1280, 5120, 16, 16, 16, 16, 16, 16, 16, ws=16, ws_bytes=ws - 1, stream=0)
+    assert e.value.status == 5
+    with pytest.raises(L.WhisperError) as e:  # NULL weight
+        L.whisper_decode_mlp_fp8(64, 1280, 5120, 16, 16, 16, None, 16, 16, 16, ws=16, ws_bytes=ws, stream=0)
+    assert e.value.status == 1
+
+
 def test_decode_linear_validation():
     """Host checks of whisper_decode_linear (no launch happens): modes, shape
     rules of the split-K and QKV forms, workspace size."""
