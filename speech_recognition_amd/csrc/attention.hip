@@ -306,7 +306,8 @@ __device__ __forceinline__ float dot16_fp8(const uint4 c, const float* q) {
 // batch is straight-line code and all its loads are in flight at once), keeps
 // a private online softmax (running max, sum and 16 output dims), and the 256
 // private states are merged once at the end: block max, rescale, sum over
-// the 64 key groups through LDS. q goes straight from global to registers.
+// the 64 key groups (DPP within each 16-lane row, LDS across the 16 rows).
+// q goes straight from global to registers.
 constexpr int SELF_KB = 8;
 
 template <typename T, int FMT>
@@ -316,8 +317,8 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
                                                                const float* __restrict__ scales,
                                                                const int32_t* __restrict__ lengths, int len_add, int H,
                                                                int cap, T* __restrict__ out, int rows_per_b) {
-  __shared__ float red[4][64];
-  __shared__ float wmax[4], wsum[4];
+  __shared__ __attribute__((aligned(16))) float red[16][64];
+  __shared__ float rowmax[16], rsum[16];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bc = b / rows_per_b;  // cache batch row of query row b
   const int n = lengths ? max(0, min(lengths[bc] + len_add + b % rows_per_b, cap)) : cap;
@@ -378,32 +379,50 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
     }
     m = mn;
   }
-  // merge the private states: block max, rescale, sum over the 16 key groups of
-  // a wave with lane shuffles (lanes of equal part), then over the 4 waves in LDS
-  const float wm = wave_max(m);
-  if (lane == 0) wmax[wave] = wm;
-  __syncthreads();
-  const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+  // merge the private states. A 16-lane row holds key groups 4 r .. 4 r + 3
+  // of its wave, each in 4 parts: the row's max and the sums over its 4 key
+  // groups of equal part (scaled to that max) come from DPP row rotations
+  // (VALU, no LDS traffic); the 16 rows of the block then meet in LDS once:
+  // each output dim rescales the rows' sums to the block max as it adds them.
+  const int rrow = wave * 4 + (lane >> 4);  // this lane's row, 0..15
+  float rm = m;
+  rm = fmaxf(rm, dpp_f<0x128>(rm));  // row_ror:8
+  rm = fmaxf(rm, dpp_f<0x124>(rm));  // row_ror:4
+  rm = fmaxf(rm, dpp_f<0x122>(rm));  // row_ror:2
+  rm = fmaxf(rm, dpp_f<0x121>(rm));  // row_ror:1
+  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - rm);
   float ls = l * f;
+  ls += dpp_f<0x128>(ls);
+  ls += dpp_f<0x124>(ls);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] *= f;
-#pragma unroll
-  for (int o = 4; o < 64; o <<= 1) {
-    ls += __shfl_xor(ls, o, 64);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += __shfl_xor(acc[i], o, 64);
+  for (int i = 0; i < 16; ++i) {
+    float a = acc[i] * f;
+    a += dpp_f<0x128>(a);
+    a += dpp_f<0x124>(a);
+    acc[i] = a;
   }
-  if (lane < 4) {
+  if ((lane & 12) == 0) {  // lanes 0..3 of the row: its 4 parts
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave][lane * 16 + i] = acc[i];
-    if (lane == 0) wsum[wave] = ls;
+    for (int i = 0; i < 16; i += 4)
+      *(float4*)&red[rrow][part * 16 + i] = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+    if (part == 0) {
+      rsum[rrow] = ls;
+      rowmax[rrow] = rm;
+    }
   }
   __syncthreads();
   if (tid < 64) {
-    const float sum = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-    const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-    const float v = (n > 0) ? s * sv / sum : 0.f;
+    float mx = rowmax[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, rowmax[r]);
+    float sum = 0.f, sacc = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = rowmax[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rowmax[r] - mx);
+      sum = fmaf(rsum[r], w, sum);
+      sacc = fmaf(red[r][tid], w, sacc);
+    }
+    const float v = (n > 0) ? sacc * sv / sum : 0.f;
     out[(long)b * H * 64 + h * 64 + tid] = Act<T>::st(v);
   }
 }
