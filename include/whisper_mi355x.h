@@ -310,13 +310,14 @@ whisper_status whisper_decode_step_enc(const whisper_dims* dims, const void* pac
  * showcase page's precision.py card: in the mixed_fp8 preset the decoder FFN
  * runs in fp8 E4M3, weights and activations). packed8: whisper_pack_weights_fp8
  * output, which holds E4M3 codes of each decoder layer's fc1 and fc2 with one
- * amax scale per tensor (fl32(amax) / 448). Per layer: a = LayerNorm(x) of
- * each row in fp32 is quantised with its own scale (fl32(amax |a|) / 448,
- * code = e4m3(fl32(a * fl32(1 / s)))); fc1 sums code values times weight code
- * values in fp32, times the two scales, + bias, GELU, stored bf16; each
- * hidden row is quantised the same way with its own scale; fc2 likewise,
- * + bias, added to the residual stream. The rest of the step is
- * whisper_decode_step_enc. Requires d_model and d_ffn multiples of 256 (and of
+ * amax scale per tensor (fl32(amax) / 448). Per layer: each row's
+ * a = bf16(LayerNorm(x)) (fp32 statistics; rounded to bf16 like every
+ * activation of the step) is quantised with its own scale (fl32(amax |a|) /
+ * 448, code = e4m3(fl32(a * fl32(1 / s)))); fc1 sums code values times weight
+ * code values in fp32, times the two scales, + bias, GELU, stored bf16; each
+ * stored hidden row is quantised the same way with its own scale; fc2
+ * likewise, + bias, added to the residual stream (whisper_decode_mlp_fp8 runs
+ * this sublayer alone). The rest of the step is whisper_decode_step_enc. Requires d_model and d_ffn multiples of 256 (and of
  * 80), d_ffn a multiple of 1024. ws: whisper_workspace_size(dims, batch,
  * WHISPER_WS_DECODE_ENC_FP8) bytes. Errors as whisper_decode_step_enc. */
 whisper_status whisper_decode_step_enc_fp8(const whisper_dims* dims, const void* packed, const void* packed8,
