@@ -460,8 +460,8 @@ hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, cons
 // kg, kg + KPP, ...; per batch of CROSS_NB passes it loads the K and V rows
 // together (addresses clamped to the last frame, so the batch is
 // straight-line code), keeps a private online softmax, and the private states
-// are merged once at the end and written as the final output: no partials, no
-// combine pass.
+// are merged once at the end (DPP within each 16-lane row, LDS across the 16
+// rows) and written as the final output: no partials, no combine pass.
 constexpr int CROSS_NB = 8;
 
 // 16 bytes of a K or V row as fp32 (no address-taken register arrays)
@@ -485,8 +485,8 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
   constexpr int TPK = 64 / EPT;         // lanes per key row
   constexpr int KPP = 256 / TPK;        // keys per pass
   typedef typename std::conditional<sizeof(T) == 2, uint4, float4>::type V16;
-  __shared__ float red[4][64];
-  __shared__ float wmax[4], wsum[4];
+  __shared__ __attribute__((aligned(16))) float red[16][64];
+  __shared__ float rowmax[16], rsum[16];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = tid % TPK, kg = tid / TPK;
   float qreg[EPT];
@@ -544,32 +544,48 @@ __global__ __launch_bounds__(256) void attn_decode_cross_kernel(const T* __restr
     }
     m = mn;
   }
-  // merge: block max, rescale, sum over the key groups of a wave with lane
-  // shuffles (lanes of equal part), then over the 4 waves in LDS
-  const float wm = wave_max(m);
-  if (lane == 0) wmax[wave] = wm;
-  __syncthreads();
-  const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+  // merge: each 16-lane row (16 / TPK key groups of TPK parts) takes its max
+  // and its sums over key groups of equal part with DPP row rotations; the 16
+  // rows of the block meet in LDS once, each output dim rescaling the rows'
+  // sums to the block max as it adds them
+  static_assert(TPK == 8 || TPK == 16, "a 16-lane row holds whole key groups");
+  const int rrow = wave * 4 + (lane >> 4);
+  float rm = m;
+  rm = fmaxf(rm, dpp_f<0x128>(rm));  // row_ror:8
+  rm = fmaxf(rm, dpp_f<0x124>(rm));  // row_ror:4
+  rm = fmaxf(rm, dpp_f<0x122>(rm));  // row_ror:2
+  rm = fmaxf(rm, dpp_f<0x121>(rm));  // row_ror:1
+  const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - rm);
   float ls = l * f;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] *= f;
+  if constexpr (TPK == 8) {
+    ls += dpp_f<0x128>(ls);
 #pragma unroll
-  for (int o = TPK; o < 64; o <<= 1) {
-    ls += __shfl_xor(ls, o, 64);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+    for (int e = 0; e < EPT; ++e) acc[e] += dpp_f<0x128>(acc[e]);
   }
-  if (lane < TPK) {
+  if ((lane & 15) < TPK) {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) red[wave][lane * EPT + e] = acc[e];
-    if (lane == 0) wsum[wave] = ls;
+    for (int e = 0; e < EPT; e += 4)
+      *(float4*)&red[rrow][part * EPT + e] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    if ((lane & 15) == 0) {
+      rsum[rrow] = ls;
+      rowmax[rrow] = rm;
+    }
   }
   __syncthreads();
   if (tid < 64) {
-    const float sum = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-    const float s = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-    out[((long)b * H + h) * 64 + tid] = Act<T>::st(T_ > 0 ? s / sum : 0.f);
+    float mx = rowmax[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, rowmax[r]);
+    float sum = 0.f, sacc = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float w = rowmax[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rowmax[r] - mx);
+      sum = fmaf(rsum[r], w, sum);
+      sacc = fmaf(red[r][tid], w, sacc);
+    }
+    out[((long)b * H + h) * 64 + tid] = Act<T>::st(T_ > 0 ? sacc / sum : 0.f);
   }
 }
 
