@@ -141,7 +141,7 @@ int weight_count(const whisper_dims* d) {
 }
 
 // ------------------------------------------------------------------ workspace layout
-struct EncWS { size_t x0, g1, x, a, dlt, qkv, att, hf, codes, part, ascale, total; };
+struct EncWS { size_t x0, g1, x, a, dlt, qkv, att, hf, codes, part, ascale, rowmax, total; };
 EncWS enc_ws(const whisper_dims* d, int B, bool fp8 = false) {
   EncWS W{};
   const size_t e = esz(d->act), D = d->d_model, T = d->n_audio_ctx, rows = (size_t)B * T;
@@ -157,10 +157,12 @@ EncWS enc_ws(const whisper_dims* d, int B, bool fp8 = false) {
   const size_t hf_b = std::max(rows * d->d_ffn * e, (size_t)B * (N_FRAMES + 2) * D * e);
   W.hf = take(hf_b);
   W.g1 = W.hf;   // conv1 output lives in the MLP buffer before the first block
-  if (fp8) {     // E4M3 codes of the activation entering an fp8 site, per-chunk amax partials and scales
+  if (fp8) {     // E4M3 codes of the activation entering an fp8 site, per-chunk amax partials and scales,
+                 // and the LayerNorm outputs' row maxima
     W.codes = take(rows * std::max((size_t)d->d_ffn, D));
     W.part = take((size_t)B * 64 * 4);
     W.ascale = take((size_t)B * 4);
+    W.rowmax = take(rows * 4);
   }
   W.total = off;
   return W;
@@ -332,12 +334,15 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
     const EncL& L = P.enc[l];
     const float* g1 = at<float>(packed, L.ln1g);
     const float* b1 = at<float>(packed, L.ln1b);
+    // fp8 sites: the LayerNorm also leaves each row's max |output|, from which
+    // the quantiser takes the chunk's scale without a pass of its own
+    float* ROWMAX = packed8 ? at<float>(ws, W.rowmax) : nullptr;
     if (have_delta)
-      WH_TRY(launch_layernorm(t, false, Dl, X, g1, b1, 1e-5f, M, D, A, X, s));
+      WH_TRY(launch_layernorm(t, false, Dl, X, g1, b1, 1e-5f, M, D, A, X, s, ROWMAX));
     else if (x_ready)
-      WH_TRY(launch_layernorm(t, true, X, nullptr, g1, b1, 1e-5f, M, D, A, nullptr, s));
+      WH_TRY(launch_layernorm(t, true, X, nullptr, g1, b1, 1e-5f, M, D, A, nullptr, s, ROWMAX));
     else
-      WH_TRY(launch_layernorm(t, false, h_in, nullptr, g1, b1, 1e-5f, M, D, A, X, s));
+      WH_TRY(launch_layernorm(t, false, h_in, nullptr, g1, b1, 1e-5f, M, D, A, X, s, ROWMAX));
     x_ready = true;
     const float* sc8 = packed8 ? at<float>(packed8, P8.scales) + 8 * l : nullptr;
     uint8_t* CODES = packed8 ? at<uint8_t>(ws, W.codes) : nullptr;
@@ -353,7 +358,7 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
     if (packed8) {
       const uint8_t* q8 = at<uint8_t>(packed8, P8.qkv[l]);
       const float* bq = at<float>(packed, L.bqkv);
-      WH_TRY(launch_chunk_quant_fp8(A, M, D, T, PART, ASC, CODES, s));
+      WH_TRY(launch_chunk_quant_rows_fp8(A, M, D, T, ROWMAX, ASC, CODES, s));
       for (int r = 0; r < 3; ++r)  // query, key, value: one weight scale each
         WH_TRY(fp8_site(EPI_STORE, q8 + (size_t)r * D * D, sc8 + r, D, D, bq + r * D, (u16_t*)QKV + r * D, 3 * D));
     } else {
@@ -366,10 +371,11 @@ whisper_status run_enc_layers(const whisper_dims* d, const void* packed, const P
     WH_TRY(launch_gemm(t, EPI_STORE, gp(ATT, D, at<void>(packed, L.wo), D, M, D, D, at<float>(packed, L.bo), Dl, D), s));
     {
       ProfScope ps(WHISPER_PROF_ENCODER_LAYERNORM, s);
-      WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s));
+      WH_TRY(launch_layernorm(t, false, Dl, X, at<float>(packed, L.ln2g), at<float>(packed, L.ln2b), 1e-5f, M, D, A, X, s,
+                              ROWMAX));
     }
     if (packed8) {
-      WH_TRY(launch_chunk_quant_fp8(A, M, D, T, PART, ASC, CODES, s));
+      WH_TRY(launch_chunk_quant_rows_fp8(A, M, D, T, ROWMAX, ASC, CODES, s));
       {
         ProfScope ps(WHISPER_PROF_ENCODER_FFN1, s);
         WH_TRY(fp8_site(EPI_GELU, at<uint8_t>(packed8, P8.w1[l]), sc8 + 3, F, D, at<float>(packed, L.b1), HF, F));

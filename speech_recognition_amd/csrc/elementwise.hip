@@ -42,7 +42,7 @@ template <> struct Vec4<float> {
 template <typename TH, typename T>
 __global__ __launch_bounds__(256) void layernorm_kernel(const TH* h, const float* res, const float* g,
                                                         const float* b, float eps, int M, int d, T* normed,
-                                                        float* total) {
+                                                        float* total, float* row_amax) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;
   const int nc = d >> 2;
@@ -71,6 +71,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TH* h, const float
       for (int k = 0; k < 4; ++k) { const float t = v[i][k] - mean; sq += t * t; }
   const float var = wave_sum(sq) / (float)d;
   const float rstd = 1.0f / sqrtf(var + eps);
+  float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = lane + i * 64;
@@ -81,24 +82,31 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const TH* h, const float
         float o[4] = {(v[i][0] - mean) * rstd * gg.x + bb.x, (v[i][1] - mean) * rstd * gg.y + bb.y,
                       (v[i][2] - mean) * rstd * gg.z + bb.z, (v[i][3] - mean) * rstd * gg.w + bb.w};
         Vec4<T>::st(normed + off + c * 4, o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(Act<T>::round(o[k])));  // as stored
       }
     }
+  }
+  if (row_amax) {
+    amax = wave_max(amax);
+    if (lane == 0) row_amax[row] = amax;
   }
 }
 
 hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* res, const float* g, const float* b,
-                            float eps, int M, int d, void* normed, float* total, hipStream_t s) {
+                            float eps, int M, int d, void* normed, float* total, hipStream_t s, float* row_amax) {
   if (M <= 0) return hipSuccess;
+  if (row_amax && !normed) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
   if (t == ACT_BF16 && !h_f32)
     hipLaunchKernelGGL((layernorm_kernel<u16, u16>), grid, dim3(256), 0, s, (const u16*)h, res, g, b, eps, M, d,
-                       (u16*)normed, total);
+                       (u16*)normed, total, row_amax);
   else if (t == ACT_BF16)
     hipLaunchKernelGGL((layernorm_kernel<float, u16>), grid, dim3(256), 0, s, (const float*)h, res, g, b, eps, M, d,
-                       (u16*)normed, total);
+                       (u16*)normed, total, row_amax);
   else
     hipLaunchKernelGGL((layernorm_kernel<float, float>), grid, dim3(256), 0, s, (const float*)h, res, g, b, eps, M,
-                       d, (float*)normed, total);
+                       d, (float*)normed, total, row_amax);
   return hipGetLastError();
 }
 
@@ -241,6 +249,51 @@ __global__ __launch_bounds__(256) void chunk_quant_kernel(const u16* __restrict_
     *(uint2*)(codes + begin + i * 8) = uint2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
                                              q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
   }
+}
+
+// The same quantisation of a bf16 activation whose rows' maxima |x| are
+// already known (row_amax[m], as the LayerNorm kernel leaves them): each
+// workgroup reduces its chunk's row maxima, so no amax pass over x is needed.
+__global__ __launch_bounds__(256) void chunk_quant_rows_kernel(const u16* __restrict__ x, int K, long rows,
+                                                               int rows_per_chunk, const float* __restrict__ row_amax,
+                                                               float* __restrict__ scales,
+                                                               uint8_t* __restrict__ codes) {
+  const int c = blockIdx.y;
+  const long r0 = (long)c * rows_per_chunk, r1 = min(r0 + rows_per_chunk, rows);
+  float m = 0.f;
+  for (long r = r0 + threadIdx.x; r < r1; r += 256) m = fmaxf(m, row_amax[r]);
+  m = wave_max(m);
+  __shared__ float sm[4];
+  __shared__ float s_inv;
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mx = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    const float sc = (mx > 0.f) ? mx / 448.0f : 1.0f;
+    s_inv = 1.0f / sc;
+    if (blockIdx.x == 0) scales[c] = sc;
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  const long begin = r0 * K, n8 = (r1 - r0) * K / 8;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)CQ_PARTS * 256) {
+    float v[8];
+    load8(x + begin + i * 8, v);
+    uint32_t q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = e4m3_encode(v[k] * inv);
+    *(uint2*)(codes + begin + i * 8) = uint2{q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24),
+                                             q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24)};
+  }
+}
+
+hipError_t launch_chunk_quant_rows_fp8(const void* x, long rows, int K, int rows_per_chunk, const float* row_amax,
+                                       float* scales, uint8_t* codes, hipStream_t s) {
+  if (rows <= 0 || K % 8 || rows_per_chunk <= 0 || !row_amax) return hipErrorInvalidValue;
+  const int n_chunks = (int)((rows + rows_per_chunk - 1) / rows_per_chunk);
+  hipLaunchKernelGGL(chunk_quant_rows_kernel, dim3(CQ_PARTS, n_chunks), dim3(256), 0, s, (const u16*)x, K, rows,
+                     rows_per_chunk, row_amax, scales, codes);
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_quant_fp8(const void* x, long rows, int K, int rows_per_chunk, float* partial,

@@ -145,8 +145,10 @@ hipError_t launch_absorb_combine(const void* upart, const float* ml, int M, int 
 // ------------------------------------------------------------------ LayerNorm
 // h is in the activation type (or fp32 when h_f32); residual and total are the
 // fp32 residual stream; normed is in the activation type.
+// row_amax (optional, needs normed): per row, max |normed| as stored
 hipError_t launch_layernorm(ActType t, bool h_f32, const void* h, const float* res, const float* g, const float* b,
-                            float eps, int M, int d, void* normed, float* total, hipStream_t s);
+                            float eps, int M, int d, void* normed, float* total, hipStream_t s,
+                            float* row_amax = nullptr);
 
 // ------------------------------------------------------------------ fp8 codec
 // fmt: FP8_E4M3 or FP8_E5M2 (common.hpp); the amax scale divides by that
@@ -159,6 +161,9 @@ hipError_t launch_fp8_dequantize(ActType t, int fmt, const uint8_t* codes, size_
                                  hipStream_t s);
 // bf16 x [rows, K] -> E4M3 codes with one amax scale per chunk of
 // rows_per_chunk rows; partial: 64 floats per chunk; scales: one per chunk.
+// launch_chunk_quant_fp8 for an activation whose rows' max |x| are known
+hipError_t launch_chunk_quant_rows_fp8(const void* x, long rows, int K, int rows_per_chunk, const float* row_amax,
+                                       float* scales, uint8_t* codes, hipStream_t s);
 hipError_t launch_chunk_quant_fp8(const void* x, long rows, int K, int rows_per_chunk, float* partial,
                                   float* scales, uint8_t* codes, hipStream_t s);
 
