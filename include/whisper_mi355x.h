@@ -82,7 +82,7 @@ typedef struct {
 enum { WHISPER_WS_LOGMEL = 0, WHISPER_WS_ENCODE = 1, WHISPER_WS_CROSS_KV = 2, WHISPER_WS_DECODE = 3,
        WHISPER_WS_ENCODE_FP8 = 4 /* whisper_encode_fp8 / whisper_encode_layers_fp8 */,
        WHISPER_WS_DECODE_ENC = 5 /* whisper_decode_step_enc / whisper_decode_prefill_enc, batch = query rows */,
-       WHISPER_WS_DECODE_ENC_FP8 = 6 /* whisper_decode_step_enc_fp8 */ };
+       WHISPER_WS_DECODE_ENC_FP8 = 6 /* whisper_decode_step_enc_fp8 / whisper_decode_prefill_enc_fp8 */ };
 
 /* ------------------------------------------------------------------ weights
  * Logical weights are fp32 device tensors in PyTorch layout, passed as an
@@ -299,7 +299,9 @@ whisper_status whisper_decode_prefill(const whisper_dims* dims, const void* pack
  * head computes softmax((W_k,h^T q_h) . E^T / 8) over the frames, u_h =
  * sum_t p_t E_t, and W_v,h u_h + b_v,h: the same attention, reading E once per
  * layer (half the bytes of K and V) and never forming K or V, so no
- * whisper_cross_kv pass is needed. ws: whisper_workspace_size(dims, batch *
+ * whisper_cross_kv pass is needed. The frames are shared among workgroups
+ * according to the number of activation rows, so a prefill here agrees with
+ * successive steps to rounding, not bit for bit. ws: whisper_workspace_size(dims, batch *
  * n_tokens, WHISPER_WS_DECODE_ENC) bytes. Errors as whisper_decode_prefill. */
 whisper_status whisper_decode_step_enc(const whisper_dims* dims, const void* packed, int batch, int kv_cap,
                                        const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
@@ -330,6 +332,16 @@ whisper_status whisper_decode_prefill_enc(const whisper_dims* dims, const void* 
                                           const float* kv_scales, const void* enc_out, float* logits,
                                           int32_t* argmax, int32_t* dev_error, void* ws, size_t ws_bytes,
                                           void* stream);
+/* whisper_decode_prefill_enc with the decoder MLP as mixed_fp8 sites, as
+ * whisper_decode_step_enc_fp8 (each of the batch * n_tokens activation rows
+ * takes its own activation scales): the computation of n_tokens successive
+ * whisper_decode_step_enc_fp8 calls. ws: whisper_workspace_size(dims,
+ * batch * n_tokens, WHISPER_WS_DECODE_ENC_FP8) bytes. */
+whisper_status whisper_decode_prefill_enc_fp8(const whisper_dims* dims, const void* packed, const void* packed8,
+                                              int batch, int n_tokens, int kv_cap, const int32_t* tokens,
+                                              int32_t* lengths, uint8_t* kv_cache, const float* kv_scales,
+                                              const void* enc_out, float* logits, int32_t* argmax,
+                                              int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
 /* Decoder step with fp8 cross-attention K/V (the fp8 cross-attention site of
  * the showcase page's precision presets, whose aggressive preset takes E5M2

@@ -34,7 +34,7 @@ EXPORTS = [
     "whisper_decode_linear_workspace_size", "whisper_decode_linear", "whisper_debug_kv_arm",
     "whisper_debug_kv_disarm", "whisper_decode_step_noalloc", "whisper_decode_step_enc", "whisper_decode_prefill_enc",
     "whisper_decode_step_enc_fp8", "whisper_decode_mlp_fp8_workspace_size", "whisper_decode_mlp_fp8",
-    "whisper_e4m3_round_host",
+    "whisper_e4m3_round_host", "whisper_decode_prefill_enc_fp8",
 ]
 
 DEC_LN_STORE, DEC_LN_GELU, DEC_LN_F32, DEC_LN_QKV, DEC_RESID, DEC_RESID_SPLITK = 0, 1, 2, 3, 4, 5
@@ -116,6 +116,7 @@ _SIG = {
     "whisper_decode_mlp_fp8_workspace_size": (Z, [I, I, I]),
     "whisper_decode_mlp_fp8": (I, [I, I, I, P, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_e4m3_round_host": (I, [P, P, Z]),
+    "whisper_decode_prefill_enc_fp8": (I, [P, P, P, I, I, I, P, P, P, P, P, P, P, P, P, Z, P]),
     "whisper_debug_kv_arm": (I, [P, P, Z]),
     "whisper_debug_kv_disarm": (None, []),
     "whisper_profile_arm": (I, [I, P, P, I]),
@@ -270,6 +271,14 @@ def whisper_decode_prefill_enc(dims, packed, batch, n_tokens, kv_cap, tokens, le
     _check(lib().whisper_decode_prefill_enc(dp, _p(packed), batch, n_tokens, kv_cap, _p(tokens), _p(lengths),
                                             _p(kv_cache), _p(kv_scales), _p(enc_out), _p(logits), _p(argmax),
                                             _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
+
+
+def whisper_decode_prefill_enc_fp8(dims, packed, packed8, batch, n_tokens, kv_cap, tokens, lengths, kv_cache,
+                                   kv_scales, enc_out, logits, argmax, dev_error, ws, ws_bytes, stream=None):
+    dd, dp = _dims_ptr(dims)
+    _check(lib().whisper_decode_prefill_enc_fp8(dp, _p(packed), _p(packed8), batch, n_tokens, kv_cap, _p(tokens),
+                                                _p(lengths), _p(kv_cache), _p(kv_scales), _p(enc_out), _p(logits),
+                                                _p(argmax), _p(dev_error), _p(ws), ws_bytes, _stream(stream)))
 
 
 def whisper_decode_prefill(dims, packed, batch, n_tokens, kv_cap, tokens, lengths, kv_cache, kv_scales, cross_kv,

@@ -1220,6 +1220,15 @@ whisper_status whisper_decode_prefill_enc(const whisper_dims* d, const void* pac
                       nullptr, enc_out, logits, argmax, dev_error, ws, ws_bytes, stream);
 }
 
+whisper_status whisper_decode_prefill_enc_fp8(const whisper_dims* d, const void* packed, const void* packed8, int B,
+                                              int n_tokens, int cap, const int32_t* tokens, int32_t* lengths,
+                                              uint8_t* kv_cache, const float* kv_scales, const void* enc_out,
+                                              float* logits, int32_t* argmax, int32_t* dev_error, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  return prefill_impl("decode_prefill_enc_fp8", d, packed, B, n_tokens, cap, tokens, lengths, kv_cache, kv_scales,
+                      nullptr, enc_out, logits, argmax, dev_error, ws, ws_bytes, stream, packed8);
+}
+
 whisper_status whisper_decode_step_xq(const whisper_dims* d, const void* packed, int B, int cap,
                                       const int32_t* tokens, int32_t* lengths, uint8_t* kv_cache,
                                       const float* kv_scales, const uint8_t* cross_codes, const float* cross_scales,

@@ -142,6 +142,14 @@ class Whisper:
         """tokens [B, P]: P prompt tokens per row in one pass (equal to P decode steps)."""
         B, n_tok = tokens.shape
         assert B == state.batch and state.cross_codes is None
+        if state.ffn_fp8:
+            if self.packed8 is None or state.enc is None:
+                raise ValueError("the fp8 MLP sites need mixed_fp8=True and a state over the encoder output")
+            ws, nb = self.workspace(B * n_tok, L.WS_DECODE_ENC_FP8)
+            L.whisper_decode_prefill_enc_fp8(self.dims, self.packed, self.packed8, B, n_tok, state.cap,
+                                             tokens.contiguous(), state.lengths, state.kv_cache, state.kv_scales,
+                                             state.enc, logits, state.argmax, state.dev_error, ws, nb)
+            return state.argmax
         if state.enc is not None:
             ws, nb = self.workspace(B * n_tok, L.WS_DECODE_ENC)
             L.whisper_decode_prefill_enc(self.dims, self.packed, B, n_tok, state.cap, tokens.contiguous(),

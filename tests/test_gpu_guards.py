@@ -50,7 +50,7 @@ def decoder():
     return dims, m
 
 
-@pytest.mark.parametrize("kind", ["step", "step_enc", "prefill_enc", "step_xq", "step_enc_fp8"])
+@pytest.mark.parametrize("kind", ["step", "step_enc", "prefill_enc", "step_xq", "step_enc_fp8", "prefill_enc_fp8"])
 def test_decode_poisoned_workspace_and_canaries(decoder, kind):
     dims, m = decoder
     B, cap, P = 37, 64, 3
@@ -64,9 +64,9 @@ def test_decode_poisoned_workspace_and_canaries(decoder, kind):
     pre[(pre & 0x7F) == 0x7F] = 0  # no NaN codes in the prefilled slots
     sc = torch.full((Ly, 2), 0.02, device=DEV)
     toks = gen_tokens(DEV, dims.cfg_id, P, B, V)
-    rows = B * P if kind == "prefill_enc" else B
+    rows = B * P if kind in ("prefill_enc", "prefill_enc_fp8") else B
     which = {"step_enc": L.WS_DECODE_ENC, "prefill_enc": L.WS_DECODE_ENC,
-             "step_enc_fp8": L.WS_DECODE_ENC_FP8}.get(kind, L.WS_DECODE)
+             "step_enc_fp8": L.WS_DECODE_ENC_FP8, "prefill_enc_fp8": L.WS_DECODE_ENC_FP8}.get(kind, L.WS_DECODE)
     nbytes = L.whisper_workspace_size(dims, rows, which)
 
     def run(byte):
@@ -82,6 +82,10 @@ def test_decode_poisoned_workspace_and_canaries(decoder, kind):
         if kind == "prefill_enc":
             L.whisper_decode_prefill_enc(dims, m.packed, B, P, cap, toks.t().contiguous(), lengths, kv, sc, enc, lg,
                                          am, err, ws, nbytes)
+            outs.append((lg.clone(), am.clone()))
+        elif kind == "prefill_enc_fp8":
+            L.whisper_decode_prefill_enc_fp8(dims, m.packed, m.packed8, B, P, cap, toks.t().contiguous(), lengths, kv,
+                                             sc, enc, lg, am, err, ws, nbytes)
             outs.append((lg.clone(), am.clone()))
         else:
             for t in range(2):

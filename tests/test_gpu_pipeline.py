@@ -703,6 +703,57 @@ def test_decode_prefill_equals_successive_steps_and_oracle():
               mode == "independent", extra_rows=[5] if mode == "forced" else ())
 
 
+@pytest.mark.parametrize("fp8_mlp", [False, True])
+def test_decode_prefill_from_encoder_output_against_oracle(fp8_mlp):
+    """The prefill over the encoder output (whisper_decode_prefill_enc, and
+    with the decoder MLP as mixed_fp8 sites whisper_decode_prefill_enc_fp8)
+    against the oracle's P steps on two rows, then one more step (forced
+    caches; bars as in drive). Beside it, P successive steps on the GPU: the
+    same lengths, and last-token logits within the same bar of the prefill's
+    (the cross-attention over the encoder output splits the frames by the
+    number of activation rows, so the two agree to rounding, and fp8 sites
+    turn rounding-level differences into code flips)."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=2)
+    B, P, cap, prefill_max = 24, 4, 96, 40
+    say(f"decode prefill from the encoder output{', fp8 MLP sites' if fp8_mlp else ''}: large-v3 shape 2 layers, "
+        f"B={B}, {P} prompt tokens")
+    m, W = model_for(dims, ln_random=True, fp8_encoder=fp8_mlp)
+    H, Lyr = dims.n_heads, dims.n_dec_layers
+    enc = gen_normal(DEV, (B, 1500, 1280), dims.cfg_id, 8, bf16=True).to(torch.bfloat16)
+    lengths0 = gen_prefill_lengths(DEV, dims.cfg_id, B, prefill_max)
+    sc = torch.full((Lyr, 2), 0.02)
+    toks = gen_tokens(DEV, dims.cfg_id, P + 1, B, dims.n_vocab)
+    prefill = torch.randint(0, 256, (Lyr, 2, B, H, cap, 64), dtype=torch.uint8,
+                            generator=torch.Generator().manual_seed(13)).to(DEV)
+    prefill[(prefill & 0x7F) == 0x7F] = 0
+    s1 = DecodeState(dims, B, cap, None, sc, lengths0, enc=enc, ffn_fp8=fp8_mlp)
+    s2 = DecodeState(dims, B, cap, None, sc, lengths0, enc=enc, ffn_fp8=fp8_mlp)
+    s1.kv_cache.copy_(prefill)
+    s2.kv_cache.copy_(prefill)
+    lg1 = torch.empty(B, dims.n_vocab, dtype=torch.float32, device=DEV)
+    lg2 = torch.empty_like(lg1)
+    m.decode_prefill(s1, toks[:P].t().contiguous(), lg1)
+    for t in range(P):
+        m.decode_step(s2, toks[t], lg2)
+    torch.cuda.synchronize()
+    assert int(s1.dev_error[0].item()) == 0 and int(s2.dev_error[0].item()) == 0
+    assert torch.equal(s1.lengths, lengths0.to(DEV) + P) and torch.equal(s1.lengths, s2.lengths)
+    pre_vs_steps = max(rel_err(host(lg1)[b], host(lg2)[b]) for b in range(B))
+    say(f"  prefill against {P} successive steps: last-token logits max rel diff {pre_vs_steps:.2e}")
+    rows = [0, B - 1]
+    Wh = host_weights(W, "decoder.")
+    cross_rows = {b: O.cross_kv(host(enc[b]), Wh, H, Lyr) for b in rows}
+    cross = [({b: cross_rows[b][l][0] for b in rows}, {b: cross_rows[b][l][1] for b in rows}) for l in range(Lyr)]
+    pre = prefill.cpu().numpy()
+    st = DecodeState(dims, B, cap, None, sc, lengths0, enc=enc, ffn_fp8=fp8_mlp)
+    st.kv_cache.copy_(prefill)
+    cache = [[{b: pre[l, kv, b].copy() for b in rows} for kv in range(2)] for l in range(Lyr)]
+    oracle = dict(W=Wh, H=H, cross=cross, cache=cache, sc=sc.numpy(), n_vocab=dims.n_vocab)
+    stats = drive(m, st, oracle, [("prefill", toks[:P].t().contiguous()), ("step", toks[P])], rows,
+                  "prefill enc" + (" fp8 mlp" if fp8_mlp else ""), False, extra_rows=[5], mixed_fp8=fp8_mlp)
+    assert pre_vs_steps < max(TOL, 2.0 * stats["sens"]), "prefill and successive steps differ beyond the fp8 bar"
+
+
 @pytest.mark.parametrize("cross_fp8", [False, True])
 def test_plan_batch_pass_fits_its_budget(cross_fp8):
     """A batch sized by whisper_plan_batch runs the whole pass (log-mel,
