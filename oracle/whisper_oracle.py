@@ -549,6 +549,8 @@ def _quantised_weight(w):
         return hit[3], hit[4]
     sw = e4m3_scale_from_amax(w)
     wv = e4m3_value(e4m3_quantize(w, sw))
+    for k in [k for k, v in _WEIGHT_CODES.items() if v[0]() is None]:  # arrays gone since
+        del _WEIGHT_CODES[k]
     try:
         ref = weakref.ref(w)
     except TypeError:  # an array that takes no weak reference is not kept
