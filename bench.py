@@ -89,7 +89,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by independent 30 s chunks with no exchange step)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
