@@ -213,6 +213,16 @@ def main():
     kernels = {}
     if not args.no_kernel_probes:
         kernels = kernel_probes(model, mel, enc, state, tokens, logits, lengths0, dims, B, TD, L, torch, np)
+        # decode attention of one layer as a whole (the cross-attention over the
+        # encoder output timed in the timed region, the self-attention over the
+        # fp8 cache by its probe; bytes at each measurement's own lengths)
+        sa = kernels["decode_self_attention_fp8"]
+        by = cross_bytes + sa["bytes_per_launch"]
+        us = cross_ms * 1e3 + sa["avg_launch_us"]
+        kernels["decode_attention_per_layer"] = {
+            "bound": "hbm", "achieved": round(by / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": round(by), "us": round(us, 2),
+            "parts": "attn_cross_enc_kernel (timed region) + attn_decode_self_kernel (probe)"}
 
     result = {
         "metric": "RTFx and decode tok/s at Whisper large-v3 shape, fp8 KV, batch 64",
