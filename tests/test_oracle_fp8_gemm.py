@@ -149,3 +149,45 @@ def test_decode_step_mixed_fp8_ffn_site():
     rel = np.abs(lg8 - lg).max() / np.abs(lg).max()
     assert 0 < rel < 0.15
     assert np.array_equal(lg8r[1], lg8[1])
+
+
+def test_decode_step_mixed_fp8_mlp_recomputed_with_torch_quantiser():
+    """One decoder layer: the mixed_fp8 step's residual output equals the
+    residual entering its MLP (the same step with the MLP weights zeroed)
+    plus fc2(GELU(fc1(LN(x)))) recomputed with torch's float8_e4m3fn
+    quantiser, each row with its own activation scales and each weight with
+    its tensor's (fp64 products of the code values)."""
+    from tests.test_oracle_layers import _tiny_weights
+    rng = np.random.default_rng(17)
+    d, H, V, ctx, Tenc, B = 64, 2, 50, 8, 7, 3
+    W = _tiny_weights(rng, d=d, n_dec=1, vocab=V, ctx=ctx)
+    p = "decoder.blocks.0."
+    W[p + "mlp.0.bias"] = rng.standard_normal(W[p + "mlp.0.bias"].shape) * 0.1
+    W[p + "mlp.2.bias"] = rng.standard_normal(W[p + "mlp.2.bias"].shape) * 0.1
+    enc = rng.standard_normal((B, Tenc, d))
+    cross_b = [O.cross_kv(enc[b], W, H, 1) for b in range(B)]
+    cross = [(np.stack([c[0][0] for c in cross_b]), np.stack([c[0][1] for c in cross_b]))]
+    toks = rng.integers(0, V, B)
+    scales = np.full((1, 2), np.float32(0.03), np.float32)
+    W0 = dict(W)
+    for k in ("mlp.0.weight", "mlp.0.bias", "mlp.2.weight", "mlp.2.bias"):
+        W0[p + k] = np.zeros_like(W[p + k])
+    cache = lambda: np.zeros((1, 2, B, H, ctx, d // H), np.uint8)  # noqa: E731
+    _, tr0 = O.decode_step(W0, H, toks, np.zeros(B, int), cache(), scales, cross)
+    _, tr8 = O.decode_step(W, H, toks, np.zeros(B, int), cache(), scales, cross, mixed_fp8=True)
+    x_pre = tr0["x"]
+
+    def tq(a, s):
+        y = torch.from_numpy(np.asarray(a, np.float32)) * torch.tensor(np.float32(1.0) / np.float32(s))
+        return y.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+    def site(a, w, b):
+        sw = np.float32(np.float32(np.abs(w).max()) / np.float32(448.0))
+        sa = np.float32(np.float32(np.abs(a).max()) / np.float32(448.0))
+        return (tq(a, sa) @ tq(w, sw).T) * (float(sa) * float(sw)) + b
+
+    for r in range(B):
+        m = O.layer_norm(x_pre[r], W[p + "mlp_ln.weight"], W[p + "mlp_ln.bias"])
+        h = O.gelu(site(m, W[p + "mlp.0.weight"], W[p + "mlp.0.bias"]))
+        want = x_pre[r] + site(h, W[p + "mlp.2.weight"], W[p + "mlp.2.bias"])
+        assert np.allclose(tr8["x"][r], want, rtol=1e-12, atol=1e-12), r
