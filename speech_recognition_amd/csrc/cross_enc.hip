@@ -42,12 +42,13 @@ hipError_t launch_pack_kt(const float* wk, int d, void* wkt, hipStream_t s) {
 // ------------------------------------------------------------------ q' = W_k,h^T q_h
 // q'^T[n][m] = sum_j W_kT[h][n][j] q[m][h*64 + j] with MFMA 16x16x32: A = W_kT
 // rows (16 n x 32 j), B = q^T (32 j x 16 rows m); the result lane holds 4
-// consecutive n of one row m (one 8-byte store). Workgroup: one head, 256
-// columns n, 64 rows m; wave w takes columns 64 w .. 64 w + 63.
-__global__ __launch_bounds__(256) void absorb_q_kernel(const u16* __restrict__ q, const u16* __restrict__ wkt,
-                                                       int M, int H, int d, u16* __restrict__ qp) {
-  const int h = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.y * 256 + wave * 64, m0 = blockIdx.z * 64;
+// consecutive n of one row m (one 8-byte store). Workgroup: one wave, one
+// head, 64 columns n, 64 rows m, so at batch 64 the 400 workgroups spread the
+// 3.3 MB of W_k^T and of q' over every compute unit.
+__global__ __launch_bounds__(64) void absorb_q_kernel(const u16* __restrict__ q, const u16* __restrict__ wkt,
+                                                      int M, int H, int d, u16* __restrict__ qp) {
+  const int h = blockIdx.x, lane = threadIdx.x & 63;
+  const int n0 = blockIdx.y * 64, m0 = blockIdx.z * 64;
   if (n0 >= d) return;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   uint4 a[4][2], bq[4][2];
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const u16* __restrict__ q
 
 hipError_t launch_absorb_q(const void* q, const void* wkt, int M, int H, int d, void* qp, hipStream_t s) {
   if (M <= 0 || H <= 0 || d % 256 || H * 64 != d) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(H, d / 256, (M + 63) / 64), dim3(256), 0, s, (const u16*)q,
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(H, d / 64, (M + 63) / 64), dim3(64), 0, s, (const u16*)q,
                      (const u16*)wkt, M, H, d, (u16*)qp);
   return hipGetLastError();
 }
@@ -397,25 +398,30 @@ hipError_t launch_attn_cross_enc(const void* qp, const void* E, int M, int H, in
 // u[m][h][:] = sum_s w_s U_s[h][:] / sum_s w_s l_s over the segments s of row
 // m (w_s = exp2(max_s - max)): the shares of workgroups w_first .. w_last,
 // in the slot of row m within each share. One workgroup of 256 threads per
-// (row, head): the first threads find the segments' slots and weights
-// (at most 256 segments: one per workgroup of the attention), then every
-// thread combines 8 columns per pass.
+// (row, head): the first threads read the segments' slots, maxima and sums
+// (at most 256 segments: one per workgroup of the attention) at once, then
+// every thread combines 8 columns per pass, with the loads of up to
+// XC_SEG segments issued before their sums (a row has 4-5 segments at batch
+// 64), in segment order.
+constexpr int XC_SEG = 8;
 __global__ __launch_bounds__(256) void absorb_combine_kernel(const u16* __restrict__ upart,
                                                              const float* __restrict__ ml, int H, int d, int nsub,
                                                              long G, int n_wg, int kmax, u16* __restrict__ u) {
   __shared__ long s_slot[256];
-  __shared__ float s_w[256];
+  __shared__ float s_w[256], s_l[256];
   __shared__ float s_inv;
   const int mh = blockIdx.x, m = mh / H, h = mh - (mh / H) * H, tid = threadIdx.x;
   auto wg_of = [&](long g_) { return (int)(((g_ + 1) * n_wg - 1) / G); };
   const int wf = wg_of((long)m * nsub), ns = wg_of((long)(m + 1) * nsub - 1) - wf + 1;
-  float mseg = -INFINITY;
+  float mseg = -INFINITY, lseg = 0.f;
   if (tid < ns) {
     const int w_ = wf + tid;
     const int r0 = (int)(((long)w_ * G / n_wg) / nsub);
     const long slot = ((long)w_ * kmax + (m - r0)) * H + h;
     s_slot[tid] = slot;
-    mseg = ml[slot * 2];
+    const float2 v = *(const float2*)(ml + slot * 2);
+    mseg = v.x;
+    lseg = v.y;
   }
   // the row's max over its segments, then each segment's weight
   float mx = mseg;
@@ -424,25 +430,35 @@ __global__ __launch_bounds__(256) void absorb_combine_kernel(const u16* __restri
   if ((tid & 63) == 0) s_mx[tid >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
-  if (tid < ns) s_w[tid] = __builtin_amdgcn_exp2f(mseg - mx);
+  if (tid < ns) {
+    s_w[tid] = __builtin_amdgcn_exp2f(mseg - mx);
+    s_l[tid] = lseg;
+  }
   __syncthreads();
   if (tid == 0) {
     float den = 0.f;
-    for (int k = 0; k < ns; ++k) den += s_w[k] * ml[s_slot[k] * 2 + 1];
+    for (int k = 0; k < ns; ++k) den += s_w[k] * s_l[k];
     s_inv = 1.0f / den;
   }
   __syncthreads();
   const float inv = s_inv;
   for (int ch = tid; ch < d / 8; ch += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < ns; ++k) {
-      const float wt = s_w[k];
-      const uint4 v = *(const uint4*)(upart + s_slot[k] * d + ch * 8);
-      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+    for (int k0 = 0; k0 < ns; k0 += XC_SEG) {
+      uint4 v[XC_SEG];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(wt, __uint_as_float(a[q] << 16), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(wt, __uint_as_float(a[q] & 0xffff0000u), acc[2 * q + 1]);
+      for (int k = 0; k < XC_SEG; ++k)
+        if (k0 + k < ns) v[k] = *(const uint4*)(upart + s_slot[k0 + k] * d + ch * 8);
+#pragma unroll
+      for (int k = 0; k < XC_SEG; ++k) {
+        if (k0 + k >= ns) break;
+        const float wt = s_w[k0 + k];
+        const uint32_t a[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wt, __uint_as_float(a[q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wt, __uint_as_float(a[q] & 0xffff0000u), acc[2 * q + 1]);
+        }
       }
     }
     *(uint4*)(u + ((long)m * H + h) * d + ch * 8) =
