@@ -468,6 +468,15 @@ def test_decode_from_encoder_output_full_and_ragged_batch():
     run_decode_case(dims4, 37, 672, 448, 2, [0, 36], "v3x4 enc B=37", from_enc=True)
 
 
+def test_decode_from_encoder_output_small_batch_many_segments():
+    """At batch 2 the frames of each row are shared over 23-24 workgroups, so
+    the combine step gathers each row from more segments than it loads at
+    once (eight): its chunked path, against the oracle."""
+    dims = CONFIGS["v3_decode"].with_(n_dec_layers=4)
+    say("decode from the encoder output, large-v3 shape, 4 layers, B=2, 2 steps")
+    run_decode_case(dims, 2, 672, 448, 2, [0, 1], "v3x4 enc B=2", from_enc=True)
+
+
 def test_decode_mixed_fp8_mlp_large_v3_shape():
     """The decoder MLP as mixed_fp8 sites (whisper_decode_step_enc_fp8: fc1
     and fc2 in E4M3, per-tensor weight scales, one activation scale per
