@@ -203,7 +203,7 @@ Packed8 layout8(const whisper_dims* d) {
 // The MLP down-projection (K = d_ffn) runs split-K over DEC_KSPLIT workgroups
 // per 16 x 80 output tile; its partials and tile counters live here.
 constexpr int DEC_KSPLIT = 4, DEC_SPLIT_COLS = 80;
-struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, amx, total; };
+struct DecWS { size_t x, a, dlt, q, att, qc, hf, logits, part, cnt, n_cnt, xg, amx, order, total; };
 DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   DecWS W;
   const size_t e = esz(d->act), D = d->d_model;
@@ -220,6 +220,7 @@ DecWS dec_ws(const whisper_dims* d, int B, bool with_logits = true) {
   W.cnt = take(tiles * 4);
   W.xg = take((size_t)((B + 15) & ~15) * D * 4);  // prefill: the last position of each batch row, 16-row tiles
   W.amx = take((size_t)B * ((d->n_vocab + 15) / 16) * 8);  // argmax: per-row maxima of 16-column blocks
+  W.order = take((size_t)B * 8);  // rows by cache length, longest first (row, length)
   W.total = off;
   return W;
 }
@@ -456,8 +457,9 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
   u16_t* HF = at<u16_t>(ws, W.hf);
   int32_t* CNT = at<int32_t>(ws, W.cnt);
   WH_CHECK(kvtrace_check(L, B, D, "decode"));
+  int2* ORD = R == 1 ? at<int2>(ws, W.order) : nullptr;
   WH_TRY(launch_embed(ACT_BF16, at<void>(packed, P.tok), at<void>(packed, P.pos), tokens, lengths, B, D, d->n_vocab,
-                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R));
+                      d->n_text_ctx, cap, X, dev_error, s, CNT, (int)W.n_cnt, 1, R, ORD));
   const Packed8 P8 = packed8 ? layout8(d) : Packed8{};
   auto gemm = [&](DecPro pro, DecEpi epi, size_t w_off, size_t b_off, size_t c1_off, int N, int K, const u16_t* A,
                   u16_t* out, float* out_f32, int layer, bool split = false, int a_group = 0) {
@@ -494,7 +496,7 @@ whisper_status decode_step_fused(const whisper_dims* d, const void* packed, cons
     {
       ProfScope ps(WHISPER_PROF_DECODE_SELF_ATTENTION, s);
       WH_TRY(launch_attn_decode_self(ACT_BF16, Q, D, kc, kc + kv_layer / 2, kv_scales + 2 * l, lengths, 1, B, H, cap,
-                                     ATT, s, R));
+                                     ATT, s, R, FP8_E4M3, ORD));
     }
     WH_TRY(gemm(PRO_A, DEPI_RESID, Lw.wo, Lw.bo, 0, D, D, ATT, nullptr, nullptr, l));
     WH_TRY(gemm(PRO_X, DEPI_STORE, Lw.wqc, Lw.bqc, Lw.c1qc, D, D, nullptr, QC, nullptr, l));

@@ -307,7 +307,9 @@ __device__ __forceinline__ float dot16_fp8(const uint4 c, const float* q) {
 // a private online softmax (running max, sum and 16 output dims), and the 256
 // private states are merged once at the end: block max, rescale, sum over
 // the 64 key groups (DPP within each 16-lane row, LDS across the 16 rows).
-// q goes straight from global to registers.
+// q goes straight from global to registers. Given a row order (longest cache
+// first), workgroup y takes row order[y]: the longest rows start in the first
+// round of workgroups and the shortest fill the last one.
 constexpr int SELF_KB = 8;
 
 template <typename T, int FMT>
@@ -316,12 +318,23 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
                                                                const uint8_t* __restrict__ vc,
                                                                const float* __restrict__ scales,
                                                                const int32_t* __restrict__ lengths, int len_add, int H,
-                                                               int cap, T* __restrict__ out, int rows_per_b) {
+                                                               int cap, T* __restrict__ out, int rows_per_b,
+                                                               const int2* __restrict__ order) {
   __shared__ __attribute__((aligned(16))) float red[16][64];
   __shared__ float rowmax[16], rsum[16];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // with order (one query row per cache row): workgroups take rows longest
+  // first, each row's length read with its index
+  int b = blockIdx.y, len = 0;
+  if (order) {
+    const int2 o = order[blockIdx.y];
+    b = o.x;
+    len = o.y;
+  } else if (lengths) {
+    len = lengths[b / rows_per_b];
+  }
   const int bc = b / rows_per_b;  // cache batch row of query row b
-  const int n = lengths ? max(0, min(lengths[bc] + len_add + b % rows_per_b, cap)) : cap;
+  const int n = (lengths || order) ? max(0, min(len + len_add + b % rows_per_b, cap)) : cap;
   const int part = tid & 3, kg = tid >> 2;
   float qreg[16];
   {
@@ -430,26 +443,27 @@ __global__ __launch_bounds__(256) void attn_decode_self_kernel(const T* __restri
 template <int FMT>
 static void decode_self_fmt(ActType t, const void* q, long q_stride, const uint8_t* k_codes, const uint8_t* v_codes,
                             const float* scales, const int32_t* lengths, int len_add, int B, int H, int cap,
-                            void* out, hipStream_t s, int rows_per_b) {
+                            void* out, hipStream_t s, int rows_per_b, const int2* order) {
   dim3 grid(H, B);
   if (t == ACT_BF16)
     hipLaunchKernelGGL((attn_decode_self_kernel<u16, FMT>), grid, dim3(256), 0, s, (const u16*)q, q_stride, k_codes,
-                       v_codes, scales, lengths, len_add, H, cap, (u16*)out, rows_per_b);
+                       v_codes, scales, lengths, len_add, H, cap, (u16*)out, rows_per_b, order);
   else
     hipLaunchKernelGGL((attn_decode_self_kernel<float, FMT>), grid, dim3(256), 0, s, (const float*)q, q_stride,
-                       k_codes, v_codes, scales, lengths, len_add, H, cap, (float*)out, rows_per_b);
+                       k_codes, v_codes, scales, lengths, len_add, H, cap, (float*)out, rows_per_b, order);
 }
 
 hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths, int len_add,
-                                   int B, int H, int cap, void* out, hipStream_t s, int rows_per_b, int fmt) {
-  if (cap > DEC_MAX_CAP || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
+                                   int B, int H, int cap, void* out, hipStream_t s, int rows_per_b, int fmt,
+                                   const int2* order) {
+  if (cap > DEC_MAX_CAP || rows_per_b < 1 || B % rows_per_b || (order && rows_per_b != 1)) return hipErrorInvalidValue;
   if (fmt == FP8_E5M2)
     decode_self_fmt<FP8_E5M2>(t, q, q_stride, k_codes, v_codes, scales, lengths, len_add, B, H, cap, out, s,
-                              rows_per_b);
+                              rows_per_b, order);
   else
     decode_self_fmt<FP8_E4M3>(t, q, q_stride, k_codes, v_codes, scales, lengths, len_add, B, H, cap, out, s,
-                              rows_per_b);
+                              rows_per_b, order);
   return hipGetLastError();
 }
 

@@ -472,14 +472,33 @@ hipError_t launch_zero_rows(ActType t, void* base, long row_elems, long rows_per
 // (in a prefill of R tokens per batch row, row b is token b % R of batch row
 // b / R, at position lengths[b / R] + b % R).
 // Out-of-range token ids or positions write zeros and raise the device error.
+// With order, each workgroup also ranks its row among all rows by cache
+// length (longest first, lower row first on ties) and writes (row, length)
+// at that rank: the dispatch order of the step's self-attention.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* pos_emb, const int32_t* tokens,
                                                     const int32_t* lengths, int d, int n_vocab, int n_ctx, int cap,
                                                     float* x, int32_t* dev_error, int32_t* zero, int n_zero,
-                                                    int x_tiled, int rows_per_b) {
+                                                    int x_tiled, int rows_per_b, int2* order) {
   const int b = blockIdx.x;
   if (b == 0)  // the step's split-K counters start at zero
     for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
+  if (order) {
+    // rows ranked by cache length, longest first (lower row first on ties):
+    // order[rank] = (row, length), so the self-attention can dispatch the
+    // longest rows first
+    __shared__ int s_cnt[4];
+    const int B = gridDim.x, nb = lengths[b];
+    int c = 0;
+    for (int j = threadIdx.x; j < B; j += 256) {
+      const int nj = lengths[j];
+      c += (nj > nb || (nj == nb && j < b)) ? 1 : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) order[s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3]] = make_int2(b, nb);
+  }
   const int tok = tokens[b], pos = lengths[b / rows_per_b] + b % rows_per_b;
   const bool ok = tok >= 0 && tok < n_vocab && pos >= 0 && pos < n_ctx && pos < cap;
   if (!ok && dev_error && threadIdx.x == 0) *dev_error = (pos >= cap) ? 6 : 1;
@@ -493,14 +512,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* tok_emb, const T* p
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
                         int32_t* dev_error, hipStream_t s, int32_t* zero, int n_zero, int x_tiled,
-                        int rows_per_b) {
-  if ((x_tiled && d % 32) || rows_per_b < 1 || B % rows_per_b) return hipErrorInvalidValue;
+                        int rows_per_b, int2* order) {
+  if ((x_tiled && d % 32) || rows_per_b < 1 || B % rows_per_b || (order && rows_per_b != 1))
+    return hipErrorInvalidValue;
   if (t == ACT_BF16)
     hipLaunchKernelGGL(embed_kernel<u16>, dim3(B), dim3(256), 0, s, (const u16*)tok_emb, (const u16*)pos_emb, tokens,
-                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b);
+                       lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b, order);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(B), dim3(256), 0, s, (const float*)tok_emb, (const float*)pos_emb,
-                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b);
+                       tokens, lengths, d, n_vocab, n_ctx, cap, x, dev_error, zero, n_zero, x_tiled, rows_per_b,
+                       order);
   return hipGetLastError();
 }
 

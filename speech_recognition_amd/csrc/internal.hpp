@@ -174,11 +174,13 @@ hipError_t launch_attn_encoder(ActType t, const void* qkv, int B, int T, int H, 
 // rows_per_b (R): query row m reads cache batch row m / R and attends over
 // n = lengths[m / R] + len_add + m % R keys (B = query rows)
 // fmt: code format of k_codes / v_codes (FP8_E4M3 for the KV cache; either
-// format for fp8 cross-attention K/V).
+// format for fp8 cross-attention K/V). order (R = 1 only; NULL: row order):
+// B (row, length) pairs, longest first, as launch_embed writes them; the
+// workgroups then take the rows in that order with the lengths given there.
 hipError_t launch_attn_decode_self(ActType t, const void* q, long q_stride, const uint8_t* k_codes,
                                    const uint8_t* v_codes, const float* scales, const int32_t* lengths,
                                    int len_add, int B, int H, int cap, void* out, hipStream_t s, int rows_per_b = 1,
-                                   int fmt = 0);
+                                   int fmt = 0, const int2* order = nullptr);
 // Decode cross-attention over head-major K/V [B / R][H][T][64] (query row m
 // reads K/V batch row m / R, R = rows_per_b); one pass per (row, head).
 hipError_t launch_attn_decode_cross(ActType t, const void* q, const void* k, const void* v, int B, int H, int T,
@@ -204,8 +206,9 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s
 hipError_t launch_embed(ActType t, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* lengths, int B, int d, int n_vocab, int n_ctx, int cap, float* x,
                         int32_t* dev_error, hipStream_t s, int32_t* zero = nullptr, int n_zero = 0,
-                        int x_tiled = 0, int rows_per_b = 1);  // x_tiled: x in the 16-row tiles of dec_x_index;
-                        // rows_per_b (R): B rows, row m is token m of batch row m / R at lengths[m / R] + m % R
+                        int x_tiled = 0, int rows_per_b = 1, int2* order = nullptr);  // x_tiled: x in the 16-row tiles of dec_x_index;
+                        // rows_per_b (R): B rows, row m is token m of batch row m / R at lengths[m / R] + m % R;
+                        // order (R = 1 only; NULL: off): [B] (row, lengths[row]) ranked longest first, ties by row
 hipError_t launch_argmax_part(const int2* part, int B, int NB, int32_t* argmax, int32_t* lengths, hipStream_t s,
                               int len_inc = 1);
 hipError_t launch_argmax(const float* logits, int B, int V, int32_t* argmax, int32_t* lengths, hipStream_t s,
