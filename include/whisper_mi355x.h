@@ -262,8 +262,8 @@ whisper_status whisper_decode_step(const whisper_dims* dims, const void* packed,
  * process ends; the call itself allocates nothing. Arguments and results are
  * those of whisper_decode_step, except that logits must be given (non-NULL).
  * A batch whose workspace without logits (whisper_workspace_size(dims, batch,
- * WHISPER_WS_DECODE) less batch * n_vocab * 4 bytes, about 80 KB per row at
- * the large-v3 shape: up to 101 rows) exceeds the array returns
+ * WHISPER_WS_DECODE) less batch * n_vocab * 4 bytes, about 81 KB per row at
+ * the large-v3 shape: up to 100 rows) exceeds the array returns
  * WHISPER_ERR_WORKSPACE before launching anything. Every call on one GPU
  * shares that GPU's array: calls that overlap in time on one GPU (other
  * streams, other threads) race and must be serialised by the caller; the
